@@ -1,0 +1,13 @@
+"""MI355X (gfx950) implementation of the DeepSeek-V4 CSA / HCA attention forward.
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``libcsa.so`` (``include/csa.h``); this package is the thin Python binding over it
+(torch tensors supply device memory and streams).  Build the library with
+``python -m compressed_sparse_attention_07_amd.build``.
+"""
+
+from ._lib import (  # noqa: F401
+    CSA_BF16, CSA_F32, CSA_FP8MIX, CSA_MODE_CSA, CSA_MODE_HCA, CSA_MXFP4, Buf, CSAError, EXPORTS, LIB_PATH,
+    csa_compress, csa_forward, csa_forward_workspace_size, csa_index_scores, csa_quantize, csa_sparse_mqa, csa_topk,
+    hca_dense_attn, layer_desc, lib,
+)

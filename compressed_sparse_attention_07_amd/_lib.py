@@ -1,0 +1,279 @@
+"""ctypes binding of libcsa.so: argument marshalling only.
+
+Every function here forwards torch tensors (device memory owned by the caller) and
+the current HIP stream to the C entry point of the same name in include/csa.h.
+No step of the computation happens in Python; if the library is missing the call
+raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcsa.so")
+
+CSA_F32, CSA_BF16, CSA_FP8MIX, CSA_MXFP4 = 0, 1, 2, 3
+CSA_MODE_CSA, CSA_MODE_HCA = 0, 1
+STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_DTYPE",
+          4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_DEVICE", 6: "CSA_ERR_UNSUPPORTED"}
+
+EXPORTS = ["csa_abi_version", "csa_last_error", "csa_device_check", "csa_compress", "csa_quantize",
+           "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size",
+           "csa_sparse_mqa", "hca_dense_attn_workspace_size", "hca_dense_attn",
+           "csa_forward_workspace_size", "csa_forward"]
+
+
+class CSAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class csa_buf(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("rope", C.c_void_p), ("scale", C.c_void_p),
+                ("dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
+class csa_layer_desc(C.Structure):
+    _fields_ = [("struct_size", C.c_int32), ("mode", C.c_int32),
+                ("B", C.c_int64), ("T", C.c_int64), ("t0", C.c_int64), ("Tq", C.c_int64),
+                ("cache_rows", C.c_int64), ("Tw", C.c_int64),
+                ("D", C.c_int32), ("H", C.c_int32), ("HI", C.c_int32), ("DI", C.c_int32),
+                ("ratio", C.c_int32), ("topk", C.c_int32), ("n_win", C.c_int32), ("rope_dims", C.c_int32),
+                ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("pos_offset", C.c_int64),
+                ("stream_dtype", C.c_int32), ("pad0", C.c_int32)]
+
+
+class csa_forward_io(C.Structure):
+    _fields_ = [("ca", C.c_void_p), ("cb", C.c_void_p), ("za", C.c_void_p), ("zb", C.c_void_p),
+                ("bias_a", C.c_void_p), ("bias_b", C.c_void_p), ("prev_cb", C.c_void_p), ("prev_zb", C.c_void_p),
+                ("ica", C.c_void_p), ("icb", C.c_void_p), ("iza", C.c_void_p), ("izb", C.c_void_p),
+                ("ibias_a", C.c_void_p), ("ibias_b", C.c_void_p), ("iprev_cb", C.c_void_p), ("iprev_zb", C.c_void_p),
+                ("kv_cache", csa_buf), ("ik_cache", csa_buf), ("q", csa_buf), ("q_pos", C.c_void_p),
+                ("qI", csa_buf), ("wI", C.c_void_p), ("win", csa_buf), ("win_pos0", C.c_void_p),
+                ("sink", C.c_void_p), ("out", csa_buf), ("scores_out", C.c_void_p), ("idx_out", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcsa.so (built in-tree); raise loudly if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m compressed_sparse_attention_07_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+        bp = C.POINTER(csa_buf)
+        L.csa_abi_version.restype = C.c_int
+        L.csa_last_error.restype = C.c_char_p
+        L.csa_device_check.restype = C.c_int
+        L.csa_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, i32, i64, i32, f32, i64,
+                                   bp, i64, vp]
+        L.csa_quantize.argtypes = [vp, i64, i32, i32, bp, vp]
+        L.csa_index_scores.argtypes = [bp, vp, bp, vp, i64, i64, i32, i32, i64, i64, i32, vp, vp]
+        L.csa_topk_workspace_size.argtypes = [i64, i64, i32]
+        L.csa_topk_workspace_size.restype = sz
+        L.csa_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.csa_sparse_mqa_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32]
+        L.csa_sparse_mqa_workspace_size.restype = sz
+        L.csa_sparse_mqa.argtypes = [bp, vp, bp, i64, vp, i32, bp, vp, i64, vp, f32, i32, f32, i64, i64, i64, i32,
+                                     i32, i64, i32, bp, vp, sz, vp]
+        L.hca_dense_attn_workspace_size.argtypes = [i64, i64, i32, i32, i64, i32]
+        L.hca_dense_attn_workspace_size.restype = sz
+        L.hca_dense_attn.argtypes = [bp, vp, bp, i64, i32, bp, vp, i64, vp, f32, i32, f32, i64, i64, i64, i32, i32,
+                                     i64, i32, bp, vp, sz, vp]
+        L.csa_forward_workspace_size.argtypes = [C.POINTER(csa_layer_desc)]
+        L.csa_forward_workspace_size.restype = sz
+        L.csa_forward.argtypes = [C.POINTER(csa_layer_desc), C.POINTER(csa_forward_io), vp, sz, vp]
+        for name in EXPORTS:
+            if name not in ("csa_topk_workspace_size", "csa_sparse_mqa_workspace_size",
+                            "hca_dense_attn_workspace_size", "csa_forward_workspace_size",
+                            "csa_last_error", "csa_abi_version"):
+                getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise CSAError(status, lib().csa_last_error().decode())
+
+
+def ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def stream_handle(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ buffers
+
+
+class Buf:
+    """A tensor (or tensor triple) in one of the library's storage formats."""
+
+    def __init__(self, dtype: int, data, rope=None, scale=None):
+        self.dtype, self.data, self.rope, self.scale = dtype, data, rope, scale
+
+    @property
+    def shape(self):
+        if self.dtype in (CSA_F32, CSA_BF16):
+            return tuple(self.data.shape)
+        if self.dtype == CSA_FP8MIX:
+            return tuple(self.data.shape[:-1]) + (self.data.shape[-1] + self.rope.shape[-1],)
+        return tuple(self.data.shape[:-1]) + (2 * self.data.shape[-1],)
+
+    def rows(self, lo: int, hi: int) -> "Buf":
+        """View of rows [lo, hi) along dim 1 (the per-sequence row axis)."""
+        sl = lambda t: None if t is None else t[:, lo:hi]
+        return Buf(self.dtype, sl(self.data), sl(self.rope), sl(self.scale))
+
+    def c(self) -> csa_buf:
+        return csa_buf(ptr(self.data), ptr(self.rope), ptr(self.scale), self.dtype, 0)
+
+    @staticmethod
+    def of(t) -> "Buf":
+        if isinstance(t, Buf):
+            return t
+        if t.dtype == torch.float32:
+            return Buf(CSA_F32, t)
+        if t.dtype == torch.bfloat16:
+            return Buf(CSA_BF16, t)
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+    @staticmethod
+    def empty(shape, dtype: int, rope_dims: int = 0, device="cuda") -> "Buf":
+        *lead, D = shape
+        lead = tuple(lead)
+        if dtype == CSA_F32:
+            return Buf(dtype, torch.empty(lead + (D,), dtype=torch.float32, device=device))
+        if dtype == CSA_BF16:
+            return Buf(dtype, torch.empty(lead + (D,), dtype=torch.bfloat16, device=device))
+        if dtype == CSA_FP8MIX:
+            return Buf(dtype, torch.empty(lead + (D - rope_dims,), dtype=torch.uint8, device=device),
+                       torch.empty(lead + (rope_dims,), dtype=torch.bfloat16, device=device),
+                       torch.empty(lead, dtype=torch.float32, device=device))
+        if dtype == CSA_MXFP4:
+            return Buf(dtype, torch.empty(lead + (D // 2,), dtype=torch.uint8, device=device), None,
+                       torch.empty(lead + (D // 32,), dtype=torch.uint8, device=device))
+        raise ValueError(dtype)
+
+
+def _ws(nbytes: int, device, ws=None):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _dt(t) -> int:
+    return Buf.of(t).dtype
+
+
+# ------------------------------------------------------------------ entry points
+
+
+def csa_compress(ca, cb, za, zb, out: Buf, *, ratio: int, overlap: bool, t0: int = 0, bias_a=None, bias_b=None,
+                 prev_cb=None, prev_zb=None, rope_dims: int = 0, rope_base: float = 10000.0, pos_offset: int = 0,
+                 stream=None) -> None:
+    B, T, D = ca.shape
+    out_rows = out.shape[1]
+    bo = out.c()
+    check(lib().csa_compress(ptr(ca), ptr(cb), ptr(za), ptr(zb), _dt(ca), ptr(bias_a), ptr(bias_b), ptr(prev_cb),
+                             ptr(prev_zb), B, T, D, ratio, 1 if overlap else 0, t0, rope_dims, rope_base, pos_offset,
+                             C.byref(bo), out_rows, stream_handle(stream)))
+
+
+def csa_quantize(x, out: Buf, *, rope_dims: int = 0, stream=None) -> None:
+    D = x.shape[-1]
+    rows = x.numel() // D
+    bo = out.c()
+    check(lib().csa_quantize(ptr(x), rows, D, rope_dims, C.byref(bo), stream_handle(stream)))
+
+
+def csa_index_scores(qI, wI, kI, q_pos, scores, *, ratio: int, stream=None) -> None:
+    qb, kb = Buf.of(qI), Buf.of(kI)
+    B, Tq, HI, DI = qb.shape
+    _, kI_rows, _ = kb.shape
+    N = scores.shape[-1]
+    cq, ck = qb.c(), kb.c()
+    check(lib().csa_index_scores(C.byref(cq), ptr(wI), C.byref(ck), ptr(q_pos), B, Tq, HI, DI, N, kI_rows, ratio,
+                                 ptr(scores), stream_handle(stream)))
+
+
+def csa_topk(scores, k: int, idx, count=None, *, ws=None, stream=None) -> None:
+    N = scores.shape[-1]
+    rows = scores.numel() // N if N else scores.numel()
+    need = lib().csa_topk_workspace_size(rows, N, k)
+    w, wb = _ws(need, scores.device, ws)
+    check(lib().csa_topk(ptr(scores), rows, N, k, ptr(idx), ptr(count), ptr(w), wb, stream_handle(stream)))
+
+
+def csa_sparse_mqa(q, q_pos, kv, idx, win, win_pos0, sink, out, *, N: int, n_win: int, softmax_scale: float,
+                   rope_dims: int, rope_base: float = 10000.0, pos_offset: int = 0, ws=None, stream=None) -> None:
+    qb, kvb, wb_, ob = Buf.of(q), Buf.of(kv), Buf.of(win), Buf.of(out)
+    B, Tq, H, D = qb.shape
+    kv_rows = kvb.shape[1]
+    Tw = wb_.shape[1]
+    K = idx.shape[-1]
+    need = lib().csa_sparse_mqa_workspace_size(B, Tq, H, D, K, n_win)
+    w, wbytes = _ws(need, q.device if not isinstance(q, Buf) else q.data.device, ws)
+    cq, ck, cw, co = qb.c(), kvb.c(), wb_.c(), ob.c()
+    check(lib().csa_sparse_mqa(C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ptr(idx), K, C.byref(cw), ptr(win_pos0),
+                               Tw, ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
+                               C.byref(co), ptr(w), wbytes, stream_handle(stream)))
+
+
+def hca_dense_attn(q, q_pos, kv, win, win_pos0, sink, out, *, N: int, ratio: int, n_win: int, softmax_scale: float,
+                   rope_dims: int, rope_base: float = 10000.0, pos_offset: int = 0, ws=None, stream=None) -> None:
+    qb, kvb, wb_, ob = Buf.of(q), Buf.of(kv), Buf.of(win), Buf.of(out)
+    B, Tq, H, D = qb.shape
+    kv_rows = kvb.shape[1]
+    Tw = wb_.shape[1]
+    need = lib().hca_dense_attn_workspace_size(B, Tq, H, D, N, n_win)
+    w, wbytes = _ws(need, qb.data.device, ws)
+    cq, ck, cw, co = qb.c(), kvb.c(), wb_.c(), ob.c()
+    check(lib().hca_dense_attn(C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ratio, C.byref(cw), ptr(win_pos0), Tw,
+                               ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
+                               C.byref(co), ptr(w), wbytes, stream_handle(stream)))
+
+
+def layer_desc(**kw) -> csa_layer_desc:
+    d = csa_layer_desc()
+    d.struct_size = C.sizeof(csa_layer_desc)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def csa_forward_workspace_size(desc: csa_layer_desc) -> int:
+    return lib().csa_forward_workspace_size(C.byref(desc))
+
+
+def csa_forward(desc: csa_layer_desc, io: dict, *, ws=None, stream=None) -> None:
+    """io maps csa_forward_io field names to tensors / Buf objects (missing = NULL)."""
+    cio = csa_forward_io()
+    keep = []
+    for name, val in io.items():
+        if val is None:
+            continue
+        if isinstance(val, Buf) or (name in ("kv_cache", "ik_cache", "q", "qI", "win", "out")):
+            b = Buf.of(val).c()
+            keep.append(b)
+            setattr(cio, name, b)
+        else:
+            setattr(cio, name, ptr(val))
+    need = csa_forward_workspace_size(desc)
+    dev = Buf.of(io["q"]).data.device
+    w, wbytes = _ws(need, dev, ws)
+    check(lib().csa_forward(C.byref(desc), C.byref(cio), ptr(w), wbytes, stream_handle(stream)))

@@ -1,0 +1,376 @@
+// K1: softmax-weighted KV compression (CSA overlap / HCA block) and the fp32 ->
+// storage-format quantizer.
+//
+// Method: [V4-CN] "DeepSeek-V4中文翻译" §2.3.1 (CSA compression equations: the
+// current block's a-branch and the previous block's b-branch, soft-maxed per
+// channel across the 2m positions) and §2.3.2 (HCA: one block of m' positions, no
+// overlap); partial RoPE of the entry, §2.3.3; storage formats §2.3.4 / §3.4.
+//
+// Design (HBM stream-and-reduce): every input row is read exactly once.  A thread
+// owns 8 consecutive channels of one entry and a subset ("row group") of its
+// positions; consecutive lanes own consecutive channel chunks, so every wave load
+// is a contiguous row segment.  Each thread runs an online softmax over its rows
+// in batches of 8 (all loads of a batch are issued before any math), row groups
+// are merged in fixed order through LDS, then the epilogue applies RoPE and the
+// output format (fp32, bf16, FP8-mixed with a per-entry scale, MXFP4 with a
+// per-32 scale), reducing the scale maxima with LDS atomics.
+#include "device_common.h"
+#include "launch.h"
+
+namespace csa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 8;      // channels per thread
+constexpr int kBatch = 8;    // rows per online-softmax batch
+
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float v[kVec]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[kVec]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float v[kVec]) {
+  uint4 a = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16lo(a.x); v[1] = bf16hi(a.x);
+  v[2] = bf16lo(a.y); v[3] = bf16hi(a.y);
+  v[4] = bf16lo(a.z); v[5] = bf16hi(a.z);
+  v[6] = bf16lo(a.w); v[7] = bf16hi(a.w);
+}
+
+struct OutDesc {
+  void* data;
+  void* rope;
+  void* scale;
+  int dtype;
+  int D;
+  int R;
+};
+
+// Store 8 channels (chunk c) of the entry at global row `row`.  `amax_slot` is an
+// LDS word per entry (FP8MIX) or per 32-block (MXFP4) already holding the reduced
+// maximum magnitude.  Must be called after the LDS maxima are final.
+__device__ __forceinline__ void store_chunk(const OutDesc& o, int64_t row, int c, const float v[kVec],
+                                            const uint32_t* amax_lds_entry) {
+  const int d0 = c * kVec;
+  switch (o.dtype) {
+    case CSA_F32: {
+      float* p = static_cast<float*>(o.data) + row * o.D + d0;
+      reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      break;
+    }
+    case CSA_BF16: {
+      uint16_t* p = static_cast<uint16_t*>(o.data) + row * o.D + d0;
+      *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      break;
+    }
+    case CSA_FP8MIX: {
+      const int nope = o.D - o.R;
+      if (d0 >= nope) {
+        uint16_t* p = static_cast<uint16_t*>(o.rope) + row * o.R + (d0 - nope);
+        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      } else {
+        float amax = __uint_as_float(amax_lds_entry[0]);
+        float s = amax > 0.f ? amax / 448.0f : 1.0f;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] / s) << (8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
+        uint8_t* p = static_cast<uint8_t*>(o.data) + row * nope + d0;
+        *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+        if (c == 0) static_cast<float*>(o.scale)[row] = s;
+      }
+      break;
+    }
+    case CSA_MXFP4: {
+      const int blk = d0 / 32;
+      float amax = __uint_as_float(amax_lds_entry[blk]);
+      int X = -127;
+      if (amax > 0.f) X = ilogbf(amax) - 2;
+      X = X < -127 ? -127 : (X > 127 ? 127 : X);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) packed |= f32_to_e2m1(ldexpf(v[i], -X)) << (4 * i);
+      uint8_t* p = static_cast<uint8_t*>(o.data) + row * (o.D / 2) + d0 / 2;
+      *reinterpret_cast<uint32_t*>(p) = packed;
+      if ((d0 & 31) == 0) static_cast<uint8_t*>(o.scale)[row * (o.D / 32) + blk] = static_cast<uint8_t>(X + 127);
+      break;
+    }
+  }
+}
+
+// Contribute this chunk's magnitudes to the LDS maxima used by the quantized formats.
+__device__ __forceinline__ void amax_chunk(const OutDesc& o, int c, const float v[kVec],
+                                           uint32_t* amax_lds_entry) {
+  const int d0 = c * kVec;
+  if (o.dtype == CSA_FP8MIX) {
+    if (d0 >= o.D - o.R) return;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) m = fmaxf(m, fabsf(v[i]));
+    atomicMax(&amax_lds_entry[0], __float_as_uint(m));
+  } else if (o.dtype == CSA_MXFP4) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) m = fmaxf(m, fabsf(v[i]));
+    atomicMax(&amax_lds_entry[d0 / 32], __float_as_uint(m));
+  }
+}
+
+__device__ __forceinline__ int amax_words(int dtype, int D) {
+  return dtype == CSA_MXFP4 ? D / 32 : 1;
+}
+
+struct CompressArgs {
+  const void* ca;
+  const void* cb;
+  const void* za;
+  const void* zb;
+  const float* bias_a;
+  const float* bias_b;
+  const void* prev_cb;
+  const void* prev_zb;
+  int64_t B, T, t0, out_rows, pos_offset;
+  int D, ratio, overlap, R;
+  int chunks, G, entries_per_wg;
+  double log2_base;
+  OutDesc out;
+};
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
+  // LDS: row-group partials (m, s, acc[8]) and per-entry scale maxima
+  __shared__ float part[kThreads * (2 + kVec)];
+  __shared__ uint32_t amax_lds[kThreads];  // entries_per_wg * amax_words <= 256
+
+  const int tid = threadIdx.x;
+  const int tpe = a.chunks * a.G;                       // threads per entry
+  const int e_local = tid / tpe;
+  const int r_in = tid % tpe;
+  const int g = r_in / a.chunks;                         // row group
+  const int c = r_in % a.chunks;                         // channel chunk
+  const int64_t n_entries = a.T / a.ratio;
+  const int64_t e_glob = static_cast<int64_t>(blockIdx.x) * a.entries_per_wg + e_local;
+  const int64_t total = a.B * n_entries;
+  const bool active = e_local < a.entries_per_wg && e_glob < total;
+  const int aw = amax_words(a.out.dtype, a.D);
+
+  for (int i = tid; i < a.entries_per_wg * aw && i < kThreads; i += kThreads) amax_lds[i] = 0u;
+
+  float m[kVec], s[kVec], acc[kVec];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) { m[i] = -INFINITY; s[i] = 0.f; acc[i] = 0.f; }
+
+  int64_t b = 0, il = 0, I = 0;
+  if (active) {
+    b = e_glob / n_entries;
+    il = e_glob % n_entries;              // local entry index within this call
+    I = a.t0 / a.ratio + il;              // absolute entry index
+    const int r = a.ratio;
+    // positions: [0, r) a-rows of block I; [r, 2r) b-rows of block I-1 (CSA, I >= 1)
+    const int nrows = (a.overlap && I >= 1) ? 2 * r : r;
+    const TIn* ca = static_cast<const TIn*>(a.ca) + (b * a.T) * a.D;
+    const TIn* za = static_cast<const TIn*>(a.za) + (b * a.T) * a.D;
+    const TIn* cb = static_cast<const TIn*>(a.cb) + (b * a.T) * a.D;
+    const TIn* zb = static_cast<const TIn*>(a.zb) + (b * a.T) * a.D;
+    const TIn* pcb = static_cast<const TIn*>(a.prev_cb) + b * r * a.D;
+    const TIn* pzb = static_cast<const TIn*>(a.prev_zb) + b * r * a.D;
+    const int d0 = c * kVec;
+
+    for (int base = g; base < nrows; base += a.G * kBatch) {
+      float z[kBatch][kVec], v[kBatch][kVec];
+      int nb = 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int pos = base + q * a.G;
+        if (pos < nrows) {
+          nb = q + 1;
+          const TIn *cp, *zp;
+          const float* bp;
+          if (pos < r) {
+            const int64_t row = il * r + pos;
+            cp = ca + row * a.D + d0;
+            zp = za + row * a.D + d0;
+            bp = a.bias_a ? a.bias_a + pos * a.D + d0 : nullptr;
+          } else {
+            const int j = pos - r;
+            if (il >= 1) {
+              const int64_t row = (il - 1) * r + j;
+              cp = cb + row * a.D + d0;
+              zp = zb + row * a.D + d0;
+            } else {
+              cp = pcb + j * a.D + d0;
+              zp = pzb + j * a.D + d0;
+            }
+            bp = a.bias_b ? a.bias_b + j * a.D + d0 : nullptr;
+          }
+          load8<TIn>(cp, v[q]);
+          load8<TIn>(zp, z[q]);
+          if (bp) {
+            float4 b0 = reinterpret_cast<const float4*>(bp)[0];
+            float4 b1 = reinterpret_cast<const float4*>(bp)[1];
+            z[q][0] += b0.x; z[q][1] += b0.y; z[q][2] += b0.z; z[q][3] += b0.w;
+            z[q][4] += b1.x; z[q][5] += b1.y; z[q][6] += b1.z; z[q][7] += b1.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < kVec; ++ch) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+          if (q < nb) bm = fmaxf(bm, z[q][ch]);
+        const float nm = fmaxf(m[ch], bm);
+        if (nm == -INFINITY) continue;               // every logit so far is -inf
+        const float sc = __expf(m[ch] - nm);         // 0 when m was -inf
+        float ss = s[ch] * sc, aa = acc[ch] * sc;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          if (q < nb) {
+            const float p = __expf(z[q][ch] - nm);
+            ss += p;
+            aa = fmaf(p, v[q][ch], aa);
+          }
+        }
+        m[ch] = nm; s[ch] = ss; acc[ch] = aa;
+      }
+    }
+  }
+
+  // merge row groups in fixed order
+  if (a.G > 1) {
+    float* my = part + tid * (2 + kVec);
+    // pack: m for channel 0 only is not enough (per-channel maxima) -> store all
+    // channels in three passes to keep LDS at (2+8) floats per thread
+    __syncthreads();
+#pragma unroll
+    for (int ch = 0; ch < kVec; ++ch) {
+      my[0] = m[ch]; my[1] = s[ch]; my[2 + ch] = acc[ch];
+      __syncthreads();
+      if (active && g == 0) {
+        float mm = m[ch], sum = s[ch], ac = acc[ch];
+        for (int gg = 1; gg < a.G; ++gg) {
+          const float* o = part + (e_local * tpe + gg * a.chunks + c) * (2 + kVec);
+          const float om = o[0];
+          const float nm = fmaxf(mm, om);
+          if (nm == -INFINITY) continue;
+          const float s1 = __expf(mm - nm), s2 = __expf(om - nm);
+          sum = sum * s1 + o[1] * s2;
+          ac = ac * s1 + o[2 + ch] * s2;
+          mm = nm;
+        }
+        m[ch] = mm; s[ch] = sum; acc[ch] = ac;
+      }
+      __syncthreads();
+    }
+  }
+
+  float val[kVec];
+  const bool owner = active && g == 0;
+  if (owner) {
+#pragma unroll
+    for (int ch = 0; ch < kVec; ++ch) val[ch] = acc[ch] / s[ch];
+    // partial RoPE at position pos_offset + ratio * I
+    const int d0 = c * kVec;
+    const int nope = a.D - a.R;
+    if (a.R > 0 && d0 + kVec > nope) {
+      const double pos = static_cast<double>(a.pos_offset + I * a.ratio);
+#pragma unroll
+      for (int ch = 0; ch < kVec; ch += 2) {
+        const int d = d0 + ch;
+        if (d >= nope) {
+          float cs, sn;
+          rope_cs(pos, (d - nope) / 2, a.R, a.log2_base, &cs, &sn);
+          const float x0 = val[ch], x1 = val[ch + 1];
+          val[ch] = x0 * cs - x1 * sn;
+          val[ch + 1] = x0 * sn + x1 * cs;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (owner) amax_chunk(a.out, c, val, amax_lds + e_local * aw);
+  __syncthreads();
+  if (owner) {
+    const int64_t row = b * a.out_rows + I;
+    store_chunk(a.out, row, c, val, amax_lds + e_local * aw);
+  }
+}
+
+struct QuantArgs {
+  const float* x;
+  int64_t rows;
+  int D, chunks, entries_per_wg;
+  OutDesc out;
+};
+
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
+  __shared__ uint32_t amax_lds[kThreads];
+  const int tid = threadIdx.x;
+  const int e_local = tid / a.chunks;
+  const int c = tid % a.chunks;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * a.entries_per_wg + e_local;
+  const bool active = e_local < a.entries_per_wg && row < a.rows;
+  const int aw = amax_words(a.out.dtype, a.D);
+  for (int i = tid; i < a.entries_per_wg * aw && i < kThreads; i += kThreads) amax_lds[i] = 0u;
+  float v[kVec];
+  if (active) load8<float>(a.x + row * a.D + c * kVec, v);
+  __syncthreads();
+  if (active) amax_chunk(a.out, c, v, amax_lds + e_local * aw);
+  __syncthreads();
+  if (active) store_chunk(a.out, row, c, v, amax_lds + e_local * aw);
+}
+
+}  // namespace
+
+int launch_compress(const CompressLaunch& L, hipStream_t stream) {
+  CompressArgs a{};
+  a.ca = L.ca; a.cb = L.cb; a.za = L.za; a.zb = L.zb;
+  a.bias_a = L.bias_a; a.bias_b = L.bias_b;
+  a.prev_cb = L.prev_cb; a.prev_zb = L.prev_zb;
+  a.B = L.B; a.T = L.T; a.t0 = L.t0; a.out_rows = L.out_rows; a.pos_offset = L.pos_offset;
+  a.D = L.D; a.ratio = L.ratio; a.overlap = L.overlap; a.R = L.rope_dims;
+  a.log2_base = L.log2_base;
+  a.out = OutDesc{L.out.data, L.out.rope, L.out.scale, L.out.dtype, L.D, L.rope_dims};
+  a.chunks = L.D / kVec;
+  const int nrows = L.overlap ? 2 * L.ratio : L.ratio;
+  // row groups: enough to keep every wave busy on long blocks (HCA), one for CSA
+  int G = 1;
+  while (G * 2 * a.chunks <= kThreads && nrows / (G * 2) >= kBatch) G *= 2;
+  a.G = G;
+  a.entries_per_wg = kThreads / (a.chunks * G);
+  const int64_t n_entries = L.B * (L.T / L.ratio);
+  if (n_entries == 0) return 0;
+  const int64_t grid = (n_entries + a.entries_per_wg - 1) / a.entries_per_wg;
+  if (L.stream_dtype == CSA_F32)
+    hipLaunchKernelGGL(compress_kernel<float>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(compress_kernel<uint16_t>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_quantize(const float* x, int64_t rows, int D, int rope_dims, const csa_buf& out,
+                    hipStream_t stream) {
+  if (rows == 0) return 0;
+  QuantArgs a{};
+  a.x = x; a.rows = rows; a.D = D;
+  a.chunks = D / kVec;
+  a.entries_per_wg = kThreads / a.chunks;
+  a.out = OutDesc{out.data, out.rope, out.scale, out.dtype, D, rope_dims};
+  const int64_t grid = (rows + a.entries_per_wg - 1) / a.entries_per_wg;
+  hipLaunchKernelGGL(quantize_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa

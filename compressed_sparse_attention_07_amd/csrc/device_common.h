@@ -1,0 +1,160 @@
+// Device helpers shared by the gfx950 kernels of libcsa: storage-format
+// conversions, RoPE angles, wave-level reductions.  CDNA4 only (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+// ----------------------------------------------------------------- bf16 <-> f32
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// nearest-even; NaN stays NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// --------------------------------------------------------------------- e4m3 (OCP)
+
+// e4m3 code -> float (exact).  0x7f / 0xff decode to NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xfu;
+  uint32_t m = c & 0x7u;
+  if (e == 0xfu && m == 0x7u) return __uint_as_float(0x7fc00000u | s);
+  float mag;
+  if (e == 0) {
+    mag = static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2^(e-7)
+  }
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// e4m3 code -> bf16 bits (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
+  return static_cast<uint16_t>(__float_as_uint(e4m3_to_f32(c)) >> 16);
+}
+
+// float -> e4m3 code, nearest-even, saturating to +-448, sign bit follows the input
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t s = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                   // NaN
+  if (a >= 0x43e00000u) return s | 0x7eu;              // |x| >= 448 (incl. inf) -> 448
+  int e = static_cast<int>(a >> 23) - 127;             // binade of |x| (normal fp32)
+  if (a < 0x00800000u) e = -127;                        // fp32 subnormal: far below range
+  if (e < -6) {
+    // e4m3 subnormal range: quantum 2^-9, code = rne(|x| / 2^-9)
+    float q = __uint_as_float(a) * 512.0f;              // exact scaling by 2^9
+    uint32_t r = static_cast<uint32_t>(__builtin_rintf(q));  // rint = nearest-even
+    return s | r;                                       // r == 8 is the smallest normal code
+  }
+  // normal: keep 3 mantissa bits, nearest-even on the 20 dropped bits
+  uint32_t mant = a & 0x7fffffu;
+  uint32_t keep = mant >> 20;
+  uint32_t rest = mant & 0xfffffu;
+  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | keep;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1;  // may carry into exponent
+  if (code > 0x7eu) code = 0x7eu;
+  return s | code;
+}
+
+// --------------------------------------------------------------------- e2m1 (OCP MX)
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const float mags[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  float m = mags[c & 7u];
+  return (c & 8u) ? -m : m;
+}
+
+// value already divided by the block scale -> 4-bit code, nearest-even, saturating at 6
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  uint32_t s = (__float_as_uint(v) >> 28) & 0x8u;
+  float a = fabsf(v);
+  uint32_t c;
+  // thresholds between neighbours; at an exact midpoint the even code wins
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  if (a != a) c = 7;  // NaN input: saturate (MX fp4 has no NaN)
+  return s | c;
+}
+
+// ---------------------------------------------------------------------- RoPE angles
+
+// (cos, sin) of pos * base^(-2j/R), argument formed and reduced mod 2*pi in fp64 so
+// that positions near 2^20 keep full fp32 accuracy.
+__device__ __forceinline__ void rope_cs(double pos, int j, int R, double log2_base, float* c,
+                                        float* s) {
+  double theta = exp2(-2.0 * static_cast<double>(j) / static_cast<double>(R) * log2_base);
+  double ang = pos * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  double k = rint(ang * (1.0 / two_pi));
+  double red = fma(-k, two_pi, ang);
+  float fr = static_cast<float>(red);
+  float ss, cc;
+  sincosf(fr, &ss, &cc);
+  *c = cc;
+  *s = ss;
+}
+
+// ------------------------------------------------------------------ wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T ceil_div(T a, T b) {
+  return (a + b - 1) / b;
+}
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key;
+// -0 and +0 map to the same key).  Non-finite inputs (inf, NaN) map to 0, which no
+// finite value reaches.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace csa

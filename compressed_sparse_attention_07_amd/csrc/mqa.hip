@@ -1,0 +1,694 @@
+// K4: shared-KV multi-query attention over (selected or all visible) compressed
+// entries plus the raw sliding window, with attention sink and partial / inverse
+// RoPE.  [V4-CN] "DeepSeek-V4中文翻译" §2.3.1 (shared-KV MQA: an entry is both key
+// and value of every head), §2.3.2 (HCA: dense over all compressed entries),
+// §2.3.3 (window branch, sink logit added to the softmax denominator, RoPE on the
+// last 64 dims and the output rotated back by the query position); [NOTES]
+// csa()/hca() sketches: one attention over concat(entries, window).
+//
+// MFMA path (bf16 queries, bf16 or FP8-mixed cache): a workgroup owns one query
+// token, a group of heads (16 per wave) and a range of key slots.  Key tiles of 32
+// rows are gathered into LDS twice: row-major (A operand of S^T = K Q^T) and
+// transposed (A operand of O^T = V^T P^T).  Computing the transposed products
+// makes every lane hold one head's column in both results, so the online-softmax
+// rescale is one factor per lane and P^T feeds the PV product straight from the
+// S^T registers (the contraction order over the tile's keys is permuted to match
+// the lanes' own keys).  FP8-mixed entries are staged as exact bf16 codes and the
+// per-entry scale is applied to the logits and to P (non-RoPE dims only).  With
+// several key ranges per token, partial (max, sum, O) go to the workspace and a
+// combine kernel merges them in fixed split order, so results do not depend on
+// scheduling or batch composition.
+#include "device_common.h"
+#include "launch.h"
+
+namespace csa {
+
+namespace {
+
+struct AttnArgs {
+  const void* q;
+  const int64_t* q_pos;
+  const void* kv;
+  const uint16_t* kv_rope;
+  const float* kv_scale;
+  int64_t kv_rows;
+  const void* win;
+  const uint16_t* win_rope;
+  const float* win_scale;
+  const int64_t* win_pos0;
+  int64_t Tw;
+  const int32_t* idx;
+  int K, ratio, sparse;
+  const float* sink;
+  float scale;
+  int R;
+  double log2_base;
+  int64_t pos_offset;
+  int64_t B, Tq, N;
+  int H, D, n_win;
+  int hpw, nsplit, sps;
+  void* out;
+  int out_dtype;
+  float* part_o;   // [tokens, H, nsplit, D]
+  float2* part_ml; // [tokens, H, nsplit]
+};
+
+struct Slots {
+  int64_t b, p, nsel, wstart, nslots;
+};
+
+__device__ __forceinline__ Slots token_slots(const AttnArgs& a, int64_t bt) {
+  Slots s;
+  s.b = bt / a.Tq;
+  s.p = a.q_pos[bt];
+  if (a.sparse) {
+    s.nsel = a.K;
+  } else {
+    int64_t v = s.p / a.ratio;
+    s.nsel = v > a.N ? a.N : (v < 0 ? 0 : v);
+  }
+  s.wstart = s.p - a.n_win + 1 > 0 ? s.p - a.n_win + 1 : 0;
+  s.nslots = s.nsel + (s.p - s.wstart + 1);
+  return s;
+}
+
+// Source row of slot `slot`: returns entry row (>= 0) in kv, or window row in win
+// (is_win), or -1 if the slot is empty.
+__device__ __forceinline__ int64_t slot_row(const AttnArgs& a, const Slots& s, int64_t bt, int64_t slot,
+                                            bool* is_win, int64_t* wpos) {
+  if (slot < s.nsel) {
+    *is_win = false;
+    int64_t e = a.sparse ? static_cast<int64_t>(a.idx[bt * a.K + slot]) : slot;
+    return e >= 0 ? s.b * a.kv_rows + e : -1;
+  }
+  *is_win = true;
+  const int64_t pw = s.wstart + (slot - s.nsel);
+  *wpos = pw;
+  return s.b * a.Tw + (pw - a.win_pos0[s.b]);
+}
+
+// ================================================================ MFMA path
+
+constexpr int kKT = 32;   // keys per tile
+constexpr int kVP = 36;   // pitch (bf16) of the transposed tile
+
+// At D = 512 a wave needs ~300 registers (16 heads x 512 fp32 accumulators plus
+// the queries), so those workgroups are capped at 4 waves (one per SIMD).
+template <int D>
+constexpr int mfma_max_threads() { return D >= 512 ? 256 : 512; }
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int KP = D + 8;       // row-major pitch (bf16): 16-byte rows, conflict-free reads
+  constexpr int NS = D / 32;      // k-steps of the QK product
+  constexpr int NDB = D / 16;     // 16-row blocks of the PV product
+  __shared__ __attribute__((aligned(16))) uint16_t Krow[kKT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kVP];
+  __shared__ float kscale[kKT];
+  __shared__ int kvalid[kKT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int nthreads = blockDim.x;
+
+  const int n_hg = a.H / a.hpw;
+  int64_t blk = blockIdx.x;
+  const int hg = static_cast<int>(blk % n_hg);
+  blk /= n_hg;
+  const int sp = static_cast<int>(blk % a.nsplit);
+  const int64_t bt = blk / a.nsplit;
+  const Slots S = token_slots(a, bt);
+  const int64_t s_lo = static_cast<int64_t>(sp) * a.sps;
+  const int64_t s_hi = min(S.nslots, s_lo + a.sps);
+  const int h = hg * a.hpw + wid * 16 + col;  // head of this lane's result column
+  const int nope = D - a.R;
+  const double qpos = static_cast<double>(S.p + a.pos_offset);
+
+  // (cos, sin) of the query position for every RoPE pair, shared by the query
+  // rotation and the inverse rotation of the output
+  __shared__ float2 qcs[64];
+  for (int j = tid; j < a.R / 2; j += nthreads) {
+    float c, sn;
+    rope_cs(qpos, j, a.R, a.log2_base, &c, &sn);
+    qcs[j] = make_float2(c, sn);
+  }
+  __syncthreads();
+
+  // queries (B operand of S^T = K Q^T): q[h][32s + 8grp .. +8], RoPE'd at the query position
+  bf16x8 qreg[NS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (bt * a.H + h) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int d0 = 32 * s + 8 * grp;
+      uint4 raw = *reinterpret_cast<const uint4*>(qp + d0);
+      if (d0 + 8 > nope) {
+        float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
+                      bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          if (d0 + e >= nope) {
+            const float2 cs = qcs[(d0 + e - nope) / 2];
+            const float x0 = v[e], x1 = v[e + 1];
+            v[e] = x0 * cs.x - x1 * cs.y;
+            v[e + 1] = x0 * cs.y + x1 * cs.x;
+          }
+        }
+        raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7]));
+      }
+      qreg[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int64_t s0 = s_lo; s0 < s_hi; s0 += kKT) {
+    // ---- gather 32 key rows into LDS (row-major), dequantize, rope window rows
+    constexpr int CH = D / 8;
+    for (int i = tid; i < kKT * CH; i += nthreads) {
+      const int j = i / CH;
+      const int c = i % CH;
+      const int d0 = 8 * c;
+      const int64_t slot = s0 + j;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      float sc = 1.f;
+      bool valid = false;
+      if (slot < s_hi) {
+        bool is_win = false;
+        int64_t wpos = 0;
+        const int64_t row = slot_row(a, S, bt, slot, &is_win, &wpos);
+        if (row >= 0) {
+          valid = true;
+          const void* base = is_win ? a.win : a.kv;
+          if (FP8) {
+            const uint16_t* rp = is_win ? a.win_rope : a.kv_rope;
+            const float* sp_ = is_win ? a.win_scale : a.kv_scale;
+            sc = sp_[row];
+            if (d0 < nope) {
+              uint2 cd = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + row * nope + d0);
+              val.x = e4m3_to_bf16(cd.x & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.x >> 8) & 0xff)) << 16);
+              val.y = e4m3_to_bf16((cd.x >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.x >> 24)) << 16);
+              val.z = e4m3_to_bf16(cd.y & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.y >> 8) & 0xff)) << 16);
+              val.w = e4m3_to_bf16((cd.y >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.y >> 24)) << 16);
+            } else {
+              val = *reinterpret_cast<const uint4*>(rp + row * a.R + (d0 - nope));
+            }
+          } else {
+            val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D + d0);
+          }
+          if (is_win && d0 + 8 > nope) {
+            float v[8] = {bf16lo(val.x), bf16hi(val.x), bf16lo(val.y), bf16hi(val.y),
+                          bf16lo(val.z), bf16hi(val.z), bf16lo(val.w), bf16hi(val.w)};
+            const double kp = static_cast<double>(wpos + a.pos_offset);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              if (d0 + e >= nope) {
+                float cc, sn;
+                rope_cs(kp, (d0 + e - nope) / 2, a.R, a.log2_base, &cc, &sn);
+                const float x0 = v[e], x1 = v[e + 1];
+                v[e] = x0 * cc - x1 * sn;
+                v[e + 1] = x0 * sn + x1 * cc;
+              }
+            }
+            val = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7]));
+          }
+        }
+      }
+      *reinterpret_cast<uint4*>(&Krow[j * KP + d0]) = val;
+      if (c == 0) {
+        kscale[j] = sc;
+        kvalid[j] = valid ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    // ---- transposed copy: Vt[d][j] (pairs of keys packed in one dword)
+    for (int i = tid; i < D * (kKT / 2); i += nthreads) {
+      const int d = i % D;
+      const int jp = i / D;
+      const uint32_t lo = Krow[(2 * jp) * KP + d];
+      const uint32_t hi = Krow[(2 * jp + 1) * KP + d];
+      *reinterpret_cast<uint32_t*>(&Vt[d * kVP + 2 * jp]) = lo | (hi << 16);
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
+    f32x4 sacc[2], racc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      racc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kr = &Krow[(16 * kb + col) * KP + 8 * grp];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
+        if (FP8 && 32 * s >= nope)
+          racc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[s], racc[kb], 0, 0, 0);
+        else
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+      }
+    }
+    // ---- online softmax for head h over this lane's 8 keys (16kb + 4grp + r)
+    float z[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * kb + 4 * grp + r;
+        float v = FP8 ? fmaf(kscale[j], sacc[kb][r], racc[kb][r]) : sacc[kb][r];
+        v = kvalid[j] ? a.scale * v : -INFINITY;
+        z[kb][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    const float m_new = fmaxf(m_run, mt);
+    const bool none = (m_new == -INFINITY);
+    const float alpha = none ? 1.f : __expf(m_run - m_new);
+    float pn[8], pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = none ? 0.f : __expf(z[kb][r] - m_new);
+        psum += p;
+        pr[4 * kb + r] = p;
+        pn[4 * kb + r] = FP8 ? p * kscale[16 * kb + 4 * grp + r] : p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const bf16x8 pB = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3]), pack_bf16x2(pn[4], pn[5]),
+                           pack_bf16x2(pn[6], pn[7])));
+    bf16x8 pR = pB;
+    if (FP8)
+      pR = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
+                             pack_bf16x2(pr[6], pr[7])));
+    // ---- O^T += V^T P^T: A operand rows d = 16db + col, keys (4grp..+3) and (16+4grp..+3)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      acc[db] *= alpha;
+      const uint16_t* vr = &Vt[(16 * db + col) * kVP + 4 * grp];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, (FP8 && 16 * db >= nope) ? pR : pB, acc[db], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // sum of exponentials for head h: the four row groups hold disjoint keys
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, WAVE);
+  l_tot += __shfl_xor(l_tot, 32, WAVE);
+
+  const int64_t th = bt * a.H + h;
+  if (a.nsplit > 1) {
+    float* po = a.part_o + (th * a.nsplit + sp) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<float4*>(po + 16 * db + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    if (grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
+    return;
+  }
+  // ---- finalize: sink, normalise, inverse RoPE, store bf16
+  const float sk = a.sink[h];
+  float inv;
+  if (sk == INFINITY) inv = 0.f;
+  else if (sk == -INFINITY) inv = 1.f / l_tot;
+  else inv = 1.f / (l_tot + __expf(sk - m_run));
+  uint16_t* op = static_cast<uint16_t*>(a.out) + th * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d0 = 16 * db + 4 * grp;
+    float v[4] = {acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv};
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      if (d0 + e >= nope) {
+        // rotate back by the query position: angle -> -angle
+        const float2 cs = qcs[(d0 + e - nope) / 2];
+        const float x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * cs.x + x1 * cs.y;
+        v[e + 1] = x1 * cs.x - x0 * cs.y;
+      }
+    }
+    *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
+// Merge the split partials of every (token, head) in split order.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int per = a.D / 4;
+  const int64_t th = gid / per;
+  if (th >= a.B * a.Tq * a.H) return;
+  const int d0 = static_cast<int>(gid % per) * 4;
+  const int h = static_cast<int>(th % a.H);
+  const int64_t bt = th / a.H;
+  const float2* ml = a.part_ml + th * a.nsplit;
+  float M = -INFINITY;
+  for (int i = 0; i < a.nsplit; ++i) M = fmaxf(M, ml[i].x);
+  float L = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < a.nsplit; ++i) {
+    const float2 v = ml[i];
+    if (v.x == -INFINITY) continue;
+    const float w = __expf(v.x - M);
+    L += w * v.y;
+    const float4 po = *reinterpret_cast<const float4*>(a.part_o + (th * a.nsplit + i) * a.D + d0);
+    o[0] += w * po.x; o[1] += w * po.y; o[2] += w * po.z; o[3] += w * po.w;
+  }
+  const float sk = a.sink[h];
+  float inv;
+  if (sk == INFINITY) inv = 0.f;
+  else if (sk == -INFINITY) inv = 1.f / L;
+  else inv = 1.f / (L + __expf(sk - M));
+  float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  const int nope = a.D - a.R;
+  const int64_t p = a.q_pos[bt];
+  if (d0 + 4 > nope) {
+    const double qpos = static_cast<double>(p + a.pos_offset);
+    for (int e = 0; e < 4; e += 2) {
+      if (d0 + e >= nope) {
+        float c, sn;
+        rope_cs(-qpos, (d0 + e - nope) / 2, a.R, a.log2_base, &c, &sn);
+        const float x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * c - x1 * sn;
+        v[e + 1] = x0 * sn + x1 * c;
+      }
+    }
+  }
+  if (a.out_dtype == CSA_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + th * a.D + d0) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + th * a.D + d0) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
+// ================================================================ SIMT path
+
+constexpr int kSimtThreads = 256;
+constexpr int kSimtHeads = 8;        // heads per workgroup, 32 lanes each
+constexpr int kSimtLDS = 8192;       // floats of staged keys
+constexpr int kSimtDPT = 32;         // max dims per lane (D <= 1024)
+
+template <int KVF>
+__device__ __forceinline__ float kv_elem(const AttnArgs& a, bool is_win, int64_t row, int d) {
+  const void* base = is_win ? a.win : a.kv;
+  if (KVF == CSA_F32) return static_cast<const float*>(base)[row * a.D + d];
+  if (KVF == CSA_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[row * a.D + d]);
+  const int nope = a.D - a.R;
+  if (d < nope) {
+    const float* sc = is_win ? a.win_scale : a.kv_scale;
+    return e4m3_to_f32(static_cast<const uint8_t*>(base)[row * nope + d]) * sc[row];
+  }
+  const uint16_t* rp = is_win ? a.win_rope : a.kv_rope;
+  return bf16_to_f32(rp[row * a.R + (d - nope)]);
+}
+
+template <typename TQ, int KVF>
+__global__ __launch_bounds__(kSimtThreads) void attn_simt_kernel(AttnArgs a) {
+  __shared__ float kt[kSimtLDS];
+  __shared__ int kvalid[kSimtLDS];
+  const int D = a.D;
+  const int KT = kSimtLDS / D;
+  const int tid = threadIdx.x;
+  const int hl = tid >> 5;       // head within group
+  const int i = tid & 31;        // lane within head
+  const int n_hg = (a.H + kSimtHeads - 1) / kSimtHeads;
+  const int hg = static_cast<int>(blockIdx.x % n_hg);
+  const int64_t bt = blockIdx.x / n_hg;
+  const int h = hg * kSimtHeads + hl;
+  const bool hok = h < a.H;
+  const Slots S = token_slots(a, bt);
+  const int nope = D - a.R;
+  const double qpos = static_cast<double>(S.p + a.pos_offset);
+
+  float q[kSimtDPT], acc[kSimtDPT];
+  const TQ* qp = static_cast<const TQ*>(a.q) + (bt * a.H + (hok ? h : 0)) * D;
+  auto ldq = [&](int d) -> float {
+    if constexpr (sizeof(TQ) == 4) return reinterpret_cast<const float*>(qp)[d];
+    else return bf16_to_f32(reinterpret_cast<const uint16_t*>(qp)[d]);
+  };
+#pragma unroll
+  for (int u = 0; u < kSimtDPT; ++u) {
+    const int d = i + 32 * u;
+    q[u] = 0.f;
+    acc[u] = 0.f;
+    if (d < D) {
+      float x = ldq(d);
+      if (d >= nope) {
+        float c, sn;
+        rope_cs(qpos, (d - nope) / 2, a.R, a.log2_base, &c, &sn);
+        const float xp = ldq(d ^ 1);
+        x = (d & 1) ? fmaf(xp, sn, x * c) : fmaf(-xp, sn, x * c);
+      }
+      q[u] = x;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int64_t s0 = 0; s0 < S.nslots; s0 += KT) {
+    __syncthreads();
+    for (int e = tid; e < KT * D; e += kSimtThreads) {
+      const int j = e / D;
+      const int d = e % D;
+      const int64_t slot = s0 + j;
+      float v = 0.f;
+      int ok = 0;
+      if (slot < S.nslots) {
+        bool is_win = false;
+        int64_t wpos = 0;
+        const int64_t row = slot_row(a, S, bt, slot, &is_win, &wpos);
+        if (row >= 0) {
+          ok = 1;
+          v = kv_elem<KVF>(a, is_win, row, d);
+          if (is_win && d >= nope) {
+            float c, sn;
+            rope_cs(static_cast<double>(wpos + a.pos_offset), (d - nope) / 2, a.R, a.log2_base, &c, &sn);
+            const float vp = kv_elem<KVF>(a, is_win, row, d ^ 1);
+            v = (d & 1) ? fmaf(vp, sn, v * c) : fmaf(-vp, sn, v * c);
+          }
+        }
+      }
+      kt[e] = v;
+      if (d == 0) kvalid[j] = ok;
+    }
+    __syncthreads();
+    const int nk = static_cast<int>(min(static_cast<int64_t>(KT), S.nslots - s0));
+    for (int j = 0; j < nk; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int u = 0; u < kSimtDPT; ++u) {
+        const int d = i + 32 * u;
+        if (d < D) part = fmaf(q[u], kt[j * D + d], part);
+      }
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) part += __shfl_xor(part, o, 32);
+      if (!kvalid[j]) continue;
+      const float z = a.scale * part;
+      const float m_new = fmaxf(m_run, z);
+      const float alpha = __expf(m_run - m_new);
+      const float p = __expf(z - m_new);
+      l_run = l_run * alpha + p;
+#pragma unroll
+      for (int u = 0; u < kSimtDPT; ++u) {
+        const int d = i + 32 * u;
+        if (d < D) acc[u] = fmaf(p, kt[j * D + d], acc[u] * alpha);
+      }
+      m_run = m_new;
+    }
+  }
+  if (!hok) return;
+  const float sk = a.sink[h];
+  float inv;
+  if (sk == INFINITY) inv = 0.f;
+  else if (sk == -INFINITY) inv = 1.f / l_run;
+  else inv = 1.f / (l_run + __expf(sk - m_run));
+  TQ* op = static_cast<TQ*>(a.out) + (bt * a.H + h) * D;
+#pragma unroll
+  for (int u = 0; u < kSimtDPT; ++u) {
+    const int d = i + 32 * u;
+    float v = acc[u] * inv;
+    // partner of the RoPE pair lives in lane i^1 (same u)
+    const float vp = __shfl_xor(v, 1, 32);
+    if (d < D) {
+      if (d >= nope) {
+        float c, sn;
+        rope_cs(-qpos, (d - nope) / 2, a.R, a.log2_base, &c, &sn);
+        v = (d & 1) ? fmaf(vp, sn, v * c) : fmaf(-vp, sn, v * c);
+      }
+      if constexpr (sizeof(TQ) == 4) reinterpret_cast<float*>(op)[d] = v;
+      else reinterpret_cast<uint16_t*>(op)[d] = f32_to_bf16(v);
+    }
+  }
+}
+
+// ================================================================ planning
+
+struct Plan {
+  bool mfma;
+  int hpw, nsplit, sps;
+};
+
+// Largest head group (multiple of 16 dividing H) that fits one workgroup.
+int base_hpw(int H, int D) {
+  const int max_hpw = D >= 512 ? 64 : 128;
+  int hpw = H;
+  while (hpw > max_hpw && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) hpw /= 2;
+  return hpw <= max_hpw ? hpw : 0;
+}
+
+Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma) {
+  Plan p{mfma, 0, 1, 0};
+  if (!mfma) return p;
+  const int64_t tokens = B * Tq;
+  int hpw = base_hpw(H, D);
+  int64_t units = tokens * (H / hpw);
+  while (units < 256 && hpw > 32 && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) {
+    hpw /= 2;
+    units *= 2;
+  }
+  int64_t ns = 1;
+  if (units < 256) {
+    ns = (512 + units - 1) / units;
+    const int64_t cap = (max_slots + 63) / 64;
+    if (ns > cap) ns = cap;
+    if (ns < 1) ns = 1;
+  }
+  int64_t sps = ((max_slots + ns - 1) / ns + kKT - 1) / kKT * kKT;
+  if (sps < kKT) sps = kKT;
+  ns = (max_slots + sps - 1) / sps;
+  if (ns < 1) ns = 1;
+  p.hpw = hpw;
+  p.nsplit = static_cast<int>(ns);
+  p.sps = static_cast<int>(sps);
+  return p;
+}
+
+bool mfma_ok(const AttnLaunch& L) {
+  if (L.q.dtype != CSA_BF16) return false;
+  if (L.kv.dtype != CSA_BF16 && L.kv.dtype != CSA_FP8MIX) return false;
+  if (L.win.dtype != L.kv.dtype) return false;
+  if (L.H % 16 != 0) return false;
+  if (L.D != 128 && L.D != 256 && L.D != 512) return false;
+  if (base_hpw(L.H, L.D) == 0) return false;
+  if (L.rope_dims > 128) return false;
+  if (L.kv.dtype == CSA_FP8MIX && ((L.D - L.rope_dims) % 32 != 0)) return false;
+  return true;
+}
+
+int64_t max_slots_of(const AttnLaunch& L) {
+  return (L.sparse ? static_cast<int64_t>(L.K) : L.N) + L.n_win;
+}
+
+AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
+  AttnArgs a{};
+  a.q = L.q.data;
+  a.q_pos = L.q_pos;
+  a.kv = L.kv.data;
+  a.kv_rope = static_cast<const uint16_t*>(L.kv.rope);
+  a.kv_scale = static_cast<const float*>(L.kv.scale);
+  a.kv_rows = L.kv_rows;
+  a.win = L.win.data;
+  a.win_rope = static_cast<const uint16_t*>(L.win.rope);
+  a.win_scale = static_cast<const float*>(L.win.scale);
+  a.win_pos0 = L.win_pos0;
+  a.Tw = L.Tw;
+  a.idx = L.idx;
+  a.K = L.K;
+  a.ratio = L.ratio;
+  a.sparse = L.sparse;
+  a.sink = L.sink;
+  a.scale = L.scale;
+  a.R = L.rope_dims;
+  a.log2_base = L.log2_base;
+  a.pos_offset = L.pos_offset;
+  a.B = L.B;
+  a.Tq = L.Tq;
+  a.N = L.N;
+  a.H = L.H;
+  a.D = L.D;
+  a.n_win = L.n_win;
+  a.hpw = P.hpw;
+  a.nsplit = P.nsplit;
+  a.sps = P.sps;
+  a.out = L.out.data;
+  a.out_dtype = L.out.dtype;
+  if (P.mfma && P.nsplit > 1) {
+    const int64_t th = L.B * L.Tq * L.H;
+    a.part_o = static_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + th * P.nsplit * L.D * sizeof(float));
+  }
+  return a;
+}
+
+}  // namespace
+
+bool attn_uses_mfma(const AttnLaunch& L) { return mfma_ok(L); }
+
+size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma_path) {
+  Plan P = make_plan(B, Tq, H, D, max_slots, mfma_path);
+  if (!P.mfma || P.nsplit <= 1) return 0;
+  const int64_t th = B * Tq * H;
+  return static_cast<size_t>(th * P.nsplit) * (static_cast<size_t>(D) * sizeof(float) + sizeof(float2));
+}
+
+int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int64_t tokens = L.B * L.Tq;
+  if (tokens == 0) return 0;
+  const bool mfma = mfma_ok(L);
+  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma);
+  if (mfma && P.nsplit > 1 && ws_bytes < attn_workspace_bytes(L.B, L.Tq, L.H, L.D, max_slots_of(L), true))
+    return -3;
+  AttnArgs a = make_args(L, P, ws);
+  if (mfma) {
+    const int64_t grid = tokens * (L.H / P.hpw) * P.nsplit;
+    const dim3 block(P.hpw / 16 * WAVE);
+    const bool fp8 = L.kv.dtype == CSA_FP8MIX;
+#define CSA_LAUNCH_MFMA(DD)                                                                              \
+  if (L.D == DD) {                                                                                       \
+    if (fp8) hipLaunchKernelGGL((attn_mfma_kernel<DD, true>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a); \
+    else hipLaunchKernelGGL((attn_mfma_kernel<DD, false>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);    \
+  }
+    CSA_LAUNCH_MFMA(128)
+    CSA_LAUNCH_MFMA(256)
+    CSA_LAUNCH_MFMA(512)
+#undef CSA_LAUNCH_MFMA
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (P.nsplit > 1) {
+      const int64_t threads = tokens * L.H * (L.D / 4);
+      hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>((threads + 255) / 256)), dim3(256), 0,
+                         stream, a);
+      if (hipGetLastError() != hipSuccess) return -1;
+    }
+    return 0;
+  }
+  const int n_hg = (L.H + kSimtHeads - 1) / kSimtHeads;
+  const dim3 grid(static_cast<uint32_t>(tokens * n_hg));
+  const bool qf32 = L.q.dtype == CSA_F32;
+#define CSA_LAUNCH_SIMT(KVF)                                                                                \
+  if (L.kv.dtype == KVF) {                                                                                  \
+    if (qf32) hipLaunchKernelGGL((attn_simt_kernel<float, KVF>), grid, dim3(kSimtThreads), 0, stream, a);   \
+    else hipLaunchKernelGGL((attn_simt_kernel<uint16_t, KVF>), grid, dim3(kSimtThreads), 0, stream, a);     \
+  }
+  CSA_LAUNCH_SIMT(CSA_F32)
+  CSA_LAUNCH_SIMT(CSA_BF16)
+  CSA_LAUNCH_SIMT(CSA_FP8MIX)
+#undef CSA_LAUNCH_SIMT
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa

@@ -1,0 +1,273 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) CSA / HCA attention library (libcsa.so).
+ *
+ * The library computes one forward pass of the DeepSeek-V4 hybrid attention layer
+ * as the report defines it (cited by page title and section):
+ *
+ *   [V4-CN]  "DeepSeek-V4中文翻译（翻译模型：Opus4.7）" (blog.uika.cn), report §2.3.1-§2.3.4,
+ *            §3.4, §3.6.1;
+ *   [NOTES]  "DeepSeek-V4：把百万 token 上下文从额度变成架构问题"
+ *            (awesome.papernotes.org), "关键设计 1" and "关键设计 2".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a DEVICE pointer owned by the caller: dense,
+ *   row-major, last dimension contiguous, in the shape written beside it.  The
+ *   library never allocates device memory; scratch comes from a caller workspace
+ *   whose size the matching *_workspace_size() query returns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *   call only ENQUEUES work on it and returns; results are valid after the stream
+ *   is synchronised.  Calls are re-entrant; two calls that share output or
+ *   workspace buffers must be ordered by the caller (same stream).
+ * - Errors: all arguments are validated on the host before anything is launched.
+ *   On error the call returns a non-zero csa_status, launches nothing and leaves
+ *   outputs untouched; csa_last_error() then returns a message (thread-local,
+ *   valid until the next call on that thread).  No C++ exception crosses the ABI.
+ *   CSA_ERR_DEVICE means no gfx950 device is current or a launch failed.
+ * - Device-resident data (indices, positions) is NOT validated: entry indices must
+ *   lie in [0, N) or be -1, positions must be >= 0, and the raw window buffer must
+ *   cover every window position a query needs.  Violations are undefined.
+ * - Positions are absolute token indices from the start of the sequence.  A
+ *   compressed entry i covers tokens [ratio*i, ratio*(i+1)) and carries RoPE
+ *   position ratio*i.  `pos_offset` is added to every RoPE position and to nothing
+ *   else (block visibility and windows use the plain positions).
+ * - RoPE ([V4-CN] §2.3.3) rotates the last `rope_dims` dims in adjacent pairs
+ *   (D-R+2j, D-R+2j+1) by angle pos * rope_base^(-2j/R); rope_dims is even and
+ *   D - rope_dims is even.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  CSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of the supported range  */
+  CSA_ERR_DTYPE = 3,       /* dtype (combination) not supported by this call    */
+  CSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
+  CSA_ERR_DEVICE = 5,      /* no gfx950 device current, or a launch failed      */
+  CSA_ERR_UNSUPPORTED = 6  /* valid request this build does not implement       */
+} csa_status;
+
+/*
+ * Storage formats of a csa_buf ([V4-CN] §2.3.4 and §3.4):
+ *   CSA_F32    data = float [rows, D]
+ *   CSA_BF16   data = bf16  [rows, D]  (raw 16-bit patterns)
+ *   CSA_FP8MIX data  = uint8 e4m3 (OCP, max 448) [rows, D-R]  -- the non-RoPE dims
+ *              rope  = bf16 [rows, R]                         -- the RoPE dims
+ *              scale = float [rows]; value = e4m3(code) * scale for the first D-R dims
+ *   CSA_MXFP4  data  = uint8 [rows, D/2], two e2m1 codes per byte, element 2j in
+ *                      the low nibble; D % 32 == 0
+ *              scale = uint8 e8m0 [rows, D/32]; value = e2m1 * 2^(code-127) per 32
+ *                      contiguous elements
+ */
+typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8MIX = 2, CSA_MXFP4 = 3 } csa_dtype;
+
+typedef struct csa_buf {
+  void* data;
+  void* rope;   /* FP8MIX only */
+  void* scale;  /* FP8MIX, MXFP4 */
+  int32_t dtype;
+  int32_t reserved;
+} csa_buf;
+
+int csa_abi_version(void);
+const char* csa_last_error(void);
+/* CSA_OK iff the current HIP device is a gfx950 GPU. */
+csa_status csa_device_check(void);
+
+/*
+ * csa_compress -- softmax-weighted KV compression ([V4-CN] §2.3.1 compression
+ * equations for CSA, §2.3.2 for HCA; [NOTES] "关键设计 1": weights are per channel).
+ *
+ * For every entry i with t0/ratio <= i < (t0+T)/ratio of every sequence b and every
+ * channel d, the logits of the positions are
+ *     overlap=1 (CSA):  Z^a[ratio*i + j, d] + bias_a[j, d]              j < ratio
+ *                       Z^b[ratio*(i-1) + j, d] + bias_b[j, d]          j < ratio, i >= 1
+ *     overlap=0 (HCA):  Z^a[ratio*i + j, d] + bias_a[j, d]              j < ratio
+ * they are soft-maxed across the positions (per channel), and the entry is the
+ * weighted sum of the matching C^a / C^b rows.  Entry 0 has no previous block.
+ * The last rope_dims dims are then rotated to position pos_offset + ratio*i.
+ *
+ *   ca, za           [B, T, D]  rows of tokens t0 .. t0+T-1 (C^a, Z^a; for HCA: C, Z)
+ *   cb, zb           [B, T, D]  b-branch rows (overlap=1 only; NULL for overlap=0)
+ *   in_dtype         CSA_F32 or CSA_BF16 (all four streams and prev_* share it)
+ *   bias_a, bias_b   float [ratio, D] or NULL (= 0)
+ *   prev_cb, prev_zb [B, ratio, D] the b-branch rows of tokens t0-ratio .. t0-1;
+ *                    required iff overlap=1 and t0 > 0, else ignored
+ *   T                multiple of ratio (T = 0 is a no-op); t0 multiple of ratio
+ *   out              [B, out_rows, D] in F32, BF16, FP8MIX (R = rope_dims) or
+ *                    MXFP4 (D % 32 == 0); entry i is written to row i of its sequence,
+ *                    so (t0+T)/ratio <= out_rows.  Other rows are untouched.
+ * Limits: 1 <= ratio <= 1024, 2 <= D <= 2048, D % 8 == 0.
+ */
+csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb,
+                        int32_t in_dtype, const float* bias_a, const float* bias_b,
+                        const void* prev_cb, const void* prev_zb, int64_t B, int64_t T,
+                        int32_t D, int32_t ratio, int32_t overlap, int64_t t0,
+                        int32_t rope_dims, float rope_base, int64_t pos_offset,
+                        const csa_buf* out, int64_t out_rows, void* stream);
+
+/*
+ * csa_quantize -- store fp32 rows [rows, D] in another storage format
+ * (CSA_BF16, CSA_FP8MIX with R = rope_dims, CSA_MXFP4).  Rounding: nearest-even;
+ * fp8 saturates at +-448; FP8MIX scale = amax(|non-RoPE dims|)/448 in fp32 (1 for an
+ * all-zero entry), codes = e4m3(x / scale); MXFP4 block exponent
+ * X = floor(log2(amax)) - 2 (OCP MX), codes = e2m1(x / 2^X), saturating at 6.
+ * ([V4-CN] §2.3.4 mixed FP8/BF16 KV storage; §3.4 FP4 indexer QK path.)
+ */
+csa_status csa_quantize(const float* x, int64_t rows, int32_t D, int32_t rope_dims,
+                        const csa_buf* out, void* stream);
+
+/*
+ * csa_index_scores -- lightning indexer ([V4-CN] §2.3.1 index-score equation):
+ *     scores[b,t,s] = sum_h wI[b,t,h] * max(0, qI[b,t,h,:] . kI[b,s,:])
+ * for s < floor(q_pos[b,t] / ratio) (a query sees only earlier compressed blocks,
+ * [V4-CN] §2.3.3), and -inf for the other s < N.
+ *
+ *   qI      [B, Tq, HI, DI]  F32, BF16 or MXFP4 (same dtype as kI)
+ *   wI      float [B, Tq, HI]
+ *   kI      [B, kI_rows, DI] compressed indexer keys; the first N rows are used
+ *   q_pos   int64 [B, Tq]
+ *   scores  float [B, Tq, N]
+ * Limits: HI <= 128, DI <= 512, DI % 8 == 0 (MXFP4: DI % 32 == 0).
+ */
+csa_status csa_index_scores(const csa_buf* qI, const float* wI, const csa_buf* kI,
+                            const int64_t* q_pos, int64_t B, int64_t Tq, int32_t HI,
+                            int32_t DI, int64_t N, int64_t kI_rows, int32_t ratio,
+                            float* scores, void* stream);
+
+/*
+ * csa_topk -- top-k selector ([V4-CN] §2.3.1; [NOTES] C_t = TopK_k(I_t,:)).
+ * For each row of scores [rows, N] selects the min(k, #finite) largest finite
+ * scores; equal scores are taken in increasing index order; -inf / NaN are never
+ * selected.  idx [rows, k] receives the selected indices in ascending order,
+ * padded with -1; count [rows] (optional, may be NULL) the number selected.
+ * Limits: 1 <= k <= 4096, N < 2^31.
+ */
+size_t csa_topk_workspace_size(int64_t rows, int64_t N, int32_t k);
+csa_status csa_topk(const float* scores, int64_t rows, int64_t N, int32_t k, int32_t* idx,
+                    int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_sparse_mqa -- shared-KV multi-query attention over the selected compressed
+ * entries plus the raw sliding window ([V4-CN] §2.3.1 shared-KV MQA: each entry is
+ * both key and value for all heads; §2.3.3 window branch, attention sink, partial
+ * and inverse RoPE; [NOTES] csa() sketch: one attention over concat(selected, window)).
+ *
+ * For query t of sequence b (position p = q_pos[b,t]) the keys are
+ *     kv[b, idx[b,t,j]]                     for the K slots with idx >= 0
+ *     RoPE(win[b, r - win_pos0[b]], r)      for r = max(0, p-n_win+1) .. p
+ * and for every head h
+ *     z_j   = softmax_scale * RoPE(q[b,t,h], p) . key_j
+ *     o     = sum_j exp(z_j) key_j / (sum_j exp(z_j) + exp(sink[h]))
+ *     out   = RoPE(o, -p)
+ * (sink = -inf removes the sink term; +inf gives 0).
+ *
+ *   q       [B, Tq, H, D]  F32 or BF16, not roped;  out: same shape and dtype
+ *   kv      [B, kv_rows, D] compressed entries (already roped), F32/BF16/FP8MIX
+ *   idx     int32 [B, Tq, K]
+ *   win     [B, Tw, D] raw (un-roped) entries of positions win_pos0[b] ..; same
+ *           dtype as kv
+ *   sink    float [H]
+ * Limits: D <= 1024; H <= 256; K + n_win <= 2^20.  The MFMA path needs a BF16 or
+ * FP8MIX cache, BF16 q, H % 16 == 0 and D % 32 == 0; other combinations run a
+ * slower SIMT kernel.
+ */
+size_t csa_sparse_mqa_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t D, int32_t K,
+                                     int32_t n_win);
+csa_status csa_sparse_mqa(const csa_buf* q, const int64_t* q_pos, const csa_buf* kv,
+                          int64_t kv_rows, const int32_t* idx, int32_t K, const csa_buf* win,
+                          const int64_t* win_pos0, int64_t Tw, const float* sink,
+                          float softmax_scale, int32_t rope_dims, float rope_base,
+                          int64_t pos_offset, int64_t B, int64_t Tq, int32_t H, int32_t D,
+                          int64_t N, int32_t n_win, const csa_buf* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * hca_dense_attn -- HCA core attention ([V4-CN] §2.3.2; [NOTES] hca() sketch):
+ * as csa_sparse_mqa, with the compressed keys being every entry i < min(N,
+ * floor(p / ratio)) instead of an index list.
+ */
+size_t hca_dense_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t D, int64_t N,
+                                     int32_t n_win);
+csa_status hca_dense_attn(const csa_buf* q, const int64_t* q_pos, const csa_buf* kv,
+                          int64_t kv_rows, int32_t ratio, const csa_buf* win,
+                          const int64_t* win_pos0, int64_t Tw, const float* sink,
+                          float softmax_scale, int32_t rope_dims, float rope_base,
+                          int64_t pos_offset, int64_t B, int64_t Tq, int32_t H, int32_t D,
+                          int64_t N, int32_t n_win, const csa_buf* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * csa_forward -- one layer forward (prefill chunk or decode step):
+ *   mode CSA: compress the T new tokens of the KV streams and of the indexer-key
+ *             streams into the caches (entries t0/m .. (t0+T)/m - 1), score every
+ *             query against the N = (t0+T)/m entries, select top-k, attend;
+ *   mode HCA: compress with ratio m', attend densely.
+ * ([NOTES] csa()/hca() sketches; [V4-CN] §2.3.1-§2.3.3.)
+ */
+typedef enum csa_mode { CSA_MODE_CSA = 0, CSA_MODE_HCA = 1 } csa_mode;
+
+typedef struct csa_layer_desc {
+  int32_t struct_size;   /* sizeof(csa_layer_desc) */
+  int32_t mode;          /* csa_mode */
+  int64_t B;             /* sequences */
+  int64_t T;             /* new tokens to compress (multiple of ratio, may be 0) */
+  int64_t t0;            /* absolute index of the first new token (multiple of ratio) */
+  int64_t Tq;            /* query tokens per sequence */
+  int64_t cache_rows;    /* rows of kv_cache / ik_cache per sequence */
+  int64_t Tw;            /* rows of the raw window buffer per sequence */
+  int32_t D;             /* KV / head dim */
+  int32_t H;             /* query heads */
+  int32_t HI, DI;        /* indexer heads and dim (CSA) */
+  int32_t ratio;         /* m (CSA) or m' (HCA) */
+  int32_t topk;          /* k (CSA) */
+  int32_t n_win;         /* sliding window */
+  int32_t rope_dims;
+  float rope_base;
+  float softmax_scale;
+  int64_t pos_offset;
+  int32_t stream_dtype;  /* C/Z streams: F32 or BF16 */
+  int32_t pad0;
+} csa_layer_desc;
+
+typedef struct csa_forward_io {
+  /* KV streams of the new tokens [B, T, D] (HCA: ca = C, za = Z; cb, zb unused) */
+  const void *ca, *cb, *za, *zb;
+  const float *bias_a, *bias_b;          /* [ratio, D] or NULL */
+  const void *prev_cb, *prev_zb;         /* [B, ratio, D], CSA with t0 > 0 */
+  /* indexer-key streams of the new tokens [B, T, DI] (CSA) */
+  const void *ica, *icb, *iza, *izb;
+  const float *ibias_a, *ibias_b;
+  const void *iprev_cb, *iprev_zb;
+  csa_buf kv_cache;                      /* [B, cache_rows, D]  in/out */
+  csa_buf ik_cache;                      /* [B, cache_rows, DI] in/out (CSA) */
+  csa_buf q;                             /* [B, Tq, H, D] */
+  const int64_t* q_pos;                  /* [B, Tq] */
+  csa_buf qI;                            /* [B, Tq, HI, DI] (CSA) */
+  const float* wI;                       /* [B, Tq, HI] (CSA) */
+  csa_buf win;                           /* [B, Tw, D] raw */
+  const int64_t* win_pos0;               /* [B] */
+  const float* sink;                     /* [H] */
+  csa_buf out;                           /* [B, Tq, H, D] */
+  float* scores_out;                     /* optional [B, Tq, N] copy of the index scores */
+  int32_t* idx_out;                      /* optional [B, Tq, topk] selected entries */
+} csa_forward_io;
+
+size_t csa_forward_workspace_size(const csa_layer_desc* L);
+csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* ws,
+                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

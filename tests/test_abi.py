@@ -1,0 +1,123 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host (before any device work); with no GPU the
+device check fails cleanly.  No compute call is made."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_built
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "csa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(csa_\w+|hca_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ensure_built()
+
+
+def test_every_declared_symbol_is_exported(L):
+    from compressed_sparse_attention_07_amd import EXPORTS
+    declared = _declared_symbols()
+    assert set(declared) == set(EXPORTS), (declared, EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version(L):
+    assert L.csa_abi_version() == 1
+
+
+def _buf(dtype=1, data=0x100000):
+    from compressed_sparse_attention_07_amd._lib import csa_buf
+    return csa_buf(data, 0, 0, dtype, 0)
+
+
+def test_compress_rejects_bad_arguments(L):
+    out = _buf()
+    p = 0x100000
+    # NULL input
+    st = L.csa_compress(None, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 2, None)
+    assert st == 1 and b"required" in L.csa_last_error()
+    # T not a multiple of ratio
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 9, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 3, None)
+    assert st == 2
+    # odd rope dims
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 3, 10000.0, 0, C.byref(out), 2, None)
+    assert st == 2
+    # t0 > 0 without the previous block
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 4, 0, 10000.0, 0, C.byref(out), 3, None)
+    assert st == 1
+    # unsupported input dtype
+    st = L.csa_compress(p, p, p, p, 2, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 2, None)
+    assert st == 3
+    # output too short
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 1, None)
+    assert st == 2
+    # misaligned pointer
+    st = L.csa_compress(p + 2, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 2, None)
+    assert st == 2
+    # MXFP4 output needs D % 32 == 0 and a scale pointer
+    mx = _buf(3)
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(mx), 2, None)
+    assert st == 1
+
+
+def test_topk_and_index_reject_bad_arguments(L):
+    p = 0x100000
+    assert L.csa_topk(None, 1, 10, 4, p, None, None, 0, None) == 1
+    assert L.csa_topk(p, 1, 10, 0, p, None, None, 0, None) == 2
+    assert L.csa_topk(p, 1, 10, 5000, p, None, None, 0, None) == 2
+    q, k = _buf(1), _buf(0)
+    st = L.csa_index_scores(C.byref(q), p, C.byref(k), p, 1, 1, 4, 32, 8, 8, 4, p, None)
+    assert st == 3  # dtype mismatch
+    k = _buf(1)
+    st = L.csa_index_scores(C.byref(q), p, C.byref(k), p, 1, 1, 4, 30, 8, 8, 4, p, None)
+    assert st == 2  # DI not a multiple of 8
+    st = L.csa_index_scores(C.byref(q), p, C.byref(k), p, 1, 1, 4, 32, 8, 4, 4, p, None)
+    assert st == 2  # kI_rows < N
+
+
+def test_attention_rejects_bad_arguments(L):
+    p = 0x100000
+    q, kv, win, out = _buf(1), _buf(1), _buf(1), _buf(1)
+    args = lambda **o: dict(dict(K=4, n_win=8, H=16, D=128, N=10, kv_rows=10, Tw=16, out=out), **o)
+    def call(**o):
+        a = args(**o)
+        return L.csa_sparse_mqa(C.byref(q), p, C.byref(kv), a["kv_rows"], p, a["K"], C.byref(win), p, a["Tw"], p,
+                                1.0, 64, 10000.0, 0, 1, 1, a["H"], a["D"], a["N"], a["n_win"], C.byref(a["out"]),
+                                None, 0, None)
+    assert call(n_win=0) == 2
+    assert call(kv_rows=5) == 2
+    assert call(D=1030) == 2
+    assert call(out=_buf(0)) == 3          # out dtype differs from q
+    fp8 = _buf(2)                           # FP8MIX without rope/scale pointers
+    assert L.csa_sparse_mqa(C.byref(q), p, C.byref(fp8), 10, p, 4, C.byref(win), p, 16, p, 1.0, 64, 10000.0, 0, 1,
+                            1, 16, 128, 10, 8, C.byref(out), None, 0, None) == 1
+
+
+def test_forward_rejects_bad_descriptor(L):
+    from compressed_sparse_attention_07_amd._lib import csa_forward_io, csa_layer_desc
+    d = csa_layer_desc()
+    d.struct_size = 12
+    io = csa_forward_io()
+    assert L.csa_forward(C.byref(d), C.byref(io), None, 0, None) == 2
+    assert L.csa_forward_workspace_size(C.byref(d)) == 0
+
+
+def test_valid_call_without_gpu_reports_device_error(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert L.csa_device_check() == 5
+    p = 0x100000
+    out = _buf()
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 2, None)
+    assert st == 5 and L.csa_last_error()

@@ -213,7 +213,9 @@ def csa_index_scores(qI, wI, kI, q_pos, scores, *, ratio: int, stream=None) -> N
 
 def csa_topk(scores, k: int, idx, count=None, *, ws=None, stream=None) -> None:
     N = scores.shape[-1]
-    rows = scores.numel() // N if N else scores.numel()
+    rows = 1
+    for d in scores.shape[:-1]:
+        rows *= d
     need = lib().csa_topk_workspace_size(rows, N, k)
     w, wb = _ws(need, scores.device, ws)
     check(lib().csa_topk(ptr(scores), rows, N, k, ptr(idx), ptr(count), ptr(w), wb, stream_handle(stream)))

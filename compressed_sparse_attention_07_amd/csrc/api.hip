@@ -75,8 +75,7 @@ csa_status check_buf(const csa_buf* b, const char* name) {
   if (!b) return fail(CSA_ERR_NULL, "%s is NULL", name);
   if (b->dtype < CSA_F32 || b->dtype > CSA_MXFP4) return fail(CSA_ERR_DTYPE, "%s has unknown dtype %d", name, b->dtype);
   if (!b->data) return fail(CSA_ERR_NULL, "%s.data is NULL", name);
-  if (b->dtype == CSA_FP8MIX && (!b->rope || !b->scale))
-    return fail(CSA_ERR_NULL, "%s (FP8MIX) needs rope and scale pointers", name);
+  if (b->dtype == CSA_FP8MIX && !b->scale) return fail(CSA_ERR_NULL, "%s (FP8MIX) needs a scale pointer", name);
   if (b->dtype == CSA_MXFP4 && !b->scale) return fail(CSA_ERR_NULL, "%s (MXFP4) needs a scale pointer", name);
   if (!aligned16(b->data) || (b->rope && !aligned16(b->rope)))
     return fail(CSA_ERR_SHAPE, "%s pointers must be 16-byte aligned", name);
@@ -116,6 +115,8 @@ csa_status validate_compress(const void* ca, const void* cb, const void* za, con
   CSA_TRY(check_rope(D, rope_dims, rope_base));
   if (out->dtype == CSA_FP8MIX && (D - rope_dims) % 8)
     return fail(CSA_ERR_SHAPE, "FP8MIX output needs D - rope_dims to be a multiple of 8");
+  if (out->dtype == CSA_FP8MIX && rope_dims > 0 && !out->rope)
+    return fail(CSA_ERR_NULL, "FP8MIX output with rope_dims > 0 needs a rope pointer");
   if (out->dtype == CSA_MXFP4 && D % 32) return fail(CSA_ERR_SHAPE, "MXFP4 output needs D %% 32 == 0");
   if (out_rows < (t0 + T) / ratio)
     return fail(CSA_ERR_SHAPE, "out_rows=%lld < (t0+T)/ratio=%lld", (long long)out_rows, (long long)((t0 + T) / ratio));
@@ -146,6 +147,8 @@ csa_status validate_attn(const csa_buf* q, const int64_t* q_pos, const csa_buf* 
   if (Tw < 1 && B * Tq > 0) return fail(CSA_ERR_SHAPE, "the window buffer is empty");
   CSA_TRY(check_rope(D, rope_dims, rope_base));
   if (kv->dtype == CSA_FP8MIX && (D - rope_dims) % 8) return fail(CSA_ERR_SHAPE, "FP8MIX needs (D - rope_dims) %% 8 == 0");
+  if (kv->dtype == CSA_FP8MIX && rope_dims > 0 && (!kv->rope || !win->rope))
+    return fail(CSA_ERR_NULL, "FP8MIX caches with rope_dims > 0 need rope pointers");
   return CSA_OK;
 }
 
@@ -246,6 +249,7 @@ csa_status csa_quantize(const float* x, int64_t rows, int32_t D, int32_t rope_di
   if (out->dtype == CSA_FP8MIX) {
     CSA_TRY(check_rope(D, rope_dims, 10000.f));
     if ((D - rope_dims) % 8) return fail(CSA_ERR_SHAPE, "FP8MIX needs (D - rope_dims) %% 8 == 0");
+    if (rope_dims > 0 && !out->rope) return fail(CSA_ERR_NULL, "FP8MIX with rope_dims > 0 needs a rope pointer");
   }
   if (out->dtype == CSA_MXFP4 && D % 32) return fail(CSA_ERR_SHAPE, "MXFP4 needs D %% 32 == 0");
   if (!aligned16(x)) return fail(CSA_ERR_SHAPE, "x must be 16-byte aligned");
@@ -288,7 +292,7 @@ size_t csa_topk_workspace_size(int64_t rows, int64_t N, int32_t k) { return topk
 
 csa_status csa_topk(const float* scores, int64_t rows, int64_t N, int32_t k, int32_t* idx, int32_t* count, void* ws,
                     size_t ws_bytes, void* stream) {
-  if (!scores || !idx) return fail(CSA_ERR_NULL, "scores and idx are required");
+  if (!idx || (!scores && rows > 0 && N > 0)) return fail(CSA_ERR_NULL, "scores and idx are required");
   if (rows < 0 || N < 0 || N >= (static_cast<int64_t>(1) << 31)) return fail(CSA_ERR_SHAPE, "N out of range");
   if (k < 1 || k > 4096) return fail(CSA_ERR_SHAPE, "k=%d out of [1, 4096]", k);
   const size_t need = topk_workspace_bytes(rows, N, k);

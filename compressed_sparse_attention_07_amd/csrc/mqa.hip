@@ -90,29 +90,56 @@ __device__ __forceinline__ int64_t slot_row(const AttnArgs& a, const Slots& s, i
 // ================================================================ MFMA path
 
 constexpr int kKT = 32;   // keys per tile
-constexpr int kVP = 36;   // pitch (bf16) of the transposed tile
 
-// At D = 512 a wave needs ~300 registers (16 heads x 512 fp32 accumulators plus
-// the queries), so those workgroups are capped at 4 waves (one per SIMD).
+// At D = 512 a wave needs ~400 registers (16 heads x 512 fp32 accumulators, the
+// queries and one prefetched tile), so those workgroups are capped at 4 waves.
 template <int D>
-constexpr int mfma_max_threads() { return D >= 512 ? 256 : 512; }
+constexpr int mfma_max_waves() { return D >= 512 ? 4 : 8; }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int KP = D + 8;       // row-major pitch (bf16): 16-byte rows, conflict-free reads
-  constexpr int NS = D / 32;      // k-steps of the QK product
-  constexpr int NDB = D / 16;     // 16-row blocks of the PV product
-  __shared__ __attribute__((aligned(16))) uint16_t Krow[kKT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kVP];
-  __shared__ float kscale[kKT];
-  __shared__ int kvalid[kKT];
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i mod 4)
+// of the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3.  With lane j of group g
+// addressing row (key) base + 4g + j/4, column d0 + 4(j mod 4) of the row-major tile,
+// lane i gets the four keys base + 4g + e at column d0 + i: a column of V, i.e. a row
+// of V^T, which is the A operand layout of the PV product.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+}
+
+__device__ __forceinline__ void rope_cs_theta(double pos, double theta, float* c, float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double ang = pos * theta;
+  const double red = fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);
+  sincosf(static_cast<float>(red), s, c);
+}
+
+template <int D, int NW, bool FP8>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int KP = D + 8;            // row pitch (bf16): conflict-free 16-byte row reads
+  constexpr int NS = D / 32;           // k-steps of S^T = K Q^T
+  constexpr int NDB = D / 16;          // 16-row blocks of O^T = V^T P^T
+  constexpr int CH = D / 8;            // 16-byte chunks per key row
+  constexpr int IPT = kKT * CH / NT;   // chunks per thread per tile
+  static_assert(IPT * NT == kKT * CH, "tile must split evenly");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Krow[2][kKT * KP];
+  __shared__ float kscale[2][kKT];
+  __shared__ int kvalid[2][kKT];
+  __shared__ int64_t src_row[2][kKT];  // row in kv / win, -1 = empty
+  __shared__ int64_t src_pos[2][kKT];  // window position (window rows)
+  __shared__ int src_win[2][kKT];
+  __shared__ float2 qcs[64];           // (cos, sin) of the query position per RoPE pair
+  __shared__ double theta[64];         // RoPE frequencies
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int nthreads = blockDim.x;
 
   const int n_hg = a.H / a.hpw;
   int64_t blk = blockIdx.x;
@@ -123,18 +150,110 @@ __global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnAr
   const Slots S = token_slots(a, bt);
   const int64_t s_lo = static_cast<int64_t>(sp) * a.sps;
   const int64_t s_hi = min(S.nslots, s_lo + a.sps);
+  const int ntiles = s_hi > s_lo ? static_cast<int>((s_hi - s_lo + kKT - 1) / kKT) : 0;
   const int h = hg * a.hpw + wid * 16 + col;  // head of this lane's result column
   const int nope = D - a.R;
   const double qpos = static_cast<double>(S.p + a.pos_offset);
 
-  // (cos, sin) of the query position for every RoPE pair, shared by the query
-  // rotation and the inverse rotation of the output
-  __shared__ float2 qcs[64];
-  for (int j = tid; j < a.R / 2; j += nthreads) {
+  for (int j = tid; j < a.R / 2; j += NT) {
+    const double th = exp2(-2.0 * static_cast<double>(j) / static_cast<double>(a.R) * a.log2_base);
+    theta[j] = th;
     float c, sn;
-    rope_cs(qpos, j, a.R, a.log2_base, &c, &sn);
+    rope_cs_theta(qpos, th, &c, &sn);
     qcs[j] = make_float2(c, sn);
   }
+
+  // resolve the source rows of tile t into src[buf]
+  auto resolve = [&](int t, int buf) {
+    if (tid < kKT) {
+      const int64_t slot = s_lo + static_cast<int64_t>(t) * kKT + tid;
+      int64_t row = -1, wpos = 0;
+      bool is_win = false;
+      if (slot < s_hi) row = slot_row(a, S, bt, slot, &is_win, &wpos);
+      src_row[buf][tid] = row;
+      src_pos[buf][tid] = wpos;
+      src_win[buf][tid] = is_win ? 1 : 0;
+    }
+  };
+  // issue the global loads of tile t (sources in src[buf]) into registers
+  uint4 pre[IPT];
+  float pre_sc[IPT];
+  auto load_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int item = tid + NT * u;
+      const int j = item / CH;
+      const int c = item % CH;
+      const int d0 = 8 * c;
+      const int64_t row = src_row[buf][j];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      float sc = 1.f;
+      if (row >= 0) {
+        const bool w = src_win[buf][j] != 0;
+        const void* base = w ? a.win : a.kv;
+        if (FP8) {
+          if (c == 0) sc = (w ? a.win_scale : a.kv_scale)[row];
+          if (d0 < nope) {
+            const uint2 cd = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + row * nope + d0);
+            v.x = cd.x;
+            v.y = cd.y;
+          } else {
+            v = *reinterpret_cast<const uint4*>((w ? a.win_rope : a.kv_rope) + row * a.R + (d0 - nope));
+          }
+        } else {
+          v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D + d0);
+        }
+      }
+      pre[u] = v;
+      pre_sc[u] = sc;
+    }
+  };
+  // dequantize / rope the registers and store them as tile `buf` (row-major bf16)
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int item = tid + NT * u;
+      const int j = item / CH;
+      const int c = item % CH;
+      const int d0 = 8 * c;
+      uint4 v = pre[u];
+      const int64_t row = src_row[buf][j];
+      if (FP8 && d0 < nope) {
+        const uint2 cd = make_uint2(v.x, v.y);
+        v.x = e4m3_to_bf16(cd.x & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.x >> 8) & 0xff)) << 16);
+        v.y = e4m3_to_bf16((cd.x >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.x >> 24)) << 16);
+        v.z = e4m3_to_bf16(cd.y & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.y >> 8) & 0xff)) << 16);
+        v.w = e4m3_to_bf16((cd.y >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.y >> 24)) << 16);
+      }
+      if (row >= 0 && src_win[buf][j] && d0 + 8 > nope) {
+        // window rows are raw: rotate their RoPE dims to their own position
+        float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                      bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+        const double kp = static_cast<double>(src_pos[buf][j] + a.pos_offset);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          if (d0 + e >= nope) {
+            float cc, sn;
+            rope_cs_theta(kp, theta[(d0 + e - nope) / 2], &cc, &sn);
+            const float x0 = x[e], x1 = x[e + 1];
+            x[e] = x0 * cc - x1 * sn;
+            x[e + 1] = x0 * sn + x1 * cc;
+          }
+        }
+        v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                       pack_bf16x2(x[6], x[7]));
+      }
+      *reinterpret_cast<uint4*>(&Krow[buf][j * KP + d0]) = v;
+      if (c == 0) {
+        kscale[buf][j] = pre_sc[u];
+        kvalid[buf][j] = row >= 0 ? 1 : 0;
+      }
+    }
+  };
+
+  // prologue: sources of tiles 0 and 1, data of tile 0
+  resolve(0, 0);
+  resolve(1, 1);
   __syncthreads();
 
   // queries (B operand of S^T = K Q^T): q[h][32s + 8grp .. +8], RoPE'd at the query position
@@ -163,89 +282,30 @@ __global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnAr
       qreg[s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
 
   f32x4 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int64_t s0 = s_lo; s0 < s_hi; s0 += kKT) {
-    // ---- gather 32 key rows into LDS (row-major), dequantize, rope window rows
-    constexpr int CH = D / 8;
-    for (int i = tid; i < kKT * CH; i += nthreads) {
-      const int j = i / CH;
-      const int c = i % CH;
-      const int d0 = 8 * c;
-      const int64_t slot = s0 + j;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      float sc = 1.f;
-      bool valid = false;
-      if (slot < s_hi) {
-        bool is_win = false;
-        int64_t wpos = 0;
-        const int64_t row = slot_row(a, S, bt, slot, &is_win, &wpos);
-        if (row >= 0) {
-          valid = true;
-          const void* base = is_win ? a.win : a.kv;
-          if (FP8) {
-            const uint16_t* rp = is_win ? a.win_rope : a.kv_rope;
-            const float* sp_ = is_win ? a.win_scale : a.kv_scale;
-            sc = sp_[row];
-            if (d0 < nope) {
-              uint2 cd = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + row * nope + d0);
-              val.x = e4m3_to_bf16(cd.x & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.x >> 8) & 0xff)) << 16);
-              val.y = e4m3_to_bf16((cd.x >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.x >> 24)) << 16);
-              val.z = e4m3_to_bf16(cd.y & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.y >> 8) & 0xff)) << 16);
-              val.w = e4m3_to_bf16((cd.y >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.y >> 24)) << 16);
-            } else {
-              val = *reinterpret_cast<const uint4*>(rp + row * a.R + (d0 - nope));
-            }
-          } else {
-            val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D + d0);
-          }
-          if (is_win && d0 + 8 > nope) {
-            float v[8] = {bf16lo(val.x), bf16hi(val.x), bf16lo(val.y), bf16hi(val.y),
-                          bf16lo(val.z), bf16hi(val.z), bf16lo(val.w), bf16hi(val.w)};
-            const double kp = static_cast<double>(wpos + a.pos_offset);
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              if (d0 + e >= nope) {
-                float cc, sn;
-                rope_cs(kp, (d0 + e - nope) / 2, a.R, a.log2_base, &cc, &sn);
-                const float x0 = v[e], x1 = v[e + 1];
-                v[e] = x0 * cc - x1 * sn;
-                v[e + 1] = x0 * sn + x1 * cc;
-              }
-            }
-            val = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                             pack_bf16x2(v[6], v[7]));
-          }
-        }
-      }
-      *reinterpret_cast<uint4*>(&Krow[j * KP + d0]) = val;
-      if (c == 0) {
-        kscale[j] = sc;
-        kvalid[j] = valid ? 1 : 0;
-      }
-    }
-    __syncthreads();
-    // ---- transposed copy: Vt[d][j] (pairs of keys packed in one dword)
-    for (int i = tid; i < D * (kKT / 2); i += nthreads) {
-      const int d = i % D;
-      const int jp = i / D;
-      const uint32_t lo = Krow[(2 * jp) * KP + d];
-      const uint32_t hi = Krow[(2 * jp + 1) * KP + d];
-      *reinterpret_cast<uint32_t*>(&Vt[d * kVP + 2 * jp]) = lo | (hi << 16);
-    }
-    __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, nxt = cur ^ 1;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(nxt);  // in flight during this tile's MFMAs
 
+    const uint16_t* K = Krow[cur];
     // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
     f32x4 sacc[2], racc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       racc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = &Krow[(16 * kb + col) * KP + 8 * grp];
+      const uint16_t* kr = K + (16 * kb + col) * KP + 8 * grp;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
@@ -263,8 +323,8 @@ __global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnAr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * kb + 4 * grp + r;
-        float v = FP8 ? fmaf(kscale[j], sacc[kb][r], racc[kb][r]) : sacc[kb][r];
-        v = kvalid[j] ? a.scale * v : -INFINITY;
+        float v = FP8 ? fmaf(kscale[cur][j], sacc[kb][r], racc[kb][r]) : sacc[kb][r];
+        v = kvalid[cur][j] ? a.scale * v : -INFINITY;
         z[kb][r] = v;
         mt = fmaxf(mt, v);
       }
@@ -283,7 +343,7 @@ __global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnAr
         const float p = none ? 0.f : __expf(z[kb][r] - m_new);
         psum += p;
         pr[4 * kb + r] = p;
-        pn[4 * kb + r] = FP8 ? p * kscale[16 * kb + 4 * grp + r] : p;
+        pn[4 * kb + r] = FP8 ? p * kscale[cur][16 * kb + 4 * grp + r] : p;
       }
     }
     l_run = l_run * alpha + psum;
@@ -296,16 +356,20 @@ __global__ __launch_bounds__(mfma_max_threads<D>()) void attn_mfma_kernel(AttnAr
       pR = __builtin_bit_cast(
           bf16x8, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
                              pack_bf16x2(pr[6], pr[7])));
-    // ---- O^T += V^T P^T: A operand rows d = 16db + col, keys (4grp..+3) and (16+4grp..+3)
+    // ---- O^T += V^T P^T; V^T rows come straight from the row-major tile by transpose reads:
+    //      keys 4grp + (0..3) and 16 + 4grp + (0..3), matching P^T's key order
+    const uint16_t* vb = K + (4 * grp + (col >> 2)) * KP + 4 * (col & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       acc[db] *= alpha;
-      const uint16_t* vr = &Vt[(16 * db + col) * kVP + 4 * grp];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const s16x4 lo = lds_read_tr(vb + 16 * db);
+      const s16x4 hi = lds_read_tr(vb + 16 * KP + 16 * db);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, (FP8 && 16 * db >= nope) ? pR : pB, acc[db], 0, 0, 0);
     }
+
+    if (more) store_tile(nxt);
+    if (t + 2 < ntiles) resolve(t + 2, cur);
     __syncthreads();
   }
 
@@ -545,7 +609,7 @@ struct Plan {
 
 // Largest head group (multiple of 16 dividing H) that fits one workgroup.
 int base_hpw(int H, int D) {
-  const int max_hpw = D >= 512 ? 64 : 128;
+  const int max_hpw = 16 * (D >= 512 ? mfma_max_waves<512>() : mfma_max_waves<128>());
   int hpw = H;
   while (hpw > max_hpw && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) hpw /= 2;
   return hpw <= max_hpw ? hpw : 0;
@@ -557,14 +621,19 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
   const int64_t tokens = B * Tq;
   int hpw = base_hpw(H, D);
   int64_t units = tokens * (H / hpw);
-  while (units < 256 && hpw > 32 && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) {
+  // smaller head groups give more workgroups without split partials, but below these
+  // sizes the prefetch registers no longer fit next to the accumulators
+  const int min_hpw = D >= 512 ? 64 : (D >= 256 ? 32 : 16);
+  while (units < 256 && hpw > min_hpw && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) {
     hpw /= 2;
     units *= 2;
   }
+  // split the key slots when there are too few (token, head group) units to fill
+  // the chip; every split adds H*D fp32 partials per token
   int64_t ns = 1;
   if (units < 256) {
-    ns = (512 + units - 1) / units;
-    const int64_t cap = (max_slots + 63) / 64;
+    ns = (256 + units - 1) / units;
+    const int64_t cap = (max_slots + 127) / 128;
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
   }
@@ -584,7 +653,8 @@ bool mfma_ok(const AttnLaunch& L) {
   if (L.win.dtype != L.kv.dtype) return false;
   if (L.H % 16 != 0) return false;
   if (L.D != 128 && L.D != 256 && L.D != 512) return false;
-  if (base_hpw(L.H, L.D) == 0) return false;
+  const int nw = base_hpw(L.H, L.D) / 16;
+  if (nw != 1 && nw != 2 && nw != 4 && nw != 8) return false;  // instantiated workgroup sizes
   if (L.rope_dims > 128) return false;
   if (L.kv.dtype == CSA_FP8MIX && ((L.D - L.rope_dims) % 32 != 0)) return false;
   return true;
@@ -658,15 +728,20 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
     const int64_t grid = tokens * (L.H / P.hpw) * P.nsplit;
     const dim3 block(P.hpw / 16 * WAVE);
     const bool fp8 = L.kv.dtype == CSA_FP8MIX;
-#define CSA_LAUNCH_MFMA(DD)                                                                              \
-  if (L.D == DD) {                                                                                       \
-    if (fp8) hipLaunchKernelGGL((attn_mfma_kernel<DD, true>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a); \
-    else hipLaunchKernelGGL((attn_mfma_kernel<DD, false>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);    \
+#define CSA_LAUNCH_MFMA_W(DD, NWV)                                                                     \
+  if (L.D == DD && nw == NWV) {                                                                        \
+    if (fp8) hipLaunchKernelGGL((attn_mfma_kernel<DD, NWV, true>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a); \
+    else hipLaunchKernelGGL((attn_mfma_kernel<DD, NWV, false>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);    \
   }
+#define CSA_LAUNCH_MFMA(DD) CSA_LAUNCH_MFMA_W(DD, 1) CSA_LAUNCH_MFMA_W(DD, 2) CSA_LAUNCH_MFMA_W(DD, 4)
+    const int nw = P.hpw / 16;
     CSA_LAUNCH_MFMA(128)
     CSA_LAUNCH_MFMA(256)
     CSA_LAUNCH_MFMA(512)
+    CSA_LAUNCH_MFMA_W(128, 8)
+    CSA_LAUNCH_MFMA_W(256, 8)
 #undef CSA_LAUNCH_MFMA
+#undef CSA_LAUNCH_MFMA_W
     if (hipGetLastError() != hipSuccess) return -1;
     if (P.nsplit > 1) {
       const int64_t threads = tokens * L.H * (L.D / 4);

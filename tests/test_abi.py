@@ -98,7 +98,7 @@ def test_attention_rejects_bad_arguments(L):
     assert call(kv_rows=5) == 2
     assert call(D=1030) == 2
     assert call(out=_buf(0)) == 3          # out dtype differs from q
-    fp8 = _buf(2)                           # FP8MIX without rope/scale pointers
+    fp8 = _buf(2)                           # FP8MIX without a scale pointer
     assert L.csa_sparse_mqa(C.byref(q), p, C.byref(fp8), 10, p, 4, C.byref(win), p, 16, p, 1.0, 64, 10000.0, 0, 1,
                             1, 16, 128, 10, 8, C.byref(out), None, 0, None) == 1
 

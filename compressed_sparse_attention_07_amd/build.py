@@ -5,7 +5,7 @@
 Each csrc/*.hip file is compiled to an object under _build/ (in parallel) and the
 objects are linked into compressed_sparse_attention_07_amd/libcsa.so.  hipcc
 cross-compiles without a GPU.  Packed-fp32 instruction selection is disabled for
-all device code (-packed-fp32-ops).
+all device code (-packed-fp32-ops), and MFMA accumulators are allocated in VGPRs.
 """
 
 from __future__ import annotations
@@ -32,6 +32,9 @@ CFLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: with AGPR accumulators the compiler copies
+    # them to VGPRs at every loop head around the attention softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

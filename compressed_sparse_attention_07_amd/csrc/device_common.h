@@ -22,16 +22,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// nearest-even; NaN stays NaN
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -112,20 +112,25 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
 
 // ---------------------------------------------------------------------- RoPE angles
 
-// (cos, sin) of pos * base^(-2j/R), argument formed and reduced mod 2*pi in fp64 so
-// that positions near 2^20 keep full fp32 accuracy.
-__device__ __forceinline__ void rope_cs(double pos, int j, int R, double log2_base, float* c,
-                                        float* s) {
-  double theta = exp2(-2.0 * static_cast<double>(j) / static_cast<double>(R) * log2_base);
-  double ang = pos * theta;
-  const double two_pi = 6.283185307179586476925286766559;
-  double k = rint(ang * (1.0 / two_pi));
-  double red = fma(-k, two_pi, ang);
-  float fr = static_cast<float>(red);
-  float ss, cc;
-  sincosf(fr, &ss, &cc);
-  *c = cc;
-  *s = ss;
+// RoPE angles are formed in fp64 as revolutions (angle / 2pi) and reduced to
+// [-1/2, 1/2], then evaluated with the hardware sine / cosine, which take their
+// argument in revolutions.  Positions near 2^20 thereby keep full fp32 accuracy
+// and the code stays a handful of instructions (no library range reduction).
+__device__ __forceinline__ double rope_theta_rev(int j, int R, double log2_base) {
+  return exp2(-2.0 * static_cast<double>(j) / static_cast<double>(R) * log2_base) *
+         0.15915494309189533576888376337251;  // 1 / (2 pi)
+}
+
+__device__ __forceinline__ void rope_cs_rev(double pos, double theta_rev, float* c, float* s) {
+  const double r = pos * theta_rev;
+  const float f = static_cast<float>(r - rint(r));
+  *s = __builtin_amdgcn_sinf(f);
+  *c = __builtin_amdgcn_cosf(f);
+}
+
+// (cos, sin) of pos * base^(-2j/R)
+__device__ __forceinline__ void rope_cs(double pos, int j, int R, double log2_base, float* c, float* s) {
+  rope_cs_rev(pos, rope_theta_rev(j, R, log2_base), c, s);
 }
 
 // ------------------------------------------------------------------ wave reductions

@@ -107,18 +107,21 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
   }
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kI.data) + b * a.kI_rows * a.DI;
-  for (int64_t s0 = s_begin; s0 < s_end; s0 += 16 * kTiles) {
+  // keys of 64 entries starting at s0 (B operand: entry = col, k = 32ks + 8grp .. +8)
+  auto load = [&](bf16x8 (&kb)[kTiles][KS], int64_t s0) {
+#pragma unroll
+    for (int tI = 0; tI < kTiles; ++tI) {
+      int64_t s = s0 + tI * 16 + col;
+      if (s >= vis_end) s = vis_end - 1;   // clamp: in bounds, masked below
+      const uint16_t* kp = kbase + s * a.DI + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kb[tI][ks] = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
+    }
+  };
+  // scores of the 64 entries at s0: lane (grp, col) stores entry s0 + 16*grp + col
+  auto score = [&](const bf16x8 (&kb)[kTiles][KS], int64_t s0) {
     float res = -INFINITY;
     if (s0 < vis_end) {
-      bf16x8 kb[kTiles][KS];
-#pragma unroll
-      for (int tI = 0; tI < kTiles; ++tI) {
-        int64_t s = s0 + tI * 16 + col;
-        if (s >= vis_end) s = vis_end - 1;   // clamp: in bounds, masked below
-        const uint16_t* kp = kbase + s * a.DI + grp * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kb[tI][ks] = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
-      }
       float part[kTiles];
 #pragma unroll
       for (int tI = 0; tI < kTiles; ++tI) {
@@ -137,7 +140,6 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
         sc += __shfl_xor(sc, 32, WAVE);
         part[tI] = sc;
       }
-      // lane (grp, col) stores entry s0 + 16*grp + col
 #pragma unroll
       for (int tI = 0; tI < kTiles; ++tI)
         if (grp == tI) res = part[tI];
@@ -145,6 +147,20 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
     }
     const int64_t s = s0 + lane;
     if (s < s_end) out[s] = res;
+  };
+
+  // two register buffers: the next 64 entries are in flight while the current ones
+  // go through the MFMAs and the epilogue
+  constexpr int64_t kStep = 16 * kTiles;
+  bf16x8 kA[kTiles][KS], kB[kTiles][KS];
+  int64_t s0 = s_begin;
+  if (s0 < vis_end) load(kA, s0);
+  for (; s0 < s_end; s0 += 2 * kStep) {
+    if (s0 + kStep < vis_end) load(kB, s0 + kStep);
+    score(kA, s0);
+    if (s0 + kStep >= s_end) break;
+    if (s0 + 2 * kStep < vis_end) load(kA, s0 + 2 * kStep);
+    score(kB, s0 + kStep);
   }
 }
 
@@ -156,7 +172,9 @@ MfmaKern pick_ks(int KS) {
     case 1: return index_mfma_kernel<HB, 1>;
     case 2: return index_mfma_kernel<HB, 2>;
     case 4: return index_mfma_kernel<HB, 4>;
-    case 8: return index_mfma_kernel<HB, 8>;
+    case 8:
+      if constexpr (HB * 8 <= 32) return index_mfma_kernel<HB, 8>;  // larger tiles would spill
+      return nullptr;
   }
   return nullptr;
 }

@@ -49,12 +49,12 @@ struct AttnArgs {
   int hpw, nsplit, sps;
   void* out;
   int out_dtype;
-  float* part_o;   // [tokens, H, nsplit, D]
-  float2* part_ml; // [tokens, H, nsplit]
+  uint16_t* part_o; // [tokens, H, nsplit, D] bf16, O / l of the split
+  float2* part_ml;  // [tokens, H, nsplit] (running max, sum of exponentials)
 };
 
 struct Slots {
-  int64_t b, p, nsel, wstart, nslots;
+  int64_t b, p, nsel, wstart, nslots, wp0;
 };
 
 __device__ __forceinline__ Slots token_slots(const AttnArgs& a, int64_t bt) {
@@ -69,6 +69,7 @@ __device__ __forceinline__ Slots token_slots(const AttnArgs& a, int64_t bt) {
   }
   s.wstart = s.p - a.n_win + 1 > 0 ? s.p - a.n_win + 1 : 0;
   s.nslots = s.nsel + (s.p - s.wstart + 1);
+  s.wp0 = a.win_pos0[s.b];
   return s;
 }
 
@@ -84,7 +85,7 @@ __device__ __forceinline__ int64_t slot_row(const AttnArgs& a, const Slots& s, i
   *is_win = true;
   const int64_t pw = s.wstart + (slot - s.nsel);
   *wpos = pw;
-  return s.b * a.Tw + (pw - a.win_pos0[s.b]);
+  return s.b * a.Tw + (pw - s.wp0);
 }
 
 // ================================================================ MFMA path
@@ -109,13 +110,6 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
       (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
 }
 
-__device__ __forceinline__ void rope_cs_theta(double pos, double theta, float* c, float* s) {
-  const double two_pi = 6.283185307179586476925286766559;
-  const double ang = pos * theta;
-  const double red = fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);
-  sincosf(static_cast<float>(red), s, c);
-}
-
 template <int D, int NW, bool FP8>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
@@ -127,13 +121,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   static_assert(IPT * NT == kKT * CH, "tile must split evenly");
 
   __shared__ __attribute__((aligned(16))) uint16_t Krow[2][kKT * KP];
-  __shared__ float kscale[2][kKT];
-  __shared__ int kvalid[2][kKT];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[NW * 16 * KP];  // RoPE'd queries of the group
+  __shared__ __attribute__((aligned(16))) float kscale[2][kKT];
+  __shared__ __attribute__((aligned(16))) int kvalid[2][kKT];
   __shared__ int64_t src_row[2][kKT];  // row in kv / win, -1 = empty
   __shared__ int64_t src_pos[2][kKT];  // window position (window rows)
   __shared__ int src_win[2][kKT];
   __shared__ float2 qcs[64];           // (cos, sin) of the query position per RoPE pair
-  __shared__ double theta[64];         // RoPE frequencies
+  __shared__ double theta[64];         // RoPE frequencies in revolutions per position
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,23 +151,41 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   const double qpos = static_cast<double>(S.p + a.pos_offset);
 
   for (int j = tid; j < a.R / 2; j += NT) {
-    const double th = exp2(-2.0 * static_cast<double>(j) / static_cast<double>(a.R) * a.log2_base);
+    const double th = rope_theta_rev(j, a.R, a.log2_base);
     theta[j] = th;
     float c, sn;
-    rope_cs_theta(qpos, th, &c, &sn);
+    rope_cs_rev(qpos, th, &c, &sn);
     qcs[j] = make_float2(c, sn);
   }
 
-  // resolve the source rows of tile t into src[buf]
-  auto resolve = [&](int t, int buf) {
+  // resolve the source rows of tile t into src[buf] in two halves: the entry-index
+  // load is issued early (resolve_load) and consumed after the tile's MFMAs
+  // (resolve_store), so its latency overlaps the compute
+  int32_t r_e = 0;
+  auto resolve_load = [&](int t) {
+    if (tid < kKT) {
+      const int64_t slot = s_lo + static_cast<int64_t>(t) * kKT + tid;
+      r_e = (a.sparse && slot < s_hi && slot < S.nsel) ? a.idx[bt * a.K + slot] : 0;
+    }
+  };
+  auto resolve_store = [&](int t, int buf) {
     if (tid < kKT) {
       const int64_t slot = s_lo + static_cast<int64_t>(t) * kKT + tid;
       int64_t row = -1, wpos = 0;
-      bool is_win = false;
-      if (slot < s_hi) row = slot_row(a, S, bt, slot, &is_win, &wpos);
+      int win = 0;
+      if (slot < s_hi) {
+        if (slot < S.nsel) {
+          const int64_t e = a.sparse ? static_cast<int64_t>(r_e) : slot;
+          row = e >= 0 ? S.b * a.kv_rows + e : -1;
+        } else {
+          win = 1;
+          wpos = S.wstart + (slot - S.nsel);
+          row = S.b * a.Tw + (wpos - S.wp0);
+        }
+      }
       src_row[buf][tid] = row;
       src_pos[buf][tid] = wpos;
-      src_win[buf][tid] = is_win ? 1 : 0;
+      src_win[buf][tid] = win;
     }
   };
   // issue the global loads of tile t (sources in src[buf]) into registers
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
       pre_sc[u] = sc;
     }
   };
-  // dequantize / rope the registers and store them as tile `buf` (row-major bf16)
+  // dequantize the registers and store them as tile `buf` (row-major bf16)
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
@@ -217,7 +230,6 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
       const int c = item % CH;
       const int d0 = 8 * c;
       uint4 v = pre[u];
-      const int64_t row = src_row[buf][j];
       if (FP8 && d0 < nope) {
         const uint2 cd = make_uint2(v.x, v.y);
         v.x = e4m3_to_bf16(cd.x & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.x >> 8) & 0xff)) << 16);
@@ -225,45 +237,60 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         v.z = e4m3_to_bf16(cd.y & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16((cd.y >> 8) & 0xff)) << 16);
         v.w = e4m3_to_bf16((cd.y >> 16) & 0xff) | (static_cast<uint32_t>(e4m3_to_bf16(cd.y >> 24)) << 16);
       }
-      if (row >= 0 && src_win[buf][j] && d0 + 8 > nope) {
-        // window rows are raw: rotate their RoPE dims to their own position
-        float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                      bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
-        const double kp = static_cast<double>(src_pos[buf][j] + a.pos_offset);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          if (d0 + e >= nope) {
-            float cc, sn;
-            rope_cs_theta(kp, theta[(d0 + e - nope) / 2], &cc, &sn);
-            const float x0 = x[e], x1 = x[e + 1];
-            x[e] = x0 * cc - x1 * sn;
-            x[e + 1] = x0 * sn + x1 * cc;
-          }
-        }
-        v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                       pack_bf16x2(x[6], x[7]));
-      }
       *reinterpret_cast<uint4*>(&Krow[buf][j * KP + d0]) = v;
       if (c == 0) {
         kscale[buf][j] = pre_sc[u];
-        kvalid[buf][j] = row >= 0 ? 1 : 0;
+        kvalid[buf][j] = src_row[buf][j] >= 0 ? 1 : 0;
       }
     }
   };
+  // window rows are raw: rotate the RoPE dims of tile `buf` to each row's own position
+  // (only tiles that reach into the window run this)
+  const int RCH = a.R / 8;  // 16-byte chunks of RoPE dims per row
+  auto rope_window_rows = [&](int buf) {
+    for (int item = tid; item < kKT * RCH; item += NT) {
+      const int j = item / RCH;
+      if (!src_win[buf][j] || src_row[buf][j] < 0) continue;
+      const int d0 = nope + 8 * (item % RCH);
+      uint4 v = *reinterpret_cast<const uint4*>(&Krow[buf][j * KP + d0]);
+      float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      const double kp = static_cast<double>(src_pos[buf][j] + a.pos_offset);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float cc, sn;
+        rope_cs_rev(kp, theta[(d0 + e - nope) / 2], &cc, &sn);
+        const float x0 = x[e], x1 = x[e + 1];
+        x[e] = x0 * cc - x1 * sn;
+        x[e + 1] = x0 * sn + x1 * cc;
+      }
+      v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7]));
+      *reinterpret_cast<uint4*>(&Krow[buf][j * KP + d0]) = v;
+    }
+  };
+  // does tile t hold window rows?  (slots >= nsel are window positions)
+  auto tile_has_window = [&](int t) {
+    const int64_t first = s_lo + static_cast<int64_t>(t) * kKT;
+    return min(first + kKT, s_hi) > S.nsel && first < s_hi;
+  };
 
   // prologue: sources of tiles 0 and 1, data of tile 0
-  resolve(0, 0);
-  resolve(1, 1);
+  resolve_load(0);
+  resolve_store(0, 0);
+  resolve_load(1);
+  resolve_store(1, 1);
   __syncthreads();
 
-  // queries (B operand of S^T = K Q^T): q[h][32s + 8grp .. +8], RoPE'd at the query position
-  bf16x8 qreg[NS];
+  // queries of the head group, RoPE'd at the query position, staged once in LDS;
+  // the B operand of S^T = K Q^T (q[h][32s + 8grp .. +8]) is read from there per tile,
+  // which keeps the registers for the accumulators
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (bt * a.H + h) * D;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int d0 = 32 * s + 8 * grp;
-      uint4 raw = *reinterpret_cast<const uint4*>(qp + d0);
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw) * D;
+    for (int i = tid; i < NW * 16 * CH; i += NT) {
+      const int hr = i / CH;
+      const int d0 = 8 * (i % CH);
+      uint4 raw = *reinterpret_cast<const uint4*>(qg + hr * D + d0);
       if (d0 + 8 > nope) {
         float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
                       bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
@@ -279,14 +306,19 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                          pack_bf16x2(v[6], v[7]));
       }
-      qreg[s] = __builtin_bit_cast(bf16x8, raw);
+      *reinterpret_cast<uint4*>(&Qs[hr * KP + d0]) = raw;
     }
   }
+  const uint16_t* qrow = Qs + (wid * 16 + col) * KP + 8 * grp;
   if (ntiles > 0) {
     load_tile(0);
     store_tile(0);
   }
   __syncthreads();
+  if (ntiles > 0 && tile_has_window(0)) {
+    rope_window_rows(0);
+    __syncthreads();
+  }
 
   f32x4 acc[NDB];
 #pragma unroll
@@ -297,6 +329,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     const int cur = t & 1, nxt = cur ^ 1;
     const bool more = t + 1 < ntiles;
     if (more) load_tile(nxt);  // in flight during this tile's MFMAs
+    if (t + 2 < ntiles) resolve_load(t + 2);
 
     const uint16_t* K = Krow[cur];
     // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
@@ -305,49 +338,66 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       racc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = K + (16 * kb + col) * KP + 8 * grp;
+    }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 32 * s);
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + (16 * kb + col) * KP + 8 * grp + 32 * s);
         if (FP8 && 32 * s >= nope)
-          racc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[s], racc[kb], 0, 0, 0);
+          racc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, racc[kb], 0, 0, 0);
         else
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf, sacc[kb], 0, 0, 0);
       }
     }
     // ---- online softmax for head h over this lane's 8 keys (16kb + 4grp + r)
-    float z[2][4];
+    float z[2][4], ksc[2][4];
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const int4 kv4 = *reinterpret_cast<const int4*>(&kvalid[cur][16 * kb + 4 * grp]);
+      const float4 ks4 = *reinterpret_cast<const float4*>(&kscale[cur][16 * kb + 4 * grp]);
+      const int vv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+      const float kk[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * kb + 4 * grp + r;
-        float v = FP8 ? fmaf(kscale[cur][j], sacc[kb][r], racc[kb][r]) : sacc[kb][r];
-        v = kvalid[cur][j] ? a.scale * v : -INFINITY;
+        ksc[kb][r] = kk[r];
+        float v = FP8 ? fmaf(kk[r], sacc[kb][r], racc[kb][r]) : sacc[kb][r];
+        v = vv[r] ? a.scale * v : -INFINITY;
         z[kb][r] = v;
         mt = fmaxf(mt, v);
       }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
     mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
-    const float m_new = fmaxf(m_run, mt);
-    const bool none = (m_new == -INFINITY);
-    const float alpha = none ? 1.f : __expf(m_run - m_new);
+    // Lazy rescaling: the exponentials use a reference max m_run that is raised only
+    // when a logit exceeds it by more than kSlack (so p <= e^kSlack); O and l always
+    // refer to the same m_run, so the result is exact whatever the reference.
+    constexpr float kSlack = 8.f;
+    const bool raise = mt > m_run + kSlack;
+    const float m_ref = raise ? mt : m_run;
+    if (__any(raise)) {  // wave-uniform: rescale the accumulators of the heads that moved
+      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : __expf(m_run - m_ref);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    m_run = m_ref;
+    const bool none = (m_run == -INFINITY);
     float pn[8], pr[8];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = none ? 0.f : __expf(z[kb][r] - m_new);
+        const float p = none ? 0.f : __expf(z[kb][r] - m_run);
         psum += p;
         pr[4 * kb + r] = p;
-        pn[4 * kb + r] = FP8 ? p * kscale[cur][16 * kb + 4 * grp + r] : p;
+        pn[4 * kb + r] = FP8 ? p * ksc[kb][r] : p;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
     const bf16x8 pB = __builtin_bit_cast(
         bf16x8, make_uint4(pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3]), pack_bf16x2(pn[4], pn[5]),
                            pack_bf16x2(pn[6], pn[7])));
@@ -361,7 +411,6 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     const uint16_t* vb = K + (4 * grp + (col >> 2)) * KP + 4 * (col & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      acc[db] *= alpha;
       const s16x4 lo = lds_read_tr(vb + 16 * db);
       const s16x4 hi = lds_read_tr(vb + 16 * KP + 16 * db);
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -369,8 +418,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     }
 
     if (more) store_tile(nxt);
-    if (t + 2 < ntiles) resolve(t + 2, cur);
+    if (t + 2 < ntiles) resolve_store(t + 2, cur);
     __syncthreads();
+    if (more && tile_has_window(t + 1)) {
+      rope_window_rows(nxt);
+      __syncthreads();
+    }
   }
 
   // sum of exponentials for head h: the four row groups hold disjoint keys
@@ -380,10 +433,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 
   const int64_t th = bt * a.H + h;
   if (a.nsplit > 1) {
-    float* po = a.part_o + (th * a.nsplit + sp) * D;
+    // normalised partial (a convex combination of keys) stored as bf16
+    uint16_t* po = a.part_o + (th * a.nsplit + sp) * D;
+    const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<float4*>(po + 16 * db + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+      *reinterpret_cast<uint2*>(po + 16 * db + 4 * grp) =
+          make_uint2(pack_bf16x2(acc[db][0] * il, acc[db][1] * il), pack_bf16x2(acc[db][2] * il, acc[db][3] * il));
     if (grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
     return;
   }
@@ -429,10 +485,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int i = 0; i < a.nsplit; ++i) {
     const float2 v = ml[i];
     if (v.x == -INFINITY) continue;
-    const float w = __expf(v.x - M);
-    L += w * v.y;
-    const float4 po = *reinterpret_cast<const float4*>(a.part_o + (th * a.nsplit + i) * a.D + d0);
-    o[0] += w * po.x; o[1] += w * po.y; o[2] += w * po.z; o[3] += w * po.w;
+    const float w = __expf(v.x - M) * v.y;
+    L += w;
+    const uint2 po = *reinterpret_cast<const uint2*>(a.part_o + (th * a.nsplit + i) * a.D + d0);
+    o[0] += w * bf16lo(po.x); o[1] += w * bf16hi(po.x); o[2] += w * bf16lo(po.y); o[3] += w * bf16hi(po.y);
   }
   const float sk = a.sink[h];
   float inv;
@@ -699,8 +755,8 @@ AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
   a.out_dtype = L.out.dtype;
   if (P.mfma && P.nsplit > 1) {
     const int64_t th = L.B * L.Tq * L.H;
-    a.part_o = static_cast<float*>(ws);
-    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + th * P.nsplit * L.D * sizeof(float));
+    a.part_o = static_cast<uint16_t*>(ws);
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + th * P.nsplit * L.D * sizeof(uint16_t));
   }
   return a;
 }
@@ -713,7 +769,7 @@ size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slo
   Plan P = make_plan(B, Tq, H, D, max_slots, mfma_path);
   if (!P.mfma || P.nsplit <= 1) return 0;
   const int64_t th = B * Tq * H;
-  return static_cast<size_t>(th * P.nsplit) * (static_cast<size_t>(D) * sizeof(float) + sizeof(float2));
+  return static_cast<size_t>(th * P.nsplit) * (static_cast<size_t>(D) * sizeof(uint16_t) + sizeof(float2));
 }
 
 int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12            # B/s, MI355X published
 MFMA_BF16_PEAK = 2.5e15      # FLOP/s dense bf16, MI355X published
+COPY_PROBE_BYTES = 1 << 30  # bytes read (and written) by one copy-probe launch
+WORKLOAD_TAG = "csa_decode_b16_ctx128k"
 METRIC = "CSA decode tokens/s @128K ctx; indexer+MQA % MFMA peak, compress/top-k % HBM"
 
 
@@ -64,6 +66,78 @@ def read_traffic(kernel_file: str, src: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
+def _short(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").replace("csa::", "").split("(")[0]
+
+
+def summarize_trace(db_path: str, out: str, command: str):
+    """Per-kernel duration summary of a `rocprofv3 --kernel-trace` database (rocpd SQLite)."""
+    import sqlite3
+    cur = sqlite3.connect(db_path).cursor()
+    rows = cur.execute("select name, count(*), avg(duration), min(duration), max(duration), "
+                       "sum(duration), avg(grid_x / workgroup_x) from kernels group by name "
+                       "order by sum(duration) desc").fetchall()
+    lines = [f"# rocprofv3 kernel-trace summary", f"# command: {command}",
+             f"# {'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s} {'wgs':>7s}"]
+    for n, c, av, mn, mx, tot, wgs in rows:
+        lines.append(f"{_short(n)[:60]:60s} {c:6d} {av / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} "
+                     f"{tot / 1e3:10.1f} {wgs:7.0f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines[:14]))
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: str, command: str):
+    """HBM traffic per launch of `kernel` from FETCH_SIZE / WRITE_SIZE counter runs.
+
+    Both counters (KiB per dispatch) are scaled by what they read for the copy probe
+    (torch.neg over 1 GiB: 1 GiB read, 1 GiB written).  Dispatches of `kernel` are
+    grouped by grid size and the most frequent grid (the decode step's) is reported.
+    """
+    import collections
+    import csv
+
+    def load(path, counter):
+        per = collections.defaultdict(list)
+        probe = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "neg_kernel" in name:  # only the copy probe calls torch.neg
+                probe.append(v)
+            elif _short(name).startswith(kernel):
+                per[(_short(name), int(r["Grid_Size"]))].append(v)
+        return per, probe
+
+    fetch, pf = load(fetch_csv, "FETCH_SIZE")
+    write, pw = load(write_csv, "WRITE_SIZE")
+    if not pf or not pw or not fetch:
+        raise SystemExit(f"missing probe or kernel dispatches (probe {len(pf)}/{len(pw)}, kernel {len(fetch)})")
+    key = max(fetch, key=lambda k: len(fetch[k]))
+    kib = COPY_PROBE_BYTES / 1024
+    f_fac = kib / (sum(pf) / len(pf))
+    w_fac = kib / (sum(pw) / len(pw))
+    f_avg = sum(fetch[key]) / len(fetch[key])
+    w_avg = sum(write[key]) / len(write[key]) if write.get(key) else 0.0
+    traffic = (f_avg * f_fac + w_avg * w_fac) * 1024
+    lines = [f"# HBM traffic per launch of {key[0]} (grid {key[1]} threads), decode step of the headline workload",
+             f"# command (FETCH_SIZE pass): {command.replace('@COUNTER@', 'FETCH_SIZE')}",
+             f"# command (WRITE_SIZE pass): {command.replace('@COUNTER@', 'WRITE_SIZE')}",
+             f"# summarised by: python bench.py --summarize-pmc <fetch.csv> <write.csv> --kernel {kernel}",
+             f"kernel = {key[0]}", f"grid_threads = {key[1]}", f"dispatches = {len(fetch[key])}",
+             f"fetch_kib_per_dispatch = {f_avg:.1f}", f"write_kib_per_dispatch = {w_avg:.1f}",
+             f"probe_fetch_kib = {sum(pf) / len(pf):.1f}", f"probe_write_kib = {sum(pw) / len(pw):.1f}",
+             f"fetch_scale = {f_fac:.4f}", f"write_scale = {w_fac:.4f}",
+             f"traffic_bytes_per_launch = {traffic:.0f}", f"source_hash = {src}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+KERNEL_SOURCES = {"attn_mfma_kernel": ("mqa.hip",), "attn_combine_kernel": ("mqa.hip",),
+                  "index_mfma_kernel": ("indexer.hip",), "topk_kernel": ("topk.hip",),
+                  "compress_kernel": ("compress.hip",)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,10 +145,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--stage-reps", type=int, default=20)
-    ap.add_argument("--cpu-seqs", type=int, default=1, help="sequences timed for the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB device copy (PMC calibration)")
+    ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write an HBM-traffic summary from two counter runs (no GPU work)")
+    ap.add_argument("--kernel", default="attn_mfma_kernel")
+    ap.add_argument("--profile-cmd", default="", help="command recorded in the summary")
+    ap.add_argument("--out", help="summary file")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, args.profile_cmd)
+        return
+    if args.summarize_pmc:
+        out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{WORKLOAD_TAG}_pmc.txt")
+        summarize_pmc(*args.summarize_pmc, args.kernel, src_hash(*KERNEL_SOURCES[args.kernel]), out,
+                      args.profile_cmd)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
               "the decode workload shards by sequence (see DESIGN.md)", file=sys.stderr)
@@ -238,23 +326,25 @@ def main():
         achieved, peak, unit = dom["bytes"] / dom["t"] / 1e9, HBM_PEAK / 1e9, "GB/s"
     else:
         achieved, peak, unit = dom["flops"] / dom["t"] / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
-    traffic = read_traffic(f"{dom['kernel']}_cfg1_decode_pmc.txt", src_hash(*dom["src"]))
+    traffic = read_traffic(f"{dom['kernel']}_{WORKLOAD_TAG}_pmc.txt", src_hash(*dom["src"]))
     roofline = dict(kernel=dom["kernel"], stage=dom_name, bound=stage_out[dom_name]["bound"],
                     achieved=round(achieved, 2), peak=peak, unit=unit, frac=round(achieved / peak, 4),
                     traffic=traffic, algorithmic_bytes=dom["bytes"], avg_launch_us=round(dom["t"] * 1e6, 2))
 
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB): the
+        # reference for scaling the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.zeros(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log("copy probe: 3 x 1 GiB device copies done")
+        log("copy probe: 3 x neg over 1 GiB done")
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_seqs, steps_in[0], dev)
+        cpu = cpu_baseline(cfg, args.cpu_seconds, dev)
 
     cache_build = dict(us=round(build_ms * 1e3, 1), GBps=round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
                        hbm_frac=round(build_bytes / (build_ms * 1e-3) / HBM_PEAK, 4),
@@ -281,18 +371,19 @@ def _seq(buf, b):
     return csa.Buf(buf.dtype, sl(buf.data), sl(buf.rope), sl(buf.scale))
 
 
-def cpu_baseline(cfg, nseq, d, dev):
-    """Time the fp64 oracle's decode step (same workload) on `nseq` sequences.
+def cpu_baseline(cfg, seconds, dev):
+    """Time the fp64 oracle's decode step (same workload) for about `seconds` of CPU work.
 
-    The oracle builds its own caches from the same seeded streams (untimed), then
-    the decode step -- compress the newest block, score every entry, top-k, MQA
-    over the selection and the window -- is timed.
+    The oracle builds sequence 0's caches from the same seeded streams (untimed).
+    Then decode steps with fresh seeded inputs (new block, queries, window, sink)
+    are timed one after another -- compress the newest block, score every entry,
+    top-k, MQA over the selection and the window -- until `seconds` have been spent.
     """
     import numpy as np
     import torch
 
     from oracle import csa_oracle as O
-    from synth import Gen
+    from synth import Gen, qstd
 
     try:
         from threadpoolctl import threadpool_info
@@ -301,36 +392,47 @@ def cpu_baseline(cfg, nseq, d, dev):
         threads = 1
     cores = len(os.sched_getaffinity(0))
     f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
-    m, D, R, ctx = cfg.m, cfg.D, cfg.R, cfg.ctx
+    m, D, R, ctx, DI, W = cfg.m, cfg.D, cfg.R, cfg.ctx, cfg.DI, cfg.n_win
+    bf = torch.bfloat16
     t0 = ctx - m
-    total = 0.0
-    for b in range(nseq):
-        g = Gen(cfg.seed * 1000 + b, dev)
-        s = [f(g.normal((1, ctx, cfg.D), dtype=torch.bfloat16)[0]) for _ in range(4)]
-        si = [f(g.normal((1, ctx, cfg.DI), dtype=torch.bfloat16)[0]) for _ in range(4)]
-        log(f"cpu baseline: oracle cache build for sequence {b} (untimed)")
-        kv = O.compress(*s, ratio=m, overlap=True, rope_dims=R, rope_base=cfg.rope_base)
-        ik = O.compress(*si, ratio=m, overlap=True)
-        del s, si
+    g = Gen(cfg.seed * 1000, dev)
+    s = [f(g.normal((1, ctx, D), dtype=bf)[0]) for _ in range(4)]
+    si = [f(g.normal((1, ctx, DI), dtype=bf)[0]) for _ in range(4)]
+    log("cpu baseline: oracle cache build for sequence 0 (untimed)")
+    kv = O.compress(*s, ratio=m, overlap=True, rope_dims=R, rope_base=cfg.rope_base)
+    ik = O.compress(*si, ratio=m, overlap=True)
+    del s, si
+    pos = np.array([ctx])
+    total, steps = 0.0, 0
+    while total < seconds and steps < 100000:
+        g = Gen(cfg.seed * 7919 + steps, dev)
+        blk = [f(g.normal((m, D), dtype=bf)) for _ in range(6)]
+        iblk = [f(g.normal((m, DI), dtype=bf)) for _ in range(6)]
+        q = f(g.normal((1, cfg.H, D), qstd(D), dtype=bf))
+        qI = f(g.normal((1, cfg.HI, DI), qstd(DI), dtype=bf))
+        wI = f(g.uniform((1, cfg.HI)))
+        win = f(g.normal((W, D), dtype=bf))
+        sink = f(g.normal((cfg.H,)))
         tic = time.perf_counter()
-        e = O.compress(f(d["ca"][b]), f(d["cb"][b]), f(d["za"][b]), f(d["zb"][b]), ratio=m, overlap=True, t0=t0,
-                       prev_cb=f(d["prev_cb"][b]), prev_zb=f(d["prev_zb"][b]), rope_dims=R, rope_base=cfg.rope_base)
+        e = O.compress(*blk[:4], ratio=m, overlap=True, t0=t0, prev_cb=blk[4], prev_zb=blk[5], rope_dims=R,
+                       rope_base=cfg.rope_base)
         kv[-1] = e[0]
-        ei = O.compress(f(d["ica"][b]), f(d["icb"][b]), f(d["iza"][b]), f(d["izb"][b]), ratio=m, overlap=True,
-                        t0=t0, prev_cb=f(d["iprev_cb"][b]), prev_zb=f(d["iprev_zb"][b]))
+        ei = O.compress(*iblk[:4], ratio=m, overlap=True, t0=t0, prev_cb=iblk[4], prev_zb=iblk[5])
         ik[-1] = ei[0]
-        pos = np.array([ctx])
-        sc = O.index_scores(f(d["qI"][b]), f(d["wI"][b]), ik, pos, m)
+        sc = O.index_scores(qI, wI, ik, pos, m)
         idx, _ = O.topk(sc, cfg.k)
-        O.mqa(f(d["q"][b]), pos, kv, idx, f(d["win"][b]), ctx - cfg.n_win + 1, cfg.n_win, f(d["sink"]),
-              scale=cfg.softmax_scale, rope_dims=R, rope_base=cfg.rope_base)
+        O.mqa(q, pos, kv, idx, win, ctx - W + 1, W, sink, scale=cfg.softmax_scale, rope_dims=R,
+              rope_base=cfg.rope_base)
         total += time.perf_counter() - tic
-    rate = nseq / total
-    log(f"cpu baseline: {nseq} sequence(s) in {total:.2f} s -> {rate:.2f} tokens/s ({threads} BLAS threads, "
+        steps += 1
+    rate = steps / total
+    log(f"cpu baseline: {steps} decode steps in {total:.2f} s -> {rate:.2f} tokens/s ({threads} BLAS threads, "
         f"{cores} cores)")
     return dict(value=round(rate, 3), unit="tokens/s", cores=threads, host_cores=cores, kind="oracle",
-                sample=f"{nseq} of {cfg.B} sequences: one decode step each (compress newest block, score 32768 "
-                       f"entries, top-{cfg.k}, MQA over {cfg.k}+{cfg.n_win} keys); oracle caches built untimed")
+                seconds=round(total, 2),
+                sample=f"{steps} decode steps of sequence 0 (fresh seeded block, queries, window and sink per "
+                       f"step): compress the newest block, score {ctx // m} entries, top-{cfg.k}, MQA over "
+                       f"{cfg.k}+{W} keys; the oracle's caches are built once, untimed")
 
 
 if __name__ == "__main__":

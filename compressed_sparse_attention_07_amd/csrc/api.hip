@@ -449,7 +449,6 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     C.pos_offset = L->pos_offset;
     C.out = io->kv_cache;
     C.out_rows = L->cache_rows;
-    if (launch_compress(C, s) != 0) return launched(-1, "csa_forward/compress");
     if (csa_mode) {
       CompressLaunch I = C;
       I.ca = io->ica;
@@ -463,7 +462,9 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
       I.D = L->DI;
       I.rope_dims = 0;
       I.out = io->ik_cache;
-      if (launch_compress(I, s) != 0) return launched(-1, "csa_forward/compress-indexer");
+      if (launch_compress2(C, I, s) != 0) return launched(-1, "csa_forward/compress");
+    } else if (launch_compress(C, s) != 0) {
+      return launched(-1, "csa_forward/compress");
     }
   }
   if (csa_mode) {

@@ -149,10 +149,7 @@ struct CompressArgs {
 };
 
 template <typename TIn>
-__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
-  // LDS: row-group partials (m, s, acc[8]) and per-entry scale maxima
-  __shared__ float part[kThreads * (2 + kVec)];
-  __shared__ uint32_t amax_lds[kThreads];  // entries_per_wg * amax_words <= 256
+__device__ __forceinline__ void compress_block(const CompressArgs& a, int64_t block, float* part, uint32_t* amax_lds) {
 
   const int tid = threadIdx.x;
   const int tpe = a.chunks * a.G;                       // threads per entry
@@ -161,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   const int g = r_in / a.chunks;                         // row group
   const int c = r_in % a.chunks;                         // channel chunk
   const int64_t n_entries = a.T / a.ratio;
-  const int64_t e_glob = static_cast<int64_t>(blockIdx.x) * a.entries_per_wg + e_local;
+  const int64_t e_glob = block * a.entries_per_wg + e_local;
   const int64_t total = a.B * n_entries;
   const bool active = e_local < a.entries_per_wg && e_glob < total;
   const int aw = amax_words(a.out.dtype, a.D);
@@ -308,6 +305,25 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   }
 }
 
+// One launch runs up to two compressions (the KV stream and the indexer-key stream
+// of a layer): blocks [0, grid0) belong to job 0, the rest to job 1.
+struct CompressArgs2 {
+  CompressArgs job[2];
+  int64_t grid0;
+};
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs2 a) {
+  // LDS: row-group partials (m, s, acc[8]) and per-entry scale maxima
+  __shared__ float part[kThreads * (2 + kVec)];
+  __shared__ uint32_t amax_lds[kThreads];  // entries_per_wg * amax_words <= 256
+  const int64_t blk = blockIdx.x;
+  if (blk < a.grid0)
+    compress_block<TIn>(a.job[0], blk, part, amax_lds);
+  else
+    compress_block<TIn>(a.job[1], blk - a.grid0, part, amax_lds);
+}
+
 struct QuantArgs {
   const float* x;
   int64_t rows;
@@ -334,8 +350,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 
 }  // namespace
 
-int launch_compress(const CompressLaunch& L, hipStream_t stream) {
-  CompressArgs a{};
+namespace {
+
+// Fill the job description of one compression and return its block count.
+int64_t make_job(const CompressLaunch& L, CompressArgs& a) {
+  a = CompressArgs{};
   a.ca = L.ca; a.cb = L.cb; a.za = L.za; a.zb = L.zb;
   a.bias_a = L.bias_a; a.bias_b = L.bias_b;
   a.prev_cb = L.prev_cb; a.prev_zb = L.prev_zb;
@@ -351,13 +370,31 @@ int launch_compress(const CompressLaunch& L, hipStream_t stream) {
   a.G = G;
   a.entries_per_wg = kThreads / (a.chunks * G);
   const int64_t n_entries = L.B * (L.T / L.ratio);
-  if (n_entries == 0) return 0;
-  const int64_t grid = (n_entries + a.entries_per_wg - 1) / a.entries_per_wg;
-  if (L.stream_dtype == CSA_F32)
+  return (n_entries + a.entries_per_wg - 1) / a.entries_per_wg;
+}
+
+int launch(const CompressArgs2& a, int64_t grid, int stream_dtype, hipStream_t stream) {
+  if (grid == 0) return 0;
+  if (stream_dtype == CSA_F32)
     hipLaunchKernelGGL(compress_kernel<float>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(compress_kernel<uint16_t>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace
+
+int launch_compress(const CompressLaunch& L, hipStream_t stream) {
+  CompressArgs2 a{};
+  a.grid0 = make_job(L, a.job[0]);
+  return launch(a, a.grid0, L.stream_dtype, stream);
+}
+
+int launch_compress2(const CompressLaunch& L0, const CompressLaunch& L1, hipStream_t stream) {
+  CompressArgs2 a{};
+  a.grid0 = make_job(L0, a.job[0]);
+  const int64_t g1 = make_job(L1, a.job[1]);
+  return launch(a, a.grid0 + g1, L0.stream_dtype, stream);
 }
 
 int launch_quantize(const float* x, int64_t rows, int D, int rope_dims, const csa_buf& out,

@@ -23,6 +23,8 @@ struct CompressLaunch {
   int64_t out_rows;
 };
 int launch_compress(const CompressLaunch& L, hipStream_t stream);
+// two compressions sharing the stream dtype (KV and indexer keys) in one launch
+int launch_compress2(const CompressLaunch& L0, const CompressLaunch& L1, hipStream_t stream);
 int launch_quantize(const float* x, int64_t rows, int D, int rope_dims, const csa_buf& out,
                     hipStream_t stream);
 

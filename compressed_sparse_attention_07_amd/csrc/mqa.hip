@@ -18,6 +18,8 @@
 // several key ranges per token, partial (max, sum, O) go to the workspace and a
 // combine kernel merges them in fixed split order, so results do not depend on
 // scheduling or batch composition.
+#include <cmath>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -43,6 +45,7 @@ struct AttnArgs {
   float scale;
   int R;
   double log2_base;
+  double theta_rev[64];  // RoPE frequency of pair j in revolutions per position
   int64_t pos_offset;
   int64_t B, Tq, N;
   int H, D, n_win;
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   const double qpos = static_cast<double>(S.p + a.pos_offset);
 
   for (int j = tid; j < a.R / 2; j += NT) {
-    const double th = rope_theta_rev(j, a.R, a.log2_base);
+    const double th = a.theta_rev[j];
     theta[j] = th;
     float c, sn;
     rope_cs_rev(qpos, th, &c, &sn);
@@ -161,14 +164,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   // resolve the source rows of tile t into src[buf] in two halves: the entry-index
   // load is issued early (resolve_load) and consumed after the tile's MFMAs
   // (resolve_store), so its latency overlaps the compute
-  int32_t r_e = 0;
-  auto resolve_load = [&](int t) {
+  auto resolve_load = [&](int t) -> int32_t {
+    int32_t e = 0;
     if (tid < kKT) {
       const int64_t slot = s_lo + static_cast<int64_t>(t) * kKT + tid;
-      r_e = (a.sparse && slot < s_hi && slot < S.nsel) ? a.idx[bt * a.K + slot] : 0;
+      e = (a.sparse && slot < s_hi && slot < S.nsel) ? a.idx[bt * a.K + slot] : 0;
     }
+    return e;
   };
-  auto resolve_store = [&](int t, int buf) {
+  auto resolve_store = [&](int t, int buf, int32_t r_e) {
     if (tid < kKT) {
       const int64_t slot = s_lo + static_cast<int64_t>(t) * kKT + tid;
       int64_t row = -1, wpos = 0;
@@ -275,45 +279,56 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     return min(first + kKT, s_hi) > S.nsel && first < s_hi;
   };
 
-  // prologue: sources of tiles 0 and 1, data of tile 0
-  resolve_load(0);
-  resolve_store(0, 0);
-  resolve_load(1);
-  resolve_store(1, 1);
+  // prologue: the entry indices of tiles 0 and 1 and the queries are fetched together,
+  // tile 0's rows are requested as soon as its indices are known, and the query RoPE /
+  // LDS staging runs while they are in flight
+  constexpr int QIT = 16 * CH / 64;  // 16-byte query chunks per thread (NW*16 heads over NW*64 threads)
+  uint4 qv[QIT];
+  {
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw) * D;
+#pragma unroll
+    for (int u = 0; u < QIT; ++u) {
+      const int i = tid + NT * u;
+      qv[u] = *reinterpret_cast<const uint4*>(qg + (i / CH) * D + 8 * (i % CH));
+    }
+  }
+  {
+    const int32_t e0 = resolve_load(0);
+    const int32_t e1 = resolve_load(1);
+    resolve_store(0, 0, e0);
+    resolve_store(1, 1, e1);
+  }
   __syncthreads();
+  if (ntiles > 0) load_tile(0);
 
   // queries of the head group, RoPE'd at the query position, staged once in LDS;
   // the B operand of S^T = K Q^T (q[h][32s + 8grp .. +8]) is read from there per tile,
   // which keeps the registers for the accumulators
-  {
-    const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw) * D;
-    for (int i = tid; i < NW * 16 * CH; i += NT) {
-      const int hr = i / CH;
-      const int d0 = 8 * (i % CH);
-      uint4 raw = *reinterpret_cast<const uint4*>(qg + hr * D + d0);
-      if (d0 + 8 > nope) {
-        float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
-                      bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          if (d0 + e >= nope) {
-            const float2 cs = qcs[(d0 + e - nope) / 2];
-            const float x0 = v[e], x1 = v[e + 1];
-            v[e] = x0 * cs.x - x1 * cs.y;
-            v[e + 1] = x0 * cs.y + x1 * cs.x;
-          }
+  for (int u = 0; u < QIT; ++u) {
+    const int i = tid + NT * u;
+    const int hr = i / CH;
+    const int d0 = 8 * (i % CH);
+    uint4 raw = qv[u];
+    if (d0 + 8 > nope) {
+      float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
+                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        if (d0 + e >= nope) {
+          const float2 cs = qcs[(d0 + e - nope) / 2];
+          const float x0 = v[e], x1 = v[e + 1];
+          v[e] = x0 * cs.x - x1 * cs.y;
+          v[e + 1] = x0 * cs.y + x1 * cs.x;
         }
-        raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                         pack_bf16x2(v[6], v[7]));
       }
-      *reinterpret_cast<uint4*>(&Qs[hr * KP + d0]) = raw;
+      raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
     }
+    *reinterpret_cast<uint4*>(&Qs[hr * KP + d0]) = raw;
   }
   const uint16_t* qrow = Qs + (wid * 16 + col) * KP + 8 * grp;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) store_tile(0);
   __syncthreads();
   if (ntiles > 0 && tile_has_window(0)) {
     rope_window_rows(0);
@@ -329,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     const int cur = t & 1, nxt = cur ^ 1;
     const bool more = t + 1 < ntiles;
     if (more) load_tile(nxt);  // in flight during this tile's MFMAs
-    if (t + 2 < ntiles) resolve_load(t + 2);
+    const int32_t e2 = (t + 2 < ntiles) ? resolve_load(t + 2) : 0;
 
     const uint16_t* K = Krow[cur];
     // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     }
 
     if (more) store_tile(nxt);
-    if (t + 2 < ntiles) resolve_store(t + 2, cur);
+    if (t + 2 < ntiles) resolve_store(t + 2, cur, e2);
     __syncthreads();
     if (more && tile_has_window(t + 1)) {
       rope_window_rows(nxt);
@@ -468,53 +483,71 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of every (token, head) in split order.
+// Merge the split partials of every (token, head) in split order: one wave per
+// (token, head), lane l owns output dims [8l, 8l + 8) (D <= 512, nsplit <= 64).
+// The split weights exp(m_i - M) * l_i are formed once per wave (lane i holds split
+// i) and broadcast; every lane issues all its partial loads before combining.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int per = a.D / 4;
-  const int64_t th = gid / per;
+  const int lane = threadIdx.x & 63;
+  const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (th >= a.B * a.Tq * a.H) return;
-  const int d0 = static_cast<int>(gid % per) * 4;
   const int h = static_cast<int>(th % a.H);
   const int64_t bt = th / a.H;
-  const float2* ml = a.part_ml + th * a.nsplit;
-  float M = -INFINITY;
-  for (int i = 0; i < a.nsplit; ++i) M = fmaxf(M, ml[i].x);
-  float L = 0.f;
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < a.nsplit; ++i) {
-    const float2 v = ml[i];
-    if (v.x == -INFINITY) continue;
-    const float w = __expf(v.x - M) * v.y;
-    L += w;
-    const uint2 po = *reinterpret_cast<const uint2*>(a.part_o + (th * a.nsplit + i) * a.D + d0);
-    o[0] += w * bf16lo(po.x); o[1] += w * bf16hi(po.x); o[2] += w * bf16lo(po.y); o[3] += w * bf16hi(po.y);
+  const int ns = a.nsplit;
+  const float2 ml = lane < ns ? a.part_ml[th * ns + lane] : make_float2(-INFINITY, 0.f);
+  const float M = wave_max(ml.x);
+  const float wgt = (ml.x == -INFINITY) ? 0.f : __expf(ml.x - M) * ml.y;
+  const float L = wave_sum(wgt);
+  const int d0 = 8 * lane;
+  const bool on = d0 < a.D;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* pb = a.part_o + (th * ns) * a.D + d0;
+  for (int i0 = 0; i0 < ns; i0 += 8) {
+    uint4 pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      pv[u] = (on && i0 + u < ns) ? *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(i0 + u) * a.D)
+                                   : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = __shfl(wgt, (i0 + u) & 63, WAVE);
+      if (i0 + u < ns) {
+        o[0] = fmaf(w, bf16lo(pv[u].x), o[0]); o[1] = fmaf(w, bf16hi(pv[u].x), o[1]);
+        o[2] = fmaf(w, bf16lo(pv[u].y), o[2]); o[3] = fmaf(w, bf16hi(pv[u].y), o[3]);
+        o[4] = fmaf(w, bf16lo(pv[u].z), o[4]); o[5] = fmaf(w, bf16hi(pv[u].z), o[5]);
+        o[6] = fmaf(w, bf16lo(pv[u].w), o[6]); o[7] = fmaf(w, bf16hi(pv[u].w), o[7]);
+      }
+    }
   }
+  if (!on) return;
   const float sk = a.sink[h];
   float inv;
   if (sk == INFINITY) inv = 0.f;
   else if (sk == -INFINITY) inv = 1.f / L;
   else inv = 1.f / (L + __expf(sk - M));
-  float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= inv;
   const int nope = a.D - a.R;
-  const int64_t p = a.q_pos[bt];
-  if (d0 + 4 > nope) {
-    const double qpos = static_cast<double>(p + a.pos_offset);
-    for (int e = 0; e < 4; e += 2) {
+  if (d0 + 8 > nope) {
+    const double qpos = static_cast<double>(a.q_pos[bt] + a.pos_offset);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
       if (d0 + e >= nope) {
         float c, sn;
-        rope_cs(-qpos, (d0 + e - nope) / 2, a.R, a.log2_base, &c, &sn);
-        const float x0 = v[e], x1 = v[e + 1];
-        v[e] = x0 * c - x1 * sn;
-        v[e + 1] = x0 * sn + x1 * c;
+        rope_cs_rev(-qpos, a.theta_rev[(d0 + e - nope) / 2], &c, &sn);
+        const float x0 = o[e], x1 = o[e + 1];
+        o[e] = x0 * c - x1 * sn;
+        o[e + 1] = x0 * sn + x1 * c;
       }
     }
   }
   if (a.out_dtype == CSA_F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + th * a.D + d0) = make_float4(v[0], v[1], v[2], v[3]);
+    float* op = static_cast<float*>(a.out) + th * a.D + d0;
+    reinterpret_cast<float4*>(op)[0] = make_float4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<float4*>(op)[1] = make_float4(o[4], o[5], o[6], o[7]);
   } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + th * a.D + d0) =
-        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + th * a.D + d0) =
+        make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
   }
 }
 
@@ -689,7 +722,8 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
   int64_t ns = 1;
   if (units < 256) {
     ns = (256 + units - 1) / units;
-    const int64_t cap = (max_slots + 127) / 128;
+    int64_t cap = (max_slots + 127) / 128;
+    if (cap > 64) cap = 64;  // the combine kernel holds one split per lane
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
   }
@@ -741,6 +775,10 @@ AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
   a.scale = L.scale;
   a.R = L.rope_dims;
   a.log2_base = L.log2_base;
+  for (int j = 0; j < 64; ++j)
+    a.theta_rev[j] = j < L.rope_dims / 2
+                         ? std::exp2(-2.0 * j / L.rope_dims * L.log2_base) * 0.15915494309189533576888376337251
+                         : 0.0;
   a.pos_offset = L.pos_offset;
   a.B = L.B;
   a.Tq = L.Tq;
@@ -800,9 +838,8 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
 #undef CSA_LAUNCH_MFMA_W
     if (hipGetLastError() != hipSuccess) return -1;
     if (P.nsplit > 1) {
-      const int64_t threads = tokens * L.H * (L.D / 4);
-      hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>((threads + 255) / 256)), dim3(256), 0,
-                         stream, a);
+      const int64_t waves = tokens * L.H;
+      hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>((waves + 3) / 4)), dim3(256), 0, stream, a);
       if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;

@@ -324,7 +324,7 @@ csa_status csa_sparse_mqa(const csa_buf* q, const int64_t* q_pos, const csa_buf*
 }
 
 size_t hca_dense_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t D, int64_t N, int32_t n_win) {
-  return attn_workspace_bytes(B, Tq, H, D, N + n_win, true);
+  return attn_workspace_bytes(B, Tq, H, D, N + n_win, false);
 }
 
 csa_status hca_dense_attn(const csa_buf* q, const int64_t* q_pos, const csa_buf* kv, int64_t kv_rows, int32_t ratio,
@@ -337,7 +337,7 @@ csa_status hca_dense_attn(const csa_buf* q, const int64_t* q_pos, const csa_buf*
   if (ratio < 1) return fail(CSA_ERR_SHAPE, "ratio must be >= 1");
   AttnLaunch L = make_attn(q, q_pos, kv, kv_rows, 0, nullptr, 0, ratio, win, win_pos0, Tw, sink, softmax_scale,
                            rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win, out);
-  const size_t need = attn_uses_mfma(L) ? attn_workspace_bytes(B, Tq, H, D, N + n_win, true) : 0;
+  const size_t need = attn_uses_mfma(L) ? attn_workspace_bytes(B, Tq, H, D, N + n_win, false) : 0;
   if (need > ws_bytes || (need > 0 && !ws))
     return fail(CSA_ERR_WORKSPACE, "hca_dense_attn needs %zu workspace bytes, got %zu", need, ws_bytes);
   CSA_TRY(check_device());
@@ -366,7 +366,7 @@ FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx) {
     off += p.idx_bytes;
     p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, static_cast<int64_t>(L->topk) + L->n_win, true));
   } else {
-    p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, p.N + L->n_win, true));
+    p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, p.N + L->n_win, false));
   }
   p.attn_off = off;
   off += p.attn_bytes;

@@ -64,7 +64,7 @@ struct AttnLaunch {
   int H, D, n_win;
   csa_buf out;
 };
-size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_keys, bool mfma_path);
+size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_keys, bool sparse);
 bool attn_uses_mfma(const AttnLaunch& L);
 int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stream);
 

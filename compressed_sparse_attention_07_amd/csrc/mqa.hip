@@ -18,6 +18,7 @@
 // several key ranges per token, partial (max, sum, O) go to the workspace and a
 // combine kernel merges them in fixed split order, so results do not depend on
 // scheduling or batch composition.
+#include <algorithm>
 #include <cmath>
 
 #include "device_common.h"
@@ -483,6 +484,339 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+// ================================================================ LDS-DMA path (bf16, D = 512)
+//
+// The computation of attn_mfma_kernel, with the key rows brought into LDS by direct
+// global->LDS loads: one global_load_lds_dwordx4 moves one 1 KiB row, lane i's 16
+// bytes landing at M0 + 16 i.  No registers hold tiles in flight, so a ring of
+// kDmaStages tiles keeps three tiles of gathered rows in flight while the fourth is
+// computed on.  The queries live in registers (B operand of S^T = K Q^T), loaded and
+// roped there once.  With 8 waves (128 heads) two waves share each SIMD, so one wave's
+// LDS reads overlap the other's MFMAs.  Each wave issues the same number of row loads for every
+// tile (an empty slot loads the query's own window row, which the softmax masks), so
+// "tile t has landed" is "at most (rows per wave) x (tiles issued after t) vector
+// memory operations outstanding", waited for with s_waitcnt and made visible to the
+// other waves by the barrier that follows.  The compiler does not see these loads;
+// the loop issues no other vector-memory operation.
+
+constexpr int kDmaStages = 4;
+constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
+
+// One row load to LDS.  M0 is saved and restored around the instruction (the address
+// is taken at issue), so the compiler's own uses of M0 are unaffected.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(lds_byte)
+               : "memory");
+}
+
+// a wave-uniform 64-bit value, moved to scalar registers
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
+  constexpr int D = 512;
+  constexpr int NT = NW * 64;
+  constexpr int KP = D + 8;            // row pitch (bf16)
+  constexpr int NS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int RPW = kKT / NW;        // rows each wave loads per tile
+  constexpr int STAGE = kKT * KP;      // bf16 per ring stage
+  static_assert(RPW * (kDmaStages - 2) < 64, "outstanding row loads must fit vmcnt");
+
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kDmaStages * STAGE];
+  __shared__ __attribute__((aligned(16))) int idx_s[kDmaIdxCap];
+  __shared__ __attribute__((aligned(16))) int kvalid[kDmaStages][kKT];
+  __shared__ int64_t wpos_s[kDmaStages][kKT];  // window position of a window row, -1 otherwise
+  __shared__ float2 qcs[64];
+  __shared__ double theta[64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  const int n_hg = a.H / a.hpw;
+  int64_t blk = blockIdx.x;
+  const int hg = static_cast<int>(blk % n_hg);
+  blk /= n_hg;
+  const int sp = static_cast<int>(blk % a.nsplit);
+  const int64_t bt = blk / a.nsplit;
+  const int64_t s_lo = static_cast<int64_t>(sp) * a.sps;
+  // prologue: the queries (straight into the B-operand registers: lane (col, grp) holds
+  // q[head col][32 s + 8 grp .. + 8]), the range's entry indices and the positions are
+  // loaded together -- none depends on another
+  const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  uint4 qraw[NS];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw + wid * 16 + col) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+  }
+  int32_t idx_pre[kDmaIdxCap / NT];
+  const int64_t n_idx = a.sparse ? min(s_lo + a.sps, static_cast<int64_t>(a.K)) - s_lo : 0;
+#pragma unroll
+  for (int u = 0; u < kDmaIdxCap / NT; ++u) {
+    const int64_t i = tid + static_cast<int64_t>(u) * NT;
+    idx_pre[u] = i < n_idx ? a.idx[bt * a.K + s_lo + i] : 0;
+  }
+  const Slots S = token_slots(a, bt);
+  const int64_t s_hi = min(S.nslots, s_lo + a.sps);
+  const int ntiles = s_hi > s_lo ? static_cast<int>((s_hi - s_lo + kKT - 1) / kKT) : 0;
+  const int h = hg * a.hpw + wid * 16 + col;
+  const int nope = D - a.R;
+  const double qpos = static_cast<double>(S.p + a.pos_offset);
+  const uint16_t* kvp = static_cast<const uint16_t*>(a.kv);
+  const uint16_t* winp = static_cast<const uint16_t*>(a.win);
+
+  for (int j = tid; j < a.R / 2; j += NT) {
+    const double th = a.theta_rev[j];
+    theta[j] = th;
+    float c, sn;
+    rope_cs_rev(qpos, th, &c, &sn);
+    qcs[j] = make_float2(c, sn);
+  }
+
+#pragma unroll
+  for (int u = 0; u < kDmaIdxCap / NT; ++u) {
+    const int64_t i = tid + static_cast<int64_t>(u) * NT;
+    if (i < n_idx) idx_s[i] = idx_pre[u];
+  }
+  // every load the compiler tracks completes here, before the first row load it cannot
+  // see is issued (a later wait for these registers would also wait for the row loads)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qraw[s].x), "v"(qraw[s].y), "v"(qraw[s].z), "v"(qraw[s].w));
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // source row of slot j of tile u; empty slots read the query's own window row (the
+  // softmax masks them).  Every quantity here is wave-uniform.
+  const int64_t u_lo = uni64(s_lo), u_hi = uni64(s_hi), u_nsel = uni64(S.nsel), u_wstart = uni64(S.wstart);
+  const uint16_t* kv_b = kvp + uni64(S.b * a.kv_rows) * D;
+  const uint16_t* win_b = winp + uni64(S.b * a.Tw - S.wp0) * D;  // row of window position p: win_b + p*D
+  const uint16_t* win_self = win_b + uni64(S.p) * D;
+  // issue the row loads of tile u into ring stage u % kDmaStages: lane i < RPW resolves
+  // row wid*RPW + i, then each row's base address is broadcast to one row load
+  auto issue = [&](int u) {
+    const int st = u % kDmaStages;
+    const uint16_t* src = win_self;
+    if (lane < RPW) {
+      const int j = wid * RPW + lane;
+      const int64_t slot = u_lo + static_cast<int64_t>(u) * kKT + j;
+      const bool live = slot < u_hi;
+      const bool sel = slot < u_nsel;
+      int64_t e = slot;
+      if (a.sparse) e = idx_s[min(slot - u_lo, static_cast<int64_t>(kDmaIdxCap - 1))];
+      const int64_t wp = u_wstart + (slot - u_nsel);
+      const bool ok = live && (!sel || e >= 0);
+      kvalid[st][j] = ok ? 1 : 0;
+      wpos_s[st][j] = (ok && !sel) ? wp : -1;
+      src = !ok ? win_self : (sel ? kv_b + e * D : win_b + wp * D);
+    }
+    const uint64_t sa = reinterpret_cast<uint64_t>(src);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      // readlane returns int: widen through uint32_t so the low half is not sign-extended
+      const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sa), i));
+      const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sa >> 32), i));
+      const uint16_t* row = reinterpret_cast<const uint16_t*>((hi << 32) | lo);
+      lds_dma16(row + lane * 8, ring_b + (st * STAGE + (wid * RPW + i) * KP) * 2);
+    }
+  };
+  // window rows are raw: rotate their RoPE dims to each row's own position
+  const int RCH = a.R / 8;
+  auto rope_window_rows = [&](int st) {
+    uint16_t* T = ring + st * STAGE;
+    for (int item = tid; item < kKT * RCH; item += NT) {
+      const int j = item / RCH;
+      const int64_t wpj = wpos_s[st][j];
+      if (wpj < 0) continue;
+      const int d0 = nope + 8 * (item % RCH);
+      uint4 v = *reinterpret_cast<const uint4*>(&T[j * KP + d0]);
+      float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      const double kp = static_cast<double>(wpj + a.pos_offset);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float cc, sn;
+        rope_cs_rev(kp, theta[(d0 + e - nope) / 2], &cc, &sn);
+        const float x0 = x[e], x1 = x[e + 1];
+        x[e] = x0 * cc - x1 * sn;
+        x[e + 1] = x0 * sn + x1 * cc;
+      }
+      *reinterpret_cast<uint4*>(&T[j * KP + d0]) =
+          make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7]));
+    }
+  };
+  auto tile_has_window = [&](int t) {
+    const int64_t first = s_lo + static_cast<int64_t>(t) * kKT;
+    return min(first + kKT, s_hi) > S.nsel && first < s_hi;
+  };
+
+  // tiles 0..2 in flight while the queries are roped in registers
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+  bf16x8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    uint4 raw = qraw[s];
+    const int d0 = 32 * s + 8 * grp;
+    if (d0 + 8 > nope) {
+      float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
+                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        if (d0 + e >= nope) {
+          const float2 cs = qcs[(d0 + e - nope) / 2];
+          const float x0 = v[e], x1 = v[e + 1];
+          v[e] = x0 * cs.x - x1 * cs.y;
+          v[e + 1] = x0 * cs.y + x1 * cs.x;
+        }
+      }
+      raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t % kDmaStages;
+    const int later = min(ntiles - 1 - t, kDmaStages - 2);  // tiles issued after t
+    if (later >= 2) wait_vmcnt<2 * RPW>();
+    else if (later == 1) wait_vmcnt<RPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (tile_has_window(t)) {
+      rope_window_rows(st);
+      __syncthreads();
+    }
+    if (t + kDmaStages - 1 < ntiles) issue(t + kDmaStages - 1);  // into the stage freed by tile t-1
+
+    const uint16_t* K = ring + st * STAGE;
+    // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + (16 * kb + col) * KP + 8 * grp + 32 * s);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+      }
+    }
+    // ---- online softmax for head h over this lane's 8 keys (16kb + 4grp + r)
+    float z[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int4 kv4 = *reinterpret_cast<const int4*>(&kvalid[st][16 * kb + 4 * grp]);
+      const int vv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = vv[r] ? a.scale * sacc[kb][r] : -INFINITY;
+        z[kb][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    constexpr float kSlack = 8.f;  // lazy rescale, as in attn_mfma_kernel
+    const bool raise = mt > m_run + kSlack;
+    const float m_ref = raise ? mt : m_run;
+    if (__any(raise)) {
+      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : __expf(m_run - m_ref);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    m_run = m_ref;
+    const bool none = (m_run == -INFINITY);
+    float pn[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = none ? 0.f : __expf(z[kb][r] - m_run);
+        psum += p;
+        pn[4 * kb + r] = p;
+      }
+    }
+    l_run += psum;
+    const bf16x8 pB = __builtin_bit_cast(
+        bf16x8, make_uint4(pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3]), pack_bf16x2(pn[4], pn[5]),
+                           pack_bf16x2(pn[6], pn[7])));
+    // ---- O^T += V^T P^T (V^T by transpose reads of the row-major tile)
+    const uint16_t* vb = K + (4 * grp + (col >> 2)) * KP + 4 * (col & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const s16x4 lo = lds_read_tr(vb + 16 * db);
+      const s16x4 hi = lds_read_tr(vb + 16 * KP + 16 * db);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pB, acc[db], 0, 0, 0);
+    }
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, WAVE);
+  l_tot += __shfl_xor(l_tot, 32, WAVE);
+
+  const int64_t th = bt * a.H + h;
+  if (a.nsplit > 1) {
+    uint16_t* po = a.part_o + (th * a.nsplit + sp) * D;
+    const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<uint2*>(po + 16 * db + 4 * grp) =
+          make_uint2(pack_bf16x2(acc[db][0] * il, acc[db][1] * il), pack_bf16x2(acc[db][2] * il, acc[db][3] * il));
+    if (grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
+    return;
+  }
+  const float sk = a.sink[h];
+  float inv;
+  if (sk == INFINITY) inv = 0.f;
+  else if (sk == -INFINITY) inv = 1.f / l_tot;
+  else inv = 1.f / (l_tot + __expf(sk - m_run));
+  uint16_t* op = static_cast<uint16_t*>(a.out) + th * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int d0 = 16 * db + 4 * grp;
+    float v[4] = {acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv};
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      if (d0 + e >= nope) {
+        const float2 cs = qcs[(d0 + e - nope) / 2];
+        const float x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * cs.x + x1 * cs.y;
+        v[e + 1] = x1 * cs.x - x0 * cs.y;
+      }
+    }
+    *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
 // Merge the split partials of every (token, head) in split order: one wave per
 // (token, head), lane l owns output dims [8l, 8l + 8) (D <= 512, nsplit <= 64).
 // The split weights exp(m_i - M) * l_i are formed once per wave (lane i holds split
@@ -696,37 +1030,48 @@ struct Plan {
   int hpw, nsplit, sps;
 };
 
-// Largest head group (multiple of 16 dividing H) that fits one workgroup.
-int base_hpw(int H, int D) {
-  const int max_hpw = 16 * (D >= 512 ? mfma_max_waves<512>() : mfma_max_waves<128>());
+constexpr int kDmaMaxWaves = 8;
+
+// Largest head group (multiple of 16 dividing H) of at most max_waves waves.
+int head_group(int H, int max_waves) {
   int hpw = H;
-  while (hpw > max_hpw && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) hpw /= 2;
-  return hpw <= max_hpw ? hpw : 0;
+  while (hpw > 16 * max_waves && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) hpw /= 2;
+  return hpw <= 16 * max_waves ? hpw : 0;
 }
 
-Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma) {
+// Head group of attn_mfma_kernel.
+int base_hpw(int H, int D) {
+  return head_group(H, D >= 512 ? mfma_max_waves<512>() : mfma_max_waves<128>());
+}
+
+Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma, bool sparse, bool dma) {
   Plan p{mfma, 0, 1, 0};
   if (!mfma) return p;
   const int64_t tokens = B * Tq;
-  int hpw = base_hpw(H, D);
+  int hpw = dma ? head_group(H, kDmaMaxWaves) : base_hpw(H, D);
   int64_t units = tokens * (H / hpw);
-  // smaller head groups give more workgroups without split partials, but below these
-  // sizes the prefetch registers no longer fit next to the accumulators
-  const int min_hpw = D >= 512 ? 64 : (D >= 256 ? 32 : 16);
-  while (units < 256 && hpw > min_hpw && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) {
-    hpw /= 2;
-    units *= 2;
+  if (!dma) {
+    // smaller head groups give more workgroups without split partials, but below these
+    // sizes the prefetch registers no longer fit next to the accumulators
+    const int min_hpw = D >= 512 ? 64 : (D >= 256 ? 32 : 16);
+    while (units < 256 && hpw > min_hpw && (hpw / 2) % 16 == 0 && H % (hpw / 2) == 0) {
+      hpw /= 2;
+      units *= 2;
+    }
   }
   // split the key slots when there are too few (token, head group) units to fill
-  // the chip; every split adds H*D fp32 partials per token
+  // the chip; every split adds H*D bf16 partials per token
   int64_t ns = 1;
   if (units < 256) {
     ns = (256 + units - 1) / units;
-    int64_t cap = (max_slots + 127) / 128;
+    int64_t cap = (max_slots + (dma ? 63 : 127)) / (dma ? 64 : 128);
     if (cap > 64) cap = 64;  // the combine kernel holds one split per lane
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
   }
+  // a sparse range's entry indices are staged in LDS by the DMA kernel
+  if (sparse && max_slots <= 64 * kDmaIdxCap && ns < (max_slots + kDmaIdxCap - 1) / kDmaIdxCap)
+    ns = (max_slots + kDmaIdxCap - 1) / kDmaIdxCap;
   int64_t sps = ((max_slots + ns - 1) / ns + kKT - 1) / kKT * kKT;
   if (sps < kKT) sps = kKT;
   ns = (max_slots + sps - 1) / sps;
@@ -752,6 +1097,14 @@ bool mfma_ok(const AttnLaunch& L) {
 
 int64_t max_slots_of(const AttnLaunch& L) {
   return (L.sparse ? static_cast<int64_t>(L.K) : L.N) + L.n_win;
+}
+
+// bf16 cache, D = 512, 2, 4 or 8 waves: the LDS-DMA kernel
+bool dma_ok(const AttnLaunch& L) {
+  if (!mfma_ok(L) || L.kv.dtype != CSA_BF16 || L.D != 512) return false;
+  if (L.sparse && max_slots_of(L) > 64 * kDmaIdxCap) return false;
+  const int nw = head_group(L.H, kDmaMaxWaves) / 16;
+  return nw == 2 || nw == 4 || nw == 8;
 }
 
 AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
@@ -803,19 +1156,22 @@ AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
 
 bool attn_uses_mfma(const AttnLaunch& L) { return mfma_ok(L); }
 
-size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma_path) {
-  Plan P = make_plan(B, Tq, H, D, max_slots, mfma_path);
-  if (!P.mfma || P.nsplit <= 1) return 0;
+size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool sparse) {
+  // the larger of the two MFMA kernels' needs (which one runs depends on the cache dtype)
+  int64_t ns = make_plan(B, Tq, H, D, max_slots, true, sparse, false).nsplit;
+  if (D == 512) ns = std::max<int64_t>(ns, make_plan(B, Tq, H, D, max_slots, true, sparse, true).nsplit);
+  if (ns <= 1) return 0;
   const int64_t th = B * Tq * H;
-  return static_cast<size_t>(th * P.nsplit) * (static_cast<size_t>(D) * sizeof(uint16_t) + sizeof(float2));
+  return static_cast<size_t>(th * ns) * (static_cast<size_t>(D) * sizeof(uint16_t) + sizeof(float2));
 }
 
 int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int64_t tokens = L.B * L.Tq;
   if (tokens == 0) return 0;
   const bool mfma = mfma_ok(L);
-  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma);
-  if (mfma && P.nsplit > 1 && ws_bytes < attn_workspace_bytes(L.B, L.Tq, L.H, L.D, max_slots_of(L), true))
+  const bool dma = mfma && dma_ok(L);
+  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma, L.sparse != 0, dma);
+  if (mfma && P.nsplit > 1 && ws_bytes < attn_workspace_bytes(L.B, L.Tq, L.H, L.D, max_slots_of(L), L.sparse != 0))
     return -3;
   AttnArgs a = make_args(L, P, ws);
   if (mfma) {
@@ -829,11 +1185,18 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
   }
 #define CSA_LAUNCH_MFMA(DD) CSA_LAUNCH_MFMA_W(DD, 1) CSA_LAUNCH_MFMA_W(DD, 2) CSA_LAUNCH_MFMA_W(DD, 4)
     const int nw = P.hpw / 16;
+    if (dma) {
+      if (L.sparse && P.sps > kDmaIdxCap) return -1;  // excluded by the plan
+      if (nw == 8) hipLaunchKernelGGL(attn_dma_kernel<8>, dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+      else if (nw == 4) hipLaunchKernelGGL(attn_dma_kernel<4>, dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+      else hipLaunchKernelGGL(attn_dma_kernel<2>, dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+    } else {
     CSA_LAUNCH_MFMA(128)
     CSA_LAUNCH_MFMA(256)
     CSA_LAUNCH_MFMA(512)
     CSA_LAUNCH_MFMA_W(128, 8)
     CSA_LAUNCH_MFMA_W(256, 8)
+    }
 #undef CSA_LAUNCH_MFMA
 #undef CSA_LAUNCH_MFMA_W
     if (hipGetLastError() != hipSuccess) return -1;

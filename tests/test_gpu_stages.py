@@ -252,6 +252,10 @@ ATTN_CASES = [
     (2, 2, 64, 512, 300, 128, 128, "bf16", "fp8mix", 64, 1.0, [1300, 5000]),
     (1, 3, 32, 256, 120, 40, 16, "bf16", "bf16", 64, 1.0, [50, 60, 70]),
     (1, 2, 8, 64, 50, 10, 8, "f32", "fp8mix", 16, 0.5, [40, 44]),
+    # 2-wave groups; 2040 + 128 slots exceed one workgroup's staged index range
+    (1, 2, 32, 512, 3000, 2040, 128, "bf16", "bf16", 64, 1.0, [9000, 12100]),
+    # window clipped at position 0, fewer selected entries than one tile
+    (2, 1, 128, 512, 40, 30, 128, "bf16", "bf16", 64, 1.0, [60]),
 ]
 
 
@@ -300,6 +304,8 @@ HCA_CASES = [
     (1, 3, 8, 128, 64, 128, 128, "f32", "f32", [127, 5000, 8191]),
     (1, 2, 128, 512, 300, 128, 128, "bf16", "bf16", [20000, 38400]),
     (2, 2, 64, 512, 100, 128, 128, "bf16", "fp8mix", [12800, 9000]),
+    # 2-wave groups; the first query sees no compressed entry
+    (1, 3, 32, 512, 80, 128, 128, "bf16", "bf16", [64, 5000, 10239]),
 ]
 
 

@@ -268,6 +268,9 @@ csa_status csa_index_scores(const csa_buf* qI, const float* wI, const csa_buf* k
   if (HI < 1 || HI > 128) return fail(CSA_ERR_SHAPE, "HI=%d out of [1, 128]", HI);
   if (DI < 8 || DI > 512 || DI % 8) return fail(CSA_ERR_SHAPE, "DI=%d must be a multiple of 8 in [8, 512]", DI);
   if (qI->dtype == CSA_MXFP4 && DI % 32) return fail(CSA_ERR_SHAPE, "MXFP4 needs DI %% 32 == 0");
+  if (!aligned16(qI->data) || !aligned16(kI->data)) return fail(CSA_ERR_SHAPE, "qI and kI must be 16-byte aligned");
+  if (qI->dtype == CSA_MXFP4 && ((reinterpret_cast<uintptr_t>(qI->scale) | reinterpret_cast<uintptr_t>(kI->scale)) & 3))
+    return fail(CSA_ERR_SHAPE, "MXFP4 scale planes must be 4-byte aligned");
   if (B < 0 || Tq < 0 || N < 0) return fail(CSA_ERR_SHAPE, "sizes must be non-negative");
   if (kI_rows < N) return fail(CSA_ERR_SHAPE, "kI_rows < N");
   if (ratio < 1) return fail(CSA_ERR_SHAPE, "ratio must be >= 1");
@@ -418,6 +421,13 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     if (io->qI.dtype != io->ik_cache.dtype) return fail(CSA_ERR_DTYPE, "qI and ik_cache must share a dtype");
     if (L->HI < 1 || L->HI > 128 || L->DI < 8 || L->DI > 512 || L->DI % 8)
       return fail(CSA_ERR_SHAPE, "indexer shape HI=%d DI=%d unsupported", L->HI, L->DI);
+    if (io->qI.dtype == CSA_FP8MIX) return fail(CSA_ERR_DTYPE, "the indexer takes F32, BF16 or MXFP4");
+    if (io->qI.dtype == CSA_MXFP4 && L->DI % 32) return fail(CSA_ERR_SHAPE, "MXFP4 needs DI %% 32 == 0");
+    if (!aligned16(io->qI.data) || !aligned16(io->ik_cache.data))
+      return fail(CSA_ERR_SHAPE, "qI and ik_cache must be 16-byte aligned");
+    if (io->qI.dtype == CSA_MXFP4 &&
+        ((reinterpret_cast<uintptr_t>(io->qI.scale) | reinterpret_cast<uintptr_t>(io->ik_cache.scale)) & 3))
+      return fail(CSA_ERR_SHAPE, "MXFP4 scale planes must be 4-byte aligned");
   }
   const FwdPlan P = plan_forward(L, io->scores_out != nullptr, io->idx_out != nullptr);
   if (P.total > 0 && (!ws || ws_bytes < P.total))

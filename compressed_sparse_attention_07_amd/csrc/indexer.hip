@@ -12,8 +12,15 @@
 // cross-lane adds finish the sum over heads, and each lane stores one score of a
 // 64-entry run (one coalesced 256-byte store per iteration).
 //
-// The SIMT kernel (fp32, or shapes the MFMA tiling does not cover) computes one
-// score per thread with the token's queries staged in LDS.
+// MXFP4 path ([V4-CN] §3.4: the indexer QK in FP4): both operands are e2m1 codes with
+// an e8m0 scale per 32 elements, fed to v_mfma_scale_f32_16x16x128_f8f6f4.  Its operand
+// layout is the storage layout: lane (col, grp) holds 32 consecutive codes of row col
+// (16 bytes, element 2i in the low nibble of byte i) for elements 32 grp .. 32 grp + 31
+// of a 128-element step, plus that block's scale byte.  The products of the dequantized
+// values are exact in fp32; accumulation is fp32.
+//
+// The SIMT kernels (fp32, or shapes the MFMA tilings do not cover) compute one score
+// per thread with the token's queries staged (dequantized) in LDS.
 #include "device_common.h"
 #include "launch.h"
 
@@ -58,6 +65,48 @@ __global__ __launch_bounds__(kSimtThreads) void index_simt_kernel(IndexLaunch a)
       for (int h = 0; h < nh; ++h) {
         float dot = 0.f;
         for (int d = 0; d < a.DI; ++d) dot = fmaf(qs[h * a.DI + d], ld<T>(k, d), dot);
+        score = fmaf(ws[h0 + h], fmaxf(dot, 0.f), score);
+      }
+    }
+  }
+  if (s < a.N) a.scores[bt * a.N + s] = s < vis ? score : -INFINITY;
+}
+
+// MXFP4 keys and queries: dequantized element d of row r (codes [., DI/2], scales [., DI/32])
+__device__ __forceinline__ float mx_elem(const uint8_t* codes, const uint8_t* scales, int64_t r, int DI, int d) {
+  const uint8_t c = codes[r * (DI / 2) + d / 2];
+  const int code = (d & 1) ? (c >> 4) : (c & 15);
+  return ldexpf(e2m1_to_f32(code), static_cast<int>(scales[r * (DI / 32) + d / 32]) - 127);
+}
+
+__global__ __launch_bounds__(kSimtThreads) void index_simt_mxfp4_kernel(IndexLaunch a) {
+  __shared__ float qs[kSimtQ];
+  __shared__ float ws[128];
+  const int64_t bt = blockIdx.y;
+  const int64_t b = bt / a.Tq;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kSimtThreads + threadIdx.x;
+  const int64_t pos = a.q_pos[bt];
+  int64_t vis = pos / a.ratio;
+  if (vis > a.N) vis = a.N;
+  if (vis < 0) vis = 0;
+  const uint8_t* qc = static_cast<const uint8_t*>(a.qI.data);
+  const uint8_t* qsc = static_cast<const uint8_t*>(a.qI.scale);
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kI.data);
+  const uint8_t* ksc = static_cast<const uint8_t*>(a.kI.scale);
+  const int64_t krow = b * a.kI_rows + (s < vis ? s : 0);
+  for (int h = threadIdx.x; h < a.HI; h += kSimtThreads) ws[h] = a.wI[bt * a.HI + h];
+  const int hc = kSimtQ / a.DI;
+  float score = 0.f;
+  for (int h0 = 0; h0 < a.HI; h0 += hc) {
+    const int nh = min(hc, a.HI - h0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nh * a.DI; i += kSimtThreads)
+      qs[i] = mx_elem(qc, qsc, bt * a.HI + h0 + i / a.DI, a.DI, i % a.DI);
+    __syncthreads();
+    if (s < vis) {
+      for (int h = 0; h < nh; ++h) {
+        float dot = 0.f;
+        for (int d = 0; d < a.DI; ++d) dot = fmaf(qs[h * a.DI + d], mx_elem(kc, ksc, krow, a.DI, d), dot);
         score = fmaf(ws[h0 + h], fmaxf(dot, 0.f), score);
       }
     }
@@ -164,7 +213,125 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
   }
 }
 
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+
+// MXFP4 scores: HB head blocks of 16, KS4 steps of 128 elements (DI = 128 KS4).  One
+// wave per token and key range, as index_mfma_kernel.
+template <int HB, int KS4>
+__global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLaunch a, int keys_per_wave,
+                                                                          int64_t waves_per_token) {
+  constexpr int DI = 128 * KS4;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + (threadIdx.x >> 6);
+  const int64_t total = a.B * a.Tq * waves_per_token;
+  if (wave >= total) return;
+  const int64_t bt = wave / waves_per_token;
+  const int64_t b = bt / a.Tq;
+  const int64_t s_begin = (wave % waves_per_token) * keys_per_wave;
+  const int64_t s_end = min(s_begin + keys_per_wave, a.N);
+  const int64_t pos = a.q_pos[bt];
+  int64_t vis = pos / a.ratio;
+  vis = vis > a.N ? a.N : (vis < 0 ? 0 : vis);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  float* out = a.scores + bt * a.N;
+  const int64_t vis_end = min(s_end, vis);
+
+  // queries: A operand (rows = heads), codes and block scale per lane
+  v8i32 qa[HB][KS4];
+  int qsc[HB][KS4];
+  float w[HB][4];
+  if (s_begin < vis_end) {
+    const uint8_t* qc = static_cast<const uint8_t*>(a.qI.data) + bt * a.HI * (DI / 2);
+    const uint8_t* qs = static_cast<const uint8_t*>(a.qI.scale) + bt * a.HI * (DI / 32);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = hb * 16 + col;
+#pragma unroll
+      for (int ks = 0; ks < KS4; ++ks) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qc + h * (DI / 2) + ks * 64 + grp * 16);
+        qa[hb][ks] = v8i32{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z),
+                           static_cast<int>(v.w), 0, 0, 0, 0};
+        qsc[hb][ks] = qs[h * (DI / 32) + ks * 4 + grp];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[hb][r] = a.wI[bt * a.HI + hb * 16 + grp * 4 + r];
+    }
+  }
+
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kI.data) + b * a.kI_rows * (DI / 2);
+  const uint8_t* ksp = static_cast<const uint8_t*>(a.kI.scale) + b * a.kI_rows * (DI / 32);
+  // keys of 64 entries starting at s0: codes (B operand) and the 4 block scales per step
+  auto load = [&](uint4 (&kb)[kTiles][KS4], uint32_t (&ks4)[kTiles][KS4], int64_t s0) {
+#pragma unroll
+    for (int tI = 0; tI < kTiles; ++tI) {
+      int64_t s = s0 + tI * 16 + col;
+      if (s >= vis_end) s = vis_end - 1;  // clamp: in bounds, masked below
+#pragma unroll
+      for (int ks = 0; ks < KS4; ++ks) {
+        kb[tI][ks] = *reinterpret_cast<const uint4*>(kc + s * (DI / 2) + ks * 64 + grp * 16);
+        ks4[tI][ks] = *reinterpret_cast<const uint32_t*>(ksp + s * (DI / 32) + ks * 4);
+      }
+    }
+  };
+  auto score = [&](const uint4 (&kb)[kTiles][KS4], const uint32_t (&ks4)[kTiles][KS4], int64_t s0) {
+    float res = -INFINITY;
+    if (s0 < vis_end) {
+      float part[kTiles];
+#pragma unroll
+      for (int tI = 0; tI < kTiles; ++tI) {
+        float sc = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS4; ++ks) {
+            const uint4 v = kb[tI][ks];
+            const v8i32 bop = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z),
+                               static_cast<int>(v.w), 0, 0, 0, 0};
+            const int kscale = static_cast<int>((ks4[tI][ks] >> (8 * grp)) & 0xffu);
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb][ks], bop, acc, 4, 4, 0, qsc[hb][ks], 0,
+                                                                    kscale);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
+        }
+        sc += __shfl_xor(sc, 16, WAVE);
+        sc += __shfl_xor(sc, 32, WAVE);
+        part[tI] = sc;
+      }
+#pragma unroll
+      for (int tI = 0; tI < kTiles; ++tI)
+        if (grp == tI) res = part[tI];
+      if (s0 + lane >= vis_end) res = -INFINITY;
+    }
+    const int64_t s = s0 + lane;
+    if (s < s_end) out[s] = res;
+  };
+
+  constexpr int64_t kStep = 16 * kTiles;
+  uint4 kA[kTiles][KS4], kB[kTiles][KS4];
+  uint32_t sA[kTiles][KS4], sB[kTiles][KS4];
+  int64_t s0 = s_begin;
+  if (s0 < vis_end) load(kA, sA, s0);
+  for (; s0 < s_end; s0 += 2 * kStep) {
+    if (s0 + kStep < vis_end) load(kB, sB, s0 + kStep);
+    score(kA, sA, s0);
+    if (s0 + kStep >= s_end) break;
+    if (s0 + 2 * kStep < vis_end) load(kA, sA, s0 + 2 * kStep);
+    score(kB, sB, s0 + kStep);
+  }
+}
+
 typedef void (*MfmaKern)(IndexLaunch, int, int64_t);
+
+MfmaKern pick_mxfp4(int HB, int KS4) {
+#define CSA_MX(H_, K_) \
+  if (HB == H_ && KS4 == K_) return index_mxfp4_kernel<H_, K_>;
+  CSA_MX(1, 1) CSA_MX(2, 1) CSA_MX(4, 1) CSA_MX(8, 1) CSA_MX(1, 2) CSA_MX(2, 2) CSA_MX(4, 2)
+#undef CSA_MX
+  return nullptr;
+}
 
 template <int HB>
 MfmaKern pick_ks(int KS) {
@@ -193,6 +360,22 @@ MfmaKern pick_mfma(int HB, int KS) {
 
 int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
   if (L.B == 0 || L.Tq == 0 || L.N == 0) return 0;
+  if (L.qI.dtype == CSA_MXFP4) {
+    MfmaKern k = (L.HI % 16 == 0 && L.DI % 128 == 0) ? pick_mxfp4(L.HI / 16, L.DI / 128) : nullptr;
+    if (k) {
+      // MXFP4 keys are 68 bytes (DI = 128): longer ranges per wave for the same bytes
+      const int64_t tokens = L.B * L.Tq;
+      int kpw = 512;
+      while (kpw < 8192 && tokens * ((L.N + kpw - 1) / kpw) > 8192) kpw *= 2;
+      const int64_t wpt = (L.N + kpw - 1) / kpw;
+      const int64_t grid = (tokens * wpt + kWavesPerWG - 1) / kWavesPerWG;
+      hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(grid)), dim3(kWavesPerWG * WAVE), 0, stream, L, kpw, wpt);
+    } else {
+      dim3 grid(static_cast<uint32_t>((L.N + kSimtThreads - 1) / kSimtThreads), static_cast<uint32_t>(L.B * L.Tq));
+      hipLaunchKernelGGL(index_simt_mxfp4_kernel, grid, dim3(kSimtThreads), 0, stream, L);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   if (L.qI.dtype == CSA_BF16 && L.HI % 16 == 0 && L.DI % 32 == 0) {
     MfmaKern k = pick_mfma(L.HI / 16, L.DI / 32);
     if (k) {

@@ -150,6 +150,11 @@ INDEX_CASES = [
     (2, 3, 16, 32, 300, 4, "bf16"),
     (1, 4, 4, 32, 77, 4, "bf16"),
     (1, 6, 64, 128, 4100, 128, "bf16"),
+    # MXFP4 queries and keys: scaled fp4 MFMA (DI % 128 == 0, HI % 16 == 0), else the SIMT kernel
+    (2, 5, 64, 128, 1000, 4, "mxfp4"),
+    (1, 3, 16, 256, 300, 4, "mxfp4"),
+    (1, 6, 64, 128, 4100, 128, "mxfp4"),
+    (1, 4, 8, 64, 100, 4, "mxfp4"),
 ]
 
 
@@ -158,10 +163,24 @@ def test_index_scores(case):
     B, Tq, HI, DI, N, ratio, dt = case
     say(f"index_scores {case}")
     g = Gen(21 + N, DEV)
-    td = TD[dt]
-    qI = g.normal((B, Tq, HI, DI), qstd(DI), dtype=td)
-    wI = g.uniform((B, Tq, HI))
-    kI = g.normal((B, N + 3, DI), dtype=td)
+    if dt == "mxfp4":
+        # seeded fp32 Gaussians quantized on the GPU; the oracle reads the CPU quantizer's
+        # exact dequantized values (the two quantizers agree bit for bit)
+        q32 = g.normal((B, Tq, HI, DI), qstd(DI))
+        wI = g.uniform((B, Tq, HI))
+        k32 = g.normal((B, N + 3, DI))
+        qI = csa.Buf.empty((B, Tq, HI, DI), csa.CSA_MXFP4)
+        kI = csa.Buf.empty((B, N + 3, DI), csa.CSA_MXFP4)
+        csa.csa_quantize(q32, qI)
+        csa.csa_quantize(k32, kI)
+        q_o = Q.mxfp4_dequantize(*Q.mxfp4_quantize(q32.cpu().numpy()))
+        k_o = Q.mxfp4_dequantize(*Q.mxfp4_quantize(k32.cpu().numpy()))
+    else:
+        td = TD[dt]
+        qI = g.normal((B, Tq, HI, DI), qstd(DI), dtype=td)
+        wI = g.uniform((B, Tq, HI))
+        kI = g.normal((B, N + 3, DI), dtype=td)
+        q_o, k_o = f64(qI), f64(kI)
     pos = g.integers(0, ratio * N + 3 * ratio, (B, Tq))
     pos[:, 0] = 0
     pos[:, 1 % Tq] = ratio * (N // 2) + ratio - 1     # last token of a block: its own block stays hidden
@@ -171,7 +190,7 @@ def test_index_scores(case):
     torch.cuda.synchronize()
     got = scores.cpu().numpy().astype(np.float64)
     for b in range(B):
-        want = O.index_scores(f64(qI[b]), f64(wI[b]), f64(kI[b, :N]), pos[b].cpu().numpy(), ratio)
+        want = O.index_scores(q_o[b], f64(wI[b]), k_o[b, :N], pos[b].cpu().numpy(), ratio)
         assert np.array_equal(np.isneginf(got[b]), np.isneginf(want)), "mask differs"
         fin = np.isfinite(want)
         assert_close(got[b][fin], want[fin], "f32", f"scores b={b}")

@@ -1,22 +1,32 @@
 #!/usr/bin/env python3
-"""Benchmark of the CSA decode step at 128K context on one MI355X.
+"""Benchmark of the CSA / HCA attention forward on one MI355X.
 
-Workload (the headline configuration): B = 16 sequences, 131,072 tokens of context
-each, CSA with m = 4 (32,768 compressed entries per sequence), shared KV dim 512
-(last 64 dims RoPE), lightning indexer 64 heads x 128, top-k 1024, 128 query heads
-x 512, window 128, bf16.  Inputs are seeded synthetic tensors (synth module); the
-KV and indexer-key caches are built by csa_compress from each sequence's streams
-before timing.
+Default workload (the headline): CSA decode at 128K context.
+- B = 16 sequences, 131,072 tokens of context each.
+- m = 4, so 32,768 compressed entries per sequence.
+- Shared KV dim 512, with the last 64 dims RoPE'd.
+- Lightning indexer 64 heads x 128, top-k 1024.
+- 128 query heads x 512, window 128, bf16.
 
-One step = one csa_forward call for the new token of every sequence: compress the
-newest 4-token block (one entry per sequence; a real decoder does this every 4th
-step, so this over-counts), score all 32,768 entries, select the top 1024, and
-attend over them plus the 128-token window.  Each step uses the caches of a
-different "layer" (--layers copies, cycled) so that caches are read from HBM, not
-from the 256 MB Infinity Cache, as in a multi-layer decode.
+A decode step serves one new token per sequence with one csa_forward call: score
+every entry, select the top 1024, and attend over them plus the window. Every 4th
+step also compresses the newest 4-token block (KV and indexer key, one entry per
+sequence), as a decoder does once per block. Steps cycle over --layers copies of
+the caches, so the caches are read from HBM rather than the 256 MB Infinity Cache,
+as in a multi-layer decode.
 
-Prints one JSON line (see the keys below).  Stage times are measured with HIP
-events on the stream the kernels run on.
+Other workloads (--config):
+- 2:  CSA chunked prefill, 1M context, the last 2048 tokens as queries.
+- 3d: HCA decode, B = 32, 1M context each (8192 entries).
+- 3p: HCA 2048-token prefill chunk at 1M context.
+- 4:  mixed-precision CSA decode, B = 8, 1M context, FP8-mixed KV cache, MXFP4
+      indexer.
+
+Inputs are seeded synthetic tensors (module synth). Caches are built by
+csa_compress before timing (config 4: seeded fp32 Gaussians quantized directly).
+
+Prints one JSON line. Stage times are measured with HIP events on the stream the
+kernels run on.
 """
 
 from __future__ import annotations
@@ -24,19 +34,23 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
+from dataclasses import dataclass, field
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12            # B/s, MI355X published
 MFMA_BF16_PEAK = 2.5e15      # FLOP/s dense bf16, MI355X published
-COPY_PROBE_BYTES = 1 << 30  # bytes read (and written) by one copy-probe launch
-WORKLOAD_TAG = "csa_decode_b16_ctx128k"
+MFMA_FP4_PEAK = 10.1e15      # FLOP/s dense fp4 / MXFP4
+COPY_PROBE_BYTES = 1 << 30   # bytes read (and written) by one copy-probe launch
 METRIC = "CSA decode tokens/s @128K ctx; indexer+MQA % MFMA peak, compress/top-k % HBM"
+
+WORKLOAD_TAGS = {"1": "csa_decode_b16_ctx128k", "2": "csa_prefill_t2048_ctx1m", "3d": "hca_decode_b32_ctx1m",
+                 "3p": "hca_prefill_t2048_ctx1m", "4": "csa_decode_b8_ctx1m_fp8kv_mxfp4idx"}
+WORKLOAD_TAG = WORKLOAD_TAGS["1"]
 
 
 def log(msg):
@@ -66,6 +80,321 @@ def read_traffic(kernel_file: str, src: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
+# ============================================================================ workloads
+
+
+@dataclass
+class Stage:
+    run: object                 # fn(i) launching the stage on layer i % layers
+    bytes: float                # algorithmic bytes per launch
+    flops: float                # algorithmic FLOP per launch
+    kernel: str                 # dominant kernel's name prefix
+    src: tuple                  # its source files
+    peak_flops: float = MFMA_BF16_PEAK
+
+
+@dataclass
+class Workload:
+    key: str
+    name: str
+    cfg: object
+    tokens: int                 # query tokens served per step
+    desc_full: object           # csa_layer_desc of a step that compresses (T > 0), or None
+    desc_attend: object         # csa_layer_desc of a step without compression
+    ios: list                   # per layer: csa_forward io dict
+    compress_every: int         # 1: every step compresses; 4: every 4th; 0: never
+    ws: object = None
+    stages: dict = field(default_factory=dict)
+    build: dict = field(default_factory=dict)
+    meta: dict = field(default_factory=dict)
+
+    def step(self, i):
+        import compressed_sparse_attention_07_amd as csa
+        io = self.ios[i % len(self.ios)]
+        full = self.compress_every and (i % self.compress_every == 0)
+        csa.csa_forward(self.desc_full if full else self.desc_attend, io, ws=self.ws)
+
+
+def _copy_buf(dst, src):
+    dst.data.copy_(src.data)
+    if src.rope is not None:
+        dst.rope.copy_(src.rope)
+    if src.scale is not None:
+        dst.scale.copy_(src.scale)
+
+
+def _seq(buf, b):
+    """csa_buf view of sequence b of a [B, rows, D] buffer (as a batch of one)."""
+    import compressed_sparse_attention_07_amd as csa
+    sl = lambda t: None if t is None else t[b:b + 1]
+    return csa.Buf(buf.dtype, sl(buf.data), sl(buf.rope), sl(buf.scale))
+
+
+def _compress_bulk(csa, g, cache, b, tokens, D, m, overlap, R, base, chunk, bf, timer):
+    """Compress tokens [0, tokens) of sequence b into cache rows [0, tokens/m), in chunks.
+
+    Streams are drawn chunk by chunk from g; the previous block of each chunk is the
+    tail of the one before.  Returns (seconds, bytes) spent in csa_compress."""
+    secs, nbytes = 0.0, 0
+    prev = None
+    for c0 in range(0, tokens, chunk):
+        T = min(chunk, tokens - c0)
+        n_st = 4 if overlap else 2
+        s = [g.normal((1, T, D), dtype=bf) for _ in range(n_st)]
+        dst = _seq(cache, b)
+        kw = dict(ratio=m, overlap=overlap, t0=c0, rope_dims=R, rope_base=base)
+        if overlap:
+            ca, cb, za, zb = s
+            if c0 > 0:
+                kw.update(prev_cb=prev[0], prev_zb=prev[1])
+        else:
+            ca, za = s
+            cb = zb = None
+        t = timer()
+        csa.csa_compress(ca, cb, za, zb, dst, **kw)
+        secs += timer(t)
+        nbytes += n_st * T * D * 2 + (T // m) * D * 2
+        if overlap:
+            prev = (cb[:, T - m:].contiguous(), zb[:, T - m:].contiguous())
+        del s
+    return secs, nbytes
+
+
+def _event_timer():
+    import torch
+
+    def timer(start=None):
+        if start is None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            return e0
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(e1) * 1e-3
+    return timer
+
+
+def build_workload(key: str, layers: int, dev: str = "cuda") -> Workload:
+    """Inputs, caches and forward descriptors of one workload (see the module docstring)."""
+    import torch
+
+    import compressed_sparse_attention_07_amd as csa
+    from synth import CONFIGS, Gen, qstd
+
+    bf = torch.bfloat16
+    timer = _event_timer()
+    cfgid = {"1": 1, "2": 2, "3d": 3, "3p": 3, "4": 4}[key]
+    cfg = CONFIGS[cfgid]
+    D, R, HI, DI, k, H, W = cfg.D, cfg.R, cfg.HI, cfg.DI, cfg.k, cfg.H, cfg.n_win
+    m, ctx, base = cfg.m, cfg.ctx, cfg.rope_base
+    hca = cfg.mode == "hca"
+    B = {"1": cfg.B, "2": 1, "3d": 32, "3p": 1, "4": cfg.B}[key]
+    Tq = {"1": 1, "2": 2048, "3d": 1, "3p": 2048, "4": 1}[key]
+    decode = Tq == 1
+    L = max(1, layers)
+    N = ctx // m
+    kv_fmt = csa.CSA_FP8MIX if cfg.kv_format == "fp8mix" else csa.CSA_BF16
+    ik_fmt = csa.CSA_MXFP4 if cfg.ik_format == "mxfp4" else csa.CSA_BF16
+
+    # ------------------------------------------------------------------ caches (layer 0)
+    kv0 = csa.Buf.empty((B, N, D), kv_fmt, rope_dims=R if kv_fmt == csa.CSA_FP8MIX else 0)
+    ik0 = None if hca else csa.Buf.empty((B, N, DI), ik_fmt)
+    # decode: the step recompresses the newest block (t0 = ctx - m); prefill: the last 2048 tokens
+    T_step = 0 if key in ("3d", "4") else (m if decode else Tq)
+    t0 = ctx - T_step
+    build_secs, build_bytes = 0.0, 0
+    log(f"[{key}] building caches: B={B} ctx={ctx} N={N} layers={L}")
+    for b in range(B):
+        g = Gen(cfg.seed * 1000 + b, dev)
+        if key == "4":
+            # seeded fp32 Gaussians quantized directly into the storage formats
+            for r0 in range(0, N, 1 << 16):
+                r1 = min(N, r0 + (1 << 16))
+                x = g.normal((r1 - r0, D))
+                csa.csa_quantize(x, csa.Buf(kv0.dtype, kv0.data[b, r0:r1], kv0.rope[b, r0:r1], kv0.scale[b, r0:r1]),
+                                 rope_dims=R)
+                xi = g.normal((r1 - r0, DI))
+                csa.csa_quantize(xi, csa.Buf(ik0.dtype, ik0.data[b, r0:r1], None, ik0.scale[b, r0:r1]))
+            continue
+        tokens = t0 if T_step else ctx
+        chunk = 1 << 17
+        sec, nb = _compress_bulk(csa, g, kv0, b, tokens, D, m, not hca, R, base, chunk, bf, timer)
+        build_secs += sec
+        build_bytes += nb
+        if not hca:
+            sec, nb = _compress_bulk(csa, g, ik0, b, tokens, DI, m, True, 0, base, chunk, bf, timer)
+            build_secs += sec
+            build_bytes += nb
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ step inputs
+    g = Gen(cfg.seed, dev)
+    pos = (torch.full((B, Tq), ctx, dtype=torch.int64, device=dev) if decode else
+           torch.arange(ctx - Tq, ctx, dtype=torch.int64, device=dev).expand(B, Tq).contiguous())
+    p_last = ctx if decode else ctx - 1
+    p_first = ctx if decode else ctx - Tq
+    wfirst = max(0, p_first - W + 1)
+    Tw = p_last - wfirst + 1
+    ios = []
+    for li in range(L):
+        if li == 0:
+            kv, ik = kv0, ik0
+        else:
+            kv = csa.Buf.empty((B, N, D), kv_fmt, rope_dims=R if kv_fmt == csa.CSA_FP8MIX else 0)
+            _copy_buf(kv, kv0)
+            ik = None
+            if not hca:
+                ik = csa.Buf.empty((B, N, DI), ik_fmt)
+                _copy_buf(ik, ik0)
+        io = dict(kv_cache=kv, q_pos=pos, win_pos0=torch.full((B,), wfirst, dtype=torch.int64, device=dev),
+                  q=g.normal((B, Tq, H, D), qstd(D), dtype=bf), sink=g.normal((H,)),
+                  out=torch.empty((B, Tq, H, D), dtype=bf, device=dev))
+        if T_step:
+            nst = 2 if hca else 4
+            st = [g.normal((B, T_step, D), dtype=bf) for _ in range(nst)]
+            prev = [g.normal((B, m, D), dtype=bf) for _ in range(2)] if not hca else [None, None]
+            io.update(ca=st[0], za=st[1] if hca else st[2])
+            if not hca:
+                io.update(cb=st[1], zb=st[3], prev_cb=prev[0], prev_zb=prev[1])
+                ist = [g.normal((B, T_step, DI), dtype=bf) for _ in range(4)]
+                iprev = [g.normal((B, m, DI), dtype=bf) for _ in range(2)]
+                io.update(ica=ist[0], icb=ist[1], iza=ist[2], izb=ist[3], iprev_cb=iprev[0], iprev_zb=iprev[1])
+        if kv_fmt == csa.CSA_FP8MIX:
+            win = csa.Buf.empty((B, Tw, D), kv_fmt, rope_dims=R)
+            csa.csa_quantize(g.normal((B, Tw, D)), win, rope_dims=R)
+        else:
+            win = g.normal((B, Tw, D), dtype=bf)
+        io["win"] = win
+        if not hca:
+            if ik_fmt == csa.CSA_MXFP4:
+                qI = csa.Buf.empty((B, Tq, HI, DI), ik_fmt)
+                csa.csa_quantize(g.normal((B, Tq, HI, DI), qstd(DI)), qI)
+            else:
+                qI = g.normal((B, Tq, HI, DI), qstd(DI), dtype=bf)
+            io.update(ik_cache=ik, qI=qI, wI=g.uniform((B, Tq, HI)))
+        ios.append(io)
+
+    def desc(T):
+        return csa.layer_desc(mode=csa.CSA_MODE_HCA if hca else csa.CSA_MODE_CSA, B=B, T=T, t0=ctx - T if T else ctx,
+                              Tq=Tq, cache_rows=N, Tw=Tw, D=D, H=H, HI=HI, DI=DI, ratio=m, topk=k, n_win=W,
+                              rope_dims=R, rope_base=base, softmax_scale=cfg.softmax_scale, pos_offset=0,
+                              stream_dtype=csa.CSA_BF16)
+
+    desc_full = desc(T_step) if T_step else None
+    desc_att = desc(0)
+    every = 0 if not T_step else (4 if decode else 1)
+    wl = Workload(key=key, name=WORKLOAD_TAGS[key], cfg=cfg, tokens=B * Tq, desc_full=desc_full,
+                  desc_attend=desc_att, ios=ios, compress_every=every)
+    need = csa.csa_forward_workspace_size(desc_full if desc_full is not None else desc_att)
+    wl.ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+    wl.meta = dict(B=B, Tq=Tq, ctx=ctx, m=m, N=N, D=D, R=R, HI=HI, DI=DI, k=k, H=H, W=W, T_step=T_step, Tw=Tw,
+                   kv_format=cfg.kv_format, ik_format=cfg.ik_format, mode=cfg.mode)
+    if build_secs > 0:
+        wl.build = dict(us=round(build_secs * 1e6, 1), bytes=build_bytes,
+                        GBps=round(build_bytes / build_secs / 1e9, 1),
+                        hbm_frac=round(build_bytes / build_secs / HBM_PEAK, 4))
+    _add_stages(wl, csa, torch, dev)
+    return wl
+
+
+def _add_stages(wl: Workload, csa, torch, dev):
+    """Per-stage launches with the step's shapes, and their algorithmic work."""
+    M = wl.meta
+    B, Tq, N, D, R, HI, DI, k, H, W, m = (M[x] for x in ("B", "Tq", "N", "D", "R", "HI", "DI", "k", "H", "W", "m"))
+    hca = M["mode"] == "hca"
+    T = M["T_step"]
+    ctx = M["ctx"]
+    L = len(wl.ios)
+    kv_entry = (D - R) + 2 * R + 4 if M["kv_format"] == "fp8mix" else 2 * D
+    ik_entry = DI // 2 + DI // 32 if M["ik_format"] == "mxfp4" else 2 * DI
+    q_entry = ik_entry
+    pos = wl.ios[0]["q_pos"].cpu()
+    vis = [[min(N, int(p) // m) for p in row] for row in pos.tolist()]
+    sum_vis = sum(sum(r) for r in vis)
+    cfg = wl.cfg
+
+    if T:
+        def st_compress(i):
+            io = wl.ios[i % L]
+            t0 = ctx - T
+            csa.csa_compress(io["ca"], io.get("cb"), io["za"], io.get("zb"), io["kv_cache"], ratio=m, overlap=not hca,
+                             t0=t0, prev_cb=io.get("prev_cb"), prev_zb=io.get("prev_zb"), rope_dims=R,
+                             rope_base=cfg.rope_base)
+            if not hca:
+                csa.csa_compress(io["ica"], io["icb"], io["iza"], io["izb"], io["ik_cache"], ratio=m, overlap=True,
+                                 t0=t0, prev_cb=io["iprev_cb"], prev_zb=io["iprev_zb"])
+        nst = 2 if hca else 4
+        cb = B * (nst * T * D * 2 + (T // m) * kv_entry)
+        if not hca:
+            cb += B * (4 * T * DI * 2 + (T // m) * ik_entry)
+        wl.stages["compress"] = Stage(st_compress, cb, 0.0, "compress_kernel", ("compress.hip",))
+
+    if not hca:
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+
+        def st_index(i):
+            io = wl.ios[i % L]
+            csa.csa_index_scores(io["qI"], io["wI"], io["ik_cache"], io["q_pos"], scores, ratio=m)
+
+        def st_topk(i):
+            csa.csa_topk(scores, k, idx)
+
+        mx = M["ik_format"] == "mxfp4"
+        wl.stages["index_scores"] = Stage(
+            st_index, B * N * ik_entry + B * Tq * (HI * q_entry + HI * 4 + N * 4), 2.0 * HI * DI * sum_vis,
+            "index_mxfp4_kernel" if mx else "index_mfma_kernel", ("indexer.hip",),
+            MFMA_FP4_PEAK if mx else MFMA_BF16_PEAK)
+        wl.stages["topk"] = Stage(st_topk, B * Tq * (N * 4 + k * 4), 0.0, "topk_kernel", ("topk.hip",))
+        mqa_ws = torch.empty(max(1, csa.lib().csa_sparse_mqa_workspace_size(B, Tq, H, D, k, W)), dtype=torch.uint8,
+                             device=dev)
+        outs = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=dev)
+
+        def st_attn(i):
+            io = wl.ios[i % L]
+            csa.csa_sparse_mqa(io["q"], io["q_pos"], io["kv_cache"], idx, io["win"], io["win_pos0"], io["sink"],
+                               outs, N=N, n_win=W, softmax_scale=cfg.softmax_scale, rope_dims=R,
+                               rope_base=cfg.rope_base, ws=mqa_ws)
+        keys = [min(k, v) + min(W, int(p) + 1) for row, prow in zip(vis, pos.tolist()) for v, p in zip(row, prow)]
+        # algorithmic bytes: every distinct entry once (a prefill chunk's selections overlap), q, out, indices
+        uniq = min(sum(keys), B * (N + M["Tw"]))
+        wl.stages["sparse_mqa"] = Stage(st_attn, uniq * kv_entry + B * Tq * (4 * H * D + 4 * k),
+                                        4.0 * H * D * sum(keys), "attn_", ("mqa.hip",))
+        wl.stages["_prime"] = Stage(lambda i: (st_index(i), st_topk(i)), 0, 0, "", ())
+    else:
+        mqa_ws = torch.empty(max(1, csa.lib().hca_dense_attn_workspace_size(B, Tq, H, D, N, W)), dtype=torch.uint8,
+                             device=dev)
+        outs = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=dev)
+
+        def st_attn(i):
+            io = wl.ios[i % L]
+            csa.hca_dense_attn(io["q"], io["q_pos"], io["kv_cache"], io["win"], io["win_pos0"], io["sink"], outs, N=N,
+                               ratio=m, n_win=W, softmax_scale=cfg.softmax_scale, rope_dims=R,
+                               rope_base=cfg.rope_base, ws=mqa_ws)
+        keys = [v + min(W, int(p) + 1) for row, prow in zip(vis, pos.tolist()) for v, p in zip(row, prow)]
+        uniq = B * (N + M["Tw"]) if Tq > 1 else sum(keys)
+        wl.stages["dense_attn"] = Stage(st_attn, uniq * kv_entry + B * Tq * 4 * H * D, 4.0 * H * D * sum(keys),
+                                        "attn_", ("mqa.hip",))
+
+
+def time_stage(fn, reps):
+    import torch
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e-3
+
+
+# ============================================================================ profiles
+
+
 def _short(name: str) -> str:
     return name.replace("(anonymous namespace)::", "").replace("void ", "").replace("csa::", "").split("(")[0]
 
@@ -77,21 +406,21 @@ def summarize_trace(db_path: str, out: str, command: str):
     rows = cur.execute("select name, count(*), avg(duration), min(duration), max(duration), "
                        "sum(duration), avg(grid_x / workgroup_x) from kernels group by name "
                        "order by sum(duration) desc").fetchall()
-    lines = [f"# rocprofv3 kernel-trace summary", f"# command: {command}",
+    lines = ["# rocprofv3 kernel-trace summary", f"# command: {command}",
              f"# {'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s} {'wgs':>7s}"]
     for n, c, av, mn, mx, tot, wgs in rows:
         lines.append(f"{_short(n)[:60]:60s} {c:6d} {av / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} "
                      f"{tot / 1e3:10.1f} {wgs:7.0f}")
     open(out, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines[:14]))
+    print("\n".join(lines[:16]))
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: str, command: str):
+def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: str, command: str, workload: str):
     """HBM traffic per launch of `kernel` from FETCH_SIZE / WRITE_SIZE counter runs.
 
     Both counters (KiB per dispatch) are scaled by what they read for the copy probe
     (torch.neg over 1 GiB: 1 GiB read, 1 GiB written).  Dispatches of `kernel` are
-    grouped by grid size and the most frequent grid (the decode step's) is reported.
+    grouped by grid size and the most frequent grid (the timed step's) is reported.
     """
     import collections
     import csv
@@ -113,14 +442,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: st
     write, pw = load(write_csv, "WRITE_SIZE")
     if not pf or not pw or not fetch:
         raise SystemExit(f"missing probe or kernel dispatches (probe {len(pf)}/{len(pw)}, kernel {len(fetch)})")
-    key = max(fetch, key=lambda k: len(fetch[k]))
+    key = max(fetch, key=lambda kk: len(fetch[kk]))
     kib = COPY_PROBE_BYTES / 1024
     f_fac = kib / (sum(pf) / len(pf))
     w_fac = kib / (sum(pw) / len(pw))
     f_avg = sum(fetch[key]) / len(fetch[key])
     w_avg = sum(write[key]) / len(write[key]) if write.get(key) else 0.0
     traffic = (f_avg * f_fac + w_avg * w_fac) * 1024
-    lines = [f"# HBM traffic per launch of {key[0]} (grid {key[1]} threads), decode step of the headline workload",
+    lines = [f"# HBM traffic per launch of {key[0]} (most frequent grid: {key[1]} threads), workload {workload}",
              f"# command (FETCH_SIZE pass): {command.replace('@COUNTER@', 'FETCH_SIZE')}",
              f"# command (WRITE_SIZE pass): {command.replace('@COUNTER@', 'WRITE_SIZE')}",
              f"# summarised by: python bench.py --summarize-pmc <fetch.csv> <write.csv> --kernel {kernel}",
@@ -133,25 +462,30 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: st
     print("\n".join(lines))
 
 
-KERNEL_SOURCES = {"attn_mfma_kernel": ("mqa.hip",), "attn_combine_kernel": ("mqa.hip",),
-                  "index_mfma_kernel": ("indexer.hip",), "topk_kernel": ("topk.hip",),
+KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip",),
+                  "attn_combine_kernel": ("mqa.hip",), "index_mfma_kernel": ("indexer.hip",),
+                  "index_mxfp4_kernel": ("indexer.hip",), "topk_kernel": ("topk.hip",),
                   "compress_kernel": ("compress.hip",)}
+
+
+# ============================================================================ main
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layers", type=int, default=4)
-    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 48 decode, 6 prefill)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="1", choices=sorted(WORKLOAD_TAGS))
+    ap.add_argument("--layers", type=int, default=None, help="cache copies cycled over (default: 4 decode, 1 prefill)")
+    ap.add_argument("--stage-reps", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB device copy (PMC calibration)")
     ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write an HBM-traffic summary from two counter runs (no GPU work)")
-    ap.add_argument("--kernel", default="attn_mfma_kernel")
+    ap.add_argument("--kernel", default="attn_dma_kernel")
     ap.add_argument("--profile-cmd", default="", help="command recorded in the summary")
     ap.add_argument("--out", help="summary file")
     args = ap.parse_args()
@@ -159,9 +493,10 @@ def main():
         summarize_trace(args.summarize_trace, args.out, args.profile_cmd)
         return
     if args.summarize_pmc:
-        out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{WORKLOAD_TAG}_pmc.txt")
+        tag = WORKLOAD_TAGS[args.config]
+        out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{tag}_pmc.txt")
         summarize_pmc(*args.summarize_pmc, args.kernel, src_hash(*KERNEL_SOURCES[args.kernel]), out,
-                      args.profile_cmd)
+                      args.profile_cmd, tag)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -171,213 +506,113 @@ def main():
     import torch
 
     import compressed_sparse_attention_07_amd as csa
-    from synth import CONFIGS, Gen, qstd
 
     if not os.path.exists(csa.LIB_PATH):
         from compressed_sparse_attention_07_amd import build
         build.build()
-    dev = "cuda"
     assert csa.lib().csa_device_check() == 0, csa.lib().csa_last_error()
-    cfg = CONFIGS[1]
-    B, ctx, m, D, R, HI, DI, k, H, W = cfg.B, cfg.ctx, cfg.m, cfg.D, cfg.R, cfg.HI, cfg.DI, cfg.k, cfg.H, cfg.n_win
-    N = ctx // m
-    bf = torch.bfloat16
-    L = max(1, args.layers)
-    t_new = ctx                      # position of the new token
-    t0 = ctx - m                     # the newest complete block, recompressed every step
+    decode = args.config in ("1", "3d", "4")
+    steps = args.steps if args.steps is not None else (48 if decode else 6)
+    warmup = args.warmup if args.warmup is not None else (8 if decode else 2)
+    layers = args.layers if args.layers is not None else (4 if decode else 1)
+    reps = args.stage_reps if args.stage_reps is not None else (20 if decode else 4)
 
-    # ---------------------------------------------------------------- caches
-    log(f"building caches: B={B} ctx={ctx} N={N} layers={L}")
-    kv = [csa.Buf.empty((B, N, D), csa.CSA_BF16) for _ in range(L)]
-    ik = [csa.Buf.empty((B, N, DI), csa.CSA_BF16) for _ in range(L)]
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    build_ms = 0.0
-    build_bytes = 0
-    for b in range(B):
-        g = Gen(cfg.seed * 1000 + b, dev)
-        s = [g.normal((1, ctx, D), dtype=bf) for _ in range(4)]
-        si = [g.normal((1, ctx, DI), dtype=bf) for _ in range(4)]
-        e0, e1 = ev(), ev()
-        e0.record()
-        csa.csa_compress(s[0], s[1], s[2], s[3], _seq(kv[0], b), ratio=m,
-                         overlap=True, rope_dims=R, rope_base=cfg.rope_base)
-        csa.csa_compress(si[0], si[1], si[2], si[3], _seq(ik[0], b), ratio=m, overlap=True)
-        e1.record()
-        torch.cuda.synchronize()
-        build_ms += e0.elapsed_time(e1)
-        build_bytes += 4 * ctx * (D + DI) * 2 + N * (D + DI) * 2
-        del s, si
-    for li in range(1, L):
-        kv[li].data.copy_(kv[0].data)
-        ik[li].data.copy_(ik[0].data)
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- step inputs
-    g = Gen(cfg.seed, dev)
-    steps_in = []
-    for li in range(L):
-        d = dict(
-            ca=g.normal((B, m, D), dtype=bf), cb=g.normal((B, m, D), dtype=bf), za=g.normal((B, m, D), dtype=bf),
-            zb=g.normal((B, m, D), dtype=bf), prev_cb=g.normal((B, m, D), dtype=bf),
-            prev_zb=g.normal((B, m, D), dtype=bf),
-            ica=g.normal((B, m, DI), dtype=bf), icb=g.normal((B, m, DI), dtype=bf),
-            iza=g.normal((B, m, DI), dtype=bf), izb=g.normal((B, m, DI), dtype=bf),
-            iprev_cb=g.normal((B, m, DI), dtype=bf), iprev_zb=g.normal((B, m, DI), dtype=bf),
-            q=g.normal((B, 1, H, D), qstd(D), dtype=bf), qI=g.normal((B, 1, HI, DI), qstd(DI), dtype=bf),
-            wI=g.uniform((B, 1, HI)), win=g.normal((B, W, D), dtype=bf), sink=g.normal((H,)),
-        )
-        d.update(kv_cache=kv[li], ik_cache=ik[li], q_pos=torch.full((B, 1), t_new, dtype=torch.int64, device=dev),
-                 win_pos0=torch.full((B,), t_new - W + 1, dtype=torch.int64, device=dev),
-                 out=torch.empty((B, 1, H, D), dtype=bf, device=dev))
-        steps_in.append(d)
-    desc = csa.layer_desc(mode=csa.CSA_MODE_CSA, B=B, T=m, t0=t0, Tq=1, cache_rows=N, Tw=W, D=D, H=H, HI=HI, DI=DI,
-                          ratio=m, topk=k, n_win=W, rope_dims=R, rope_base=cfg.rope_base,
-                          softmax_scale=cfg.softmax_scale, pos_offset=0, stream_dtype=csa.CSA_BF16)
-    ws = torch.empty(csa.csa_forward_workspace_size(desc), dtype=torch.uint8, device=dev)
-
-    def step(i):
-        csa.csa_forward(desc, steps_in[i % L], ws=ws)
+    wl = build_workload(args.config, layers)
 
     # ---------------------------------------------------------------- timed steps
-    for i in range(args.warmup):
-        step(i)
+    for i in range(warmup):
+        wl.step(i)
     torch.cuda.synchronize()
-    e0, e1 = ev(), ev()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
-    for i in range(args.steps):
-        step(i)
+    for i in range(steps):
+        wl.step(i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    value = B / (ms_per_step * 1e-3)
-    log(f"decode step {ms_per_step * 1e3:.1f} us ({wall / args.steps * 1e6:.1f} us wall) -> {value:,.0f} tokens/s")
+    ms_per_step = e0.elapsed_time(e1) / steps
+    value = wl.tokens / (ms_per_step * 1e-3)
+    log(f"[{args.config}] step {ms_per_step * 1e3:.1f} us ({wall / steps * 1e6:.1f} us wall) -> {value:,.0f} tokens/s")
 
     # ---------------------------------------------------------------- stages
-    scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
-    outs = torch.empty((B, 1, H, D), dtype=bf, device=dev)
-    mqa_ws = torch.empty(max(1, csa.lib().csa_sparse_mqa_workspace_size(B, 1, H, D, k, W)), dtype=torch.uint8,
-                         device=dev)
-
-    def st_compress(i):
-        d = steps_in[i % L]
-        csa.csa_compress(d["ca"], d["cb"], d["za"], d["zb"], kv[i % L], ratio=m, overlap=True, t0=t0,
-                         prev_cb=d["prev_cb"], prev_zb=d["prev_zb"], rope_dims=R, rope_base=cfg.rope_base)
-        csa.csa_compress(d["ica"], d["icb"], d["iza"], d["izb"], ik[i % L], ratio=m, overlap=True, t0=t0,
-                         prev_cb=d["iprev_cb"], prev_zb=d["iprev_zb"])
-
-    def st_index(i):
-        d = steps_in[i % L]
-        csa.csa_index_scores(d["qI"], d["wI"], ik[i % L], d["q_pos"], scores, ratio=m)
-
-    def st_topk(i):
-        csa.csa_topk(scores, k, idx)
-
-    def st_mqa(i):
-        d = steps_in[i % L]
-        csa.csa_sparse_mqa(d["q"], d["q_pos"], kv[i % L], idx, d["win"], d["win_pos0"], d["sink"], outs, N=N,
-                           n_win=W, softmax_scale=cfg.softmax_scale, rope_dims=R, rope_base=cfg.rope_base, ws=mqa_ws)
-
-    def timeit(fn, reps):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        a, b_ = ev(), ev()
-        a.record()
-        for i in range(reps):
-            fn(i)
-        b_.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b_) / reps * 1e-3  # seconds per call
-
-    st_index(0)
-    st_topk(0)
+    if "_prime" in wl.stages:
+        wl.stages.pop("_prime").run(0)
     torch.cuda.synchronize()
-    reps = args.stage_reps
-    t_comp = timeit(st_compress, reps)
-    t_idx = timeit(st_index, reps)
-    t_topk = timeit(st_topk, reps)
-    t_mqa = timeit(st_mqa, reps)
-
-    # algorithmic work per launch (what the method must move / compute)
-    stages = {
-        "compress": dict(t=t_comp, bytes=B * (2 * m * 2 * (D + DI) * 2 + (D + DI) * 2), flops=0.0,
-                         kernel="compress_kernel", src=("compress.hip",)),
-        "index_scores": dict(t=t_idx, bytes=B * (N * DI * 2 + HI * DI * 2 + HI * 4 + N * 4),
-                             flops=2.0 * B * HI * DI * N, kernel="index_mfma_kernel", src=("indexer.hip",)),
-        "topk": dict(t=t_topk, bytes=B * (N * 4 + k * 4), flops=0.0, kernel="topk_kernel", src=("topk.hip",)),
-        "sparse_mqa": dict(t=t_mqa, bytes=B * ((k + W) * D * 2 + 2 * H * D * 2 + k * 4),
-                           flops=4.0 * B * H * (k + W) * D, kernel="attn_mfma_kernel", src=("mqa.hip",)),
-    }
     stage_out = {}
-    for name, s in stages.items():
-        gbs = s["bytes"] / s["t"] / 1e9
-        tfs = s["flops"] / s["t"] / 1e12
-        bound = "mfma" if s["flops"] / MFMA_BF16_PEAK > s["bytes"] / HBM_PEAK else "hbm"
-        stage_out[name] = dict(us=round(s["t"] * 1e6, 2), GBps=round(gbs, 1), TFLOPs=round(tfs, 2),
-                               hbm_frac=round(s["bytes"] / s["t"] / HBM_PEAK, 4),
-                               mfma_frac=round(s["flops"] / s["t"] / MFMA_BF16_PEAK, 4), bound=bound)
-        log(f"  {name:13s} {s['t'] * 1e6:8.2f} us  {gbs:8.1f} GB/s  {tfs:7.2f} TFLOP/s  ({bound}-bound)")
-    dom_name = max(stages, key=lambda n: stages[n]["t"])
-    dom = stages[dom_name]
+    times = {}
+    for name, s in wl.stages.items():
+        t = time_stage(s.run, reps)
+        times[name] = t
+        gbs = s.bytes / t / 1e9
+        tfs = s.flops / t / 1e12
+        bound = "mfma" if s.flops / s.peak_flops > s.bytes / HBM_PEAK else "hbm"
+        stage_out[name] = dict(us=round(t * 1e6, 2), GBps=round(gbs, 1), TFLOPs=round(tfs, 2),
+                               hbm_frac=round(s.bytes / t / HBM_PEAK, 4),
+                               mfma_frac=round(s.flops / t / s.peak_flops, 4), bound=bound,
+                               algorithmic_bytes=int(s.bytes), algorithmic_flops=int(s.flops))
+        log(f"  {name:13s} {t * 1e6:9.2f} us  {gbs:8.1f} GB/s  {tfs:7.2f} TFLOP/s  ({bound}-bound)")
+    dom_name = max(wl.stages, key=lambda n: times[n])
+    dom = wl.stages[dom_name]
     if stage_out[dom_name]["bound"] == "hbm":
-        achieved, peak, unit = dom["bytes"] / dom["t"] / 1e9, HBM_PEAK / 1e9, "GB/s"
+        achieved, peak, unit = dom.bytes / times[dom_name] / 1e9, HBM_PEAK / 1e9, "GB/s"
     else:
-        achieved, peak, unit = dom["flops"] / dom["t"] / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
-    traffic = read_traffic(f"{dom['kernel']}_{WORKLOAD_TAG}_pmc.txt", src_hash(*dom["src"]))
-    roofline = dict(kernel=dom["kernel"], stage=dom_name, bound=stage_out[dom_name]["bound"],
-                    achieved=round(achieved, 2), peak=peak, unit=unit, frac=round(achieved / peak, 4),
-                    traffic=traffic, algorithmic_bytes=dom["bytes"], avg_launch_us=round(dom["t"] * 1e6, 2))
+        achieved, peak, unit = dom.flops / times[dom_name] / 1e12, dom.peak_flops / 1e12, "TFLOP/s"
+    kern = dom.kernel
+    if kern == "attn_":
+        kern = "attn_dma_kernel" if wl.meta["kv_format"] != "fp8mix" else "attn_mfma_kernel"
+    traffic = read_traffic(f"{kern}_{wl.name}_pmc.txt", src_hash(*dom.src))
+    roofline = dict(kernel=kern, stage=dom_name, bound=stage_out[dom_name]["bound"], achieved=round(achieved, 2),
+                    peak=peak, unit=unit, frac=round(achieved / peak, 4), traffic=traffic,
+                    algorithmic_bytes=int(dom.bytes), algorithmic_flops=int(dom.flops),
+                    avg_launch_us=round(times[dom_name] * 1e6, 2))
 
     if args.copy_probe:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB): the
         # reference for scaling the FETCH_SIZE / WRITE_SIZE counters
-        src = torch.zeros(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        src = torch.zeros(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         log("copy probe: 3 x neg over 1 GiB done")
 
-    # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_seconds, dev)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
 
-    cache_build = dict(us=round(build_ms * 1e3, 1), GBps=round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
-                       hbm_frac=round(build_bytes / (build_ms * 1e-3) / HBM_PEAK, 4),
-                       bytes=build_bytes)
+    M = wl.meta
+    config = {"workload": wl.cfg.name if args.config in ("1", "2", "4") else
+              ("HCA decode bf16, B=32, 1M context, m'=128, D=512, H=128" if args.config == "3d" else
+               "HCA prefill bf16, 2048-token chunk at 1M context, m'=128, D=512, H=128"),
+              "B": M["B"], "context": M["ctx"], "query_tokens_per_seq": M["Tq"], "m": M["m"], "entries": M["N"],
+              "D": M["D"], "rope_dims": M["R"], "heads": M["H"], "window": M["W"], "kv_format": M["kv_format"],
+              "layers_cycled": len(wl.ios)}
+    if M["mode"] == "csa":
+        config.update(indexer=f"{M['HI']}x{M['DI']}", topk=M["k"], ik_format=M["ik_format"])
+    config["step"] = ("csa_forward per new token; the newest block is compressed every 4th step" if decode and
+                      wl.compress_every == 4 else
+                      "csa_forward over the chunk (compress + attend)" if not decode else "csa_forward (attend only)")
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "context": ctx, "m": m, "entries": N, "D": D, "rope_dims": R,
-                   "indexer": f"{HI}x{DI}", "topk": k, "heads": H, "window": W, "layers_cycled": L,
-                   "step": "csa_forward: compress newest block + index + top-k + sparse MQA"},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "stages": stage_out,
-        "cache_build_compress": cache_build,
+        "metric": METRIC if args.config == "1" else f"{wl.name} tokens/s; per-stage % of HBM / MFMA peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if M["kv_format"] != "fp8mix" else "bf16+fp8kv+mxfp4idx",
+        "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu, "stages": stage_out,
     }
+    if wl.build:
+        line["cache_build_compress"] = wl.build
     print(json.dumps(line), flush=True)
 
 
-def _seq(buf, b):
-    """csa_buf view of sequence b of a [B, rows, D] buffer (as a batch of one)."""
-    import compressed_sparse_attention_07_amd as csa
-    sl = lambda t: None if t is None else t[b:b + 1]
-    return csa.Buf(buf.dtype, sl(buf.data), sl(buf.rope), sl(buf.scale))
+def cpu_baseline(wl: Workload, seconds: float):
+    """Time the fp64 oracle on a bounded sample of the workload, for about `seconds`.
 
-
-def cpu_baseline(cfg, seconds, dev):
-    """Time the fp64 oracle's decode step (same workload) for about `seconds` of CPU work.
-
-    The oracle builds sequence 0's caches from the same seeded streams (untimed).
-    Then decode steps with fresh seeded inputs (new block, queries, window, sink)
-    are timed one after another -- compress the newest block, score every entry,
-    top-k, MQA over the selection and the window -- until `seconds` have been spent.
+    Decode: the oracle builds one sequence's caches from the same seeded streams
+    (untimed), then times decode steps with fresh seeded inputs -- compress the newest
+    block, score every entry, top-k, MQA over the selection and the window.
+    Other workloads: the oracle's per-query work (index scores, top-k, attention) for
+    a sample of query tokens over the GPU-built caches, read back once.
     """
     import numpy as np
     import torch
@@ -392,47 +627,97 @@ def cpu_baseline(cfg, seconds, dev):
         threads = 1
     cores = len(os.sched_getaffinity(0))
     f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
-    m, D, R, ctx, DI, W = cfg.m, cfg.D, cfg.R, cfg.ctx, cfg.DI, cfg.n_win
+    M, cfg = wl.meta, wl.cfg
+    m, D, R, ctx, DI, W, H, HI, k = M["m"], M["D"], M["R"], M["ctx"], M["DI"], M["W"], M["H"], M["HI"], M["k"]
     bf = torch.bfloat16
-    t0 = ctx - m
-    g = Gen(cfg.seed * 1000, dev)
-    s = [f(g.normal((1, ctx, D), dtype=bf)[0]) for _ in range(4)]
-    si = [f(g.normal((1, ctx, DI), dtype=bf)[0]) for _ in range(4)]
-    log("cpu baseline: oracle cache build for sequence 0 (untimed)")
-    kv = O.compress(*s, ratio=m, overlap=True, rope_dims=R, rope_base=cfg.rope_base)
-    ik = O.compress(*si, ratio=m, overlap=True)
-    del s, si
-    pos = np.array([ctx])
     total, steps = 0.0, 0
-    while total < seconds and steps < 100000:
-        g = Gen(cfg.seed * 7919 + steps, dev)
-        blk = [f(g.normal((m, D), dtype=bf)) for _ in range(6)]
-        iblk = [f(g.normal((m, DI), dtype=bf)) for _ in range(6)]
-        q = f(g.normal((1, cfg.H, D), qstd(D), dtype=bf))
-        qI = f(g.normal((1, cfg.HI, DI), qstd(DI), dtype=bf))
-        wI = f(g.uniform((1, cfg.HI)))
-        win = f(g.normal((W, D), dtype=bf))
-        sink = f(g.normal((cfg.H,)))
-        tic = time.perf_counter()
-        e = O.compress(*blk[:4], ratio=m, overlap=True, t0=t0, prev_cb=blk[4], prev_zb=blk[5], rope_dims=R,
-                       rope_base=cfg.rope_base)
-        kv[-1] = e[0]
-        ei = O.compress(*iblk[:4], ratio=m, overlap=True, t0=t0, prev_cb=iblk[4], prev_zb=iblk[5])
-        ik[-1] = ei[0]
-        sc = O.index_scores(qI, wI, ik, pos, m)
-        idx, _ = O.topk(sc, cfg.k)
-        O.mqa(q, pos, kv, idx, win, ctx - W + 1, W, sink, scale=cfg.softmax_scale, rope_dims=R,
-              rope_base=cfg.rope_base)
-        total += time.perf_counter() - tic
-        steps += 1
+    if wl.key == "1":
+        t0 = ctx - m
+        g = Gen(cfg.seed * 1000, "cuda")
+        s = [f(g.normal((1, ctx, D), dtype=bf)[0]) for _ in range(4)]
+        si = [f(g.normal((1, ctx, DI), dtype=bf)[0]) for _ in range(4)]
+        log("cpu baseline: oracle cache build for sequence 0 (untimed)")
+        kv = O.compress(*s, ratio=m, overlap=True, rope_dims=R, rope_base=cfg.rope_base)
+        ik = O.compress(*si, ratio=m, overlap=True)
+        del s, si
+        pos = np.array([ctx])
+        while total < seconds and steps < 100000:
+            g = Gen(cfg.seed * 7919 + steps, "cuda")
+            blk = [f(g.normal((m, D), dtype=bf)) for _ in range(6)]
+            iblk = [f(g.normal((m, DI), dtype=bf)) for _ in range(6)]
+            q = f(g.normal((1, H, D), qstd(D), dtype=bf))
+            qI = f(g.normal((1, HI, DI), qstd(DI), dtype=bf))
+            wI = f(g.uniform((1, HI)))
+            win = f(g.normal((W, D), dtype=bf))
+            sink = f(g.normal((H,)))
+            tic = time.perf_counter()
+            if steps % 4 == 0:  # the newest block, every 4th step as in the timed loop
+                e = O.compress(*blk[:4], ratio=m, overlap=True, t0=t0, prev_cb=blk[4], prev_zb=blk[5],
+                               rope_dims=R, rope_base=cfg.rope_base)
+                kv[-1] = e[0]
+                ei = O.compress(*iblk[:4], ratio=m, overlap=True, t0=t0, prev_cb=iblk[4], prev_zb=iblk[5])
+                ik[-1] = ei[0]
+            sc = O.index_scores(qI, wI, ik, pos, m)
+            idx, _ = O.topk(sc, k)
+            O.mqa(q, pos, kv, idx, win, ctx - W + 1, W, sink, scale=cfg.softmax_scale, rope_dims=R,
+                  rope_base=cfg.rope_base)
+            total += time.perf_counter() - tic
+            steps += 1
+        sample = (f"{steps} decode steps of sequence 0 (fresh seeded block, queries, window and sink per step; the "
+                  f"block compressed every 4th step): score {ctx // m} entries, top-{k}, MQA over {k}+{W} keys; the "
+                  "oracle's caches are built once, untimed")
+    else:
+        from oracle import quant as Q
+        io = wl.ios[0]
+        hca = M["mode"] == "hca"
+
+        def deq(buf, b):
+            if buf.dtype == 2:  # FP8MIX
+                return Q.fp8mix_dequantize(buf.data[b].cpu().numpy(), buf.rope[b].view(torch.int16).cpu().numpy()
+                                           .view(np.uint16), buf.scale[b].cpu().numpy())
+            if buf.dtype == 3:  # MXFP4
+                return Q.mxfp4_dequantize(buf.data[b].cpu().numpy(), buf.scale[b].cpu().numpy())
+            return f(buf.data[b])
+
+        def dense(x, b):
+            return deq(x, b) if not isinstance(x, torch.Tensor) else f(x[b])
+        Tq, B = M["Tq"], M["B"]
+        order = np.random.default_rng(0).permutation(Tq)
+        for b in range(B):
+            if total >= seconds:
+                break
+            log(f"cpu baseline: reading caches of sequence {b} back (untimed)")
+            kv = deq(io["kv_cache"], b)
+            ik = None if hca else deq(io["ik_cache"], b)
+            qI_all = None if hca else dense(io["qI"], b)
+            pos = io["q_pos"][b].cpu().numpy()
+            win = dense(io["win"], b)
+            wp0 = int(io["win_pos0"][b])
+            sink = f(io["sink"])
+            for t in order:
+                if total >= seconds:
+                    break
+                t = int(t)
+                q = f(io["q"][b, t:t + 1])
+                p = pos[t:t + 1]
+                tic = time.perf_counter()
+                if hca:
+                    O.hca_dense(q, p, kv, win, wp0, W, sink, ratio=m, scale=cfg.softmax_scale, rope_dims=R,
+                                rope_base=cfg.rope_base)
+                else:
+                    sc = O.index_scores(qI_all[t:t + 1], f(io["wI"][b, t:t + 1]), ik, p, m)
+                    idx, _ = O.topk(sc, k)
+                    O.mqa(q, p, kv, idx, win, wp0, W, sink, scale=cfg.softmax_scale, rope_dims=R,
+                          rope_base=cfg.rope_base)
+                total += time.perf_counter() - tic
+                steps += 1
+            del kv, ik
+        sample = (f"{steps} query tokens ({'dense attention' if hca else 'index, top-k, MQA'}) over the GPU-built "
+                  "caches, read back per sequence untimed; the chunk's compression is not in the sample")
     rate = steps / total
-    log(f"cpu baseline: {steps} decode steps in {total:.2f} s -> {rate:.2f} tokens/s ({threads} BLAS threads, "
-        f"{cores} cores)")
+    log(f"cpu baseline: {steps} units in {total:.2f} s -> {rate:.2f} tokens/s ({threads} BLAS threads, {cores} cores)")
     return dict(value=round(rate, 3), unit="tokens/s", cores=threads, host_cores=cores, kind="oracle",
-                seconds=round(total, 2),
-                sample=f"{steps} decode steps of sequence 0 (fresh seeded block, queries, window and sink per "
-                       f"step): compress the newest block, score {ctx // m} entries, top-{cfg.k}, MQA over "
-                       f"{cfg.k}+{W} keys; the oracle's caches are built once, untimed")
+                seconds=round(total, 2), sample=sample)
 
 
 if __name__ == "__main__":

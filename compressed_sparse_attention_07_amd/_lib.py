@@ -262,20 +262,44 @@ def csa_forward_workspace_size(desc: csa_layer_desc) -> int:
     return lib().csa_forward_workspace_size(C.byref(desc))
 
 
-def csa_forward(desc: csa_layer_desc, io: dict, *, ws=None, stream=None) -> None:
-    """io maps csa_forward_io field names to tensors / Buf objects (missing = NULL)."""
+def _forward_io(io: dict) -> csa_forward_io:
     cio = csa_forward_io()
-    keep = []
     for name, val in io.items():
         if val is None:
             continue
         if isinstance(val, Buf) or (name in ("kv_cache", "ik_cache", "q", "qI", "win", "out")):
-            b = Buf.of(val).c()
-            keep.append(b)
-            setattr(cio, name, b)
+            setattr(cio, name, Buf.of(val).c())
         else:
             setattr(cio, name, ptr(val))
+    return cio
+
+
+def csa_forward(desc: csa_layer_desc, io: dict, *, ws=None, stream=None) -> None:
+    """io maps csa_forward_io field names to tensors / Buf objects (missing = NULL)."""
+    cio = _forward_io(io)
     need = csa_forward_workspace_size(desc)
     dev = Buf.of(io["q"]).data.device
     w, wbytes = _ws(need, dev, ws)
     check(lib().csa_forward(C.byref(desc), C.byref(cio), ptr(w), wbytes, stream_handle(stream)))
+
+
+class ForwardCall:
+    """A csa_forward call with its arguments marshalled once (for repeated launches).
+
+    Holds references to every tensor it points at; the call itself is one C call."""
+
+    def __init__(self, desc: csa_layer_desc, io: dict, *, ws=None, stream=None):
+        self.desc = desc
+        self.io = dict(io)
+        self.cio = _forward_io(self.io)
+        need = csa_forward_workspace_size(desc)
+        self.w, self.wbytes = _ws(need, Buf.of(io["q"]).data.device, ws)
+        self.wptr = ptr(self.w)
+        self.stream = stream_handle(stream)
+        self.fn = lib().csa_forward
+        self.args = (C.byref(self.desc), C.byref(self.cio), self.wptr, self.wbytes, self.stream)
+
+    def __call__(self) -> None:
+        st = self.fn(*self.args)
+        if st != 0:
+            check(st)

@@ -353,7 +353,7 @@ namespace {
 
 struct FwdPlan {
   int64_t N;
-  size_t scores_off, scores_bytes, idx_off, idx_bytes, attn_off, attn_bytes, total;
+  size_t scores_off, scores_bytes, idx_off, idx_bytes, topk_off, topk_bytes, attn_off, attn_bytes, total;
 };
 
 FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx) {
@@ -367,6 +367,9 @@ FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx) {
     p.idx_bytes = have_idx ? 0 : align256(static_cast<size_t>(L->B * L->Tq * L->topk) * sizeof(int32_t));
     p.idx_off = off;
     off += p.idx_bytes;
+    p.topk_bytes = align256(topk_workspace_bytes(L->B * L->Tq, p.N, L->topk));
+    p.topk_off = off;
+    off += p.topk_bytes;
     p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, static_cast<int64_t>(L->topk) + L->n_win, true));
   } else {
     p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, p.N + L->n_win, false));
@@ -495,7 +498,7 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     X.scores = scores;
     int rc = launch_index_scores(X, s);
     if (rc != 0) return launched(rc, "csa_forward/index_scores");
-    rc = launch_topk(scores, L->B * L->Tq, N, L->topk, idx, nullptr, nullptr, s);
+    rc = launch_topk(scores, L->B * L->Tq, N, L->topk, idx, nullptr, w + P.topk_off, s);
     if (rc != 0) return launched(rc, "csa_forward/topk");
     AttnLaunch A = make_attn(&io->q, io->q_pos, &io->kv_cache, L->cache_rows, 1, idx, L->topk, 1, &io->win, io->win_pos0,
                              L->Tw, io->sink, L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset, L->B, L->Tq,

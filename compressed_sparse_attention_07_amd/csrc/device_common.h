@@ -147,6 +147,54 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---- cross-lane steps without LDS: DPP row shifts inside each 16-lane row, then the
+// four row results through readlane.  update_dpp(old, v, row_shr:n, bound_ctrl): a lane
+// whose source lies outside its row gets 0 (bound_ctrl) or keeps `old`.
+template <int CTRL, bool ZERO>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, 0xf, 0xf, ZERO));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+  v += dpp_u32<kRowShr1, true>(0u, v);
+  v += dpp_u32<kRowShr2, true>(0u, v);
+  v += dpp_u32<kRowShr4, true>(0u, v);
+  v += dpp_u32<kRowShr8, true>(0u, v);
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                 r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// wave-wide reductions; the result is uniform
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u32<kRowShr1, true>(0u, v);
+  v += dpp_u32<kRowShr2, true>(0u, v);
+  v += dpp_u32<kRowShr4, true>(0u, v);
+  v += dpp_u32<kRowShr8, true>(0u, v);
+  return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
+         __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kRowShr1, true>(0u, v));
+  v = max(v, dpp_u32<kRowShr2, true>(0u, v));
+  v = max(v, dpp_u32<kRowShr4, true>(0u, v));
+  v = max(v, dpp_u32<kRowShr8, true>(0u, v));
+  return max(max(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 15)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 31))),
+             max(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 47)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63))));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kRowShr1, false>(0xffffffffu, v));
+  v = min(v, dpp_u32<kRowShr2, false>(0xffffffffu, v));
+  v = min(v, dpp_u32<kRowShr4, false>(0xffffffffu, v));
+  v = min(v, dpp_u32<kRowShr8, false>(0xffffffffu, v));
+  return min(min(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 15)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 31))),
+             min(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 47)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63))));
+}
+
 template <typename T>
 __device__ __forceinline__ T ceil_div(T a, T b) {
   return (a + b - 1) / b;

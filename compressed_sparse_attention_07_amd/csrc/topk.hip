@@ -1,23 +1,33 @@
 // K3: top-k selector over index-score rows.  [V4-CN] "DeepSeek-V4中文翻译" §2.3.1
 // (the top-k selector keeps k compressed entries per query); [NOTES] C_t = TopK_k(I_t,:).
 //
-// One workgroup of 16 waves per row.  Every score becomes an order-preserving uint32
-// key once (non-finite -> 0, never chosen; -0 and +0 share a key), and all passes
-// work on keys.  Each thread owns 32 consecutive keys of a 32768-key tile: rows up to
-// that size stay in registers across every pass (read from memory once); longer rows
-// stream tile by tile.  The exact threshold key theta (the k-th largest) and the
-// number r of theta-valued entries to keep (lowest indices first) come from:
-//   A. the finite count and the smallest / largest finite key;
-//   B. a 2048-bin histogram of (key - min) >> shift, a monotone map spread over the
-//      row's actual key range, so LDS atomic collisions stay rare even though index
-//      scores share their leading bits; a suffix scan finds the bin holding the k-th
-//      largest key;
-//   C. the keys of that bin (typically a few dozen) are gathered in LDS and ranked.
-// If the threshold bin is crowded (heavy ties), an exact MSB-first 8-bit radix
-// select over the row takes over.  Finally an order-preserving compaction writes
-// every key > theta and the first r keys == theta in ascending index order: wave
-// prefix sums plus a 16-wave LDS scan give every entry its output slot, so no sort
-// is needed.  Unused slots get -1.
+// Result per row: the indices of the min(k, #finite) largest scores, ties broken
+// towards the lower index, in ascending index order, padded with -1 (and the count).
+//
+// Every score becomes an order-preserving uint32 key once (non-finite -> 0, never
+// chosen; -0 and +0 share a key).  A row is cut into slices of at most 16384 keys and
+// selection runs in (at most a few) levels:
+//   level 1: one workgroup per (row, slice) keeps its slice's top-k as (key, index)
+//            pairs in index order;
+//   level n: the same selection over the concatenated candidate lists of a row
+//            (which stay in index order); the last level writes the indices.
+// An entry of the row's top-k is also in its slice's top-k (fewer than k entries of
+// the slice beat it; a tie it wins by index it also wins inside the slice), so the
+// levels are exact.  Short rows with many rows per launch take one level.
+//
+// Inside a workgroup every key stays in registers (PER consecutive keys per thread):
+//   A. count of finite keys and their smallest / largest key (wave reductions);
+//   B. an MSB-first radix select over v = key - min with 11-bit digits: each level is
+//      an LDS histogram of the keys that match the digits chosen so far, then a
+//      suffix scan picks the digit holding the remaining-th largest.  Starting from
+//      the slice's own key range, at most three levels give the exact threshold key
+//      theta (the k-th largest) and the number of theta-valued entries to keep; a
+//      level whose threshold bin holds exactly the entries still needed ends early
+//      (the whole bin is kept);
+//   C. an order-preserving compaction: every key > theta and the first `ties` keys
+//      == theta, in index order, placed by per-thread counts and a wave + LDS scan.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -25,289 +35,391 @@ namespace csa {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / WAVE;
-constexpr int kPer = 32;                // consecutive entries per thread
-constexpr int kTile = kThreads * kPer;  // entries per tile (32768)
 constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;
-constexpr int kRankCap = 1024;          // candidates ranked directly in LDS
+constexpr int kMaxSlice = 16384;  // keys per workgroup
 
-__device__ __forceinline__ void load_keys(const float* row, int64_t N, int64_t base, bool vec_ok,
-                                          uint32_t (&key)[kPer]) {
-  if (vec_ok && base + kPer <= N) {
-#pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
-      const float4 a = *reinterpret_cast<const float4*>(row + base + 4 * q);
-      key[4 * q] = score_key(a.x);
-      key[4 * q + 1] = score_key(a.y);
-      key[4 * q + 2] = score_key(a.z);
-      key[4 * q + 3] = score_key(a.w);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) key[j] = (base + j < N) ? score_key(row[base + j]) : 0u;
-  }
-}
-
-// inclusive scan of a 32-bit value across the wave
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(v, o, WAVE);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
-struct Shared {
-  uint32_t hist[kBins];
-  uint32_t cand[kRankCap];
-  uint32_t wave_a[kWaves], wave_b[kWaves], wave_c[kWaves];
-  uint32_t info[4];
-  uint32_t theta, ties, ncand;
+struct TopkArgs {
+  const float* scores;      // level 1 input: [rows, n_in]
+  const uint32_t* in_key;   // later levels: [rows, n_in] candidate keys (0 = none)
+  const int32_t* in_idx;    //               and their row indices
+  int64_t n_in;             // input entries per row
+  int64_t slice;            // entries per slice (workgroup)
+  int slices;               // slices per row
+  int k;
+  uint32_t* out_key;        // candidate output: [rows, slices, k]
+  int32_t* out_idx;         // candidate output [rows, slices, k], or the final [rows, k]
+  int32_t* count;           // final level: [rows] or NULL
 };
 
-// Exact MSB-first radix select of the k-th largest key (k < number of finite keys).
-template <bool RES>
-__device__ __forceinline__ void radix_select(const float* row, int64_t N, bool vec_ok, uint32_t k, Shared& sh,
-                                             uint32_t (&key)[kPer], uint32_t* theta, uint32_t* ties) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  uint32_t prefix = 0, pmask = 0, remaining = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kThreads) sh.hist[i] = 0u;
-    __syncthreads();
-    for (int64_t tb = 0; tb < N; tb += kTile) {
-      if (!RES) load_keys(row, N, tb + static_cast<int64_t>(tid) * kPer, vec_ok, key);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&sh.hist[(key[j] >> shift) & 0xffu], 1u);
-    }
-    __syncthreads();
-    if (wid == 0) {
-      uint32_t c[4], local = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = sh.hist[4 * lane + j]; local += c[j]; }
-      uint32_t incl = local;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t u = __shfl_down(incl, o, WAVE);
-        if (lane + o < 64) incl += u;
-      }
-      uint32_t above = incl - local;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < remaining && remaining <= above + c[j]) {
-          sh.info[0] = static_cast<uint32_t>(4 * lane + j);
-          sh.info[1] = above;
-        }
-        above += c[j];
-      }
-    }
-    __syncthreads();
-    remaining -= sh.info[1];
-    prefix |= sh.info[0] << shift;
-    pmask |= 0xffu << shift;
-    __syncthreads();
-  }
-  *theta = prefix;
-  *ties = remaining;
+template <int NT>
+struct Shared {
+  alignas(16) uint32_t hist[2][kBins];  // radix levels alternate between the two
+  alignas(16) uint4 wave_abc[NT / WAVE];
+  uint32_t wave_a[NT / WAVE];
+  uint32_t info[3];
+};
+
+__device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Raw buffer view of [p, p + bytes): dword loads past the end return 0 (hardware range
+// check), so a partly filled thread range needs no per-element address or guard.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* p, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), 0x00020000);
 }
 
-template <bool RES>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores, int64_t N, int k,
-                                                        int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-  __shared__ Shared sh;
+// PAIRS: input is (key, index) candidates; FINAL: write indices (and count) only.
+template <int NT, int PER, bool PAIRS, bool FINAL>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
+  constexpr int NW = NT / WAVE;
+  __shared__ Shared<NT> sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int64_t r = blockIdx.x;
-  const float* row = scores + r * N;
-  int32_t* out = idx + r * static_cast<int64_t>(k);
-  const bool vec_ok = (N & 3) == 0;
-  const uint32_t K = static_cast<uint32_t>(k);
-  uint32_t key[kPer];  // this thread's 32 keys of the current tile
-  if (RES) load_keys(row, N, static_cast<int64_t>(tid) * kPer, vec_ok, key);
+  const int64_t r = blockIdx.x / a.slices;
+  const int sl = static_cast<int>(blockIdx.x % a.slices);
+  const int64_t lo = static_cast<int64_t>(sl) * a.slice;
+  const int64_t hi = min(a.n_in, lo + a.slice);
+  const int64_t base = lo + static_cast<int64_t>(tid) * PER;  // first entry of this thread
+  const uint32_t K = static_cast<uint32_t>(a.k);
 
-  // ---- A: finite count, smallest and largest finite key
-  uint32_t nfin = 0, kmax = 0, kmin1 = 0xffffffffu;  // kmin1 = min(key - 1): 0 wraps to the top
-  for (int64_t tb = 0; tb < N; tb += kTile) {
-    if (!RES) load_keys(row, N, tb + static_cast<int64_t>(tid) * kPer, vec_ok, key);
+  // ---- load: PER consecutive keys per thread (a candidate's index is read again only
+  //      when it is written out)
+  uint32_t key[PER];
+  const int32_t* ir = PAIRS ? a.in_idx + r * a.n_in + base : nullptr;
+  if (PAIRS) {
+    const uint32_t* kr = a.in_key + r * a.n_in + base;
+    if (base + PER <= hi && aligned16(kr)) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      nfin += key[j] != 0u ? 1u : 0u;
-      kmax = max(kmax, key[j]);
-      kmin1 = min(kmin1, key[j] - 1u);
+      for (int q = 0; q < PER / 4; ++q) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(kr + 4 * q);
+        key[4 * q] = kv.x; key[4 * q + 1] = kv.y; key[4 * q + 2] = kv.z; key[4 * q + 3] = kv.w;
+      }
+    } else {
+      // view of the workgroup's slice (uniform), lane offsets from the slice start
+      const __amdgpu_buffer_rsrc_t bk = buffer_view(a.in_key + r * a.n_in + lo, (hi - lo) * 4);
+      const int off = 4 * tid * PER;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        key[j] = __builtin_amdgcn_raw_buffer_load_b32(bk, off + 4 * j, 0, 0);  // 0 past the end: no candidate
+    }
+  } else {
+    const float* row = a.scores + r * a.n_in + base;
+    if (base + PER <= hi && aligned16(row)) {
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(row + 4 * q);
+        key[4 * q] = score_key(v.x);
+        key[4 * q + 1] = score_key(v.y);
+        key[4 * q + 2] = score_key(v.z);
+        key[4 * q + 3] = score_key(v.w);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t bs = buffer_view(a.scores + r * a.n_in + lo, (hi - lo) * 4);
+      const int off = 4 * tid * PER;
+      uint32_t x[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) x[j] = __builtin_amdgcn_raw_buffer_load_b32(bs, off + 4 * j, 0, 0);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t kk = score_key(__builtin_bit_cast(float, x[j]));
+        key[j] = base + j < hi ? kk : 0u;
+      }
     }
   }
+
+  // ---- A: finite count, smallest and largest finite key
+  uint32_t nfin = 0, kmax = 0, kmin1 = 0xffffffffu;  // kmin1 = min(key - 1): key 0 wraps to the top
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    nfin += __shfl_xor(nfin, o, WAVE);
-    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(kmax, o, WAVE)));
-    kmin1 = min(kmin1, static_cast<uint32_t>(__shfl_xor(kmin1, o, WAVE)));
+  for (int j = 0; j < PER; ++j) {
+    nfin += key[j] != 0u ? 1u : 0u;
+    kmax = max(kmax, key[j]);
+    kmin1 = min(kmin1, key[j] - 1u);
   }
-  if (lane == 0) {
-    sh.wave_a[wid] = nfin;
-    sh.wave_b[wid] = kmax;
-    sh.wave_c[wid] = kmin1;
-  }
+  nfin = wave_sum_u32(nfin);
+  kmax = wave_max_u32(kmax);
+  kmin1 = wave_min_u32(kmin1);
+  if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, kmax, kmin1, 0u);
+  for (int i = tid; i < kBins; i += NT) sh.hist[0][i] = 0u;  // the first radix level's histogram
   __syncthreads();
   nfin = 0;
   kmax = 0;
   kmin1 = 0xffffffffu;
-  for (int w = 0; w < kWaves; ++w) {
-    nfin += sh.wave_a[w];
-    kmax = max(kmax, sh.wave_b[w]);
-    kmin1 = min(kmin1, sh.wave_c[w]);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint4 v = sh.wave_abc[w];
+    nfin += v.x;
+    kmax = max(kmax, v.y);
+    kmin1 = min(kmin1, v.z);
   }
   const uint32_t kmin = kmin1 + 1u;
 
+  // ---- B: threshold key theta and the number of theta-valued entries kept
   uint32_t theta, ties;
+  uint32_t koff = 0;  // keys below are stored as key - koff (finite keys stay >= 1)
   const uint32_t total_sel = nfin < K ? nfin : K;
   if (nfin <= K) {
-    theta = 0u;  // key > 0 <=> finite score: take them all
+    theta = 0u;  // key > 0 <=> finite score: keep them all
     ties = 0u;
   } else if (kmin == kmax) {
-    theta = kmax;  // every finite score is equal: the first k by index
+    theta = kmax;  // every finite key is equal: the first k by index
     ties = K;
   } else {
-    // ---- B: histogram of (key - kmin) >> shift over the row's key range
+    // work on w = key - kmin + 1 (finite keys in [1, span + 1], 0 = not finite)
+    koff = kmin - 1u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) key[j] = key[j] != 0u ? key[j] - koff : 0u;
     const uint32_t span = kmax - kmin;
-    const int bits = 32 - __clz(span);
-    const int shift = bits > kBinBits ? bits - kBinBits : 0;
-    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0u;
-    if (tid == 0) sh.ncand = 0u;
-    __syncthreads();
-    for (int64_t tb = 0; tb < N; tb += kTile) {
-      if (!RES) load_keys(row, N, tb + static_cast<int64_t>(tid) * kPer, vec_ok, key);
+    int shift = 32 - __clz(span);  // low bits of v = w - 1 still to decide
+    uint32_t pval = 0, pmask = 0, remaining = K;
+    // one level: histogram of the matching keys' next digit (hist[cur], cleared before),
+    // barrier; wave 0 finds the threshold digit while the other waves clear the other
+    // histogram for the next level; barrier; everyone reads the result
+    for (int cur = 0;; cur ^= 1) {
+      const int nsh = shift > kBinBits ? shift - kBinBits : 0;
+      const uint32_t dmask = (1u << (shift - nsh)) - 1u;
+      // keep the per-key terms inside the level loop (hoisting them would double the
+      // registers the keys occupy)
 #pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (key[j] != 0u) atomicAdd(&sh.hist[(key[j] - kmin) >> shift], 1u);
-    }
-    __syncthreads();
-    if (wid == 0) {
-      constexpr int PB = kBins / WAVE;  // bins per lane
-      uint32_t local = 0;
-      for (int j = 0; j < PB; ++j) local += sh.hist[PB * lane + j];
-      uint32_t incl = local;
+      for (int j = 0; j < PER; ++j) asm volatile("" : "+v"(key[j]));
+      uint32_t* hc = sh.hist[cur];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t u = __shfl_down(incl, o, WAVE);
-        if (lane + o < 64) incl += u;
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t v = key[j] - 1u;
+        if (key[j] != 0u && (v & pmask) == pval) atomicAdd(&hc[(v >> nsh) & dmask], 1u);
+        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the addresses computed ahead
       }
-      uint32_t above = incl - local;
-      for (int j = PB - 1; j >= 0; --j) {
-        const uint32_t c = sh.hist[PB * lane + j];
-        if (above < K && K <= above + c) {
-          sh.info[0] = static_cast<uint32_t>(PB * lane + j);
-          sh.info[1] = above;
-          sh.info[2] = c;
+      __syncthreads();
+      if (wid == 0) {
+        constexpr int PB = kBins / WAVE;  // bins per lane, held in registers
+        const uint4* hb = reinterpret_cast<const uint4*>(&hc[PB * lane]);
+        uint32_t c[PB];
+#pragma unroll
+        for (int j = 0; j < PB / 4; ++j) {
+          const uint4 v = hb[j];
+          c[4 * j] = v.x; c[4 * j + 1] = v.y; c[4 * j + 2] = v.z; c[4 * j + 3] = v.w;
         }
-        above += c;
-      }
-    }
-    __syncthreads();
-    const uint32_t bstar = sh.info[0];
-    const uint32_t above = sh.info[1];
-    const uint32_t ncand = sh.info[2];
-    const uint32_t need = K - above;  // entries to take from the threshold bin (>= 1)
-    if (ncand <= static_cast<uint32_t>(kRankCap)) {
-      // ---- C: gather the threshold bin and rank it exactly
-      for (int64_t tb = 0; tb < N; tb += kTile) {
-        if (!RES) load_keys(row, N, tb + static_cast<int64_t>(tid) * kPer, vec_ok, key);
+        uint32_t local = 0;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          if (key[j] != 0u && ((key[j] - kmin) >> shift) == bstar) {
-            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-            sh.cand[slot] = key[j];
+        for (int j = 0; j < PB; ++j) local += c[j];
+        const uint32_t pre = wave_prefix_sum(local);
+        const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + local;  // this lane and those above
+        uint32_t above = incl - local;
+        if (above < remaining && remaining <= incl) {  // the threshold bin is one of this lane's
+          uint32_t bin = 0, abv = 0, cnt = 0;
+#pragma unroll
+          for (int j = PB - 1; j >= 0; --j) {
+            if (above < remaining && remaining <= above + c[j]) {
+              bin = static_cast<uint32_t>(PB * lane + j);
+              abv = above;
+              cnt = c[j];
+            }
+            above += c[j];
           }
+          sh.info[0] = bin;
+          sh.info[1] = abv;
+          sh.info[2] = cnt;
         }
+      } else if (nsh > 0) {
+        uint32_t* hn = sh.hist[cur ^ 1];
+        for (int i = tid - WAVE; i < kBins; i += NT - WAVE) hn[i] = 0u;
       }
       __syncthreads();
-      for (uint32_t i = tid; i < ncand; i += kThreads) {
-        const uint32_t ki = sh.cand[i];
-        uint32_t gt = 0, eq = 0;
-        for (uint32_t j = 0; j < ncand; ++j) {
-          const uint32_t kj = sh.cand[j];
-          gt += kj > ki ? 1u : 0u;
-          eq += kj == ki ? 1u : 0u;
-        }
-        if (gt < need && need <= gt + eq) {
-          sh.theta = ki;          // every writer stores the same pair
-          sh.ties = need - gt;
-        }
+      remaining -= sh.info[1];
+      pval |= sh.info[0] << nsh;
+      pmask |= dmask << nsh;
+      if (sh.info[2] == remaining) {
+        // the threshold bin holds exactly the entries still needed: take all of it,
+        // i.e. every key >= the bin's lowest value (w = pval + 1)
+        theta = pval;
+        ties = 0u;
+        break;
       }
-      __syncthreads();
-      theta = sh.theta;
-      ties = sh.ties;
-    } else {
-      radix_select<RES>(row, N, vec_ok, K, sh, key, &theta, &ties);
+      if (nsh == 0) {
+        theta = pval + 1u;  // in the w domain
+        ties = remaining;
+        break;
+      }
+      shift = nsh;
     }
   }
 
-  // ---- D: ordered compaction of key > theta, and the first `ties` keys == theta
-  uint32_t run_gt = 0, run_tie = 0;  // totals of earlier tiles (uniform across the WG)
-  for (int64_t tile = 0; tile < N; tile += kTile) {
-    const int64_t base = tile + static_cast<int64_t>(tid) * kPer;
-    if (!RES) load_keys(row, N, base, vec_ok, key);
-    uint32_t ngt = 0, ntie = 0;
+  // ---- C: ordered compaction of key > theta and the first `ties` keys == theta
+  uint32_t ngt = 0, ntie = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      ngt += key[j] > theta ? 1u : 0u;
-      ntie += (key[j] == theta && key[j] != 0u) ? 1u : 0u;
-    }
-    const uint32_t packed = ngt | (ntie << 16);
-    const uint32_t incl = wave_incl_scan(packed);
-    __syncthreads();
-    if (lane == 63) sh.wave_a[wid] = incl;
-    __syncthreads();
-    uint32_t before = incl - packed;
-    uint32_t tile_tot = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t t = sh.wave_a[w];
-      if (w < wid) before += t;
-      tile_tot += t;
-    }
-    uint32_t gt_before = run_gt + (before & 0xffffu);
-    uint32_t tie_before = run_tie + (before >> 16);
-    if (ngt + ntie > 0) {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const bool gt = key[j] > theta;
-        const bool tie = key[j] == theta && key[j] != 0u;
-        if (gt || (tie && tie_before < ties)) {
-          const uint32_t slot = gt_before + (tie_before < ties ? tie_before : ties);
-          out[slot] = static_cast<int32_t>(base + j);
-        }
-        gt_before += gt ? 1u : 0u;
-        tie_before += tie ? 1u : 0u;
-      }
-    }
-    run_gt += tile_tot & 0xffffu;
-    run_tie += tile_tot >> 16;
+  for (int j = 0; j < PER; ++j) {
+    ngt += key[j] > theta ? 1u : 0u;
+    ntie += (key[j] == theta && key[j] != 0u) ? 1u : 0u;
   }
-  for (int i = static_cast<int>(total_sel) + tid; i < k; i += kThreads) out[i] = -1;
-  if (count && tid == 0) count[r] = static_cast<int32_t>(total_sel);
+  const uint32_t packed = ngt | (ntie << 16);  // at most 32768 each
+  const uint32_t incl = wave_prefix_sum(packed);
+  __syncthreads();  // every thread is done reading the per-wave values of A
+  if (lane == 63) sh.wave_a[wid] = incl;
+  __syncthreads();
+  uint32_t before = incl - packed;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w < wid) before += sh.wave_a[w];
+  uint32_t gt_before = before & 0xffffu;
+  uint32_t tie_before = before >> 16;
+  // candidate indices, loaded now that the radix registers are free
+  int32_t ix[PAIRS ? PER : 1];
+  if (PAIRS) {
+    if (base + PER <= hi && aligned16(ir)) {
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) {
+        const int4 iv = *reinterpret_cast<const int4*>(ir + 4 * q);
+        ix[4 * q] = iv.x; ix[4 * q + 1] = iv.y; ix[4 * q + 2] = iv.z; ix[4 * q + 3] = iv.w;
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t bi = buffer_view(a.in_idx + r * a.n_in + lo, (hi - lo) * 4);
+      const int off = 4 * tid * PER;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) ix[j] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(bi, off + 4 * j, 0, 0));
+    }
+  }
+  int32_t* oi;
+  uint32_t* ok = nullptr;
+  if (FINAL) {
+    oi = a.out_idx + r * static_cast<int64_t>(a.k);
+  } else {
+    const int64_t o = (r * a.slices + sl) * static_cast<int64_t>(a.k);
+    oi = a.out_idx + o;
+    ok = a.out_key + o;
+  }
+  if (ngt + ntie > 0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool gt = key[j] > theta;
+      const bool tie = key[j] == theta && key[j] != 0u;
+      if (gt || (tie && tie_before < ties)) {
+        const uint32_t slot = gt_before + (tie_before < ties ? tie_before : ties);
+        oi[slot] = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(base + j);
+        if (!FINAL) ok[slot] = key[j] + koff;
+      }
+      gt_before += gt ? 1u : 0u;
+      tie_before += tie ? 1u : 0u;
+      if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (int i = static_cast<int>(total_sel) + tid; i < a.k; i += NT) {
+    oi[i] = -1;
+    if (!FINAL) ok[i] = 0u;
+  }
+  if (FINAL && a.count && tid == 0) a.count[r] = static_cast<int32_t>(total_sel);
+}
+
+// workgroup shapes: (threads, keys per thread), slice capacity = threads * keys
+struct Shape {
+  int nt, per;
+  int64_t cap() const { return static_cast<int64_t>(nt) * per; }
+};
+constexpr Shape kShapes[] = {{256, 16}, {512, 16}, {1024, 16}};
+
+Shape shape_for(int64_t n) {
+  for (const Shape& s : kShapes)
+    if (s.cap() >= n) return s;
+  return kShapes[2];
+}
+
+template <bool PAIRS, bool FINAL>
+void launch_shape(const Shape& s, int64_t blocks, const TopkArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  if (s.nt == 256) hipLaunchKernelGGL((topk_kernel<256, 16, PAIRS, FINAL>), grid, dim3(256), 0, stream, a);
+  else if (s.nt == 512) hipLaunchKernelGGL((topk_kernel<512, 16, PAIRS, FINAL>), grid, dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL((topk_kernel<1024, 16, PAIRS, FINAL>), grid, dim3(1024), 0, stream, a);
+}
+
+// Selection levels: input entries per row, slice length and slices per row of each.
+struct Levels {
+  int n;
+  int64_t len[16], slice[16];
+  int slices[16];
+};
+
+Levels plan_levels(int64_t rows, int64_t N, int k) {
+  Levels L{};
+  // level-1 slices: halved from 32768 (not below 4096 or 2k) while the launch has fewer
+  // workgroups than compute units and one further level still covers the candidates
+  int64_t sl = kMaxSlice;
+  while (sl > 4096 && sl / 2 >= 2 * static_cast<int64_t>(k) && rows * ((N + sl - 1) / sl) < 256 &&
+         ((N + sl / 2 - 1) / (sl / 2)) * k <= kMaxSlice)
+    sl /= 2;
+  int64_t len = N;
+  int i = 0;
+  // k <= kMaxSlice / 4, so every level shrinks a row at least 2.5x: 16 levels cover N < 2^31
+  while (i < 15 && (len > kMaxSlice || (i == 0 && len > sl))) {
+    const int64_t s = i == 0 ? sl : kMaxSlice;
+    L.len[i] = len;
+    L.slice[i] = s;
+    L.slices[i] = static_cast<int>((len + s - 1) / s);
+    len = static_cast<int64_t>(L.slices[i]) * k;
+    ++i;
+  }
+  L.len[i] = len;
+  L.slice[i] = len;
+  L.slices[i] = 1;
+  L.n = i + 1;
+  return L;
+}
+
+size_t level_buffer_bytes(int64_t rows, const Levels& L, int k) {
+  int64_t mx = 0;
+  for (int i = 0; i + 1 < L.n; ++i) mx = std::max<int64_t>(mx, static_cast<int64_t>(L.slices[i]) * k);
+  return (static_cast<size_t>(rows * mx) * (sizeof(uint32_t) + sizeof(int32_t)) + 255) / 256 * 256;
 }
 
 }  // namespace
 
-size_t topk_workspace_bytes(int64_t, int64_t, int) { return 0; }
+// Workspace: two candidate buffers (keys + indices), sized for the largest level output.
+size_t topk_workspace_bytes(int64_t rows, int64_t N, int k) {
+  if (rows <= 0 || N <= 0) return 0;
+  const Levels L = plan_levels(rows, N, k);
+  return L.n == 1 ? 0 : 2 * level_buffer_bytes(rows, L, k);
+}
 
-int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, void*,
+int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, void* ws,
                 hipStream_t stream) {
   if (rows == 0) return 0;
-  if (N <= kTile)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(static_cast<uint32_t>(rows)), dim3(kThreads), 0, stream, scores, N, k,
-                       idx, count);
-  else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(static_cast<uint32_t>(rows)), dim3(kThreads), 0, stream, scores, N,
-                       k, idx, count);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  const Levels L = N > 0 ? plan_levels(rows, N, k) : Levels{1, {0}, {1}, {1}};
+  const size_t one = level_buffer_bytes(rows, L, k);
+  char* w = static_cast<char*>(ws);
+  const uint32_t* in_key = nullptr;
+  const int32_t* in_idx = nullptr;
+  for (int i = 0; i < L.n; ++i) {
+    const bool final_level = i + 1 == L.n;
+    TopkArgs a{};
+    a.scores = scores;
+    a.in_key = in_key;
+    a.in_idx = in_idx;
+    a.n_in = L.len[i];
+    a.slice = L.slice[i] > 0 ? L.slice[i] : 1;
+    a.slices = L.slices[i];
+    a.k = k;
+    a.count = count;
+    if (final_level) {
+      a.out_idx = idx;
+    } else {
+      char* buf = w + (i & 1) * one;
+      const int64_t n_out = rows * static_cast<int64_t>(L.slices[i]) * k;
+      a.out_key = reinterpret_cast<uint32_t*>(buf);
+      a.out_idx = reinterpret_cast<int32_t*>(buf + n_out * sizeof(uint32_t));
+    }
+    const Shape s = shape_for(a.slice);
+    const int64_t blocks = rows * L.slices[i];
+    if (i == 0) {
+      if (final_level) launch_shape<false, true>(s, blocks, a, stream);
+      else launch_shape<false, false>(s, blocks, a, stream);
+    } else {
+      if (final_level) launch_shape<true, true>(s, blocks, a, stream);
+      else launch_shape<true, false>(s, blocks, a, stream);
+    }
+    if (hipGetLastError() != hipSuccess) return -1;
+    in_key = a.out_key;
+    in_idx = a.out_idx;
+  }
+  return 0;
 }
 
 }  // namespace csa

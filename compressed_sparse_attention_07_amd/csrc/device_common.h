@@ -195,6 +195,32 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
              min(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 47)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63))));
 }
 
+// ---- direct global -> LDS loads
+//
+// One 16-byte-per-lane load to LDS (global_load_lds_dwordx4): lane i's 16 bytes land at
+// M0 + 16 i.  Used for 1 KiB rows / row groups.  M0 is saved and restored around the instruction (the address
+// is taken at issue), so the compiler's own uses of M0 are unaffected.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(lds_byte)
+               : "memory");
+}
+
+// a wave-uniform 64-bit value, moved to scalar registers
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T ceil_div(T a, T b) {
   return (a + b - 1) / b;

@@ -12,6 +12,14 @@
 // cross-lane adds finish the sum over heads, and each lane stores one score of a
 // 64-entry run (one coalesced 256-byte store per iteration).
 //
+// Prefill path (bf16, many queries per sequence): a workgroup of 8 waves owns 16
+// queries of one sequence and a range of keys.  Key tiles (64 keys) are brought into
+// a 4-stage LDS ring by direct global->LDS loads and shared by all 16 queries; each
+// wave keeps two queries' q^I in registers, so every key fragment read from LDS feeds
+// 2 x HB MFMA chains.  The 16-byte chunks of each key row are XOR-swizzled by the key
+// index (applied through the load addresses), so the 16 keys of an operand read hit
+// distinct banks.
+//
 // MXFP4 path ([V4-CN] §3.4: the indexer QK in FP4): both operands are e2m1 codes with
 // an e8m0 scale per 32 elements, fed to v_mfma_scale_f32_16x16x128_f8f6f4.  Its operand
 // layout is the storage layout: lane (col, grp) holds 32 consecutive codes of row col
@@ -213,6 +221,195 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
   }
 }
 
+
+// ------------------------------------------------------------------ prefill (LDS-shared keys)
+
+constexpr int kPfWaves = 8;
+constexpr int kPfTokPerWave = 2;
+constexpr int kPfTok = kPfWaves * kPfTokPerWave;  // queries per workgroup
+constexpr int kPfKeys = 64;                   // keys per ring stage
+constexpr int kPfStages = 4;
+
+// HB head blocks of 16, KS k-steps of 32 (DI = 32 KS).  Grid: (sequence, query group,
+// key range of keys_per_wg) flattened.
+template <int HB, int KS>
+__global__ __launch_bounds__(kPfWaves * WAVE) void index_prefill_kernel(IndexLaunch a, int64_t keys_per_wg,
+                                                                         int64_t ranges, int64_t groups) {
+  constexpr int DI = 32 * KS;
+  constexpr int RB = 2 * DI;                 // bytes per key row
+  constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  constexpr int STAGE_B = kPfKeys * RB;      // bytes per stage
+  constexpr int DMA_PER_WAVE = STAGE_B / 1024 / kPfWaves;
+  static_assert(DMA_PER_WAVE >= 1 && DMA_PER_WAVE * kPfWaves * 1024 == STAGE_B, "stage must split into waves");
+  static_assert(DMA_PER_WAVE * (kPfStages - 2) < 64, "vmcnt range");
+  constexpr int NSUB = kPfKeys / 64;         // 64-key groups per stage
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kPfStages * STAGE_B];
+  __shared__ int64_t vis_w[kPfWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t kr = blockIdx.x % ranges;
+  const int64_t tg = blockIdx.x / ranges;
+  const int64_t b = tg / groups;
+  const int64_t tq0 = (tg % groups) * kPfTok;
+  const int64_t s_begin = kr * keys_per_wg;
+  const int64_t s_end = min(s_begin + keys_per_wg, a.N);
+
+  // this wave's two queries: q^I (A operand, rows = heads) and head weights
+  bf16x8 qa[kPfTokPerWave][HB][KS];
+  float w[kPfTokPerWave][HB][4];
+  int64_t vis[kPfTokPerWave];
+  int64_t vmax = 0;
+#pragma unroll
+  for (int u = 0; u < kPfTokPerWave; ++u) {
+    const int64_t tq = tq0 + wid * kPfTokPerWave + u;
+    vis[u] = 0;
+    if (tq < a.Tq) {
+      const int64_t bt = b * a.Tq + tq;
+      int64_t v = a.q_pos[bt] / a.ratio;
+      vis[u] = v > a.N ? a.N : (v < 0 ? 0 : v);
+      const uint16_t* q = static_cast<const uint16_t*>(a.qI.data) + bt * a.HI * DI;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qa[u][hb][ks] = *reinterpret_cast<const bf16x8*>(q + (hb * 16 + col) * DI + ks * 32 + grp * 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[u][hb][r] = a.wI[bt * a.HI + hb * 16 + grp * 4 + r];
+      }
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[u][hb][ks] = bf16x8{};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[u][hb][r] = 0.f;
+      }
+    }
+    vmax = max(vmax, vis[u]);
+  }
+  if (lane == 0) vis_w[wid] = vmax;
+  // every load the compiler tracks completes before the first row load it cannot see
+#pragma unroll
+  for (int u = 0; u < kPfTokPerWave; ++u)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 t = __builtin_bit_cast(uint4, qa[u][hb][ks]);
+        asm volatile("" ::"v"(t.x), "v"(t.y), "v"(t.z), "v"(t.w));
+      }
+  wait_vmcnt<0>();
+  __syncthreads();
+  int64_t wg_vis = 0;
+#pragma unroll
+  for (int i = 0; i < kPfWaves; ++i) wg_vis = max(wg_vis, vis_w[i]);
+  // keys the workgroup has to score: [s_begin, s_stop); the rest of the range is -inf
+  const int64_t s_stop = uni64(min(s_end, max(s_begin, wg_vis)));
+  const int ntiles = static_cast<int>((s_stop - s_begin + kPfKeys - 1) / kPfKeys);
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.data) + uni64(b * a.kI_rows) * RB;
+  const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+
+  // stage u: keys s_begin + kPfKeys u ..; instruction m covers stage bytes [1024 m, +1024)
+  auto issue = [&](int u) {
+    const int st = u % kPfStages;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int m = wid * DMA_PER_WAVE + i;
+      const int off = m * 1024 + 16 * lane;     // byte within the stage
+      const int kk = off / RB;                  // key within the stage
+      const int pc = (off % RB) / 16;           // physical chunk
+      const int lc = pc ^ (kk & (CPR - 1));     // logical chunk stored there
+      int64_t s = s_begin + static_cast<int64_t>(u) * kPfKeys + kk;
+      if (s >= s_stop) s = s_stop - 1;          // in bounds; masked when scored
+      lds_dma16(kbase + s * RB + lc * 16, ring_b + st * STAGE_B + m * 1024);
+    }
+  };
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+
+  float* out[kPfTokPerWave];
+#pragma unroll
+  for (int u = 0; u < kPfTokPerWave; ++u) {
+    const int64_t tq = tq0 + wid * kPfTokPerWave + u;
+    out[u] = tq < a.Tq ? a.scores + (b * a.Tq + tq) * a.N : nullptr;
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t % kPfStages;
+    const int later = min(ntiles - 1 - t, kPfStages - 2);
+    if (later >= 2) wait_vmcnt<2 * DMA_PER_WAVE>();
+    else if (later == 1) wait_vmcnt<DMA_PER_WAVE>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (t + kPfStages - 1 < ntiles) issue(t + kPfStages - 1);  // into the stage freed by tile t-1
+
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const uint8_t* T = ring + st * STAGE_B + sub * 64 * RB;
+      const int64_t s0 = s_begin + static_cast<int64_t>(t) * kPfKeys + sub * 64;
+      float part[kPfTokPerWave][4];
+#pragma unroll
+      for (int tI = 0; tI < 4; ++tI) {
+        const int kk = tI * 16 + col;  // key within the 64-key group (swizzle uses kk mod CPR)
+        bf16x8 kb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kb[ks] = *reinterpret_cast<const bf16x8*>(T + kk * RB + (((4 * ks + grp) ^ (kk & (CPR - 1))) * 16));
+#pragma unroll
+        for (int u = 0; u < kPfTokPerWave; ++u) {
+          float sc = 0.f;
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][hb][ks], kb[ks], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc = fmaf(w[u][hb][r], fmaxf(acc[r], 0.f), sc);
+          }
+          sc += __shfl_xor(sc, 16, WAVE);
+          sc += __shfl_xor(sc, 32, WAVE);
+          part[u][tI] = sc;
+        }
+      }
+      // lane (col, grp) stores entry s0 + 16 grp + col of each query
+#pragma unroll
+      for (int u = 0; u < kPfTokPerWave; ++u) {
+        float res = part[u][0];
+#pragma unroll
+        for (int tI = 1; tI < 4; ++tI)
+          if (grp == tI) res = part[u][tI];
+        const int64_t s = s0 + lane;
+        if (out[u] && s < s_end) out[u][s] = s < vis[u] ? res : -INFINITY;
+      }
+    }
+  }
+  // entries of the range past every query's visible prefix
+  for (int64_t s = s_begin + static_cast<int64_t>(ntiles) * kPfKeys + lane; s < s_end; s += WAVE) {
+#pragma unroll
+    for (int u = 0; u < kPfTokPerWave; ++u)
+      if (out[u]) out[u][s] = -INFINITY;
+  }
+}
+
+typedef void (*PrefillKern)(IndexLaunch, int64_t, int64_t, int64_t);
+
+PrefillKern pick_prefill(int HB, int KS) {
+  if (KS == 4 && HB == 4) return index_prefill_kernel<4, 4>;
+  if (KS == 4 && HB == 2) return index_prefill_kernel<2, 4>;
+  if (KS == 4 && HB == 1) return index_prefill_kernel<1, 4>;
+  if (KS == 2 && HB == 4) return index_prefill_kernel<4, 2>;
+  if (KS == 2 && HB == 2) return index_prefill_kernel<2, 2>;
+  if (KS == 2 && HB == 1) return index_prefill_kernel<1, 2>;
+  return nullptr;
+}
+
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
 // MXFP4 scores: HB head blocks of 16, KS4 steps of 128 elements (DI = 128 KS4).  One
@@ -375,6 +572,20 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
       hipLaunchKernelGGL(index_simt_mxfp4_kernel, grid, dim3(kSimtThreads), 0, stream, L);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  if (L.qI.dtype == CSA_BF16 && L.HI % 16 == 0 && L.DI % 32 == 0 && L.Tq >= kPfTok) {
+    // many queries per sequence: keys staged once in LDS for kPfTok queries at a time
+    PrefillKern k = pick_prefill(L.HI / 16, L.DI / 32);
+    if (k) {
+      const int64_t groups = (L.Tq + kPfTok - 1) / kPfTok;
+      int64_t kpw = 8192;
+      while (kpw > kPfKeys && L.B * groups * ((L.N + kpw - 1) / kpw) < 1024) kpw /= 2;
+      const int64_t ranges = (L.N + kpw - 1) / kpw;
+      const int64_t grid = L.B * groups * ranges;
+      hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(grid)), dim3(kPfWaves * WAVE), 0, stream, L, kpw, ranges,
+                         groups);
+      return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
   }
   if (L.qI.dtype == CSA_BF16 && L.HI % 16 == 0 && L.DI % 32 == 0) {
     MfmaKern k = pick_mfma(L.HI / 16, L.DI / 32);

@@ -502,29 +502,6 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 constexpr int kDmaStages = 4;
 constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
 
-// One row load to LDS.  M0 is saved and restored around the instruction (the address
-// is taken at issue), so the compiler's own uses of M0 are unaffected.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(g), "s"(lds_byte)
-               : "memory");
-}
-
-// a wave-uniform 64-bit value, moved to scalar registers
-__device__ __forceinline__ int64_t uni64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int D = 512;

@@ -150,6 +150,11 @@ INDEX_CASES = [
     (2, 3, 16, 32, 300, 4, "bf16"),
     (1, 4, 4, 32, 77, 4, "bf16"),
     (1, 6, 64, 128, 4100, 128, "bf16"),
+    # 16+ queries per sequence: keys shared through LDS by 16 queries (ragged last group,
+    # key ranges with masked tails)
+    (1, 40, 64, 128, 3000, 4, "bf16"),
+    (2, 16, 32, 64, 500, 4, "bf16"),
+    (1, 33, 16, 128, 9000, 128, "bf16"),
     # MXFP4 queries and keys: scaled fp4 MFMA (DI % 128 == 0, HI % 16 == 0), else the SIMT kernel
     (2, 5, 64, 128, 1000, 4, "mxfp4"),
     (1, 3, 16, 256, 300, 4, "mxfp4"),

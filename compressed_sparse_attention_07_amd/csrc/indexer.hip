@@ -13,7 +13,7 @@
 // 64-entry run (one coalesced 256-byte store per iteration).
 //
 // Prefill path (bf16, many queries per sequence): a workgroup of 8 waves owns 16
-// queries of one sequence and a range of keys.  Key tiles (64 keys) are brought into
+// queries of one sequence and a range of keys.  Key tiles (128 keys) are brought into
 // a 4-stage LDS ring by direct global->LDS loads and shared by all 16 queries; each
 // wave keeps two queries' q^I in registers, so every key fragment read from LDS feeds
 // 2 x HB MFMA chains.  The 16-byte chunks of each key row are XOR-swizzled by the key
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
 constexpr int kPfWaves = 8;
 constexpr int kPfTokPerWave = 2;
 constexpr int kPfTok = kPfWaves * kPfTokPerWave;  // queries per workgroup
-constexpr int kPfKeys = 64;                   // keys per ring stage
+constexpr int kPfKeys = 128;                  // keys per ring stage
 constexpr int kPfStages = 4;
 
 // HB head blocks of 16, KS k-steps of 32 (DI = 32 KS).  Grid: (sequence, query group,

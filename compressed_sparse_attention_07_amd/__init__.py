@@ -8,7 +8,7 @@ The computation lives in hand-written HIP kernels behind the C ABI of
 
 from ._lib import (  # noqa: F401
     CSA_BF16, CSA_F32, CSA_FP8MIX, CSA_MODE_CSA, CSA_MODE_HCA, CSA_MXFP4, Buf, CSAError, EXPORTS, LIB_PATH,
-    ForwardCall,
+    ForwardCall, PreparedCall,
     csa_compress, csa_forward, csa_forward_workspace_size, csa_index_scores, csa_quantize, csa_sparse_mqa, csa_topk,
     hca_dense_attn, layer_desc, lib,
 )

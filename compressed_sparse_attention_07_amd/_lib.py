@@ -105,6 +105,19 @@ def check(status: int) -> None:
         raise CSAError(status, lib().csa_last_error().decode())
 
 
+# While a PreparedCall is being built, entry points record their C call here instead
+# of making it.
+_recording: list | None = None
+
+
+def _invoke(name: str, *args, keep=()) -> None:
+    fn = getattr(lib(), name)
+    if _recording is not None:
+        _recording.append((fn, args, keep))
+        return
+    check(fn(*args))
+
+
 def ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -189,16 +202,16 @@ def csa_compress(ca, cb, za, zb, out: Buf, *, ratio: int, overlap: bool, t0: int
     B, T, D = ca.shape
     out_rows = out.shape[1]
     bo = out.c()
-    check(lib().csa_compress(ptr(ca), ptr(cb), ptr(za), ptr(zb), _dt(ca), ptr(bias_a), ptr(bias_b), ptr(prev_cb),
-                             ptr(prev_zb), B, T, D, ratio, 1 if overlap else 0, t0, rope_dims, rope_base, pos_offset,
-                             C.byref(bo), out_rows, stream_handle(stream)))
+    _invoke("csa_compress", ptr(ca), ptr(cb), ptr(za), ptr(zb), _dt(ca), ptr(bias_a), ptr(bias_b), ptr(prev_cb),
+            ptr(prev_zb), B, T, D, ratio, 1 if overlap else 0, t0, rope_dims, rope_base, pos_offset, C.byref(bo),
+            out_rows, stream_handle(stream))
 
 
 def csa_quantize(x, out: Buf, *, rope_dims: int = 0, stream=None) -> None:
     D = x.shape[-1]
     rows = x.numel() // D
     bo = out.c()
-    check(lib().csa_quantize(ptr(x), rows, D, rope_dims, C.byref(bo), stream_handle(stream)))
+    _invoke("csa_quantize", ptr(x), rows, D, rope_dims, C.byref(bo), stream_handle(stream))
 
 
 def csa_index_scores(qI, wI, kI, q_pos, scores, *, ratio: int, stream=None) -> None:
@@ -207,8 +220,8 @@ def csa_index_scores(qI, wI, kI, q_pos, scores, *, ratio: int, stream=None) -> N
     _, kI_rows, _ = kb.shape
     N = scores.shape[-1]
     cq, ck = qb.c(), kb.c()
-    check(lib().csa_index_scores(C.byref(cq), ptr(wI), C.byref(ck), ptr(q_pos), B, Tq, HI, DI, N, kI_rows, ratio,
-                                 ptr(scores), stream_handle(stream)))
+    _invoke("csa_index_scores", C.byref(cq), ptr(wI), C.byref(ck), ptr(q_pos), B, Tq, HI, DI, N, kI_rows, ratio,
+            ptr(scores), stream_handle(stream))
 
 
 def csa_topk(scores, k: int, idx, count=None, *, ws=None, stream=None) -> None:
@@ -218,7 +231,7 @@ def csa_topk(scores, k: int, idx, count=None, *, ws=None, stream=None) -> None:
         rows *= d
     need = lib().csa_topk_workspace_size(rows, N, k)
     w, wb = _ws(need, scores.device, ws)
-    check(lib().csa_topk(ptr(scores), rows, N, k, ptr(idx), ptr(count), ptr(w), wb, stream_handle(stream)))
+    _invoke("csa_topk", ptr(scores), rows, N, k, ptr(idx), ptr(count), ptr(w), wb, stream_handle(stream), keep=(w,))
 
 
 def csa_sparse_mqa(q, q_pos, kv, idx, win, win_pos0, sink, out, *, N: int, n_win: int, softmax_scale: float,
@@ -231,9 +244,9 @@ def csa_sparse_mqa(q, q_pos, kv, idx, win, win_pos0, sink, out, *, N: int, n_win
     need = lib().csa_sparse_mqa_workspace_size(B, Tq, H, D, K, n_win)
     w, wbytes = _ws(need, q.device if not isinstance(q, Buf) else q.data.device, ws)
     cq, ck, cw, co = qb.c(), kvb.c(), wb_.c(), ob.c()
-    check(lib().csa_sparse_mqa(C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ptr(idx), K, C.byref(cw), ptr(win_pos0),
-                               Tw, ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
-                               C.byref(co), ptr(w), wbytes, stream_handle(stream)))
+    _invoke("csa_sparse_mqa", C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ptr(idx), K, C.byref(cw),
+            ptr(win_pos0), Tw, ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
+            C.byref(co), ptr(w), wbytes, stream_handle(stream), keep=(w,))
 
 
 def hca_dense_attn(q, q_pos, kv, win, win_pos0, sink, out, *, N: int, ratio: int, n_win: int, softmax_scale: float,
@@ -245,9 +258,9 @@ def hca_dense_attn(q, q_pos, kv, win, win_pos0, sink, out, *, N: int, ratio: int
     need = lib().hca_dense_attn_workspace_size(B, Tq, H, D, N, n_win)
     w, wbytes = _ws(need, qb.data.device, ws)
     cq, ck, cw, co = qb.c(), kvb.c(), wb_.c(), ob.c()
-    check(lib().hca_dense_attn(C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ratio, C.byref(cw), ptr(win_pos0), Tw,
-                               ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
-                               C.byref(co), ptr(w), wbytes, stream_handle(stream)))
+    _invoke("hca_dense_attn", C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ratio, C.byref(cw), ptr(win_pos0),
+            Tw, ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win, C.byref(co),
+            ptr(w), wbytes, stream_handle(stream), keep=(w,))
 
 
 def layer_desc(**kw) -> csa_layer_desc:
@@ -280,7 +293,7 @@ def csa_forward(desc: csa_layer_desc, io: dict, *, ws=None, stream=None) -> None
     need = csa_forward_workspace_size(desc)
     dev = Buf.of(io["q"]).data.device
     w, wbytes = _ws(need, dev, ws)
-    check(lib().csa_forward(C.byref(desc), C.byref(cio), ptr(w), wbytes, stream_handle(stream)))
+    _invoke("csa_forward", C.byref(desc), C.byref(cio), ptr(w), wbytes, stream_handle(stream), keep=(w, io))
 
 
 class ForwardCall:
@@ -303,3 +316,30 @@ class ForwardCall:
         st = self.fn(*self.args)
         if st != 0:
             check(st)
+
+
+class PreparedCall:
+    """One entry-point call with its arguments marshalled once, for repeated launches.
+
+    ``PreparedCall(csa_topk, scores, k, idx)`` runs the binding's argument handling
+    once and records the C call it would make; calling the object repeats that C call
+    on the same buffers. The object holds the tensors the call points at (and any
+    workspace the binding allocated) for as long as it lives."""
+
+    def __init__(self, entry, *args, **kwargs):
+        global _recording
+        if _recording is not None:
+            raise RuntimeError("PreparedCall cannot nest")
+        _recording = []
+        try:
+            entry(*args, **kwargs)
+            self.calls = _recording
+        finally:
+            _recording = None
+        self.refs = (args, kwargs)
+
+    def __call__(self) -> None:
+        for fn, args, _ in self.calls:
+            st = fn(*args)
+            if st != 0:
+                check(st)

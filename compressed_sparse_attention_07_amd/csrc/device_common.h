@@ -208,6 +208,17 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
                : "memory");
 }
 
+// Workgroups go to the 8 XCDs round-robin (block b runs on XCD b % 8), and each XCD
+// has its own L2.  This renumbering hands every XCD one contiguous range of logical
+// blocks, so blocks that read the same data (splits of one query token, neighbouring
+// tokens' overlapping selections) meet in one L2.  A tail of grid % 8 blocks keeps its
+// own numbers.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t grid) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t full = grid - grid % kXcd;
+  return b < full ? (b % kXcd) * (full / kXcd) + b / kXcd : b;
+}
+
 // a wave-uniform 64-bit value, moved to scalar registers
 __device__ __forceinline__ int64_t uni64(int64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));

@@ -61,20 +61,33 @@ struct Slots {
   int64_t b, p, nsel, wstart, nslots, wp0;
 };
 
-__device__ __forceinline__ Slots token_slots(const AttnArgs& a, int64_t bt) {
+// x / d for x >= 0, d >= 1, with 32-bit division whenever both fit in 32 bits
+__device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t d) {
+  if (((static_cast<uint64_t>(x) | static_cast<uint64_t>(d)) >> 32) == 0)
+    return static_cast<uint32_t>(x) / static_cast<uint32_t>(d);
+  return x / d;
+}
+
+// The slot ranges of token bt (sequence b, position p, window base wp0)
+__device__ __forceinline__ Slots slots_of(const AttnArgs& a, int64_t b, int64_t p, int64_t wp0) {
   Slots s;
-  s.b = bt / a.Tq;
-  s.p = a.q_pos[bt];
+  s.b = b;
+  s.p = p;
   if (a.sparse) {
     s.nsel = a.K;
   } else {
-    int64_t v = s.p / a.ratio;
+    int64_t v = s.p >= 0 ? div_nonneg(s.p, a.ratio) : s.p / a.ratio;
     s.nsel = v > a.N ? a.N : (v < 0 ? 0 : v);
   }
   s.wstart = s.p - a.n_win + 1 > 0 ? s.p - a.n_win + 1 : 0;
   s.nslots = s.nsel + (s.p - s.wstart + 1);
-  s.wp0 = a.win_pos0[s.b];
+  s.wp0 = wp0;
   return s;
+}
+
+__device__ __forceinline__ Slots token_slots(const AttnArgs& a, int64_t bt) {
+  const int64_t b = div_nonneg(bt, a.Tq);
+  return slots_of(a, b, a.q_pos[bt], a.win_pos0[b]);
 }
 
 // Source row of slot `slot`: returns entry row (>= 0) in kv, or window row in win
@@ -502,7 +515,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 constexpr int kDmaStages = 4;
 constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
 
-template <int NW>
+template <int NW, int R>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int D = 512;
   constexpr int NT = NW * 64;
@@ -526,24 +539,25 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  const int n_hg = a.H / a.hpw;
-  int64_t blk = blockIdx.x;
-  const int hg = static_cast<int>(blk % n_hg);
-  blk /= n_hg;
-  const int sp = static_cast<int>(blk % a.nsplit);
-  const int64_t bt = blk / a.nsplit;
+  // the grid has fewer than 2^32 blocks: 32-bit index arithmetic
+  const uint32_t n_hg = static_cast<uint32_t>(a.H / a.hpw);
+  const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
+  const int hg = __builtin_amdgcn_readfirstlane(static_cast<int>(blk % n_hg));
+  const uint32_t blk2 = blk / n_hg;
+  const int sp = __builtin_amdgcn_readfirstlane(static_cast<int>(blk2 % static_cast<uint32_t>(a.nsplit)));
+  const int64_t bt = __builtin_amdgcn_readfirstlane(static_cast<int>(blk2 / static_cast<uint32_t>(a.nsplit)));
   const int64_t s_lo = static_cast<int64_t>(sp) * a.sps;
-  // prologue: the queries (straight into the B-operand registers: lane (col, grp) holds
-  // q[head col][32 s + 8 grp .. + 8]), the range's entry indices and the positions are
-  // loaded together -- none depends on another
+  // prologue loads, in the order they are needed: the token's position and window base
+  // and the RoPE angles, the range's entry indices, then the queries (straight into the
+  // B-operand registers: lane (col, grp) holds q[head col][32 s + 8 grp .. + 8]).  Loads
+  // return in issue order, so the row loads the indices address go out while the
+  // queries are still in flight.
   const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
-  uint4 qraw[NS];
-  {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw + wid * 16 + col) * D + 8 * grp;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
-  }
+  const int64_t b_seq = div_nonneg(bt, a.Tq);
+  const int64_t p_pre = a.q_pos[bt];
+  const int64_t wp0_pre = a.win_pos0[b_seq];
+  const double th_pre = tid < R / 2 ? a.theta_rev[tid] : 0.0;  // R <= 128 < 2 NT
+  asm volatile("" ::: "memory");
   int32_t idx_pre[kDmaIdxCap / NT];
   const int64_t n_idx = a.sparse ? min(s_lo + a.sps, static_cast<int64_t>(a.K)) - s_lo : 0;
 #pragma unroll
@@ -551,21 +565,28 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const int64_t i = tid + static_cast<int64_t>(u) * NT;
     idx_pre[u] = i < n_idx ? a.idx[bt * a.K + s_lo + i] : 0;
   }
-  const Slots S = token_slots(a, bt);
+  asm volatile("" ::: "memory");  // keep the index loads ahead of the query loads
+  uint4 qraw[NS];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw + wid * 16 + col) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+  }
+  const Slots S = slots_of(a, b_seq, uni64(p_pre), uni64(wp0_pre));
   const int64_t s_hi = min(S.nslots, s_lo + a.sps);
   const int ntiles = s_hi > s_lo ? static_cast<int>((s_hi - s_lo + kKT - 1) / kKT) : 0;
   const int h = hg * a.hpw + wid * 16 + col;
-  const int nope = D - a.R;
+  constexpr int nope = D - R;  // the RoPE dims are the last R
   const double qpos = static_cast<double>(S.p + a.pos_offset);
   const uint16_t* kvp = static_cast<const uint16_t*>(a.kv);
   const uint16_t* winp = static_cast<const uint16_t*>(a.win);
 
-  for (int j = tid; j < a.R / 2; j += NT) {
-    const double th = a.theta_rev[j];
-    theta[j] = th;
+  if (tid < R / 2) {
+    theta[tid] = th_pre;
     float c, sn;
-    rope_cs_rev(qpos, th, &c, &sn);
-    qcs[j] = make_float2(c, sn);
+    rope_cs_rev(qpos, th_pre, &c, &sn);
+    qcs[tid] = make_float2(c, sn);
   }
 
 #pragma unroll
@@ -573,12 +594,10 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const int64_t i = tid + static_cast<int64_t>(u) * NT;
     if (i < n_idx) idx_s[i] = idx_pre[u];
   }
-  // every load the compiler tracks completes here, before the first row load it cannot
-  // see is issued (a later wait for these registers would also wait for the row loads)
-#pragma unroll
-  for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(qraw[s].x), "v"(qraw[s].y), "v"(qraw[s].z), "v"(qraw[s].w));
-  wait_vmcnt<0>();
-  __syncthreads();
+  // the LDS stores above (indices, angles) reach every wave; the query loads stay in
+  // flight.  The compiler's own waits for qraw count only the loads it knows of, which
+  // are issued before the row loads: such a wait can only be stricter than needed.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // source row of slot j of tile u; empty slots read the query's own window row (the
   // softmax masks them).  Every quantity here is wave-uniform.
@@ -615,7 +634,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     }
   };
   // window rows are raw: rotate their RoPE dims to each row's own position
-  const int RCH = a.R / 8;
+  constexpr int RCH = R / 8;
   auto rope_window_rows = [&](int st) {
     uint16_t* T = ring + st * STAGE;
     for (int item = tid; item < kKT * RCH; item += NT) {
@@ -1026,6 +1045,11 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
   if (!mfma) return p;
   const int64_t tokens = B * Tq;
   int hpw = dma ? head_group(H, kDmaMaxWaves) : base_hpw(H, D);
+  if (tokens == 0) {
+    p.hpw = hpw;
+    p.sps = kKT;
+    return p;
+  }
   int64_t units = tokens * (H / hpw);
   if (!dma) {
     // smaller head groups give more workgroups without split partials, but below these
@@ -1076,9 +1100,9 @@ int64_t max_slots_of(const AttnLaunch& L) {
   return (L.sparse ? static_cast<int64_t>(L.K) : L.N) + L.n_win;
 }
 
-// bf16 cache, D = 512, 2, 4 or 8 waves: the LDS-DMA kernel
+// bf16 cache, D = 512 with RoPE on the last 64 dims, 2, 4 or 8 waves: the LDS-DMA kernel
 bool dma_ok(const AttnLaunch& L) {
-  if (!mfma_ok(L) || L.kv.dtype != CSA_BF16 || L.D != 512) return false;
+  if (!mfma_ok(L) || L.kv.dtype != CSA_BF16 || L.D != 512 || L.rope_dims != 64) return false;
   if (L.sparse && max_slots_of(L) > 64 * kDmaIdxCap) return false;
   const int nw = head_group(L.H, kDmaMaxWaves) / 16;
   return nw == 2 || nw == 4 || nw == 8;
@@ -1164,9 +1188,9 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
     const int nw = P.hpw / 16;
     if (dma) {
       if (L.sparse && P.sps > kDmaIdxCap) return -1;  // excluded by the plan
-      if (nw == 8) hipLaunchKernelGGL(attn_dma_kernel<8>, dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
-      else if (nw == 4) hipLaunchKernelGGL(attn_dma_kernel<4>, dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
-      else hipLaunchKernelGGL(attn_dma_kernel<2>, dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+      if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+      else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_dma_kernel<2, 64>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
     } else {
     CSA_LAUNCH_MFMA(128)
     CSA_LAUNCH_MFMA(256)

@@ -121,3 +121,18 @@ def test_valid_call_without_gpu_reports_device_error(L):
     out = _buf()
     st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(out), 2, None)
     assert st == 5 and L.csa_last_error()
+
+
+def test_workspace_sizes_with_no_query_tokens(L):
+    """Sizes are host arithmetic: zero query tokens (a compress-only forward) need no
+    attention workspace and must not divide by zero."""
+    from compressed_sparse_attention_07_amd import layer_desc
+    assert L.csa_sparse_mqa_workspace_size(16, 0, 128, 512, 1024, 128) == 0
+    assert L.csa_sparse_mqa_workspace_size(0, 1, 128, 512, 1024, 128) == 0
+    assert L.hca_dense_attn_workspace_size(1, 0, 128, 512, 8192, 128) == 0
+    assert L.csa_topk_workspace_size(0, 32768, 1024) == 0
+    d = layer_desc(mode=0, B=16, T=4, t0=131068, Tq=0, cache_rows=32768, Tw=128, D=512, H=128, HI=64, DI=128, ratio=4,
+                   topk=1024, n_win=128, rope_dims=64, rope_base=10000.0, softmax_scale=0.044, stream_dtype=1)
+    assert L.csa_forward_workspace_size(C.byref(d)) >= 0
+    d.Tq = 1
+    assert L.csa_forward_workspace_size(C.byref(d)) > 0

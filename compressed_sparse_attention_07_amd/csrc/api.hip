@@ -85,6 +85,7 @@ csa_status check_buf(const csa_buf* b, const char* name) {
 csa_status check_rope(int32_t D, int32_t R, float base) {
   if (R < 0 || R > D || (R & 1) || ((D - R) & 1))
     return fail(CSA_ERR_SHAPE, "rope_dims=%d must be even, <= D=%d, with D-rope_dims even", R, D);
+  if (R > 128) return fail(CSA_ERR_UNSUPPORTED, "rope_dims=%d: at most 128 RoPE dims are supported", R);
   if (R > 0 && !(base > 0.f && std::isfinite(base))) return fail(CSA_ERR_SHAPE, "rope_base must be positive");
   return CSA_OK;
 }

@@ -6,14 +6,21 @@
 // channel across the 2m positions) and §2.3.2 (HCA: one block of m' positions, no
 // overlap); partial RoPE of the entry, §2.3.3; storage formats §2.3.4 / §3.4.
 //
-// Design (HBM stream-and-reduce): every input row is read exactly once.  A thread
-// owns 8 consecutive channels of one entry and a subset ("row group") of its
-// positions; consecutive lanes own consecutive channel chunks, so every wave load
-// is a contiguous row segment.  Each thread runs an online softmax over its rows
-// in batches of 8 (all loads of a batch are issued before any math), row groups
-// are merged in fixed order through LDS, then the epilogue applies RoPE and the
-// output format (fp32, bf16, FP8-mixed with a per-entry scale, MXFP4 with a
-// per-32 scale), reducing the scale maxima with LDS atomics.
+// Design (HBM stream-and-reduce): every input row is read exactly once, a thread owns
+// 8 consecutive channels of one entry, and consecutive lanes own consecutive channel
+// chunks, so every wave load is a contiguous row segment.  Loaded rows stay in the
+// input format in registers until the math needs them, which keeps the register count
+// low enough for four or five waves per SIMD: the loads of some waves then overlap the
+// arithmetic of others.  Three paths, chosen per launch:
+//   - at most 8 rows per entry (CSA with ratio 4): all of a thread's rows are loaded
+//     at once and each channel is reduced in one pass (max, then exp-weighted sums);
+//   - long non-overlapping blocks (HCA): row groups of consecutive rows, each walked
+//     in batches of 8 with a running (max, sum, weighted sum), merged in LDS in group
+//     order;
+//   - anything else: the general online softmax with row groups merged through LDS.
+// The epilogue applies RoPE and the output format (fp32, bf16, FP8-mixed with a
+// per-entry scale, MXFP4 with a per-32 scale), reducing the scale maxima with LDS
+// atomics.
 #include "device_common.h"
 #include "launch.h"
 
@@ -24,6 +31,43 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVec = 8;      // channels per thread
 constexpr int kBatch = 8;    // rows per online-softmax batch
+
+// Eight consecutive input channels as loaded: kept in the input format until the
+// math needs them, so a batch of rows in flight costs 4 (bf16) or 8 (f32) registers
+// per row and stream rather than 8 unpacked floats.
+template <typename TIn>
+struct Raw8;
+
+template <>
+struct Raw8<uint16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t x = i < 2 ? w.x : (i < 4 ? w.y : (i < 6 ? w.z : w.w));
+    return (i & 1) ? bf16hi(x) : bf16lo(x);
+  }
+};
+
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ float get(int i) const {
+    switch (i) {
+      case 0: return a.x;
+      case 1: return a.y;
+      case 2: return a.z;
+      case 3: return a.w;
+      case 4: return b.x;
+      case 5: return b.y;
+      case 6: return b.z;
+      default: return b.w;
+    }
+  }
+};
 
 template <typename TIn>
 __device__ __forceinline__ void load8(const TIn* p, float v[kVec]);
@@ -132,6 +176,8 @@ __device__ __forceinline__ int amax_words(int dtype, int D) {
   return dtype == CSA_MXFP4 ? D / 32 : 1;
 }
 
+// Kept small: the short-lived workgroups of the compression paths each read their
+// arguments, and a larger argument block measurably slows the bulk launches.
 struct CompressArgs {
   const void* ca;
   const void* cb;
@@ -144,9 +190,225 @@ struct CompressArgs {
   int64_t B, T, t0, out_rows, pos_offset;
   int D, ratio, overlap, R;
   int chunks, G, entries_per_wg;
+  int mode;  // kModeGeneral, kModeSmall or kModeGroups
   double log2_base;
   OutDesc out;
 };
+
+constexpr int kModeGeneral = 0;  // online softmax in batches of kBatch rows, 256 threads
+constexpr int kModeSmall = 1;    // at most kBatch rows per entry, 256 threads
+constexpr int kModeGroups = 2;   // no overlap, ratio a multiple of kBatch, row groups
+
+// Entry epilogue, shared by both compression paths: partial RoPE of the owner's
+// chunk at position pos_offset + ratio * I, the scale maxima of the quantized
+// formats, then the store.  Every thread of the workgroup calls it (it holds barriers).
+__device__ __forceinline__ void finish_entry(const CompressArgs& a, bool owner, int64_t b, int64_t I, int c,
+                                             float val[kVec], uint32_t* amax_entry) {
+  if (owner) {
+    const int d0 = c * kVec;
+    const int nope = a.D - a.R;
+    if (a.R > 0 && d0 + kVec > nope) {
+      const double pos = static_cast<double>(a.pos_offset + I * a.ratio);
+#pragma unroll
+      for (int ch = 0; ch < kVec; ch += 2) {
+        const int d = d0 + ch;
+        if (d >= nope) {
+          float cs, sn;
+          rope_cs(pos, (d - nope) / 2, a.R, a.log2_base, &cs, &sn);
+          const float x0 = val[ch], x1 = val[ch + 1];
+          val[ch] = x0 * cs - x1 * sn;
+          val[ch + 1] = x0 * sn + x1 * cs;
+        }
+      }
+    }
+  }
+  if (a.out.dtype == CSA_FP8MIX || a.out.dtype == CSA_MXFP4) {  // scales need the entry's maxima
+    __syncthreads();
+    if (owner) amax_chunk(a.out, c, val, amax_entry);
+    __syncthreads();
+  }
+  if (owner) store_chunk(a.out, b * a.out_rows + I, c, val, amax_entry);
+}
+
+// Entries of at most kBatch rows (CSA with ratio <= 4, HCA with ratio <= 8): one thread
+// per 8 channels of an entry loads all the entry's rows at once, kept in the input
+// format, then reduces each channel in one pass (max, then exp-weighted sums).  No
+// online rescaling and no row groups, so few registers stay live and more waves fit.
+template <typename TIn>
+__device__ __forceinline__ void compress_small(const CompressArgs& a, int64_t block, uint32_t* amax_lds) {
+  const int tid = threadIdx.x;
+  const int e_local = tid / a.chunks;
+  const int c = tid % a.chunks;
+  const int64_t n_entries = a.T / a.ratio;
+  const int64_t e_glob = block * a.entries_per_wg + e_local;
+  const bool active = e_local < a.entries_per_wg && e_glob < a.B * n_entries;
+  const int aw = amax_words(a.out.dtype, a.D);
+  for (int i = tid; i < a.entries_per_wg * aw && i < kThreads; i += kThreads) amax_lds[i] = 0u;
+
+  float val[kVec];
+  int64_t b = 0, I = 0;
+  if (active) {
+    b = e_glob / n_entries;
+    const int64_t il = e_glob % n_entries;
+    I = a.t0 / a.ratio + il;
+    const int r = a.ratio;
+    const int nrows = (a.overlap && I >= 1) ? 2 * r : r;  // <= kBatch
+    const int d0 = c * kVec;
+    const int64_t D = a.D;
+    const TIn* cA = static_cast<const TIn*>(a.ca) + (b * a.T + il * r) * D + d0;
+    const TIn* zA = static_cast<const TIn*>(a.za) + (b * a.T + il * r) * D + d0;
+    const TIn* cB = cA;
+    const TIn* zB = zA;
+    if (a.overlap) {
+      cB = il >= 1 ? static_cast<const TIn*>(a.cb) + (b * a.T + (il - 1) * r) * D + d0
+                   : static_cast<const TIn*>(a.prev_cb) + b * r * D + d0;
+      zB = il >= 1 ? static_cast<const TIn*>(a.zb) + (b * a.T + (il - 1) * r) * D + d0
+                   : static_cast<const TIn*>(a.prev_zb) + b * r * D + d0;
+    }
+    Raw8<TIn> z[kBatch], v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (q < nrows) {
+        const bool in_a = q < r;
+        const int64_t off = static_cast<int64_t>(in_a ? q : q - r) * D;
+        v[q].load((in_a ? cA : cB) + off);
+        z[q].load((in_a ? zA : zB) + off);
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < kVec; ++ch) {
+      float zc[kBatch];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (q < nrows) {
+          zc[q] = z[q].get(ch);
+          const float* bp = q < r ? a.bias_a : a.bias_b;  // bias rows: [ratio, D] per branch
+          if (bp) zc[q] += bp[(q < r ? q : q - r) * D + d0 + ch];
+          bm = fmaxf(bm, zc[q]);
+        }
+      }
+      float ss = 0.f, aa = 0.f;
+      if (bm != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          if (q < nrows) {
+            const float p = __expf(zc[q] - bm);
+            ss += p;
+            aa = fmaf(p, v[q].get(ch), aa);
+          }
+        }
+      }
+      val[ch] = aa / ss;
+    }
+  }
+  finish_entry(a, active, b, I, c, val, amax_lds + e_local * aw);
+}
+
+// Long non-overlapping blocks (HCA, ratio a multiple of kBatch): G row groups of
+// ratio / G consecutive rows.  A thread walks its group's rows of 8 channels in
+// batches of kBatch (the batch's loads kept in the input format and issued together),
+// reducing each batch in one pass and folding it into a running (max, sum, weighted
+// sum).  The G partials of every channel meet in LDS and one thread per channel merges
+// them in group order.  Small workgroups with few live registers let several
+// workgroups share a CU, so one's loads overlap another's arithmetic.
+template <typename TIn>
+__device__ __forceinline__ void compress_groups(const CompressArgs& a, int64_t block, float* part,
+                                                uint32_t* amax_lds) {
+  const int tid = threadIdx.x;
+  const int tpe = a.chunks * a.G;  // threads per entry
+  const int e_local = tid / tpe;
+  const int r_in = tid % tpe;
+  const int g = r_in / a.chunks;
+  const int c = r_in % a.chunks;
+  const int64_t n_entries = a.T / a.ratio;
+  const int64_t e_glob = block * a.entries_per_wg + e_local;
+  const bool active = e_local < a.entries_per_wg && e_glob < a.B * n_entries;
+  const int aw = amax_words(a.out.dtype, a.D);
+  const int D = a.D;
+  const int rpt = a.ratio / a.G;  // rows per thread, a multiple of kBatch
+  for (int i = tid; i < a.entries_per_wg * aw && i < kThreads; i += kThreads) amax_lds[i] = 0u;
+
+  int64_t b = 0, I = 0;
+  const int d0 = c * kVec;
+  // partial triples: part[((e_local * G + g) * D + d) * 3 + {max, sum, weighted sum}]
+  float* my = part + (static_cast<int64_t>(e_local * a.G + g) * D + d0) * 3;
+  if (active) {
+    b = e_glob / n_entries;
+    const int64_t il = e_glob % n_entries;
+    I = a.t0 / a.ratio + il;
+    const int64_t row0 = b * a.T + il * a.ratio + g * rpt;
+    const TIn* cp = static_cast<const TIn*>(a.ca) + row0 * D + d0;
+    const TIn* zp = static_cast<const TIn*>(a.za) + row0 * D + d0;
+    float m[kVec], sm[kVec], ac[kVec];
+#pragma unroll
+    for (int ch = 0; ch < kVec; ++ch) { m[ch] = -INFINITY; sm[ch] = 0.f; ac[ch] = 0.f; }
+    for (int k0 = 0; k0 < rpt; k0 += kBatch) {
+      Raw8<TIn> z[kBatch], v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        v[q].load(cp + static_cast<int64_t>(k0 + q) * D);
+        z[q].load(zp + static_cast<int64_t>(k0 + q) * D);
+      }
+#pragma unroll
+      for (int ch = 0; ch < kVec; ++ch) {
+        float zc[kBatch];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          zc[q] = z[q].get(ch);
+          if (a.bias_a) zc[q] += a.bias_a[(g * rpt + k0 + q) * D + d0 + ch];
+          bm = fmaxf(bm, zc[q]);
+        }
+        const float nm = fmaxf(m[ch], bm);
+        if (nm == -INFINITY) continue;  // every logit so far is -inf
+        const float sc = __expf(m[ch] - nm);  // 0 while m is -inf
+        float ss = sm[ch] * sc, aa = ac[ch] * sc;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const float p = __expf(zc[q] - nm);
+          ss += p;
+          aa = fmaf(p, v[q].get(ch), aa);
+        }
+        m[ch] = nm; sm[ch] = ss; ac[ch] = aa;
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < kVec; ++ch) {
+      my[3 * ch] = m[ch];
+      my[3 * ch + 1] = sm[ch];
+      my[3 * ch + 2] = ac[ch];
+    }
+  }
+  __syncthreads();
+  // merge the G groups of every channel in group order; the result overwrites group
+  // 0's weighted-sum slot of that channel (only this thread reads that channel)
+  const int nch = a.entries_per_wg * D;
+  for (int idx = tid; idx < nch; idx += kThreads) {
+    const int e = idx / D, d = idx % D;
+    if (block * a.entries_per_wg + e >= a.B * n_entries) continue;
+    float mm = -INFINITY, sum = 0.f, acc = 0.f;
+    for (int gg = 0; gg < a.G; ++gg) {
+      const float* o = part + (static_cast<int64_t>(e * a.G + gg) * D + d) * 3;
+      const float om = o[0];
+      const float nm = fmaxf(mm, om);
+      if (nm == -INFINITY) continue;
+      const float s1 = __expf(mm - nm), s2 = __expf(om - nm);
+      sum = sum * s1 + o[1] * s2;
+      acc = acc * s1 + o[2] * s2;
+      mm = nm;
+    }
+    part[(static_cast<int64_t>(e * a.G) * D + d) * 3 + 2] = acc / sum;
+  }
+  __syncthreads();
+  const bool owner = active && g == 0;
+  float val[kVec];
+  if (owner) {
+#pragma unroll
+    for (int ch = 0; ch < kVec; ++ch) val[ch] = my[3 * ch + 2];
+  }
+  finish_entry(a, owner, b, I, c, val, amax_lds + e_local * aw);
+}
 
 template <typename TIn>
 __device__ __forceinline__ void compress_block(const CompressArgs& a, int64_t block, float* part, uint32_t* amax_lds) {
@@ -177,57 +439,53 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int64_t bl
     const int r = a.ratio;
     // positions: [0, r) a-rows of block I; [r, 2r) b-rows of block I-1 (CSA, I >= 1)
     const int nrows = (a.overlap && I >= 1) ? 2 * r : r;
-    const TIn* ca = static_cast<const TIn*>(a.ca) + (b * a.T) * a.D;
-    const TIn* za = static_cast<const TIn*>(a.za) + (b * a.T) * a.D;
-    const TIn* cb = static_cast<const TIn*>(a.cb) + (b * a.T) * a.D;
-    const TIn* zb = static_cast<const TIn*>(a.zb) + (b * a.T) * a.D;
-    const TIn* pcb = static_cast<const TIn*>(a.prev_cb) + b * r * a.D;
-    const TIn* pzb = static_cast<const TIn*>(a.prev_zb) + b * r * a.D;
     const int d0 = c * kVec;
+    // row pointers of the two branches: position pos < r reads row pos of the a-block
+    // (rows [il r, il r + r) of ca / za), position r + j reads row j of the b-block
+    // (the previous block of cb / zb, or the caller's prev_cb / prev_zb for the first
+    // entry of the call)
+    const int64_t D = a.D;
+    const TIn* cA = static_cast<const TIn*>(a.ca) + (b * a.T + il * r) * D + d0;
+    const TIn* zA = static_cast<const TIn*>(a.za) + (b * a.T + il * r) * D + d0;
+    const TIn* cB = nullptr;
+    const TIn* zB = nullptr;
+    if (a.overlap) {
+      cB = il >= 1 ? static_cast<const TIn*>(a.cb) + (b * a.T + (il - 1) * r) * D + d0
+                   : static_cast<const TIn*>(a.prev_cb) + b * r * D + d0;
+      zB = il >= 1 ? static_cast<const TIn*>(a.zb) + (b * a.T + (il - 1) * r) * D + d0
+                   : static_cast<const TIn*>(a.prev_zb) + b * r * D + d0;
+    }
 
     for (int base = g; base < nrows; base += a.G * kBatch) {
-      float z[kBatch][kVec], v[kBatch][kVec];
+      Raw8<TIn> z[kBatch], v[kBatch];
       int nb = 0;
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int pos = base + q * a.G;
         if (pos < nrows) {
           nb = q + 1;
-          const TIn *cp, *zp;
-          const float* bp;
-          if (pos < r) {
-            const int64_t row = il * r + pos;
-            cp = ca + row * a.D + d0;
-            zp = za + row * a.D + d0;
-            bp = a.bias_a ? a.bias_a + pos * a.D + d0 : nullptr;
-          } else {
-            const int j = pos - r;
-            if (il >= 1) {
-              const int64_t row = (il - 1) * r + j;
-              cp = cb + row * a.D + d0;
-              zp = zb + row * a.D + d0;
-            } else {
-              cp = pcb + j * a.D + d0;
-              zp = pzb + j * a.D + d0;
-            }
-            bp = a.bias_b ? a.bias_b + j * a.D + d0 : nullptr;
-          }
-          load8<TIn>(cp, v[q]);
-          load8<TIn>(zp, z[q]);
-          if (bp) {
-            float4 b0 = reinterpret_cast<const float4*>(bp)[0];
-            float4 b1 = reinterpret_cast<const float4*>(bp)[1];
-            z[q][0] += b0.x; z[q][1] += b0.y; z[q][2] += b0.z; z[q][3] += b0.w;
-            z[q][4] += b1.x; z[q][5] += b1.y; z[q][6] += b1.z; z[q][7] += b1.w;
-          }
+          const bool in_a = pos < r;
+          const int64_t off = static_cast<int64_t>(in_a ? pos : pos - r) * D;
+          const TIn* cp = (in_a ? cA : cB) + off;
+          const TIn* zp = (in_a ? zA : zB) + off;
+          v[q].load(cp);
+          z[q].load(zp);
         }
       }
 #pragma unroll
       for (int ch = 0; ch < kVec; ++ch) {
+        float zc[kBatch];
         float bm = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q)
-          if (q < nb) bm = fmaxf(bm, z[q][ch]);
+        for (int q = 0; q < kBatch; ++q) {
+          if (q < nb) {
+            zc[q] = z[q].get(ch);
+            const int pos = base + q * a.G;  // bias rows: [ratio, D] per branch
+            const float* bp = pos < r ? a.bias_a : a.bias_b;
+            if (bp) zc[q] += bp[(pos < r ? pos : pos - r) * a.D + d0 + ch];
+            bm = fmaxf(bm, zc[q]);
+          }
+        }
         const float nm = fmaxf(m[ch], bm);
         if (nm == -INFINITY) continue;               // every logit so far is -inf
         const float sc = __expf(m[ch] - nm);         // 0 when m was -inf
@@ -235,9 +493,9 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int64_t bl
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
           if (q < nb) {
-            const float p = __expf(z[q][ch] - nm);
+            const float p = __expf(zc[q] - nm);
             ss += p;
-            aa = fmaf(p, v[q][ch], aa);
+            aa = fmaf(p, v[q].get(ch), aa);
           }
         }
         m[ch] = nm; s[ch] = ss; acc[ch] = aa;
@@ -278,31 +536,8 @@ __device__ __forceinline__ void compress_block(const CompressArgs& a, int64_t bl
   if (owner) {
 #pragma unroll
     for (int ch = 0; ch < kVec; ++ch) val[ch] = acc[ch] / s[ch];
-    // partial RoPE at position pos_offset + ratio * I
-    const int d0 = c * kVec;
-    const int nope = a.D - a.R;
-    if (a.R > 0 && d0 + kVec > nope) {
-      const double pos = static_cast<double>(a.pos_offset + I * a.ratio);
-#pragma unroll
-      for (int ch = 0; ch < kVec; ch += 2) {
-        const int d = d0 + ch;
-        if (d >= nope) {
-          float cs, sn;
-          rope_cs(pos, (d - nope) / 2, a.R, a.log2_base, &cs, &sn);
-          const float x0 = val[ch], x1 = val[ch + 1];
-          val[ch] = x0 * cs - x1 * sn;
-          val[ch + 1] = x0 * sn + x1 * cs;
-        }
-      }
-    }
   }
-  __syncthreads();
-  if (owner) amax_chunk(a.out, c, val, amax_lds + e_local * aw);
-  __syncthreads();
-  if (owner) {
-    const int64_t row = b * a.out_rows + I;
-    store_chunk(a.out, row, c, val, amax_lds + e_local * aw);
-  }
+  finish_entry(a, owner, b, I, c, val, amax_lds + e_local * aw);
 }
 
 // One launch runs up to two compressions (the KV stream and the indexer-key stream
@@ -312,16 +547,27 @@ struct CompressArgs2 {
   int64_t grid0;
 };
 
-template <typename TIn>
+template <int MODE>
+constexpr int mode_part_floats() {
+  return MODE == kModeGroups ? kThreads * kVec * 3 : (MODE == kModeSmall ? 1 : kThreads * (2 + kVec));
+}
+
+template <typename TIn, int MODE>
 __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs2 a) {
-  // LDS: row-group partials (m, s, acc[8]) and per-entry scale maxima
-  __shared__ float part[kThreads * (2 + kVec)];
-  __shared__ uint32_t amax_lds[kThreads];  // entries_per_wg * amax_words <= 256
+  // LDS: row-group partials and per-entry scale maxima
+  __shared__ float part[mode_part_floats<MODE>()];
+  __shared__ uint32_t amax_lds[kThreads];  // entries_per_wg * amax_words <= kThreads
   const int64_t blk = blockIdx.x;
-  if (blk < a.grid0)
-    compress_block<TIn>(a.job[0], blk, part, amax_lds);
-  else
-    compress_block<TIn>(a.job[1], blk - a.grid0, part, amax_lds);
+  if constexpr (MODE == kModeSmall) {
+    if (blk < a.grid0) compress_small<TIn>(a.job[0], blk, amax_lds);
+    else compress_small<TIn>(a.job[1], blk - a.grid0, amax_lds);
+  } else if constexpr (MODE == kModeGroups) {
+    if (blk < a.grid0) compress_groups<TIn>(a.job[0], blk, part, amax_lds);
+    else compress_groups<TIn>(a.job[1], blk - a.grid0, part, amax_lds);
+  } else {
+    if (blk < a.grid0) compress_block<TIn>(a.job[0], blk, part, amax_lds);
+    else compress_block<TIn>(a.job[1], blk - a.grid0, part, amax_lds);
+  }
 }
 
 struct QuantArgs {
@@ -353,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a) {
 namespace {
 
 // Fill the job description of one compression and return its block count.
-int64_t make_job(const CompressLaunch& L, CompressArgs& a) {
+int64_t make_job(const CompressLaunch& L, CompressArgs& a, bool general_only = false) {
   a = CompressArgs{};
   a.ca = L.ca; a.cb = L.cb; a.za = L.za; a.zb = L.zb;
   a.bias_a = L.bias_a; a.bias_b = L.bias_b;
@@ -364,21 +610,46 @@ int64_t make_job(const CompressLaunch& L, CompressArgs& a) {
   a.out = OutDesc{L.out.data, L.out.rope, L.out.scale, L.out.dtype, L.D, L.rope_dims};
   a.chunks = L.D / kVec;
   const int nrows = L.overlap ? 2 * L.ratio : L.ratio;
-  // row groups: enough to keep every wave busy on long blocks (HCA), one for CSA
-  int G = 1;
-  while (G * 2 * a.chunks <= kThreads && nrows / (G * 2) >= kBatch) G *= 2;
-  a.G = G;
-  a.entries_per_wg = kThreads / (a.chunks * G);
+  if (general_only) {
+    a.mode = kModeGeneral;  // set below
+  } else if (nrows <= kBatch) {
+    a.mode = kModeSmall;
+    a.G = 1;
+    a.entries_per_wg = kThreads / a.chunks;
+  } else if (!L.overlap && L.ratio % kBatch == 0 && a.chunks <= kThreads) {
+    // the most groups that fit the workgroup and split the block into whole batches
+    int G = 1;
+    while (2 * G * a.chunks <= kThreads && (L.ratio / kBatch) % (2 * G) == 0) G *= 2;
+    a.mode = kModeGroups;
+    a.G = G;
+    a.entries_per_wg = kThreads / (a.chunks * G);
+  }
+  if (general_only || (a.mode != kModeSmall && a.mode != kModeGroups)) {
+    // row groups: enough to keep every wave busy on long blocks
+    int G = 1;
+    while (G * 2 * a.chunks <= kThreads && nrows / (G * 2) >= kBatch) G *= 2;
+    a.mode = kModeGeneral;
+    a.G = G;
+    a.entries_per_wg = kThreads / (a.chunks * G);
+  }
   const int64_t n_entries = L.B * (L.T / L.ratio);
   return (n_entries + a.entries_per_wg - 1) / a.entries_per_wg;
 }
 
+template <int MODE>
+void launch_mode(const CompressArgs2& a, int64_t grid, int stream_dtype, hipStream_t stream) {
+  const dim3 g(static_cast<uint32_t>(grid)), t(kThreads);
+  if (stream_dtype == CSA_F32) hipLaunchKernelGGL((compress_kernel<float, MODE>), g, t, 0, stream, a);
+  else hipLaunchKernelGGL((compress_kernel<uint16_t, MODE>), g, t, 0, stream, a);
+}
+
 int launch(const CompressArgs2& a, int64_t grid, int stream_dtype, hipStream_t stream) {
   if (grid == 0) return 0;
-  if (stream_dtype == CSA_F32)
-    hipLaunchKernelGGL(compress_kernel<float>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, a);
+  const int mode = a.job[0].mode;  // the two jobs of one launch share a path
+  if (grid != a.grid0 && a.job[1].mode != mode) return -1;
+  if (mode == kModeSmall) launch_mode<kModeSmall>(a, grid, stream_dtype, stream);
+  else if (mode == kModeGroups) launch_mode<kModeGroups>(a, grid, stream_dtype, stream);
+  else launch_mode<kModeGeneral>(a, grid, stream_dtype, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -393,7 +664,11 @@ int launch_compress(const CompressLaunch& L, hipStream_t stream) {
 int launch_compress2(const CompressLaunch& L0, const CompressLaunch& L1, hipStream_t stream) {
   CompressArgs2 a{};
   a.grid0 = make_job(L0, a.job[0]);
-  const int64_t g1 = make_job(L1, a.job[1]);
+  int64_t g1 = make_job(L1, a.job[1]);
+  if (a.job[0].mode != a.job[1].mode) {  // both take the general path
+    a.grid0 = make_job(L0, a.job[0], true);
+    g1 = make_job(L1, a.job[1], true);
+  }
   return launch(a, a.grid0 + g1, L0.stream_dtype, stream);
 }
 

@@ -32,8 +32,8 @@
  *   position ratio*i.  `pos_offset` is added to every RoPE position and to nothing
  *   else (block visibility and windows use the plain positions).
  * - RoPE ([V4-CN] §2.3.3) rotates the last `rope_dims` dims in adjacent pairs
- *   (D-R+2j, D-R+2j+1) by angle pos * rope_base^(-2j/R); rope_dims is even and
- *   D - rope_dims is even.
+ *   (D-R+2j, D-R+2j+1) by angle pos * rope_base^(-2j/R); rope_dims is even,
+ *   D - rope_dims is even and rope_dims <= 128 (else CSA_ERR_UNSUPPORTED).
  */
 #ifndef CSA_H
 #define CSA_H

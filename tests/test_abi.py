@@ -52,6 +52,10 @@ def test_compress_rejects_bad_arguments(L):
     # odd rope dims
     st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 3, 10000.0, 0, C.byref(out), 2, None)
     assert st == 2
+    # more than 128 RoPE dims (D = 512, R = 256)
+    st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 512, 4, 1, 0, 256, 10000.0, 0, C.byref(out), 2,
+                        None)
+    assert st == 6 and b"128" in L.csa_last_error()
     # t0 > 0 without the previous block
     st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 4, 0, 10000.0, 0, C.byref(out), 3, None)
     assert st == 1

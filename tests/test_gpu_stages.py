@@ -65,6 +65,15 @@ COMPRESS_CASES = [
     (1, 96, 32, 8, False, 0, 0, "f32", "f32", False, 0),
     (2, 40, 512, 4, True, 0, 64, "bf16", "fp8mix", False, 0),
     (2, 40, 128, 4, True, 0, 0, "bf16", "mxfp4", False, 0),
+    # the online-softmax path: overlap with ratio 8, ratio not a multiple of 8, and
+    # blocks too long for one workgroup of row groups
+    (1, 96, 64, 8, True, 0, 16, "f32", "f32", True, 0),
+    (1, 96, 128, 12, False, 0, 64, "bf16", "bf16", False, 0),
+    (1, 512, 512, 256, False, 0, 64, "bf16", "bf16", False, 0),
+    # row groups with quantized outputs, bias and a partly filled last workgroup
+    (2, 256, 512, 16, False, 32, 64, "bf16", "fp8mix", True, 3),
+    (1, 256, 128, 32, False, 0, 0, "bf16", "mxfp4", False, 0),
+    (3, 160, 128, 32, False, 0, 0, "f32", "f32", False, 0),
 ]
 
 

@@ -52,13 +52,62 @@ struct TopkArgs {
   int32_t* count;           // final level: [rows] or NULL
 };
 
+constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one wave
+
 template <int NT>
 struct Shared {
   alignas(16) uint32_t hist[2][kBins];  // radix levels alternate between the two
   alignas(16) uint4 wave_abc[NT / WAVE];
   uint32_t wave_a[NT / WAVE];
   uint32_t info[3];
+  uint32_t ncand;
+  uint32_t cand[kFewCand];
 };
+
+// the float a finite key encodes (inverse of score_key)
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Wave 0's step of a selection level: lane l owns bins [PB l, PB l + PB) of hc; finds
+// the bin holding the remaining-th largest counted entry and writes (bin, entries in
+// higher bins, entries in the bin) to info.  The bins are read twice from LDS rather
+// than held in registers, which would cost PB registers in every thread.
+__device__ __forceinline__ void find_bin(const uint32_t* hc, uint32_t remaining, uint32_t* info) {
+  constexpr int PB = kBins / WAVE;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const uint4* hb = reinterpret_cast<const uint4*>(&hc[PB * lane]);
+  uint32_t local = 0;
+#pragma unroll 2
+  for (int j = 0; j < PB / 4; ++j) {
+    const uint4 v = hb[j];
+    local += v.x + v.y + v.z + v.w;
+  }
+  const uint32_t pre = wave_prefix_sum(local);
+  const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + local;  // this lane and those above
+  uint32_t above = incl - local;
+  asm volatile("" ::: "memory");  // re-read the bins below instead of keeping them
+  if (above < remaining && remaining <= incl) {  // the threshold bin is one of this lane's
+    uint32_t bin = 0, abv = 0, cnt = 0;
+#pragma unroll 1
+    for (int q = PB / 4 - 1; q >= 0; --q) {
+      const uint4 v = hb[q];
+      const uint32_t cq[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (above < remaining && remaining <= above + cq[j]) {
+          bin = static_cast<uint32_t>(PB * lane + 4 * q + j);
+          abv = above;
+          cnt = cq[j];
+        }
+        above += cq[j];
+      }
+    }
+    info[0] = bin;
+    info[1] = abv;
+    info[2] = cnt;
+  }
+}
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -69,25 +118,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* p, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), 0x00020000);
 }
 
-// PAIRS: input is (key, index) candidates; FINAL: write indices (and count) only.
-template <int NT, int PER, bool PAIRS, bool FINAL>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
-  constexpr int NW = NT / WAVE;
-  __shared__ Shared<NT> sh;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int64_t r = blockIdx.x / a.slices;
-  const int sl = static_cast<int>(blockIdx.x % a.slices);
+// Load slice blk's keys: PER consecutive entries per thread (scores become keys; a
+// candidate's index is read again only when it is written out).
+template <int NT, int PER, bool PAIRS>
+__device__ __forceinline__ void load_slice(const TopkArgs& a, int64_t blk, uint32_t (&key)[PER]) {
+  const int tid = static_cast<int>(threadIdx.x);
+  const int64_t r = static_cast<uint32_t>(blk) / static_cast<uint32_t>(a.slices);
+  const int sl = static_cast<int>(static_cast<uint32_t>(blk) % static_cast<uint32_t>(a.slices));
   const int64_t lo = static_cast<int64_t>(sl) * a.slice;
   const int64_t hi = min(a.n_in, lo + a.slice);
   const int64_t base = lo + static_cast<int64_t>(tid) * PER;  // first entry of this thread
-  const uint32_t K = static_cast<uint32_t>(a.k);
-
-  // ---- load: PER consecutive keys per thread (a candidate's index is read again only
-  //      when it is written out)
-  uint32_t key[PER];
-  const int32_t* ir = PAIRS ? a.in_idx + r * a.n_in + base : nullptr;
   if (PAIRS) {
     const uint32_t* kr = a.in_key + r * a.n_in + base;
     if (base + PER <= hi && aligned16(kr)) {
@@ -129,6 +169,24 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
   }
 
+}
+
+// Select slice blk's top-k from its keys (every thread of the workgroup calls this;
+// it holds barriers).
+template <int NT, int PER, bool PAIRS, bool FINAL>
+__device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, int64_t blk, uint32_t (&key)[PER]) {
+  constexpr int NW = NT / WAVE;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int64_t r = static_cast<uint32_t>(blk) / static_cast<uint32_t>(a.slices);
+  const int sl = static_cast<int>(static_cast<uint32_t>(blk) % static_cast<uint32_t>(a.slices));
+  const int64_t lo = static_cast<int64_t>(sl) * a.slice;
+  const int64_t hi = min(a.n_in, lo + a.slice);
+  const int64_t base = lo + static_cast<int64_t>(tid) * PER;  // first entry of this thread
+  const uint32_t K = static_cast<uint32_t>(a.k);
+  const int32_t* ir = PAIRS ? a.in_idx + r * a.n_in + base : nullptr;
+
   // ---- A: finite count, smallest and largest finite key
   uint32_t nfin = 0, kmax = 0, kmin1 = 0xffffffffu;  // kmin1 = min(key - 1): key 0 wraps to the top
 #pragma unroll
@@ -141,7 +199,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   kmax = wave_max_u32(kmax);
   kmin1 = wave_min_u32(kmin1);
   if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, kmax, kmin1, 0u);
-  for (int i = tid; i < kBins; i += NT) sh.hist[0][i] = 0u;  // the first radix level's histogram
+  for (int i = tid; i < 2 * kBins; i += NT) (&sh.hist[0][0])[i] = 0u;
+  if (tid == 0) sh.ncand = 0u;
   __syncthreads();
   nfin = 0;
   kmax = 0;
@@ -166,6 +225,56 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     theta = kmax;  // every finite key is equal: the first k by index
     ties = K;
   } else {
+    // Stage 0: a histogram of the values on a linear scale between the slice's extremes
+    // (bin = floor((v - vmin) * kBins / (vmax - vmin)), monotone in v, so each bin is a
+    // contiguous key range).  Scores spread over many bins, so the atomics rarely meet,
+    // and the threshold bin usually holds a few entries: one wave then ranks them
+    // exactly.  Otherwise (or if the scale is not finite) the radix levels below run.
+    bool found = false;
+    const float vlo = key_value(kmin);
+    const float scale = static_cast<float>(kBins) / (key_value(kmax) - vlo);
+    if (scale > 0.f && scale < INFINITY) {
+      auto vbin = [&](uint32_t kk) {
+        const uint32_t b = static_cast<uint32_t>((key_value(kk) - vlo) * scale);
+        return b < static_cast<uint32_t>(kBins) ? b : static_cast<uint32_t>(kBins - 1);
+      };
+      uint32_t* h1 = sh.hist[1];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (key[j] != 0u) atomicAdd(&h1[vbin(key[j])], 1u);
+        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      if (wid == 0) find_bin(h1, K, sh.info);
+      __syncthreads();
+      const uint32_t tb = sh.info[0], rem = K - sh.info[1], cnt = sh.info[2];
+      if (cnt <= kFewCand) {
+        // gather the threshold bin's keys (any order) and rank them in wave 0
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+          if (key[j] != 0u && vbin(key[j]) == tb) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
+        __syncthreads();
+        if (wid == 0) {
+          const uint32_t c = lane < static_cast<int>(cnt) ? sh.cand[lane] : 0u;
+          uint32_t gt = 0, eq = 0;
+          for (int i = 0; i < static_cast<int>(cnt); ++i) {
+            const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c), i));
+            gt += o > c ? 1u : 0u;
+            eq += o == c ? 1u : 0u;
+          }
+          // lanes holding the threshold key all write the same pair
+          if (lane < static_cast<int>(cnt) && gt < rem && rem <= gt + eq) {
+            sh.info[0] = c;
+            sh.info[1] = rem - gt;
+          }
+        }
+        __syncthreads();
+        theta = sh.info[0];  // raw key domain (koff = 0)
+        ties = sh.info[1];
+        found = true;
+      }
+    }
+    if (!found) {
     // work on w = key - kmin + 1 (finite keys in [1, span + 1], 0 = not finite)
     koff = kmin - 1u;
 #pragma unroll
@@ -192,35 +301,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       }
       __syncthreads();
       if (wid == 0) {
-        constexpr int PB = kBins / WAVE;  // bins per lane, held in registers
-        const uint4* hb = reinterpret_cast<const uint4*>(&hc[PB * lane]);
-        uint32_t c[PB];
-#pragma unroll
-        for (int j = 0; j < PB / 4; ++j) {
-          const uint4 v = hb[j];
-          c[4 * j] = v.x; c[4 * j + 1] = v.y; c[4 * j + 2] = v.z; c[4 * j + 3] = v.w;
-        }
-        uint32_t local = 0;
-#pragma unroll
-        for (int j = 0; j < PB; ++j) local += c[j];
-        const uint32_t pre = wave_prefix_sum(local);
-        const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + local;  // this lane and those above
-        uint32_t above = incl - local;
-        if (above < remaining && remaining <= incl) {  // the threshold bin is one of this lane's
-          uint32_t bin = 0, abv = 0, cnt = 0;
-#pragma unroll
-          for (int j = PB - 1; j >= 0; --j) {
-            if (above < remaining && remaining <= above + c[j]) {
-              bin = static_cast<uint32_t>(PB * lane + j);
-              abv = above;
-              cnt = c[j];
-            }
-            above += c[j];
-          }
-          sh.info[0] = bin;
-          sh.info[1] = abv;
-          sh.info[2] = cnt;
-        }
+        find_bin(hc, remaining, sh.info);
       } else if (nsh > 0) {
         uint32_t* hn = sh.hist[cur ^ 1];
         for (int i = tid - WAVE; i < kBins; i += NT - WAVE) hn[i] = 0u;
@@ -242,6 +323,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         break;
       }
       shift = nsh;
+    }
     }
   }
 
@@ -310,12 +392,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   if (FINAL && a.count && tid == 0) a.count[r] = static_cast<int32_t>(total_sel);
 }
 
+// PAIRS: input is (key, index) candidates; FINAL: write indices (and count) only.
+template <int NT, int PER, bool PAIRS, bool FINAL>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
+  __shared__ Shared<NT> sh;
+  uint32_t key[PER];
+  load_slice<NT, PER, PAIRS>(a, blockIdx.x, key);
+  select_slice<NT, PER, PAIRS, FINAL>(a, sh, blockIdx.x, key);
+}
+
 // workgroup shapes: (threads, keys per thread), slice capacity = threads * keys
 struct Shape {
   int nt, per;
   int64_t cap() const { return static_cast<int64_t>(nt) * per; }
 };
-constexpr Shape kShapes[] = {{256, 16}, {512, 16}, {1024, 16}};
+// 16384-entry slices take 512 threads of 32 entries: two workgroups share a CU, so the
+// barrier-separated phases of one overlap the other's
+constexpr Shape kShapes[] = {{256, 16}, {512, 16}, {512, 32}};
 
 Shape shape_for(int64_t n) {
   for (const Shape& s : kShapes)
@@ -323,12 +416,16 @@ Shape shape_for(int64_t n) {
   return kShapes[2];
 }
 
+template <int NT, int PER, bool PAIRS, bool FINAL>
+void launch_nt(int64_t blocks, const TopkArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((topk_kernel<NT, PER, PAIRS, FINAL>), dim3(static_cast<uint32_t>(blocks)), dim3(NT), 0, stream, a);
+}
+
 template <bool PAIRS, bool FINAL>
 void launch_shape(const Shape& s, int64_t blocks, const TopkArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(blocks));
-  if (s.nt == 256) hipLaunchKernelGGL((topk_kernel<256, 16, PAIRS, FINAL>), grid, dim3(256), 0, stream, a);
-  else if (s.nt == 512) hipLaunchKernelGGL((topk_kernel<512, 16, PAIRS, FINAL>), grid, dim3(512), 0, stream, a);
-  else hipLaunchKernelGGL((topk_kernel<1024, 16, PAIRS, FINAL>), grid, dim3(1024), 0, stream, a);
+  if (s.nt == 256) launch_nt<256, 16, PAIRS, FINAL>(blocks, a, stream);
+  else if (s.per == 16) launch_nt<512, 16, PAIRS, FINAL>(blocks, a, stream);
+  else launch_nt<512, 32, PAIRS, FINAL>(blocks, a, stream);
 }
 
 // Selection levels: input entries per row, slice length and slices per row of each.

@@ -242,6 +242,31 @@ def test_topk(rows, N, k):
     assert np.array_equal(idx.cpu().numpy(), wi)
 
 
+@pytest.mark.parametrize("N,k", [(20000, 1024), (20000, 37), (3000, 700)])
+def test_topk_value_spreads(N, k):
+    """Rows whose values exercise both ways of finding the threshold: the linear-scale
+    histogram with a small threshold bin, and the radix levels it falls back to (a
+    crowded threshold bin, a value range too wide or too narrow for the scale)."""
+    say(f"topk spreads N={N} k={k}")
+    g = Gen(77 + N + k, DEV)
+    s = g.normal((7, N))
+    s[0] = torch.round(s[0] * 1024) / 1024                 # ties inside small bins
+    s[1, ::97] = 3e38                                       # range overflows
+    s[1, 1::97] = -3e38
+    s[2] = torch.arange(N, device=DEV, dtype=torch.float32) % 50 * 1e-45  # denormals only
+    s[3, torch.rand(N, generator=g.g, device=DEV) < 0.95] = 0.25  # crowded threshold bin
+    s[4, 5] = 1e30                                          # one outlier
+    s[5] = s[5] * 1e-30                                     # small normal values
+    s[6, ::3] = -float("inf")
+    idx = torch.empty((7, k), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((7,), dtype=torch.int32, device=DEV)
+    csa.csa_topk(s, k, idx, cnt)
+    torch.cuda.synchronize()
+    wi, wc = O.topk(s.cpu().numpy().astype(np.float64), k)
+    assert np.array_equal(cnt.cpu().numpy(), wc)
+    assert np.array_equal(idx.cpu().numpy(), wi)
+
+
 # ------------------------------------------------------------------ attention
 
 

@@ -88,7 +88,7 @@ class Stage:
     run: object                 # fn(i) launching the stage on layer i % layers
     bytes: float                # algorithmic bytes per launch
     flops: float                # algorithmic FLOP per launch
-    kernel: str                 # dominant kernel's name prefix
+    kernel: str                 # the kernels one launch of the stage runs, joined by "+"
     src: tuple                  # its source files
     peak_flops: float = MFMA_BF16_PEAK
 
@@ -314,6 +314,13 @@ def build_workload(key: str, layers: int, dev: str = "cuda") -> Workload:
     return wl
 
 
+def _attn_kernels(ws, M) -> str:
+    """The attention kernels one call launches: the main kernel, plus the combine kernel
+    when the key range is split (the call then needs a workspace for the partials)."""
+    main = "attn_dma_kernel" if M["kv_format"] != "fp8mix" and M["D"] == 512 and M["R"] == 64 else "attn_mfma_kernel"
+    return main + ("+attn_combine_kernel" if ws.numel() > 1 else "")
+
+
 def _add_stages(wl: Workload, csa, torch, dev):
     """Per-stage launches with the step's shapes, and their algorithmic work."""
     M = wl.meta
@@ -354,7 +361,8 @@ def _add_stages(wl: Workload, csa, torch, dev):
         mx = M["ik_format"] == "mxfp4"
         wl.stages["index_scores"] = Stage(
             st_index, B * N * ik_entry + B * Tq * (HI * q_entry + HI * 4 + N * 4), 2.0 * HI * DI * sum_vis,
-            "index_mxfp4_kernel" if mx else "index_mfma_kernel", ("indexer.hip",),
+            "index_mxfp4_kernel" if mx else ("index_prefill_kernel" if Tq >= 16 else "index_mfma_kernel"),
+            ("indexer.hip",),
             MFMA_FP4_PEAK if mx else MFMA_BF16_PEAK)
         wl.stages["topk"] = Stage(st_topk, B * Tq * (N * 4 + k * 4), 0.0, "topk_kernel", ("topk.hip",))
         mqa_ws = torch.empty(max(1, csa.lib().csa_sparse_mqa_workspace_size(B, Tq, H, D, k, W)), dtype=torch.uint8,
@@ -370,7 +378,7 @@ def _add_stages(wl: Workload, csa, torch, dev):
         # algorithmic bytes: every distinct entry once (a prefill chunk's selections overlap), q, out, indices
         uniq = min(sum(keys), B * (N + M["Tw"]))
         wl.stages["sparse_mqa"] = Stage(st_attn, uniq * kv_entry + B * Tq * (4 * H * D + 4 * k),
-                                        4.0 * H * D * sum(keys), "attn_", ("mqa.hip",))
+                                        4.0 * H * D * sum(keys), _attn_kernels(mqa_ws, M), ("mqa.hip",))
         wl.stages["_prime"] = Stage(lambda i: (st_index(i), st_topk(i)), 0, 0, "", ())
     else:
         mqa_ws = torch.empty(max(1, csa.lib().hca_dense_attn_workspace_size(B, Tq, H, D, N, W)), dtype=torch.uint8,
@@ -385,7 +393,7 @@ def _add_stages(wl: Workload, csa, torch, dev):
         keys = [v + min(W, int(p) + 1) for row, prow in zip(vis, pos.tolist()) for v, p in zip(row, prow)]
         uniq = B * (N + M["Tw"]) if Tq > 1 else sum(keys)
         wl.stages["dense_attn"] = Stage(st_attn, uniq * kv_entry + B * Tq * 4 * H * D, 4.0 * H * D * sum(keys),
-                                        "attn_", ("mqa.hip",))
+                                        _attn_kernels(mqa_ws, M), ("mqa.hip",))
 
 
 def _prepare_stages(wl: Workload, csa):
@@ -417,8 +425,11 @@ def _short(name: str) -> str:
     return name.replace("(anonymous namespace)::", "").replace("void ", "").replace("csa::", "").split("(")[0]
 
 
-def summarize_trace(db_path: str, out: str, command: str):
-    """Per-kernel duration summary of a `rocprofv3 --kernel-trace` database (rocpd SQLite)."""
+def summarize_trace(db_path: str, out: str, command: str, kernel: str = ""):
+    """Per-kernel duration summary of a `rocprofv3 --kernel-trace` database (rocpd SQLite).
+
+    With `kernel` ("a" or "a+b": the kernels one stage launch runs), a last line gives
+    the sum of their average durations, the figure bench.py's roofline time matches."""
     import sqlite3
     cur = sqlite3.connect(db_path).cursor()
     rows = cur.execute("select name, count(*), avg(duration), min(duration), max(duration), "
@@ -426,22 +437,32 @@ def summarize_trace(db_path: str, out: str, command: str):
                        "order by sum(duration) desc").fetchall()
     lines = ["# rocprofv3 kernel-trace summary", f"# command: {command}",
              f"# {'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s} {'wgs':>7s}"]
+    avg = {}
     for n, c, av, mn, mx, tot, wgs in rows:
         lines.append(f"{_short(n)[:60]:60s} {c:6d} {av / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} "
                      f"{tot / 1e3:10.1f} {wgs:7.0f}")
+        avg.setdefault(_short(n).split("<")[0], av / 1e3)
+    if kernel:
+        parts = [avg.get(kn, float("nan")) for kn in kernel.split("+")]
+        lines.append(f"# stage kernels {kernel}: average durations {' + '.join(f'{p:.2f}' for p in parts)} = "
+                     f"{sum(parts):.2f} us per launch")
     open(out, "w").write("\n".join(lines) + "\n")
-    print("\n".join(lines[:16]))
+    print("\n".join(lines[:16] + lines[-1:]))
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: str, command: str, workload: str):
-    """HBM traffic per launch of `kernel` from FETCH_SIZE / WRITE_SIZE counter runs.
+    """HBM traffic per launch of `kernel` (or of kernels "a+b" launched together) from
+    FETCH_SIZE / WRITE_SIZE counter runs.
 
     Both counters (KiB per dispatch) are scaled by what they read for the copy probe
-    (torch.neg over 1 GiB: 1 GiB read, 1 GiB written).  Dispatches of `kernel` are
-    grouped by grid size and the most frequent grid (the timed step's) is reported.
+    (torch.neg over 1 GiB: 1 GiB read, 1 GiB written).  Dispatches of each kernel are
+    grouped by grid size and the most frequent grid (the timed step's) is reported;
+    the traffic of kernels launched together is summed.
     """
     import collections
     import csv
+
+    names = kernel.split("+")
 
     def load(path, counter):
         per = collections.defaultdict(list)
@@ -452,37 +473,47 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: st
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
             if "neg_kernel" in name:  # only the copy probe calls torch.neg
                 probe.append(v)
-            elif _short(name).startswith(kernel):
-                per[(_short(name), int(r["Grid_Size"]))].append(v)
+            else:
+                for kn in names:
+                    if _short(name).startswith(kn):
+                        per[(kn, _short(name), int(r["Grid_Size"]))].append(v)
         return per, probe
 
     fetch, pf = load(fetch_csv, "FETCH_SIZE")
     write, pw = load(write_csv, "WRITE_SIZE")
     if not pf or not pw or not fetch:
         raise SystemExit(f"missing probe or kernel dispatches (probe {len(pf)}/{len(pw)}, kernel {len(fetch)})")
-    key = max(fetch, key=lambda kk: len(fetch[kk]))
     kib = COPY_PROBE_BYTES / 1024
     f_fac = kib / (sum(pf) / len(pf))
     w_fac = kib / (sum(pw) / len(pw))
-    f_avg = sum(fetch[key]) / len(fetch[key])
-    w_avg = sum(write[key]) / len(write[key]) if write.get(key) else 0.0
-    traffic = (f_avg * f_fac + w_avg * w_fac) * 1024
-    lines = [f"# HBM traffic per launch of {key[0]} (most frequent grid: {key[1]} threads), workload {workload}",
+    lines = [f"# HBM traffic per launch of {kernel}, workload {workload}",
              f"# command (FETCH_SIZE pass): {command.replace('@COUNTER@', 'FETCH_SIZE')}",
              f"# command (WRITE_SIZE pass): {command.replace('@COUNTER@', 'WRITE_SIZE')}",
              f"# summarised by: python bench.py --summarize-pmc <fetch.csv> <write.csv> --kernel {kernel}",
-             f"kernel = {key[0]}", f"grid_threads = {key[1]}", f"dispatches = {len(fetch[key])}",
-             f"fetch_kib_per_dispatch = {f_avg:.1f}", f"write_kib_per_dispatch = {w_avg:.1f}",
              f"probe_fetch_kib = {sum(pf) / len(pf):.1f}", f"probe_write_kib = {sum(pw) / len(pw):.1f}",
-             f"fetch_scale = {f_fac:.4f}", f"write_scale = {w_fac:.4f}",
-             f"traffic_bytes_per_launch = {traffic:.0f}", f"source_hash = {src}"]
+             f"fetch_scale = {f_fac:.4f}", f"write_scale = {w_fac:.4f}"]
+    traffic = 0.0
+    for kn in names:
+        keys = [kk for kk in fetch if kk[0] == kn]
+        if not keys:
+            raise SystemExit(f"no dispatches of {kn}")
+        key = max(keys, key=lambda kk: len(fetch[kk]))
+        f_avg = sum(fetch[key]) / len(fetch[key])
+        w_avg = sum(write[key]) / len(write[key]) if write.get(key) else 0.0
+        t = (f_avg * f_fac + w_avg * w_fac) * 1024
+        traffic += t
+        lines += [f"kernel = {key[1]} (most frequent grid: {key[2]} threads, {len(fetch[key])} dispatches)",
+                  f"  fetch_kib_per_dispatch = {f_avg:.1f}", f"  write_kib_per_dispatch = {w_avg:.1f}",
+                  f"  traffic_bytes = {t:.0f}"]
+    lines += [f"traffic_bytes_per_launch = {traffic:.0f}", f"source_hash = {src}"]
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
 KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip",),
                   "attn_combine_kernel": ("mqa.hip",), "index_mfma_kernel": ("indexer.hip",),
-                  "index_mxfp4_kernel": ("indexer.hip",), "topk_kernel": ("topk.hip",),
+                  "index_mxfp4_kernel": ("indexer.hip",), "index_prefill_kernel": ("indexer.hip",),
+                  "topk_kernel": ("topk.hip",),
                   "compress_kernel": ("compress.hip",)}
 
 
@@ -508,13 +539,13 @@ def main():
     ap.add_argument("--out", help="summary file")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.out, args.profile_cmd)
+        summarize_trace(args.summarize_trace, args.out, args.profile_cmd, args.kernel)
         return
     if args.summarize_pmc:
         tag = WORKLOAD_TAGS[args.config]
         out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{tag}_pmc.txt")
-        summarize_pmc(*args.summarize_pmc, args.kernel, src_hash(*KERNEL_SOURCES[args.kernel]), out,
-                      args.profile_cmd, tag)
+        srcs = sorted({f for kn in args.kernel.split("+") for f in KERNEL_SOURCES[kn]})
+        summarize_pmc(*args.summarize_pmc, args.kernel, src_hash(*srcs), out, args.profile_cmd, tag)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -577,8 +608,6 @@ def main():
     else:
         achieved, peak, unit = dom.flops / times[dom_name] / 1e12, dom.peak_flops / 1e12, "TFLOP/s"
     kern = dom.kernel
-    if kern == "attn_":
-        kern = "attn_dma_kernel" if wl.meta["kv_format"] != "fp8mix" else "attn_mfma_kernel"
     traffic = read_traffic(f"{kern}_{wl.name}_pmc.txt", src_hash(*dom.src))
     roofline = dict(kernel=kern, stage=dom_name, bound=stage_out[dom_name]["bound"], achieved=round(achieved, 2),
                     peak=peak, unit=unit, frac=round(achieved / peak, 4), traffic=traffic,

@@ -818,28 +818,39 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
 // The split weights exp(m_i - M) * l_i are formed once per wave (lane i holds split
 // i) and broadcast; every lane issues all its partial loads before combining.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int kBatchSplits = 16;  // partial loads in flight per lane
   const int lane = threadIdx.x & 63;
   const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (th >= a.B * a.Tq * a.H) return;
   const int h = static_cast<int>(th % a.H);
   const int64_t bt = th / a.H;
   const int ns = a.nsplit;
+  const int d0 = 8 * lane;
+  const bool on = d0 < a.D;
+  // every load this wave needs is issued before any is waited for: the sink, the
+  // position, the split statistics and the first batch of partial rows
+  const float sk = a.sink[h];
+  const int64_t qp = a.q_pos[bt];
   const float2 ml = lane < ns ? a.part_ml[th * ns + lane] : make_float2(-INFINITY, 0.f);
+  const uint16_t* pb = a.part_o + (th * ns) * a.D + d0;
+  uint4 pv[kBatchSplits];
+#pragma unroll
+  for (int u = 0; u < kBatchSplits; ++u)
+    pv[u] = (on && u < ns) ? *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(u) * a.D)
+                           : make_uint4(0, 0, 0, 0);
   const float M = wave_max(ml.x);
   const float wgt = (ml.x == -INFINITY) ? 0.f : __expf(ml.x - M) * ml.y;
   const float L = wave_sum(wgt);
-  const int d0 = 8 * lane;
-  const bool on = d0 < a.D;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const uint16_t* pb = a.part_o + (th * ns) * a.D + d0;
-  for (int i0 = 0; i0 < ns; i0 += 8) {
-    uint4 pv[8];
+  for (int i0 = 0; i0 < ns; i0 += kBatchSplits) {
+    if (i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      pv[u] = (on && i0 + u < ns) ? *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(i0 + u) * a.D)
-                                   : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < kBatchSplits; ++u)
+        pv[u] = (on && i0 + u < ns) ? *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(i0 + u) * a.D)
+                                    : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kBatchSplits; ++u) {
       const float w = __shfl(wgt, (i0 + u) & 63, WAVE);
       if (i0 + u < ns) {
         o[0] = fmaf(w, bf16lo(pv[u].x), o[0]); o[1] = fmaf(w, bf16hi(pv[u].x), o[1]);
@@ -850,7 +861,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     }
   }
   if (!on) return;
-  const float sk = a.sink[h];
   float inv;
   if (sk == INFINITY) inv = 0.f;
   else if (sk == -INFINITY) inv = 1.f / L;
@@ -859,7 +869,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int e = 0; e < 8; ++e) o[e] *= inv;
   const int nope = a.D - a.R;
   if (d0 + 8 > nope) {
-    const double qpos = static_cast<double>(a.q_pos[bt] + a.pos_offset);
+    const double qpos = static_cast<double>(qp + a.pos_offset);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       if (d0 + e >= nope) {

@@ -779,37 +779,47 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   l_tot += __shfl_xor(l_tot, 16, WAVE);
   l_tot += __shfl_xor(l_tot, 32, WAVE);
 
+  // The result rows (normalised partials, or the final output) leave through LDS: each
+  // lane holds 4 dims of one head, so direct stores would write 32-byte pieces of 16
+  // rows; staged in the ring (free once every wave is past its last tile), each store
+  // writes one 1 KiB row.
   const int64_t th = bt * a.H + h;
-  if (a.nsplit > 1) {
-    uint16_t* po = a.part_o + (th * a.nsplit + sp) * D;
-    const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<uint2*>(po + 16 * db + 4 * grp) =
-          make_uint2(pack_bf16x2(acc[db][0] * il, acc[db][1] * il), pack_bf16x2(acc[db][2] * il, acc[db][3] * il));
-    if (grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
-    return;
+  const bool part = a.nsplit > 1;
+  float scl;
+  if (part) {
+    scl = l_tot > 0.f ? 1.f / l_tot : 0.f;  // normalised partial: a convex combination of keys
+  } else {
+    const float sk = a.sink[h];
+    if (sk == INFINITY) scl = 0.f;
+    else if (sk == -INFINITY) scl = 1.f / l_tot;
+    else scl = 1.f / (l_tot + __expf(sk - m_run));
   }
-  const float sk = a.sink[h];
-  float inv;
-  if (sk == INFINITY) inv = 0.f;
-  else if (sk == -INFINITY) inv = 1.f / l_tot;
-  else inv = 1.f / (l_tot + __expf(sk - m_run));
-  uint16_t* op = static_cast<uint16_t*>(a.out) + th * D;
+  __syncthreads();  // every wave is done reading the ring
+  uint16_t* rows = ring + wid * 16 * KP;  // this wave's 16 result rows, pitch KP
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int d0 = 16 * db + 4 * grp;
-    float v[4] = {acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv};
+    float v[4] = {acc[db][0] * scl, acc[db][1] * scl, acc[db][2] * scl, acc[db][3] * scl};
+    if (!part && d0 >= nope) {
+      // rotate back by the query position: angle -> -angle
 #pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      if (d0 + e >= nope) {
+      for (int e = 0; e < 4; e += 2) {
         const float2 cs = qcs[(d0 + e - nope) / 2];
         const float x0 = v[e], x1 = v[e + 1];
         v[e] = x0 * cs.x + x1 * cs.y;
         v[e + 1] = x1 * cs.x - x0 * cs.y;
       }
     }
-    *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    *reinterpret_cast<uint2*>(rows + col * KP + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+  if (part && grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
+  // lane l moves dims [8 l, 8 l + 8) of each of the wave's 16 rows (written by this wave)
+  const int64_t h0 = bt * a.H + hg * a.hpw + wid * 16;  // the wave's first (token, head) row
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r) {
+    const uint4 v = *reinterpret_cast<const uint4*>(rows + r * KP + 8 * lane);
+    uint16_t* dst = part ? a.part_o + ((h0 + r) * a.nsplit + sp) * D : static_cast<uint16_t*>(a.out) + (h0 + r) * D;
+    *reinterpret_cast<uint4*>(dst + 8 * lane) = v;
   }
 }
 

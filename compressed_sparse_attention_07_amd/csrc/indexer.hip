@@ -5,12 +5,14 @@
 //
 // bf16 path: one wave owns one query token and a contiguous range of entries.  The
 // token's indexer queries [HI, DI] stay in registers as the MFMA A operand (heads =
-// rows); each 16-entry tile of keys is loaded straight from HBM into the B operand
-// (16 lanes x 64 contiguous bytes per load), multiplied with
-// v_mfma_f32_16x16x32_bf16, and reduced in the epilogue: every lane applies ReLU
-// and the head weights to the 4 heads x 1 entry it holds per head block, two
-// cross-lane adds finish the sum over heads, and each lane stores one score of a
-// 64-entry run (one coalesced 256-byte store per iteration).
+// rows); the wave streams its keys through a private LDS ring (whole contiguous KiBs
+// per direct global->LDS load, 16-byte chunks XOR-swizzled by entry), reads each
+// 16-entry tile back as the B operand, multiplies with v_mfma_f32_16x16x32_bf16, and
+// reduces in the epilogue: every lane applies ReLU and the head weights to the 4
+// heads x 1 entry it holds per head block, two cross-lane adds finish the sum over
+// heads, and each lane stores one score of a 64-entry run (one coalesced 256-byte
+// store per four tiles).  Rows longer than 256 bytes load the B operand straight from
+// HBM instead (16 lanes x 64 contiguous bytes per load).
 //
 // Prefill path (bf16, many queries per sequence): a workgroup of 8 waves owns 16
 // queries of one sequence and a range of keys.  Key tiles (128 keys) are brought into
@@ -221,6 +223,128 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
   }
 }
 
+
+// Streaming variant of the same work split (one wave per token and entry range, no
+// key sharing between waves): loading a 16-entry B operand straight from HBM reads
+// 64 bytes from each of 16 rows per instruction, which streams measurably slower than
+// whole contiguous KiBs.  Here each wave instead copies its rows into a private LDS
+// ring of NST stages (16 TPS entries each) with direct global->LDS loads: every
+// instruction fetches one contiguous KiB (RB-byte rows, the 16-byte chunks of a row
+// XOR-swizzled by the entry index through the per-lane addresses), and the operand is
+// read back from LDS with conflict-free 16-byte reads.  A wave only ever reads the
+// stages it filled itself, so the loop has no barrier: the wave's own vmcnt orders
+// its loads.
+template <int STEP, int MAXL>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (MAXL == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXL) wait_vmcnt<STEP * MAXL>();
+    else wait_stage<STEP, MAXL - 1>(later);
+  }
+}
+
+template <int HB, int KS, int TPS, int NST>
+__global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexLaunch a, int keys_per_wave,
+                                                                          int64_t waves_per_token) {
+  constexpr int DI = 32 * KS;
+  constexpr int RB = 2 * DI;             // bytes per key row
+  constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  constexpr int KPS = 16 * TPS;          // entries per stage
+  constexpr int STAGE_B = KPS * RB;
+  constexpr int DPS = STAGE_B / 1024;    // direct loads per stage
+  static_assert(DPS >= 1 && DPS * 1024 == STAGE_B, "a stage is whole KiBs");
+  static_assert(NST >= 2 && DPS * (NST - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWavesPerWG][NST * STAGE_B];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + wid;
+  if (wave >= a.B * a.Tq * waves_per_token) return;  // whole waves only
+  const int64_t bt = wave / waves_per_token;
+  const int64_t b = bt / a.Tq;
+  const int64_t s_begin = (wave % waves_per_token) * keys_per_wave;
+  const int64_t s_end = min(s_begin + keys_per_wave, a.N);
+  int64_t vis = a.q_pos[bt] / a.ratio;
+  vis = vis > a.N ? a.N : (vis < 0 ? 0 : vis);
+  const int64_t vis_end = uni64(min(s_end, vis));
+  const int nst = vis_end > s_begin ? static_cast<int>((vis_end - s_begin + KPS - 1) / KPS) : 0;
+
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.data) + uni64(b * a.kI_rows) * RB;
+  const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wid][0]));
+  // stage u: entries s_begin + KPS u ..; load i covers stage bytes [1024 i, +1024)
+  auto issue = [&](int u) {
+    const int st = u % NST;
+#pragma unroll
+    for (int i = 0; i < DPS; ++i) {
+      const int off = i * 1024 + 16 * lane;
+      const int kk = off / RB;                // entry within the stage
+      const int lc = ((off % RB) / 16) ^ (kk & (CPR - 1));  // logical chunk stored at this slot
+      int64_t s = s_begin + static_cast<int64_t>(u) * KPS + kk;
+      if (s >= vis_end) s = vis_end - 1;      // in bounds; masked when stored
+      lds_dma16(kbase + s * RB + lc * 16, ring_b + st * STAGE_B + i * 1024);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u)
+    if (u < nst) issue(u);
+
+  // queries and head weights, behind the first stages (loads return in issue order)
+  bf16x8 qa[HB][KS];
+  float w[HB][4];
+  if (nst > 0) {
+    const uint16_t* q = static_cast<const uint16_t*>(a.qI.data) + bt * a.HI * DI;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[hb][ks] = *reinterpret_cast<const bf16x8*>(q + (hb * 16 + col) * DI + ks * 32 + grp * 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[hb][r] = a.wI[bt * a.HI + hb * 16 + grp * 4 + r];
+    }
+  }
+
+  float* out = a.scores + bt * a.N;
+  float res = -INFINITY;
+  for (int t = 0; t < nst; ++t) {
+    wait_stage<DPS, NST - 2>(min(nst - 1 - t, NST - 2));
+    if (t + NST - 1 < nst) issue(t + NST - 1);  // into the stage read in iteration t-1
+    const uint8_t* T = &ring[wid][(t % NST) * STAGE_B];
+#pragma unroll
+    for (int tI = 0; tI < TPS; ++tI) {
+      const int kk = tI * 16 + col;
+      bf16x8 kb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[ks] = *reinterpret_cast<const bf16x8*>(T + kk * RB + (((4 * ks + grp) ^ (kk & (CPR - 1))) * 16));
+      float sc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hb][ks], kb[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
+      }
+      sc += __shfl_xor(sc, 16, WAVE);
+      sc += __shfl_xor(sc, 32, WAVE);
+      // tiles are stored in runs of four: lane (col, grp) holds entry 16 grp + col of the run
+      const int tile = t * TPS + tI;
+      const int g = tile & 3;
+      if (grp == g) res = sc;
+      if (g == 3 || (t == nst - 1 && tI == TPS - 1)) {
+        const int64_t s = s_begin + static_cast<int64_t>(tile - g) * 16 + lane;
+        if (s < s_end) out[s] = s < vis_end ? res : -INFINITY;
+        res = -INFINITY;
+      }
+    }
+  }
+  // entries past the visible prefix that no run covered
+  const int64_t covered = s_begin + static_cast<int64_t>((nst * TPS + 3) / 4) * 64;
+  for (int64_t s = covered + lane; s < s_end; s += WAVE) out[s] = -INFINITY;
+}
 
 // ------------------------------------------------------------------ prefill (LDS-shared keys)
 
@@ -543,6 +667,29 @@ MfmaKern pick_ks(int KS) {
   return nullptr;
 }
 
+constexpr int kStreamTPS = 1;  // 16-entry tiles per ring stage
+constexpr int kStreamNST = 4;  // ring stages per wave
+
+template <int HB>
+MfmaKern pick_stream_ks(int KS) {
+  switch (KS) {
+    case 1: return index_stream_kernel<HB, 1, kStreamTPS, kStreamNST>;
+    case 2: return index_stream_kernel<HB, 2, kStreamTPS, kStreamNST>;
+    case 4: return index_stream_kernel<HB, 4, kStreamTPS, kStreamNST>;
+  }
+  return nullptr;  // longer rows: the direct-load kernel
+}
+
+MfmaKern pick_stream(int HB, int KS) {
+  switch (HB) {
+    case 1: return pick_stream_ks<1>(KS);
+    case 2: return pick_stream_ks<2>(KS);
+    case 4: return pick_stream_ks<4>(KS);
+    case 8: return pick_stream_ks<8>(KS);
+  }
+  return nullptr;
+}
+
 MfmaKern pick_mfma(int HB, int KS) {
   switch (HB) {
     case 1: return pick_ks<1>(KS);
@@ -588,12 +735,13 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
     }
   }
   if (L.qI.dtype == CSA_BF16 && L.HI % 16 == 0 && L.DI % 32 == 0) {
-    MfmaKern k = pick_mfma(L.HI / 16, L.DI / 32);
+    MfmaKern k = pick_stream(L.HI / 16, L.DI / 32);
+    if (!k) k = pick_mfma(L.HI / 16, L.DI / 32);
     if (k) {
       // entries per wave: small ranges when there are few tokens (decode) so that the
       // whole chip streams the keys; longer ranges amortise the query load otherwise
       const int64_t tokens = L.B * L.Tq;
-      int kpw = 256;
+      int kpw = 128;
       while (kpw < 4096 && tokens * ((L.N + kpw - 1) / kpw) > 8192) kpw *= 2;
       const int64_t wpt = (L.N + kpw - 1) / kpw;
       const int64_t waves = tokens * wpt;

@@ -5,7 +5,8 @@
 // towards the lower index, in ascending index order, padded with -1 (and the count).
 //
 // Every score becomes an order-preserving uint32 key once (non-finite -> 0, never
-// chosen; -0 and +0 share a key).  A row is cut into slices of at most 16384 keys and
+// chosen; -0 and +0 share a key).  A few rows of at most 32768 keys take one
+// workgroup each; otherwise a row is cut into slices of at most 16384 keys and
 // selection runs in (at most a few) levels:
 //   level 1: one workgroup per (row, slice) keeps its slice's top-k as (key, index)
 //            pairs in index order;
@@ -107,6 +108,53 @@ __device__ __forceinline__ void find_bin(const uint32_t* hc, uint32_t remaining,
     info[1] = abv;
     info[2] = cnt;
   }
+}
+
+// The same step by the whole workgroup: thread t owns bins [BPT t, BPT t + BPT); the
+// entries in higher bins come from a wave prefix sum and the per-wave totals.  Ends
+// with a barrier after which info holds the result.
+template <int NT>
+__device__ __forceinline__ void find_bin_block(const uint32_t* hc, uint32_t remaining, Shared<NT>& sh) {
+  constexpr int BPT = kBins / NT;
+  constexpr int NW = NT / WAVE;
+  static_assert(BPT >= 2 && BPT * NT == kBins, "bins per thread");
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  uint32_t c[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; j += 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(&hc[BPT * tid + j]);
+    c[j] = v.x;
+    c[j + 1] = v.y;
+  }
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) local += c[j];
+  const uint32_t incl = wave_prefix_sum(local);
+  const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
+  if (lane == 63) sh.wave_a[wid] = wtot;
+  __syncthreads();
+  uint32_t above = wtot - incl;  // later lanes of this wave
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w > wid) above += sh.wave_a[w];
+  if (above < remaining && remaining <= above + local) {  // exactly one thread
+    uint32_t bin = 0, abv = 0, cnt = 0;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (above < remaining && remaining <= above + c[j]) {
+        bin = static_cast<uint32_t>(BPT * tid + j);
+        abv = above;
+        cnt = c[j];
+      }
+      above += c[j];
+    }
+    sh.info[0] = bin;
+    sh.info[1] = abv;
+    sh.info[2] = cnt;
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -239,20 +287,26 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
         return b < static_cast<uint32_t>(kBins) ? b : static_cast<uint32_t>(kBins - 1);
       };
       uint32_t* h1 = sh.hist[1];
+      // each key's bin is kept (two 16-bit bins per register; 0xffff: not finite) for
+      // the gather below
+      uint32_t binp[PER / 2];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (key[j] != 0u) atomicAdd(&h1[vbin(key[j])], 1u);
-        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < PER; j += 2) {
+        const uint32_t b0 = key[j] != 0u ? vbin(key[j]) : 0xffffu;
+        const uint32_t b1 = key[j + 1] != 0u ? vbin(key[j + 1]) : 0xffffu;
+        if (key[j] != 0u) atomicAdd(&h1[b0], 1u);
+        if (key[j + 1] != 0u) atomicAdd(&h1[b1], 1u);
+        binp[j / 2] = b0 | (b1 << 16);
+        if ((j & 3) == 2) __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
-      if (wid == 0) find_bin(h1, K, sh.info);
-      __syncthreads();
+      find_bin_block<NT>(h1, K, sh);
       const uint32_t tb = sh.info[0], rem = K - sh.info[1], cnt = sh.info[2];
       if (cnt <= kFewCand) {
         // gather the threshold bin's keys (any order) and rank them in wave 0
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-          if (key[j] != 0u && vbin(key[j]) == tb) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
+          if (((binp[j / 2] >> (16 * (j & 1))) & 0xffffu) == tb) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
         __syncthreads();
         if (wid == 0) {
           const uint32_t c = lane < static_cast<int>(cnt) ? sh.cand[lane] : 0u;
@@ -407,13 +461,15 @@ struct Shape {
   int64_t cap() const { return static_cast<int64_t>(nt) * per; }
 };
 // 16384-entry slices take 512 threads of 32 entries: two workgroups share a CU, so the
-// barrier-separated phases of one overlap the other's
-constexpr Shape kShapes[] = {{256, 16}, {512, 16}, {512, 32}};
+// barrier-separated phases of one overlap the other's.  The 32768-entry shape serves
+// only single-level selections of a few rows.
+constexpr Shape kShapes[] = {{256, 16}, {512, 16}, {512, 32}, {1024, 32}};
+constexpr int64_t kOneLevelMax = 32768;  // a row this long may take one workgroup
 
 Shape shape_for(int64_t n) {
   for (const Shape& s : kShapes)
     if (s.cap() >= n) return s;
-  return kShapes[2];
+  return kShapes[3];
 }
 
 template <int NT, int PER, bool PAIRS, bool FINAL>
@@ -425,7 +481,8 @@ template <bool PAIRS, bool FINAL>
 void launch_shape(const Shape& s, int64_t blocks, const TopkArgs& a, hipStream_t stream) {
   if (s.nt == 256) launch_nt<256, 16, PAIRS, FINAL>(blocks, a, stream);
   else if (s.per == 16) launch_nt<512, 16, PAIRS, FINAL>(blocks, a, stream);
-  else launch_nt<512, 32, PAIRS, FINAL>(blocks, a, stream);
+  else if (s.nt == 512) launch_nt<512, 32, PAIRS, FINAL>(blocks, a, stream);
+  else launch_nt<1024, 32, PAIRS, FINAL>(blocks, a, stream);
 }
 
 // Selection levels: input entries per row, slice length and slices per row of each.
@@ -437,6 +494,15 @@ struct Levels {
 
 Levels plan_levels(int64_t rows, int64_t N, int k) {
   Levels L{};
+  // a few rows of at most 32768 entries: one workgroup per row and one level, which
+  // ends sooner than two levels of many workgroups each
+  if (N <= kOneLevelMax && rows <= 64) {
+    L.n = 1;
+    L.len[0] = N;
+    L.slice[0] = N;
+    L.slices[0] = 1;
+    return L;
+  }
   // level-1 slices: halved from 32768 (not below 4096 or 2k) while the launch has fewer
   // workgroups than compute units and one further level still covers the candidates
   int64_t sl = kMaxSlice;

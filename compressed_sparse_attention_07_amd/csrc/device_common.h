@@ -208,6 +208,15 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
                : "memory");
 }
 
+// The same for one dword per lane: the wave's 64 dwords land contiguously at lds_byte.
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(lds_byte)
+               : "memory");
+}
+
 // Workgroups go to the 8 XCDs round-robin (block b runs on XCD b % 8), and each XCD
 // has its own L2.  This renumbering hands every XCD one contiguous range of logical
 // blocks, so blocks that read the same data (splits of one query token, neighbouring

@@ -233,7 +233,10 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
 // XOR-swizzled by the entry index through the per-lane addresses), and the operand is
 // read back from LDS with conflict-free 16-byte reads.  A wave only ever reads the
 // stages it filled itself, so the loop has no barrier: the wave's own vmcnt orders
-// its loads.
+// its loads.  The four waves of a workgroup serve one token (the host rounds the
+// waves per token up to a multiple of four), so its queries (swizzled like the keys)
+// and head weights come into LDS once per workgroup, also by direct loads, ahead of
+// the first key stages.
 template <int STEP, int MAXL>
 __device__ __forceinline__ void wait_stage(int later) {
   if constexpr (MAXL == 0) {
@@ -254,24 +257,53 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
   constexpr int STAGE_B = KPS * RB;
   constexpr int DPS = STAGE_B / 1024;    // direct loads per stage
   static_assert(DPS >= 1 && DPS * 1024 == STAGE_B, "a stage is whole KiBs");
-  static_assert(NST >= 2 && DPS * (NST - 2) < 64, "vmcnt range");
+  static_assert(NST >= 2 && DPS * (NST - 1) < 64, "vmcnt range");
+  constexpr int QOPS = HB * KS;          // KiBs of queries: HI x DI bf16
+  constexpr int WOPS = (16 * HB + 63) / 64;  // head weights: 64 floats per dword load
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWavesPerWG][NST * STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t qsh[QOPS * 1024];
+  __shared__ __attribute__((aligned(16))) float wsh[WOPS * 64];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + wid;
-  if (wave >= a.B * a.Tq * waves_per_token) return;  // whole waves only
-  const int64_t bt = wave / waves_per_token;
-  const int64_t b = bt / a.Tq;
-  const int64_t s_begin = (wave % waves_per_token) * keys_per_wave;
+  // fewer than 2^32 waves and tokens (the grid is 32-bit): 32-bit index arithmetic
+  const uint32_t wpt = static_cast<uint32_t>(waves_per_token);
+  const uint32_t wave = blockIdx.x * kWavesPerWG + static_cast<uint32_t>(wid);
+  const uint32_t bt32 = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG / wpt);  // the workgroup's token
+  const int64_t bt = bt32;
+  const int64_t b = bt32 / static_cast<uint32_t>(a.Tq);
+  const int64_t s_begin = static_cast<int64_t>(wave - bt32 * wpt) * keys_per_wave;
   const int64_t s_end = min(s_begin + keys_per_wave, a.N);
-  int64_t vis = a.q_pos[bt] / a.ratio;
+  const int64_t pos = a.q_pos[bt];  // a scalar load, waited for only where vis is needed
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // the token's queries and head weights, split over the waves (load i by wave i % 4)
+  {
+    const uint8_t* q = static_cast<const uint8_t*>(a.qI.data) + uni64(bt * a.HI) * RB;
+    const uint32_t q_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(qsh));
+#pragma unroll
+    for (int j = 0; j < (QOPS + kWavesPerWG - 1) / kWavesPerWG; ++j) {
+      const int i = wid + kWavesPerWG * j;
+      if (i >= QOPS) break;
+      const int off = i * 1024 + 16 * lane;
+      const int row = off / RB;
+      const int lc = ((off % RB) / 16) ^ (row & (CPR - 1));
+      lds_dma16(q + row * RB + lc * 16, q_b + i * 1024);
+    }
+    const float* wr = a.wI + uni64(bt * a.HI);
+    const uint32_t w_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wsh));
+#pragma unroll
+    for (int i = 0; i < WOPS; ++i)
+      if ((QOPS + i) % kWavesPerWG == wid) {  // wave-uniform
+        const int e = 64 * i + lane;
+        lds_dma4(wr + (e < 16 * HB ? e : 0), w_b + i * 256);  // lanes past HI re-read weight 0
+      }
+  }
+  int64_t vis = (pos >= 0 && pos <= 0xffffffffll) ? static_cast<int64_t>(static_cast<uint32_t>(pos) / static_cast<uint32_t>(a.ratio))
+                                                 : pos / a.ratio;
   vis = vis > a.N ? a.N : (vis < 0 ? 0 : vis);
   const int64_t vis_end = uni64(min(s_end, vis));
   const int nst = vis_end > s_begin ? static_cast<int>((vis_end - s_begin + KPS - 1) / KPS) : 0;
-
-  const int col = lane & 15;
-  const int grp = lane >> 4;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.data) + uni64(b * a.kI_rows) * RB;
   const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wid][0]));
   // stage u: entries s_begin + KPS u ..; load i covers stage bytes [1024 i, +1024)
@@ -290,20 +322,23 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
 #pragma unroll
   for (int u = 0; u < NST - 1; ++u)
     if (u < nst) issue(u);
+  // the query loads were issued before every key stage: wait for them alone
+  wait_stage<DPS, NST - 1>(min(nst, NST - 1));
+  __syncthreads();
 
-  // queries and head weights, behind the first stages (loads return in issue order)
   bf16x8 qa[HB][KS];
   float w[HB][4];
-  if (nst > 0) {
-    const uint16_t* q = static_cast<const uint16_t*>(a.qI.data) + bt * a.HI * DI;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
+    const int row = hb * 16 + col;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qa[hb][ks] = *reinterpret_cast<const bf16x8*>(q + (hb * 16 + col) * DI + ks * 32 + grp * 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[hb][r] = a.wI[bt * a.HI + hb * 16 + grp * 4 + r];
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qa[hb][ks] = *reinterpret_cast<const bf16x8*>(qsh + row * RB + (((4 * ks + grp) ^ (row & (CPR - 1))) * 16));
+    const float4 wv = *reinterpret_cast<const float4*>(&wsh[hb * 16 + grp * 4]);
+    w[hb][0] = wv.x;
+    w[hb][1] = wv.y;
+    w[hb][2] = wv.z;
+    w[hb][3] = wv.w;
   }
 
   float* out = a.scores + bt * a.N;
@@ -668,7 +703,7 @@ MfmaKern pick_ks(int KS) {
 }
 
 constexpr int kStreamTPS = 1;  // 16-entry tiles per ring stage
-constexpr int kStreamNST = 4;  // ring stages per wave
+constexpr int kStreamNST = 3;  // ring stages per wave (two workgroups of 64 KiB share a CU)
 
 template <int HB>
 MfmaKern pick_stream_ks(int KS) {
@@ -736,6 +771,7 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
   }
   if (L.qI.dtype == CSA_BF16 && L.HI % 16 == 0 && L.DI % 32 == 0) {
     MfmaKern k = pick_stream(L.HI / 16, L.DI / 32);
+    const bool streamed = k != nullptr;
     if (!k) k = pick_mfma(L.HI / 16, L.DI / 32);
     if (k) {
       // entries per wave: small ranges when there are few tokens (decode) so that the
@@ -743,7 +779,15 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
       const int64_t tokens = L.B * L.Tq;
       int kpw = 128;
       while (kpw < 4096 && tokens * ((L.N + kpw - 1) / kpw) > 8192) kpw *= 2;
-      const int64_t wpt = (L.N + kpw - 1) / kpw;
+      int64_t wpt = (L.N + kpw - 1) / kpw;
+      if (streamed) {
+        wpt = (wpt + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;  // one token per workgroup
+        if (tokens * wpt >= (int64_t{1} << 32)) {  // its index arithmetic is 32-bit
+          k = pick_mfma(L.HI / 16, L.DI / 32);
+          wpt = (L.N + kpw - 1) / kpw;
+          if (!k) return -1;
+        }
+      }
       const int64_t waves = tokens * wpt;
       const int64_t grid = (waves + kWavesPerWG - 1) / kWavesPerWG;
       hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(grid)), dim3(kWavesPerWG * WAVE), 0, stream, L, kpw, wpt);

@@ -1060,17 +1060,27 @@ int base_hpw(int H, int D) {
   return head_group(H, D >= 512 ? mfma_max_waves<512>() : mfma_max_waves<128>());
 }
 
+// Key-slot splits.  They depend on the per-sequence shape only (query tokens, heads,
+// slots) and never on B, and the combine reads the splits in order, so a sequence's
+// output is bitwise the same whatever else shares its batch (the pages ask decode to
+// be batch-invariant and deterministic).  Decode-shaped launches (fewer than 256
+// (token, head group) units per sequence) cut every query's slots into splits of at
+// least kMinSplit slots, at most kMaxSplits of them; prefill-shaped ones do not split.
+constexpr int64_t kMinSplitDma = 96;    // three 32-key tiles
+constexpr int64_t kMinSplitMfma = 128;
+constexpr int64_t kMaxSplitsSparse = 12;
+constexpr int64_t kMaxSplitsDense = 8;  // long dense key lists: fewer, longer splits
+
 Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma, bool sparse, bool dma) {
   Plan p{mfma, 0, 1, 0};
   if (!mfma) return p;
-  const int64_t tokens = B * Tq;
   int hpw = dma ? head_group(H, kDmaMaxWaves) : base_hpw(H, D);
-  if (tokens == 0) {
+  if (B * Tq == 0) {
     p.hpw = hpw;
     p.sps = kKT;
     return p;
   }
-  int64_t units = tokens * (H / hpw);
+  int64_t units = Tq * (H / hpw);  // per sequence
   if (!dma) {
     // smaller head groups give more workgroups without split partials, but below these
     // sizes the prefetch registers no longer fit next to the accumulators
@@ -1080,14 +1090,12 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
       units *= 2;
     }
   }
-  // split the key slots when there are too few (token, head group) units to fill
-  // the chip; every split adds H*D bf16 partials per token
   int64_t ns = 1;
   if (units < 256) {
-    ns = (256 + units - 1) / units;
-    int64_t cap = (max_slots + (dma ? 63 : 127)) / (dma ? 64 : 128);
-    if (cap > 64) cap = 64;  // the combine kernel holds one split per lane
-    if (ns > cap) ns = cap;
+    const int64_t min_split = dma ? kMinSplitDma : kMinSplitMfma;
+    const int64_t mx = sparse ? kMaxSplitsSparse : kMaxSplitsDense;
+    ns = (max_slots + min_split - 1) / min_split;
+    if (ns > mx) ns = mx;
     if (ns < 1) ns = 1;
   }
   // a sparse range's entry indices are staged in LDS by the DMA kernel

@@ -417,3 +417,42 @@ def test_runs_are_bitwise_deterministic():
         outs.append(o)
     torch.cuda.synchronize()
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def _one(x, b):
+    """Sequence b of a batched input, as a batch of one (copies, so nothing is shared)."""
+    if x is None:
+        return None
+    if isinstance(x, csa.Buf):
+        s = lambda t: None if t is None else t[b:b + 1].contiguous()
+        return csa.Buf(x.dtype, s(x.data), s(x.rope), s(x.scale))
+    return x[b:b + 1].contiguous()
+
+
+@pytest.mark.parametrize("kvf,dense", [("bf16", False), ("fp8mix", False), ("bf16", True)])
+def test_decode_is_batch_invariant(kvf, dense):
+    """A sequence's decode output does not depend on what else is in the batch: alone
+    and inside a batch of 16 it is bitwise the same (key-slot splits depend on the
+    sequence's own shape, and the combine reads them in order)."""
+    say(f"batch invariance kv={kvf} dense={dense}")
+    g = Gen(83, DEV)
+    B, H, D, n_win = 16, 128, 512, 128
+    N, K, ratio = (2048, 0, 128) if dense else (600, 256, 4)
+    q, pos, kv, _, idx, win, _, win_pos0, sink = _attn_inputs(g, B, 1, H, D, N, K, n_win, "bf16", kvf, 64,
+                                                                [N * ratio], holes=False)
+
+    def run(q, pos, kv, idx, win, win_pos0):
+        o = torch.empty_like(q)
+        if dense:
+            csa.hca_dense_attn(q, pos, kv, win, win_pos0, sink, o, N=N, ratio=ratio, n_win=n_win, softmax_scale=1.0,
+                               rope_dims=64)
+        else:
+            csa.csa_sparse_mqa(q, pos, kv, idx, win, win_pos0, sink, o, N=N, n_win=n_win, softmax_scale=1.0,
+                               rope_dims=64)
+        return o
+
+    full = run(q, pos, kv, idx, win, win_pos0)
+    for b in (0, 5, 15):
+        one = run(_one(q, b), _one(pos, b), _one(kv, b), _one(idx, b), _one(win, b), _one(win_pos0, b))
+        torch.cuda.synchronize()
+        assert torch.equal(full[b:b + 1].view(torch.int16), one.view(torch.int16)), f"sequence {b}"

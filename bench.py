@@ -132,44 +132,35 @@ def _copy_buf(dst, src):
         dst.scale.copy_(src.scale)
 
 
-def _seq(buf, b):
-    """csa_buf view of sequence b of a [B, rows, D] buffer (as a batch of one)."""
-    import compressed_sparse_attention_07_amd as csa
-    sl = lambda t: None if t is None else t[b:b + 1]
-    return csa.Buf(buf.dtype, sl(buf.data), sl(buf.rope), sl(buf.scale))
+def _compress_bulk(csa, gens, cache, b0, tokens, D, m, overlap, R, base, bf, timer):
+    """Compress tokens [0, tokens) of sequences b0 .. b0 + len(gens) - 1 into cache rows
+    [0, tokens/m) with one launch (the sequences form the batch).
 
-
-def _compress_bulk(csa, g, cache, b, tokens, D, m, overlap, R, base, chunk, bf, timer):
-    """Compress tokens [0, tokens) of sequence b into cache rows [0, tokens/m), in chunks.
-
-    Streams are drawn chunk by chunk from g; the previous block of each chunk is the
-    tail of the one before.  Each chunk's compression runs twice (it is idempotent) and
-    the second run is timed: the first touches the freshly allocated stream buffers.
-    Returns (seconds, bytes) of the timed runs."""
-    secs, nbytes = 0.0, 0
-    prev = None
-    for c0 in range(0, tokens, chunk):
-        T = min(chunk, tokens - c0)
-        n_st = 4 if overlap else 2
-        s = [g.normal((1, T, D), dtype=bf) for _ in range(n_st)]
-        dst = _seq(cache, b)
-        kw = dict(ratio=m, overlap=overlap, t0=c0, rope_dims=R, rope_base=base)
-        if overlap:
-            ca, cb, za, zb = s
-            if c0 > 0:
-                kw.update(prev_cb=prev[0], prev_zb=prev[1])
-        else:
-            ca, za = s
-            cb = zb = None
-        call = csa.PreparedCall(csa.csa_compress, ca, cb, za, zb, dst, **kw)
-        call()  # first touch of the freshly drawn stream buffers (page-table walks); same result
-        t = timer()
-        call()
-        secs += timer(t)
-        nbytes += n_st * T * D * 2 + (T // m) * D * 2
-        if overlap:
-            prev = (cb[:, T - m:].contiguous(), zb[:, T - m:].contiguous())
-        del s
+    Each sequence's streams are drawn from its own generator, in the same order whatever
+    the batching.  The compression runs twice (it is idempotent) and the second run is
+    timed: the first touches the freshly allocated stream buffers.  Returns (seconds,
+    bytes) of the timed run."""
+    import torch
+    nb_seq = len(gens)
+    n_st = 4 if overlap else 2
+    s = [torch.empty((nb_seq, tokens, D), dtype=bf, device="cuda") for _ in range(n_st)]
+    for i, g in enumerate(gens):
+        for j in range(n_st):
+            s[j][i] = g.normal((tokens, D), dtype=bf)
+    dst = csa.Buf(cache.dtype, *(None if t is None else t[b0:b0 + nb_seq] for t in (cache.data, cache.rope, cache.scale)))
+    kw = dict(ratio=m, overlap=overlap, t0=0, rope_dims=R, rope_base=base)
+    if overlap:
+        ca, cb, za, zb = s
+    else:
+        ca, za = s
+        cb = zb = None
+    call = csa.PreparedCall(csa.csa_compress, ca, cb, za, zb, dst, **kw)
+    call()  # first touch of the freshly drawn stream buffers (page-table walks); same result
+    t = timer()
+    call()
+    secs = timer(t)
+    nbytes = nb_seq * (n_st * tokens * D * 2 + (tokens // m) * D * 2)
+    del s
     return secs, nbytes
 
 
@@ -221,6 +212,22 @@ def build_workload(key: str, layers: int, dev: str = "cuda") -> Workload:
     t0 = ctx - T_step
     build_secs, build_bytes = 0.0, 0
     log(f"[{key}] building caches: B={B} ctx={ctx} N={N} layers={L}")
+    # stream memory of one sequence's cache build; sequences are compressed together in
+    # launches of at most 16 GiB of streams
+    tokens = t0 if T_step else ctx
+    seq_bytes = (4 if not hca else 2) * tokens * (D + (0 if hca else DI)) * 2
+    per_launch = max(1, min(B, (16 << 30) // max(1, seq_bytes)))
+    if key != "4":
+        for b0 in range(0, B, per_launch):
+            bs = range(b0, min(B, b0 + per_launch))
+            gens = [Gen(cfg.seed * 1000 + b, dev) for b in bs]
+            sec, nb = _compress_bulk(csa, gens, kv0, b0, tokens, D, m, not hca, R, base, bf, timer)
+            build_secs += sec
+            build_bytes += nb
+            if not hca:
+                sec, nb = _compress_bulk(csa, gens, ik0, b0, tokens, DI, m, True, 0, base, bf, timer)
+                build_secs += sec
+                build_bytes += nb
     for b in range(B):
         g = Gen(cfg.seed * 1000 + b, dev)
         if key == "4":
@@ -232,16 +239,6 @@ def build_workload(key: str, layers: int, dev: str = "cuda") -> Workload:
                                  rope_dims=R)
                 xi = g.normal((r1 - r0, DI))
                 csa.csa_quantize(xi, csa.Buf(ik0.dtype, ik0.data[b, r0:r1], None, ik0.scale[b, r0:r1]))
-            continue
-        tokens = t0 if T_step else ctx
-        chunk = 1 << 17
-        sec, nb = _compress_bulk(csa, g, kv0, b, tokens, D, m, not hca, R, base, chunk, bf, timer)
-        build_secs += sec
-        build_bytes += nb
-        if not hca:
-            sec, nb = _compress_bulk(csa, g, ik0, b, tokens, DI, m, True, 0, base, chunk, bf, timer)
-            build_secs += sec
-            build_bytes += nb
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ step inputs

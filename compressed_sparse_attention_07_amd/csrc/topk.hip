@@ -4,11 +4,11 @@
 // Result per row: the indices of the min(k, #finite) largest scores, ties broken
 // towards the lower index, in ascending index order, padded with -1 (and the count).
 //
-// Every score becomes an order-preserving uint32 key once (non-finite -> 0, never
-// chosen; -0 and +0 share a key).  A few rows of at most 32768 keys take one
-// workgroup each; otherwise a row is cut into slices of at most 16384 keys and
-// selection runs in (at most a few) levels:
-//   level 1: one workgroup per (row, slice) keeps its slice's top-k as (key, index)
+// Scores are kept as floats (NaN and +-inf become -inf, which is never chosen; -0 and
+// +0 compare equal).  A few rows of at most 32768 scores take one workgroup each;
+// otherwise a row is cut into slices of at most 16384 scores and selection runs in
+// (at most a few) levels:
+//   level 1: one workgroup per (row, slice) keeps its slice's top-k as (value, index)
 //            pairs in index order;
 //   level n: the same selection over the concatenated candidate lists of a row
 //            (which stay in index order); the last level writes the indices.
@@ -16,17 +16,18 @@
 // the slice beat it; a tie it wins by index it also wins inside the slice), so the
 // levels are exact.  Short rows with many rows per launch take one level.
 //
-// Inside a workgroup every key stays in registers (PER consecutive keys per thread):
-//   A. count of finite keys and their smallest / largest key (wave reductions);
-//   B. an MSB-first radix select over v = key - min with 11-bit digits: each level is
-//      an LDS histogram of the keys that match the digits chosen so far, then a
-//      suffix scan picks the digit holding the remaining-th largest.  Starting from
-//      the slice's own key range, at most three levels give the exact threshold key
-//      theta (the k-th largest) and the number of theta-valued entries to keep; a
-//      level whose threshold bin holds exactly the entries still needed ends early
-//      (the whole bin is kept);
-//   C. an order-preserving compaction: every key > theta and the first `ties` keys
-//      == theta, in index order, placed by per-thread counts and a wave + LDS scan.
+// Inside a workgroup every value stays in registers, thread t holding entries
+// t, t + NT, t + 2 NT, ... (so each round of a wave covers 64 consecutive entries):
+//   A. count of finite values (ballots) and their smallest / largest value;
+//   B. the threshold value theta (the k-th largest) and the number of theta-valued
+//      entries to keep: a histogram of the values on a linear scale between the
+//      extremes (monotone bins); when the threshold bin holds at most 64 entries one
+//      wave ranks them exactly.  Otherwise an MSB-first radix select with 11-bit
+//      digits over order-preserving integer keys (at most three levels);
+//   C. an order-preserving compaction: every value > theta and the first `ties`
+//      values == theta, in index order.  Per (round, wave) counts from ballots go
+//      through one workgroup prefix scan; inside a round a lane's slot is the
+//      round's base plus the ballot bits below it.
 #include <algorithm>
 
 #include "device_common.h"
@@ -42,13 +43,13 @@ constexpr int kMaxSlice = 16384;  // keys per workgroup
 
 struct TopkArgs {
   const float* scores;      // level 1 input: [rows, n_in]
-  const uint32_t* in_key;   // later levels: [rows, n_in] candidate keys (0 = none)
+  const float* in_val;      // later levels: [rows, n_in] candidate values (-inf = none)
   const int32_t* in_idx;    //               and their row indices
   int64_t n_in;             // input entries per row
   int64_t slice;            // entries per slice (workgroup)
   int slices;               // slices per row
   int k;
-  uint32_t* out_key;        // candidate output: [rows, slices, k]
+  float* out_val;           // candidate output: [rows, slices, k]
   int32_t* out_idx;         // candidate output [rows, slices, k], or the final [rows, k]
   int32_t* count;           // final level: [rows] or NULL
 };
@@ -57,7 +58,9 @@ constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one w
 
 template <int NT>
 struct Shared {
-  alignas(16) uint32_t hist[2][kBins];  // radix levels alternate between the two
+  // radix levels alternate between the two; one spare slot past each counts
+  // non-finite values in the linear-scale histogram (never read)
+  alignas(16) uint32_t hist[2][kBins + 4];
   alignas(16) uint4 wave_abc[NT / WAVE];
   uint32_t wave_a[NT / WAVE];
   uint32_t info[3];
@@ -166,293 +169,296 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* p, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), 0x00020000);
 }
 
-// Load slice blk's keys: PER consecutive entries per thread (scores become keys; a
-// candidate's index is read again only when it is written out).
+// Load slice blk's values: thread t holds entries t + NT j of the slice.
 template <int NT, int PER, bool PAIRS>
-__device__ __forceinline__ void load_slice(const TopkArgs& a, int64_t blk, uint32_t (&key)[PER]) {
+__device__ __forceinline__ void load_slice(const TopkArgs& a, int64_t blk, float (&v)[PER]) {
   const int tid = static_cast<int>(threadIdx.x);
   const int64_t r = static_cast<uint32_t>(blk) / static_cast<uint32_t>(a.slices);
   const int sl = static_cast<int>(static_cast<uint32_t>(blk) % static_cast<uint32_t>(a.slices));
   const int64_t lo = static_cast<int64_t>(sl) * a.slice;
-  const int64_t hi = min(a.n_in, lo + a.slice);
-  const int64_t base = lo + static_cast<int64_t>(tid) * PER;  // first entry of this thread
-  if (PAIRS) {
-    const uint32_t* kr = a.in_key + r * a.n_in + base;
-    if (base + PER <= hi && aligned16(kr)) {
+  const int n = static_cast<int>(min(a.n_in, lo + a.slice) - lo);  // <= NT * PER
+  const float* src = (PAIRS ? a.in_val : a.scores) + r * a.n_in + lo;
+  if (n == NT * PER) {
 #pragma unroll
-      for (int q = 0; q < PER / 4; ++q) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(kr + 4 * q);
-        key[4 * q] = kv.x; key[4 * q + 1] = kv.y; key[4 * q + 2] = kv.z; key[4 * q + 3] = kv.w;
-      }
-    } else {
-      // view of the workgroup's slice (uniform), lane offsets from the slice start
-      const __amdgpu_buffer_rsrc_t bk = buffer_view(a.in_key + r * a.n_in + lo, (hi - lo) * 4);
-      const int off = 4 * tid * PER;
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        key[j] = __builtin_amdgcn_raw_buffer_load_b32(bk, off + 4 * j, 0, 0);  // 0 past the end: no candidate
-    }
+    for (int j = 0; j < PER; ++j) v[j] = src[j * NT + tid];
   } else {
-    const float* row = a.scores + r * a.n_in + base;
-    if (base + PER <= hi && aligned16(row)) {
+    // loads past the slice return 0 (hardware range check) and are replaced by -inf
+    const __amdgpu_buffer_rsrc_t bs = buffer_view(src, static_cast<int64_t>(n) * 4);
 #pragma unroll
-      for (int q = 0; q < PER / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(row + 4 * q);
-        key[4 * q] = score_key(v.x);
-        key[4 * q + 1] = score_key(v.y);
-        key[4 * q + 2] = score_key(v.z);
-        key[4 * q + 3] = score_key(v.w);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t bs = buffer_view(a.scores + r * a.n_in + lo, (hi - lo) * 4);
-      const int off = 4 * tid * PER;
-      uint32_t x[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) x[j] = __builtin_amdgcn_raw_buffer_load_b32(bs, off + 4 * j, 0, 0);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const uint32_t kk = score_key(__builtin_bit_cast(float, x[j]));
-        key[j] = base + j < hi ? kk : 0u;
-      }
+    for (int j = 0; j < PER; ++j) {
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs, 4 * (j * NT + tid), 0, 0));
+      v[j] = j * NT + tid < n ? x : -INFINITY;
     }
   }
-
+  if (!PAIRS) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = __builtin_isfinite(v[j]) ? v[j] : -INFINITY;
+  }
 }
 
-// Select slice blk's top-k from its keys (every thread of the workgroup calls this;
+__device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {  // set bits of m below this lane
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Select slice blk's top-k from its values (every thread of the workgroup calls this;
 // it holds barriers).
 template <int NT, int PER, bool PAIRS, bool FINAL>
-__device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, int64_t blk, uint32_t (&key)[PER]) {
+__device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, int64_t blk, float (&v)[PER]) {
   constexpr int NW = NT / WAVE;
+  static_assert(PER % 2 == 0 && PER <= 64, "rounds per thread");
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t r = static_cast<uint32_t>(blk) / static_cast<uint32_t>(a.slices);
   const int sl = static_cast<int>(static_cast<uint32_t>(blk) % static_cast<uint32_t>(a.slices));
   const int64_t lo = static_cast<int64_t>(sl) * a.slice;
-  const int64_t hi = min(a.n_in, lo + a.slice);
-  const int64_t base = lo + static_cast<int64_t>(tid) * PER;  // first entry of this thread
+  const int n = static_cast<int>(min(a.n_in, lo + a.slice) - lo);
   const uint32_t K = static_cast<uint32_t>(a.k);
-  const int32_t* ir = PAIRS ? a.in_idx + r * a.n_in + base : nullptr;
 
-  // ---- A: finite count, smallest and largest finite key
-  uint32_t nfin = 0, kmax = 0, kmin1 = 0xffffffffu;  // kmin1 = min(key - 1): key 0 wraps to the top
+  // ---- A: finite count, smallest and largest finite value
+  uint32_t nfin = 0;
+  float vmax = -INFINITY, vmin = INFINITY;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    nfin += key[j] != 0u ? 1u : 0u;
-    kmax = max(kmax, key[j]);
-    kmin1 = min(kmin1, key[j] - 1u);
+    const bool fin = v[j] > -INFINITY;
+    nfin += fin ? 1u : 0u;
+    vmax = fmaxf(vmax, v[j]);
+    vmin = fminf(vmin, fin ? v[j] : INFINITY);
   }
   nfin = wave_sum_u32(nfin);
-  kmax = wave_max_u32(kmax);
-  kmin1 = wave_min_u32(kmin1);
-  if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, kmax, kmin1, 0u);
-  for (int i = tid; i < 2 * kBins; i += NT) (&sh.hist[0][0])[i] = 0u;
+  vmax = wave_max(vmax);
+  vmin = -wave_max(-vmin);
+  if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, __float_as_uint(vmax), __float_as_uint(vmin), 0u);
+  for (int i = tid; i < 2 * (kBins + 4); i += NT) (&sh.hist[0][0])[i] = 0u;
   if (tid == 0) sh.ncand = 0u;
   __syncthreads();
   nfin = 0;
-  kmax = 0;
-  kmin1 = 0xffffffffu;
+  vmax = -INFINITY;
+  vmin = INFINITY;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const uint4 v = sh.wave_abc[w];
-    nfin += v.x;
-    kmax = max(kmax, v.y);
-    kmin1 = min(kmin1, v.z);
+    const uint4 x = sh.wave_abc[w];
+    nfin += x.x;
+    vmax = fmaxf(vmax, __uint_as_float(x.y));
+    vmin = fminf(vmin, __uint_as_float(x.z));
   }
-  const uint32_t kmin = kmin1 + 1u;
 
-  // ---- B: threshold key theta and the number of theta-valued entries kept
-  uint32_t theta, ties;
-  uint32_t koff = 0;  // keys below are stored as key - koff (finite keys stay >= 1)
+  // ---- B: threshold value theta and the number of theta-valued entries kept
+  float theta;
+  uint32_t ties, total_eq = 0;  // total_eq: entries == theta (needed when 0 < ties)
   const uint32_t total_sel = nfin < K ? nfin : K;
   if (nfin <= K) {
-    theta = 0u;  // key > 0 <=> finite score: keep them all
+    theta = -INFINITY;  // keep every finite value
     ties = 0u;
-  } else if (kmin == kmax) {
-    theta = kmax;  // every finite key is equal: the first k by index
+  } else if (vmin == vmax) {
+    theta = vmax;  // every finite value is equal: the first k by index
     ties = K;
+    total_eq = nfin;
   } else {
-    // Stage 0: a histogram of the values on a linear scale between the slice's extremes
-    // (bin = floor((v - vmin) * kBins / (vmax - vmin)), monotone in v, so each bin is a
-    // contiguous key range).  Scores spread over many bins, so the atomics rarely meet,
-    // and the threshold bin usually holds a few entries: one wave then ranks them
-    // exactly.  Otherwise (or if the scale is not finite) the radix levels below run.
     bool found = false;
-    const float vlo = key_value(kmin);
-    const float scale = static_cast<float>(kBins) / (key_value(kmax) - vlo);
+    const float scale = static_cast<float>(kBins) / (vmax - vmin);
     if (scale > 0.f && scale < INFINITY) {
-      auto vbin = [&](uint32_t kk) {
-        const uint32_t b = static_cast<uint32_t>((key_value(kk) - vlo) * scale);
-        return b < static_cast<uint32_t>(kBins) ? b : static_cast<uint32_t>(kBins - 1);
+      // bin = floor((v - vmin) * kBins / (vmax - vmin)), monotone in v, so each bin is
+      // a contiguous value range; non-finite values go to the spare slot.  Scores
+      // spread over many bins, so the atomics rarely meet and the threshold bin
+      // usually holds a few entries, which one wave then ranks exactly.  Each value's
+      // bin is kept (two 16-bit bins per register) for the gather.
+      auto vbin = [&](float x) {
+        const uint32_t b = static_cast<uint32_t>((x - vmin) * scale);
+        return x > -INFINITY ? (b < static_cast<uint32_t>(kBins) ? b : static_cast<uint32_t>(kBins - 1))
+                             : static_cast<uint32_t>(kBins);
       };
       uint32_t* h1 = sh.hist[1];
-      // each key's bin is kept (two 16-bit bins per register; 0xffff: not finite) for
-      // the gather below
       uint32_t binp[PER / 2];
 #pragma unroll
       for (int j = 0; j < PER; j += 2) {
-        const uint32_t b0 = key[j] != 0u ? vbin(key[j]) : 0xffffu;
-        const uint32_t b1 = key[j + 1] != 0u ? vbin(key[j + 1]) : 0xffffu;
-        if (key[j] != 0u) atomicAdd(&h1[b0], 1u);
-        if (key[j + 1] != 0u) atomicAdd(&h1[b1], 1u);
+        const uint32_t b0 = vbin(v[j]), b1 = vbin(v[j + 1]);
+        atomicAdd(&h1[b0], 1u);
+        atomicAdd(&h1[b1], 1u);
         binp[j / 2] = b0 | (b1 << 16);
-        if ((j & 3) == 2) __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
       find_bin_block<NT>(h1, K, sh);
       const uint32_t tb = sh.info[0], rem = K - sh.info[1], cnt = sh.info[2];
       if (cnt <= kFewCand) {
-        // gather the threshold bin's keys (any order) and rank them in wave 0
+        // gather the threshold bin's values (any order) and rank them in wave 0
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-          if (((binp[j / 2] >> (16 * (j & 1))) & 0xffffu) == tb) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
+          if (((binp[j / 2] >> (16 * (j & 1))) & 0xffffu) == tb) sh.cand[atomicAdd(&sh.ncand, 1u)] = __float_as_uint(v[j]);
         __syncthreads();
         if (wid == 0) {
-          const uint32_t c = lane < static_cast<int>(cnt) ? sh.cand[lane] : 0u;
+          const float c = lane < static_cast<int>(cnt) ? __uint_as_float(sh.cand[lane]) : 0.f;
           uint32_t gt = 0, eq = 0;
           for (int i = 0; i < static_cast<int>(cnt); ++i) {
-            const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c), i));
+            const float o = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(c), i));
             gt += o > c ? 1u : 0u;
             eq += o == c ? 1u : 0u;
           }
-          // lanes holding the threshold key all write the same pair
+          // lanes holding the threshold value all write the same triple (every
+          // theta-valued entry of the slice is in this bin)
           if (lane < static_cast<int>(cnt) && gt < rem && rem <= gt + eq) {
-            sh.info[0] = c;
+            sh.info[0] = __float_as_uint(c);
             sh.info[1] = rem - gt;
+            sh.info[2] = eq;
           }
         }
         __syncthreads();
-        theta = sh.info[0];  // raw key domain (koff = 0)
+        theta = __uint_as_float(sh.info[0]);
         ties = sh.info[1];
+        total_eq = sh.info[2];
         found = true;
       }
     }
     if (!found) {
-    // work on w = key - kmin + 1 (finite keys in [1, span + 1], 0 = not finite)
-    koff = kmin - 1u;
+      // radix levels over w = key - kmin + 1 of the order-preserving integer keys
+      // (finite values give 1 .. span + 1, 0 = not finite), held in v's registers as
+      // bit patterns and turned back into values afterwards
+      const uint32_t kmin = score_key(vmin), kmax = score_key(vmax);
+      const uint32_t koff = kmin - 1u;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) key[j] = key[j] != 0u ? key[j] - koff : 0u;
-    const uint32_t span = kmax - kmin;
-    int shift = 32 - __clz(span);  // low bits of v = w - 1 still to decide
-    uint32_t pval = 0, pmask = 0, remaining = K;
-    // one level: histogram of the matching keys' next digit (hist[cur], cleared before),
-    // barrier; wave 0 finds the threshold digit while the other waves clear the other
-    // histogram for the next level; barrier; everyone reads the result
-    for (int cur = 0;; cur ^= 1) {
-      const int nsh = shift > kBinBits ? shift - kBinBits : 0;
-      const uint32_t dmask = (1u << (shift - nsh)) - 1u;
-      // keep the per-key terms inside the level loop (hoisting them would double the
-      // registers the keys occupy)
+      for (int j = 0; j < PER; ++j) v[j] = __uint_as_float(v[j] > -INFINITY ? score_key(v[j]) - koff : 0u);
+      const uint32_t span = kmax - kmin;
+      int shift = 32 - __clz(span);  // low bits of w - 1 still to decide
+      uint32_t pval = 0, pmask = 0, remaining = K;
+      uint32_t theta_w;
+      // one level: histogram of the matching keys' next digit (hist[cur], cleared before),
+      // barrier; wave 0 finds the threshold digit while the other waves clear the other
+      // histogram for the next level; barrier; everyone reads the result
+      for (int cur = 0;; cur ^= 1) {
+        const int nsh = shift > kBinBits ? shift - kBinBits : 0;
+        const uint32_t dmask = (1u << (shift - nsh)) - 1u;
+        uint32_t* hc = sh.hist[cur];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) asm volatile("" : "+v"(key[j]));
-      uint32_t* hc = sh.hist[cur];
+        for (int j = 0; j < PER; ++j) {
+          const uint32_t w = __float_as_uint(v[j]);
+          const uint32_t x = w - 1u;
+          if (w != 0u && (x & pmask) == pval) atomicAdd(&hc[(x >> nsh) & dmask], 1u);
+          if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the addresses computed ahead
+        }
+        __syncthreads();
+        if (wid == 0) {
+          find_bin(hc, remaining, sh.info);
+        } else if (nsh > 0) {
+          uint32_t* hn = sh.hist[cur ^ 1];
+          for (int i = tid - WAVE; i < kBins; i += NT - WAVE) hn[i] = 0u;
+        }
+        __syncthreads();
+        remaining -= sh.info[1];
+        pval |= sh.info[0] << nsh;
+        pmask |= dmask << nsh;
+        if (sh.info[2] == remaining) {
+          // the threshold bin holds exactly the entries still needed: take all of it,
+          // i.e. every key above w = pval (the bin's lowest is pval + 1)
+          theta_w = pval;
+          ties = 0u;
+          break;
+        }
+        if (nsh == 0) {
+          theta_w = pval + 1u;  // the exact threshold key
+          ties = remaining;
+          total_eq = sh.info[2];  // the last level's bin holds exactly that key
+          break;
+        }
+        shift = nsh;
+      }
+      theta = key_value(theta_w + koff);  // w = 0 + koff >= the key below every finite value
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const uint32_t v = key[j] - 1u;
-        if (key[j] != 0u && (v & pmask) == pval) atomicAdd(&hc[(v >> nsh) & dmask], 1u);
-        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the addresses computed ahead
+        const uint32_t w = __float_as_uint(v[j]);
+        v[j] = w != 0u ? key_value(w + koff) : -INFINITY;
       }
-      __syncthreads();
-      if (wid == 0) {
-        find_bin(hc, remaining, sh.info);
-      } else if (nsh > 0) {
-        uint32_t* hn = sh.hist[cur ^ 1];
-        for (int i = tid - WAVE; i < kBins; i += NT - WAVE) hn[i] = 0u;
-      }
-      __syncthreads();
-      remaining -= sh.info[1];
-      pval |= sh.info[0] << nsh;
-      pmask |= dmask << nsh;
-      if (sh.info[2] == remaining) {
-        // the threshold bin holds exactly the entries still needed: take all of it,
-        // i.e. every key >= the bin's lowest value (w = pval + 1)
-        theta = pval;
-        ties = 0u;
-        break;
-      }
-      if (nsh == 0) {
-        theta = pval + 1u;  // in the w domain
-        ties = remaining;
-        break;
-      }
-      shift = nsh;
-    }
     }
   }
 
-  // ---- C: ordered compaction of key > theta and the first `ties` keys == theta
-  uint32_t ngt = 0, ntie = 0;
+  // ---- C: per (round, wave) counts, then one prefix scan in index order (round-major,
+  // then wave); the histograms are free now.  When every theta-valued entry or none is
+  // kept one comparison selects (count in the low half); otherwise the counts of
+  // v > theta and v == theta are packed in the two halves.
+  const bool one_test = ties == 0u || ties == total_eq;
+  const bool with_eq = ties != 0u;
+  uint32_t* tab = sh.hist[0];  // [NW][PER]
+  uint32_t mine = 0;           // lane j < PER: this wave's count(s) of round j
+  if (one_test) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    ngt += key[j] > theta ? 1u : 0u;
-    ntie += (key[j] == theta && key[j] != 0u) ? 1u : 0u;
-  }
-  const uint32_t packed = ngt | (ntie << 16);  // at most 32768 each
-  const uint32_t incl = wave_prefix_sum(packed);
-  __syncthreads();  // every thread is done reading the per-wave values of A
-  if (lane == 63) sh.wave_a[wid] = incl;
-  __syncthreads();
-  uint32_t before = incl - packed;
+    for (int j = 0; j < PER; ++j) {
+      const bool sel = with_eq ? v[j] >= theta : v[j] > theta;
+      const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(sel)));
+      mine = lane == j ? c : mine;
+    }
+  } else {
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
-    if (w < wid) before += sh.wave_a[w];
-  uint32_t gt_before = before & 0xffffu;
-  uint32_t tie_before = before >> 16;
-  // candidate indices, loaded now that the radix registers are free
-  int32_t ix[PAIRS ? PER : 1];
-  if (PAIRS) {
-    if (base + PER <= hi && aligned16(ir)) {
-#pragma unroll
-      for (int q = 0; q < PER / 4; ++q) {
-        const int4 iv = *reinterpret_cast<const int4*>(ir + 4 * q);
-        ix[4 * q] = iv.x; ix[4 * q + 1] = iv.y; ix[4 * q + 2] = iv.z; ix[4 * q + 3] = iv.w;
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t bi = buffer_view(a.in_idx + r * a.n_in + lo, (hi - lo) * 4);
-      const int off = 4 * tid * PER;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) ix[j] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(bi, off + 4 * j, 0, 0));
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(v[j] > theta))) |
+                         (static_cast<uint32_t>(__popcll(__ballot(v[j] == theta))) << 16);
+      mine = lane == j ? c : mine;
     }
   }
+  if (lane < PER) tab[wid * PER + lane] = mine;
+  __syncthreads();
+  constexpr int T = PER * NW;  // <= NT
+  const int jw = tid / NW, ww = tid % NW;  // thread tid scans entry (round jw, wave ww)
+  const uint32_t cx = tid < T ? tab[ww * PER + jw] : 0u;
+  const uint32_t incl = wave_prefix_sum(cx);
+  if (lane == 63) sh.wave_a[wid] = incl;
+  __syncthreads();
+  uint32_t pre = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) pre += w < wid ? sh.wave_a[w] : 0u;
+  if (tid < T) tab[ww * PER + jw] = pre + incl - cx;  // exclusive prefix
+  __syncthreads();
+  const uint32_t base = lane < PER ? tab[wid * PER + lane] : 0u;  // lane j: round j's prefix
+
+  // candidate indices, loaded now that the selection registers are free
+  int32_t ix[PAIRS ? PER : 1];
+  if (PAIRS) {
+    const __amdgpu_buffer_rsrc_t bi = buffer_view(a.in_idx + r * a.n_in + lo, static_cast<int64_t>(n) * 4);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ix[j] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(bi, 4 * (j * NT + tid), 0, 0));
+  }
   int32_t* oi;
-  uint32_t* ok = nullptr;
+  float* ov = nullptr;
   if (FINAL) {
     oi = a.out_idx + r * static_cast<int64_t>(a.k);
   } else {
     const int64_t o = (r * a.slices + sl) * static_cast<int64_t>(a.k);
     oi = a.out_idx + o;
-    ok = a.out_key + o;
+    ov = a.out_val + o;
   }
-  if (ngt + ntie > 0) {
+  auto put = [&](int j, uint32_t slot) {
+    oi[slot] = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(lo + j * NT + tid);
+    if (!FINAL) ov[slot] = v[j];
+  };
+  if (one_test) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const bool gt = key[j] > theta;
-      const bool tie = key[j] == theta && key[j] != 0u;
-      if (gt || (tie && tie_before < ties)) {
-        const uint32_t slot = gt_before + (tie_before < ties ? tie_before : ties);
-        oi[slot] = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(base + j);
-        if (!FINAL) ok[slot] = key[j] + koff;
-      }
-      gt_before += gt ? 1u : 0u;
-      tie_before += tie ? 1u : 0u;
-      if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      const uint32_t bj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), j));
+      const bool sel = with_eq ? v[j] >= theta : v[j] > theta;
+      if (sel) put(j, bj + lane_prefix(__ballot(sel)));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t bj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), j));
+      const bool gt = v[j] > theta, eq = v[j] == theta;
+      const uint32_t gb = (bj & 0xffffu) + lane_prefix(__ballot(gt));
+      const uint32_t tbf = (bj >> 16) + lane_prefix(__ballot(eq));
+      if (gt || (eq && tbf < ties)) put(j, gb + (tbf < ties ? tbf : ties));
     }
   }
   for (int i = static_cast<int>(total_sel) + tid; i < a.k; i += NT) {
     oi[i] = -1;
-    if (!FINAL) ok[i] = 0u;
+    if (!FINAL) ov[i] = -INFINITY;
   }
   if (FINAL && a.count && tid == 0) a.count[r] = static_cast<int32_t>(total_sel);
 }
 
-// PAIRS: input is (key, index) candidates; FINAL: write indices (and count) only.
+// PAIRS: input is (value, index) candidates; FINAL: write indices (and count) only.
 template <int NT, int PER, bool PAIRS, bool FINAL>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   __shared__ Shared<NT> sh;
-  uint32_t key[PER];
-  load_slice<NT, PER, PAIRS>(a, blockIdx.x, key);
-  select_slice<NT, PER, PAIRS, FINAL>(a, sh, blockIdx.x, key);
+  float v[PER];
+  load_slice<NT, PER, PAIRS>(a, blockIdx.x, v);
+  select_slice<NT, PER, PAIRS, FINAL>(a, sh, blockIdx.x, v);
 }
 
 // workgroup shapes: (threads, keys per thread), slice capacity = threads * keys
@@ -548,13 +554,13 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
   const Levels L = N > 0 ? plan_levels(rows, N, k) : Levels{1, {0}, {1}, {1}};
   const size_t one = level_buffer_bytes(rows, L, k);
   char* w = static_cast<char*>(ws);
-  const uint32_t* in_key = nullptr;
+  const float* in_val = nullptr;
   const int32_t* in_idx = nullptr;
   for (int i = 0; i < L.n; ++i) {
     const bool final_level = i + 1 == L.n;
     TopkArgs a{};
     a.scores = scores;
-    a.in_key = in_key;
+    a.in_val = in_val;
     a.in_idx = in_idx;
     a.n_in = L.len[i];
     a.slice = L.slice[i] > 0 ? L.slice[i] : 1;
@@ -566,7 +572,7 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
     } else {
       char* buf = w + (i & 1) * one;
       const int64_t n_out = rows * static_cast<int64_t>(L.slices[i]) * k;
-      a.out_key = reinterpret_cast<uint32_t*>(buf);
+      a.out_val = reinterpret_cast<float*>(buf);
       a.out_idx = reinterpret_cast<int32_t*>(buf + n_out * sizeof(uint32_t));
     }
     const Shape s = shape_for(a.slice);
@@ -579,7 +585,7 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
       else launch_shape<true, false>(s, blocks, a, stream);
     }
     if (hipGetLastError() != hipSuccess) return -1;
-    in_key = a.out_key;
+    in_val = a.out_val;
     in_idx = a.out_idx;
   }
   return 0;

@@ -5,7 +5,7 @@ and csa_forward descriptors as the benchmark), runs one step, and checks sampled
 outputs against the oracle one by one:
 
 - compressed entries of the step's chunk (oracle over the chunk's own streams) and
-  of the first bulk chunk (streams regenerated from the same seeded generator);
+  of the cache build (streams regenerated from the same seeded generator);
 - whole index-score rows of sampled queries (oracle over the GPU-stored keys);
 - the top-k set of those rows (near-tie rule: differences only where the oracle
   score is within 1e-4 relative of the k-th score);
@@ -95,12 +95,13 @@ def _check_chunk_compress(wl, io, b):
 
 
 def _check_bulk_compress(wl, samples=48):
-    """Sampled entries of the first bulk chunk of sequence 0 (streams regenerated)."""
+    """Sampled entries of sequence 0's cache build (streams regenerated: each sequence's
+    generator draws its whole KV streams, then its whole indexer streams)."""
     M, cfg = wl.meta, wl.cfg
     m, D, R, DI = M["m"], M["D"], M["R"], M["DI"]
     hca = M["mode"] == "hca"
     tokens = (M["ctx"] - M["T_step"]) if M["T_step"] else M["ctx"]
-    T = min(1 << 17, tokens)
+    T = tokens
     g = Gen(cfg.seed * 1000, DEV)
     n_st = 2 if hca else 4
     s = [g.normal((T, D), dtype=torch.bfloat16) for _ in range(n_st)]
@@ -121,10 +122,7 @@ def _check_bulk_compress(wl, samples=48):
         got = f64(wl.ios[0]["kv_cache"].data[0, i:i + 1])
         assert_close(got, want[:1], "bf16", f"bulk KV entry {i}")
     if not hca:
-        # the indexer streams are drawn after every KV chunk of the sequence
-        for c0 in range(T, tokens, 1 << 17):
-            for _ in range(4):
-                g.normal((min(1 << 17, tokens - c0), D), dtype=torch.bfloat16)
+        del s
         si = [g.normal((T, DI), dtype=torch.bfloat16) for _ in range(4)]
         for i in ents[1:8]:
             blk = [f64(x[m * (i - 1):m * (i + 1)]) for x in si]

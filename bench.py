@@ -317,7 +317,9 @@ def build_workload(key: str, layers: int, dev: str = "cuda") -> Workload:
 def _attn_kernels(ws, M) -> str:
     """The attention kernels one call launches: the main kernel, plus the combine kernel
     when the key range is split (the call then needs a workspace for the partials)."""
-    main = "attn_dma_kernel" if M["kv_format"] != "fp8mix" and M["D"] == 512 and M["R"] == 64 else "attn_mfma_kernel"
+    # D = 512 with 64 RoPE dims takes the LDS-DMA kernel (bf16 or FP8MIX cache; FP8MIX with 4 or 8 waves)
+    dma = M["D"] == 512 and M["R"] == 64 and (M["kv_format"] != "fp8mix" or M["H"] % 64 == 0)
+    main = "attn_dma_kernel" if dma else "attn_mfma_kernel"
     return main + ("+attn_combine_kernel" if ws.numel() > 1 else "")
 
 
@@ -361,7 +363,8 @@ def _add_stages(wl: Workload, csa, torch, dev):
         mx = M["ik_format"] == "mxfp4"
         wl.stages["index_scores"] = Stage(
             st_index, B * N * ik_entry + B * Tq * (HI * q_entry + HI * 4 + N * 4), 2.0 * HI * DI * sum_vis,
-            "index_mxfp4_kernel" if mx else ("index_prefill_kernel" if Tq >= 16 else "index_mfma_kernel"),
+            "index_mxfp4_kernel" if mx else ("index_prefill_kernel" if Tq >= 16 else
+                                             ("index_stream_kernel" if DI <= 128 else "index_mfma_kernel")),
             ("indexer.hip",),
             MFMA_FP4_PEAK if mx else MFMA_BF16_PEAK)
         wl.stages["topk"] = Stage(st_topk, B * Tq * (N * 4 + k * 4), 0.0, "topk_kernel", ("topk.hip",))
@@ -512,6 +515,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: st
 
 KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip",),
                   "attn_combine_kernel": ("mqa.hip",), "index_mfma_kernel": ("indexer.hip",),
+                  "index_stream_kernel": ("indexer.hip",),
                   "index_mxfp4_kernel": ("indexer.hip",), "index_prefill_kernel": ("indexer.hip",),
                   "topk_kernel": ("topk.hip",),
                   "compress_kernel": ("compress.hip",)}

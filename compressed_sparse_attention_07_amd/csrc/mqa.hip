@@ -511,11 +511,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 // memory operations outstanding", waited for with s_waitcnt and made visible to the
 // other waves by the barrier that follows.  The compiler does not see these loads;
 // the loop issues no other vector-memory operation.
+//
+// FP8MIX caches (FP8 = true): a row is three direct loads (448 e4m3 codes, 64 bf16
+// RoPE dims, the f32 entry scale) into a ring of raw rows; once a tile has landed,
+// one pass of the workgroup converts it (hardware e4m3 -> f32, times the scale,
+// rounded to bf16; window rows' RoPE dims rotated) into a single bf16 tile that the
+// MFMA loop reads exactly as in the bf16 case.
 
 constexpr int kDmaStages = 4;
 constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
 
-template <int NW, int R>
+template <int NW, int R, bool FP8>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int D = 512;
   constexpr int NT = NW * 64;
@@ -524,9 +530,15 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int NDB = D / 16;
   constexpr int RPW = kKT / NW;        // rows each wave loads per tile
   constexpr int STAGE = kKT * KP;      // bf16 per ring stage
-  static_assert(RPW * (kDmaStages - 2) < 64, "outstanding row loads must fit vmcnt");
+  constexpr int LPR = FP8 ? 3 : 1;     // direct loads per row
+  constexpr int RAWROW = (D - R) + 2 * R;  // bytes of an FP8MIX row: codes, then bf16 RoPE dims
+  static_assert(RPW * LPR * (kDmaStages - 2) < 64, "outstanding row loads must fit vmcnt");
+  static_assert(!FP8 || STAGE * 2 + kDmaStages * kKT * RAWROW <= kDmaStages * STAGE * 2, "raw rows fit the ring");
 
+  // bf16: kDmaStages tiles.  FP8MIX: the converted tile (the first STAGE) and the raw
+  // rows of kDmaStages tiles behind it.  The epilogue reuses all of it.
   __shared__ __attribute__((aligned(16))) uint16_t ring[kDmaStages * STAGE];
+  __shared__ float rscale[FP8 ? kDmaStages : 1][kKT];  // FP8MIX entry scales
   __shared__ __attribute__((aligned(16))) int idx_s[kDmaIdxCap];
   __shared__ __attribute__((aligned(16))) int kvalid[kDmaStages][kKT];
   __shared__ int64_t wpos_s[kDmaStages][kKT];  // window position of a window row, -1 otherwise
@@ -609,6 +621,45 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   // row wid*RPW + i, then each row's base address is broadcast to one row load
   auto issue = [&](int u) {
     const int st = u % kDmaStages;
+    if constexpr (FP8) {
+      // lane i < RPW resolves row wid*RPW + i to (row number, window or cache)
+      int64_t rid = S.b * a.Tw + (S.p - S.wp0);  // empty slot: the query's own window row
+      int isw = 1;
+      if (lane < RPW) {
+        const int j = wid * RPW + lane;
+        const int64_t slot = u_lo + static_cast<int64_t>(u) * kKT + j;
+        const bool live = slot < u_hi;
+        const bool sel = slot < u_nsel;
+        int64_t e = slot;
+        if (a.sparse) e = idx_s[min(slot - u_lo, static_cast<int64_t>(kDmaIdxCap - 1))];
+        const int64_t wp = u_wstart + (slot - u_nsel);
+        const bool ok = live && (!sel || e >= 0);
+        kvalid[st][j] = ok ? 1 : 0;
+        wpos_s[st][j] = (ok && !sel) ? wp : -1;
+        if (ok && sel) {
+          rid = S.b * a.kv_rows + e;
+          isw = 0;
+        } else if (ok) {
+          rid = S.b * a.Tw + (wp - S.wp0);
+        }
+      }
+      const uint32_t raw_b = ring_b + STAGE * 2 + (st * kKT + wid * RPW) * RAWROW;
+      const uint32_t sc_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&rscale[st][wid * RPW]));
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int64_t r = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(
+                              __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint64_t>(rid) >> 32), i))) << 32) |
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(rid), i)));
+        const bool w = __builtin_amdgcn_readlane(isw, i) != 0;
+        const uint8_t* codes = static_cast<const uint8_t*>(w ? a.win : a.kv) + r * (D - R);
+        const uint16_t* rope = (w ? a.win_rope : a.kv_rope) + r * R;
+        const float* scl = (w ? a.win_scale : a.kv_scale) + r;
+        if (lane < (D - R) / 16) lds_dma16(codes + lane * 16, raw_b + i * RAWROW);
+        if (lane < R / 8) lds_dma16(rope + lane * 8, raw_b + i * RAWROW + (D - R));
+        if (lane == 0) lds_dma4(scl, sc_b + i * 4);
+      }
+      return;
+    }
     const uint16_t* src = win_self;
     if (lane < RPW) {
       const int j = wid * RPW + lane;
@@ -663,6 +714,44 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const int64_t first = s_lo + static_cast<int64_t>(t) * kKT;
     return min(first + kKT, s_hi) > S.nsel && first < s_hi;
   };
+  // FP8MIX: raw rows of stage st -> the bf16 tile (codes times the entry scale; window
+  // rows' RoPE dims rotated to their own position)
+  auto convert = [&](int st) {
+    const uint8_t* Rw = reinterpret_cast<const uint8_t*>(ring + STAGE) + st * kKT * RAWROW;
+    for (int item = tid; item < kKT * (D / 8); item += NT) {
+      const int j = item / (D / 8);
+      const int d0 = 8 * (item % (D / 8));
+      uint4 o;
+      if (d0 < nope) {
+        const uint2 cd = *reinterpret_cast<const uint2*>(Rw + j * RAWROW + d0);
+        const float sc = rscale[st][j];
+        typedef float f2_t __attribute__((ext_vector_type(2)));
+        const f2_t x0 = __builtin_amdgcn_cvt_pk_f32_fp8(cd.x, false), x1 = __builtin_amdgcn_cvt_pk_f32_fp8(cd.x, true);
+        const f2_t x2 = __builtin_amdgcn_cvt_pk_f32_fp8(cd.y, false), x3 = __builtin_amdgcn_cvt_pk_f32_fp8(cd.y, true);
+        o = make_uint4(pack_bf16x2(x0.x * sc, x0.y * sc), pack_bf16x2(x1.x * sc, x1.y * sc),
+                       pack_bf16x2(x2.x * sc, x2.y * sc), pack_bf16x2(x3.x * sc, x3.y * sc));
+      } else {
+        o = *reinterpret_cast<const uint4*>(Rw + j * RAWROW + nope + 2 * (d0 - nope));
+        const int64_t wpj = wpos_s[st][j];
+        if (wpj >= 0) {
+          float x[8] = {bf16lo(o.x), bf16hi(o.x), bf16lo(o.y), bf16hi(o.y),
+                        bf16lo(o.z), bf16hi(o.z), bf16lo(o.w), bf16hi(o.w)};
+          const double kp = static_cast<double>(wpj + a.pos_offset);
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float cc, sn;
+            rope_cs_rev(kp, theta[(d0 + e - nope) / 2], &cc, &sn);
+            const float y0 = x[e], y1 = x[e + 1];
+            x[e] = y0 * cc - y1 * sn;
+            x[e + 1] = y0 * sn + y1 * cc;
+          }
+          o = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                         pack_bf16x2(x[6], x[7]));
+        }
+      }
+      *reinterpret_cast<uint4*>(&ring[j * KP + d0]) = o;
+    }
+  };
 
   // tiles 0..2 in flight while the queries are roped in registers
   if (ntiles > 0) issue(0);
@@ -699,17 +788,20 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int st = t % kDmaStages;
     const int later = min(ntiles - 1 - t, kDmaStages - 2);  // tiles issued after t
-    if (later >= 2) wait_vmcnt<2 * RPW>();
-    else if (later == 1) wait_vmcnt<RPW>();
+    if (later >= 2) wait_vmcnt<2 * RPW * LPR>();
+    else if (later == 1) wait_vmcnt<RPW * LPR>();
     else wait_vmcnt<0>();
     __syncthreads();
-    if (tile_has_window(t)) {
+    if constexpr (FP8) {
+      convert(st);  // the previous tile's readers are past the barrier above
+      __syncthreads();
+    } else if (tile_has_window(t)) {
       rope_window_rows(st);
       __syncthreads();
     }
     if (t + kDmaStages - 1 < ntiles) issue(t + kDmaStages - 1);  // into the stage freed by tile t-1
 
-    const uint16_t* K = ring + st * STAGE;
+    const uint16_t* K = FP8 ? ring : ring + st * STAGE;
     // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
     f32x4 sacc[2];
 #pragma unroll
@@ -1128,11 +1220,21 @@ int64_t max_slots_of(const AttnLaunch& L) {
   return (L.sparse ? static_cast<int64_t>(L.K) : L.N) + L.n_win;
 }
 
-// bf16 cache, D = 512 with RoPE on the last 64 dims, 2, 4 or 8 waves: the LDS-DMA kernel
+// bf16 or FP8MIX cache, D = 512 with RoPE on the last 64 dims, 2, 4 or 8 waves: the
+// LDS-DMA kernel (its row loads move 16-byte chunks of 16-byte aligned rows)
 bool dma_ok(const AttnLaunch& L) {
-  if (!mfma_ok(L) || L.kv.dtype != CSA_BF16 || L.D != 512 || L.rope_dims != 64) return false;
+  if (!mfma_ok(L) || L.D != 512 || L.rope_dims != 64) return false;
+  if (L.kv.dtype == CSA_FP8MIX) {
+    auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
+    if (!al(L.kv.data, 16) || !al(L.win.data, 16) || !al(L.kv.rope, 16) || !al(L.win.rope, 16) ||
+        !al(L.kv.scale, 4) || !al(L.win.scale, 4))
+      return false;
+  } else if (L.kv.dtype != CSA_BF16) {
+    return false;
+  }
   if (L.sparse && max_slots_of(L) > 64 * kDmaIdxCap) return false;
   const int nw = head_group(L.H, kDmaMaxWaves) / 16;
+  if (L.kv.dtype == CSA_FP8MIX) return nw == 4 || nw == 8;  // three loads per row: 16 rows per wave would overflow vmcnt
   return nw == 2 || nw == 4 || nw == 8;
 }
 
@@ -1216,9 +1318,15 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
     const int nw = P.hpw / 16;
     if (dma) {
       if (L.sparse && P.sps > kDmaIdxCap) return -1;  // excluded by the plan
-      if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
-      else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
-      else hipLaunchKernelGGL((attn_dma_kernel<2, 64>), dim3(static_cast<uint32_t>(grid)), block, 0, stream, a);
+      const dim3 g(static_cast<uint32_t>(grid));
+      if (fp8) {  // 4 or 8 waves (dma_ok)
+        if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, true>), g, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_dma_kernel<4, 64, true>), g, block, 0, stream, a);
+      } else {
+        if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, false>), g, block, 0, stream, a);
+        else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64, false>), g, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_dma_kernel<2, 64, false>), g, block, 0, stream, a);
+      }
     } else {
     CSA_LAUNCH_MFMA(128)
     CSA_LAUNCH_MFMA(256)

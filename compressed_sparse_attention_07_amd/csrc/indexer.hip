@@ -578,15 +578,18 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
                                                                           int64_t waves_per_token) {
   constexpr int DI = 128 * KS4;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerWG + (threadIdx.x >> 6);
-  const int64_t total = a.B * a.Tq * waves_per_token;
-  if (wave >= total) return;
-  const int64_t bt = wave / waves_per_token;
-  const int64_t b = bt / a.Tq;
-  const int64_t s_begin = (wave % waves_per_token) * keys_per_wave;
+  // fewer than 2^32 waves and tokens (the grid is 32-bit): 32-bit index arithmetic
+  const uint32_t wpt = static_cast<uint32_t>(waves_per_token);
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG + (threadIdx.x >> 6));
+  if (wave >= static_cast<uint64_t>(a.B * a.Tq) * wpt) return;
+  const uint32_t bt32 = wave / wpt;
+  const int64_t bt = bt32;
+  const int64_t b = bt32 / static_cast<uint32_t>(a.Tq);
+  const int64_t s_begin = static_cast<int64_t>(wave - bt32 * wpt) * keys_per_wave;
   const int64_t s_end = min(s_begin + keys_per_wave, a.N);
   const int64_t pos = a.q_pos[bt];
-  int64_t vis = pos / a.ratio;
+  int64_t vis = (pos >= 0 && pos <= 0xffffffffll) ? static_cast<int64_t>(static_cast<uint32_t>(pos) / static_cast<uint32_t>(a.ratio))
+                                                 : pos / a.ratio;
   vis = vis > a.N ? a.N : (vis < 0 ? 0 : vis);
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -681,6 +684,8 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
 
 typedef void (*MfmaKern)(IndexLaunch, int, int64_t);
 
+constexpr int kMxfp4Kpw = 512;  // smallest key range per wave of the MXFP4 kernel
+
 MfmaKern pick_mxfp4(int HB, int KS4) {
 #define CSA_MX(H_, K_) \
   if (HB == H_ && KS4 == K_) return index_mxfp4_kernel<H_, K_>;
@@ -744,10 +749,11 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
     if (k) {
       // MXFP4 keys are 68 bytes (DI = 128): longer ranges per wave for the same bytes
       const int64_t tokens = L.B * L.Tq;
-      int kpw = 512;
+      int kpw = kMxfp4Kpw;
       while (kpw < 8192 && tokens * ((L.N + kpw - 1) / kpw) > 8192) kpw *= 2;
       const int64_t wpt = (L.N + kpw - 1) / kpw;
       const int64_t grid = (tokens * wpt + kWavesPerWG - 1) / kWavesPerWG;
+      if (tokens * wpt >= (int64_t{1} << 32)) return -1;  // beyond the kernel's 32-bit wave index
       hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(grid)), dim3(kWavesPerWG * WAVE), 0, stream, L, kpw, wpt);
     } else {
       dim3 grid(static_cast<uint32_t>((L.N + kSimtThreads - 1) / kSimtThreads), static_cast<uint32_t>(L.B * L.Tq));

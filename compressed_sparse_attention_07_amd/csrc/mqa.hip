@@ -519,13 +519,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 // MFMA loop reads exactly as in the bf16 case.
 
 constexpr int kDmaStages = 4;
+constexpr bool kDmaPipe = true;  // prefill launches take the software-pipelined loop
 constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
 
-template <int NW, int R, bool FP8>
+template <int NW, int R, bool FP8, bool PIPE = false>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int D = 512;
   constexpr int NT = NW * 64;
-  constexpr int KP = D + 8;            // row pitch (bf16)
+  constexpr int KP = D + 16;           // row pitch (bf16): 1056 B, the S^T operand reads run at full LDS rate
   constexpr int NS = D / 32;
   constexpr int NDB = D / 16;
   constexpr int RPW = kKT / NW;        // rows each wave loads per tile
@@ -785,25 +786,8 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t % kDmaStages;
-    const int later = min(ntiles - 1 - t, kDmaStages - 2);  // tiles issued after t
-    if (later >= 2) wait_vmcnt<2 * RPW * LPR>();
-    else if (later == 1) wait_vmcnt<RPW * LPR>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if constexpr (FP8) {
-      convert(st);  // the previous tile's readers are past the barrier above
-      __syncthreads();
-    } else if (tile_has_window(t)) {
-      rope_window_rows(st);
-      __syncthreads();
-    }
-    if (t + kDmaStages - 1 < ntiles) issue(t + kDmaStages - 1);  // into the stage freed by tile t-1
-
-    const uint16_t* K = FP8 ? ring : ring + st * STAGE;
-    // ---- S^T = K Q^T for the 32 keys (two 16-key blocks)
-    f32x4 sacc[2];
+  // ---- S^T = K Q^T for the 32 keys of a tile (two 16-key blocks)
+  auto qk = [&](const uint16_t* K, f32x4 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -814,7 +798,9 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
       }
     }
-    // ---- online softmax for head h over this lane's 8 keys (16kb + 4grp + r)
+  };
+  // ---- online softmax for head h over this lane's 8 keys (16kb + 4grp + r); returns P^T
+  auto softmax = [&](int st, const f32x4 (&sacc)[2]) -> bf16x8 {
     float z[2][4];
     float mt = -INFINITY;
 #pragma unroll
@@ -853,10 +839,11 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
       }
     }
     l_run += psum;
-    const bf16x8 pB = __builtin_bit_cast(
-        bf16x8, make_uint4(pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3]), pack_bf16x2(pn[4], pn[5]),
-                           pack_bf16x2(pn[6], pn[7])));
-    // ---- O^T += V^T P^T (V^T by transpose reads of the row-major tile)
+    return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3]),
+                                                 pack_bf16x2(pn[4], pn[5]), pack_bf16x2(pn[6], pn[7])));
+  };
+  // ---- O^T += V^T P^T (V^T by transpose reads of the row-major tile)
+  auto pv = [&](const uint16_t* K, const bf16x8 pB) {
     const uint16_t* vb = K + (4 * grp + (col >> 2)) * KP + 4 * (col & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -865,6 +852,69 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pB, acc[db], 0, 0, 0);
     }
+  };
+
+  if constexpr (PIPE && !FP8) {
+    // Software-pipelined: tile t+1's S^T products are issued before tile t's softmax,
+    // so the softmax arithmetic runs while the matrix cores work.  Ring use at the top
+    // of iteration t: t (its PV is pending), t+1 (products now), t+2 and t+3 in flight;
+    // tile t+3 is issued once every wave is past tile t-1.
+    f32x4 sc[2];
+    if (ntiles > 0) {
+      if (ntiles > 2) wait_vmcnt<2 * RPW>();
+      else if (ntiles > 1) wait_vmcnt<RPW>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (tile_has_window(0)) {
+        rope_window_rows(0);
+        __syncthreads();
+      }
+      qk(ring, sc);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      const int st = t % kDmaStages;
+      f32x4 sn[2];
+      if (t + 1 < ntiles) {
+        // issued so far: tiles 0 .. min(t + 2, ntiles - 1); wait for t+1
+        if (t + 2 < ntiles) wait_vmcnt<RPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        const int st1 = (t + 1) % kDmaStages;
+        if (tile_has_window(t + 1)) {
+          rope_window_rows(st1);
+          __syncthreads();
+        }
+        if (t + 3 < ntiles) issue(t + 3);  // into the stage of tile t-1
+        qk(ring + st1 * STAGE, sn);
+      }
+      const bf16x8 pB = softmax(st, sc);
+      pv(ring + st * STAGE, pB);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
+    }
+  } else {
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t % kDmaStages;
+    const int later = min(ntiles - 1 - t, kDmaStages - 2);  // tiles issued after t
+    if (later >= 2) wait_vmcnt<2 * RPW * LPR>();
+    else if (later == 1) wait_vmcnt<RPW * LPR>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if constexpr (FP8) {
+      convert(st);  // the previous tile's readers are past the barrier above
+      __syncthreads();
+    } else if (tile_has_window(t)) {
+      rope_window_rows(st);
+      __syncthreads();
+    }
+    if (t + kDmaStages - 1 < ntiles) issue(t + kDmaStages - 1);  // into the stage freed by tile t-1
+
+    const uint16_t* K = FP8 ? ring : ring + st * STAGE;
+    f32x4 sacc[2];
+    qk(K, sacc);
+    const bf16x8 pB = softmax(st, sacc);
+    pv(K, pB);
+  }
   }
 
   float l_tot = l_run;
@@ -1323,9 +1373,15 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
         if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, true>), g, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_dma_kernel<4, 64, true>), g, block, 0, stream, a);
       } else {
-        if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, false>), g, block, 0, stream, a);
-        else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64, false>), g, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_dma_kernel<2, 64, false>), g, block, 0, stream, a);
+        if (kDmaPipe && P.nsplit == 1) {  // long key ranges: the software-pipelined loop
+          if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, false, true>), g, block, 0, stream, a);
+          else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64, false, true>), g, block, 0, stream, a);
+          else hipLaunchKernelGGL((attn_dma_kernel<2, 64, false, true>), g, block, 0, stream, a);
+        } else {
+          if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, false>), g, block, 0, stream, a);
+          else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64, false>), g, block, 0, stream, a);
+          else hipLaunchKernelGGL((attn_dma_kernel<2, 64, false>), g, block, 0, stream, a);
+        }
       }
     } else {
     CSA_LAUNCH_MFMA(128)

@@ -196,6 +196,16 @@ __device__ __forceinline__ void load_slice(const TopkArgs& a, int64_t blk, float
   }
 }
 
+// lane J of `mine` gets f(J) (a wave-uniform value), for J = J0 .. PER-1
+template <int J, int PER, typename F>
+__device__ __forceinline__ void count_rounds(uint32_t& mine, const F& f) {
+  if constexpr (J < PER) {
+    const uint32_t c = f(J);
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(mine) : "s"(c), "i"(J));
+    count_rounds<J + 1, PER>(mine, f);
+  }
+}
+
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {  // set bits of m below this lane
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
@@ -378,36 +388,32 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
   const bool with_eq = ties != 0u;
   uint32_t* tab = sh.hist[0];  // [NW][PER]
   uint32_t mine = 0;           // lane j < PER: this wave's count(s) of round j
-  if (one_test) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool sel = with_eq ? v[j] >= theta : v[j] > theta;
-      const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(sel)));
-      mine = lane == j ? c : mine;
-    }
+  // the (wave-uniform) count of round j goes straight into lane j
+  if (one_test && with_eq) {
+    count_rounds<0, PER>(mine, [&](int j) { return static_cast<uint32_t>(__popcll(__ballot(v[j] >= theta))); });
+  } else if (one_test) {
+    count_rounds<0, PER>(mine, [&](int j) { return static_cast<uint32_t>(__popcll(__ballot(v[j] > theta))); });
   } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(v[j] > theta))) |
-                         (static_cast<uint32_t>(__popcll(__ballot(v[j] == theta))) << 16);
-      mine = lane == j ? c : mine;
-    }
+    count_rounds<0, PER>(mine, [&](int j) {
+      return static_cast<uint32_t>(__popcll(__ballot(v[j] > theta))) |
+             (static_cast<uint32_t>(__popcll(__ballot(v[j] == theta))) << 16);
+    });
   }
   if (lane < PER) tab[wid * PER + lane] = mine;
   __syncthreads();
-  constexpr int T = PER * NW;  // <= NT
-  const int jw = tid / NW, ww = tid % NW;  // thread tid scans entry (round jw, wave ww)
-  const uint32_t cx = tid < T ? tab[ww * PER + jw] : 0u;
-  const uint32_t incl = wave_prefix_sum(cx);
-  if (lane == 63) sh.wave_a[wid] = incl;
-  __syncthreads();
-  uint32_t pre = 0;
+  // lane j < PER of wave w: the entries before round j of wave w in index order are
+  // all of rounds < j plus round j of waves < w; every wave reads the whole table
+  // instead of a separate scan pass (two barriers fewer)
+  uint32_t row = 0, before_w = 0;
+  if (lane < PER) {
 #pragma unroll
-  for (int w = 0; w < NW; ++w) pre += w < wid ? sh.wave_a[w] : 0u;
-  if (tid < T) tab[ww * PER + jw] = pre + incl - cx;  // exclusive prefix
-  __syncthreads();
-  const uint32_t base = lane < PER ? tab[wid * PER + lane] : 0u;  // lane j: round j's prefix
-
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t c = tab[w * PER + lane];
+      row += c;
+      before_w += w < wid ? c : 0u;
+    }
+  }
+  const uint32_t base = wave_prefix_sum(row) - row + before_w;  // lane j: round j's prefix
   // candidate indices, loaded now that the selection registers are free
   int32_t ix[PAIRS ? PER : 1];
   if (PAIRS) {
@@ -428,11 +434,18 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
     oi[slot] = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(lo + j * NT + tid);
     if (!FINAL) ov[slot] = v[j];
   };
-  if (one_test) {
+  if (one_test && with_eq) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const uint32_t bj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), j));
-      const bool sel = with_eq ? v[j] >= theta : v[j] > theta;
+      const bool sel = v[j] >= theta;
+      if (sel) put(j, bj + lane_prefix(__ballot(sel)));
+    }
+  } else if (one_test) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t bj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), j));
+      const bool sel = v[j] > theta;
       if (sel) put(j, bj + lane_prefix(__ballot(sel)));
     }
   } else {

@@ -236,8 +236,16 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
     vmin = fminf(vmin, fin ? v[j] : INFINITY);
   }
   nfin = wave_sum_u32(nfin);
-  vmax = wave_max(vmax);
-  vmin = -wave_max(-vmin);
+  {
+    // extremes through order-preserving integer images (DPP reductions); +-inf map to
+    // the ends of the order, and the values here are never NaN
+    auto okey = [](float x) {
+      const uint32_t u = __float_as_uint(x);
+      return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    };
+    vmax = key_value(wave_max_u32(okey(vmax)));
+    vmin = key_value(wave_min_u32(okey(vmin)));
+  }
   if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, __float_as_uint(vmax), __float_as_uint(vmin), 0u);
   for (int i = tid; i < 2 * (kBins + 4); i += NT) (&sh.hist[0][0])[i] = 0u;
   if (tid == 0) sh.ncand = 0u;

@@ -186,6 +186,26 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 15)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 31))),
              max(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 47)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63))));
 }
+// float sum and max over the wave by DPP row shifts (no LDS round trips); the result
+// is uniform and the order of the additions is fixed
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __uint_as_float(dpp_u32<kRowShr1, true>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kRowShr2, true>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kRowShr4, true>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kRowShr8, true>(0u, __float_as_uint(v)));
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 15));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 31));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 47));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v);
+// max of non-NaN floats through their order-preserving integer images
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t k = wave_max_u32((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_u32<kRowShr1, false>(0xffffffffu, v));
   v = min(v, dpp_u32<kRowShr2, false>(0xffffffffu, v));

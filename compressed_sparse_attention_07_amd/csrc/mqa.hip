@@ -980,36 +980,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int d0 = 8 * lane;
   const bool on = d0 < a.D;
   // every load this wave needs is issued before any is waited for: the sink, the
-  // position, the split statistics and the first batch of partial rows
+  // position, the split statistics and the first batch of partial rows.  The row loads
+  // are unconditional (splits past ns re-read split 0, lanes past D re-read dims 0..7;
+  // both get weight 0 or are not stored), so none waits inside a branch.
   const float sk = a.sink[h];
   const int64_t qp = a.q_pos[bt];
-  const float2 ml = lane < ns ? a.part_ml[th * ns + lane] : make_float2(-INFINITY, 0.f);
-  const uint16_t* pb = a.part_o + (th * ns) * a.D + d0;
+  const float2 ml = a.part_ml[th * ns + (lane < ns ? lane : 0)];
+  const float mlx = lane < ns ? ml.x : -INFINITY;
+  const uint16_t* pb = a.part_o + (th * ns) * a.D + (on ? d0 : 0);
   uint4 pv[kBatchSplits];
 #pragma unroll
   for (int u = 0; u < kBatchSplits; ++u)
-    pv[u] = (on && u < ns) ? *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(u) * a.D)
-                           : make_uint4(0, 0, 0, 0);
-  const float M = wave_max(ml.x);
-  const float wgt = (ml.x == -INFINITY) ? 0.f : __expf(ml.x - M) * ml.y;
-  const float L = wave_sum(wgt);
+    pv[u] = *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(u < ns ? u : 0) * a.D);
+  const float M = wave_max_dpp(mlx);
+  const float wgt = (mlx == -INFINITY) ? 0.f : __expf(mlx - M) * ml.y;
+  const float L = wave_sum_dpp(wgt);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int i0 = 0; i0 < ns; i0 += kBatchSplits) {
     if (i0 > 0) {
 #pragma unroll
       for (int u = 0; u < kBatchSplits; ++u)
-        pv[u] = (on && i0 + u < ns) ? *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(i0 + u) * a.D)
-                                    : make_uint4(0, 0, 0, 0);
+        pv[u] = *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(i0 + u < ns ? i0 + u : 0) * a.D);
     }
 #pragma unroll
     for (int u = 0; u < kBatchSplits; ++u) {
-      const float w = __shfl(wgt, (i0 + u) & 63, WAVE);
-      if (i0 + u < ns) {
-        o[0] = fmaf(w, bf16lo(pv[u].x), o[0]); o[1] = fmaf(w, bf16hi(pv[u].x), o[1]);
-        o[2] = fmaf(w, bf16lo(pv[u].y), o[2]); o[3] = fmaf(w, bf16hi(pv[u].y), o[3]);
-        o[4] = fmaf(w, bf16lo(pv[u].z), o[4]); o[5] = fmaf(w, bf16hi(pv[u].z), o[5]);
-        o[6] = fmaf(w, bf16lo(pv[u].w), o[6]); o[7] = fmaf(w, bf16hi(pv[u].w), o[7]);
-      }
+      // splits past ns carry weight 0 (their lanes hold m = -inf) and finite rows
+      const float w = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), (i0 + u) & 63));
+      o[0] = fmaf(w, bf16lo(pv[u].x), o[0]); o[1] = fmaf(w, bf16hi(pv[u].x), o[1]);
+      o[2] = fmaf(w, bf16lo(pv[u].y), o[2]); o[3] = fmaf(w, bf16hi(pv[u].y), o[3]);
+      o[4] = fmaf(w, bf16lo(pv[u].z), o[4]); o[5] = fmaf(w, bf16hi(pv[u].z), o[5]);
+      o[6] = fmaf(w, bf16lo(pv[u].w), o[6]); o[7] = fmaf(w, bf16hi(pv[u].w), o[7]);
     }
   }
   if (!on) return;

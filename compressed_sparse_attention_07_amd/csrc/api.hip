@@ -191,6 +191,7 @@ csa_status launched(int rc, const char* what) {
   if (rc == 0) return ok();
   if (rc == -3) return fail(CSA_ERR_WORKSPACE, "%s: workspace too small", what);
   if (rc == -2) return fail(CSA_ERR_UNSUPPORTED, "%s: dtype combination not implemented", what);
+  if (rc == -4) return fail(CSA_ERR_SHAPE, "%s: 2^32 or more workgroups", what);
   return fail(CSA_ERR_DEVICE, "%s: kernel launch failed (%s)", what, hipGetErrorString(hipGetLastError()));
 }
 

@@ -29,32 +29,31 @@ namespace csa {
 namespace {
 
 struct AttnArgs {
+  // what every workgroup reads first sits at the front of the argument block (three
+  // 64-byte lines), so a prologue fetches it in one burst
+  int H, D, n_win, hpw;
+  int nsplit, sps, K, ratio;
+  int sparse, R, out_dtype;
+  uint32_t nblk;  // blocks in the grid of the attention launch
+  float scale;
+  int64_t B, Tq, N;
+  int64_t kv_rows, Tw, pos_offset;
   const void* q;
   const int64_t* q_pos;
+  const int64_t* win_pos0;
+  const int32_t* idx;
   const void* kv;
+  const void* win;
   const uint16_t* kv_rope;
   const float* kv_scale;
-  int64_t kv_rows;
-  const void* win;
   const uint16_t* win_rope;
   const float* win_scale;
-  const int64_t* win_pos0;
-  int64_t Tw;
-  const int32_t* idx;
-  int K, ratio, sparse;
   const float* sink;
-  float scale;
-  int R;
-  double log2_base;
-  double theta_rev[64];  // RoPE frequency of pair j in revolutions per position
-  int64_t pos_offset;
-  int64_t B, Tq, N;
-  int H, D, n_win;
-  int hpw, nsplit, sps;
   void* out;
-  int out_dtype;
   uint16_t* part_o; // [tokens, H, nsplit, D] bf16, O / l of the split
   float2* part_ml;  // [tokens, H, nsplit] (running max, sum of exponentials)
+  double log2_base;
+  double theta_rev[64];  // RoPE frequency of pair j in revolutions per position
 };
 
 struct Slots {
@@ -552,9 +551,14 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
 
+  // The argument block's scalars are all fetched before the first is used: otherwise
+  // the compiler loads them a cache line at a time, each load after a full wait.
+  asm volatile("" ::"s"(a.H), "s"(a.hpw), "s"(a.nsplit), "s"(a.sps), "s"(a.K), "s"(a.sparse), "s"(a.n_win),
+               "s"(a.ratio), "s"(a.Tq), "s"(a.N), "s"(a.kv_rows), "s"(a.Tw), "s"(a.pos_offset), "s"(a.q),
+               "s"(a.q_pos), "s"(a.win_pos0), "s"(a.idx), "s"(a.kv), "s"(a.win), "s"(a.nblk));
   // the grid has fewer than 2^32 blocks: 32-bit index arithmetic
   const uint32_t n_hg = static_cast<uint32_t>(a.H / a.hpw);
-  const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
+  const uint32_t blk = xcd_block(blockIdx.x, a.nblk);
   const int hg = __builtin_amdgcn_readfirstlane(static_cast<int>(blk % n_hg));
   const uint32_t blk2 = blk / n_hg;
   const int sp = __builtin_amdgcn_readfirstlane(static_cast<int>(blk2 % static_cast<uint32_t>(a.nsplit)));
@@ -566,7 +570,8 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   // return in issue order, so the row loads the indices address go out while the
   // queries are still in flight.
   const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
-  const int64_t b_seq = div_nonneg(bt, a.Tq);
+  // bt < 2^32 (the grid) and so is Tq
+  const int64_t b_seq = static_cast<uint32_t>(bt) / static_cast<uint32_t>(a.Tq);
   const int64_t p_pre = a.q_pos[bt];
   const int64_t wp0_pre = a.win_pos0[b_seq];
   const double th_pre = tid < R / 2 ? a.theta_rev[tid] : 0.0;  // R <= 128 < 2 NT
@@ -1357,6 +1362,8 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
   AttnArgs a = make_args(L, P, ws);
   if (mfma) {
     const int64_t grid = tokens * (L.H / P.hpw) * P.nsplit;
+    if (grid >= (static_cast<int64_t>(1) << 32)) return -4;  // the kernels index blocks in 32 bits
+    a.nblk = static_cast<uint32_t>(grid);
     const dim3 block(P.hpw / 16 * WAVE);
     const bool fp8 = L.kv.dtype == CSA_FP8MIX;
 #define CSA_LAUNCH_MFMA_W(DD, NWV)                                                                     \

@@ -52,14 +52,23 @@ struct TopkArgs {
   float* out_val;           // candidate output: [rows, slices, k]
   int32_t* out_idx;         // candidate output [rows, slices, k], or the final [rows, k]
   int32_t* count;           // final level: [rows] or NULL
+  // Pre-thresholded selection (many long rows): row_tau[r] is an estimate from below of
+  // row r's k-th largest score.  A first-level slice whose entries >= tau fit in k keeps
+  // just those.  The last level (of two) flags a row whose candidates turned out to miss
+  // part of its top-k (redo[r] = 1, else 0), and a repair kernel recomputes such rows
+  // one workgroup each, through the spare candidate buffer.
+  const float* row_tau;     // first and last level: [rows] or NULL
+  int32_t* redo;            // last level and repair: [rows]
+  int64_t n_row;            // repair: scores per row
+  float* spare_val;         // repair: [rows, ceil(n_row / capacity), k] scratch
+  int32_t* spare_idx;
 };
 
 constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one wave
 
 template <int NT>
 struct Shared {
-  // radix levels alternate between the two; one spare slot past each counts
-  // non-finite values in the linear-scale histogram (never read)
+  // radix levels alternate between the two
   alignas(16) uint32_t hist[2][kBins + 4];
   alignas(16) uint4 wave_abc[NT / WAVE];
   uint32_t wave_a[NT / WAVE];
@@ -211,9 +220,10 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {  // set bits of m 
 }
 
 // Select slice blk's top-k from its values (every thread of the workgroup calls this;
-// it holds barriers).
+// it holds barriers).  Returns true, having written nothing but the flag, when the row
+// must be recomputed (last level of a pre-thresholded selection).
 template <int NT, int PER, bool PAIRS, bool FINAL>
-__device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, int64_t blk, float (&v)[PER]) {
+__device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, int64_t blk, float (&v)[PER]) {
   constexpr int NW = NT / WAVE;
   static_assert(PER % 2 == 0 && PER <= 64, "rounds per thread");
   const int tid = static_cast<int>(threadIdx.x);
@@ -236,6 +246,14 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
     vmin = fminf(vmin, fin ? v[j] : INFINITY);
   }
   nfin = wave_sum_u32(nfin);
+  // entries >= the row's estimated threshold (pre-thresholded first level)
+  const float tau = (!PAIRS && a.row_tau) ? a.row_tau[r] : -INFINITY;
+  uint32_t nge = 0;
+  if (tau > -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) nge += v[j] >= tau ? 1u : 0u;
+    nge = wave_sum_u32(nge);
+  }
   {
     // extremes through order-preserving integer images (DPP reductions); +-inf map to
     // the ends of the order, and the values here are never NaN
@@ -246,28 +264,43 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
     vmax = key_value(wave_max_u32(okey(vmax)));
     vmin = key_value(wave_min_u32(okey(vmin)));
   }
-  if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, __float_as_uint(vmax), __float_as_uint(vmin), 0u);
+  if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, __float_as_uint(vmax), __float_as_uint(vmin), nge);
   for (int i = tid; i < 2 * (kBins + 4); i += NT) (&sh.hist[0][0])[i] = 0u;
   if (tid == 0) sh.ncand = 0u;
   __syncthreads();
   nfin = 0;
   vmax = -INFINITY;
   vmin = INFINITY;
+  nge = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     const uint4 x = sh.wave_abc[w];
     nfin += x.x;
     vmax = fmaxf(vmax, __uint_as_float(x.y));
     vmin = fminf(vmin, __uint_as_float(x.z));
+    nge += x.w;
+  }
+  // last level: fewer than k candidates while a finite threshold was applied, so
+  // entries below it may belong to the row's top-k; the row is flagged for the repair
+  if (FINAL && a.row_tau) {
+    const bool shortfall = nfin < K && a.row_tau[r] > -INFINITY;
+    if (tid == 0) a.redo[r] = shortfall ? 1 : 0;
+    if (shortfall) return true;
   }
 
   // ---- B: threshold value theta and the number of theta-valued entries kept
   float theta;
   uint32_t ties, total_eq = 0;  // total_eq: entries == theta (needed when 0 < ties)
-  const uint32_t total_sel = nfin < K ? nfin : K;
+  uint32_t total_sel = nfin < K ? nfin : K;
   if (nfin <= K) {
     theta = -INFINITY;  // keep every finite value
     ties = 0u;
+  } else if (tau > -INFINITY && nge <= K) {
+    // every entry >= tau (all finite), in index order: one >= test
+    theta = tau;
+    ties = 1u;
+    total_eq = 1u;
+    total_sel = nge;
   } else if (vmin == vmax) {
     theta = vmax;  // every finite value is equal: the first k by index
     ties = K;
@@ -277,7 +310,7 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
     const float scale = static_cast<float>(kBins) / (vmax - vmin);
     if (scale > 0.f && scale < INFINITY) {
       // bin = floor((v - vmin) * kBins / (vmax - vmin)), monotone in v, so each bin is
-      // a contiguous value range; non-finite values go to the spare slot.  Scores
+      // a contiguous value range; non-finite values (bin kBins) are not counted.  Scores
       // spread over many bins, so the atomics rarely meet and the threshold bin
       // usually holds a few entries, which one wave then ranks exactly.  Each value's
       // bin is kept (two 16-bit bins per register) for the gather.
@@ -291,8 +324,8 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
 #pragma unroll
       for (int j = 0; j < PER; j += 2) {
         const uint32_t b0 = vbin(v[j]), b1 = vbin(v[j + 1]);
-        atomicAdd(&h1[b0], 1u);
-        atomicAdd(&h1[b1], 1u);
+        if (b0 < static_cast<uint32_t>(kBins)) atomicAdd(&h1[b0], 1u);
+        if (b1 < static_cast<uint32_t>(kBins)) atomicAdd(&h1[b1], 1u);
         binp[j / 2] = b0 | (b1 << 16);
       }
       __syncthreads();
@@ -471,6 +504,43 @@ __device__ __forceinline__ void select_slice(const TopkArgs& a, Shared<NT>& sh, 
     if (!FINAL) ov[i] = -INFINITY;
   }
   if (FINAL && a.count && tid == 0) a.count[r] = static_cast<int32_t>(total_sel);
+  return false;
+}
+
+// Exact selection of row r inside one workgroup, for a row whose pre-thresholded
+// candidates fell short: the row's slices of NT * PER scores one after another, each
+// slice's top-k into the row's part of the spare buffer, then the top-k of those.
+template <int NT, int PER>
+__device__ __forceinline__ void redo_row(const TopkArgs& a, Shared<NT>& sh, int64_t r) {
+  constexpr int64_t cap = static_cast<int64_t>(NT) * PER;
+  float v[PER];
+  TopkArgs b{};
+  b.scores = a.scores;
+  b.n_in = a.n_row;
+  b.slice = cap;
+  b.slices = static_cast<int>((a.n_row + cap - 1) / cap);
+  b.k = a.k;
+  b.out_val = a.spare_val;
+  b.out_idx = a.spare_idx;
+  for (int j = 0; j < b.slices; ++j) {
+    const int64_t blk = r * b.slices + j;
+    __syncthreads();  // the shared state is reused
+    load_slice<NT, PER, false>(b, blk, v);
+    select_slice<NT, PER, false, false>(b, sh, blk, v);
+  }
+  __threadfence();  // the candidates are read back by other waves of this workgroup
+  __syncthreads();
+  TopkArgs c{};
+  c.in_val = a.spare_val;
+  c.in_idx = a.spare_idx;
+  c.n_in = static_cast<int64_t>(b.slices) * a.k;  // <= cap (checked by the host)
+  c.slice = c.n_in;
+  c.slices = 1;
+  c.k = a.k;
+  c.out_idx = a.out_idx;
+  c.count = a.count;
+  load_slice<NT, PER, true>(c, r, v);
+  select_slice<NT, PER, true, true>(c, sh, r, v);
 }
 
 // PAIRS: input is (value, index) candidates; FINAL: write indices (and count) only.
@@ -480,6 +550,51 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   float v[PER];
   load_slice<NT, PER, PAIRS>(a, blockIdx.x, v);
   select_slice<NT, PER, PAIRS, FINAL>(a, sh, blockIdx.x, v);
+}
+
+// Rows flagged by the last level, each recomputed by one workgroup (most launches find
+// none: every workgroup reads its rows' flags and ends)
+template <int NT, int PER>
+__global__ __launch_bounds__(NT) void topk_repair_kernel(TopkArgs a, int64_t rows) {
+  __shared__ Shared<NT> sh;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    if (a.redo[r] == 0) continue;  // the same flag for the whole workgroup
+    redo_row<NT, PER>(a, sh, r);
+    __syncthreads();
+  }
+}
+
+// The rank-th largest of a spread sample of the row (kTauRuns runs of 256 consecutive
+// scores, evenly spaced) estimates the row's k-th largest from below when rank is a
+// few times k * sample / N: the fraction of the row at or above the sample's rank-th
+// largest has mean rank / sample and relative spread 1 / sqrt(rank).  One wave per
+// row finds it by a bitwise search over order-preserving keys (non-finite = 0, below
+// everything); -inf when fewer than rank sampled scores are finite.
+constexpr int kTauThreads = 256;
+constexpr int kTauRuns = 16;
+constexpr int kTauRun = 256;
+constexpr int kTauSample = kTauRuns * kTauRun;
+__global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(const float* scores, int64_t rows, int64_t N,
+                                                               uint32_t rank, float* tau) {
+  constexpr int PER = kTauSample / WAVE;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * (kTauThreads / WAVE) + (threadIdx.x >> 6);
+  if (r >= rows) return;  // no barriers below
+  const float* row = scores + r * N;
+  const int64_t step = (N - kTauRun) / (kTauRuns - 1);
+  uint32_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    key[j] = score_key(row[(j / (kTauRun / WAVE)) * step + (j % (kTauRun / WAVE)) * WAVE + lane]);
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c += key[j] >= cand ? 1u : 0u;
+    if (wave_sum_u32(c) >= rank) T = cand;
+  }
+  if (lane == 0) tau[r] = T != 0u ? key_value(T) : -INFINITY;
 }
 
 // workgroup shapes: (threads, keys per thread), slice capacity = threads * keys
@@ -510,6 +625,14 @@ void launch_shape(const Shape& s, int64_t blocks, const TopkArgs& a, hipStream_t
   else if (s.per == 16) launch_nt<512, 16, PAIRS, FINAL>(blocks, a, stream);
   else if (s.nt == 512) launch_nt<512, 32, PAIRS, FINAL>(blocks, a, stream);
   else launch_nt<1024, 32, PAIRS, FINAL>(blocks, a, stream);
+}
+
+void launch_repair(const Shape& s, int64_t rows, const TopkArgs& a, hipStream_t stream) {
+  const dim3 g(static_cast<uint32_t>(std::min<int64_t>(rows, 256)));
+  if (s.nt == 256) hipLaunchKernelGGL((topk_repair_kernel<256, 16>), g, dim3(256), 0, stream, a, rows);
+  else if (s.per == 16) hipLaunchKernelGGL((topk_repair_kernel<512, 16>), g, dim3(512), 0, stream, a, rows);
+  else if (s.nt == 512) hipLaunchKernelGGL((topk_repair_kernel<512, 32>), g, dim3(512), 0, stream, a, rows);
+  else hipLaunchKernelGGL((topk_repair_kernel<1024, 32>), g, dim3(1024), 0, stream, a, rows);
 }
 
 // Selection levels: input entries per row, slice length and slices per row of each.
@@ -560,21 +683,37 @@ size_t level_buffer_bytes(int64_t rows, const Levels& L, int k) {
   return (static_cast<size_t>(rows * mx) * (sizeof(uint32_t) + sizeof(int32_t)) + 255) / 256 * 256;
 }
 
+// Pre-thresholding pays off for many long rows: the sample rank aims at 4k entries per
+// row at or above the estimate, and a first-level slice's expected share of those must
+// stay well under k (so slices nearly always take the cheap path).
+uint32_t tau_rank(int64_t rows, int64_t N, int k, const Levels& L) {
+  if (L.n != 2 || rows < 256 || N < 8 * L.slice[0] || N < 4 * static_cast<int64_t>(kTauSample)) return 0;
+  // a row recomputed by the last level's workgroup: slices of its capacity, whose
+  // candidates fit it (and the spare buffer)
+  const int64_t cap = shape_for(L.slice[1]).cap();
+  const int64_t sl = (N + cap - 1) / cap;
+  if (sl * k > cap || sl > L.slices[0]) return 0;
+  const int64_t rank = (4 * static_cast<int64_t>(k) * kTauSample + N - 1) / N;
+  return rank >= 1 && rank <= kTauSample / 8 ? static_cast<uint32_t>(rank) : 0u;
+}
+
+size_t tau_bytes(int64_t rows) { return (static_cast<size_t>(rows) * 8 + 255) / 256 * 256; }
+
 }  // namespace
 
-// Workspace: two candidate buffers (keys + indices), sized for the largest level output.
+// Workspace: two candidate buffers (keys + indices), sized for the largest level
+// output, then (pre-thresholded selection) the row thresholds and repair flags.
 size_t topk_workspace_bytes(int64_t rows, int64_t N, int k) {
   if (rows <= 0 || N <= 0) return 0;
   const Levels L = plan_levels(rows, N, k);
-  return L.n == 1 ? 0 : 2 * level_buffer_bytes(rows, L, k);
+  if (L.n == 1) return 0;
+  return 2 * level_buffer_bytes(rows, L, k) + (tau_rank(rows, N, k, L) ? tau_bytes(rows) : 0);
 }
 
-int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, void* ws,
-                hipStream_t stream) {
-  if (rows == 0) return 0;
-  const Levels L = N > 0 ? plan_levels(rows, N, k) : Levels{1, {0}, {1}, {1}};
-  const size_t one = level_buffer_bytes(rows, L, k);
-  char* w = static_cast<char*>(ws);
+namespace {
+
+int run_levels(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, char* w,
+               size_t one, const Levels& L, const float* row_tau, int32_t* redo, hipStream_t stream) {
   const float* in_val = nullptr;
   const int32_t* in_idx = nullptr;
   for (int i = 0; i < L.n; ++i) {
@@ -588,8 +727,10 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
     a.slices = L.slices[i];
     a.k = k;
     a.count = count;
+    if (i == 0 || final_level) a.row_tau = row_tau;
     if (final_level) {
       a.out_idx = idx;
+      a.redo = redo;
     } else {
       char* buf = w + (i & 1) * one;
       const int64_t n_out = rows * static_cast<int64_t>(L.slices[i]) * k;
@@ -606,10 +747,41 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
       else launch_shape<true, false>(s, blocks, a, stream);
     }
     if (hipGetLastError() != hipSuccess) return -1;
+    if (final_level && row_tau) {
+      // flagged rows again, exactly, through the spare buffer (not the one holding
+      // this level's input, which level 0 wrote)
+      const int64_t cap = s.cap();
+      const int64_t n_spare = rows * ((N + cap - 1) / cap) * k;
+      char* spare = w + (i & 1) * one;
+      a.n_row = N;
+      a.spare_val = reinterpret_cast<float*>(spare);
+      a.spare_idx = reinterpret_cast<int32_t*>(spare + n_spare * sizeof(uint32_t));
+      launch_repair(s, rows, a, stream);
+      if (hipGetLastError() != hipSuccess) return -1;
+    }
     in_val = a.out_val;
     in_idx = a.out_idx;
   }
   return 0;
+}
+
+}  // namespace
+
+int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, void* ws,
+                hipStream_t stream) {
+  if (rows == 0) return 0;
+  const Levels L = N > 0 ? plan_levels(rows, N, k) : Levels{1, {0}, {1}, {1}};
+  const size_t one = level_buffer_bytes(rows, L, k);
+  char* w = static_cast<char*>(ws);
+  const uint32_t rank = N > 0 ? tau_rank(rows, N, k, L) : 0u;
+  if (rank == 0) return run_levels(scores, rows, N, k, idx, count, w, one, L, nullptr, nullptr, stream);
+  float* tau = reinterpret_cast<float*>(w + 2 * one);
+  int32_t* redo = reinterpret_cast<int32_t*>(w + 2 * one + static_cast<size_t>(rows) * 4);
+  constexpr int64_t rows_per_wg = kTauThreads / WAVE;
+  hipLaunchKernelGGL(topk_tau_kernel, dim3(static_cast<uint32_t>((rows + rows_per_wg - 1) / rows_per_wg)),
+                     dim3(kTauThreads), 0, stream, scores, rows, N, rank, tau);
+  if (hipGetLastError() != hipSuccess) return -1;
+  return run_levels(scores, rows, N, k, idx, count, w, one, L, tau, redo, stream);
 }
 
 }  // namespace csa

@@ -267,6 +267,42 @@ def test_topk_value_spreads(N, k):
     assert np.array_equal(idx.cpu().numpy(), wi)
 
 
+@pytest.mark.parametrize("k", [1024, 100])
+def test_topk_prethresholded(k):
+    """Many long rows take the pre-thresholded levels (a sampled estimate of each row's
+    k-th largest score, slices keeping their entries at or above it).  Rows here cover
+    the cheap path, ties at the estimate, a masked tail that leaves too few sampled
+    scores finite (no estimate), a row whose estimate overshoots (only sampled positions
+    are large: the row is recomputed by the plain levels), equal rows and special
+    values; all must match the definition exactly."""
+    rows, N = 256, 131072
+    say(f"topk prethresholded rows={rows} N={N} k={k}")
+    g = Gen(5150 + k, DEV)
+    s = g.normal((rows, N))
+    s[200] = torch.round(s[200] * 2) / 2
+    s[201, 1000:] = -float("inf")
+    s[202, 40000:] = -float("inf")
+    # positions a spread sample of 64 runs of 64 would read: large values at 150 of
+    # them, zeros elsewhere, so fewer than k entries reach the sample's estimate
+    step = (N - 64) // 63
+    sampled = (torch.arange(64, device=DEV)[:, None] * step + torch.arange(64, device=DEV)[None, :]).flatten()
+    s[203] = 0.0
+    s[203, sampled[::27][:150]] = 10.0 + torch.arange(150, device=DEV, dtype=torch.float32)
+    s[204] = 1.0
+    s[205, ::5] = float("nan")
+    s[205, 1::7] = -0.0
+    s[205, 2::7] = 0.0
+    s[206] = -float("inf")
+    idx = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((rows,), dtype=torch.int32, device=DEV)
+    csa.csa_topk(s, k, idx, cnt)
+    torch.cuda.synchronize()
+    wi, wc = O.topk(s.cpu().numpy().astype(np.float64), k)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    bad = [r for r in range(rows) if gc[r] != wc[r] or not np.array_equal(gi[r], wi[r])]
+    assert not bad, f"rows differ: {bad[:10]}"
+
+
 # ------------------------------------------------------------------ attention
 
 

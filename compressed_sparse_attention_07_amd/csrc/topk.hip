@@ -58,6 +58,11 @@ struct TopkArgs {
   // part of its top-k (redo[r] = 1, else 0), and a repair kernel recomputes such rows
   // one workgroup each, through the spare candidate buffer.
   const float* row_tau;     // first and last level: [rows] or NULL
+  // ... whose first level then writes each slice's candidate count instead of padding
+  // its k slots, and whose last level reads only the counted candidates (k a multiple
+  // of the last level's thread count, so a thread's j-th slot lies in a uniform slice)
+  int32_t* out_cnt;         // first level: [rows, slices] or NULL
+  const int32_t* in_cnt;    // last level: [rows, n_in / k] or NULL
   int32_t* redo;            // last level and repair: [rows]
   int64_t n_row;            // repair: scores per row
   float* spare_val;         // repair: [rows, ceil(n_row / capacity), k] scratch
@@ -187,6 +192,21 @@ __device__ __forceinline__ void load_slice(const TopkArgs& a, int64_t blk, float
   const int64_t lo = static_cast<int64_t>(sl) * a.slice;
   const int n = static_cast<int>(min(a.n_in, lo + a.slice) - lo);  // <= NT * PER
   const float* src = (PAIRS ? a.in_val : a.scores) + r * a.n_in + lo;
+  if (PAIRS && a.in_cnt) {
+    // slot j NT + t lies in candidate list (j NT) / k (one slice per row here, lo = 0):
+    // slots past that list's count read nothing (out of the buffer's range) and are -inf
+    const __amdgpu_buffer_rsrc_t bs = buffer_view(src, static_cast<int64_t>(n) * 4);
+    const int32_t* cnt = a.in_cnt + r * (a.n_in / a.k);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = j * NT;
+      const int c = e < n ? cnt[e / a.k] : 0;  // wave-uniform
+      const bool ok = (e % a.k) + tid < c;
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs, ok ? 4 * (e + tid) : 0x7ffffff0, 0, 0));
+      v[j] = ok ? x : -INFINITY;
+    }
+    return;
+  }
   if (n == NT * PER) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] = src[j * NT + tid];
@@ -460,7 +480,11 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
   if (PAIRS) {
     const __amdgpu_buffer_rsrc_t bi = buffer_view(a.in_idx + r * a.n_in + lo, static_cast<int64_t>(n) * 4);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) ix[j] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(bi, 4 * (j * NT + tid), 0, 0));
+    for (int j = 0; j < PER; ++j) {
+      // slots holding no candidate (-inf) are never selected: their index is not read
+      const uint32_t off = (a.in_cnt && !(v[j] > -INFINITY)) ? 0x7ffffff0u : 4u * (j * NT + tid);
+      ix[j] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(bi, off, 0, 0));
+    }
   }
   int32_t* oi;
   float* ov = nullptr;
@@ -499,9 +523,13 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
       if (gt || (eq && tbf < ties)) put(j, gb + (tbf < ties ? tbf : ties));
     }
   }
-  for (int i = static_cast<int>(total_sel) + tid; i < a.k; i += NT) {
-    oi[i] = -1;
-    if (!FINAL) ov[i] = -INFINITY;
+  if (!FINAL && a.out_cnt) {
+    if (tid == 0) a.out_cnt[r * a.slices + sl] = static_cast<int32_t>(total_sel);
+  } else {
+    for (int i = static_cast<int>(total_sel) + tid; i < a.k; i += NT) {
+      oi[i] = -1;
+      if (!FINAL) ov[i] = -INFINITY;
+    }
   }
   if (FINAL && a.count && tid == 0) a.count[r] = static_cast<int32_t>(total_sel);
   return false;
@@ -557,42 +585,80 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 template <int NT, int PER>
 __global__ __launch_bounds__(NT) void topk_repair_kernel(TopkArgs a, int64_t rows) {
   __shared__ Shared<NT> sh;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    if (a.redo[r] == 0) continue;  // the same flag for the whole workgroup
-    redo_row<NT, PER>(a, sh, r);
-    __syncthreads();
+  __shared__ int32_t flag[NT];
+  const int tid = static_cast<int>(threadIdx.x);
+  // rows blockIdx.x + gridDim.x * i; one flag per thread and chunk, all read at once
+  for (int64_t c0 = 0; c0 * gridDim.x + blockIdx.x < rows; c0 += NT) {
+    const int64_t rr = (c0 + tid) * gridDim.x + blockIdx.x;
+    const int32_t f = rr < rows ? a.redo[rr] : 0;
+    flag[tid] = f;
+    if (!__syncthreads_or(f)) continue;
+    for (int i = 0; i < NT; ++i) {
+      if (flag[i] == 0) continue;  // the same for the whole workgroup
+      redo_row<NT, PER>(a, sh, (c0 + i) * gridDim.x + blockIdx.x);
+      __syncthreads();
+    }
+    __syncthreads();  // flag[] is rewritten by the next chunk
   }
 }
 
-// The rank-th largest of a spread sample of the row (kTauRuns runs of 256 consecutive
-// scores, evenly spaced) estimates the row's k-th largest from below when rank is a
+// The rank-th largest of a spread sample of the row (kTauRuns runs of kTauRun
+// consecutive scores, evenly spaced; few runs, so few pages per row; shifted by a
+// row-dependent multiple of 64 scores, so rows with a power-of-two length do not all
+// start their runs on the same memory channels) estimates the row's k-th largest from below when rank is a
 // few times k * sample / N: the fraction of the row at or above the sample's rank-th
 // largest has mean rank / sample and relative spread 1 / sqrt(rank).  One wave per
-// row finds it by a bitwise search over order-preserving keys (non-finite = 0, below
-// everything); -inf when fewer than rank sampled scores are finite.
+// row finds it, to 16 bits, by a bitwise search over order-preserving keys (non-finite
+// = 0, below everything); -inf when fewer than rank sampled scores are finite.
 constexpr int kTauThreads = 256;
-constexpr int kTauRuns = 16;
-constexpr int kTauRun = 256;
+constexpr int kTauRuns = 4;
+constexpr int kTauRun = 1024;
 constexpr int kTauSample = kTauRuns * kTauRun;
+constexpr int kTauJitter = 64 * 64;  // largest run shift
 __global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(const float* scores, int64_t rows, int64_t N,
                                                                uint32_t rank, float* tau) {
   constexpr int PER = kTauSample / WAVE;
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * (kTauThreads / WAVE) + (threadIdx.x >> 6);
   if (r >= rows) return;  // no barriers below
-  const float* row = scores + r * N;
-  const int64_t step = (N - kTauRun) / (kTauRuns - 1);
+  const int64_t step = ((N - kTauRun - kTauJitter) / (kTauRuns - 1)) & ~static_cast<int64_t>(63);
+  const float* row = scores + r * N + ((static_cast<uint32_t>(r) * 2654435761u) >> 26) * 64;
   uint32_t key[PER];
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
+    // 16-byte loads: lane l holds scores 4 l .. 4 l + 3 of each 256-score piece
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    key[j] = score_key(row[(j / (kTauRun / WAVE)) * step + (j % (kTauRun / WAVE)) * WAVE + lane]);
+    for (int j = 0; j < PER; j += 4) {
+      const int piece = j / 4;  // kTauRun / 256 pieces per run
+      const float4 x = *reinterpret_cast<const float4*>(
+          row + (piece / (kTauRun / 256)) * step + (piece % (kTauRun / 256)) * 256 + 4 * lane);
+      key[j] = score_key(x.x);
+      key[j + 1] = score_key(x.y);
+      key[j + 2] = score_key(x.z);
+      key[j + 3] = score_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      key[j] = score_key(row[(j / (kTauRun / WAVE)) * step + (j % (kTauRun / WAVE)) * WAVE + lane]);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    // a plain register value: otherwise the compiler keeps each key's finiteness as a
+    // lane mask and re-tests it in every step of the search
+    asm volatile("" : "+v"(key[j]));
+  }
+  // the top 16 key bits suffice (the low ones cleared, T stays a lower bound of the
+  // rank-th largest key); counts come from ballots, so the sums are scalar
   uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= 16; --b) {
     const uint32_t cand = T | (1u << b);
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) c += key[j] >= cand ? 1u : 0u;
-    if (wave_sum_u32(c) >= rank) T = cand;
+    for (int j = 0; j < PER; ++j) {
+      c += static_cast<uint32_t>(__popcll(__ballot(key[j] >= cand)));
+      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound the masks held at once
+    }
+    if (c >= rank) T = cand;
   }
   if (lane == 0) tau[r] = T != 0u ? key_value(T) : -INFINITY;
 }
@@ -628,7 +694,7 @@ void launch_shape(const Shape& s, int64_t blocks, const TopkArgs& a, hipStream_t
 }
 
 void launch_repair(const Shape& s, int64_t rows, const TopkArgs& a, hipStream_t stream) {
-  const dim3 g(static_cast<uint32_t>(std::min<int64_t>(rows, 256)));
+  const dim3 g(static_cast<uint32_t>(std::min<int64_t>(rows, 32)));
   if (s.nt == 256) hipLaunchKernelGGL((topk_repair_kernel<256, 16>), g, dim3(256), 0, stream, a, rows);
   else if (s.per == 16) hipLaunchKernelGGL((topk_repair_kernel<512, 16>), g, dim3(512), 0, stream, a, rows);
   else if (s.nt == 512) hipLaunchKernelGGL((topk_repair_kernel<512, 32>), g, dim3(512), 0, stream, a, rows);
@@ -697,7 +763,10 @@ uint32_t tau_rank(int64_t rows, int64_t N, int k, const Levels& L) {
   return rank >= 1 && rank <= kTauSample / 8 ? static_cast<uint32_t>(rank) : 0u;
 }
 
-size_t tau_bytes(int64_t rows) { return (static_cast<size_t>(rows) * 8 + 255) / 256 * 256; }
+// thresholds and repair flags, then the first level's per-slice candidate counts
+size_t tau_bytes(int64_t rows, const Levels& L) {
+  return (static_cast<size_t>(rows) * (8 + 4 * static_cast<size_t>(L.slices[0])) + 255) / 256 * 256;
+}
 
 }  // namespace
 
@@ -707,13 +776,13 @@ size_t topk_workspace_bytes(int64_t rows, int64_t N, int k) {
   if (rows <= 0 || N <= 0) return 0;
   const Levels L = plan_levels(rows, N, k);
   if (L.n == 1) return 0;
-  return 2 * level_buffer_bytes(rows, L, k) + (tau_rank(rows, N, k, L) ? tau_bytes(rows) : 0);
+  return 2 * level_buffer_bytes(rows, L, k) + (tau_rank(rows, N, k, L) ? tau_bytes(rows, L) : 0);
 }
 
 namespace {
 
 int run_levels(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, char* w,
-               size_t one, const Levels& L, const float* row_tau, int32_t* redo, hipStream_t stream) {
+               size_t one, const Levels& L, const float* row_tau, int32_t* redo, int32_t* cnt, hipStream_t stream) {
   const float* in_val = nullptr;
   const int32_t* in_idx = nullptr;
   for (int i = 0; i < L.n; ++i) {
@@ -728,6 +797,10 @@ int run_levels(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx
     a.k = k;
     a.count = count;
     if (i == 0 || final_level) a.row_tau = row_tau;
+    // ragged candidate lists (pre-thresholded, two levels): see TopkArgs
+    const bool ragged = row_tau && k % shape_for(L.slice[L.n - 1]).nt == 0;
+    if (ragged && i == 0) a.out_cnt = cnt;
+    if (ragged && final_level) a.in_cnt = cnt;
     if (final_level) {
       a.out_idx = idx;
       a.redo = redo;
@@ -774,14 +847,15 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
   const size_t one = level_buffer_bytes(rows, L, k);
   char* w = static_cast<char*>(ws);
   const uint32_t rank = N > 0 ? tau_rank(rows, N, k, L) : 0u;
-  if (rank == 0) return run_levels(scores, rows, N, k, idx, count, w, one, L, nullptr, nullptr, stream);
+  if (rank == 0) return run_levels(scores, rows, N, k, idx, count, w, one, L, nullptr, nullptr, nullptr, stream);
   float* tau = reinterpret_cast<float*>(w + 2 * one);
   int32_t* redo = reinterpret_cast<int32_t*>(w + 2 * one + static_cast<size_t>(rows) * 4);
+  int32_t* cnt = reinterpret_cast<int32_t*>(w + 2 * one + static_cast<size_t>(rows) * 8);
   constexpr int64_t rows_per_wg = kTauThreads / WAVE;
   hipLaunchKernelGGL(topk_tau_kernel, dim3(static_cast<uint32_t>((rows + rows_per_wg - 1) / rows_per_wg)),
                      dim3(kTauThreads), 0, stream, scores, rows, N, rank, tau);
   if (hipGetLastError() != hipSuccess) return -1;
-  return run_levels(scores, rows, N, k, idx, count, w, one, L, tau, redo, stream);
+  return run_levels(scores, rows, N, k, idx, count, w, one, L, tau, redo, cnt, stream);
 }
 
 }  // namespace csa

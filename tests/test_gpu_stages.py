@@ -282,10 +282,12 @@ def test_topk_prethresholded(k):
     s[200] = torch.round(s[200] * 2) / 2
     s[201, 1000:] = -float("inf")
     s[202, 40000:] = -float("inf")
-    # positions a spread sample of 64 runs of 64 would read: large values at 150 of
-    # them, zeros elsewhere, so fewer than k entries reach the sample's estimate
-    step = (N - 64) // 63
-    sampled = (torch.arange(64, device=DEV)[:, None] * step + torch.arange(64, device=DEV)[None, :]).flatten()
+    # positions the spread sample (4 runs of 1024, shifted per row) reads for row 203:
+    # large values at 150 of them, zeros elsewhere, so fewer than k entries reach the
+    # sample's estimate
+    step = (N - 1024 - 4096) // 3 // 64 * 64
+    shift = ((203 * 2654435761) % 2**32 >> 26) * 64
+    sampled = (shift + torch.arange(4, device=DEV)[:, None] * step + torch.arange(1024, device=DEV)[None, :]).flatten()
     s[203] = 0.0
     s[203, sampled[::27][:150]] = 10.0 + torch.arange(150, device=DEV, dtype=torch.float32)
     s[204] = 1.0

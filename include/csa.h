@@ -152,6 +152,10 @@ csa_status csa_index_scores(const csa_buf* qI, const float* wI, const csa_buf* k
  * selected.  idx [rows, k] receives the selected indices in ascending order,
  * padded with -1; count [rows] (optional, may be NULL) the number selected.
  * Limits: 1 <= k <= 4096, N < 2^31.
+ * ws (device, caller-owned, at least csa_topk_workspace_size bytes, 0 for rows of
+ * at most 32768 scores when rows <= 64) holds the candidate lists between selection
+ * levels and, for many long rows, a sampled per-row estimate of the k-th score; the
+ * result is exact whatever the estimate (rows it misjudges are recomputed).
  */
 size_t csa_topk_workspace_size(int64_t rows, int64_t N, int32_t k);
 csa_status csa_topk(const float* scores, int64_t rows, int64_t N, int32_t k, int32_t* idx,

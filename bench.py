@@ -552,8 +552,8 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.kernel, src_hash(*srcs), out, args.profile_cmd, tag)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "the decode workload shards by sequence (see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): there is no multi-GPU path; "
+              "decode shards by sequence, each GPU serving its own sequences", file=sys.stderr)
         sys.exit(2)
 
     import torch

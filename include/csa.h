@@ -54,7 +54,7 @@ typedef enum csa_status {
   CSA_ERR_DTYPE = 3,       /* dtype (combination) not supported by this call    */
   CSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
   CSA_ERR_DEVICE = 5,      /* no gfx950 device current, or a launch failed      */
-  CSA_ERR_UNSUPPORTED = 6  /* valid request this build does not implement       */
+  CSA_ERR_UNSUPPORTED = 6  /* valid request the library does not implement      */
 } csa_status;
 
 /*

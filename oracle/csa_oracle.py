@@ -22,7 +22,7 @@ the definition states.  Sources (see ``oracle/__init__.py`` for the page list):
 * ``hca_dense``     -- [V4-CN] §2.3.2 and [NOTES] "关键设计 2": dense attention over
   every visible compressed entry plus the window.
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
 softmax axis = positions (per channel); entry 0 has no previous block (b-branch
 empty); compressed entry i sits at RoPE position ratio*i; entry i is visible to the
 query at t iff i < floor(t/ratio); the window is positions max(0,t-n_win+1)..t,

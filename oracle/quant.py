@@ -15,7 +15,7 @@ element by element, with exact float64 arithmetic wherever the format allows:
 Where the pages fix the use: [V4-CN] §2.3.4 (RoPE dims kept in BF16, the other KV
 dims in FP8) and §3.4 (the indexer's QK path cached, loaded and multiplied in
 MXFP4 with 1x32 scaling tiles).  The per-entry FP8 scale s = amax/448 (computed in
-fp32) is this build's reading; the pages do not give the scale recipe.
+fp32) is the reading taken here; the pages do not give the scale recipe.
 
 Decisions (a quantized code) are taken in the precision the format and the
 reading fix: the scale and x/s are single fp32 operations, exactly as a device

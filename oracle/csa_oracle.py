@@ -16,11 +16,14 @@ the definition states.  Sources (see ``oracle/__init__.py`` for the page list):
 * ``topk``          -- [V4-CN] §2.3.1 (top-k selector) / [NOTES] "关键设计 1"
   (C_t = TopK_k(I_t,:)).
 * ``mqa``           -- [V4-CN] §2.3.1 (shared-KV MQA: an entry is both key and
-  value), §2.3.3 (sliding-window branch, attention sink denominator, inverse RoPE);
-  [NOTES] csa()/hca() sketches: one attention over the concatenation of the
-  selected/compressed entries and the window.
+  value), §2.3.3 (sliding-window branch whose raw KV entries join the compressed
+  ones in the core attention, attention sink denominator, inverse RoPE).
 * ``hca_dense``     -- [V4-CN] §2.3.2 and [NOTES] "关键设计 2": dense attention over
   every visible compressed entry plus the window.
+* ``csa_layer`` / ``hca_layer`` -- one layer of one sequence composed from the
+  definitions above ([V4-CN] §2.3.1-§2.3.3): compressed entries, each query's
+  selected (CSA) or visible (HCA) entries, its window keys, one softmax with the
+  sink, the output rotated back.
 
 Readings where the pages are silent or garbled:
 softmax axis = positions (per channel); entry 0 has no previous block (b-branch
@@ -31,7 +34,10 @@ roped at their own positions, in one softmax with the entries; inverse RoPE uses
 ascending and padded with -1; pos_offset shifts every RoPE position (only).
 
 Parity: every function is pinned by tests/test_oracle_*.py (closed forms,
-invariants, brute force, library routines); none is "parity unpinned".
+invariants, brute force, library routines); none is "parity unpinned".  The layer
+compositions are pinned by shift invariance, constant streams, the bf16 storage
+points, the equality of CSA with k >= visible and dense attention, and scalar-loop
+brute force of both layers on tiny inputs.
 """
 
 from __future__ import annotations
@@ -269,11 +275,39 @@ def store(x, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def _window_keys(win, win_pos0: int, p: int, n_win: int, pos_offset: int, rope_dims: int,
+                 rope_base: float) -> np.ndarray:
+    """Raw tokens of the sliding window of the query at position p, each roped at its
+    own position ([V4-CN] §2.3.3: the last n_win uncompressed tokens, the query's own
+    included)."""
+    wpos = window_positions(p, n_win)
+    return rope(np.asarray(win, dtype=np.float64)[wpos - win_pos0], wpos + pos_offset, rope_dims, rope_base)
+
+
+def _query_output(q_t, p: int, entries, wkeys, sink, scale: float, rope_dims: int, rope_base: float,
+                  pos_offset: int) -> np.ndarray:
+    """Core attention of one query token ([V4-CN] §2.3.1 shared-KV MQA, §2.3.3): the
+    query heads are roped at p, attend to the compressed entries it uses followed by
+    its window keys in one softmax with the sink term, and the result is rotated back
+    by -p."""
+    keys = np.concatenate([entries.reshape(-1, wkeys.shape[1]), wkeys], axis=0)
+    o = _attend_one(rope(q_t, p + pos_offset, rope_dims, rope_base), keys, sink, scale)
+    return rope(o, -(p + pos_offset), rope_dims, rope_base)
+
+
 def csa_layer(streams, istreams, q, q_pos, qI, wI, win, win_pos0, sink, *,
               ratio: int, k: int, n_win: int, scale: float, rope_dims: int,
               rope_base: float, pos_offset: int = 0, dtype: str = "f32"):
-    """One CSA layer forward of one sequence from token 0 (prefill of the whole context).
+    """One CSA layer forward of one sequence whose tokens start at position 0.
 
+    From the definitions of [V4-CN] §2.3.1 and §2.3.3:
+    * the compressed KV entries are the overlapped compression of the KV streams,
+      with partial RoPE at each entry's position; the compressed indexer keys are the
+      same compression of the indexer streams, without RoPE;
+    * query t's index scores cover the entries it may see (earlier complete blocks),
+      and its selected set is the top-k of those scores;
+    * query t attends to its selected entries followed by its window's raw tokens,
+      in one softmax with the sink term, and its output is rotated back by -t.
     streams = (Ca, Cb, Za, Zb) [T, D]; istreams = indexer-key streams [T, DI].
     Stage outputs are rounded to ``dtype`` where the device stores them
     (compressed KV, compressed indexer keys, final output).
@@ -286,18 +320,35 @@ def csa_layer(streams, istreams, q, q_pos, qI, wI, win, win_pos0, sink, *,
     ik = store(compress(ICa, ICb, IZa, IZb, ratio=ratio, overlap=True), dtype)
     scores = index_scores(qI, wI, ik, q_pos, ratio)
     idx, cnt = topk(scores, k)
-    out = mqa(q, q_pos, kv, idx, win, win_pos0, n_win, sink, scale=scale,
-              rope_dims=rope_dims, rope_base=rope_base, pos_offset=pos_offset)
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros(q.shape)
+    for t in range(q.shape[0]):
+        p = int(q_pos[t])
+        chosen = idx[t, :cnt[t]]
+        wkeys = _window_keys(win, win_pos0, p, n_win, pos_offset, rope_dims, rope_base)
+        out[t] = _query_output(q[t], p, kv[chosen], wkeys, sink, scale, rope_dims, rope_base, pos_offset)
     return dict(kv=kv, ik=ik, scores=scores, idx=idx, count=cnt, out=store(out, dtype))
 
 
 def hca_layer(streams, q, q_pos, win, win_pos0, sink, *, ratio: int, n_win: int,
               scale: float, rope_dims: int, rope_base: float, pos_offset: int = 0,
               dtype: str = "f32"):
-    """One HCA layer forward of one sequence from token 0.  streams = (C, Z) [T, D]."""
+    """One HCA layer forward of one sequence whose tokens start at position 0.
+
+    From [V4-CN] §2.3.2 and §2.3.3: the entries are the non-overlapping compression of
+    the streams (C, Z) [T, D] over blocks of ``ratio`` tokens, with partial RoPE at each
+    entry's position; query t attends to every entry it may see (earlier complete
+    blocks) followed by its window's raw tokens, in one softmax with the sink term,
+    and its output is rotated back by -t.
+    """
     C, Z = streams
     kv = store(compress(C, None, Z, None, ratio=ratio, overlap=False, rope_dims=rope_dims,
                         rope_base=rope_base, pos_offset=pos_offset), dtype)
-    out = hca_dense(q, q_pos, kv, win, win_pos0, n_win, sink, ratio=ratio, scale=scale,
-                    rope_dims=rope_dims, rope_base=rope_base, pos_offset=pos_offset)
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros(q.shape)
+    for t in range(q.shape[0]):
+        p = int(q_pos[t])
+        visible = kv[:visible_count(p, ratio, kv.shape[0])]
+        wkeys = _window_keys(win, win_pos0, p, n_win, pos_offset, rope_dims, rope_base)
+        out[t] = _query_output(q[t], p, visible, wkeys, sink, scale, rope_dims, rope_base, pos_offset)
     return dict(kv=kv, out=store(out, dtype))

@@ -387,3 +387,145 @@ def test_visible_set_sizes_printed_on_the_pages():
     assert O.visible_count(n, g["m"], 10 ** 9) == g["csa_candidates"]
     assert O.visible_count(n, g["m_prime"], 10 ** 9) == g["hca_entries"]
     assert min(g["topk"], O.visible_count(n, g["m"], 10 ** 9)) + g["n_win"] == g["csa_visible"]
+
+
+# ------------------------------------------------------------------ HCA layer pins
+
+
+def _hca_inputs(seed, T=48, D=12, H=3, Tq=5):
+    r = rng(seed)
+    C_ = r.standard_normal((T, D))
+    Z = r.standard_normal((T, D))
+    q = r.standard_normal((Tq, H, D)) / math.sqrt(D)
+    win = r.standard_normal((T, D))
+    sink = r.standard_normal(H)
+    pos = np.array([3, 17, 30, 41, T - 1])[:Tq]
+    return (C_, Z), q, pos, win, sink
+
+
+def test_hca_layer_shift_invariance():
+    # every key and the query carry RoPE at their own position, so a uniform shift of
+    # the positions leaves the output unchanged; entries left un-roped would break this
+    streams, q, pos, win, sink = _hca_inputs(40)
+    kw = dict(ratio=8, n_win=6, scale=0.7, rope_dims=8, rope_base=RB, dtype="f32")
+    a = O.hca_layer(streams, q, pos, win, 0, sink, pos_offset=0, **kw)
+    b = O.hca_layer(streams, q, pos, win, 0, sink, pos_offset=98765, **kw)
+    assert np.allclose(a["out"], b["out"], rtol=1e-5, atol=1e-7)
+    c = O.hca_layer(streams, q, pos, win, 0, sink, pos_offset=0, ratio=8, n_win=6, scale=0.7, rope_dims=0,
+                    rope_base=RB, dtype="f32")
+    assert not np.allclose(a["out"], c["out"], atol=1e-3)   # the RoPE dims do matter here
+
+
+def test_hca_layer_constant_stream_reproduces_constant():
+    # weights sum to 1 in the compressor and in the attention: a constant C and a
+    # constant window give that constant at every query and head (no RoPE, no sink term)
+    streams, q, pos, win, _ = _hca_inputs(41)
+    c = rng(5).standard_normal(12)
+    Cc = np.tile(c, (48, 1))
+    out = O.hca_layer((Cc, streams[1]), q, pos, np.tile(c, (48, 1)), 0, np.full(3, -np.inf), ratio=8, n_win=6,
+                      scale=1.3, rope_dims=0, rope_base=RB, dtype="f32")
+    assert np.allclose(out["kv"], np.tile(c, (6, 1)), rtol=1e-6)
+    assert np.allclose(out["out"], np.tile(c, (5, 3, 1)), rtol=1e-6)
+
+
+def test_hca_layer_bf16_storage_points():
+    # with bf16 storage, the cached entries and the output are bf16 values (the device
+    # stores both), and they differ from the fp32-stored run by at most a few bf16 steps
+    streams, q, pos, win, sink = _hca_inputs(42)
+    kw = dict(ratio=8, n_win=6, scale=1.0, rope_dims=8, rope_base=RB)
+    a = O.hca_layer(streams, q, pos, win, 0, sink, dtype="bf16", **kw)
+    b = O.hca_layer(streams, q, pos, win, 0, sink, dtype="f32", **kw)
+    for x in (a["kv"], a["out"]):
+        bits = np.asarray(x, dtype=np.float32).view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0), "values are not bf16-representable"
+    assert not np.array_equal(a["kv"], b["kv"])
+    assert np.allclose(a["kv"], b["kv"], rtol=2 ** -8, atol=0)
+    assert np.allclose(a["out"], b["out"], rtol=2e-2, atol=2e-2)
+
+
+def _scalar_rope(v, p, R, base):
+    v = [float(x) for x in v]
+    D = len(v)
+    for j in range(R // 2):
+        a = p * base ** (-2.0 * j / R)
+        x0, x1 = v[D - R + 2 * j], v[D - R + 2 * j + 1]
+        v[D - R + 2 * j] = x0 * math.cos(a) - x1 * math.sin(a)
+        v[D - R + 2 * j + 1] = x0 * math.sin(a) + x1 * math.cos(a)
+    return v
+
+
+def _scalar_attend(qv, keys, sink, scale):
+    z = [scale * sum(a * b for a, b in zip(qv, k)) for k in keys]
+    M = max(z + [sink])
+    e = [math.exp(x - M) for x in z]
+    den = sum(e) + math.exp(sink - M)
+    return [sum(e[j] * keys[j][d] for j in range(len(keys))) / den for d in range(len(qv))]
+
+
+def test_hca_layer_scalar_brute_force():
+    # the whole layer written with scalar loops: per-channel softmax over each block's
+    # rows, entry i roped at ratio*i, query t sees entries i < t // ratio and the raw
+    # tokens t-n_win+1 .. t (roped at their positions), one softmax with the sink,
+    # output rotated back by -t
+    (C_, Z), q, pos, win, sink = _hca_inputs(43, T=32, D=8, H=2, Tq=4)
+    pos = np.array([0, 7, 20, 31])
+    ratio, n_win, R, scale = 4, 5, 4, 0.9
+    T, D = C_.shape
+    ents = []
+    for i in range(T // ratio):
+        e = []
+        for d in range(D):
+            lg = [Z[ratio * i + j, d] for j in range(ratio)]
+            mx = max(lg)
+            w = [math.exp(x - mx) for x in lg]
+            e.append(sum(w[j] * C_[ratio * i + j, d] for j in range(ratio)) / sum(w))
+        ents.append(_scalar_rope(e, ratio * i, R, RB))
+    want = np.zeros(q.shape)
+    for t, p in enumerate(pos):
+        keys = ents[:p // ratio] + [_scalar_rope(win[r], r, R, RB) for r in range(max(0, p - n_win + 1), p + 1)]
+        for h in range(q.shape[1]):
+            o = _scalar_attend(_scalar_rope(q[t, h], p, R, RB), keys, sink[h], scale)
+            want[t, h] = _scalar_rope(o, -p, R, RB)
+    got = O.hca_layer((C_, Z), q, pos, win, 0, sink, ratio=ratio, n_win=n_win, scale=scale, rope_dims=R,
+                      rope_base=RB, dtype="f32")
+    assert np.allclose(got["kv"], O.store(np.array(ents), "f32"), rtol=1e-6, atol=1e-7)
+    assert np.allclose(got["out"], O.store(want, "f32"), rtol=1e-6, atol=1e-7)
+
+
+def test_csa_layer_scalar_brute_force():
+    # the CSA layer with scalar loops: overlapped compression (entry 0 without a
+    # previous block), scores over earlier blocks, top-k by sorting (ties to the lower
+    # index), attention over the selection and the window with the sink
+    streams, istreams, q, pos, qI, wI, win, sink = _layer_inputs(44, T=32, D=8, DI=4, H=2, HI=2, Tq=4)
+    pos = np.array([2, 9, 22, 31])
+    ratio, k, n_win, R, scale = 4, 3, 5, 4, 0.8
+    T = 32
+
+    def comp(Ca, Cb, Za, Zb, rope_R):
+        out = []
+        for i in range(T // ratio):
+            e = []
+            for d in range(Ca.shape[1]):
+                rows = [(Za[ratio * i + j, d], Ca[ratio * i + j, d]) for j in range(ratio)]
+                if i > 0:
+                    rows += [(Zb[ratio * (i - 1) + j, d], Cb[ratio * (i - 1) + j, d]) for j in range(ratio)]
+                mx = max(z for z, _ in rows)
+                w = [math.exp(z - mx) for z, _ in rows]
+                e.append(sum(wi * c for wi, (_, c) in zip(w, rows)) / sum(w))
+            out.append(_scalar_rope(e, ratio * i, rope_R, RB) if rope_R else e)
+        return out
+    kv = comp(*streams, R)
+    ik = comp(*istreams, 0)
+    want = np.zeros(q.shape)
+    for t, p in enumerate(pos):
+        vis = p // ratio
+        sc = [sum(wI[t, h] * max(0.0, sum(a * b for a, b in zip(qI[t, h], ik[s]))) for h in range(2))
+              for s in range(vis)]
+        chosen = sorted(sorted(range(vis), key=lambda s: (-sc[s], s))[:k])
+        keys = [kv[s] for s in chosen] + [_scalar_rope(win[r], r, R, RB) for r in range(max(0, p - n_win + 1), p + 1)]
+        for h in range(2):
+            o = _scalar_attend(_scalar_rope(q[t, h], p, R, RB), keys, sink[h], scale)
+            want[t, h] = _scalar_rope(o, -p, R, RB)
+    got = O.csa_layer(streams, istreams, q, pos, qI, wI, win, 0, sink, ratio=ratio, k=k, n_win=n_win, scale=scale,
+                      rope_dims=R, rope_base=RB, dtype="f32")
+    assert np.allclose(got["out"], O.store(want, "f32"), rtol=1e-6, atol=1e-7)

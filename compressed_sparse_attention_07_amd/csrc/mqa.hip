@@ -1222,6 +1222,11 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
   Plan p{mfma, 0, 1, 0};
   if (!mfma) return p;
   int hpw = dma ? head_group(H, kDmaMaxWaves) : base_hpw(H, D);
+  if (hpw <= 0 || H % hpw != 0) {
+    // no head group of an instantiated size: the SIMT kernel, which needs no workspace
+    p.mfma = false;
+    return p;
+  }
   if (B * Tq == 0) {
     p.hpw = hpw;
     p.sps = kKT;
@@ -1344,6 +1349,7 @@ bool attn_uses_mfma(const AttnLaunch& L) { return mfma_ok(L); }
 
 size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool sparse) {
   // the larger of the two MFMA kernels' needs (which one runs depends on the cache dtype)
+  if (H < 1 || D < 1) return 0;
   int64_t ns = make_plan(B, Tq, H, D, max_slots, true, sparse, false).nsplit;
   if (D == 512) ns = std::max<int64_t>(ns, make_plan(B, Tq, H, D, max_slots, true, sparse, true).nsplit);
   if (ns <= 1) return 0;
@@ -1354,9 +1360,9 @@ size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slo
 int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int64_t tokens = L.B * L.Tq;
   if (tokens == 0) return 0;
-  const bool mfma = mfma_ok(L);
-  const bool dma = mfma && dma_ok(L);
-  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma, L.sparse != 0, dma);
+  const bool dma = mfma_ok(L) && dma_ok(L);
+  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma_ok(L), L.sparse != 0, dma);
+  const bool mfma = P.mfma;
   if (mfma && P.nsplit > 1 && ws_bytes < attn_workspace_bytes(L.B, L.Tq, L.H, L.D, max_slots_of(L), L.sparse != 0))
     return -3;
   AttnArgs a = make_args(L, P, ws);

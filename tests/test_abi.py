@@ -140,3 +140,22 @@ def test_workspace_sizes_with_no_query_tokens(L):
     assert L.csa_forward_workspace_size(C.byref(d)) >= 0
     d.Tq = 1
     assert L.csa_forward_workspace_size(C.byref(d)) > 0
+
+
+@pytest.mark.parametrize("H,D", [(80, 512), (72, 512), (112, 512), (144, 128), (176, 128), (200, 128),
+                                 (48, 256), (240, 512), (17, 64)])
+def test_head_counts_without_an_mfma_head_group(L, H, D):
+    """Head counts the MFMA kernels cannot split into instantiated head groups take the
+    SIMT kernel: every size query answers (0 bytes: that kernel needs no workspace)
+    and a forward call returns a status instead of failing inside the planner."""
+    from compressed_sparse_attention_07_amd import layer_desc
+    from compressed_sparse_attention_07_amd._lib import csa_forward_io
+    assert L.csa_sparse_mqa_workspace_size(16, 1, H, D, 1024, 128) >= 0
+    assert L.hca_dense_attn_workspace_size(32, 1, H, D, 8192, 128) >= 0
+    for mode in (0, 1):
+        d = layer_desc(mode=mode, B=16, T=0, t0=4096, Tq=1, cache_rows=1024 if mode == 0 else 32, Tw=128, D=D, H=H,
+                       HI=64, DI=128, ratio=4 if mode == 0 else 128, topk=512, n_win=128, rope_dims=64 if D >= 64
+                       else 0, rope_base=10000.0, softmax_scale=1.0, stream_dtype=1)
+        assert L.csa_forward_workspace_size(C.byref(d)) >= 0
+        io = csa_forward_io()
+        assert L.csa_forward(C.byref(d), C.byref(io), None, 0, None) != 0

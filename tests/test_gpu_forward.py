@@ -2,11 +2,15 @@
 the HCA chain) against the oracle's whole-layer functions.
 
 The oracle runs its own pipeline from the same inputs.  Top-k sets must agree
-except for entries whose oracle score lies within the near-tie band of the k-th
-score: 1e-4 relative in fp32; in bf16 the band also covers the largest score
-change one bf16 rounding step of a compressed key can cause (2^-8 relative per key
-element, summed with the head weights).  Outputs are compared on every query
-whose selected set is identical.
+except for entries whose oracle score lies within 1e-4 (relative) of the k-th
+score.  In fp32 the oracle scores its own compressed keys.  In bf16 the stored keys
+of the two sides may differ by one bf16 rounding step (the compressors accumulate
+in fp32 and fp64), which moves scores by up to ~2^-8 relative, far beyond the 1e-4
+band; there the oracle scores the keys the GPU stored (themselves checked against
+the oracle's compression within the bf16 tolerance), as each stage's oracle input
+is the tensor that GPU stage consumed.  Every query's output is checked: against
+the oracle layer where the selected sets are identical, and against the oracle's
+attention over the GPU's own selection where a near tie made them differ.
 """
 
 import sys
@@ -72,7 +76,7 @@ def _run_forward(dtype, B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, scale, seed)
                 out=out, scores=scores, idx=idx)
 
 
-def _check_layer(r, b, dtype, k, ratio, n_win, R, scale, band_fn=None):
+def _check_layer(r, b, dtype, k, ratio, n_win, R, scale):
     want = O.csa_layer([f64(s[b]) for s in r["streams"]], [f64(s[b]) for s in r["istreams"]], f64(r["q"][b]),
                        r["pos"][b].cpu().numpy(), f64(r["qI"][b]), f64(r["wI"][b]), f64(r["win"][b]), 0,
                        f64(r["sink"]), ratio=ratio, k=k, n_win=n_win, scale=scale, rope_dims=R, rope_base=10000.0,
@@ -80,23 +84,32 @@ def _check_layer(r, b, dtype, k, ratio, n_win, R, scale, band_fn=None):
     kind = "f32" if dtype == "f32" else "bf16"
     assert_close(f64(r["kv"].data[b]), want["kv"], kind, "compressed KV")
     assert_close(f64(r["ik"].data[b]), want["ik"], kind, "compressed indexer keys")
-    gs = r["scores"][b].cpu().numpy().astype(np.float64)
-    assert np.array_equal(np.isneginf(gs), np.isneginf(want["scores"]))
-    fin = np.isfinite(want["scores"])
+    pos = r["pos"][b].cpu().numpy()
     if dtype == "f32":
-        assert_close(gs[fin], want["scores"][fin], "f32", "scores")
+        ref_scores = want["scores"]
+    else:
+        ref_scores = O.index_scores(f64(r["qI"][b]), f64(r["wI"][b]), f64(r["ik"].data[b]), pos, ratio)
+    gs = r["scores"][b].cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(gs), np.isneginf(ref_scores))
+    fin = np.isfinite(ref_scores)
+    assert_close(gs[fin], ref_scores[fin], "f32", "scores")
     gi = r["idx"][b].cpu().numpy()
-    exact_rows = []
+    got_out = f64(r["out"][b])
+    n_exact = 0
     for t in range(gi.shape[0]):
         cnt = int((gi[t] >= 0).sum())
-        band_abs = band_fn(b, t) if band_fn else None
-        ok, exact = topk_sets_agree(gi[t], cnt, want["scores"][t], k, band_abs=band_abs)
+        ok, exact = topk_sets_agree(gi[t], cnt, ref_scores[t], k)
         assert ok, f"top-k set of query {t} differs beyond the near-tie band"
-        if exact:
-            exact_rows.append(t)
-    assert len(exact_rows) >= 0.9 * gi.shape[0], len(exact_rows)
-    rows = np.array(exact_rows)
-    assert_close(f64(r["out"][b])[rows], want["out"][rows], kind, "output")
+        n_exact += exact
+        ref_idx = want["idx"][t] if dtype == "f32" else O.topk(ref_scores[t:t + 1], k)[0][0]
+        if np.array_equal(gi[t], ref_idx) and dtype == "f32":
+            wt = want["out"][t]
+        else:
+            # the oracle's attention over the GPU's own selection (and the oracle's cache)
+            wt = O.store(O.mqa(f64(r["q"][b, t:t + 1]), pos[t:t + 1], want["kv"], gi[t:t + 1], f64(r["win"][b]), 0,
+                               n_win, f64(r["sink"]), scale=scale, rope_dims=R, rope_base=10000.0)[0], dtype)
+        assert_close(got_out[t], wt, kind, f"output of query {t}")
+    say(f"  sequence {b}: {n_exact} of {gi.shape[0]} selections identical, every output checked")
 
 
 def test_forward_config0_fp32_full():
@@ -110,15 +123,8 @@ def test_forward_bf16_mfma_paths():
     say("forward bf16 small (MFMA indexer + attention)")
     B, T, D, DI, H, HI, Tq, k, ratio, n_win, R = 2, 512, 128, 32, 16, 16, 24, 16, 4, 32, 64
     r = _run_forward("bf16", B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, 1.0, 1234)
-
-    def band(b, t):
-        # one bf16 step of every key element, weighted by |q| and w, bounds the score change
-        qI, wI = f64(r["qI"][b, t]), f64(r["wI"][b, t])
-        keys = np.abs(f64(r["ik"].data[b]))
-        return 2.0 ** -8 * float((wI[:, None] * (np.abs(qI) @ keys.T)).sum(0).max())
-
     for b in range(B):
-        _check_layer(r, b, "bf16", k, ratio, n_win, R, 1.0, band_fn=band)
+        _check_layer(r, b, "bf16", k, ratio, n_win, R, 1.0)
 
 
 def test_forward_chunked_compression_matches_whole():

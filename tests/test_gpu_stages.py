@@ -172,8 +172,24 @@ INDEX_CASES = [
 ]
 
 
+# every instantiated indexer kernel shape: decode (stream / direct-load kernels, and the
+# SIMT kernel past them), 16+ queries (prefill kernel) and MXFP4 (scaled fp4 MFMA)
+INDEX_VARIANTS = ([(1, 3, hi, di, 300, 4, "bf16") for hi in (16, 32, 64, 128) for di in (32, 64, 128, 256)] +
+                  [(1, 20, hi, di, 300, 4, "bf16") for hi in (16, 32, 64, 128) for di in (64, 128)] +
+                  [(1, 3, hi, di, 300, 4, "mxfp4") for hi in (16, 32, 64, 128) for di in (128, 256)])
+
+
 @pytest.mark.parametrize("case", INDEX_CASES, ids=lambda c: "-".join(str(x) for x in c))
 def test_index_scores(case):
+    _index_case(case)
+
+
+@pytest.mark.parametrize("case", INDEX_VARIANTS, ids=lambda c: "-".join(str(x) for x in c))
+def test_index_scores_kernel_variants(case):
+    _index_case(case)
+
+
+def _index_case(case):
     B, Tq, HI, DI, N, ratio, dt = case
     say(f"index_scores {case}")
     g = Gen(21 + N, DEV)
@@ -352,6 +368,17 @@ ATTN_CASES = [
     (1, 2, 32, 512, 3000, 2040, 128, "bf16", "bf16", 64, 1.0, [9000, 12100]),
     # window clipped at position 0, fewer selected entries than one tile
     (2, 1, 128, 512, 40, 30, 128, "bf16", "bf16", 64, 1.0, [60]),
+    # every other instantiated kernel shape: LDS-DMA with 2 waves on the pipelined loop
+    # (prefill), register-staged FP8MIX with 1 and 2 waves, D = 128 / 256 with 1-8 waves
+    (1, 260, 32, 512, 400, 64, 128, "bf16", "bf16", 64, 1.0 / math.sqrt(512), list(range(1600, 1860))),
+    (1, 2, 16, 512, 300, 96, 128, "bf16", "fp8mix", 64, 1.0, [1300, 5000]),
+    (1, 2, 32, 512, 300, 96, 128, "bf16", "fp8mix", 64, 1.0, [1300, 5000]),
+    (1, 256, 32, 128, 300, 40, 64, "bf16", "bf16", 64, 1.0, list(range(1400, 1656))),
+    (1, 256, 64, 128, 300, 40, 64, "bf16", "bf16", 64, 1.0, list(range(1400, 1656))),
+    (1, 256, 128, 128, 300, 40, 64, "bf16", "bf16", 64, 1.0, list(range(1400, 1656))),
+    (1, 2, 16, 256, 300, 70, 64, "bf16", "bf16", 64, 1.0, [1300, 2000]),
+    (1, 256, 64, 256, 300, 40, 64, "bf16", "bf16", 64, 1.0, list(range(1400, 1656))),
+    (1, 256, 128, 256, 300, 40, 64, "bf16", "bf16", 64, 1.0, list(range(1400, 1656))),
 ]
 
 

@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(PKG, "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_FP8MIX, CSA_MXFP4 = 0, 1, 2, 3
 CSA_MODE_CSA, CSA_MODE_HCA = 0, 1
+CSA_FLAG_BF16_SCORES = 1
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_DTYPE",
           4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_DEVICE", 6: "CSA_ERR_UNSUPPORTED"}
 
 EXPORTS = ["csa_abi_version", "csa_last_error", "csa_device_check", "csa_compress", "csa_quantize",
-           "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_sparse_mqa_workspace_size",
+           "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_mqa_workspace_size",
            "csa_sparse_mqa", "hca_dense_attn_workspace_size", "hca_dense_attn",
            "csa_forward_workspace_size", "csa_forward"]
 
@@ -45,7 +46,7 @@ class csa_layer_desc(C.Structure):
                 ("D", C.c_int32), ("H", C.c_int32), ("HI", C.c_int32), ("DI", C.c_int32),
                 ("ratio", C.c_int32), ("topk", C.c_int32), ("n_win", C.c_int32), ("rope_dims", C.c_int32),
                 ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("pos_offset", C.c_int64),
-                ("stream_dtype", C.c_int32), ("pad0", C.c_int32)]
+                ("stream_dtype", C.c_int32), ("flags", C.c_int32)]
 
 
 class csa_forward_io(C.Structure):
@@ -80,6 +81,9 @@ def lib():
         L.csa_topk_workspace_size.argtypes = [i64, i64, i32]
         L.csa_topk_workspace_size.restype = sz
         L.csa_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.csa_index_topk_workspace_size.argtypes = [i64, i64, i32, i32, i64, i32, i32, i32]
+        L.csa_index_topk_workspace_size.restype = sz
+        L.csa_index_topk.argtypes = [bp, vp, bp, vp, i64, i64, i32, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.csa_sparse_mqa_workspace_size.argtypes = [i64, i64, i32, i32, i32, i32]
         L.csa_sparse_mqa_workspace_size.restype = sz
         L.csa_sparse_mqa.argtypes = [bp, vp, bp, i64, vp, i32, bp, vp, i64, vp, f32, i32, f32, i64, i64, i64, i32,
@@ -92,7 +96,7 @@ def lib():
         L.csa_forward_workspace_size.restype = sz
         L.csa_forward.argtypes = [C.POINTER(csa_layer_desc), C.POINTER(csa_forward_io), vp, sz, vp]
         for name in EXPORTS:
-            if name not in ("csa_topk_workspace_size", "csa_sparse_mqa_workspace_size",
+            if name not in ("csa_topk_workspace_size", "csa_sparse_mqa_workspace_size", "csa_index_topk_workspace_size",
                             "hca_dense_attn_workspace_size", "csa_forward_workspace_size",
                             "csa_last_error", "csa_abi_version"):
                 getattr(L, name).restype = C.c_int
@@ -232,6 +236,18 @@ def csa_topk(scores, k: int, idx, count=None, *, ws=None, stream=None) -> None:
     need = lib().csa_topk_workspace_size(rows, N, k)
     w, wb = _ws(need, scores.device, ws)
     _invoke("csa_topk", ptr(scores), rows, N, k, ptr(idx), ptr(count), ptr(w), wb, stream_handle(stream), keep=(w,))
+
+
+def csa_index_topk(qI, wI, kI, q_pos, k: int, idx, count=None, scores=None, *, N: int, ratio: int, flags: int = 0,
+                   ws=None, stream=None) -> None:
+    qb, kb = Buf.of(qI), Buf.of(kI)
+    B, Tq, HI, DI = qb.shape
+    _, kI_rows, _ = kb.shape
+    need = lib().csa_index_topk_workspace_size(B, Tq, HI, DI, N, k, qb.dtype, flags)
+    w, wbytes = _ws(need, qb.data.device, ws)
+    cq, ck = qb.c(), kb.c()
+    _invoke("csa_index_topk", C.byref(cq), ptr(wI), C.byref(ck), ptr(q_pos), B, Tq, HI, DI, N, kI_rows, ratio, k, flags,
+            ptr(idx), ptr(count), ptr(scores), ptr(w), wbytes, stream_handle(stream), keep=(w,))
 
 
 def csa_sparse_mqa(q, q_pos, kv, idx, win, win_pos0, sink, out, *, N: int, n_win: int, softmax_scale: float,

@@ -5,6 +5,7 @@
 // and launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -195,6 +196,57 @@ csa_status launched(int rc, const char* what) {
   return fail(CSA_ERR_DEVICE, "%s: kernel launch failed (%s)", what, hipGetErrorString(hipGetLastError()));
 }
 
+// Lightning indexer followed by top-k.  Decode-shaped bf16 launches take the selecting
+// indexer (each slice's top-k kept while scoring) and one merge level; everything else
+// scores the rows into the workspace (or the caller's score buffer) and runs csa_topk.
+struct IdxTopkPlan {
+  int sel;       // slices per row of the selecting indexer, 0 for the two-call path
+  size_t bytes;  // workspace
+};
+
+// dtype_known = false (a size query without the operands) sizes for either path
+IdxTopkPlan plan_index_topk(IndexLaunch X, int k, bool have_scores, bool dtype_known) {
+  X.sel_k = k;
+  const size_t rows = static_cast<size_t>(X.B * X.Tq);
+  const int sel = index_select_slices(X);
+  const size_t cand = sel > 0 ? align256(rows * sel * k * (sizeof(float) + sizeof(int32_t))) : 0;
+  const size_t two = (have_scores ? 0 : align256(rows * X.N * sizeof(float))) +
+                     align256(topk_workspace_bytes(X.B * X.Tq, X.N, k));
+  IdxTopkPlan p{};
+  p.sel = dtype_known ? sel : 0;
+  p.bytes = !dtype_known ? std::max(cand, two) : (sel > 0 ? cand : two);
+  return p;
+}
+
+int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int32_t* count, float* scores_out,
+                   char* w, hipStream_t s, const char** stage) {
+  X.sel_k = k;
+  const int64_t rows = X.B * X.Tq;
+  if (rows == 0 || X.N == 0) {
+    // nothing to score: every selection is empty (idx all -1, counts 0)
+    *stage = "topk";
+    return launch_topk(nullptr, rows, 0, k, idx, count, nullptr, s);
+  }
+  if (P.sel > 0) {
+    const size_t nc = static_cast<size_t>(rows) * P.sel * k;
+    X.scores = scores_out;
+    X.sel_val = reinterpret_cast<float*>(w);
+    X.sel_idx = reinterpret_cast<int32_t*>(w + nc * sizeof(float));
+    *stage = "index_select";
+    int rc = launch_index_select(X, s);
+    if (rc != 0) return rc;
+    *stage = "topk_merge";
+    return launch_topk_merge(X.sel_val, X.sel_idx, rows, P.sel, k, idx, count, s);
+  }
+  X.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
+  *stage = "index_scores";
+  int rc = launch_index_scores(X, s);
+  if (rc != 0) return rc;
+  *stage = "topk";
+  void* tws = w + (scores_out ? 0 : align256(static_cast<size_t>(rows * X.N) * sizeof(float)));
+  return launch_topk(X.scores, rows, X.N, k, idx, count, tws, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +347,63 @@ csa_status csa_index_scores(const csa_buf* qI, const float* wI, const csa_buf* k
 
 size_t csa_topk_workspace_size(int64_t rows, int64_t N, int32_t k) { return topk_workspace_bytes(rows, N, k); }
 
+size_t csa_index_topk_workspace_size(int64_t B, int64_t Tq, int32_t HI, int32_t DI, int64_t N, int32_t k,
+                                     int32_t qI_dtype, int32_t flags) {
+  if (B < 0 || Tq < 0 || N < 0 || HI < 1 || DI < 1 || k < 1) return 0;
+  IndexLaunch X{};
+  X.qI.dtype = X.kI.dtype = qI_dtype;
+  X.B = B;
+  X.Tq = Tq;
+  X.N = N;
+  X.HI = HI;
+  X.DI = DI;
+  X.score_bf16 = (flags & CSA_FLAG_BF16_SCORES) ? 1 : 0;
+  return plan_index_topk(X, k, false, true).bytes;
+}
+
+csa_status csa_index_topk(const csa_buf* qI, const float* wI, const csa_buf* kI, const int64_t* q_pos, int64_t B,
+                          int64_t Tq, int32_t HI, int32_t DI, int64_t N, int64_t kI_rows, int32_t ratio, int32_t k,
+                          int32_t flags, int32_t* idx, int32_t* count, float* scores, void* ws, size_t ws_bytes,
+                          void* stream) {
+  CSA_TRY(check_buf(qI, "qI"));
+  CSA_TRY(check_buf(kI, "kI"));
+  if (!wI || !q_pos || !idx) return fail(CSA_ERR_NULL, "wI, q_pos and idx are required");
+  if (qI->dtype != kI->dtype) return fail(CSA_ERR_DTYPE, "qI and kI must share a dtype");
+  if (qI->dtype == CSA_FP8MIX) return fail(CSA_ERR_DTYPE, "the indexer takes F32, BF16 or MXFP4");
+  if (HI < 1 || HI > 128) return fail(CSA_ERR_SHAPE, "HI=%d out of [1, 128]", HI);
+  if (DI < 8 || DI > 512 || DI % 8) return fail(CSA_ERR_SHAPE, "DI=%d must be a multiple of 8 in [8, 512]", DI);
+  if (qI->dtype == CSA_MXFP4 && DI % 32) return fail(CSA_ERR_SHAPE, "MXFP4 needs DI %% 32 == 0");
+  if (!aligned16(qI->data) || !aligned16(kI->data)) return fail(CSA_ERR_SHAPE, "qI and kI must be 16-byte aligned");
+  if (qI->dtype == CSA_MXFP4 && ((reinterpret_cast<uintptr_t>(qI->scale) | reinterpret_cast<uintptr_t>(kI->scale)) & 3))
+    return fail(CSA_ERR_SHAPE, "MXFP4 scale planes must be 4-byte aligned");
+  if (B < 0 || Tq < 0 || N < 0 || N >= (static_cast<int64_t>(1) << 31)) return fail(CSA_ERR_SHAPE, "sizes out of range");
+  if (kI_rows < N) return fail(CSA_ERR_SHAPE, "kI_rows < N");
+  if (ratio < 1) return fail(CSA_ERR_SHAPE, "ratio must be >= 1");
+  if (k < 1 || k > 4096) return fail(CSA_ERR_SHAPE, "k=%d out of [1, 4096]", k);
+  if (flags & ~CSA_FLAG_BF16_SCORES) return fail(CSA_ERR_SHAPE, "unknown flags 0x%x", flags);
+  IndexLaunch X{};
+  X.qI = *qI;
+  X.wI = wI;
+  X.kI = *kI;
+  X.q_pos = q_pos;
+  X.B = B;
+  X.Tq = Tq;
+  X.N = N;
+  X.kI_rows = kI_rows;
+  X.HI = HI;
+  X.DI = DI;
+  X.ratio = ratio;
+  X.score_bf16 = (flags & CSA_FLAG_BF16_SCORES) ? 1 : 0;
+  const IdxTopkPlan P = plan_index_topk(X, k, scores != nullptr, true);
+  if (P.bytes > 0 && (!ws || ws_bytes < P.bytes))
+    return fail(CSA_ERR_WORKSPACE, "csa_index_topk needs %zu workspace bytes, got %zu", P.bytes, ws_bytes);
+  CSA_TRY(check_device());
+  const char* stage = "";
+  const int rc = run_index_topk(X, k, P, idx, count, scores, static_cast<char*>(ws), static_cast<hipStream_t>(stream),
+                                &stage);
+  return launched(rc, stage);
+}
+
 csa_status csa_topk(const float* scores, int64_t rows, int64_t N, int32_t k, int32_t* idx, int32_t* count, void* ws,
                     size_t ws_bytes, void* stream) {
   if (!idx || (!scores && rows > 0 && N > 0)) return fail(CSA_ERR_NULL, "scores and idx are required");
@@ -355,23 +464,39 @@ namespace {
 
 struct FwdPlan {
   int64_t N;
-  size_t scores_off, scores_bytes, idx_off, idx_bytes, topk_off, topk_bytes, attn_off, attn_bytes, total;
+  IdxTopkPlan it;  // CSA: indexer + top-k
+  size_t scores_off, idx_off, idx_bytes, attn_off, attn_bytes, total;
 };
 
-FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx) {
+// The indexer launch of a forward (device pointers are filled in by csa_forward)
+IndexLaunch index_launch(const csa_layer_desc* L, int32_t qI_dtype) {
+  IndexLaunch X{};
+  X.qI.dtype = qI_dtype;
+  X.kI.dtype = qI_dtype;
+  X.B = L->B;
+  X.Tq = L->Tq;
+  X.N = (L->t0 + L->T) / L->ratio;
+  X.kI_rows = L->cache_rows;
+  X.HI = L->HI;
+  X.DI = L->DI;
+  X.ratio = L->ratio;
+  X.score_bf16 = (L->flags & CSA_FLAG_BF16_SCORES) ? 1 : 0;
+  return X;
+}
+
+// qI_dtype: the indexer's operand format (the plan depends on it); -1 for a size query
+// without the operands, which covers either plan
+FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx, int32_t qI_dtype) {
   FwdPlan p{};
   p.N = (L->t0 + L->T) / L->ratio;
   size_t off = 0;
   if (L->mode == CSA_MODE_CSA) {
-    p.scores_bytes = have_scores ? 0 : align256(static_cast<size_t>(L->B * L->Tq * p.N) * sizeof(float));
+    p.it = plan_index_topk(index_launch(L, qI_dtype < 0 ? CSA_BF16 : qI_dtype), L->topk, have_scores, qI_dtype >= 0);
     p.scores_off = off;
-    off += p.scores_bytes;
+    off += p.it.bytes;
     p.idx_bytes = have_idx ? 0 : align256(static_cast<size_t>(L->B * L->Tq * L->topk) * sizeof(int32_t));
     p.idx_off = off;
     off += p.idx_bytes;
-    p.topk_bytes = align256(topk_workspace_bytes(L->B * L->Tq, p.N, L->topk));
-    p.topk_off = off;
-    off += p.topk_bytes;
     p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, static_cast<int64_t>(L->topk) + L->n_win, true));
   } else {
     p.attn_bytes = align256(attn_workspace_bytes(L->B, L->Tq, L->H, L->D, p.N + L->n_win, false));
@@ -392,6 +517,7 @@ csa_status validate_desc(const csa_layer_desc* L) {
   if (L->T % L->ratio || L->t0 % L->ratio) return fail(CSA_ERR_SHAPE, "T and t0 must be multiples of ratio");
   if (L->cache_rows < (L->t0 + L->T) / L->ratio) return fail(CSA_ERR_SHAPE, "cache_rows < (t0+T)/ratio");
   if (L->mode == CSA_MODE_CSA && (L->topk < 1 || L->topk > 4096)) return fail(CSA_ERR_SHAPE, "topk out of [1, 4096]");
+  if (L->flags & ~CSA_FLAG_BF16_SCORES) return fail(CSA_ERR_SHAPE, "unknown flags 0x%x", L->flags);
   return CSA_OK;
 }
 
@@ -399,7 +525,7 @@ csa_status validate_desc(const csa_layer_desc* L) {
 
 size_t csa_forward_workspace_size(const csa_layer_desc* L) {
   if (validate_desc(L) != CSA_OK) return 0;
-  return plan_forward(L, false, false).total;
+  return plan_forward(L, false, false, -1).total;
 }
 
 csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* ws, size_t ws_bytes, void* stream) {
@@ -434,7 +560,8 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
         ((reinterpret_cast<uintptr_t>(io->qI.scale) | reinterpret_cast<uintptr_t>(io->ik_cache.scale)) & 3))
       return fail(CSA_ERR_SHAPE, "MXFP4 scale planes must be 4-byte aligned");
   }
-  const FwdPlan P = plan_forward(L, io->scores_out != nullptr, io->idx_out != nullptr);
+  const FwdPlan P = plan_forward(L, io->scores_out != nullptr, io->idx_out != nullptr,
+                                 csa_mode ? io->qI.dtype : CSA_BF16);
   if (P.total > 0 && (!ws || ws_bytes < P.total))
     return fail(CSA_ERR_WORKSPACE, "csa_forward needs %zu workspace bytes, got %zu", P.total, ws_bytes);
   CSA_TRY(check_device());
@@ -483,25 +610,15 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     }
   }
   if (csa_mode) {
-    float* scores = io->scores_out ? io->scores_out : reinterpret_cast<float*>(w + P.scores_off);
     int32_t* idx = io->idx_out ? io->idx_out : reinterpret_cast<int32_t*>(w + P.idx_off);
-    IndexLaunch X{};
+    IndexLaunch X = index_launch(L, io->qI.dtype);
     X.qI = io->qI;
     X.wI = io->wI;
     X.kI = io->ik_cache;
     X.q_pos = io->q_pos;
-    X.B = L->B;
-    X.Tq = L->Tq;
-    X.N = N;
-    X.kI_rows = L->cache_rows;
-    X.HI = L->HI;
-    X.DI = L->DI;
-    X.ratio = L->ratio;
-    X.scores = scores;
-    int rc = launch_index_scores(X, s);
-    if (rc != 0) return launched(rc, "csa_forward/index_scores");
-    rc = launch_topk(scores, L->B * L->Tq, N, L->topk, idx, nullptr, w + P.topk_off, s);
-    if (rc != 0) return launched(rc, "csa_forward/topk");
+    const char* stage = "";
+    const int rc = run_index_topk(X, L->topk, P.it, idx, nullptr, io->scores_out, w + P.scores_off, s, &stage);
+    if (rc != 0) return launched(rc, stage);
     AttnLaunch A = make_attn(&io->q, io->q_pos, &io->kv_cache, L->cache_rows, 1, idx, L->topk, 1, &io->win, io->win_pos0,
                              L->Tw, io->sink, L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset, L->B, L->Tq,
                              L->H, L->D, N, L->n_win, &io->out);

@@ -33,10 +33,17 @@
 // per thread with the token's queries staged (dequantized) in LDS.
 #include "device_common.h"
 #include "launch.h"
+#include "topk_select.h"
 
 namespace csa {
 
 namespace {
+
+// A score as stored: fp32, or rounded to bf16 (nearest-even) for the BF16-score
+// variant ([V4-CN] §3.4 stores the index scores in BF16 for a faster selection).
+__device__ __forceinline__ float stored_score(const IndexLaunch& a, float v) {
+  return a.score_bf16 ? __uint_as_float(static_cast<uint32_t>(f32_to_bf16(v)) << 16) : v;
+}
 
 // ------------------------------------------------------------------ SIMT path
 
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(kSimtThreads) void index_simt_kernel(IndexLaunch a)
       }
     }
   }
-  if (s < a.N) a.scores[bt * a.N + s] = s < vis ? score : -INFINITY;
+  if (s < a.N) a.scores[bt * a.N + s] = s < vis ? stored_score(a, score) : -INFINITY;
 }
 
 // MXFP4 keys and queries: dequantized element d of row r (codes [., DI/2], scales [., DI/32])
@@ -121,12 +128,14 @@ __global__ __launch_bounds__(kSimtThreads) void index_simt_mxfp4_kernel(IndexLau
       }
     }
   }
-  if (s < a.N) a.scores[bt * a.N + s] = s < vis ? score : -INFINITY;
+  if (s < a.N) a.scores[bt * a.N + s] = s < vis ? stored_score(a, score) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ MFMA path
 
 constexpr int kWavesPerWG = 4;
+constexpr int kSelKeysPerWave = 256;  // entries per wave of the selecting stream kernel
+constexpr int kSelWaves = 8;          // waves per workgroup of the selecting stream kernel
 constexpr int kTiles = 4;  // 16-entry tiles per iteration (64 entries)
 
 template <int HB, int KS>
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
       if (s0 + lane >= vis_end) res = -INFINITY;
     }
     const int64_t s = s0 + lane;
-    if (s < s_end) out[s] = res;
+    if (s < s_end) out[s] = stored_score(a, res);
   };
 
   // two register buffers: the next 64 entries are in flight while the current ones
@@ -247,9 +256,9 @@ __device__ __forceinline__ void wait_stage(int later) {
   }
 }
 
-template <int HB, int KS, int TPS, int NST>
-__global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexLaunch a, int keys_per_wave,
-                                                                          int64_t waves_per_token) {
+template <int HB, int KS, int TPS, int NST, int NWV = kWavesPerWG, bool SEL = false>
+__global__ __launch_bounds__(NWV * WAVE) void index_stream_kernel(IndexLaunch a, int keys_per_wave,
+                                                                  int64_t waves_per_token) {
   constexpr int DI = 32 * KS;
   constexpr int RB = 2 * DI;             // bytes per key row
   constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -260,7 +269,11 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
   static_assert(NST >= 2 && DPS * (NST - 1) < 64, "vmcnt range");
   constexpr int QOPS = HB * KS;          // KiBs of queries: HI x DI bf16
   constexpr int WOPS = (16 * HB + 63) / 64;  // head weights: 64 floats per dword load
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWavesPerWG][NST * STAGE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NWV][NST * STAGE_B];
+  // SEL: the workgroup's slice of the score row stays in LDS and is selected there
+  constexpr int SLICE = SEL ? NWV * kSelKeysPerWave : 1;
+  __shared__ __attribute__((aligned(16))) float sel_sc[SLICE];
+  __shared__ Shared<SEL ? NWV * WAVE : 64> sel_sh;
   __shared__ __attribute__((aligned(16))) uint8_t qsh[QOPS * 1024];
   __shared__ __attribute__((aligned(16))) float wsh[WOPS * 64];
 
@@ -268,8 +281,8 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // fewer than 2^32 waves and tokens (the grid is 32-bit): 32-bit index arithmetic
   const uint32_t wpt = static_cast<uint32_t>(waves_per_token);
-  const uint32_t wave = blockIdx.x * kWavesPerWG + static_cast<uint32_t>(wid);
-  const uint32_t bt32 = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerWG / wpt);  // the workgroup's token
+  const uint32_t wave = blockIdx.x * NWV + static_cast<uint32_t>(wid);
+  const uint32_t bt32 = __builtin_amdgcn_readfirstlane(blockIdx.x * NWV / wpt);  // the workgroup's token
   const int64_t bt = bt32;
   const int64_t b = bt32 / static_cast<uint32_t>(a.Tq);
   const int64_t s_begin = static_cast<int64_t>(wave - bt32 * wpt) * keys_per_wave;
@@ -282,8 +295,8 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
     const uint8_t* q = static_cast<const uint8_t*>(a.qI.data) + uni64(bt * a.HI) * RB;
     const uint32_t q_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(qsh));
 #pragma unroll
-    for (int j = 0; j < (QOPS + kWavesPerWG - 1) / kWavesPerWG; ++j) {
-      const int i = wid + kWavesPerWG * j;
+    for (int j = 0; j < (QOPS + NWV - 1) / NWV; ++j) {
+      const int i = wid + NWV * j;
       if (i >= QOPS) break;
       const int off = i * 1024 + 16 * lane;
       const int row = off / RB;
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
     const uint32_t w_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wsh));
 #pragma unroll
     for (int i = 0; i < WOPS; ++i)
-      if ((QOPS + i) % kWavesPerWG == wid) {  // wave-uniform
+      if ((QOPS + i) % NWV == wid) {  // wave-uniform
         const int e = 64 * i + lane;
         lds_dma4(wr + (e < 16 * HB ? e : 0), w_b + i * 256);  // lanes past HI re-read weight 0
       }
@@ -341,7 +354,14 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
     w[hb][3] = wv.w;
   }
 
-  float* out = a.scores + bt * a.N;
+  float* out = a.scores ? a.scores + bt * a.N : nullptr;
+  // SEL: entry s of the row lands at sel_sc[s - s_slice] (the workgroup's first entry)
+  const int64_t s_slice = SEL ? s_begin - static_cast<int64_t>(wid) * keys_per_wave : 0;
+  auto put = [&](int64_t s, float v) {
+    v = stored_score(a, v);
+    if (SEL) sel_sc[s - s_slice] = v;
+    if (out) out[s] = v;
+  };
   float res = -INFINITY;
   for (int t = 0; t < nst; ++t) {
     wait_stage<DPS, NST - 2>(min(nst - 1 - t, NST - 2));
@@ -371,14 +391,37 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_stream_kernel(IndexL
       if (grp == g) res = sc;
       if (g == 3 || (t == nst - 1 && tI == TPS - 1)) {
         const int64_t s = s_begin + static_cast<int64_t>(tile - g) * 16 + lane;
-        if (s < s_end) out[s] = s < vis_end ? res : -INFINITY;
+        if (s < s_end) put(s, s < vis_end ? res : -INFINITY);
         res = -INFINITY;
       }
     }
   }
   // entries past the visible prefix that no run covered
   const int64_t covered = s_begin + static_cast<int64_t>((nst * TPS + 3) / 4) * 64;
-  for (int64_t s = covered + lane; s < s_end; s += WAVE) out[s] = -INFINITY;
+  for (int64_t s = covered + lane; s < s_end; s += WAVE) put(s, -INFINITY);
+  if constexpr (SEL) {
+    // ---- the slice's top-k as (score, entry) candidates in entry order: thread t holds
+    // entries t, t + NT, ... of the slice (entries past the row are -inf)
+    constexpr int NT = NWV * WAVE;
+    constexpr int PER = SLICE / NT;
+    __syncthreads();
+    const int64_t n_here = a.N - s_slice;
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = j * NT + static_cast<int>(threadIdx.x);
+      const float x = e < n_here ? sel_sc[e] : -INFINITY;
+      v[j] = __builtin_isfinite(x) ? x : -INFINITY;
+    }
+    TopkArgs t{};
+    t.n_in = a.N;
+    t.slice = SLICE;
+    t.slices = static_cast<int>((a.N + SLICE - 1) / SLICE);
+    t.k = a.sel_k;
+    t.out_val = a.sel_val;
+    t.out_idx = a.sel_idx;
+    select_slice<NT, PER, false, false>(t, sel_sh, bt * t.slices + s_slice / SLICE, v);
+  }
 }
 
 // ------------------------------------------------------------------ prefill (LDS-shared keys)
@@ -545,7 +588,7 @@ __global__ __launch_bounds__(kPfWaves * WAVE) void index_prefill_kernel(IndexLau
         for (int tI = 1; tI < 4; ++tI)
           if (grp == tI) res = part[u][tI];
         const int64_t s = s0 + lane;
-        if (out[u] && s < s_end) out[u][s] = s < vis[u] ? res : -INFINITY;
+        if (out[u] && s < s_end) out[u][s] = s < vis[u] ? stored_score(a, res) : -INFINITY;
       }
     }
   }
@@ -665,7 +708,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
       if (s0 + lane >= vis_end) res = -INFINITY;
     }
     const int64_t s = s0 + lane;
-    if (s < s_end) out[s] = res;
+    if (s < s_end) out[s] = stored_score(a, res);
   };
 
   constexpr int64_t kStep = 16 * kTiles;
@@ -741,6 +784,45 @@ MfmaKern pick_mfma(int HB, int KS) {
 }
 
 }  // namespace
+
+// The selecting stream kernel: bf16 queries and keys with 16-head blocks and DI of 32,
+// 64 or 128, few queries per sequence (the decode shape), and every row's candidates
+// (slices x k) within one final workgroup's capacity.
+int index_select_slices(const IndexLaunch& L) {
+  if (L.qI.dtype != CSA_BF16 || L.HI % 16 != 0 || L.HI > 128 || L.Tq >= kPfTok || L.N <= 0) return 0;
+  if (L.DI != 32 && L.DI != 64 && L.DI != 128) return 0;
+  if (L.sel_k < 1 || L.sel_k > 4096) return 0;
+  constexpr int64_t slice = static_cast<int64_t>(kSelWaves) * kSelKeysPerWave;
+  const int64_t slices = (L.N + slice - 1) / slice;
+  if (slices * L.sel_k > 32768) return 0;
+  // Selecting while scoring pays only when the slices shed most of the row: the fused
+  // kernel runs one 8-wave workgroup per CU (its prologue and selection are not hidden
+  // behind other workgroups' streaming) and the merge of the candidate lists costs about
+  // as much as a one-level selection of the whole row.  Measured on the 128K decode
+  // shape (k = 1024: half of every slice kept) the two-kernel path is faster.
+  if (slices * L.sel_k * 8 > L.N) return 0;
+  if (L.B * L.Tq * slices * kSelWaves >= (int64_t{1} << 32)) return 0;
+  return static_cast<int>(slices);
+}
+
+int launch_index_select(const IndexLaunch& L, hipStream_t stream) {
+  if (L.B * L.Tq == 0) return 0;
+  const int slices = index_select_slices(L);
+  if (slices == 0) return 1;
+  const int64_t grid = L.B * L.Tq * slices;
+  const int64_t wpt = static_cast<int64_t>(slices) * kSelWaves;
+  const dim3 g(static_cast<uint32_t>(grid)), blk(kSelWaves * WAVE);
+#define CSA_SEL(HB_, KS_)                                                                                          \
+  if (L.HI / 16 == HB_ && L.DI / 32 == KS_) {                                                                       \
+    hipLaunchKernelGGL((index_stream_kernel<HB_, KS_, kStreamTPS, kStreamNST, kSelWaves, true>), g, blk, 0, stream, \
+                       L, kSelKeysPerWave, wpt);                                                                   \
+    return hipGetLastError() == hipSuccess ? 0 : -1;                                                               \
+  }
+  CSA_SEL(1, 1) CSA_SEL(1, 2) CSA_SEL(1, 4) CSA_SEL(2, 1) CSA_SEL(2, 2) CSA_SEL(2, 4)
+  CSA_SEL(4, 1) CSA_SEL(4, 2) CSA_SEL(4, 4) CSA_SEL(8, 1) CSA_SEL(8, 2) CSA_SEL(8, 4)
+#undef CSA_SEL
+  return 1;
+}
 
 int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
   if (L.B == 0 || L.Tq == 0 || L.N == 0) return 0;

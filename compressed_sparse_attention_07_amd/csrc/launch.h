@@ -35,9 +35,22 @@ struct IndexLaunch {
   const int64_t* q_pos;
   int64_t B, Tq, N, kI_rows;
   int HI, DI, ratio;
-  float* scores;
+  float* scores;         // [B, Tq, N] or NULL (selecting launch without a score copy)
+  int score_bf16;        // round every score to bf16 before it is stored or selected
+  // selecting launch (launch_index_select): each slice's top-k candidates
+  int sel_k;
+  float* sel_val;        // [B * Tq, slices, sel_k]
+  int32_t* sel_idx;
 };
 int launch_index_scores(const IndexLaunch& L, hipStream_t stream);
+// Decode-shaped bf16 lightning indexer that selects while it scores: every workgroup
+// keeps its slice's top-k candidates (the score row is never stored unless L.scores is
+// set); the candidates then go through topk_merge.  Returns 1 (nothing launched) when
+// the shape is not covered.
+int index_select_slices(const IndexLaunch& L);  // slices per row, 0 if not covered
+int launch_index_select(const IndexLaunch& L, hipStream_t stream);
+int launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int64_t rows, int slices, int k,
+                      int32_t* idx, int32_t* count, hipStream_t stream);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t N, int k);
 int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count,

@@ -970,6 +970,348 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   }
 }
 
+// ================================================================ wave-pair path (bf16, D = 512)
+//
+// The LDS-DMA kernel's tiles and row loads, with every block of 16 heads served by a
+// pair of waves: wave 2p + h (h = 0, 1) of pair p takes key dims [256 h, 256 h + 256)
+// of the S^T = K Q^T contraction and output dims [256 h, 256 h + 256) of
+// O^T = V^T P^T.  The two halves of S^T meet through LDS (a + b is the same float in
+// both waves, so both hold identical logits and take identical softmax steps).  A wave
+// thereby holds half the queries and half the accumulators of the single-wave form,
+// and the registers this frees hold a whole tile's operand fragments: every LDS read of
+// a tile is issued before its MFMAs, where the single-wave form, at its register limit,
+// waits one LDS round trip per MFMA.  Per 16 heads and tile the LDS traffic also drops
+// from 64 KiB to 36 KiB (each wave reads half of every row twice and trades 2 KiB).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
+  constexpr int D = 512;
+  constexpr int R = 64;
+  constexpr int HD = D / 2;            // dims per wave
+  constexpr int NT = NW * 64;
+  constexpr int KP = D + 16;           // row pitch (bf16), as in attn_dma_kernel
+  constexpr int NSH = HD / 32;         // k-steps of the half contraction
+  constexpr int NDBH = HD / 16;        // 16-dim blocks of the half output
+  constexpr int RPW = kKT / NW;        // rows each wave loads per tile
+  constexpr int STAGE = kKT * KP;
+  constexpr int nope = D - R;
+  static_assert(NW % 2 == 0 && RPW * (kDmaStages - 2) < 64, "wave pairs; vmcnt range");
+
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kDmaStages * STAGE];
+  __shared__ __attribute__((aligned(16))) int idx_s[kDmaIdxCap];
+  __shared__ __attribute__((aligned(16))) int kvalid[kDmaStages][kKT];
+  __shared__ int64_t wpos_s[kDmaStages][kKT];
+  __shared__ float2 qcs[64];
+  __shared__ double theta[64];
+  __shared__ __attribute__((aligned(16))) f32x4 xch[NW][2][WAVE];  // S^T halves per wave and key block
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wid & 1;              // dims half of this wave
+  const int pr = wid >> 1;             // pair: heads 16 pr .. 16 pr + 15 of the group
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  asm volatile("" ::"s"(a.H), "s"(a.hpw), "s"(a.nsplit), "s"(a.sps), "s"(a.K), "s"(a.sparse), "s"(a.n_win),
+               "s"(a.ratio), "s"(a.Tq), "s"(a.N), "s"(a.kv_rows), "s"(a.Tw), "s"(a.pos_offset), "s"(a.q),
+               "s"(a.q_pos), "s"(a.win_pos0), "s"(a.idx), "s"(a.kv), "s"(a.win), "s"(a.nblk));
+  const uint32_t n_hg = static_cast<uint32_t>(a.H / a.hpw);
+  const uint32_t blk = xcd_block(blockIdx.x, a.nblk);
+  const int hg = __builtin_amdgcn_readfirstlane(static_cast<int>(blk % n_hg));
+  const uint32_t blk2 = blk / n_hg;
+  const int sp = __builtin_amdgcn_readfirstlane(static_cast<int>(blk2 % static_cast<uint32_t>(a.nsplit)));
+  const int64_t bt = __builtin_amdgcn_readfirstlane(static_cast<int>(blk2 / static_cast<uint32_t>(a.nsplit)));
+  const int64_t s_lo = static_cast<int64_t>(sp) * a.sps;
+  const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+  const int64_t b_seq = static_cast<uint32_t>(bt) / static_cast<uint32_t>(a.Tq);
+  const int64_t p_pre = a.q_pos[bt];
+  const int64_t wp0_pre = a.win_pos0[b_seq];
+  const double th_pre = tid < R / 2 ? a.theta_rev[tid] : 0.0;
+  asm volatile("" ::: "memory");
+  int32_t idx_pre[kDmaIdxCap / NT];
+  const int64_t n_idx = a.sparse ? min(s_lo + a.sps, static_cast<int64_t>(a.K)) - s_lo : 0;
+#pragma unroll
+  for (int u = 0; u < kDmaIdxCap / NT; ++u) {
+    const int64_t i = tid + static_cast<int64_t>(u) * NT;
+    idx_pre[u] = i < n_idx ? a.idx[bt * a.K + s_lo + i] : 0;
+  }
+  asm volatile("" ::: "memory");  // keep the index loads ahead of the query loads
+  const int h = hg * a.hpw + pr * 16 + col;  // head of this lane's result column
+  uint4 qraw[NSH];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (bt * a.H + h) * D + HD * hw + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < NSH; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+  }
+  const Slots S = slots_of(a, b_seq, uni64(p_pre), uni64(wp0_pre));
+  const int64_t s_hi = min(S.nslots, s_lo + a.sps);
+  const int ntiles = s_hi > s_lo ? static_cast<int>((s_hi - s_lo + kKT - 1) / kKT) : 0;
+  const double qpos = static_cast<double>(S.p + a.pos_offset);
+  const uint16_t* kvp = static_cast<const uint16_t*>(a.kv);
+  const uint16_t* winp = static_cast<const uint16_t*>(a.win);
+
+  if (tid < R / 2) {
+    theta[tid] = th_pre;
+    float c, sn;
+    rope_cs_rev(qpos, th_pre, &c, &sn);
+    qcs[tid] = make_float2(c, sn);
+  }
+#pragma unroll
+  for (int u = 0; u < kDmaIdxCap / NT; ++u) {
+    const int64_t i = tid + static_cast<int64_t>(u) * NT;
+    if (i < n_idx) idx_s[i] = idx_pre[u];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const int64_t u_lo = uni64(s_lo), u_hi = uni64(s_hi), u_nsel = uni64(S.nsel), u_wstart = uni64(S.wstart);
+  const uint16_t* kv_b = kvp + uni64(S.b * a.kv_rows) * D;
+  const uint16_t* win_b = winp + uni64(S.b * a.Tw - S.wp0) * D;
+  const uint16_t* win_self = win_b + uni64(S.p) * D;
+  // row loads of tile u into ring stage u % kDmaStages (one 1 KiB direct load per row;
+  // an empty slot loads the query's own window row, which the softmax masks)
+  auto issue = [&](int u) {
+    const int st = u % kDmaStages;
+    const uint16_t* src = win_self;
+    if (lane < RPW) {
+      const int j = wid * RPW + lane;
+      const int64_t slot = u_lo + static_cast<int64_t>(u) * kKT + j;
+      const bool live = slot < u_hi;
+      const bool sel = slot < u_nsel;
+      int64_t e = slot;
+      if (a.sparse) e = idx_s[min(slot - u_lo, static_cast<int64_t>(kDmaIdxCap - 1))];
+      const int64_t wp = u_wstart + (slot - u_nsel);
+      const bool ok = live && (!sel || e >= 0);
+      kvalid[st][j] = ok ? 1 : 0;
+      wpos_s[st][j] = (ok && !sel) ? wp : -1;
+      src = !ok ? win_self : (sel ? kv_b + e * D : win_b + wp * D);
+    }
+    const uint64_t sa = reinterpret_cast<uint64_t>(src);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sa), i));
+      const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(sa >> 32), i));
+      const uint16_t* row = reinterpret_cast<const uint16_t*>((hi << 32) | lo);
+      lds_dma16(row + lane * 8, ring_b + (st * STAGE + (wid * RPW + i) * KP) * 2);
+    }
+  };
+  constexpr int RCH = R / 8;
+  auto rope_window_rows = [&](int st) {
+    uint16_t* T = ring + st * STAGE;
+    for (int item = tid; item < kKT * RCH; item += NT) {
+      const int j = item / RCH;
+      const int64_t wpj = wpos_s[st][j];
+      if (wpj < 0) continue;
+      const int d0 = nope + 8 * (item % RCH);
+      uint4 v = *reinterpret_cast<const uint4*>(&T[j * KP + d0]);
+      float x[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
+                    bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
+      const double kp = static_cast<double>(wpj + a.pos_offset);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float cc, sn;
+        rope_cs_rev(kp, theta[(d0 + e - nope) / 2], &cc, &sn);
+        const float x0 = x[e], x1 = x[e + 1];
+        x[e] = x0 * cc - x1 * sn;
+        x[e + 1] = x0 * sn + x1 * cc;
+      }
+      *reinterpret_cast<uint4*>(&T[j * KP + d0]) =
+          make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7]));
+    }
+  };
+  auto tile_has_window = [&](int t) {
+    const int64_t first = s_lo + static_cast<int64_t>(t) * kKT;
+    return min(first + kKT, s_hi) > S.nsel && first < s_hi;
+  };
+
+  // this wave's half of the queries, roped (only the upper half holds RoPE dims).  They
+  // are complete before the first row load is issued: the compiler's waits for them
+  // count only its own loads, and inside the loop such a wait would also wait for
+  // every row load in flight.
+  bf16x8 qf[NSH];
+#pragma unroll
+  for (int s = 0; s < NSH; ++s) {
+    uint4 raw = qraw[s];
+    const int d0 = HD * hw + 32 * s + 8 * grp;
+    if (d0 + 8 > nope) {
+      float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
+                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        if (d0 + e >= nope) {
+          const float2 cs = qcs[(d0 + e - nope) / 2];
+          const float x0 = v[e], x1 = v[e + 1];
+          v[e] = x0 * cs.x - x1 * cs.y;
+          v[e + 1] = x0 * cs.y + x1 * cs.x;
+        }
+      }
+      raw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+#pragma unroll
+  for (int s = 0; s < NSH; ++s) asm volatile("" : "+v"(qf[s]));
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+
+  f32x4 acc[NDBH];
+#pragma unroll
+  for (int i = 0; i < NDBH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t % kDmaStages;
+    const int later = min(ntiles - 1 - t, kDmaStages - 2);  // tiles issued after t
+    if (later >= 2) wait_vmcnt<2 * RPW>();
+    else if (later == 1) wait_vmcnt<RPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (tile_has_window(t)) {
+      rope_window_rows(st);
+      __syncthreads();
+    }
+    if (t + kDmaStages - 1 < ntiles) issue(t + kDmaStages - 1);  // into the stage freed by tile t-1
+    const uint16_t* K = ring + st * STAGE;
+
+    // ---- this wave's half of S^T for the tile's two 16-key blocks: every K fragment is
+    // read before the first product
+    f32x4 sacc[2];
+    {
+      bf16x8 kf[2][NSH];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < NSH; ++s)
+          kf[kb][s] = *reinterpret_cast<const bf16x8*>(K + (16 * kb + col) * KP + HD * hw + 8 * grp + 32 * s);
+      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NSH; ++s)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sacc[kb], 0, 0, 0);
+      }
+    }
+    // ---- the other half from the partner wave
+    xch[wid][0][lane] = sacc[0];
+    xch[wid][1][lane] = sacc[1];
+    __syncthreads();
+    {
+      const f32x4 o0 = xch[wid ^ 1][0][lane], o1 = xch[wid ^ 1][1][lane];
+      sacc[0] += o0;
+      sacc[1] += o1;
+    }
+    // ---- online softmax for head h over this lane's 8 keys (16 kb + 4 grp + r); the two
+    // waves of a pair compute the same values
+    float z[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int4 kv4 = *reinterpret_cast<const int4*>(&kvalid[st][16 * kb + 4 * grp]);
+      const int vv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = vv[r] ? a.scale * sacc[kb][r] : -INFINITY;
+        z[kb][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    constexpr float kSlack = 8.f;  // lazy rescale, as in attn_mfma_kernel
+    const bool raise = mt > m_run + kSlack;
+    const float m_ref = raise ? mt : m_run;
+    if (__any(raise)) {
+      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : __expf(m_run - m_ref);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDBH; ++db) acc[db] *= alpha;
+    }
+    m_run = m_ref;
+    const bool none = (m_run == -INFINITY);
+    float pn[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = none ? 0.f : __expf(z[kb][r] - m_run);
+        psum += p;
+        pn[4 * kb + r] = p;
+      }
+    }
+    l_run += psum;
+    const bf16x8 pB = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3]),
+                                                            pack_bf16x2(pn[4], pn[5]), pack_bf16x2(pn[6], pn[7])));
+    // ---- O^T += V^T P^T over this wave's output dims (V^T by transpose reads, all
+    // issued before the products)
+    {
+      const uint16_t* vb = K + (4 * grp + (col >> 2)) * KP + 4 * (col & 3) + HD * hw;
+      s16x4 lo[NDBH], hi[NDBH];
+#pragma unroll
+      for (int db = 0; db < NDBH; ++db) {
+        lo[db] = lds_read_tr(vb + 16 * db);
+        hi[db] = lds_read_tr(vb + 16 * KP + 16 * db);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < NDBH; ++db) {
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[db], hi[db], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pB, acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, WAVE);
+  l_tot += __shfl_xor(l_tot, 32, WAVE);
+
+  const int64_t th = bt * a.H + h;
+  const bool part = a.nsplit > 1;
+  float scl;
+  if (part) {
+    scl = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  } else {
+    const float sk = a.sink[h];
+    if (sk == INFINITY) scl = 0.f;
+    else if (sk == -INFINITY) scl = 1.f / l_tot;
+    else scl = 1.f / (l_tot + __expf(sk - m_run));
+  }
+  __syncthreads();  // every wave is done reading the ring
+  // result rows leave through LDS so that every store writes 512 contiguous bytes
+  uint16_t* rows = ring + pr * 16 * KP + HD * hw;  // the pair's 16 rows, this wave's half
+#pragma unroll
+  for (int db = 0; db < NDBH; ++db) {
+    const int d0 = HD * hw + 16 * db + 4 * grp;
+    float v[4] = {acc[db][0] * scl, acc[db][1] * scl, acc[db][2] * scl, acc[db][3] * scl};
+    if (!part && d0 >= nope) {
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float2 cs = qcs[(d0 + e - nope) / 2];
+        const float x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * cs.x + x1 * cs.y;
+        v[e + 1] = x1 * cs.x - x0 * cs.y;
+      }
+    }
+    *reinterpret_cast<uint2*>(rows + col * KP + 16 * db + 4 * grp) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+  if (part && hw == 0 && grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
+  // lanes 0-31 move row 2i, lanes 32-63 row 2i + 1: 16 bytes each of this wave's half
+  const int64_t h0 = bt * a.H + hg * a.hpw + pr * 16;
+  const int rsub = lane >> 5;
+  const int dl = 8 * (lane & 31);
+#pragma unroll 4
+  for (int i = 0; i < 8; ++i) {
+    const int r = 2 * i + rsub;
+    const uint4 v = *reinterpret_cast<const uint4*>(rows + r * KP + dl);
+    uint16_t* dst = part ? a.part_o + ((h0 + r) * a.nsplit + sp) * D : static_cast<uint16_t*>(a.out) + (h0 + r) * D;
+    *reinterpret_cast<uint4*>(dst + HD * hw + dl) = v;
+  }
+}
+
 // Merge the split partials of every (token, head) in split order: one wave per
 // (token, head), lane l owns output dims [8l, 8l + 8) (D <= 512, nsplit <= 64).
 // The split weights exp(m_i - M) * l_i are formed once per wave (lane i holds split
@@ -1218,10 +1560,20 @@ constexpr int64_t kMinSplitMfma = 128;
 constexpr int64_t kMaxSplitsSparse = 12;
 constexpr int64_t kMaxSplitsDense = 8;  // long dense key lists: fewer, longer splits
 
-Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma, bool sparse, bool dma) {
+// Which MFMA kernel a launch takes: the register-staged one, the LDS-DMA one (16 heads
+// per wave) or the wave-pair one (16 heads per pair of waves).
+enum class Kern { kReg, kDma, kPair };
+
+constexpr int kPairMaxBlocks = 4;       // 16-head blocks per wave-pair workgroup (8 waves)
+constexpr int64_t kMinSplitPair = 96;
+constexpr int64_t kMaxSplitsSparsePair = 8;
+
+Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma, bool sparse, Kern kern) {
   Plan p{mfma, 0, 1, 0};
   if (!mfma) return p;
-  int hpw = dma ? head_group(H, kDmaMaxWaves) : base_hpw(H, D);
+  const bool dma = kern != Kern::kReg;
+  int hpw = kern == Kern::kPair ? head_group(H, kPairMaxBlocks)
+                                : (kern == Kern::kDma ? head_group(H, kDmaMaxWaves) : base_hpw(H, D));
   if (hpw <= 0 || H % hpw != 0) {
     // no head group of an instantiated size: the SIMT kernel, which needs no workspace
     p.mfma = false;
@@ -1244,13 +1596,13 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
   }
   int64_t ns = 1;
   if (units < 256) {
-    const int64_t min_split = dma ? kMinSplitDma : kMinSplitMfma;
-    const int64_t mx = sparse ? kMaxSplitsSparse : kMaxSplitsDense;
+    const int64_t min_split = kern == Kern::kPair ? kMinSplitPair : (dma ? kMinSplitDma : kMinSplitMfma);
+    const int64_t mx = kern == Kern::kPair ? kMaxSplitsSparsePair : (sparse ? kMaxSplitsSparse : kMaxSplitsDense);
     ns = (max_slots + min_split - 1) / min_split;
     if (ns > mx) ns = mx;
     if (ns < 1) ns = 1;
   }
-  // a sparse range's entry indices are staged in LDS by the DMA kernel
+  // a sparse range's entry indices are staged in LDS by the DMA kernels
   if (sparse && max_slots <= 64 * kDmaIdxCap && ns < (max_slots + kDmaIdxCap - 1) / kDmaIdxCap)
     ns = (max_slots + kDmaIdxCap - 1) / kDmaIdxCap;
   int64_t sps = ((max_slots + ns - 1) / ns + kKT - 1) / kKT * kKT;
@@ -1296,6 +1648,25 @@ bool dma_ok(const AttnLaunch& L) {
   const int nw = head_group(L.H, kDmaMaxWaves) / 16;
   if (L.kv.dtype == CSA_FP8MIX) return nw == 4 || nw == 8;  // three loads per row: 16 rows per wave would overflow vmcnt
   return nw == 2 || nw == 4 || nw == 8;
+}
+
+// bf16 cache, D = 512 with RoPE on the last 64 dims, 16, 32 or 64 heads per group: the
+// wave-pair kernel
+bool pair_ok(const AttnLaunch& L) {
+  if (!dma_ok(L) || L.kv.dtype != CSA_BF16) return false;
+  const int hpw = head_group(L.H, kPairMaxBlocks);
+  return hpw == 16 || hpw == 32 || hpw == 64;
+}
+
+// The wave-pair kernel serves sparse decode-shaped launches (fewer than 256 (token,
+// 128-head group) units per sequence, so the key slots are split): there its shorter
+// per-tile chain wins.  Prefill and dense launches keep 128 heads per workgroup, which
+// loads each key tile once per token.  The choice depends on the per-sequence shape only.
+Kern kern_of(const AttnLaunch& L) {
+  if (!dma_ok(L)) return Kern::kReg;
+  const int hpw = head_group(L.H, kDmaMaxWaves);
+  if (L.sparse && pair_ok(L) && hpw > 0 && L.Tq * (L.H / hpw) < 256) return Kern::kPair;
+  return Kern::kDma;
 }
 
 AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
@@ -1350,8 +1721,11 @@ bool attn_uses_mfma(const AttnLaunch& L) { return mfma_ok(L); }
 size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool sparse) {
   // the larger of the two MFMA kernels' needs (which one runs depends on the cache dtype)
   if (H < 1 || D < 1) return 0;
-  int64_t ns = make_plan(B, Tq, H, D, max_slots, true, sparse, false).nsplit;
-  if (D == 512) ns = std::max<int64_t>(ns, make_plan(B, Tq, H, D, max_slots, true, sparse, true).nsplit);
+  int64_t ns = make_plan(B, Tq, H, D, max_slots, true, sparse, Kern::kReg).nsplit;
+  if (D == 512) {
+    ns = std::max<int64_t>(ns, make_plan(B, Tq, H, D, max_slots, true, sparse, Kern::kDma).nsplit);
+    ns = std::max<int64_t>(ns, make_plan(B, Tq, H, D, max_slots, true, sparse, Kern::kPair).nsplit);
+  }
   if (ns <= 1) return 0;
   const int64_t th = B * Tq * H;
   return static_cast<size_t>(th * ns) * (static_cast<size_t>(D) * sizeof(uint16_t) + sizeof(float2));
@@ -1360,8 +1734,9 @@ size_t attn_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int64_t max_slo
 int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int64_t tokens = L.B * L.Tq;
   if (tokens == 0) return 0;
-  const bool dma = mfma_ok(L) && dma_ok(L);
-  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma_ok(L), L.sparse != 0, dma);
+  const Kern kern = kern_of(L);
+  const bool dma = mfma_ok(L) && kern != Kern::kReg;
+  const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma_ok(L), L.sparse != 0, kern);
   const bool mfma = P.mfma;
   if (mfma && P.nsplit > 1 && ws_bytes < attn_workspace_bytes(L.B, L.Tq, L.H, L.D, max_slots_of(L), L.sparse != 0))
     return -3;
@@ -1382,7 +1757,12 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
     if (dma) {
       if (L.sparse && P.sps > kDmaIdxCap) return -1;  // excluded by the plan
       const dim3 g(static_cast<uint32_t>(grid));
-      if (fp8) {  // 4 or 8 waves (dma_ok)
+      if (kern == Kern::kPair) {  // two waves per 16 heads
+        const dim3 pb(P.hpw / 8 * WAVE);
+        if (P.hpw == 64) hipLaunchKernelGGL(attn_pair_kernel<8>, g, pb, 0, stream, a);
+        else if (P.hpw == 32) hipLaunchKernelGGL(attn_pair_kernel<4>, g, pb, 0, stream, a);
+        else hipLaunchKernelGGL(attn_pair_kernel<2>, g, pb, 0, stream, a);
+      } else if (fp8) {  // 4 or 8 waves (dma_ok)
         if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, true>), g, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_dma_kernel<4, 64, true>), g, block, 0, stream, a);
       } else {

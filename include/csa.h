@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -70,6 +70,15 @@ typedef enum csa_status {
  *                      contiguous elements
  */
 typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8MIX = 2, CSA_MXFP4 = 3 } csa_dtype;
+
+/*
+ * CSA_FLAG_BF16_SCORES: index scores are rounded to bf16 (nearest-even) before the
+ * top-k selection, as the report stores them to speed the selector up ([V4-CN] §3.4:
+ * FP32 -> BF16 index scores, 99.7% recall of the selected KV entries).  Equal bf16
+ * scores are then taken in increasing entry order.  Off by default: the selection is
+ * then exact on the fp32 scores.
+ */
+#define CSA_FLAG_BF16_SCORES 1
 
 typedef struct csa_buf {
   void* data;
@@ -162,6 +171,29 @@ csa_status csa_topk(const float* scores, int64_t rows, int64_t N, int32_t k, int
                     int32_t* count, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_index_topk -- lightning indexer and top-k selector in one call ([V4-CN] §2.3.1:
+ * index scores, then C_t = TopK_k(I_t,:); §3.4 for the BF16-score option).
+ * idx [B*Tq, k] and count [B*Tq] (optional) are exactly those of csa_index_scores
+ * followed by csa_topk on the same scores (with CSA_FLAG_BF16_SCORES in flags: on the
+ * scores rounded to bf16).  Few queries per sequence with bf16 operands and rows much
+ * longer than the candidates they keep (the decode shape: Tq < 16, HI % 16 == 0, DI in
+ * {32, 64, 128}, 8 * ceil(N / 2048) * k <= N) take a fused path: every workgroup keeps
+ * its 2048-entry slice's top-k while it scores, so the score row is not written, and
+ * one merge selects each row's top-k from those candidates.  Other shapes run the two
+ * stages.
+ *   scores  optional float [B, Tq, N]: when not NULL it also receives the scores
+ *   ws      device workspace of at least csa_index_topk_workspace_size(...) bytes
+ *           (candidate lists, or the score rows and top-k levels)
+ * Arguments and limits as csa_index_scores and csa_topk; flags: CSA_FLAG_* bits.
+ */
+size_t csa_index_topk_workspace_size(int64_t B, int64_t Tq, int32_t HI, int32_t DI, int64_t N, int32_t k,
+                                     int32_t qI_dtype, int32_t flags);
+csa_status csa_index_topk(const csa_buf* qI, const float* wI, const csa_buf* kI, const int64_t* q_pos,
+                          int64_t B, int64_t Tq, int32_t HI, int32_t DI, int64_t N, int64_t kI_rows,
+                          int32_t ratio, int32_t k, int32_t flags, int32_t* idx, int32_t* count,
+                          float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * csa_sparse_mqa -- shared-KV multi-query attention over the selected compressed
  * entries plus the raw sliding window ([V4-CN] §2.3.1 shared-KV MQA: each entry is
  * both key and value for all heads; §2.3.3 window branch, attention sink, partial
@@ -241,7 +273,7 @@ typedef struct csa_layer_desc {
   float softmax_scale;
   int64_t pos_offset;
   int32_t stream_dtype;  /* C/Z streams: F32 or BF16 */
-  int32_t pad0;
+  int32_t flags;         /* CSA_FLAG_* (0 = the exact default) */
 } csa_layer_desc;
 
 typedef struct csa_forward_io {

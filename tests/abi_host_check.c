@@ -79,6 +79,19 @@ int main(void) {
   (void)csa_topk_workspace_size(0, 0, 1);
   (void)csa_topk_workspace_size(1 << 20, 1 << 20, 4096);
 
+  /* fused indexer + top-k */
+  expect(csa_index_topk(&bf16, (const float*)p, &f32, (const int64_t*)p, 1, 1, 16, 128, 64, 64, 4, 8, 0, (int32_t*)p,
+                        NULL, NULL, NULL, 0, NULL) == CSA_ERR_DTYPE, "index_topk: dtype mismatch");
+  expect(csa_index_topk(&bf16, (const float*)p, &bf16, (const int64_t*)p, 1, 1, 16, 128, 64, 64, 4, 0, 0, (int32_t*)p,
+                        NULL, NULL, NULL, 0, NULL) == CSA_ERR_SHAPE, "index_topk: k = 0");
+  expect(csa_index_topk(&bf16, (const float*)p, &bf16, (const int64_t*)p, 1, 1, 16, 128, 64, 64, 4, 8, 6, (int32_t*)p,
+                        NULL, NULL, NULL, 0, NULL) == CSA_ERR_SHAPE, "index_topk: unknown flag");
+  expect(csa_index_topk(&bf16, (const float*)p, &bf16, (const int64_t*)p, 16, 1, 64, 128, 32768, 32768, 4, 1024, 0,
+                        (int32_t*)p, NULL, NULL, NULL, 0, NULL) == CSA_ERR_WORKSPACE, "index_topk: no workspace");
+  (void)csa_index_topk_workspace_size(16, 1, 64, 128, 32768, 1024, CSA_BF16, 0);
+  (void)csa_index_topk_workspace_size(1, 2048, 64, 128, 262144, 1024, CSA_BF16, CSA_FLAG_BF16_SCORES);
+  (void)csa_index_topk_workspace_size(8, 1, 64, 128, 262144, 1024, CSA_MXFP4, 0);
+
   /* attention size queries over many shapes, including head counts with no MFMA head group */
   {
     const int Hs[] = {1, 8, 16, 17, 32, 48, 64, 72, 80, 112, 128, 144, 176, 200, 240, 256};

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.csa_abi_version() == 1
+    assert L.csa_abi_version() == 2
 
 
 def _buf(dtype=1, data=0x100000):

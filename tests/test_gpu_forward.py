@@ -127,6 +127,43 @@ def test_forward_bf16_mfma_paths():
         _check_layer(r, b, "bf16", k, ratio, n_win, R, 1.0)
 
 
+def test_forward_bf16_decode_fused_selection():
+    # few queries per sequence: the indexer selects while it scores (2048-entry slices,
+    # so several slices and a partial last one here)
+    say("forward bf16 decode shape (fused indexer + top-k)")
+    B, T, D, DI, H, HI, Tq, k, ratio, n_win, R = 3, 20480, 128, 64, 16, 16, 2, 64, 4, 64, 64
+    r = _run_forward("bf16", B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, 1.0, 4321)
+    for b in range(B):
+        _check_layer(r, b, "bf16", k, ratio, n_win, R, 1.0)
+
+
+def test_forward_with_no_queries_only_compresses():
+    # Tq = 0 (a compression-only step, bf16 decode shape): the caches are written and
+    # no selection or attention launch runs
+    say("forward with Tq = 0")
+    g = Gen(98, DEV)
+    B, T, D, DI, H, HI, ratio = 2, 64, 128, 64, 16, 16, 4
+    # the query buffers exist (one token each) but the descriptor asks for none
+    streams, istreams, q, qI, wI, win, sink = _csa_case(g, B, T, D, DI, H, HI, 1, "bf16")
+    N = T // ratio
+    kv = csa.Buf.empty((B, N, D), csa.CSA_BF16)
+    ik = csa.Buf.empty((B, N, DI), csa.CSA_BF16)
+    desc = csa.layer_desc(mode=csa.CSA_MODE_CSA, B=B, T=T, t0=0, Tq=0, cache_rows=N, Tw=T, D=D, H=H, HI=HI, DI=DI,
+                          ratio=ratio, topk=8, n_win=16, rope_dims=64, rope_base=10000.0, softmax_scale=1.0,
+                          stream_dtype=csa.CSA_BF16)
+    io = dict(ca=streams[0], cb=streams[1], za=streams[2], zb=streams[3], ica=istreams[0], icb=istreams[1],
+              iza=istreams[2], izb=istreams[3], kv_cache=kv, ik_cache=ik, q=q, q_pos=torch.zeros((B, 1), dtype=torch.int64,
+              device=DEV), qI=qI, wI=wI, win=win, win_pos0=torch.zeros((B,), dtype=torch.int64, device=DEV), sink=sink,
+              out=torch.empty_like(q))
+    csa.csa_forward(desc, io)
+    torch.cuda.synchronize()
+    for b in range(B):
+        want = O.compress(*[f64(x[b]) for x in streams], ratio=ratio, overlap=True, rope_dims=64, rope_base=10000.0)
+        assert_close(f64(kv.data[b]), want, "bf16", "KV cache")
+        iwant = O.compress(*[f64(x[b]) for x in istreams], ratio=ratio, overlap=True)
+        assert_close(f64(ik.data[b]), iwant, "bf16", "indexer cache")
+
+
 def test_forward_chunked_compression_matches_whole():
     # two csa_forward calls (t0 = 0, then t0 = 128 with the previous block) build the
     # same caches as one compression of the whole sequence

@@ -24,7 +24,8 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_DTYPE"
 
 EXPORTS = ["csa_abi_version", "csa_last_error", "csa_device_check", "csa_compress", "csa_quantize",
            "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_mqa_workspace_size",
-           "csa_sparse_mqa", "hca_dense_attn_workspace_size", "hca_dense_attn",
+           "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "csa_sparse_mqa_noalloc_limit", "hca_dense_attn_workspace_size",
+           "hca_dense_attn",
            "csa_forward_workspace_size", "csa_forward"]
 
 
@@ -88,6 +89,10 @@ def lib():
         L.csa_sparse_mqa_workspace_size.restype = sz
         L.csa_sparse_mqa.argtypes = [bp, vp, bp, i64, vp, i32, bp, vp, i64, vp, f32, i32, f32, i64, i64, i64, i32,
                                      i32, i64, i32, bp, vp, sz, vp]
+        L.csa_sparse_mqa_noalloc.argtypes = [bp, vp, bp, i64, vp, i32, bp, vp, i64, vp, f32, i32, f32, i64, i64, i64,
+                                             i32, i32, i64, i32, bp, vp]
+        L.csa_sparse_mqa_noalloc_limit.argtypes = []
+        L.csa_sparse_mqa_noalloc_limit.restype = sz
         L.hca_dense_attn_workspace_size.argtypes = [i64, i64, i32, i32, i64, i32]
         L.hca_dense_attn_workspace_size.restype = sz
         L.hca_dense_attn.argtypes = [bp, vp, bp, i64, i32, bp, vp, i64, vp, f32, i32, f32, i64, i64, i64, i32, i32,
@@ -97,6 +102,7 @@ def lib():
         L.csa_forward.argtypes = [C.POINTER(csa_layer_desc), C.POINTER(csa_forward_io), vp, sz, vp]
         for name in EXPORTS:
             if name not in ("csa_topk_workspace_size", "csa_sparse_mqa_workspace_size", "csa_index_topk_workspace_size",
+                            "csa_sparse_mqa_noalloc_limit",
                             "hca_dense_attn_workspace_size", "csa_forward_workspace_size",
                             "csa_last_error", "csa_abi_version"):
                 getattr(L, name).restype = C.c_int
@@ -263,6 +269,19 @@ def csa_sparse_mqa(q, q_pos, kv, idx, win, win_pos0, sink, out, *, N: int, n_win
     _invoke("csa_sparse_mqa", C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ptr(idx), K, C.byref(cw),
             ptr(win_pos0), Tw, ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
             C.byref(co), ptr(w), wbytes, stream_handle(stream), keep=(w,))
+
+
+def csa_sparse_mqa_noalloc(q, q_pos, kv, idx, win, win_pos0, sink, out, *, N: int, n_win: int, softmax_scale: float,
+                           rope_dims: int, rope_base: float = 10000.0, pos_offset: int = 0, stream=None) -> None:
+    qb, kvb, wb_, ob = Buf.of(q), Buf.of(kv), Buf.of(win), Buf.of(out)
+    B, Tq, H, D = qb.shape
+    kv_rows = kvb.shape[1]
+    Tw = wb_.shape[1]
+    K = idx.shape[-1]
+    cq, ck, cw, co = qb.c(), kvb.c(), wb_.c(), ob.c()
+    _invoke("csa_sparse_mqa_noalloc", C.byref(cq), ptr(q_pos), C.byref(ck), kv_rows, ptr(idx), K, C.byref(cw),
+            ptr(win_pos0), Tw, ptr(sink), softmax_scale, rope_dims, rope_base, pos_offset, B, Tq, H, D, N, n_win,
+            C.byref(co), stream_handle(stream))
 
 
 def hca_dense_attn(q, q_pos, kv, win, win_pos0, sink, out, *, N: int, ratio: int, n_win: int, softmax_scale: float,

@@ -437,6 +437,73 @@ csa_status csa_sparse_mqa(const csa_buf* q, const int64_t* q_pos, const csa_buf*
   return launched(launch_attn(L, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_sparse_mqa");
 }
 
+// ------------------------------------------------------------------ allocation-free attention
+//
+// csa_sparse_mqa_noalloc keeps the split partials in this file-scope device array
+// instead of a caller workspace.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and that
+// address is what the kernels receive.  Every call on one GPU shares the array, so calls
+// that overlap on one GPU race; nothing in it needs to start at zero (each split writes
+// its partial rows and statistics in full before the merge reads them).
+
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+csa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "no usable HIP device for the scratch array");
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(CSA_ERR_DEVICE, "hipGetSymbolAddress failed for the scratch array on device %d", dev);
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status csa_sparse_mqa_noalloc(const csa_buf* q, const int64_t* q_pos, const csa_buf* kv, int64_t kv_rows,
+                                  const int32_t* idx, int32_t K, const csa_buf* win, const int64_t* win_pos0,
+                                  int64_t Tw, const float* sink, float softmax_scale, int32_t rope_dims,
+                                  float rope_base, int64_t pos_offset, int64_t B, int64_t Tq, int32_t H, int32_t D,
+                                  int64_t N, int32_t n_win, const csa_buf* out, void* stream) {
+  CSA_TRY(validate_attn(q, q_pos, kv, kv_rows, win, win_pos0, Tw, sink, rope_dims, rope_base, B, Tq, H, D, N, n_win,
+                        out));
+  if (K < 0 || K > (1 << 20)) return fail(CSA_ERR_SHAPE, "K out of range");
+  if (K > 0 && !idx) return fail(CSA_ERR_NULL, "idx is required when K > 0");
+  AttnLaunch L = make_attn(q, q_pos, kv, kv_rows, 1, idx, K, 1, win, win_pos0, Tw, sink, softmax_scale, rope_dims,
+                           rope_base, pos_offset, B, Tq, H, D, N, n_win, out);
+  const size_t need = attn_uses_mfma(L) ? attn_workspace_bytes(B, Tq, H, D, static_cast<int64_t>(K) + n_win, true) : 0;
+  if (need > kNoAllocScratchBytes)
+    return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_noalloc: %zu scratch bytes needed, the limit is %zu", need,
+                kNoAllocScratchBytes);
+  CSA_TRY(check_device());
+  void* ws = nullptr;
+  CSA_TRY(scratch_address(&ws));
+  return launched(launch_attn(L, ws, kNoAllocScratchBytes, static_cast<hipStream_t>(stream)),
+                  "csa_sparse_mqa_noalloc");
+}
+
+size_t csa_sparse_mqa_noalloc_limit(void) { return kNoAllocScratchBytes; }
+
 size_t hca_dense_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t D, int64_t N, int32_t n_win) {
   return attn_workspace_bytes(B, Tq, H, D, N + n_win, false);
 }

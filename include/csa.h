@@ -229,6 +229,25 @@ csa_status csa_sparse_mqa(const csa_buf* q, const int64_t* q_pos, const csa_buf*
                           size_t ws_bytes, void* stream);
 
 /*
+ * csa_sparse_mqa_noalloc -- csa_sparse_mqa without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * csa_sparse_mqa minus ws / ws_bytes.  The split partials live in a static device
+ * array of csa_sparse_mqa_noalloc_limit() bytes (32 MiB) that each GPU holds for the
+ * life of the process; a call needing more (csa_sparse_mqa_workspace_size larger than
+ * the limit) returns CSA_ERR_UNSUPPORTED and launches nothing.  No call allocates or
+ * frees memory.  Calls that overlap on one GPU share the array and race: order them
+ * (same stream) or use csa_sparse_mqa.
+ */
+csa_status csa_sparse_mqa_noalloc(const csa_buf* q, const int64_t* q_pos, const csa_buf* kv,
+                                  int64_t kv_rows, const int32_t* idx, int32_t K, const csa_buf* win,
+                                  const int64_t* win_pos0, int64_t Tw, const float* sink,
+                                  float softmax_scale, int32_t rope_dims, float rope_base,
+                                  int64_t pos_offset, int64_t B, int64_t Tq, int32_t H, int32_t D,
+                                  int64_t N, int32_t n_win, const csa_buf* out, void* stream);
+size_t csa_sparse_mqa_noalloc_limit(void);
+
+/*
  * hca_dense_attn -- HCA core attention ([V4-CN] §2.3.2; [NOTES] hca() sketch):
  * as csa_sparse_mqa, with the compressed keys being every entry i < min(N,
  * floor(p / ratio)) instead of an index list.

@@ -110,6 +110,13 @@ int main(void) {
   expect(csa_sparse_mqa(&bf16, (const int64_t*)p, &fp8_noscale, 10, (const int32_t*)p, 4, &bf16, (const int64_t*)p,
                         16, (const float*)p, 1.f, 64, 1e4f, 0, 1, 1, 16, 128, 10, 8, &bf16, NULL, 0, NULL) ==
          CSA_ERR_NULL, "mqa: FP8MIX without a scale");
+  expect(csa_sparse_mqa_noalloc(&bf16, (const int64_t*)p, &bf16, 10, (const int32_t*)p, 4, &bf16, (const int64_t*)p,
+                                16, (const float*)p, 1.f, 64, 1e4f, 0, 1, 1, 16, 128, 10, 0, &bf16, NULL) ==
+         CSA_ERR_SHAPE, "mqa noalloc: n_win 0");
+  expect(csa_sparse_mqa_noalloc(&bf16, (const int64_t*)p, &bf16, 64, (const int32_t*)p, 1024, &bf16, (const int64_t*)p,
+                                128, (const float*)p, 1.f, 64, 1e4f, 0, 64, 4, 128, 512, 64, 128, &bf16, NULL) ==
+         CSA_ERR_UNSUPPORTED, "mqa noalloc: above the scratch limit");
+  expect(csa_sparse_mqa_noalloc_limit() == ((size_t)32 << 20), "mqa noalloc: limit");
   expect(hca_dense_attn(&bf16, (const int64_t*)p, &bf16, 10, 0, &bf16, (const int64_t*)p, 16, (const float*)p, 1.f,
                         64, 1e4f, 0, 1, 1, 16, 128, 10, 8, &bf16, NULL, 0, NULL) == CSA_ERR_SHAPE, "hca: ratio 0");
 

@@ -80,6 +80,26 @@ def read_traffic(kernel_file: str, src: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
+def read_counters(kernel_file: str, src: str):
+    """MFMA-busy and LDS figures per launch from a committed counter summary, if it
+    matches the source."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#") and not line.startswith(" "):
+            k, v = line.strip().split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src:
+        return None
+    out = {}
+    for k in ("mfma_busy_frac", "lds_bank_conflict_frac", "valu_busy_frac", "sq_busy_cycles_per_launch"):
+        if k in vals:
+            out[k] = float(vals[k])
+    return out or None
+
+
 # ============================================================================ workloads
 
 
@@ -314,12 +334,15 @@ def build_workload(key: str, layers: int, dev: str = "cuda") -> Workload:
     return wl
 
 
-def _attn_kernels(ws, M) -> str:
+def _attn_kernels(ws, M, sparse: bool) -> str:
     """The attention kernels one call launches: the main kernel, plus the combine kernel
     when the key range is split (the call then needs a workspace for the partials)."""
-    # D = 512 with 64 RoPE dims takes the LDS-DMA kernel (bf16 or FP8MIX cache; FP8MIX with 4 or 8 waves)
+    # D = 512 with 64 RoPE dims takes the LDS-DMA kernels (bf16 or FP8MIX cache; FP8MIX
+    # with 4 or 8 waves); sparse bf16 launches with fewer than 256 query tokens per
+    # sequence (128 heads) take the wave-pair kernel
     dma = M["D"] == 512 and M["R"] == 64 and (M["kv_format"] != "fp8mix" or M["H"] % 64 == 0)
-    main = "attn_dma_kernel" if dma else "attn_mfma_kernel"
+    pair = dma and sparse and M["kv_format"] != "fp8mix" and M["Tq"] * max(1, M["H"] // 128) < 256
+    main = "attn_pair_kernel" if pair else ("attn_dma_kernel" if dma else "attn_mfma_kernel")
     return main + ("+attn_combine_kernel" if ws.numel() > 1 else "")
 
 
@@ -381,7 +404,7 @@ def _add_stages(wl: Workload, csa, torch, dev):
         # algorithmic bytes: every distinct entry once (a prefill chunk's selections overlap), q, out, indices
         uniq = min(sum(keys), B * (N + M["Tw"]))
         wl.stages["sparse_mqa"] = Stage(st_attn, uniq * kv_entry + B * Tq * (4 * H * D + 4 * k),
-                                        4.0 * H * D * sum(keys), _attn_kernels(mqa_ws, M), ("mqa.hip",))
+                                        4.0 * H * D * sum(keys), _attn_kernels(mqa_ws, M, True), ("mqa.hip",))
         wl.stages["_prime"] = Stage(lambda i: (st_index(i), st_topk(i)), 0, 0, "", ())
     else:
         mqa_ws = torch.empty(max(1, csa.lib().hca_dense_attn_workspace_size(B, Tq, H, D, N, W)), dtype=torch.uint8,
@@ -396,7 +419,7 @@ def _add_stages(wl: Workload, csa, torch, dev):
         keys = [v + min(W, int(p) + 1) for row, prow in zip(vis, pos.tolist()) for v, p in zip(row, prow)]
         uniq = B * (N + M["Tw"]) if Tq > 1 else sum(keys)
         wl.stages["dense_attn"] = Stage(st_attn, uniq * kv_entry + B * Tq * 4 * H * D, 4.0 * H * D * sum(keys),
-                                        _attn_kernels(mqa_ws, M), ("mqa.hip",))
+                                        _attn_kernels(mqa_ws, M, False), ("mqa.hip",))
 
 
 def _prepare_stages(wl: Workload, csa):
@@ -513,12 +536,120 @@ def summarize_pmc(fetch_csv: str, write_csv: str, kernel: str, src: str, out: st
     print("\n".join(lines))
 
 
-KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip",),
+COUNTERS = ("SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+            "SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
+N_CU = 256
+N_XCD = 8
+
+
+def summarize_counters(csv_path: str, kernel: str, src: str, out: str, command: str, workload: str):
+    """MFMA and LDS behaviour of `kernel` per dispatch from one `rocprofv3 --pmc` run of the
+    COUNTERS (summed over the device by the profiler).
+
+    mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x 256 CUs x GRBM_GUI_ACTIVE / 8): the
+    share of SIMD-cycles the matrix cores were busy while the GPU ran the kernel (the
+    profiler sums GRBM_GUI_ACTIVE over the 8 XCDs; at the clock the GPU actually ran, so
+    it reads above the FLOP fraction of the 2.4 GHz spec peak);
+    lds_bank_conflict_frac = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: the share of the
+    cycles the LDS was addressed that a bank conflict stalled; mfma_flop =
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the counter counts bf16 matrix work in units of
+    512 FLOP).  The most frequent grid of the kernel (the timed step's) is reported."""
+    import collections
+    import csv
+
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        name = _short(r["Kernel_Name"])
+        if not name.startswith(kernel):
+            continue
+        per[(name, int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit(f"no dispatches of {kernel}")
+    key = max(per, key=lambda k: len(per[k].get("GRBM_GUI_ACTIVE", [])))
+    avg = {c: sum(v) / len(v) for c, v in per[key].items()}
+    gui = avg.get("GRBM_GUI_ACTIVE", float("nan")) / N_XCD  # cycles the GPU was active
+    mfma_frac = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * N_CU * gui)
+    lds_frac = avg.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(1.0, avg.get("SQ_LDS_IDX_ACTIVE", 0.0))
+    lines = [f"# counters per dispatch of {kernel}, workload {workload}",
+             f"# command: {command}",
+             f"# summarised by: python bench.py --summarize-counters <counter_collection.csv> --kernel {kernel}",
+             f"kernel = {key[0]} (most frequent grid: {key[1]} threads, "
+             f"{len(per[key].get('GRBM_GUI_ACTIVE', []))} dispatches)"]
+    lines += [f"  {c} = {avg[c]:.0f}" for c in COUNTERS if c in avg]
+    lines += [f"mfma_busy_frac = {mfma_frac:.4f}", f"lds_bank_conflict_frac = {lds_frac:.4f}",
+              f"mfma_flop_per_dispatch = {avg.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0.0) * 512:.4g}",
+              f"gpu_active_cycles_per_launch = {gui:.0f}",
+              f"sq_busy_cycles_per_launch = {avg.get('SQ_BUSY_CYCLES', 0.0):.0f}",
+              f"source_hash = {src}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip",), "attn_pair_kernel": ("mqa.hip",),
                   "attn_combine_kernel": ("mqa.hip",), "index_mfma_kernel": ("indexer.hip",),
                   "index_stream_kernel": ("indexer.hip",),
                   "index_mxfp4_kernel": ("indexer.hip",), "index_prefill_kernel": ("indexer.hip",),
                   "topk_kernel": ("topk.hip",),
                   "compress_kernel": ("compress.hip",)}
+
+
+# ============================================================================ runs
+
+
+def run_workload(key: str, steps: int, warmup: int, layers: int, reps: int):
+    """Build one workload, time `steps` whole steps (after `warmup`) and each stage alone.
+
+    Returns (workload, tokens/s, ms per step, per-stage figures, dominant-stage roofline)."""
+    import torch
+
+    wl = build_workload(key, layers)
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        wl.step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    value = wl.tokens / (ms_per_step * 1e-3)
+    log(f"[{key}] step {ms_per_step * 1e3:.1f} us ({wall / steps * 1e6:.1f} us wall) -> {value:,.0f} tokens/s")
+
+    if "_prime" in wl.stages:
+        wl.stages.pop("_prime").run(0)
+    torch.cuda.synchronize()
+    stage_out = {}
+    times = {}
+    for name, s in wl.stages.items():
+        t = time_stage(s.run, reps)
+        times[name] = t
+        gbs = s.bytes / t / 1e9
+        tfs = s.flops / t / 1e12
+        bound = "mfma" if s.flops / s.peak_flops > s.bytes / HBM_PEAK else "hbm"
+        stage_out[name] = dict(us=round(t * 1e6, 2), GBps=round(gbs, 1), TFLOPs=round(tfs, 2),
+                               hbm_frac=round(s.bytes / t / HBM_PEAK, 4),
+                               mfma_frac=round(s.flops / t / s.peak_flops, 4), bound=bound, kernel=s.kernel,
+                               algorithmic_bytes=int(s.bytes), algorithmic_flops=int(s.flops))
+        log(f"  {name:13s} {t * 1e6:9.2f} us  {gbs:8.1f} GB/s  {tfs:7.2f} TFLOP/s  ({bound}-bound)")
+    dom_name = max(wl.stages, key=lambda n: times[n])
+    dom = wl.stages[dom_name]
+    if stage_out[dom_name]["bound"] == "hbm":
+        achieved, peak, unit = dom.bytes / times[dom_name] / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = dom.flops / times[dom_name] / 1e12, dom.peak_flops / 1e12, "TFLOP/s"
+    kern = dom.kernel
+    traffic = read_traffic(f"{kern}_{wl.name}_pmc.txt", src_hash(*dom.src))
+    roofline = dict(kernel=kern, stage=dom_name, bound=stage_out[dom_name]["bound"], achieved=round(achieved, 2),
+                    peak=peak, unit=unit, frac=round(achieved / peak, 4), traffic=traffic,
+                    algorithmic_bytes=int(dom.bytes), algorithmic_flops=int(dom.flops),
+                    avg_launch_us=round(times[dom_name] * 1e6, 2))
+    counters = read_counters(f"{kern.split('+')[0]}_{wl.name}_counters.txt", src_hash(*dom.src))
+    if counters:
+        roofline["counters"] = counters
+    return wl, value, ms_per_step, stage_out, roofline
 
 
 # ============================================================================ main
@@ -534,16 +665,25 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="time only --config (not the other workloads)")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB device copy (PMC calibration)")
     ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write an HBM-traffic summary from two counter runs (no GPU work)")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="write an MFMA / LDS counter summary from one counter run (no GPU work)")
     ap.add_argument("--kernel", default="attn_dma_kernel")
     ap.add_argument("--profile-cmd", default="", help="command recorded in the summary")
     ap.add_argument("--out", help="summary file")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, args.profile_cmd, args.kernel)
+        return
+    if args.summarize_counters:
+        tag = WORKLOAD_TAGS[args.config]
+        out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{tag}_counters.txt")
+        summarize_counters(args.summarize_counters, args.kernel, src_hash(*KERNEL_SOURCES[args.kernel]), out,
+                           args.profile_cmd, tag)
         return
     if args.summarize_pmc:
         tag = WORKLOAD_TAGS[args.config]
@@ -570,53 +710,7 @@ def main():
     layers = args.layers if args.layers is not None else (4 if decode else 1)
     reps = args.stage_reps if args.stage_reps is not None else (20 if decode else 4)
 
-    wl = build_workload(args.config, layers)
-
-    # ---------------------------------------------------------------- timed steps
-    for i in range(warmup):
-        wl.step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record()
-    for i in range(steps):
-        wl.step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = e0.elapsed_time(e1) / steps
-    value = wl.tokens / (ms_per_step * 1e-3)
-    log(f"[{args.config}] step {ms_per_step * 1e3:.1f} us ({wall / steps * 1e6:.1f} us wall) -> {value:,.0f} tokens/s")
-
-    # ---------------------------------------------------------------- stages
-    if "_prime" in wl.stages:
-        wl.stages.pop("_prime").run(0)
-    torch.cuda.synchronize()
-    stage_out = {}
-    times = {}
-    for name, s in wl.stages.items():
-        t = time_stage(s.run, reps)
-        times[name] = t
-        gbs = s.bytes / t / 1e9
-        tfs = s.flops / t / 1e12
-        bound = "mfma" if s.flops / s.peak_flops > s.bytes / HBM_PEAK else "hbm"
-        stage_out[name] = dict(us=round(t * 1e6, 2), GBps=round(gbs, 1), TFLOPs=round(tfs, 2),
-                               hbm_frac=round(s.bytes / t / HBM_PEAK, 4),
-                               mfma_frac=round(s.flops / t / s.peak_flops, 4), bound=bound,
-                               algorithmic_bytes=int(s.bytes), algorithmic_flops=int(s.flops))
-        log(f"  {name:13s} {t * 1e6:9.2f} us  {gbs:8.1f} GB/s  {tfs:7.2f} TFLOP/s  ({bound}-bound)")
-    dom_name = max(wl.stages, key=lambda n: times[n])
-    dom = wl.stages[dom_name]
-    if stage_out[dom_name]["bound"] == "hbm":
-        achieved, peak, unit = dom.bytes / times[dom_name] / 1e9, HBM_PEAK / 1e9, "GB/s"
-    else:
-        achieved, peak, unit = dom.flops / times[dom_name] / 1e12, dom.peak_flops / 1e12, "TFLOP/s"
-    kern = dom.kernel
-    traffic = read_traffic(f"{kern}_{wl.name}_pmc.txt", src_hash(*dom.src))
-    roofline = dict(kernel=kern, stage=dom_name, bound=stage_out[dom_name]["bound"], achieved=round(achieved, 2),
-                    peak=peak, unit=unit, frac=round(achieved / peak, 4), traffic=traffic,
-                    algorithmic_bytes=int(dom.bytes), algorithmic_flops=int(dom.flops),
-                    avg_launch_us=round(times[dom_name] * 1e6, 2))
+    wl, value, ms_per_step, stage_out, roofline = run_workload(args.config, steps, warmup, layers, reps)
 
     if args.copy_probe:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB): the
@@ -653,6 +747,21 @@ def main():
     }
     if wl.build:
         line["cache_build_compress"] = wl.build
+    if not args.no_others:
+        # the other workloads at their full sizes, fewer steps each: their step rate,
+        # every stage's time and fraction of peak, and the dominant stage's roofline
+        others = {}
+        key0, tag0 = args.config, wl.name
+        del wl
+        for key in [k for k in ("1", "2", "3d", "3p", "4") if k != key0]:
+            torch.cuda.empty_cache()
+            dec = key in ("1", "3d", "4")
+            w2, v2, ms2, st2, rf2 = run_workload(key, 16 if dec else 3, 4 if dec else 1, 4 if dec else 1,
+                                                 10 if dec else 3)
+            others[WORKLOAD_TAGS[key]] = dict(value=round(v2, 1), unit="tokens/s", ms_per_step=round(ms2, 5),
+                                              build_compress=w2.build or None, roofline=rf2, stages=st2)
+            del w2
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 

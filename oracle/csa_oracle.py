@@ -73,13 +73,27 @@ def rope(x, pos, rope_dims: int, base: float) -> np.ndarray:
     return x
 
 
+# ---------------------------------------------------------------------- RMSNorm
+
+
+def rmsnorm(x, weight, eps: float) -> np.ndarray:
+    """RMSNorm over the last dim: x / sqrt(mean(x^2) + eps) * weight.
+
+    [V4-CN] §2.3.3 (query and KV normalization): before core attention every query
+    head and the single head of the compressed KV entries get an RMSNorm; the pages
+    name the learnable weights (trained with AdamW, §2.4) but not eps."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
 # --------------------------------------------------------------------- compress
 
 
 def compress(ca, cb, za, zb, *, ratio: int, overlap: bool, t0: int = 0,
              prev_cb=None, prev_zb=None, bias_a=None, bias_b=None,
              rope_dims: int = 0, rope_base: float = 10000.0, pos_offset: int = 0,
-             entries=None) -> np.ndarray:
+             entries=None, norm_weight=None, norm_eps: float = 1e-6) -> np.ndarray:
     """Compressed entries of one sequence.
 
     ca, za: [T, D] a-branch values / weights of tokens t0..t0+T-1 (for HCA, C and Z).
@@ -93,7 +107,8 @@ def compress(ca, cb, za, zb, *, ratio: int, overlap: bool, t0: int = 0,
       logits  = [Z^a rows of block I + B^a ; Z^b rows of block I-1 + B^b]  (per channel)
       weights = softmax of the logits over the positions (per channel)
       e       = sum(weights * [C^a rows of block I ; C^b rows of block I-1])
-    then RoPE on the last ``rope_dims`` dims at position pos_offset + ratio*I.
+    then (with ``norm_weight``) the entry's RMSNorm, then RoPE on the last ``rope_dims``
+    dims at position pos_offset + ratio*I.
     """
     ca = np.asarray(ca, dtype=np.float64)
     za = np.asarray(za, dtype=np.float64)
@@ -127,6 +142,8 @@ def compress(ca, cb, za, zb, *, ratio: int, overlap: bool, t0: int = 0,
         w = np.exp(lg - lg.max(axis=0, keepdims=True))
         w = w / w.sum(axis=0, keepdims=True)
         e = (w * v).sum(axis=0)
+        if norm_weight is not None:
+            e = rmsnorm(e, norm_weight, norm_eps)
         out.append(rope(e, pos_offset + ratio * I, rope_dims, rope_base))
     if not out:
         return np.zeros((0, D))
@@ -221,17 +238,24 @@ def window_positions(t: int, n_win: int) -> np.ndarray:
 
 
 def mqa(q, q_pos, kv, sel, win, win_pos0: int, n_win: int, sink, *, scale: float,
-        rope_dims: int, rope_base: float, pos_offset: int = 0) -> np.ndarray:
+        rope_dims: int, rope_base: float, pos_offset: int = 0, q_norm=None, kv_norm=None,
+        norm_eps: float = 1e-6) -> np.ndarray:
     """Shared-KV MQA of one sequence over selected entries plus the raw window.
 
     q [Tq, H, D] (not roped), q_pos [Tq], kv [N, D] compressed entries (already
     roped), sel [Tq, K] entry indices (-1 = unused slot), win [Tw, D] raw entries
     (not roped) for absolute positions win_pos0 .. win_pos0+Tw-1, sink [H].
+    With ``q_norm`` every query head, with ``kv_norm`` every raw window entry gets its
+    RMSNorm before RoPE (the compressed entries carry theirs from the compressor).
     Returns out [Tq, H, D].
     """
     q = np.asarray(q, dtype=np.float64)
     kv = np.asarray(kv, dtype=np.float64)
     win = np.asarray(win, dtype=np.float64)
+    if q_norm is not None:
+        q = rmsnorm(q, q_norm, norm_eps)
+    if kv_norm is not None:
+        win = rmsnorm(win, kv_norm, norm_eps)
     sink = np.asarray(sink, dtype=np.float64)
     Tq, H, D = q.shape
     out = np.zeros((Tq, H, D))
@@ -251,7 +275,7 @@ def mqa(q, q_pos, kv, sel, win, win_pos0: int, n_win: int, sink, *, scale: float
 
 def hca_dense(q, q_pos, kv, win, win_pos0: int, n_win: int, sink, *, ratio: int,
               scale: float, rope_dims: int, rope_base: float,
-              pos_offset: int = 0) -> np.ndarray:
+              pos_offset: int = 0, q_norm=None, kv_norm=None, norm_eps: float = 1e-6) -> np.ndarray:
     """HCA core attention: every visible compressed entry (i < floor(t/ratio)) + window."""
     N = np.asarray(kv).shape[0]
     Tq = np.asarray(q).shape[0]
@@ -260,7 +284,8 @@ def hca_dense(q, q_pos, kv, win, win_pos0: int, n_win: int, sink, *, ratio: int,
         v = visible_count(int(q_pos[t]), ratio, N)
         sel[t, :v] = np.arange(v)
     return mqa(q, q_pos, kv, sel, win, win_pos0, n_win, sink, scale=scale,
-               rope_dims=rope_dims, rope_base=rope_base, pos_offset=pos_offset)
+               rope_dims=rope_dims, rope_base=rope_base, pos_offset=pos_offset, q_norm=q_norm,
+               kv_norm=kv_norm, norm_eps=norm_eps)
 
 
 # ------------------------------------------------------------------ whole layer
@@ -276,28 +301,34 @@ def store(x, dtype: str) -> np.ndarray:
 
 
 def _window_keys(win, win_pos0: int, p: int, n_win: int, pos_offset: int, rope_dims: int,
-                 rope_base: float) -> np.ndarray:
-    """Raw tokens of the sliding window of the query at position p, each roped at its
-    own position ([V4-CN] §2.3.3: the last n_win uncompressed tokens, the query's own
-    included)."""
+                 rope_base: float, kv_norm=None, norm_eps: float = 1e-6) -> np.ndarray:
+    """Raw tokens of the sliding window of the query at position p, each (normalized
+    and) roped at its own position ([V4-CN] §2.3.3: the last n_win uncompressed tokens,
+    the query's own included)."""
     wpos = window_positions(p, n_win)
-    return rope(np.asarray(win, dtype=np.float64)[wpos - win_pos0], wpos + pos_offset, rope_dims, rope_base)
+    rows = np.asarray(win, dtype=np.float64)[wpos - win_pos0]
+    if kv_norm is not None:
+        rows = rmsnorm(rows, kv_norm, norm_eps)
+    return rope(rows, wpos + pos_offset, rope_dims, rope_base)
 
 
 def _query_output(q_t, p: int, entries, wkeys, sink, scale: float, rope_dims: int, rope_base: float,
-                  pos_offset: int) -> np.ndarray:
+                  pos_offset: int, q_norm=None, norm_eps: float = 1e-6) -> np.ndarray:
     """Core attention of one query token ([V4-CN] §2.3.1 shared-KV MQA, §2.3.3): the
     query heads are roped at p, attend to the compressed entries it uses followed by
     its window keys in one softmax with the sink term, and the result is rotated back
     by -p."""
     keys = np.concatenate([entries.reshape(-1, wkeys.shape[1]), wkeys], axis=0)
+    if q_norm is not None:
+        q_t = rmsnorm(q_t, q_norm, norm_eps)
     o = _attend_one(rope(q_t, p + pos_offset, rope_dims, rope_base), keys, sink, scale)
     return rope(o, -(p + pos_offset), rope_dims, rope_base)
 
 
 def csa_layer(streams, istreams, q, q_pos, qI, wI, win, win_pos0, sink, *,
               ratio: int, k: int, n_win: int, scale: float, rope_dims: int,
-              rope_base: float, pos_offset: int = 0, dtype: str = "f32"):
+              rope_base: float, pos_offset: int = 0, dtype: str = "f32", q_norm=None,
+              kv_norm=None, norm_eps: float = 1e-6):
     """One CSA layer forward of one sequence whose tokens start at position 0.
 
     From the definitions of [V4-CN] §2.3.1 and §2.3.3:
@@ -310,12 +341,15 @@ def csa_layer(streams, istreams, q, q_pos, qI, wI, win, win_pos0, sink, *,
       in one softmax with the sink term, and its output is rotated back by -t.
     streams = (Ca, Cb, Za, Zb) [T, D]; istreams = indexer-key streams [T, DI].
     Stage outputs are rounded to ``dtype`` where the device stores them
-    (compressed KV, compressed indexer keys, final output).
+    (compressed KV, compressed indexer keys, final output).  ``q_norm`` / ``kv_norm``:
+    RMSNorm weights of the query heads and of the KV entries (compressed and window),
+    [V4-CN] §2.3.3; None leaves them unnormalized.
     Returns dict(kv, ik, scores, idx, count, out).
     """
     Ca, Cb, Za, Zb = streams
     kv = store(compress(Ca, Cb, Za, Zb, ratio=ratio, overlap=True, rope_dims=rope_dims,
-                        rope_base=rope_base, pos_offset=pos_offset), dtype)
+                        rope_base=rope_base, pos_offset=pos_offset, norm_weight=kv_norm,
+                        norm_eps=norm_eps), dtype)
     ICa, ICb, IZa, IZb = istreams
     ik = store(compress(ICa, ICb, IZa, IZb, ratio=ratio, overlap=True), dtype)
     scores = index_scores(qI, wI, ik, q_pos, ratio)
@@ -325,14 +359,15 @@ def csa_layer(streams, istreams, q, q_pos, qI, wI, win, win_pos0, sink, *,
     for t in range(q.shape[0]):
         p = int(q_pos[t])
         chosen = idx[t, :cnt[t]]
-        wkeys = _window_keys(win, win_pos0, p, n_win, pos_offset, rope_dims, rope_base)
-        out[t] = _query_output(q[t], p, kv[chosen], wkeys, sink, scale, rope_dims, rope_base, pos_offset)
+        wkeys = _window_keys(win, win_pos0, p, n_win, pos_offset, rope_dims, rope_base, kv_norm, norm_eps)
+        out[t] = _query_output(q[t], p, kv[chosen], wkeys, sink, scale, rope_dims, rope_base, pos_offset,
+                               q_norm, norm_eps)
     return dict(kv=kv, ik=ik, scores=scores, idx=idx, count=cnt, out=store(out, dtype))
 
 
 def hca_layer(streams, q, q_pos, win, win_pos0, sink, *, ratio: int, n_win: int,
               scale: float, rope_dims: int, rope_base: float, pos_offset: int = 0,
-              dtype: str = "f32"):
+              dtype: str = "f32", q_norm=None, kv_norm=None, norm_eps: float = 1e-6):
     """One HCA layer forward of one sequence whose tokens start at position 0.
 
     From [V4-CN] §2.3.2 and §2.3.3: the entries are the non-overlapping compression of
@@ -343,12 +378,39 @@ def hca_layer(streams, q, q_pos, win, win_pos0, sink, *, ratio: int, n_win: int,
     """
     C, Z = streams
     kv = store(compress(C, None, Z, None, ratio=ratio, overlap=False, rope_dims=rope_dims,
-                        rope_base=rope_base, pos_offset=pos_offset), dtype)
+                        rope_base=rope_base, pos_offset=pos_offset, norm_weight=kv_norm,
+                        norm_eps=norm_eps), dtype)
     q = np.asarray(q, dtype=np.float64)
     out = np.zeros(q.shape)
     for t in range(q.shape[0]):
         p = int(q_pos[t])
         visible = kv[:visible_count(p, ratio, kv.shape[0])]
-        wkeys = _window_keys(win, win_pos0, p, n_win, pos_offset, rope_dims, rope_base)
-        out[t] = _query_output(q[t], p, visible, wkeys, sink, scale, rope_dims, rope_base, pos_offset)
+        wkeys = _window_keys(win, win_pos0, p, n_win, pos_offset, rope_dims, rope_base, kv_norm, norm_eps)
+        out[t] = _query_output(q[t], p, visible, wkeys, sink, scale, rope_dims, rope_base, pos_offset,
+                               q_norm, norm_eps)
     return dict(kv=kv, out=store(out, dtype))
+
+
+# ------------------------------------------------------ grouped output projection
+
+
+def grouped_out_proj(o, w_group, w_out, *, dtype: str = "f32") -> np.ndarray:
+    """Grouped output projection of one layer ([V4-CN] §2.3.1; group count g and
+    intermediate width d_g in §4.2.1).
+
+    o [T, n_h, c] core-attention outputs; w_group [g, d_g, (n_h / g) * c] and
+    w_out [d, g * d_g] weights as [out, in] matrices.  The n_h outputs of a token are
+    split into g groups of consecutive heads, group j is projected by w_group[j] to a
+    d_g-dim intermediate output, and the concatenated intermediates are projected by
+    w_out to d dims.  The intermediate is rounded to ``dtype`` where the device stores
+    it; returns [T, d] (not rounded).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    wg = np.asarray(w_group, dtype=np.float64)
+    wo = np.asarray(w_out, dtype=np.float64)
+    T, n_h, c = o.shape
+    g = wg.shape[0]
+    per = n_h // g
+    mid = np.concatenate([o[:, j * per:(j + 1) * per, :].reshape(T, per * c) @ wg[j].T for j in range(g)], axis=1)
+    mid = store(mid, dtype)
+    return mid @ wo.T

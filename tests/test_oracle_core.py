@@ -529,3 +529,121 @@ def test_csa_layer_scalar_brute_force():
     got = O.csa_layer(streams, istreams, q, pos, qI, wI, win, 0, sink, ratio=ratio, k=k, n_win=n_win, scale=scale,
                       rope_dims=R, rope_base=RB, dtype="f32")
     assert np.allclose(got["out"], O.store(want, "f32"), rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------- RMSNorm pins
+
+
+def test_rmsnorm_closed_forms_and_brute_force():
+    w = rng(60).standard_normal(12)
+    for c in (3.5, -0.25):
+        # a constant vector normalizes to its sign times the weight (eps = 0)
+        assert np.allclose(O.rmsnorm(np.full(12, c), w, 0.0), np.sign(c) * w, rtol=1e-14)
+    x = rng(61).standard_normal((4, 12))
+    y = O.rmsnorm(x, np.ones(12), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-14)          # unit RMS
+    assert np.allclose(O.rmsnorm(7.0 * x, w, 0.0), O.rmsnorm(x, w, 0.0), rtol=1e-13)  # scale invariance
+    onehot = np.zeros(12)
+    onehot[5] = 2.0
+    z = O.rmsnorm(x, onehot, 0.0)
+    assert np.all(z[:, np.arange(12) != 5] == 0) and np.all(z[:, 5] != 0)          # per-dim weight
+    eps = 1e-3
+    for r in range(4):
+        ms = sum(float(v) * float(v) for v in x[r]) / 12
+        want = [float(x[r, d]) / math.sqrt(ms + eps) * float(w[d]) for d in range(12)]
+        assert np.allclose(O.rmsnorm(x[r], w, eps), want, rtol=1e-13)
+
+
+def test_compress_with_norm_normalizes_before_rope():
+    r = rng(62)
+    T, D, R, ratio = 32, 16, 8, 4
+    v = r.standard_normal(D)
+    Cc = np.tile(v, (T, 1))
+    Zs = [r.standard_normal((T, D)) for _ in range(2)]
+    w = r.uniform(0.5, 1.5, D)
+    # constant rows: every entry is v, normalized; no RoPE gives the closed form
+    e = O.compress(Cc, Cc, Zs[0], Zs[1], ratio=ratio, overlap=True, rope_dims=0, norm_weight=w, norm_eps=1e-5)
+    want = v / math.sqrt(float(np.mean(v * v)) + 1e-5) * w
+    assert np.allclose(e, np.tile(want, (T // ratio, 1)), rtol=1e-12)
+    # with RoPE and unit weights (eps = 0) every entry has unit RMS: the norm comes
+    # first and the rotation keeps pair norms
+    C2 = [r.standard_normal((T, D)) for _ in range(2)]
+    e2 = O.compress(C2[0], C2[1], Zs[0], Zs[1], ratio=ratio, overlap=True, rope_dims=R, rope_base=RB,
+                    norm_weight=np.ones(D), norm_eps=0.0)
+    assert np.allclose(np.sqrt(np.mean(e2 * e2, axis=-1)), 1.0, rtol=1e-12)
+    # and equals RoPE of the normalized un-roped entries; with uneven weights the order
+    # matters (the weights of a rotated pair differ), and the norm comes first
+    e3 = O.compress(C2[0], C2[1], Zs[0], Zs[1], ratio=ratio, overlap=True, rope_dims=0)
+    pos = ratio * np.arange(T // ratio)
+    assert np.allclose(e2, O.rope(O.rmsnorm(e3, np.ones(D), 0.0), pos, R, RB), rtol=1e-12, atol=1e-14)
+    e4 = O.compress(C2[0], C2[1], Zs[0], Zs[1], ratio=ratio, overlap=True, rope_dims=R, rope_base=RB,
+                    norm_weight=w, norm_eps=1e-5)
+    assert np.allclose(e4, O.rope(O.rmsnorm(e3, w, 1e-5), pos, R, RB), rtol=1e-12, atol=1e-14)
+    assert not np.allclose(e4, O.rmsnorm(O.rope(e3, pos, R, RB), w, 1e-5), rtol=1e-6)
+
+
+def test_mqa_norms_make_output_scale_invariant():
+    q, pos, kv, sel, win, sink = _mqa_inputs(63)
+    D = q.shape[-1]
+    qn, kn = rng(64).uniform(0.5, 1.5, D), rng(65).uniform(0.5, 1.5, D)
+    kw = dict(scale=0.3, rope_dims=8, rope_base=RB, q_norm=qn, kv_norm=kn, norm_eps=0.0)
+    a = O.mqa(q, pos, kv, sel, win, 40, 6, sink, **kw)
+    b = O.mqa(5.0 * q, pos, kv, sel, 0.2 * win, 40, 6, sink, **kw)   # scaled queries and raw window rows
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+    c = O.mqa(5.0 * q, pos, kv, sel, win, 40, 6, sink, scale=0.3, rope_dims=8, rope_base=RB)
+    d = O.mqa(q, pos, kv, sel, win, 40, 6, sink, scale=0.3, rope_dims=8, rope_base=RB)
+    assert not np.allclose(c, d)   # without the norms the scale does matter
+
+
+def test_layer_norms_equal_normalized_inputs():
+    # the layer with KV norm = the layer without it on pre-normalized window rows and
+    # entries (checked through the cache it returns), and q norm = normalized queries
+    streams, istreams, q, pos, qI, wI, win, sink = _layer_inputs(66)
+    D = q.shape[-1]
+    qn, kn = rng(67).uniform(0.5, 1.5, D), rng(68).uniform(0.5, 1.5, D)
+    kw = dict(ratio=4, k=5, n_win=8, scale=1.0, rope_dims=8, rope_base=RB, dtype="f32")
+    a = O.csa_layer(streams, istreams, q, pos, qI, wI, win, 0, sink, q_norm=qn, kv_norm=kn, norm_eps=1e-6, **kw)
+    b = O.csa_layer(streams, istreams, O.rmsnorm(q, qn, 1e-6), pos, qI, wI, O.rmsnorm(win, kn, 1e-6), 0, sink, **kw)
+    e = O.compress(*streams, ratio=4, overlap=True, rope_dims=8, rope_base=RB, norm_weight=kn, norm_eps=1e-6)
+    assert np.allclose(a["kv"], O.store(e, "f32"))
+    assert np.array_equal(a["idx"], b["idx"])
+    # b's entries are not normalized: compare the attention over a's entries
+    o = O.mqa(O.rmsnorm(q, qn, 1e-6), pos, a["kv"], a["idx"], O.rmsnorm(win, kn, 1e-6), 0, 8, sink, scale=1.0,
+              rope_dims=8, rope_base=RB)
+    assert np.allclose(a["out"], O.store(o, "f32"), rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------- grouped output projection pins
+
+
+def test_grouped_out_proj_identity_groups_and_brute_force():
+    r = rng(70)
+    T, n_h, c, g = 3, 8, 4, 4
+    per = n_h // g
+    o = r.standard_normal((T, n_h, c))
+    # identity group weights and identity output weights give the flattened outputs
+    wg = np.stack([np.eye(per * c) for _ in range(g)])
+    assert np.allclose(O.grouped_out_proj(o, wg, np.eye(g * per * c), dtype="f32"),
+                       O.store(o.reshape(T, n_h * c), "f32"), rtol=0, atol=0)
+    # group j depends on heads j*per .. j*per+per-1 only
+    d_g, d = 5, 6
+    wg = r.standard_normal((g, d_g, per * c))
+    wo = r.standard_normal((d, g * d_g))
+    mid_only = O.grouped_out_proj(o, wg, np.eye(g * d_g), dtype="f32")
+    o2 = o.copy()
+    o2[:, per:2 * per] = 0.0
+    mid2 = O.grouped_out_proj(o2, wg, np.eye(g * d_g), dtype="f32")
+    assert np.all(mid2[:, d_g:2 * d_g] == 0) and np.array_equal(mid2[:, :d_g], mid_only[:, :d_g])
+    # scalar brute force
+    got = O.grouped_out_proj(o, wg, wo, dtype="f32")
+    for t in range(T):
+        mid = []
+        for j in range(g):
+            flat = [float(o[t, h, k]) for h in range(j * per, (j + 1) * per) for k in range(c)]
+            mid += [float(np.float32(sum(wg[j, i, m] * flat[m] for m in range(per * c)))) for i in range(d_g)]
+        want = [sum(wo[i, m] * mid[m] for m in range(g * d_g)) for i in range(d)]
+        assert np.allclose(got[t], want, rtol=1e-12, atol=1e-12)
+    # linear in the outputs
+    o3 = r.standard_normal((T, n_h, c))
+    lin = O.grouped_out_proj(2.0 * o - 3.0 * o3, wg, wo, dtype="f32")
+    assert np.allclose(lin, 2.0 * got - 3.0 * O.grouped_out_proj(o3, wg, wo, dtype="f32"), rtol=1e-5, atol=1e-5)

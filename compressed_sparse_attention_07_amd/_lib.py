@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(PKG, "libcsa.so")
 CSA_F32, CSA_BF16, CSA_FP8MIX, CSA_MXFP4 = 0, 1, 2, 3
 CSA_MODE_CSA, CSA_MODE_HCA = 0, 1
 CSA_FLAG_BF16_SCORES = 1
+CSA_FLAG_QKV_NORM = 2
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_DTYPE",
           4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_DEVICE", 6: "CSA_ERR_UNSUPPORTED"}
 
-EXPORTS = ["csa_abi_version", "csa_last_error", "csa_device_check", "csa_compress", "csa_quantize",
+EXPORTS = ["csa_abi_version", "csa_last_error", "csa_device_check", "csa_compress", "csa_compress_norm", "csa_rmsnorm",
+           "csa_grouped_out_proj_workspace_size", "csa_grouped_out_proj", "csa_quantize",
            "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_mqa_workspace_size",
            "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "csa_sparse_mqa_noalloc_limit", "hca_dense_attn_workspace_size",
            "hca_dense_attn",
@@ -47,7 +49,8 @@ class csa_layer_desc(C.Structure):
                 ("D", C.c_int32), ("H", C.c_int32), ("HI", C.c_int32), ("DI", C.c_int32),
                 ("ratio", C.c_int32), ("topk", C.c_int32), ("n_win", C.c_int32), ("rope_dims", C.c_int32),
                 ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("pos_offset", C.c_int64),
-                ("stream_dtype", C.c_int32), ("flags", C.c_int32)]
+                ("stream_dtype", C.c_int32), ("flags", C.c_int32), ("norm_eps", C.c_float),
+                ("reserved", C.c_int32)]
 
 
 class csa_forward_io(C.Structure):
@@ -57,7 +60,8 @@ class csa_forward_io(C.Structure):
                 ("ibias_a", C.c_void_p), ("ibias_b", C.c_void_p), ("iprev_cb", C.c_void_p), ("iprev_zb", C.c_void_p),
                 ("kv_cache", csa_buf), ("ik_cache", csa_buf), ("q", csa_buf), ("q_pos", C.c_void_p),
                 ("qI", csa_buf), ("wI", C.c_void_p), ("win", csa_buf), ("win_pos0", C.c_void_p),
-                ("sink", C.c_void_p), ("out", csa_buf), ("scores_out", C.c_void_p), ("idx_out", C.c_void_p)]
+                ("sink", C.c_void_p), ("out", csa_buf), ("scores_out", C.c_void_p), ("idx_out", C.c_void_p),
+                ("q_norm", C.c_void_p), ("kv_norm", C.c_void_p)]
 
 
 _lib = None
@@ -77,6 +81,12 @@ def lib():
         L.csa_device_check.restype = C.c_int
         L.csa_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, i32, i64, i32, f32, i64,
                                    bp, i64, vp]
+        L.csa_compress_norm.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, i32, i64, i32, f32,
+                                        i64, vp, f32, bp, i64, vp]
+        L.csa_rmsnorm.argtypes = [bp, i64, i32, vp, f32, bp, vp]
+        L.csa_grouped_out_proj_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+        L.csa_grouped_out_proj_workspace_size.restype = sz
+        L.csa_grouped_out_proj.argtypes = [bp, vp, vp, i64, i32, i32, i32, i32, i32, bp, vp, sz, vp]
         L.csa_quantize.argtypes = [vp, i64, i32, i32, bp, vp]
         L.csa_index_scores.argtypes = [bp, vp, bp, vp, i64, i64, i32, i32, i64, i64, i32, vp, vp]
         L.csa_topk_workspace_size.argtypes = [i64, i64, i32]
@@ -102,6 +112,7 @@ def lib():
         L.csa_forward.argtypes = [C.POINTER(csa_layer_desc), C.POINTER(csa_forward_io), vp, sz, vp]
         for name in EXPORTS:
             if name not in ("csa_topk_workspace_size", "csa_sparse_mqa_workspace_size", "csa_index_topk_workspace_size",
+                            "csa_grouped_out_proj_workspace_size",
                             "csa_sparse_mqa_noalloc_limit",
                             "hca_dense_attn_workspace_size", "csa_forward_workspace_size",
                             "csa_last_error", "csa_abi_version"):
@@ -215,6 +226,41 @@ def csa_compress(ca, cb, za, zb, out: Buf, *, ratio: int, overlap: bool, t0: int
     _invoke("csa_compress", ptr(ca), ptr(cb), ptr(za), ptr(zb), _dt(ca), ptr(bias_a), ptr(bias_b), ptr(prev_cb),
             ptr(prev_zb), B, T, D, ratio, 1 if overlap else 0, t0, rope_dims, rope_base, pos_offset, C.byref(bo),
             out_rows, stream_handle(stream))
+
+
+def csa_compress_norm(ca, cb, za, zb, out: Buf, *, ratio: int, overlap: bool, norm_weight, norm_eps: float = 1e-6,
+                      t0: int = 0, bias_a=None, bias_b=None, prev_cb=None, prev_zb=None, rope_dims: int = 0,
+                      rope_base: float = 10000.0, pos_offset: int = 0, stream=None) -> None:
+    B, T, D = ca.shape
+    out_rows = out.shape[1]
+    bo = out.c()
+    _invoke("csa_compress_norm", ptr(ca), ptr(cb), ptr(za), ptr(zb), _dt(ca), ptr(bias_a), ptr(bias_b), ptr(prev_cb),
+            ptr(prev_zb), B, T, D, ratio, 1 if overlap else 0, t0, rope_dims, rope_base, pos_offset,
+            ptr(norm_weight), norm_eps, C.byref(bo), out_rows, stream_handle(stream))
+
+
+def csa_rmsnorm(x, weight, out, *, eps: float = 1e-6, stream=None) -> None:
+    xb, ob = Buf.of(x), Buf.of(out)
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    cx, co = xb.c(), ob.c()
+    _invoke("csa_rmsnorm", C.byref(cx), rows, D, ptr(weight), eps, C.byref(co), stream_handle(stream))
+
+
+def csa_grouped_out_proj_workspace_size(T: int, n_h: int, c: int, g: int, d_g: int, d: int) -> int:
+    return lib().csa_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)
+
+
+def csa_grouped_out_proj(o, w_group, w_out, out, *, ws=None, stream=None) -> None:
+    """o [T, n_h, c] bf16; w_group [g, d_g, (n_h/g) c] bf16; w_out [d, g d_g] bf16; out [T, d]."""
+    T, n_h, c = o.shape
+    g, d_g, _ = w_group.shape
+    d = w_out.shape[0]
+    need = csa_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d)
+    w, wbytes = _ws(need, o.device, ws)
+    co, cout = Buf.of(o).c(), Buf.of(out).c()
+    _invoke("csa_grouped_out_proj", C.byref(co), ptr(w_group), ptr(w_out), T, n_h, c, g, d_g, d, C.byref(cout),
+            ptr(w), wbytes, stream_handle(stream), keep=(w,))
 
 
 def csa_quantize(x, out: Buf, *, rope_dims: int = 0, stream=None) -> None:

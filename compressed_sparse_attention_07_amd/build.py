@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip"]
+SOURCES = ["api.hip", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "proj.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950",

@@ -260,13 +260,15 @@ csa_status csa_device_check(void) {
   return s == CSA_OK ? ok() : s;
 }
 
-csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb, int32_t in_dtype,
-                        const float* bias_a, const float* bias_b, const void* prev_cb, const void* prev_zb,
-                        int64_t B, int64_t T, int32_t D, int32_t ratio, int32_t overlap, int64_t t0,
-                        int32_t rope_dims, float rope_base, int64_t pos_offset, const csa_buf* out,
-                        int64_t out_rows, void* stream) {
+csa_status csa_compress_norm(const void* ca, const void* cb, const void* za, const void* zb, int32_t in_dtype,
+                             const float* bias_a, const float* bias_b, const void* prev_cb, const void* prev_zb,
+                             int64_t B, int64_t T, int32_t D, int32_t ratio, int32_t overlap, int64_t t0,
+                             int32_t rope_dims, float rope_base, int64_t pos_offset, const float* norm_weight,
+                             float norm_eps, const csa_buf* out, int64_t out_rows, void* stream) {
   CSA_TRY(validate_compress(ca, cb, za, zb, in_dtype, bias_a, bias_b, prev_cb, prev_zb, B, T, D, ratio, overlap, t0,
                             rope_dims, rope_base, out, out_rows));
+  if (norm_weight && (!aligned16(norm_weight) || !(norm_eps >= 0.f) || !std::isfinite(norm_eps)))
+    return fail(CSA_ERR_SHAPE, "norm_weight must be 16-byte aligned and norm_eps finite and >= 0");
   CSA_TRY(check_device());
   CompressLaunch L{};
   L.ca = ca;
@@ -289,7 +291,77 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
   L.pos_offset = pos_offset;
   L.out = *out;
   L.out_rows = out_rows;
+  L.norm_w = norm_weight;
+  L.norm_eps = norm_eps;
   return launched(launch_compress(L, static_cast<hipStream_t>(stream)), "csa_compress");
+}
+
+csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb, int32_t in_dtype,
+                        const float* bias_a, const float* bias_b, const void* prev_cb, const void* prev_zb,
+                        int64_t B, int64_t T, int32_t D, int32_t ratio, int32_t overlap, int64_t t0,
+                        int32_t rope_dims, float rope_base, int64_t pos_offset, const csa_buf* out,
+                        int64_t out_rows, void* stream) {
+  return csa_compress_norm(ca, cb, za, zb, in_dtype, bias_a, bias_b, prev_cb, prev_zb, B, T, D, ratio, overlap, t0,
+                           rope_dims, rope_base, pos_offset, nullptr, 0.f, out, out_rows, stream);
+}
+
+csa_status csa_rmsnorm(const csa_buf* x, int64_t rows, int32_t D, const float* weight, float eps,
+                       const csa_buf* out, void* stream) {
+  if (!x || !out) return fail(CSA_ERR_NULL, "x and out are required");
+  if (!weight) return fail(CSA_ERR_NULL, "weight is required");
+  if (x->dtype != out->dtype || (x->dtype != CSA_F32 && x->dtype != CSA_BF16))
+    return fail(CSA_ERR_DTYPE, "x and out must share a dtype, F32 or BF16");
+  if (rows < 0) return fail(CSA_ERR_SHAPE, "rows < 0");
+  if (D < 8 || D > 2048 || D % 8) return fail(CSA_ERR_SHAPE, "D=%d must be a multiple of 8 in [8, 2048]", D);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(CSA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (rows == 0) return ok();  // no rows: the buffers may be empty (NULL)
+  CSA_TRY(check_buf(x, "x"));
+  CSA_TRY(check_buf(out, "out"));
+  if (!aligned16(x->data) || !aligned16(out->data)) return fail(CSA_ERR_SHAPE, "x and out must be 16-byte aligned");
+  CSA_TRY(check_device());
+  return launched(launch_rmsnorm(*x, rows, D, weight, eps, *out, static_cast<hipStream_t>(stream)), "csa_rmsnorm");
+}
+
+size_t csa_grouped_out_proj_workspace_size(int64_t T, int32_t n_h, int32_t c, int32_t g, int32_t d_g, int32_t d) {
+  if (T < 0 || n_h < 1 || c < 1 || g < 1 || d_g < 1 || d < 1 || n_h % g) return 0;
+  return grouped_out_proj_workspace_bytes(T, n_h, c, g, d_g, d);
+}
+
+csa_status csa_grouped_out_proj(const csa_buf* o, const void* w_group, const void* w_out, int64_t T, int32_t n_h,
+                                int32_t c, int32_t g, int32_t d_g, int32_t d, const csa_buf* out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!o || !out) return fail(CSA_ERR_NULL, "o and out are required");
+  if (!w_group || !w_out) return fail(CSA_ERR_NULL, "w_group and w_out are required");
+  if (o->dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "o must be BF16");
+  if (out->dtype != CSA_BF16 && out->dtype != CSA_F32) return fail(CSA_ERR_DTYPE, "out must be BF16 or F32");
+  if (T < 0 || n_h < 1 || c < 1 || g < 1 || d_g < 1 || d < 1 || n_h % g || g > 1024)
+    return fail(CSA_ERR_SHAPE, "sizes must be positive and g (<= 1024) must divide n_h");
+  if ((static_cast<int64_t>(n_h / g) * c) % 32 || (static_cast<int64_t>(g) * d_g) % 32)
+    return fail(CSA_ERR_UNSUPPORTED, "(n_h / g) * c and g * d_g must be multiples of 32");
+  if (T > (int64_t(1) << 22)) return fail(CSA_ERR_SHAPE, "T=%lld above 2^22", static_cast<long long>(T));
+  if (!aligned16(w_group) || !aligned16(w_out)) return fail(CSA_ERR_SHAPE, "the weights must be 16-byte aligned");
+  if (T == 0) return ok();  // no rows: o and out may be empty (NULL)
+  CSA_TRY(check_buf(o, "o"));
+  CSA_TRY(check_buf(out, "out"));
+  if (!ws || !aligned16(ws)) return fail(CSA_ERR_WORKSPACE, "workspace required, 16-byte aligned");
+  const size_t need = csa_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "csa_grouped_out_proj needs %zu workspace bytes, got %zu", need, ws_bytes);
+  CSA_TRY(check_device());
+  GroupedProjLaunch L{};
+  L.o = o->data;
+  L.w_group = w_group;
+  L.w_out = w_out;
+  L.mid = ws;
+  L.out = out->data;
+  L.T = T;
+  L.n_h = n_h;
+  L.c = c;
+  L.g = g;
+  L.d_g = d_g;
+  L.d = d;
+  L.out_f32 = out->dtype == CSA_F32;
+  return launched(launch_grouped_out_proj(L, static_cast<hipStream_t>(stream)), "csa_grouped_out_proj");
 }
 
 csa_status csa_quantize(const float* x, int64_t rows, int32_t D, int32_t rope_dims, const csa_buf* out,
@@ -532,7 +604,9 @@ namespace {
 struct FwdPlan {
   int64_t N;
   IdxTopkPlan it;  // CSA: indexer + top-k
-  size_t scores_off, idx_off, idx_bytes, attn_off, attn_bytes, total;
+  size_t scores_off, idx_off, idx_bytes, attn_off, attn_bytes;
+  size_t nq_off, nq_bytes, nw_off, nw_bytes;  // CSA_FLAG_QKV_NORM: normalized query / window copies
+  size_t total;
 };
 
 // The indexer launch of a forward (device pointers are filled in by csa_forward)
@@ -552,8 +626,9 @@ IndexLaunch index_launch(const csa_layer_desc* L, int32_t qI_dtype) {
 }
 
 // qI_dtype: the indexer's operand format (the plan depends on it); -1 for a size query
-// without the operands, which covers either plan
-FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx, int32_t qI_dtype) {
+// without the operands, which covers either plan (and F32 query / window copies)
+FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx, int32_t qI_dtype, int32_t q_dtype = -1,
+                     int32_t win_dtype = -1) {
   FwdPlan p{};
   p.N = (L->t0 + L->T) / L->ratio;
   size_t off = 0;
@@ -570,6 +645,15 @@ FwdPlan plan_forward(const csa_layer_desc* L, bool have_scores, bool have_idx, i
   }
   p.attn_off = off;
   off += p.attn_bytes;
+  if (L->flags & CSA_FLAG_QKV_NORM) {
+    const size_t qe = q_dtype == CSA_BF16 ? 2 : 4, we = win_dtype == CSA_BF16 ? 2 : 4;
+    p.nq_bytes = align256(static_cast<size_t>(L->B * L->Tq * L->H) * L->D * qe);
+    p.nq_off = off;
+    off += p.nq_bytes;
+    p.nw_bytes = align256(static_cast<size_t>(L->B * L->Tw) * L->D * we);
+    p.nw_off = off;
+    off += p.nw_bytes;
+  }
   p.total = off;
   return p;
 }
@@ -584,7 +668,10 @@ csa_status validate_desc(const csa_layer_desc* L) {
   if (L->T % L->ratio || L->t0 % L->ratio) return fail(CSA_ERR_SHAPE, "T and t0 must be multiples of ratio");
   if (L->cache_rows < (L->t0 + L->T) / L->ratio) return fail(CSA_ERR_SHAPE, "cache_rows < (t0+T)/ratio");
   if (L->mode == CSA_MODE_CSA && (L->topk < 1 || L->topk > 4096)) return fail(CSA_ERR_SHAPE, "topk out of [1, 4096]");
-  if (L->flags & ~CSA_FLAG_BF16_SCORES) return fail(CSA_ERR_SHAPE, "unknown flags 0x%x", L->flags);
+  if (L->flags & ~(CSA_FLAG_BF16_SCORES | CSA_FLAG_QKV_NORM)) return fail(CSA_ERR_SHAPE, "unknown flags 0x%x", L->flags);
+  if ((L->flags & CSA_FLAG_QKV_NORM) && (!(L->norm_eps >= 0.f) || !std::isfinite(L->norm_eps)))
+    return fail(CSA_ERR_SHAPE, "norm_eps must be finite and >= 0");
+  if (L->reserved != 0) return fail(CSA_ERR_SHAPE, "csa_layer_desc.reserved must be 0");
   return CSA_OK;
 }
 
@@ -627,8 +714,17 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
         ((reinterpret_cast<uintptr_t>(io->qI.scale) | reinterpret_cast<uintptr_t>(io->ik_cache.scale)) & 3))
       return fail(CSA_ERR_SHAPE, "MXFP4 scale planes must be 4-byte aligned");
   }
+  const bool qkv_norm = (L->flags & CSA_FLAG_QKV_NORM) != 0;
+  if (qkv_norm) {
+    if (!io->q_norm || !io->kv_norm) return fail(CSA_ERR_NULL, "CSA_FLAG_QKV_NORM needs q_norm and kv_norm");
+    if (!aligned16(io->q_norm) || !aligned16(io->kv_norm))
+      return fail(CSA_ERR_SHAPE, "q_norm and kv_norm must be 16-byte aligned");
+    if ((io->q.dtype != CSA_F32 && io->q.dtype != CSA_BF16) || (io->win.dtype != CSA_F32 && io->win.dtype != CSA_BF16))
+      return fail(CSA_ERR_UNSUPPORTED, "CSA_FLAG_QKV_NORM takes F32 or BF16 queries and window rows");
+    if (L->D % 8 || L->D > 2048) return fail(CSA_ERR_UNSUPPORTED, "CSA_FLAG_QKV_NORM needs D %% 8 == 0, D <= 2048");
+  }
   const FwdPlan P = plan_forward(L, io->scores_out != nullptr, io->idx_out != nullptr,
-                                 csa_mode ? io->qI.dtype : CSA_BF16);
+                                 csa_mode ? io->qI.dtype : CSA_BF16, io->q.dtype, io->win.dtype);
   if (P.total > 0 && (!ws || ws_bytes < P.total))
     return fail(CSA_ERR_WORKSPACE, "csa_forward needs %zu workspace bytes, got %zu", P.total, ws_bytes);
   CSA_TRY(check_device());
@@ -658,8 +754,11 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     C.pos_offset = L->pos_offset;
     C.out = io->kv_cache;
     C.out_rows = L->cache_rows;
+    C.norm_w = qkv_norm ? io->kv_norm : nullptr;
+    C.norm_eps = L->norm_eps;
     if (csa_mode) {
       CompressLaunch I = C;
+      I.norm_w = nullptr;
       I.ca = io->ica;
       I.cb = io->icb;
       I.za = io->iza;
@@ -676,6 +775,15 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
       return launched(-1, "csa_forward/compress");
     }
   }
+  // the attention operands: the caller's query and window, or their normalized copies
+  csa_buf q = io->q, win = io->win;
+  if (qkv_norm) {
+    q.data = w + P.nq_off;
+    win.data = w + P.nw_off;
+    const int rc = launch_attn_norm(io->q, q, io->q_norm, io->win, win, io->kv_norm, io->q_pos, io->win_pos0, L->B,
+                                    L->Tq, L->Tw, L->H, L->D, L->n_win, L->norm_eps, s);
+    if (rc != 0) return launched(rc, "csa_forward/qkv_norm");
+  }
   if (csa_mode) {
     int32_t* idx = io->idx_out ? io->idx_out : reinterpret_cast<int32_t*>(w + P.idx_off);
     IndexLaunch X = index_launch(L, io->qI.dtype);
@@ -686,12 +794,12 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     const char* stage = "";
     const int rc = run_index_topk(X, L->topk, P.it, idx, nullptr, io->scores_out, w + P.scores_off, s, &stage);
     if (rc != 0) return launched(rc, stage);
-    AttnLaunch A = make_attn(&io->q, io->q_pos, &io->kv_cache, L->cache_rows, 1, idx, L->topk, 1, &io->win, io->win_pos0,
+    AttnLaunch A = make_attn(&q, io->q_pos, &io->kv_cache, L->cache_rows, 1, idx, L->topk, 1, &win, io->win_pos0,
                              L->Tw, io->sink, L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset, L->B, L->Tq,
                              L->H, L->D, N, L->n_win, &io->out);
     return launched(launch_attn(A, w + P.attn_off, P.attn_bytes, s), "csa_forward/sparse_mqa");
   }
-  AttnLaunch A = make_attn(&io->q, io->q_pos, &io->kv_cache, L->cache_rows, 0, nullptr, 0, L->ratio, &io->win,
+  AttnLaunch A = make_attn(&q, io->q_pos, &io->kv_cache, L->cache_rows, 0, nullptr, 0, L->ratio, &win,
                            io->win_pos0, L->Tw, io->sink, L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset,
                            L->B, L->Tq, L->H, L->D, N, L->n_win, &io->out);
   return launched(launch_attn(A, w + P.attn_off, P.attn_bytes, s), "csa_forward/hca_dense_attn");

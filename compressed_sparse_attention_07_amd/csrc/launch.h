@@ -21,6 +21,8 @@ struct CompressLaunch {
   int64_t pos_offset;
   csa_buf out;
   int64_t out_rows;
+  const float* norm_w;  // RMSNorm weight [D] applied to each entry before RoPE, or NULL
+  float norm_eps;
 };
 int launch_compress(const CompressLaunch& L, hipStream_t stream);
 // two compressions sharing the stream dtype (KV and indexer keys) in one launch
@@ -55,6 +57,28 @@ int launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int64_t ro
 size_t topk_workspace_bytes(int64_t rows, int64_t N, int k);
 int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count,
                 void* ws, hipStream_t stream);
+
+struct GroupedProjLaunch {
+  const void* o;        // bf16 [T, n_h, c]
+  const void* w_group;  // bf16 [g, d_g, (n_h / g) c]
+  const void* w_out;    // bf16 [d, g d_g]
+  void* mid;            // workspace: bf16 [T, g d_g], then fp32 split partials
+  void* out;            // [T, d], bf16 or f32
+  int64_t T, n_h, c, g, d_g, d;
+  int out_f32;
+};
+size_t grouped_out_proj_workspace_bytes(int64_t T, int64_t n_h, int64_t c, int64_t g, int64_t d_g, int64_t d);
+int launch_grouped_out_proj(const GroupedProjLaunch& L, hipStream_t stream);
+
+// Row-wise RMSNorm: y = x / sqrt(mean(x^2) + eps) * w, rows of D in F32 or BF16
+int launch_rmsnorm(const csa_buf& x, int64_t rows, int D, const float* w, float eps, const csa_buf& y,
+                   hipStream_t stream);
+// One launch normalizing the query heads [B*Tq*H, D] into q_out and, per sequence, the
+// window rows its queries see into the same rows of win_out ([B, Tw, D]); other rows
+// of win_out are not written.
+int launch_attn_norm(const csa_buf& q, const csa_buf& q_out, const float* q_w, const csa_buf& win,
+                     const csa_buf& win_out, const float* kv_w, const int64_t* q_pos, const int64_t* win_pos0,
+                     int64_t B, int64_t Tq, int64_t Tw, int H, int D, int n_win, float eps, hipStream_t stream);
 
 struct AttnLaunch {
   csa_buf q;

@@ -1,0 +1,212 @@
+// Grouped output projection ([V4-CN] "DeepSeek-V4中文翻译" §2.3.1: the n_h core-attention
+// outputs of a token are split into g groups, each projected to a d_g-dim intermediate
+// output, and the intermediates are projected to the model dim d; §4.2.1 gives g = 16,
+// d_g = 1024, d = 7168 for V4-Pro).  Two launches of one bf16 GEMM:
+//   mid[t, j d_g + i] = sum_k o[t, j K + k] w_group[j, i, k]   (K = (n_h / g) c; batch j)
+//   out[t, i]        = sum_k mid[t, k] w_out[i, k]            (K = g d_g)
+// Weights are [out, in] matrices, so both operands of C = A W^T are contiguous along
+// the contraction and load straight into the MFMA operand layout: lane (col, grp)
+// holds 8 consecutive k of row col (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// Each wave computes a 16 x 64 block of C (four 16 x 16 MFMA accumulators) over its
+// range of the contraction, its operands loaded from global memory two k-steps ahead
+// of the products.  A workgroup of four waves covers WM x 16 rows and WN x 64 columns
+// (WM WN = 4): a few rows (decode) take 16 x 256 tiles, so every weight row is read by
+// one wave only and the weights stream from HBM once; many rows take 64 x 64 tiles,
+// whose four waves share each weight fragment through the L1 cache.  With a few rows
+// the tiles alone cannot fill the chip, so the contraction is split over workgroups:
+// each writes an fp32 partial tile and a second pass sums the partials in split order
+// (deterministic), converting to the output format.
+#include "device_common.h"
+#include "launch.h"
+
+#include <algorithm>
+
+namespace csa {
+
+namespace {
+
+struct GemmArgs {
+  const uint16_t* A;  // [batch][M, K] rows at stride lda, batch stride sa
+  const uint16_t* W;  // [batch][N, K] rows at stride K, batch stride sw
+  void* C;            // [batch][M, N] rows at stride ldc, batch stride sc
+  int64_t M, N, K, lda, ldc, sa, sw, sc;
+  int out_f32;
+  int64_t batch;
+  int ksplit;         // contraction split over workgroups (1: no split)
+  int steps_per_split;
+  float* part;        // ksplit > 1: fp32 partials [ksplit][batch][M][N]
+};
+
+constexpr int kKStep = 32;
+constexpr int kAhead = 2;  // k-steps loaded ahead of the products
+constexpr int kFewRows = 32;          // at most this many rows: 16 x 256 tiles
+constexpr int kTargetGroups = 1024;   // workgroups a split launch aims for
+constexpr int kMinSplitSteps = 8;     // k-steps per split at least
+
+template <int WM, int WN>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+  static_assert(WM * WN == 4, "four waves");
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t batch = blockIdx.z / a.ksplit;
+  const int split = blockIdx.z % a.ksplit;
+  const int64_t m0 = (static_cast<int64_t>(blockIdx.y) * WM + wid / WN) * 16;
+  const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * WN + wid % WN) * 64;
+  if (m0 >= a.M || n0 >= a.N) return;  // a whole wave outside C (no barrier below)
+  // operand rows, clamped into C's extent (rows past it are computed and not stored)
+  const int64_t am = min(m0 + col, a.M - 1);
+  const uint16_t* ap = a.A + batch * a.sa + am * a.lda + 8 * grp;
+  const uint16_t* wp[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    wp[nb] = a.W + batch * a.sw + min(n0 + 16 * nb + col, a.N - 1) * a.K + 8 * grp;
+  const int s_begin = split * a.steps_per_split;
+  const int nsteps = min(static_cast<int>(a.K / kKStep) - s_begin, a.steps_per_split);
+  ap += static_cast<int64_t>(s_begin) * kKStep;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) wp[nb] += static_cast<int64_t>(s_begin) * kKStep;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 af[kAhead + 1], wf[kAhead + 1][4];
+  auto load = [&](int slot, int s) {
+    af[slot] = *reinterpret_cast<const bf16x8*>(ap + static_cast<int64_t>(s) * kKStep);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) wf[slot][nb] = *reinterpret_cast<const bf16x8*>(wp[nb] + static_cast<int64_t>(s) * kKStep);
+  };
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s)
+    if (s < nsteps) load(s, s);
+  for (int s0 = 0; s0 < nsteps; s0 += kAhead + 1) {
+#pragma unroll
+    for (int u = 0; u <= kAhead; ++u) {
+      const int s = s0 + u;
+      if (s >= nsteps) break;
+      if (s + kAhead < nsteps) load((u + kAhead) % (kAhead + 1), s + kAhead);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u], wf[u][nb], acc[nb], 0, 0, 0);
+    }
+  }
+  // lane (col, grp) holds C[m0 + 4 grp + r][n0 + 16 nb + col]
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t n = n0 + 16 * nb + col;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + 4 * grp + r;
+      if (m >= a.M) continue;
+      if (a.ksplit > 1) {
+        a.part[((split * a.batch + batch) * a.M + m) * a.N + n] = acc[nb][r];
+        continue;
+      }
+      const int64_t o = batch * a.sc + m * a.ldc + n;
+      if (a.out_f32) static_cast<float*>(a.C)[o] = acc[nb][r];
+      else static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(acc[nb][r]);
+    }
+  }
+}
+
+// sums the ksplit partials of every C element in split order
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per = a.M * a.N;
+  if (e >= a.batch * per) return;
+  float acc = 0.f;
+  for (int s = 0; s < a.ksplit; ++s) acc += a.part[s * a.batch * per + e];
+  const int64_t batch = e / per, m = (e % per) / a.N, n = e % a.N;
+  const int64_t o = batch * a.sc + m * a.ldc + n;
+  if (a.out_f32) static_cast<float*>(a.C)[o] = acc;
+  else static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(acc);
+}
+
+// contraction splits of a GEMM (1 unless few rows leave the chip underfilled)
+int gemm_splits(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  if (M > kFewRows || M == 0) return 1;
+  const int64_t tiles = ((N + 255) / 256) * ((M + 15) / 16) * batch;
+  const int64_t steps = K / kKStep;
+  int64_t s = (kTargetGroups + tiles - 1) / tiles;
+  s = std::min(s, steps / kMinSplitSteps);
+  return static_cast<int>(std::max<int64_t>(s, 1));
+}
+
+size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
+  const int s = gemm_splits(M, N, K, batch);
+  return s > 1 ? static_cast<size_t>(s) * batch * M * N * sizeof(float) : 0;
+}
+
+int launch_gemm(GemmArgs a, int64_t batch, float* part, hipStream_t stream) {
+  if (a.M == 0 || a.N == 0 || batch == 0) return 0;
+  if (a.K % kKStep) return -2;
+  const int steps = static_cast<int>(a.K / kKStep);
+  a.batch = batch;
+  a.ksplit = gemm_splits(a.M, a.N, a.K, batch);
+  a.steps_per_split = (steps + a.ksplit - 1) / a.ksplit;
+  a.ksplit = (steps + a.steps_per_split - 1) / a.steps_per_split;  // no empty split
+  a.part = part;
+  if (a.ksplit > 1 && !part) return -2;
+  const uint32_t gz = static_cast<uint32_t>(batch * a.ksplit);
+  if (a.M <= kFewRows) {  // few rows: 16 x 256 tiles, each weight row read once
+    const dim3 g(static_cast<uint32_t>((a.N + 255) / 256), static_cast<uint32_t>((a.M + 15) / 16), gz);
+    hipLaunchKernelGGL((gemm_bf16_kernel<1, 4>), g, dim3(256), 0, stream, a);
+  } else {
+    const dim3 g(static_cast<uint32_t>((a.N + 63) / 64), static_cast<uint32_t>((a.M + 63) / 64), gz);
+    hipLaunchKernelGGL((gemm_bf16_kernel<4, 1>), g, dim3(256), 0, stream, a);
+  }
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (a.ksplit > 1) {
+    const int64_t n = batch * a.M * a.N;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+size_t grouped_out_proj_workspace_bytes(int64_t T, int64_t n_h, int64_t c, int64_t g, int64_t d_g, int64_t d) {
+  const size_t mid = (static_cast<size_t>(T) * g * d_g * sizeof(uint16_t) + 255) & ~static_cast<size_t>(255);
+  const size_t part = std::max(gemm_part_bytes(T, d_g, (n_h / g) * c, g), gemm_part_bytes(T, d, g * d_g, 1));
+  return mid + part;
+}
+
+int launch_grouped_out_proj(const GroupedProjLaunch& L, hipStream_t stream) {
+  if (L.T == 0) return 0;
+  const size_t mid_bytes = (static_cast<size_t>(L.T) * L.g * L.d_g * sizeof(uint16_t) + 255) & ~static_cast<size_t>(255);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(L.mid) + mid_bytes);
+  const int64_t per = L.n_h / L.g;
+  const int64_t K1 = per * L.c;
+  GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(L.o);
+  a.W = static_cast<const uint16_t*>(L.w_group);
+  a.C = L.mid;
+  a.M = L.T;
+  a.N = L.d_g;
+  a.K = K1;
+  a.lda = L.n_h * L.c;
+  a.ldc = L.g * L.d_g;
+  a.sa = K1;
+  a.sw = L.d_g * K1;
+  a.sc = L.d_g;
+  a.out_f32 = 0;
+  int rc = launch_gemm(a, L.g, part, stream);
+  if (rc != 0) return rc;
+  GemmArgs b{};
+  b.A = static_cast<const uint16_t*>(L.mid);
+  b.W = static_cast<const uint16_t*>(L.w_out);
+  b.C = L.out;
+  b.M = L.T;
+  b.N = L.d;
+  b.K = L.g * L.d_g;
+  b.lda = b.K;
+  b.ldc = L.d;
+  b.out_f32 = L.out_f32;
+  return launch_gemm(b, 1, part, stream);
+}
+
+}  // namespace csa

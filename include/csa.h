@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -79,6 +79,13 @@ typedef enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8MIX = 2, CSA_MXFP4 = 
  * then exact on the fp32 scores.
  */
 #define CSA_FLAG_BF16_SCORES 1
+/*
+ * CSA_FLAG_QKV_NORM (csa_forward only): RMSNorm the query heads and the KV before
+ * core attention ([V4-CN] §2.3.3): every compressed KV entry is normalized with
+ * io->kv_norm before its RoPE, every raw window row with io->kv_norm, every query
+ * head with io->q_norm, all with desc->norm_eps.  The indexer path is unchanged.
+ */
+#define CSA_FLAG_QKV_NORM 2
 
 typedef struct csa_buf {
   void* data;
@@ -124,6 +131,57 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
                         int32_t D, int32_t ratio, int32_t overlap, int64_t t0,
                         int32_t rope_dims, float rope_base, int64_t pos_offset,
                         const csa_buf* out, int64_t out_rows, void* stream);
+
+/*
+ * csa_compress_norm -- csa_compress with an RMSNorm of every entry before its RoPE
+ * ([V4-CN] §2.3.3: KV entries are normalized ahead of core attention):
+ *     e <- e / sqrt(mean_d(e_d^2) + norm_eps) * norm_weight      (fp32)
+ * norm_weight: float [D] (16-byte aligned) or NULL (then identical to csa_compress);
+ * norm_eps finite, >= 0.  Other arguments and limits as csa_compress.
+ */
+csa_status csa_compress_norm(const void* ca, const void* cb, const void* za, const void* zb,
+                             int32_t in_dtype, const float* bias_a, const float* bias_b,
+                             const void* prev_cb, const void* prev_zb, int64_t B, int64_t T,
+                             int32_t D, int32_t ratio, int32_t overlap, int64_t t0,
+                             int32_t rope_dims, float rope_base, int64_t pos_offset,
+                             const float* norm_weight, float norm_eps, const csa_buf* out,
+                             int64_t out_rows, void* stream);
+
+/*
+ * csa_rmsnorm -- row-wise RMSNorm ([V4-CN] §2.3.3: query heads and KV entries are
+ * normalized before core attention):
+ *     out[r, d] = x[r, d] / sqrt(mean_j(x[r, j]^2) + eps) * weight[d]
+ * computed in fp32 and stored in out's dtype.
+ *   x, out   [rows, D], both F32 or both BF16, 16-byte aligned; may alias exactly
+ *   weight   float [D]
+ * Limits: 8 <= D <= 2048, D % 8 == 0; eps finite, >= 0.  rows = 0 is a no-op.
+ */
+csa_status csa_rmsnorm(const csa_buf* x, int64_t rows, int32_t D, const float* weight,
+                       float eps, const csa_buf* out, void* stream);
+
+/*
+ * csa_grouped_out_proj -- grouped output projection ([V4-CN] §2.3.1 output
+ * projection; g groups of intermediate width d_g, §4.2.1):
+ *     mid[t, j*d_g + e] = sum_i o[t, j*(n_h/g)*c + i] * w_group[j, e, i]   j < g
+ *     out[t, f]         = sum_e mid[t, e] * w_out[f, e]
+ * bf16 operands, fp32 accumulation; mid is stored in bf16 (workspace) between the
+ * two products.  With few rows the contraction is split across workgroups and the
+ * fp32 partials are summed in a fixed order, so results are deterministic.
+ *   o        bf16 [T, n_h, c] (the core-attention output of every head; 16-byte aligned)
+ *   w_group  bf16 [g, d_g, (n_h/g)*c]   (each group's projection, [out, in])
+ *   w_out    bf16 [d, g*d_g]            ([out, in])
+ *   out      [T, d], BF16 or F32
+ *   ws       csa_grouped_out_proj_workspace_size(T, n_h, c, g, d_g, d) bytes, 16-byte
+ *            aligned
+ * Limits: g divides n_h; (n_h/g)*c and g*d_g multiples of 32; T <= 2^22.  T = 0 is a
+ * no-op.
+ */
+size_t csa_grouped_out_proj_workspace_size(int64_t T, int32_t n_h, int32_t c, int32_t g,
+                                           int32_t d_g, int32_t d);
+csa_status csa_grouped_out_proj(const csa_buf* o, const void* w_group, const void* w_out,
+                                int64_t T, int32_t n_h, int32_t c, int32_t g, int32_t d_g,
+                                int32_t d, const csa_buf* out, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * csa_quantize -- store fp32 rows [rows, D] in another storage format
@@ -293,6 +351,8 @@ typedef struct csa_layer_desc {
   int64_t pos_offset;
   int32_t stream_dtype;  /* C/Z streams: F32 or BF16 */
   int32_t flags;         /* CSA_FLAG_* (0 = the exact default) */
+  float norm_eps;        /* RMSNorm epsilon (CSA_FLAG_QKV_NORM) */
+  int32_t reserved;      /* 0 */
 } csa_layer_desc;
 
 typedef struct csa_forward_io {
@@ -316,6 +376,8 @@ typedef struct csa_forward_io {
   csa_buf out;                           /* [B, Tq, H, D] */
   float* scores_out;                     /* optional [B, Tq, N] copy of the index scores */
   int32_t* idx_out;                      /* optional [B, Tq, topk] selected entries */
+  const float* q_norm;                   /* [D] query-head RMSNorm weight (CSA_FLAG_QKV_NORM) */
+  const float* kv_norm;                  /* [D] KV RMSNorm weight (CSA_FLAG_QKV_NORM) */
 } csa_forward_io;
 
 size_t csa_forward_workspace_size(const csa_layer_desc* L);

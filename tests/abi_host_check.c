@@ -120,6 +120,29 @@ int main(void) {
   expect(hca_dense_attn(&bf16, (const int64_t*)p, &bf16, 10, 0, &bf16, (const int64_t*)p, 16, (const float*)p, 1.f,
                         64, 1e4f, 0, 1, 1, 16, 128, 10, 8, &bf16, NULL, 0, NULL) == CSA_ERR_SHAPE, "hca: ratio 0");
 
+  /* RMSNorm, compress with a norm, grouped output projection */
+  {
+    const float* w = (const float*)p;
+    expect(csa_rmsnorm(&bf16, 4, 512, NULL, 1e-6f, &bf16, NULL) == CSA_ERR_NULL, "rmsnorm: no weight");
+    expect(csa_rmsnorm(&bf16, 4, 500, w, 1e-6f, &bf16, NULL) == CSA_ERR_SHAPE, "rmsnorm: D % 8");
+    expect(csa_rmsnorm(&bf16, 4, 512, w, 1e-6f, &f32, NULL) == CSA_ERR_DTYPE, "rmsnorm: mixed dtypes");
+    expect(csa_rmsnorm(&bf16, -1, 512, w, 1e-6f, &bf16, NULL) == CSA_ERR_SHAPE, "rmsnorm: negative rows");
+    expect(csa_compress_norm(p, p, p, p, CSA_BF16, NULL, NULL, NULL, NULL, 1, 8, 16, 4, 1, 0, 0, 1e4f, 0,
+                             (const float*)(p + 4), 1e-6f, &bf16, 2, NULL) == CSA_ERR_SHAPE,
+           "compress_norm: misaligned weight");
+    expect(csa_grouped_out_proj(&bf16, p, p, 16, 128, 512, 12, 1024, 7168, &bf16, p, (size_t)1 << 30, NULL) ==
+           CSA_ERR_SHAPE, "proj: g does not divide n_h");
+    expect(csa_grouped_out_proj(&f32, p, p, 16, 128, 512, 16, 1024, 7168, &bf16, p, (size_t)1 << 30, NULL) ==
+           CSA_ERR_DTYPE, "proj: f32 input");
+    expect(csa_grouped_out_proj(&bf16, p, p, 16, 128, 512, 16, 1024, 7168, &bf16, NULL, 0, NULL) == CSA_ERR_WORKSPACE,
+           "proj: no workspace");
+    expect(csa_grouped_out_proj_workspace_size(0, 128, 512, 16, 1024, 7168) == 0, "proj: size at T = 0");
+    const int64_t Ts[] = {1, 16, 32, 33, 2048, (int64_t)1 << 22};
+    for (unsigned i = 0; i < sizeof Ts / sizeof Ts[0]; ++i)
+      expect(csa_grouped_out_proj_workspace_size(Ts[i], 128, 512, 16, 1024, 7168) >= (size_t)Ts[i] * 16 * 1024 * 2,
+             "proj: size holds mid");
+  }
+
   /* forward descriptors */
   {
     csa_layer_desc d;
@@ -153,8 +176,14 @@ int main(void) {
         d.rope_base = 1e4f;
         d.softmax_scale = 1.f;
         d.stream_dtype = CSA_BF16;
+        d.flags = 0;
         (void)csa_forward_workspace_size(&d);
         expect(csa_forward(&d, &io, NULL, 0, NULL) != CSA_OK, "forward: empty io is rejected");
+        d.flags = CSA_FLAG_QKV_NORM;
+        d.norm_eps = 1e-6f;
+        expect(csa_forward_workspace_size(&d) > 0, "forward: size with norms");
+        expect(csa_forward(&d, &io, NULL, 0, NULL) != CSA_OK, "forward: norms without weights are rejected");
+        d.flags = 0;
       }
   }
   if (failures == 0) printf("abi host check: ok\n");

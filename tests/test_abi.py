@@ -32,7 +32,35 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.csa_abi_version() == 2
+    assert L.csa_abi_version() == 3
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of csa_layer_desc / csa_forward_io have the C sizes and
+    field offsets (the header compiled by the host C compiler)."""
+    import shutil
+    import subprocess
+    from compressed_sparse_attention_07_amd._lib import csa_forward_io, csa_layer_desc
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = {"csa_layer_desc": csa_layer_desc, "csa_forward_io": csa_forward_io}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "csa.h"', "int main(void) {"]
+    for sname, cls in fields.items():
+        lines.append(f'  printf("{sname} %zu\\n", sizeof({sname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{sname}.{f} %zu\\n", offsetof({sname}, {f}));')
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = str(tmp_path / "layout")
+    subprocess.run([cc, "-I" + os.path.join(ROOT, "include"), str(src), "-o", exe], check=True)
+    got = dict(line.split() for line in subprocess.run([exe], capture_output=True, text=True, check=True)
+               .stdout.splitlines())
+    for sname, cls in fields.items():
+        assert int(got[sname]) == C.sizeof(cls), sname
+        for f, _ in cls._fields_:
+            assert int(got[f"{sname}.{f}"]) == getattr(cls, f).offset, (sname, f)
 
 
 def _buf(dtype=1, data=0x100000):
@@ -72,6 +100,58 @@ def test_compress_rejects_bad_arguments(L):
     mx = _buf(3)
     st = L.csa_compress(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, C.byref(mx), 2, None)
     assert st == 1
+
+
+def test_norm_and_projection_reject_bad_arguments(L):
+    p = 0x100000
+    x, out = _buf(), _buf()
+    # RMSNorm: no weight, D not a multiple of 8, mixed dtypes, negative eps
+    assert L.csa_rmsnorm(C.byref(x), 4, 512, None, C.c_float(1e-6), C.byref(out), None) == 1
+    assert L.csa_rmsnorm(C.byref(x), 4, 500, p, C.c_float(1e-6), C.byref(out), None) == 2
+    assert L.csa_rmsnorm(C.byref(x), 4, 4096, p, C.c_float(1e-6), C.byref(out), None) == 2
+    f32 = _buf(0)
+    assert L.csa_rmsnorm(C.byref(x), 4, 512, p, C.c_float(1e-6), C.byref(f32), None) == 3
+    assert L.csa_rmsnorm(C.byref(x), 4, 512, p, C.c_float(-1.0), C.byref(out), None) == 2
+    # compress with a norm weight: misaligned weight, bad eps
+    st = L.csa_compress_norm(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, p + 4,
+                             C.c_float(1e-6), C.byref(out), 2, None)
+    assert st == 2
+    st = L.csa_compress_norm(p, p, p, p, 1, None, None, None, None, 1, 8, 16, 4, 1, 0, 0, 10000.0, 0, p,
+                             C.c_float(float("nan")), C.byref(out), 2, None)
+    assert st == 2
+    # grouped projection: g not dividing n_h, contraction not a multiple of 32, f32 input,
+    # missing workspace
+    o = _buf()
+    assert L.csa_grouped_out_proj(C.byref(o), p, p, 16, 128, 512, 12, 1024, 7168, C.byref(out), p, 1 << 30, None) == 2
+    assert L.csa_grouped_out_proj(C.byref(o), p, p, 16, 4, 12, 4, 1024, 7168, C.byref(out), p, 1 << 30, None) == 6
+    assert L.csa_grouped_out_proj(C.byref(f32), p, p, 16, 128, 512, 16, 1024, 7168, C.byref(out), p, 1 << 30,
+                                  None) == 3
+    assert L.csa_grouped_out_proj(C.byref(o), p, p, 16, 128, 512, 16, 1024, 7168, C.byref(out), None, 0, None) == 4
+    # sizes: mid (bf16) plus fp32 split partials for few rows; none for T = 0
+    assert L.csa_grouped_out_proj_workspace_size(0, 128, 512, 16, 1024, 7168) == 0
+    assert L.csa_grouped_out_proj_workspace_size(16, 128, 512, 16, 1024, 7168) >= 16 * 16 * 1024 * 2
+    assert L.csa_grouped_out_proj_workspace_size(16, 128, 512, 12, 1024, 7168) == 0
+
+
+def test_forward_norm_flag_needs_weights(L):
+    from compressed_sparse_attention_07_amd import CSA_FLAG_QKV_NORM, layer_desc
+    from compressed_sparse_attention_07_amd._lib import csa_forward_io
+    d = layer_desc(mode=0, B=16, T=0, t0=4096, Tq=1, cache_rows=1024, Tw=128, D=512, H=128, HI=64, DI=128, ratio=4,
+                   topk=512, n_win=128, rope_dims=64, rope_base=10000.0, softmax_scale=1.0, stream_dtype=1,
+                   flags=CSA_FLAG_QKV_NORM, norm_eps=1e-6)
+    plain = layer_desc(mode=0, B=16, T=0, t0=4096, Tq=1, cache_rows=1024, Tw=128, D=512, H=128, HI=64, DI=128,
+                       ratio=4, topk=512, n_win=128, rope_dims=64, rope_base=10000.0, softmax_scale=1.0,
+                       stream_dtype=1)
+    # the normalized query and window copies live in the workspace
+    assert L.csa_forward_workspace_size(C.byref(d)) >= L.csa_forward_workspace_size(C.byref(plain)) + 16 * 128 * 512 * 2
+    d.norm_eps = float("inf")
+    assert L.csa_forward_workspace_size(C.byref(d)) == 0
+    d.norm_eps = 1e-6
+    d.reserved = 1
+    assert L.csa_forward_workspace_size(C.byref(d)) == 0
+    d.reserved = 0
+    io = csa_forward_io()
+    assert L.csa_forward(C.byref(d), C.byref(io), None, 0, None) != 0
 
 
 def test_topk_and_index_reject_bad_arguments(L):

@@ -32,7 +32,7 @@ def test_abi_host_code_under_asan_and_ubsan(tmp_path):
     if not (os.path.exists(HIPCC) and os.path.exists(CLANG)):
         pytest.skip("ROCm compilers not found")
     ensure_built()
-    objs = [os.path.join(PKG, "_build", f"{n}.o") for n in ("compress", "indexer", "topk", "mqa")]
+    objs = [os.path.join(PKG, "_build", f"{n}.o") for n in ("compress", "indexer", "topk", "mqa", "proj")]
     if not all(os.path.exists(o) for o in objs):
         from compressed_sparse_attention_07_amd import build
         build.build()

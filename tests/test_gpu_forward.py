@@ -52,9 +52,12 @@ def _csa_case(g, B, T, D, DI, H, HI, Tq, dtype):
     return streams, istreams, q, qI, wI, win, sink
 
 
-def _run_forward(dtype, B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, scale, seed):
+def _run_forward(dtype, B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, scale, seed, norm=False):
     g = Gen(seed, DEV)
     streams, istreams, q, qI, wI, win, sink = _csa_case(g, B, T, D, DI, H, HI, Tq, dtype)
+    # RMSNorm weights of the query heads and the KV (near 1, as trained norms are)
+    q_norm = g.uniform((D,), 0.5, 1.5) if norm else None
+    kv_norm = g.uniform((D,), 0.5, 1.5) if norm else None
     N = T // ratio
     dt = csa.CSA_F32 if dtype == "f32" else csa.CSA_BF16
     kv = csa.Buf.empty((B, N, D), dt)
@@ -66,21 +69,24 @@ def _run_forward(dtype, B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, scale, seed)
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
     desc = csa.layer_desc(mode=csa.CSA_MODE_CSA, B=B, T=T, t0=0, Tq=Tq, cache_rows=N, Tw=T, D=D, H=H, HI=HI, DI=DI,
                           ratio=ratio, topk=k, n_win=n_win, rope_dims=R, rope_base=10000.0, softmax_scale=scale,
-                          pos_offset=0, stream_dtype=dt)
+                          pos_offset=0, stream_dtype=dt, flags=csa.CSA_FLAG_QKV_NORM if norm else 0,
+                          norm_eps=1e-6)
     io = dict(ca=streams[0], cb=streams[1], za=streams[2], zb=streams[3], ica=istreams[0], icb=istreams[1],
               iza=istreams[2], izb=istreams[3], kv_cache=kv, ik_cache=ik, q=q, q_pos=pos, qI=qI, wI=wI, win=win,
-              win_pos0=win_pos0, sink=sink, out=out, scores_out=scores, idx_out=idx)
+              win_pos0=win_pos0, sink=sink, out=out, scores_out=scores, idx_out=idx, q_norm=q_norm, kv_norm=kv_norm)
     csa.csa_forward(desc, io)
     torch.cuda.synchronize()
     return dict(streams=streams, istreams=istreams, q=q, qI=qI, wI=wI, win=win, sink=sink, pos=pos, kv=kv, ik=ik,
-                out=out, scores=scores, idx=idx)
+                out=out, scores=scores, idx=idx, q_norm=None if q_norm is None else f64(q_norm),
+                kv_norm=None if kv_norm is None else f64(kv_norm))
 
 
 def _check_layer(r, b, dtype, k, ratio, n_win, R, scale):
+    norms = dict(q_norm=r.get("q_norm"), kv_norm=r.get("kv_norm"), norm_eps=1e-6)
     want = O.csa_layer([f64(s[b]) for s in r["streams"]], [f64(s[b]) for s in r["istreams"]], f64(r["q"][b]),
                        r["pos"][b].cpu().numpy(), f64(r["qI"][b]), f64(r["wI"][b]), f64(r["win"][b]), 0,
                        f64(r["sink"]), ratio=ratio, k=k, n_win=n_win, scale=scale, rope_dims=R, rope_base=10000.0,
-                       dtype=dtype)
+                       dtype=dtype, **norms)
     kind = "f32" if dtype == "f32" else "bf16"
     assert_close(f64(r["kv"].data[b]), want["kv"], kind, "compressed KV")
     assert_close(f64(r["ik"].data[b]), want["ik"], kind, "compressed indexer keys")
@@ -107,7 +113,7 @@ def _check_layer(r, b, dtype, k, ratio, n_win, R, scale):
         else:
             # the oracle's attention over the GPU's own selection (and the oracle's cache)
             wt = O.store(O.mqa(f64(r["q"][b, t:t + 1]), pos[t:t + 1], want["kv"], gi[t:t + 1], f64(r["win"][b]), 0,
-                               n_win, f64(r["sink"]), scale=scale, rope_dims=R, rope_base=10000.0)[0], dtype)
+                               n_win, f64(r["sink"]), scale=scale, rope_dims=R, rope_base=10000.0, **norms)[0], dtype)
         assert_close(got_out[t], wt, kind, f"output of query {t}")
     say(f"  sequence {b}: {n_exact} of {gi.shape[0]} selections identical, every output checked")
 
@@ -135,6 +141,24 @@ def test_forward_bf16_decode_fused_selection():
     r = _run_forward("bf16", B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, 1.0, 4321)
     for b in range(B):
         _check_layer(r, b, "bf16", k, ratio, n_win, R, 1.0)
+
+
+def test_forward_qkv_norm_fp32():
+    # query heads, compressed entries and window rows RMS-normalized before attention
+    say("forward fp32 with Q/KV RMSNorm")
+    B, T, D, DI, H, HI, Tq, k, ratio, n_win, R = 1, 512, 128, 32, 8, 8, 40, 16, 4, 32, 64
+    r = _run_forward("f32", B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, D ** -0.5, 2024, norm=True)
+    _check_layer(r, 0, "f32", k, ratio, n_win, R, D ** -0.5)
+
+
+def test_forward_qkv_norm_bf16_decode():
+    # the headline layer shape (512-dim heads, 64 RoPE dims) at decode: the wave-pair
+    # attention kernel reads the normalized query and window copies
+    say("forward bf16 decode with Q/KV RMSNorm")
+    B, T, D, DI, H, HI, Tq, k, ratio, n_win, R = 2, 8192, 512, 128, 64, 64, 1, 256, 4, 128, 64
+    r = _run_forward("bf16", B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, D ** -0.5, 2025, norm=True)
+    for b in range(B):
+        _check_layer(r, b, "bf16", k, ratio, n_win, R, D ** -0.5)
 
 
 def test_forward_with_no_queries_only_compresses():
@@ -222,3 +246,33 @@ def test_forward_hca():
                        ratio=ratio, n_win=n_win, scale=1.0, rope_dims=64, rope_base=10000.0, dtype="bf16")
     assert_close(f64(kv.data[0]), want["kv"], "bf16", "HCA cache")
     assert_close(f64(out[0]), want["out"], "bf16", "HCA output")
+
+
+def test_forward_hca_qkv_norm():
+    say("forward HCA with Q/KV RMSNorm")
+    g = Gen(7004, DEV)
+    B, T, D, H, Tq, ratio, n_win = 2, 1024, 512, 16, 3, 128, 128
+    C_, Z = g.normal((B, T, D), dtype=torch.bfloat16), g.normal((B, T, D), dtype=torch.bfloat16)
+    q = g.normal((B, Tq, H, D), qstd(D), dtype=torch.bfloat16)
+    win = g.normal((B, T, D), dtype=torch.bfloat16)
+    sink = g.normal((H,))
+    q_norm, kv_norm = g.uniform((D,), 0.5, 1.5), g.uniform((D,), 0.5, 1.5)
+    N = T // ratio
+    kv = csa.Buf.empty((B, N, D), csa.CSA_BF16)
+    # queries of the two sequences at different positions (each sequence's own window span)
+    pos = torch.tensor([[5, 640, 1023], [127, 128, 900]], dtype=torch.int64, device=DEV)
+    win_pos0 = torch.zeros((B,), dtype=torch.int64, device=DEV)
+    out = torch.empty_like(q)
+    scale = D ** -0.5
+    desc = csa.layer_desc(mode=csa.CSA_MODE_HCA, B=B, T=T, t0=0, Tq=Tq, cache_rows=N, Tw=T, D=D, H=H, ratio=ratio,
+                          n_win=n_win, rope_dims=64, rope_base=10000.0, softmax_scale=scale, stream_dtype=csa.CSA_BF16,
+                          flags=csa.CSA_FLAG_QKV_NORM, norm_eps=1e-6)
+    csa.csa_forward(desc, dict(ca=C_, za=Z, kv_cache=kv, q=q, q_pos=pos, win=win, win_pos0=win_pos0, sink=sink,
+                               out=out, q_norm=q_norm, kv_norm=kv_norm))
+    torch.cuda.synchronize()
+    for b in range(B):
+        want = O.hca_layer((f64(C_[b]), f64(Z[b])), f64(q[b]), pos[b].cpu().numpy(), f64(win[b]), 0, f64(sink),
+                           ratio=ratio, n_win=n_win, scale=scale, rope_dims=64, rope_base=10000.0, dtype="bf16",
+                           q_norm=f64(q_norm), kv_norm=f64(kv_norm), norm_eps=1e-6)
+        assert_close(f64(kv.data[b]), want["kv"], "bf16", f"HCA normalized cache of sequence {b}")
+        assert_close(f64(out[b]), want["out"], "bf16", f"HCA output with norms, sequence {b}")

@@ -652,6 +652,81 @@ def run_workload(key: str, steps: int, warmup: int, layers: int, reps: int):
     return wl, value, ms_per_step, stage_out, roofline
 
 
+def layer_edges(wl: Workload, steps: int, reps: int):
+    """The steps either side of core attention, timed apart from the step: the same
+    forward steps with Q/KV RMSNorm (query heads, compressed entries and window rows),
+    and the grouped output projection of the step's tokens at the large model's widths
+    (128 heads x 512 -> 16 groups x 1024 -> 7168; bf16 weights, seeded)."""
+
+    import torch
+
+    import compressed_sparse_attention_07_amd as csa
+    from synth import Gen
+
+    M = wl.meta
+    if M["mode"] != "csa" or M["kv_format"] == "fp8mix":
+        return None
+    g = Gen(wl.cfg.seed + 77, "cuda")
+    D = M["D"]
+    q_norm, kv_norm = g.uniform((D,), 0.5, 1.5), g.uniform((D,), 0.5, 1.5)
+
+    def with_norm(d):
+        if d is None:
+            return None
+        d2 = csa._lib.csa_layer_desc.from_buffer_copy(d)
+        d2.flags |= csa.CSA_FLAG_QKV_NORM
+        d2.norm_eps = 1e-6
+        return d2
+
+    dfull, datt = with_norm(wl.desc_full), with_norm(wl.desc_attend)
+    ws = torch.empty(max(1, csa.csa_forward_workspace_size(dfull if dfull is not None else datt)), dtype=torch.uint8,
+                     device="cuda")
+    ios = [dict(io, q_norm=q_norm, kv_norm=kv_norm) for io in wl.ios]
+    att = [csa.ForwardCall(datt, io, ws=ws) for io in ios]
+    full = [csa.ForwardCall(dfull, io, ws=ws) for io in ios] if dfull is not None else att
+
+    def step(i):
+        f = wl.compress_every and (i % wl.compress_every == 0)
+        (full if f else att)[i % len(ios)]()
+
+    for i in range(4):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"qkv_norm_step": dict(ms_per_step=round(ms, 5), value=round(wl.tokens / (ms * 1e-3), 1),
+                                 unit="tokens/s")}
+    log(f"  with Q/KV RMSNorm: step {ms * 1e3:.1f} us")
+    del att, full, ws
+
+    T = M["B"] * M["Tq"]
+    n_h, c, ng, d_g, d = 128, 512, 16, 1024, 7168
+    o = g.normal((T, n_h, c), dtype=torch.bfloat16)
+    wg = g.normal((ng, d_g, (n_h // ng) * c), ((n_h // ng) * c) ** -0.5, dtype=torch.bfloat16)
+    wo = g.normal((d, ng * d_g), (ng * d_g) ** -0.5, dtype=torch.bfloat16)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    pws = torch.empty(max(1, csa.csa_grouped_out_proj_workspace_size(T, n_h, c, ng, d_g, d)), dtype=torch.uint8,
+                      device="cuda")
+    call = csa.PreparedCall(csa.csa_grouped_out_proj, o, wg, wo, y, ws=pws)
+    t = time_stage(lambda i: call(), reps)
+    nbytes = (wg.numel() + wo.numel() + o.numel() + y.numel()) * 2
+    flops = 2.0 * T * (n_h * c * d_g + ng * d_g * d)
+    bound = "mfma" if flops / MFMA_BF16_PEAK > nbytes / HBM_PEAK else "hbm"
+    out["grouped_out_proj"] = dict(us=round(t * 1e6, 2), tokens=T, GBps=round(nbytes / t / 1e9, 1),
+                                   TFLOPs=round(flops / t / 1e12, 2), hbm_frac=round(nbytes / t / HBM_PEAK, 4),
+                                   mfma_frac=round(flops / t / MFMA_BF16_PEAK, 4), bound=bound,
+                                   kernel="gemm_bf16_kernel" + ("+gemm_reduce_kernel" if T <= 32 else ""),
+                                   algorithmic_bytes=int(nbytes), algorithmic_flops=int(flops))
+    log(f"  grouped output projection ({T} tokens): {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s, "
+        f"{flops / t / 1e12:.1f} TFLOP/s ({bound}-bound)")
+    return out
+
+
 # ============================================================================ main
 
 
@@ -711,6 +786,7 @@ def main():
     reps = args.stage_reps if args.stage_reps is not None else (20 if decode else 4)
 
     wl, value, ms_per_step, stage_out, roofline = run_workload(args.config, steps, warmup, layers, reps)
+    edges = layer_edges(wl, steps, reps)
 
     if args.copy_probe:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB): the
@@ -747,6 +823,8 @@ def main():
     }
     if wl.build:
         line["cache_build_compress"] = wl.build
+    if edges:
+        line["layer_edges"] = edges
     if not args.no_others:
         # the other workloads at their full sizes, fewer steps each: their step rate,
         # every stage's time and fraction of peak, and the dominant stage's roofline
@@ -760,6 +838,9 @@ def main():
                                                  10 if dec else 3)
             others[WORKLOAD_TAGS[key]] = dict(value=round(v2, 1), unit="tokens/s", ms_per_step=round(ms2, 5),
                                               build_compress=w2.build or None, roofline=rf2, stages=st2)
+            e2 = layer_edges(w2, 16 if dec else 3, 10 if dec else 3)
+            if e2:
+                others[WORKLOAD_TAGS[key]]["layer_edges"] = e2
             del w2
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)

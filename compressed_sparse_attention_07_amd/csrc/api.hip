@@ -218,14 +218,15 @@ IdxTopkPlan plan_index_topk(IndexLaunch X, int k, bool have_scores, bool dtype_k
   return p;
 }
 
+// side: a normalization job riding on the final selection launch, or NULL
 int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int32_t* count, float* scores_out,
-                   char* w, hipStream_t s, const char** stage) {
+                   char* w, hipStream_t s, const char** stage, const AttnNormArgs* side = nullptr) {
   X.sel_k = k;
   const int64_t rows = X.B * X.Tq;
   if (rows == 0 || X.N == 0) {
     // nothing to score: every selection is empty (idx all -1, counts 0)
     *stage = "topk";
-    return launch_topk(nullptr, rows, 0, k, idx, count, nullptr, s);
+    return launch_topk(nullptr, rows, 0, k, idx, count, nullptr, s, side);
   }
   if (P.sel > 0) {
     const size_t nc = static_cast<size_t>(rows) * P.sel * k;
@@ -236,7 +237,7 @@ int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int
     int rc = launch_index_select(X, s);
     if (rc != 0) return rc;
     *stage = "topk_merge";
-    return launch_topk_merge(X.sel_val, X.sel_idx, rows, P.sel, k, idx, count, s);
+    return launch_topk_merge(X.sel_val, X.sel_idx, rows, P.sel, k, idx, count, s, side);
   }
   X.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
   *stage = "index_scores";
@@ -244,7 +245,7 @@ int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int
   if (rc != 0) return rc;
   *stage = "topk";
   void* tws = w + (scores_out ? 0 : align256(static_cast<size_t>(rows * X.N) * sizeof(float)));
-  return launch_topk(X.scores, rows, X.N, k, idx, count, tws, s);
+  return launch_topk(X.scores, rows, X.N, k, idx, count, tws, s, side);
 }
 
 }  // namespace
@@ -776,13 +777,19 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     }
   }
   // the attention operands: the caller's query and window, or their normalized copies
+  // (CSA: the normalization rides on the final top-k launch, whose few workgroups leave
+  // most of the chip idle; HCA: its own launch)
   csa_buf q = io->q, win = io->win;
+  AttnNormArgs norm{};
   if (qkv_norm) {
     q.data = w + P.nq_off;
     win.data = w + P.nw_off;
-    const int rc = launch_attn_norm(io->q, q, io->q_norm, io->win, win, io->kv_norm, io->q_pos, io->win_pos0, L->B,
-                                    L->Tq, L->Tw, L->H, L->D, L->n_win, L->norm_eps, s);
-    if (rc != 0) return launched(rc, "csa_forward/qkv_norm");
+    norm = make_attn_norm(io->q, q, io->q_norm, io->win, win, io->kv_norm, io->q_pos, io->win_pos0, L->B, L->Tq, L->Tw,
+                          L->H, L->D, L->n_win, L->norm_eps);
+    if (!csa_mode) {
+      const int rc = launch_attn_norm(norm, s);
+      if (rc != 0) return launched(rc, "csa_forward/qkv_norm");
+    }
   }
   if (csa_mode) {
     int32_t* idx = io->idx_out ? io->idx_out : reinterpret_cast<int32_t*>(w + P.idx_off);
@@ -792,7 +799,8 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
     X.kI = io->ik_cache;
     X.q_pos = io->q_pos;
     const char* stage = "";
-    const int rc = run_index_topk(X, L->topk, P.it, idx, nullptr, io->scores_out, w + P.scores_off, s, &stage);
+    const int rc = run_index_topk(X, L->topk, P.it, idx, nullptr, io->scores_out, w + P.scores_off, s, &stage,
+                                  qkv_norm ? &norm : nullptr);
     if (rc != 0) return launched(rc, stage);
     AttnLaunch A = make_attn(&q, io->q_pos, &io->kv_cache, L->cache_rows, 1, idx, L->topk, 1, &win, io->win_pos0,
                              L->Tw, io->sink, L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset, L->B, L->Tq,

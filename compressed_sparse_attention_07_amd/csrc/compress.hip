@@ -735,54 +735,7 @@ int launch_compress2(const CompressLaunch& L0, const CompressLaunch& L1, hipStre
   return launch(a, a.grid0 + g1, L0.stream_dtype, stream);
 }
 
-// Row-wise RMSNorm ([V4-CN] §2.3.3: query heads and KV entries are normalized before
-// core attention), one wave per row.
-struct NormArgs {
-  const void* x;
-  void* y;
-  const float* w;
-  int64_t rows;
-  int D, dtype;
-  float eps;
-};
-
-// One row: lane l owns dims 8 (l + 64 i); the sum of squares is reduced across the
-// wave in a fixed order (DPP), so results are bitwise repeatable.
-__device__ __forceinline__ void norm_row(const void* x, void* y, const float* w, int64_t row, int D, int dtype,
-                                         float eps, int lane) {
-  constexpr int kMaxIt = 2048 / (8 * WAVE);
-  float v[kMaxIt][kVec];
-  float ss = 0.f;
-#pragma unroll
-  for (int it = 0; it < kMaxIt; ++it) {
-    const int d0 = 8 * (lane + WAVE * it);
-    if (d0 < D) {
-      if (dtype == CSA_F32) load8<float>(static_cast<const float*>(x) + row * D + d0, v[it]);
-      else load8<uint16_t>(static_cast<const uint16_t*>(x) + row * D + d0, v[it]);
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) ss = fmaf(v[it][i], v[it][i], ss);
-    }
-  }
-  const float inv = 1.0f / sqrtf(wave_sum_dpp(ss) / static_cast<float>(D) + eps);
-#pragma unroll
-  for (int it = 0; it < kMaxIt; ++it) {
-    const int d0 = 8 * (lane + WAVE * it);
-    if (d0 >= D) continue;
-    float o[kVec];
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) o[i] = v[it][i] * inv * w[d0 + i];
-    if (dtype == CSA_F32) {
-      float4* p = reinterpret_cast<float4*>(static_cast<float*>(y) + row * D + d0);
-      p[0] = make_float4(o[0], o[1], o[2], o[3]);
-      p[1] = make_float4(o[4], o[5], o[6], o[7]);
-    } else {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + row * D + d0) =
-          make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                     pack_bf16x2(o[6], o[7]));
-    }
-  }
-}
-
+// Row-wise RMSNorm launches (rmsnorm.h)
 __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
@@ -793,89 +746,40 @@ int launch_rmsnorm(const csa_buf& x, int64_t rows, int D, const float* w, float 
                    hipStream_t stream) {
   if (rows == 0) return 0;
   if (x.dtype != y.dtype || (x.dtype != CSA_F32 && x.dtype != CSA_BF16) || D % kVec || D > 2048) return -2;
+  if ((rows + 3) / 4 >= (int64_t(1) << 31)) return -4;
   NormArgs a{x.data, y.data, w, rows, D, x.dtype, eps};
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<uint32_t>((rows + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// The forward's normalization launch: every query head row, then for each sequence
-// only the window rows its queries can see (positions max(0, min q_pos - n_win + 1)
-// .. max q_pos, clipped to the buffer), written at the same row of a copy.
-struct AttnNormArgs {
-  NormArgs q;
-  const void* win;
-  void* win_out;
-  const float* kv_w;
-  const int64_t* q_pos;
-  const int64_t* win_pos0;
-  int64_t Tq, Tw;
-  int win_dtype, n_win;
-  uint32_t q_blocks, w_blocks;  // blocks of the query part; window blocks per sequence
-};
+__global__ __launch_bounds__(256) void attn_norm_kernel(AttnNormArgs a) { attn_norm_block<4>(a, blockIdx.x); }
 
-__global__ __launch_bounds__(256) void attn_norm_kernel(AttnNormArgs a) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  if (blockIdx.x < a.q_blocks) {
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wid;
-    if (row < a.q.rows) norm_row(a.q.x, a.q.y, a.q.w, row, a.q.D, a.q.dtype, a.q.eps, lane);
-    return;
-  }
-  const uint32_t wb = blockIdx.x - a.q_blocks;
-  const int64_t b = wb / a.w_blocks;
-  const uint32_t part = wb % a.w_blocks;
-  __shared__ int64_t s_lo[4], s_hi[4];
-  int64_t lo = INT64_MAX, hi = INT64_MIN;
-  for (int64_t t = threadIdx.x; t < a.Tq; t += 256) {
-    const int64_t p = a.q_pos[b * a.Tq + t];
-    lo = min(lo, p);
-    hi = max(hi, p);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, static_cast<int64_t>(__shfl_xor(static_cast<long long>(lo), o)));
-    hi = max(hi, static_cast<int64_t>(__shfl_xor(static_cast<long long>(hi), o)));
-  }
-  if (lane == 0) {
-    s_lo[wid] = lo;
-    s_hi[wid] = hi;
-  }
-  __syncthreads();
-  lo = min(min(s_lo[0], s_lo[1]), min(s_lo[2], s_lo[3]));
-  hi = max(max(s_hi[0], s_hi[1]), max(s_hi[2], s_hi[3]));
-  if (lo > hi || a.n_win < 1) return;
-  const int64_t wp0 = a.win_pos0[b];
-  const int64_t first = max(max(lo - a.n_win + 1, static_cast<int64_t>(0)), wp0);
-  const int64_t last = min(hi, wp0 + a.Tw - 1);
-  for (int64_t p = first + static_cast<int64_t>(part) * 4 + wid; p <= last; p += static_cast<int64_t>(a.w_blocks) * 4)
-    norm_row(a.win, a.win_out, a.kv_w, b * a.Tw + (p - wp0), a.q.D, a.win_dtype, a.q.eps, lane);
-}
-
-int launch_attn_norm(const csa_buf& q, const csa_buf& q_out, const float* q_w, const csa_buf& win,
-                     const csa_buf& win_out, const float* kv_w, const int64_t* q_pos, const int64_t* win_pos0,
-                     int64_t B, int64_t Tq, int64_t Tw, int H, int D, int n_win, float eps, hipStream_t stream) {
-  const int64_t rows = B * Tq * H;
-  if (rows == 0) return 0;
-  if (q.dtype != q_out.dtype || (q.dtype != CSA_F32 && q.dtype != CSA_BF16) || win.dtype != win_out.dtype ||
-      (win.dtype != CSA_F32 && win.dtype != CSA_BF16) || D % kVec || D > 2048)
-    return -2;
+AttnNormArgs make_attn_norm(const csa_buf& q, const csa_buf& q_out, const float* q_w, const csa_buf& win,
+                            const csa_buf& win_out, const float* kv_w, const int64_t* q_pos, const int64_t* win_pos0,
+                            int64_t B, int64_t Tq, int64_t Tw, int H, int D, int n_win, float eps) {
   AttnNormArgs a{};
-  a.q = NormArgs{q.data, q_out.data, q_w, rows, D, q.dtype, eps};
+  a.q = NormArgs{q.data, q_out.data, q_w, B * Tq * H, D, q.dtype, eps};
   a.win = win.data;
   a.win_out = win_out.data;
   a.kv_w = kv_w;
   a.q_pos = q_pos;
   a.win_pos0 = win_pos0;
+  a.B = B;
   a.Tq = Tq;
   a.Tw = Tw;
   a.win_dtype = win.dtype;
   a.n_win = n_win;
-  a.q_blocks = static_cast<uint32_t>((rows + 3) / 4);
-  // enough waves for the rows a contiguous run of queries sees, a few rows per wave
-  const int64_t seen = Tq + n_win - 1;
-  a.w_blocks = static_cast<uint32_t>(std::min<int64_t>(std::max<int64_t>((seen + 7) / 8, 1), 1024));
-  const int64_t grid = static_cast<int64_t>(a.q_blocks) + (Tw > 0 && n_win > 0 ? B * a.w_blocks : 0);
-  if (grid >= (int64_t(1) << 31)) return -4;
-  hipLaunchKernelGGL(attn_norm_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, a);
+  return a;
+}
+
+int launch_attn_norm(AttnNormArgs a, hipStream_t stream) {
+  if (a.q.rows == 0) return 0;
+  if ((a.q.dtype != CSA_F32 && a.q.dtype != CSA_BF16) || (a.win_dtype != CSA_F32 && a.win_dtype != CSA_BF16) ||
+      a.q.D % kVec || a.q.D > 2048)
+    return -2;
+  if ((a.q.rows + 3) / 4 + a.B * 1024 >= (int64_t(1) << 31)) return -4;
+  attn_norm_shape(a, 4);
+  hipLaunchKernelGGL(attn_norm_kernel, dim3(a.blocks), dim3(256), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/csa.h"
+#include "rmsnorm.h"
 
 namespace csa {
 
@@ -51,12 +52,13 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream);
 // the shape is not covered.
 int index_select_slices(const IndexLaunch& L);  // slices per row, 0 if not covered
 int launch_index_select(const IndexLaunch& L, hipStream_t stream);
+// side: a normalization job appended to the final selection launch, or NULL
 int launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int64_t rows, int slices, int k,
-                      int32_t* idx, int32_t* count, hipStream_t stream);
+                      int32_t* idx, int32_t* count, hipStream_t stream, const AttnNormArgs* side = nullptr);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t N, int k);
 int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count,
-                void* ws, hipStream_t stream);
+                void* ws, hipStream_t stream, const AttnNormArgs* side = nullptr);
 
 struct GroupedProjLaunch {
   const void* o;        // bf16 [T, n_h, c]
@@ -73,12 +75,14 @@ int launch_grouped_out_proj(const GroupedProjLaunch& L, hipStream_t stream);
 // Row-wise RMSNorm: y = x / sqrt(mean(x^2) + eps) * w, rows of D in F32 or BF16
 int launch_rmsnorm(const csa_buf& x, int64_t rows, int D, const float* w, float eps, const csa_buf& y,
                    hipStream_t stream);
-// One launch normalizing the query heads [B*Tq*H, D] into q_out and, per sequence, the
-// window rows its queries see into the same rows of win_out ([B, Tw, D]); other rows
-// of win_out are not written.
-int launch_attn_norm(const csa_buf& q, const csa_buf& q_out, const float* q_w, const csa_buf& win,
-                     const csa_buf& win_out, const float* kv_w, const int64_t* q_pos, const int64_t* win_pos0,
-                     int64_t B, int64_t Tq, int64_t Tw, int H, int D, int n_win, float eps, hipStream_t stream);
+// The normalization job of a forward's attention operands (rmsnorm.h): query heads
+// [B*Tq*H, D] into q_out and, per sequence, the window rows its queries see into the
+// same rows of win_out ([B, Tw, D]); other rows of win_out are not written.  It runs as
+// its own launch, or rides as extra workgroups on the last top-k launch.
+AttnNormArgs make_attn_norm(const csa_buf& q, const csa_buf& q_out, const float* q_w, const csa_buf& win,
+                            const csa_buf& win_out, const float* kv_w, const int64_t* q_pos, const int64_t* win_pos0,
+                            int64_t B, int64_t Tq, int64_t Tw, int H, int D, int n_win, float eps);
+int launch_attn_norm(AttnNormArgs a, hipStream_t stream);
 
 struct AttnLaunch {
   csa_buf q;

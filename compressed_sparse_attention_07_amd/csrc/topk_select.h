@@ -22,6 +22,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "rmsnorm.h"
 
 namespace csa {
 
@@ -57,6 +58,10 @@ struct TopkArgs {
   int64_t n_row;            // repair: scores per row
   float* spare_val;         // repair: [rows, ceil(n_row / capacity), k] scratch
   int32_t* spare_idx;
+  // final level: workgroups main_blocks .. main_blocks + side.blocks - 1 run an
+  // independent normalization job instead (side.blocks = 0: none)
+  uint32_t main_blocks;
+  AttnNormArgs side;
 };
 
 constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one wave

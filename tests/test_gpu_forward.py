@@ -161,6 +161,15 @@ def test_forward_qkv_norm_bf16_decode():
         _check_layer(r, b, "bf16", k, ratio, n_win, R, D ** -0.5)
 
 
+def test_forward_qkv_norm_multilevel_topk():
+    # more than 64 selection rows over 5120 entries: the selection runs in two levels and
+    # the normalization job rides on the last one
+    say("forward bf16 with Q/KV RMSNorm, two-level top-k")
+    B, T, D, DI, H, HI, Tq, k, ratio, n_win, R = 1, 20480, 128, 64, 16, 16, 70, 64, 4, 128, 64
+    r = _run_forward("bf16", B, T, D, DI, H, HI, Tq, k, ratio, n_win, R, D ** -0.5, 2026, norm=True)
+    _check_layer(r, 0, "bf16", k, ratio, n_win, R, D ** -0.5)
+
+
 def test_forward_with_no_queries_only_compresses():
     # Tq = 0 (a compression-only step, bf16 decode shape): the caches are written and
     # no selection or attention launch runs

@@ -28,7 +28,7 @@ EXPORTS = ["csa_abi_version", "csa_last_error", "csa_device_check", "csa_compres
            "csa_index_scores", "csa_topk_workspace_size", "csa_topk", "csa_index_topk_workspace_size", "csa_index_topk", "csa_sparse_mqa_workspace_size",
            "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "csa_sparse_mqa_noalloc_limit", "hca_dense_attn_workspace_size",
            "hca_dense_attn",
-           "csa_forward_workspace_size", "csa_forward"]
+           "csa_forward_workspace_size", "csa_forward", "csa_decode_step_workspace_size", "csa_decode_step"]
 
 
 class CSAError(RuntimeError):
@@ -62,6 +62,27 @@ class csa_forward_io(C.Structure):
                 ("qI", csa_buf), ("wI", C.c_void_p), ("win", csa_buf), ("win_pos0", C.c_void_p),
                 ("sink", C.c_void_p), ("out", csa_buf), ("scores_out", C.c_void_p), ("idx_out", C.c_void_p),
                 ("q_norm", C.c_void_p), ("kv_norm", C.c_void_p)]
+
+
+class csa_decode_desc(C.Structure):
+    _fields_ = [("struct_size", C.c_int32), ("mode", C.c_int32), ("B", C.c_int64), ("slots", C.c_int64),
+                ("pages", C.c_int64), ("max_pages", C.c_int32), ("page_tokens", C.c_int32),
+                ("D", C.c_int32), ("H", C.c_int32), ("HI", C.c_int32), ("DI", C.c_int32),
+                ("ratio", C.c_int32), ("topk", C.c_int32), ("n_win", C.c_int32), ("rope_dims", C.c_int32),
+                ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("pos_offset", C.c_int64),
+                ("stream_dtype", C.c_int32), ("flags", C.c_int32), ("norm_eps", C.c_float), ("reserved", C.c_int32)]
+
+
+class csa_decode_io(C.Structure):
+    _fields_ = [("slot", C.c_void_p), ("length", C.c_void_p),
+                ("ca", C.c_void_p), ("cb", C.c_void_p), ("za", C.c_void_p), ("zb", C.c_void_p),
+                ("bias_a", C.c_void_p), ("bias_b", C.c_void_p),
+                ("ica", C.c_void_p), ("icb", C.c_void_p), ("iza", C.c_void_p), ("izb", C.c_void_p),
+                ("ibias_a", C.c_void_p), ("ibias_b", C.c_void_p), ("kv_raw", C.c_void_p),
+                ("tail", C.c_void_p), ("itail", C.c_void_p), ("win", csa_buf), ("win_pos0", C.c_void_p),
+                ("kv_pages", csa_buf), ("ik_pages", csa_buf), ("block_table", C.c_void_p),
+                ("q", csa_buf), ("qI", csa_buf), ("wI", C.c_void_p), ("sink", C.c_void_p), ("out", csa_buf),
+                ("q_norm", C.c_void_p), ("kv_norm", C.c_void_p), ("idx_out", C.c_void_p), ("scores_out", C.c_void_p)]
 
 
 _lib = None
@@ -110,9 +131,12 @@ def lib():
         L.csa_forward_workspace_size.argtypes = [C.POINTER(csa_layer_desc)]
         L.csa_forward_workspace_size.restype = sz
         L.csa_forward.argtypes = [C.POINTER(csa_layer_desc), C.POINTER(csa_forward_io), vp, sz, vp]
+        L.csa_decode_step_workspace_size.argtypes = [C.POINTER(csa_decode_desc)]
+        L.csa_decode_step_workspace_size.restype = sz
+        L.csa_decode_step.argtypes = [C.POINTER(csa_decode_desc), C.POINTER(csa_decode_io), vp, sz, vp]
         for name in EXPORTS:
             if name not in ("csa_topk_workspace_size", "csa_sparse_mqa_workspace_size", "csa_index_topk_workspace_size",
-                            "csa_grouped_out_proj_workspace_size",
+                            "csa_grouped_out_proj_workspace_size", "csa_decode_step_workspace_size",
                             "csa_sparse_mqa_noalloc_limit",
                             "hca_dense_attn_workspace_size", "csa_forward_workspace_size",
                             "csa_last_error", "csa_abi_version"):
@@ -375,6 +399,69 @@ def csa_forward(desc: csa_layer_desc, io: dict, *, ws=None, stream=None) -> None
     dev = Buf.of(io["q"]).data.device
     w, wbytes = _ws(need, dev, ws)
     _invoke("csa_forward", C.byref(desc), C.byref(cio), ptr(w), wbytes, stream_handle(stream), keep=(w, io))
+
+
+def decode_desc(**kw) -> csa_decode_desc:
+    d = csa_decode_desc()
+    d.struct_size = C.sizeof(csa_decode_desc)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def csa_decode_step_workspace_size(desc: csa_decode_desc) -> int:
+    return lib().csa_decode_step_workspace_size(C.byref(desc))
+
+
+_DECODE_BUFS = ("win", "kv_pages", "ik_pages", "q", "qI", "out")
+
+
+def _decode_io(io: dict) -> csa_decode_io:
+    cio = csa_decode_io()
+    for name, val in io.items():
+        if val is None:
+            continue
+        if name in _DECODE_BUFS:
+            setattr(cio, name, Buf.of(val).c())
+        else:
+            setattr(cio, name, ptr(val))
+    return cio
+
+
+def csa_decode_step(desc: csa_decode_desc, io: dict, *, ws=None, stream=None) -> None:
+    """io maps csa_decode_io field names to tensors / Buf objects (missing = NULL)."""
+    cio = _decode_io(io)
+    need = csa_decode_step_workspace_size(desc)
+    dev = Buf.of(io["q"]).data.device
+    w, wbytes = _ws(need, dev, ws)
+    _invoke("csa_decode_step", C.byref(desc), C.byref(cio), ptr(w), wbytes, stream_handle(stream), keep=(w, io))
+
+
+class DecodePool:
+    """Device memory of a decode state pool and its paged caches, laid out as
+    csa_decode_step documents (allocation only; every field is a plain tensor)."""
+
+    def __init__(self, *, mode: int, slots: int, pages: int, max_pages: int, page_tokens: int, D: int, DI: int,
+                 ratio: int, n_win: int, stream_dtype: int, kv_dtype: int, ik_dtype: int, device="cuda"):
+        import torch
+        st = torch.float32 if stream_dtype == CSA_F32 else torch.bfloat16
+        kt = torch.float32 if kv_dtype == CSA_F32 else torch.bfloat16
+        P = page_tokens // ratio
+        csa_mode = mode == CSA_MODE_CSA
+        self.P = P
+        self.length = torch.zeros(slots, dtype=torch.int64, device=device)
+        ring, nst = (2 * ratio, 4) if csa_mode else (ratio, 2)
+        self.tail = torch.zeros((slots, ring, nst, D), dtype=st, device=device)
+        self.itail = torch.zeros((slots, ring, 4, DI), dtype=st, device=device) if csa_mode else None
+        self.win = torch.zeros((slots, 2 * n_win, D), dtype=kt, device=device)
+        self.win_pos0 = torch.zeros(slots, dtype=torch.int64, device=device)
+        self.kv_pages = Buf.empty((pages, P, D), kv_dtype, device=device)
+        self.ik_pages = Buf.empty((pages, P, DI), ik_dtype, device=device) if csa_mode else None
+        self.block_table = torch.full((slots, max_pages), -1, dtype=torch.int32, device=device)
+
+    def io(self) -> dict:
+        return dict(length=self.length, tail=self.tail, itail=self.itail, win=self.win, win_pos0=self.win_pos0,
+                    kv_pages=self.kv_pages, ik_pages=self.ik_pages, block_table=self.block_table)
 
 
 class ForwardCall:

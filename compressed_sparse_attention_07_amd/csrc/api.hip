@@ -218,15 +218,17 @@ IdxTopkPlan plan_index_topk(IndexLaunch X, int k, bool have_scores, bool dtype_k
   return p;
 }
 
-// side: a normalization job riding on the final selection launch, or NULL
+// side: a normalization job riding on the final selection launch, or NULL; out_map:
+// the selected entries are written as pool rows of a paged cache
 int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int32_t* count, float* scores_out,
-                   char* w, hipStream_t s, const char** stage, const AttnNormArgs* side = nullptr) {
+                   char* w, hipStream_t s, const char** stage, const AttnNormArgs* side = nullptr,
+                   const PageMap* out_map = nullptr) {
   X.sel_k = k;
   const int64_t rows = X.B * X.Tq;
   if (rows == 0 || X.N == 0) {
     // nothing to score: every selection is empty (idx all -1, counts 0)
     *stage = "topk";
-    return launch_topk(nullptr, rows, 0, k, idx, count, nullptr, s, side);
+    return launch_topk(nullptr, rows, 0, k, idx, count, nullptr, s, side, out_map, X.Tq);
   }
   if (P.sel > 0) {
     const size_t nc = static_cast<size_t>(rows) * P.sel * k;
@@ -237,7 +239,7 @@ int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int
     int rc = launch_index_select(X, s);
     if (rc != 0) return rc;
     *stage = "topk_merge";
-    return launch_topk_merge(X.sel_val, X.sel_idx, rows, P.sel, k, idx, count, s, side);
+    return launch_topk_merge(X.sel_val, X.sel_idx, rows, P.sel, k, idx, count, s, side, out_map, X.Tq);
   }
   X.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
   *stage = "index_scores";
@@ -245,7 +247,7 @@ int run_index_topk(IndexLaunch X, int k, const IdxTopkPlan& P, int32_t* idx, int
   if (rc != 0) return rc;
   *stage = "topk";
   void* tws = w + (scores_out ? 0 : align256(static_cast<size_t>(rows * X.N) * sizeof(float)));
-  return launch_topk(X.scores, rows, X.N, k, idx, count, tws, s, side);
+  return launch_topk(X.scores, rows, X.N, k, idx, count, tws, s, side, out_map, X.Tq);
 }
 
 }  // namespace
@@ -811,6 +813,256 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
                            io->win_pos0, L->Tw, io->sink, L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset,
                            L->B, L->Tq, L->H, L->D, N, L->n_win, &io->out);
   return launched(launch_attn(A, w + P.attn_off, P.attn_bytes, s), "csa_forward/hca_dense_attn");
+}
+
+
+// ------------------------------------------------------------------ csa_decode_step
+
+}  // extern "C"
+
+namespace {
+
+struct DecodePlan {
+  int64_t P, N_cap;   // entries per page, indexer row length
+  int shift;
+  int K;              // attention slots from the cache (CSA: topk; HCA: N_cap)
+  IdxTopkPlan it;
+  size_t qpos_off, wp0b_off, wp0a_off, idx_off, idx_bytes, it_off, attn_off, attn_bytes;
+  size_t nq_off, nq_bytes, nw_off, nw_bytes, total;
+};
+
+int log2_exact(int64_t x) {
+  if (x < 1 || (x & (x - 1))) return -1;
+  int s = 0;
+  while ((int64_t{1} << s) < x) ++s;
+  return s;
+}
+
+csa_status validate_decode_desc(const csa_decode_desc* L) {
+  if (!L) return fail(CSA_ERR_NULL, "decode descriptor is NULL");
+  if (L->struct_size != static_cast<int32_t>(sizeof(csa_decode_desc)))
+    return fail(CSA_ERR_SHAPE, "csa_decode_desc.struct_size=%d, expected %zu", L->struct_size, sizeof(csa_decode_desc));
+  if (L->mode != CSA_MODE_CSA && L->mode != CSA_MODE_HCA) return fail(CSA_ERR_SHAPE, "unknown mode %d", L->mode);
+  if (L->reserved != 0) return fail(CSA_ERR_SHAPE, "csa_decode_desc.reserved must be 0");
+  if (L->B < 0 || L->slots < 1 || L->pages < 1 || L->max_pages < 1 || L->B > L->slots)
+    return fail(CSA_ERR_SHAPE, "need 0 <= B <= slots, pages >= 1, max_pages >= 1");
+  if (L->ratio < 1 || L->ratio > 1024) return fail(CSA_ERR_SHAPE, "ratio out of [1, 1024]");
+  if (L->page_tokens < L->ratio || L->page_tokens % L->ratio || log2_exact(L->page_tokens) < 0)
+    return fail(CSA_ERR_SHAPE, "page_tokens=%d must be a power of two and a multiple of ratio", L->page_tokens);
+  const int64_t P = L->page_tokens / L->ratio;
+  if (log2_exact(P) < 0) return fail(CSA_ERR_SHAPE, "page_tokens / ratio must be a power of two");
+  if (static_cast<int64_t>(L->max_pages) * P >= (int64_t{1} << 31) || L->pages * P >= (int64_t{1} << 31))
+    return fail(CSA_ERR_SHAPE, "cache pools and rows must stay below 2^31 entries");
+  if (L->D < 8 || L->D > 1024 || L->D % 8) return fail(CSA_ERR_SHAPE, "D=%d must be a multiple of 8 in [8, 1024]", L->D);
+  if (L->n_win < 1) return fail(CSA_ERR_SHAPE, "n_win must be >= 1");
+  if (L->stream_dtype != CSA_F32 && L->stream_dtype != CSA_BF16)
+    return fail(CSA_ERR_DTYPE, "stream_dtype must be F32 or BF16");
+  if (L->flags & ~(CSA_FLAG_BF16_SCORES | CSA_FLAG_QKV_NORM)) return fail(CSA_ERR_SHAPE, "unknown flags 0x%x", L->flags);
+  if ((L->flags & CSA_FLAG_QKV_NORM) && (!(L->norm_eps >= 0.f) || !std::isfinite(L->norm_eps)))
+    return fail(CSA_ERR_SHAPE, "norm_eps must be finite and >= 0");
+  if (L->mode == CSA_MODE_CSA) {
+    if (L->topk < 1 || L->topk > 4096) return fail(CSA_ERR_SHAPE, "topk out of [1, 4096]");
+    if (P < index_min_page_entries)
+      return fail(CSA_ERR_UNSUPPORTED, "CSA pages need at least %d entries (page_tokens >= %d)", index_min_page_entries,
+                  index_min_page_entries * L->ratio);
+    if (L->HI < 1 || L->HI > 128 || L->DI < 8 || L->DI > 512 || L->DI % 8)
+      return fail(CSA_ERR_SHAPE, "indexer shape HI=%d DI=%d unsupported", L->HI, L->DI);
+    if (L->D + L->DI > 2048) return fail(CSA_ERR_UNSUPPORTED, "D + DI must be <= 2048");
+  }
+  return CSA_OK;
+}
+
+// elem: bytes per element of q and of the window (0: a size query, which takes 4)
+DecodePlan plan_decode(const csa_decode_desc* L, bool have_idx, bool have_scores, int32_t qI_dtype, int q_elem,
+                       int win_elem) {
+  DecodePlan p{};
+  p.P = L->page_tokens / L->ratio;
+  p.shift = log2_exact(p.P);
+  p.N_cap = static_cast<int64_t>(L->max_pages) * p.P;
+  const bool csa_mode = L->mode == CSA_MODE_CSA;
+  p.K = csa_mode ? L->topk : static_cast<int>(p.N_cap);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  p.qpos_off = take(static_cast<size_t>(L->B) * 8);
+  p.wp0b_off = take(static_cast<size_t>(L->B) * 8);
+  p.wp0a_off = take(static_cast<size_t>(L->B) * 8);
+  p.idx_bytes = (csa_mode && have_idx) ? 0 : static_cast<size_t>(L->B) * p.K * sizeof(int32_t);
+  p.idx_off = take(p.idx_bytes);
+  if (csa_mode) {
+    IndexLaunch X{};
+    X.qI.dtype = qI_dtype < 0 ? CSA_BF16 : qI_dtype;
+    X.kI.dtype = X.qI.dtype;
+    X.B = L->B;
+    X.Tq = 1;
+    X.N = p.N_cap;
+    X.HI = L->HI;
+    X.DI = L->DI;
+    X.ratio = L->ratio;
+    X.score_bf16 = (L->flags & CSA_FLAG_BF16_SCORES) ? 1 : 0;
+    p.it = plan_index_topk(X, L->topk, have_scores, qI_dtype >= 0);
+    p.it_off = take(p.it.bytes);
+  }
+  p.attn_bytes = align256(attn_workspace_bytes(L->B, 1, L->H, L->D, static_cast<int64_t>(p.K) + L->n_win, true));
+  p.attn_off = take(p.attn_bytes);
+  if (L->flags & CSA_FLAG_QKV_NORM) {
+    const size_t qe = q_elem > 0 ? q_elem : 4, we = win_elem > 0 ? win_elem : 4;
+    p.nq_bytes = static_cast<size_t>(L->B) * L->H * L->D * qe;
+    p.nq_off = take(p.nq_bytes);
+    p.nw_bytes = static_cast<size_t>(L->B) * 2 * L->n_win * L->D * we;
+    p.nw_off = take(p.nw_bytes);
+  }
+  p.total = off;
+  return p;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == CSA_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_decode_step_workspace_size(const csa_decode_desc* L) {
+  if (validate_decode_desc(L) != CSA_OK) return 0;
+  return plan_decode(L, false, false, -1, 0, 0).total;
+}
+
+csa_status csa_decode_step(const csa_decode_desc* L, const csa_decode_io* io, void* ws, size_t ws_bytes,
+                           void* stream) {
+  CSA_TRY(validate_decode_desc(L));
+  if (!io) return fail(CSA_ERR_NULL, "io is NULL");
+  const bool csa_mode = L->mode == CSA_MODE_CSA;
+  const bool qkv_norm = (L->flags & CSA_FLAG_QKV_NORM) != 0;
+  const int64_t Ws = 2 * static_cast<int64_t>(L->n_win);
+  if (L->B == 0) return ok();
+  if (!io->slot || !io->length || !io->ca || !io->za || !io->kv_raw || !io->tail || !io->win_pos0 ||
+      !io->block_table)
+    return fail(CSA_ERR_NULL, "slot, length, ca, za, kv_raw, tail, win_pos0 and block_table are required");
+  if (csa_mode && (!io->cb || !io->zb || !io->ica || !io->icb || !io->iza || !io->izb || !io->itail))
+    return fail(CSA_ERR_NULL, "CSA needs cb, zb, the indexer streams and itail");
+  CSA_TRY(check_buf(&io->q, "q"));
+  CSA_TRY(check_buf(&io->kv_pages, "kv_pages"));
+  CSA_TRY(check_buf(&io->win, "win"));
+  CSA_TRY(check_buf(&io->out, "out"));
+  if (!io->sink) return fail(CSA_ERR_NULL, "sink is required");
+  if (io->q.dtype != CSA_F32 && io->q.dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "q must be F32 or BF16");
+  if (io->out.dtype != io->q.dtype) return fail(CSA_ERR_DTYPE, "out must have the dtype of q");
+  if (io->kv_pages.dtype != CSA_F32 && io->kv_pages.dtype != CSA_BF16)
+    return fail(CSA_ERR_UNSUPPORTED, "the decode state takes F32 or BF16 caches and windows");
+  if (io->win.dtype != io->kv_pages.dtype) return fail(CSA_ERR_DTYPE, "win must have the dtype of kv_pages");
+  if (L->H < 1 || L->H > 256) return fail(CSA_ERR_SHAPE, "H=%d out of [1, 256]", L->H);
+  CSA_TRY(check_rope(L->D, L->rope_dims, L->rope_base));
+  if (csa_mode) {
+    CSA_TRY(check_buf(&io->qI, "qI"));
+    CSA_TRY(check_buf(&io->ik_pages, "ik_pages"));
+    if (!io->wI) return fail(CSA_ERR_NULL, "wI is required");
+    if (io->qI.dtype != io->ik_pages.dtype) return fail(CSA_ERR_DTYPE, "qI and ik_pages must share a dtype");
+    if (io->qI.dtype == CSA_FP8MIX) return fail(CSA_ERR_DTYPE, "the indexer takes F32, BF16 or MXFP4");
+    if (io->qI.dtype == CSA_MXFP4 && L->DI % 32) return fail(CSA_ERR_SHAPE, "MXFP4 needs DI %% 32 == 0");
+  }
+  if (qkv_norm) {
+    if (!io->q_norm || !io->kv_norm) return fail(CSA_ERR_NULL, "CSA_FLAG_QKV_NORM needs q_norm and kv_norm");
+    if (!aligned16(io->q_norm) || !aligned16(io->kv_norm))
+      return fail(CSA_ERR_SHAPE, "q_norm and kv_norm must be 16-byte aligned");
+  }
+  const DecodePlan P = plan_decode(L, io->idx_out != nullptr, io->scores_out != nullptr,
+                                   csa_mode ? io->qI.dtype : -1, elem_bytes(io->q.dtype), elem_bytes(io->win.dtype));
+  if (!ws || ws_bytes < P.total || !aligned16(ws))
+    return fail(CSA_ERR_WORKSPACE, "csa_decode_step needs %zu workspace bytes (16-byte aligned), got %zu", P.total,
+                ws_bytes);
+  CSA_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int64_t* q_pos = reinterpret_cast<int64_t*>(w + P.qpos_off);
+  int64_t* wp0_b = reinterpret_cast<int64_t*>(w + P.wp0b_off);
+  int64_t* wp0_adj = reinterpret_cast<int64_t*>(w + P.wp0a_off);
+  int32_t* idx = (csa_mode && io->idx_out) ? io->idx_out : reinterpret_cast<int32_t*>(w + P.idx_off);
+  PageMap pm{io->block_table, io->slot, L->max_pages, P.shift};
+
+  StateAppendLaunch A{};
+  A.B = L->B;
+  A.ca = io->ca; A.cb = io->cb; A.za = io->za; A.zb = io->zb;
+  A.bias_a = io->bias_a; A.bias_b = csa_mode ? io->bias_b : nullptr;
+  if (csa_mode) {
+    A.ica = io->ica; A.icb = io->icb; A.iza = io->iza; A.izb = io->izb;
+    A.ibias_a = io->ibias_a; A.ibias_b = io->ibias_b;
+  }
+  A.stream_dtype = L->stream_dtype;
+  A.D = L->D;
+  A.DI = L->DI;
+  A.ratio = L->ratio;
+  A.overlap = csa_mode ? 1 : 0;
+  A.rope_dims = L->rope_dims;
+  A.log2_base = L->rope_dims > 0 ? std::log2(static_cast<double>(L->rope_base)) : 0.0;
+  A.pos_offset = L->pos_offset;
+  A.norm_w = qkv_norm ? io->kv_norm : nullptr;
+  A.norm_eps = L->norm_eps;
+  A.kv_out = io->kv_pages;
+  A.ik_out = io->ik_pages;
+  A.pmap = pm;
+  A.slot = io->slot;
+  A.length = io->length;
+  A.tail = io->tail;
+  A.itail = io->itail;
+  A.kv_raw = io->kv_raw;
+  A.win = io->win.data;
+  A.win_elem = elem_bytes(io->win.dtype);
+  A.n_win = L->n_win;
+  A.Ws = Ws;
+  A.win_pos0 = io->win_pos0;
+  A.q_pos = q_pos;
+  A.wp0_b = wp0_b;
+  A.wp0_adj = wp0_adj;
+  A.vis_idx = csa_mode ? nullptr : idx;
+  A.vis_K = P.K;
+  int rc = launch_state_append(A, s);
+  if (rc != 0) return launched(rc, "csa_decode_step/append");
+
+  // the attention's query and window: the caller's and the slots' own, or normalized
+  // copies (batch row b's window copy at rows b * Ws .., base wp0_b[b])
+  csa_buf q = io->q, win = io->win;
+  const int64_t* win_base = wp0_adj;
+  AttnNormArgs norm{};
+  if (qkv_norm) {
+    q.data = w + P.nq_off;
+    win.data = w + P.nw_off;
+    norm = make_attn_norm(io->q, q, io->q_norm, io->win, win, io->kv_norm, q_pos, wp0_b, L->B, 1, Ws, L->H, L->D,
+                          L->n_win, L->norm_eps);
+    norm.win_slot = io->slot;
+    win_base = wp0_b;
+    if (!csa_mode) {
+      rc = launch_attn_norm(norm, s);
+      if (rc != 0) return launched(rc, "csa_decode_step/qkv_norm");
+    }
+  }
+  if (csa_mode) {
+    IndexLaunch X{};
+    X.qI = io->qI;
+    X.wI = io->wI;
+    X.kI = io->ik_pages;
+    X.q_pos = q_pos;
+    X.B = L->B;
+    X.Tq = 1;
+    X.N = P.N_cap;
+    X.kI_rows = 0;
+    X.HI = L->HI;
+    X.DI = L->DI;
+    X.ratio = L->ratio;
+    X.score_bf16 = (L->flags & CSA_FLAG_BF16_SCORES) ? 1 : 0;
+    X.kmap = pm;
+    const char* stage = "";
+    rc = run_index_topk(X, L->topk, P.it, idx, nullptr, io->scores_out, w + P.it_off, s, &stage,
+                        qkv_norm ? &norm : nullptr, &pm);
+    if (rc != 0) return launched(rc, stage);
+  }
+  // the cache operand is addressed by pool rows: one row block for every sequence
+  AttnLaunch AL = make_attn(&q, q_pos, &io->kv_pages, 0, 1, idx, P.K, 1, &win, win_base, Ws, io->sink,
+                            L->softmax_scale, L->rope_dims, L->rope_base, L->pos_offset, L->B, 1, L->H, L->D, P.N_cap,
+                            L->n_win, &io->out);
+  return launched(launch_attn(AL, w + P.attn_off, P.attn_bytes, s), "csa_decode_step/attention");
 }
 
 }  // extern "C"

@@ -220,7 +220,7 @@ constexpr int kModeGroups = 2;   // no overlap, ratio a multiple of kBatch, row 
 // the store.  Every thread of the workgroup calls it (it holds barriers).
 __device__ __forceinline__ void finish_entry(const CompressArgs& a, bool owner, int64_t b, int64_t I, int c,
                                              float val[kVec], uint32_t* amax_entry, float* ss_entry,
-                                             const double* theta_tab = nullptr) {
+                                             const double* theta_tab = nullptr, int64_t out_row = -1) {
   if (a.norm_w) {  // uniform in the workgroup (one job per workgroup)
     if (owner) {
       float ss = 0.f;
@@ -264,7 +264,7 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, bool owner, 
     if (owner) amax_chunk(a.out, c, val, amax_entry);
     __syncthreads();
   }
-  if (owner) store_chunk(a.out, b * a.out_rows + I, c, val, amax_entry);
+  if (owner) store_chunk(a.out, out_row >= 0 ? out_row : b * a.out_rows + I, c, val, amax_entry);
 }
 
 // Entries of at most kBatch rows (CSA with ratio <= 4, HCA with ratio <= 8): one thread
@@ -631,6 +631,220 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs2 a) {
   }
 }
 
+// ------------------------------------------------------------ decode state append
+
+// One new token per sequence into its state-pool slot ([V4-CN] §3.6.1: the sliding
+// window and the compression branch's uncompressed tail are a per-sequence state of
+// fixed size; a block of ratio tokens is compressed as soon as it is complete).  One
+// workgroup per batch row: the token's stream rows enter the tail ring (row p mod
+// RING, RING = 2 ratio with overlap, ratio without), its raw KV row enters the window
+// (rolled over to the front when the buffer is full), and when p + 1 completes a block
+// the entry (KV, and with overlap the indexer key) is computed from the ring exactly as
+// the bulk compressor does and stored at its pool row in the paged cache.  Thread c <
+// chunks(D) owns KV channels 8c .. 8c+7 and the next chunks(DI) threads the indexer's;
+// a thread reads back only rows written by earlier launches and keeps the new token's
+// values in registers.
+struct AppendArgs {
+  CompressArgs kv;      // ca.. = the new token's rows [B, D]; out / norm / RoPE of the KV entries
+  CompressArgs ik;      // the indexer keys (overlap only; ik.D = DI, no RoPE)
+  int has_ik;
+  const int32_t* slot;  // [B]
+  int64_t* length;      // [slots]
+  void* tail;           // [slots, RING, NST, D] in the stream dtype (NST = 4 with overlap, else 2)
+  void* itail;          // [slots, RING, 4, DI]
+  const void* kv_raw;   // [B, D] in the window dtype
+  void* win;            // [slots, Ws, D]
+  int win_elem;         // bytes per window element (4 or 2)
+  int n_win;
+  int64_t Ws;
+  int64_t* win_pos0;    // [slots]
+  PageMap pmap;         // pool rows of the caches
+  int64_t* q_pos;       // [B] out: the new token's position
+  int64_t* wp0_b;       // [B] out: window base of the batch row's slot
+  int64_t* wp0_adj;     // [B] out: window base such that row b * Ws + (p - base) is the slot's row
+  int32_t* vis_idx;     // [B, vis_K] out (no overlap): pool rows of the visible entries, -1 after
+  int64_t vis_K;
+};
+
+template <typename TIn>
+__device__ __forceinline__ void raw8_store(TIn* p, const Raw8<TIn>& r);
+template <>
+__device__ __forceinline__ void raw8_store<float>(float* p, const Raw8<float>& r) {
+  reinterpret_cast<float4*>(p)[0] = r.a;
+  reinterpret_cast<float4*>(p)[1] = r.b;
+}
+template <>
+__device__ __forceinline__ void raw8_store<uint16_t>(uint16_t* p, const Raw8<uint16_t>& r) {
+  *reinterpret_cast<uint4*>(p) = r.w;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void state_append_kernel(AppendArgs a) {
+  __shared__ uint32_t amax_lds[2][kThreads];
+  __shared__ float ss_lds[2][kThreads];
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t s = a.slot[b];
+  const int64_t p = a.length[s];
+  const int r = a.kv.ratio;
+  const bool ov = a.kv.overlap != 0;
+  const int ring = ov ? 2 * r : r;
+  const int cD = a.kv.chunks, cI = a.has_ik ? a.ik.chunks : 0;
+  const bool kv_part = tid < cD;
+  const bool ik_part = !kv_part && tid < cD + cI;
+  const CompressArgs& A = kv_part ? a.kv : a.ik;
+  const int c = kv_part ? tid : tid - cD;
+  const bool completes = (p + 1) % r == 0;
+  const int64_t I = p / r;
+  for (int i = tid; i < 2 * kThreads; i += kThreads) (&amax_lds[0][0])[i] = 0u;
+
+  float val[kVec];
+  if (kv_part || ik_part) {
+    const int64_t D = A.D;
+    const int d0 = c * kVec;
+    const int ns = (kv_part && !ov) ? 2 : 4;
+    TIn* tl = static_cast<TIn*>(kv_part ? a.tail : a.itail) + s * ring * ns * D + d0;
+    // streams in ring order: overlap (C^a, C^b, Z^a, Z^b), else (C, Z)
+    const void* src[4] = {A.ca, ns == 4 ? A.cb : A.za, A.za, A.zb};
+    Raw8<TIn> cur[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < ns) {
+        cur[q].load(static_cast<const TIn*>(src[q]) + b * D + d0);
+        raw8_store<TIn>(tl + ((p % ring) * ns + q) * D, cur[q]);
+      }
+    }
+    if (completes) {
+      // online softmax per channel over the block's rows (a-branch: block I) and, with
+      // overlap, the previous block's b-branch rows
+      const int zq_a = ns == 4 ? 2 : 1, cq_b = 1, zq_b = 3;
+      float m[kVec], sum[kVec], acc[kVec];
+#pragma unroll
+      for (int ch = 0; ch < kVec; ++ch) {
+        m[ch] = -INFINITY;
+        sum[ch] = 0.f;
+        acc[ch] = 0.f;
+      }
+      const int nrows = (ov && I >= 1) ? 2 * r : r;
+      for (int q = 0; q < nrows; ++q) {
+        const bool in_a = q < r;
+        const int j = in_a ? q : q - r;
+        const int64_t pos = in_a ? I * r + j : (I - 1) * r + j;
+        const int cq = in_a ? 0 : cq_b, zq = in_a ? zq_a : zq_b;
+        Raw8<TIn> cv, zv;
+        if (pos == p) {
+          cv = cur[cq];
+          zv = cur[zq];
+        } else {
+          cv.load(tl + ((pos % ring) * ns + cq) * D);
+          zv.load(tl + ((pos % ring) * ns + zq) * D);
+        }
+        const float* bp = in_a ? A.bias_a : A.bias_b;
+#pragma unroll
+        for (int ch = 0; ch < kVec; ++ch) {
+          const float z = zv.get(ch) + (bp ? bp[j * D + d0 + ch] : 0.f);
+          const float nm = fmaxf(m[ch], z);
+          const float sc = __expf(m[ch] - nm), pz = __expf(z - nm);
+          sum[ch] = sum[ch] * sc + pz;
+          acc[ch] = acc[ch] * sc + pz * cv.get(ch);
+          m[ch] = nm;
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < kVec; ++ch) val[ch] = acc[ch] / sum[ch];
+    }
+  }
+  __syncthreads();  // the LDS maxima are cleared
+  if (completes) {
+    const int64_t row = paged_row(a.pmap, b, I);
+    finish_entry(a.kv, kv_part, 0, I, tid, val, amax_lds[0], ss_lds[0], nullptr, row);
+    if (a.has_ik) finish_entry(a.ik, ik_part, 0, I, tid - cD, val, amax_lds[1], ss_lds[1], nullptr, row);
+  }
+
+  // the raw KV row into the window; a full buffer keeps its last n_win - 1 rows first
+  const int64_t wp0 = a.win_pos0[s];
+  int64_t nwp0 = wp0;
+  const int64_t rowb = static_cast<int64_t>(a.kv.D) * a.win_elem;  // bytes per row
+  const int64_t c16 = rowb / 16;
+  uint8_t* wb = static_cast<uint8_t*>(a.win) + s * a.Ws * rowb;
+  if (p - wp0 >= a.Ws) {
+    nwp0 = p - a.n_win + 1;
+    for (int64_t i = tid; i < static_cast<int64_t>(a.n_win - 1) * c16; i += kThreads) {
+      const int64_t j = i / c16, q = i % c16;
+      reinterpret_cast<uint4*>(wb + j * rowb)[q] = reinterpret_cast<const uint4*>(wb + (nwp0 - wp0 + j) * rowb)[q];
+    }
+  }
+  for (int64_t i = tid; i < c16; i += kThreads)
+    reinterpret_cast<uint4*>(wb + (p - nwp0) * rowb)[i] =
+        reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv_raw) + b * rowb)[i];
+  if (a.vis_idx) {
+    // every entry of a block before the token's own is visible (no overlap: dense)
+    const int64_t vis = p / r;
+    for (int64_t j = tid; j < a.vis_K; j += kThreads)
+      a.vis_idx[b * a.vis_K + j] = j < vis ? static_cast<int32_t>(paged_row(a.pmap, b, j)) : -1;
+  }
+  __syncthreads();  // every thread has read length[s] and win_pos0[s]
+  if (tid == 0) {
+    a.length[s] = p + 1;
+    a.win_pos0[s] = nwp0;
+    a.q_pos[b] = p;
+    a.wp0_b[b] = nwp0;
+    a.wp0_adj[b] = nwp0 - (s - b) * a.Ws;
+  }
+}
+
+}  // namespace
+
+int launch_state_append(const StateAppendLaunch& L, hipStream_t stream) {
+  if (L.B == 0) return 0;
+  AppendArgs a{};
+  CompressArgs& k = a.kv;
+  k.ca = L.ca; k.cb = L.cb; k.za = L.za; k.zb = L.zb;
+  k.bias_a = L.bias_a; k.bias_b = L.bias_b;
+  k.D = L.D; k.ratio = L.ratio; k.overlap = L.overlap; k.R = L.rope_dims;
+  k.pos_offset = L.pos_offset;
+  k.log2_base = L.log2_base;
+  k.out = OutDesc{L.kv_out.data, L.kv_out.rope, L.kv_out.scale, L.kv_out.dtype, L.D, L.rope_dims};
+  k.norm_w = L.norm_w;
+  k.norm_eps = L.norm_eps;
+  k.chunks = L.D / kVec;
+  a.has_ik = L.overlap && L.ica;
+  if (a.has_ik) {
+    CompressArgs& i = a.ik;
+    i = k;
+    i.ca = L.ica; i.cb = L.icb; i.za = L.iza; i.zb = L.izb;
+    i.bias_a = L.ibias_a; i.bias_b = L.ibias_b;
+    i.D = L.DI;
+    i.R = 0;
+    i.out = OutDesc{L.ik_out.data, L.ik_out.rope, L.ik_out.scale, L.ik_out.dtype, L.DI, 0};
+    i.norm_w = nullptr;
+    i.chunks = L.DI / kVec;
+  }
+  if (k.chunks + (a.has_ik ? a.ik.chunks : 0) > kThreads) return -2;
+  a.slot = L.slot;
+  a.length = L.length;
+  a.tail = L.tail;
+  a.itail = L.itail;
+  a.kv_raw = L.kv_raw;
+  a.win = L.win;
+  a.win_elem = L.win_elem;
+  a.n_win = L.n_win;
+  a.Ws = L.Ws;
+  a.win_pos0 = L.win_pos0;
+  a.pmap = L.pmap;
+  a.q_pos = L.q_pos;
+  a.wp0_b = L.wp0_b;
+  a.wp0_adj = L.wp0_adj;
+  a.vis_idx = L.vis_idx;
+  a.vis_K = L.vis_K;
+  const dim3 g(static_cast<uint32_t>(L.B)), t(kThreads);
+  if (L.stream_dtype == CSA_F32) hipLaunchKernelGGL(state_append_kernel<float>, g, t, 0, stream, a);
+  else hipLaunchKernelGGL(state_append_kernel<uint16_t>, g, t, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+namespace {
+
 struct QuantArgs {
   const float* x;
   int64_t rows;
@@ -739,7 +953,7 @@ int launch_compress2(const CompressLaunch& L0, const CompressLaunch& L1, hipStre
 __global__ __launch_bounds__(256) void rmsnorm_kernel(NormArgs a) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
-  norm_row(a.x, a.y, a.w, row, a.D, a.dtype, a.eps, threadIdx.x & 63);
+  norm_row(a.x, row, a.y, row, a.w, a.D, a.dtype, a.eps, threadIdx.x & 63);
 }
 
 int launch_rmsnorm(const csa_buf& x, int64_t rows, int D, const float* w, float eps, const csa_buf& y,

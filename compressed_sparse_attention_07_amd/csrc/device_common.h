@@ -276,4 +276,18 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Paged compressed caches ([V4-CN] §3.6.1): entry e of the sequence in batch row b lives
+// at pool row  table[slot[b] * max_pages + (e >> shift)] << shift | (e & (2^shift - 1)).
+// table == NULL: unpaged, row b * rows_per_seq + e.
+struct PageMap {
+  const int32_t* table;  // [slots, max_pages] page of each block of 2^shift entries
+  const int32_t* slot;   // [B] state slot of each batch row
+  int max_pages, shift;
+};
+
+__device__ __forceinline__ int64_t paged_row(const PageMap& m, int64_t b, int64_t e) {
+  const int64_t page = m.table[static_cast<int64_t>(m.slot[b]) * m.max_pages + (e >> m.shift)];
+  return (page << m.shift) | (e & ((int64_t{1} << m.shift) - 1));
+}
+
 }  // namespace csa

@@ -33,6 +33,8 @@
 // per thread with the token's queries staged (dequantized) in LDS.
 #include "device_common.h"
 #include "launch.h"
+
+#include <algorithm>
 #include "topk_select.h"
 
 namespace csa {
@@ -57,6 +59,21 @@ __device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p
 template <>
 __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 
+// Row of key 0 of the range holding key s0 of batch row b, so that key s of the range
+// sits at row base + s: the sequence's rows, or (paged keys) the page holding s0, whose
+// table entry is read only when the range has keys (pages past the sequence may be
+// unassigned).  Ranges never cross a page (the launches cap them at the page size).
+__device__ __forceinline__ int64_t key_range_base(const IndexLaunch& a, int64_t b, int64_t s0, bool has_keys) {
+  if (!a.kmap.table) return b * a.kI_rows;
+  if (!has_keys) return 0;
+  return paged_row(a.kmap, b, s0) - s0;
+}
+
+// row of key s (per key; the SIMT kernels)
+__device__ __forceinline__ int64_t key_row(const IndexLaunch& a, int64_t b, int64_t s) {
+  return a.kmap.table ? paged_row(a.kmap, b, s) : b * a.kI_rows + s;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kSimtThreads) void index_simt_kernel(IndexLaunch a) {
   __shared__ float qs[kSimtQ];
@@ -69,7 +86,7 @@ __global__ __launch_bounds__(kSimtThreads) void index_simt_kernel(IndexLaunch a)
   if (vis > a.N) vis = a.N;
   if (vis < 0) vis = 0;
   const T* q = static_cast<const T*>(a.qI.data) + bt * a.HI * a.DI;
-  const T* k = static_cast<const T*>(a.kI.data) + (b * a.kI_rows + (s < vis ? s : 0)) * a.DI;
+  const T* k = static_cast<const T*>(a.kI.data) + key_row(a, b, s < vis ? s : 0) * a.DI;
   for (int h = threadIdx.x; h < a.HI; h += kSimtThreads) ws[h] = a.wI[bt * a.HI + h];
   const int hc = kSimtQ / a.DI;             // heads per LDS pass
   float score = 0.f;
@@ -110,7 +127,7 @@ __global__ __launch_bounds__(kSimtThreads) void index_simt_mxfp4_kernel(IndexLau
   const uint8_t* qsc = static_cast<const uint8_t*>(a.qI.scale);
   const uint8_t* kc = static_cast<const uint8_t*>(a.kI.data);
   const uint8_t* ksc = static_cast<const uint8_t*>(a.kI.scale);
-  const int64_t krow = b * a.kI_rows + (s < vis ? s : 0);
+  const int64_t krow = vis > 0 ? key_row(a, b, s < vis ? s : 0) : 0;
   for (int h = threadIdx.x; h < a.HI; h += kSimtThreads) ws[h] = a.wI[bt * a.HI + h];
   const int hc = kSimtQ / a.DI;
   float score = 0.f;
@@ -174,7 +191,8 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
     }
   }
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.kI.data) + b * a.kI_rows * a.DI;
+  const uint16_t* kbase =
+      static_cast<const uint16_t*>(a.kI.data) + key_range_base(a, b, s_begin, s_begin < vis_end) * a.DI;
   // keys of 64 entries starting at s0 (B operand: entry = col, k = 32ks + 8grp .. +8)
   auto load = [&](bf16x8 (&kb)[kTiles][KS], int64_t s0) {
 #pragma unroll
@@ -317,7 +335,8 @@ __global__ __launch_bounds__(NWV * WAVE) void index_stream_kernel(IndexLaunch a,
   vis = vis > a.N ? a.N : (vis < 0 ? 0 : vis);
   const int64_t vis_end = uni64(min(s_end, vis));
   const int nst = vis_end > s_begin ? static_cast<int>((vis_end - s_begin + KPS - 1) / KPS) : 0;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.kI.data) + uni64(b * a.kI_rows) * RB;
+  const uint8_t* kbase =
+      static_cast<const uint8_t*>(a.kI.data) + uni64(key_range_base(a, b, s_begin, vis_end > s_begin)) * RB;
   const uint32_t ring_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wid][0]));
   // stage u: entries s_begin + KPS u ..; load i covers stage bytes [1024 i, +1024)
   auto issue = [&](int u) {
@@ -661,8 +680,9 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
     }
   }
 
-  const uint8_t* kc = static_cast<const uint8_t*>(a.kI.data) + b * a.kI_rows * (DI / 2);
-  const uint8_t* ksp = static_cast<const uint8_t*>(a.kI.scale) + b * a.kI_rows * (DI / 32);
+  const int64_t krow0 = key_range_base(a, b, s_begin, s_begin < vis_end);
+  const uint8_t* kc = static_cast<const uint8_t*>(a.kI.data) + krow0 * (DI / 2);
+  const uint8_t* ksp = static_cast<const uint8_t*>(a.kI.scale) + krow0 * (DI / 32);
   // keys of 64 entries starting at s0: codes (B operand) and the 4 block scales per step
   auto load = [&](uint4 (&kb)[kTiles][KS4], uint32_t (&ks4)[kTiles][KS4], int64_t s0) {
 #pragma unroll
@@ -833,6 +853,10 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
       const int64_t tokens = L.B * L.Tq;
       int kpw = kMxfp4Kpw;
       while (kpw < 8192 && tokens * ((L.N + kpw - 1) / kpw) > 8192) kpw *= 2;
+      if (L.kmap.table) {
+        if ((1 << L.kmap.shift) < kMxfp4Kpw) return -2;
+        kpw = std::min(kpw, 1 << L.kmap.shift);  // a range stays inside one page
+      }
       const int64_t wpt = (L.N + kpw - 1) / kpw;
       const int64_t grid = (tokens * wpt + kWavesPerWG - 1) / kWavesPerWG;
       if (tokens * wpt >= (int64_t{1} << 32)) return -1;  // beyond the kernel's 32-bit wave index
@@ -843,7 +867,9 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  if (L.kmap.table && (L.kmap.shift < 0 || (1 << L.kmap.shift) < index_min_page_entries)) return -2;
   if (L.qI.dtype == CSA_BF16 && L.HI % 16 == 0 && L.DI % 32 == 0 && L.Tq >= kPfTok) {
+    if (L.kmap.table) return -2;  // the prefill kernel reads contiguous keys only
     // many queries per sequence: keys staged once in LDS for kPfTok queries at a time
     PrefillKern k = pick_prefill(L.HI / 16, L.DI / 32);
     if (k) {
@@ -867,6 +893,7 @@ int launch_index_scores(const IndexLaunch& L, hipStream_t stream) {
       const int64_t tokens = L.B * L.Tq;
       int kpw = 128;
       while (kpw < 4096 && tokens * ((L.N + kpw - 1) / kpw) > 8192) kpw *= 2;
+      if (L.kmap.table) kpw = std::min(kpw, 1 << L.kmap.shift);  // a range stays inside one page
       int64_t wpt = (L.N + kpw - 1) / kpw;
       if (streamed) {
         wpt = (wpt + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;  // one token per workgroup

@@ -31,6 +31,35 @@ int launch_compress2(const CompressLaunch& L0, const CompressLaunch& L1, hipStre
 int launch_quantize(const float* x, int64_t rows, int D, int rope_dims, const csa_buf& out,
                     hipStream_t stream);
 
+// One decode token per sequence into its state-pool slot (compress.hip)
+struct StateAppendLaunch {
+  int64_t B;
+  const void *ca, *cb, *za, *zb;      // [B, D] (no overlap: ca = C, za = Z)
+  const float *bias_a, *bias_b;
+  const void *ica, *icb, *iza, *izb;  // [B, DI] (overlap), or ica = NULL
+  const float *ibias_a, *ibias_b;
+  int stream_dtype;
+  int D, DI, ratio, overlap, rope_dims;
+  double log2_base;
+  int64_t pos_offset;
+  const float* norm_w;
+  float norm_eps;
+  csa_buf kv_out, ik_out;             // page pools
+  PageMap pmap;
+  const int32_t* slot;
+  int64_t* length;
+  void *tail, *itail;
+  const void* kv_raw;
+  void* win;
+  int win_elem, n_win;
+  int64_t Ws;
+  int64_t* win_pos0;
+  int64_t *q_pos, *wp0_b, *wp0_adj;   // [B] outputs
+  int32_t* vis_idx;                   // [B, vis_K] (no overlap) or NULL
+  int64_t vis_K;
+};
+int launch_state_append(const StateAppendLaunch& L, hipStream_t stream);
+
 struct IndexLaunch {
   csa_buf qI;
   const float* wI;
@@ -44,21 +73,30 @@ struct IndexLaunch {
   int sel_k;
   float* sel_val;        // [B * Tq, slices, sel_k]
   int32_t* sel_idx;
+  // paged keys (kmap.table != NULL; then kI_rows is unused): the MFMA kernels look a
+  // page up once per key range, so a range must not cross a page (ranges are capped at
+  // 2^kmap.shift entries, which must be at least index_min_page_entries)
+  PageMap kmap;
 };
 int launch_index_scores(const IndexLaunch& L, hipStream_t stream);
+constexpr int index_min_page_entries = 512;  // smallest page the indexer kernels take
 // Decode-shaped bf16 lightning indexer that selects while it scores: every workgroup
 // keeps its slice's top-k candidates (the score row is never stored unless L.scores is
 // set); the candidates then go through topk_merge.  Returns 1 (nothing launched) when
 // the shape is not covered.
 int index_select_slices(const IndexLaunch& L);  // slices per row, 0 if not covered
 int launch_index_select(const IndexLaunch& L, hipStream_t stream);
-// side: a normalization job appended to the final selection launch, or NULL
+// side: a normalization job appended to the final selection launch, or NULL.
+// out_map (table != NULL): the final indices are written as pool rows of a paged cache
+// (row r of the selection belongs to batch row r / tq); -1 padding stays -1.
 int launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int64_t rows, int slices, int k,
-                      int32_t* idx, int32_t* count, hipStream_t stream, const AttnNormArgs* side = nullptr);
+                      int32_t* idx, int32_t* count, hipStream_t stream, const AttnNormArgs* side = nullptr,
+                      const PageMap* out_map = nullptr, int64_t tq = 1);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t N, int k);
 int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count,
-                void* ws, hipStream_t stream, const AttnNormArgs* side = nullptr);
+                void* ws, hipStream_t stream, const AttnNormArgs* side = nullptr, const PageMap* out_map = nullptr,
+                int64_t tq = 1);
 
 struct GroupedProjLaunch {
   const void* o;        // bf16 [T, n_h, c]

@@ -7,7 +7,8 @@
 // The attention operands of a forward are normalized by one job (attn_norm_block):
 // every query head row, and for each sequence only the window rows its queries can see
 // (positions max(0, min q_pos - n_win + 1) .. max q_pos, clipped to the buffer), each
-// written to the same row of a copy.  The job runs as its own launch or as extra
+// written to the same row of a copy (the source window of a batch row may be another
+// row block of the buffer: a state-pool slot).  The job runs as its own launch or as extra
 // workgroups appended to another launch (any whole number of waves per workgroup).
 #pragma once
 
@@ -43,19 +44,19 @@ __device__ __forceinline__ void norm_load8(const void* x, int dtype, int64_t off
 
 // one row (called by a whole wave): the sum of squares, then a second pass over the
 // row (now in cache) that scales and stores, so few registers stay live
-__device__ __forceinline__ void norm_row(const void* x, void* y, const float* w, int64_t row, int D, int dtype,
-                                         float eps, int lane) {
+__device__ __forceinline__ void norm_row(const void* x, int64_t xrow, void* y, int64_t row, const float* w, int D,
+                                         int dtype, float eps, int lane) {
   float ss = 0.f;
   for (int d0 = 8 * lane; d0 < D; d0 += 8 * WAVE) {
     float v[8];
-    norm_load8(x, dtype, row * D + d0, v);
+    norm_load8(x, dtype, xrow * D + d0, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
   }
   const float inv = 1.0f / sqrtf(wave_sum_dpp(ss) / static_cast<float>(D) + eps);
   for (int d0 = 8 * lane; d0 < D; d0 += 8 * WAVE) {
     float v[8];
-    norm_load8(x, dtype, row * D + d0, v);
+    norm_load8(x, dtype, xrow * D + d0, v);
     const float4 w0 = *reinterpret_cast<const float4*>(w + d0);
     const float4 w1 = *reinterpret_cast<const float4*>(w + d0 + 4);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -80,7 +81,8 @@ struct AttnNormArgs {
   void* win_out;
   const float* kv_w;
   const int64_t* q_pos;  // [B, Tq]
-  const int64_t* win_pos0;
+  const int64_t* win_pos0;  // [B] position of row 0 of each batch row's window
+  const int32_t* win_slot;  // [B] or NULL: batch row b's source window is row block win_slot[b] of win
   int64_t B, Tq, Tw;
   int win_dtype, n_win;
   uint32_t q_blocks;     // workgroups of the query part (NW rows each)
@@ -107,7 +109,7 @@ __device__ __forceinline__ void attn_norm_block(const AttnNormArgs& a, uint32_t 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (blk < a.q_blocks) {
     const int64_t row = static_cast<int64_t>(blk) * NW + wid;
-    if (row < a.q.rows) norm_row(a.q.x, a.q.y, a.q.w, row, a.q.D, a.q.dtype, a.q.eps, lane);
+    if (row < a.q.rows) norm_row(a.q.x, row, a.q.y, row, a.q.w, a.q.D, a.q.dtype, a.q.eps, lane);
     return;
   }
   const uint32_t wb = blk - a.q_blocks;
@@ -145,8 +147,10 @@ __device__ __forceinline__ void attn_norm_block(const AttnNormArgs& a, uint32_t 
   first = first < 0 ? 0 : first;
   first = first < wp0 ? wp0 : first;
   const int64_t last = hi < wp0 + a.Tw - 1 ? hi : wp0 + a.Tw - 1;
+  const int64_t src_b = a.win_slot ? static_cast<int64_t>(a.win_slot[b]) : b;
   for (int64_t p = first + static_cast<int64_t>(part) * NW + wid; p <= last; p += static_cast<int64_t>(a.w_blocks) * NW)
-    norm_row(a.win, a.win_out, a.kv_w, b * a.Tw + (p - wp0), a.q.D, a.win_dtype, a.q.eps, lane);
+    norm_row(a.win, src_b * a.Tw + (p - wp0), a.win_out, b * a.Tw + (p - wp0), a.kv_w, a.q.D, a.win_dtype, a.q.eps,
+             lane);
 }
 
 }  // namespace csa

@@ -70,6 +70,8 @@ __device__ __forceinline__ void redo_row(const TopkArgs& a, Shared<NT>& sh, int6
   c.k = a.k;
   c.out_idx = a.out_idx;
   c.count = a.count;
+  c.omap = a.omap;
+  c.tq = a.tq;
   load_slice<NT, PER, true>(c, r, v);
   select_slice<NT, PER, true, true>(c, sh, r, v);
 }
@@ -292,9 +294,13 @@ size_t topk_workspace_bytes(int64_t rows, int64_t N, int k) {
 
 namespace {
 
-// the final launch's block count with a side job shaped for its workgroups
-int64_t with_side(TopkArgs& a, int64_t blocks, const Shape& s, const AttnNormArgs* side) {
+// the final launch's block count with a side job shaped for its workgroups (and its
+// output translation to pool rows)
+int64_t with_side(TopkArgs& a, int64_t blocks, const Shape& s, const AttnNormArgs* side, const PageMap* out_map,
+                  int64_t tq) {
   a.main_blocks = static_cast<uint32_t>(blocks);
+  if (out_map) a.omap = *out_map;
+  a.tq = tq > 0 ? tq : 1;
   if (!side) return blocks;
   a.side = *side;
   attn_norm_shape(a.side, s.nt / WAVE);
@@ -303,7 +309,7 @@ int64_t with_side(TopkArgs& a, int64_t blocks, const Shape& s, const AttnNormArg
 
 int run_levels(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, char* w,
                size_t one, const Levels& L, const float* row_tau, int32_t* redo, int32_t* cnt, hipStream_t stream,
-               const AttnNormArgs* side) {
+               const AttnNormArgs* side, const PageMap* out_map, int64_t tq) {
   const float* in_val = nullptr;
   const int32_t* in_idx = nullptr;
   for (int i = 0; i < L.n; ++i) {
@@ -332,7 +338,8 @@ int run_levels(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx
       a.out_idx = reinterpret_cast<int32_t*>(buf + n_out * sizeof(uint32_t));
     }
     const Shape s = shape_for(a.slice);
-    const int64_t blocks = final_level ? with_side(a, rows * L.slices[i], s, side) : rows * L.slices[i];
+    const int64_t blocks =
+        final_level ? with_side(a, rows * L.slices[i], s, side, out_map, tq) : rows * L.slices[i];
     if (blocks >= (int64_t(1) << 32)) return -4;
     if (i == 0) {
       if (final_level) launch_shape<false, true>(s, blocks, a, stream);
@@ -366,7 +373,8 @@ int run_levels(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx
 // entry indices in entry order, -inf / -1 padded): the lists of a row are concatenated
 // (still in entry order) and selected once, exactly as the last level of run_levels.
 int launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int64_t rows, int slices, int k,
-                      int32_t* idx, int32_t* count, hipStream_t stream, const AttnNormArgs* side) {
+                      int32_t* idx, int32_t* count, hipStream_t stream, const AttnNormArgs* side,
+                      const PageMap* out_map, int64_t tq) {
   if (rows == 0) return 0;
   TopkArgs a{};
   a.in_val = cand_val;
@@ -379,20 +387,20 @@ int launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int64_t ro
   a.count = count;
   if (a.n_in > kShapes[3].cap()) return -2;
   const Shape s = shape_for(a.n_in);
-  const int64_t blocks = with_side(a, rows, s, side);
+  const int64_t blocks = with_side(a, rows, s, side, out_map, tq);
   if (blocks >= (int64_t(1) << 32)) return -4;
   launch_shape<true, true>(s, blocks, a, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* idx, int32_t* count, void* ws,
-                hipStream_t stream, const AttnNormArgs* side) {
+                hipStream_t stream, const AttnNormArgs* side, const PageMap* out_map, int64_t tq) {
   if (rows == 0) return 0;
   const Levels L = N > 0 ? plan_levels(rows, N, k) : Levels{1, {0}, {1}, {1}};
   const size_t one = level_buffer_bytes(rows, L, k);
   char* w = static_cast<char*>(ws);
   const uint32_t rank = N > 0 ? tau_rank(rows, N, k, L) : 0u;
-  if (rank == 0) return run_levels(scores, rows, N, k, idx, count, w, one, L, nullptr, nullptr, nullptr, stream, side);
+  if (rank == 0) return run_levels(scores, rows, N, k, idx, count, w, one, L, nullptr, nullptr, nullptr, stream, side, out_map, tq);
   float* tau = reinterpret_cast<float*>(w + 2 * one);
   int32_t* redo = reinterpret_cast<int32_t*>(w + 2 * one + static_cast<size_t>(rows) * 4);
   int32_t* cnt = reinterpret_cast<int32_t*>(w + 2 * one + static_cast<size_t>(rows) * 8);
@@ -400,7 +408,7 @@ int launch_topk(const float* scores, int64_t rows, int64_t N, int k, int32_t* id
   hipLaunchKernelGGL(topk_tau_kernel, dim3(static_cast<uint32_t>((rows + rows_per_wg - 1) / rows_per_wg)),
                      dim3(kTauThreads), 0, stream, scores, rows, N, rank, tau);
   if (hipGetLastError() != hipSuccess) return -1;
-  return run_levels(scores, rows, N, k, idx, count, w, one, L, tau, redo, cnt, stream, side);
+  return run_levels(scores, rows, N, k, idx, count, w, one, L, tau, redo, cnt, stream, side, out_map, tq);
 }
 
 }  // namespace csa

@@ -62,6 +62,10 @@ struct TopkArgs {
   // independent normalization job instead (side.blocks = 0: none)
   uint32_t main_blocks;
   AttnNormArgs side;
+  // final level: omap.table != NULL writes each selected entry as its pool row in a
+  // paged cache (selection row r belongs to batch row r / tq)
+  PageMap omap;
+  int64_t tq;
 };
 
 constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one wave
@@ -491,7 +495,9 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
     ov = a.out_val + o;
   }
   auto put = [&](int j, uint32_t slot) {
-    oi[slot] = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(lo + j * NT + tid);
+    const int32_t e = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(lo + j * NT + tid);
+    if (FINAL && a.omap.table) oi[slot] = static_cast<int32_t>(paged_row(a.omap, r / a.tq, e));
+    else oi[slot] = e;
     if (!FINAL) ov[slot] = v[j];
   };
   if (one_test && with_eq) {

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum csa_status {
   CSA_OK = 0,
@@ -383,6 +383,106 @@ typedef struct csa_forward_io {
 size_t csa_forward_workspace_size(const csa_layer_desc* L);
 csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* ws,
                        size_t ws_bytes, void* stream);
+
+/*
+ * csa_decode_step -- one decode token per sequence, with a state cache and paged
+ * compressed caches ([V4-CN] §3.6.1: the sliding window and the compression branch's
+ * uncompressed tail are a fixed-size per-sequence state taken from a preallocated pool;
+ * the compressed caches are blocks of page_tokens raw tokens, which may be any multiple
+ * of lcm(m, m'), so one block table serves CSA and HCA layers).
+ *
+ * For batch row b, slot s = slot[b], position p = length[s]:
+ *   1. the token's stream rows enter the slot's tail ring and its raw KV row the window;
+ *      when p + 1 is a multiple of ratio, the block's entry (CSA: and its indexer key)
+ *      is compressed exactly as csa_compress_norm would, into the paged cache at entry
+ *      p / ratio;
+ *   2. CSA: the query at position p is scored against the entries it may see
+ *      (e < p / ratio) and the top-k kept (as csa_index_topk); HCA: every entry it may
+ *      see is used;
+ *   3. core attention over those entries and the raw window positions
+ *      max(0, p - n_win + 1) .. p, with the sink (as csa_sparse_mqa / hca_dense_attn);
+ *   4. length[s] = p + 1.
+ * Every slot has its own length (ragged batches).  A sequence's result does not depend
+ * on the other sequences of the batch: no step reduces across sequences, and the split
+ * of a query's keys over workgroups depends only on the layer shape.
+ *
+ * State pool (caller-owned device memory):
+ *   length     int64 [slots]
+ *   tail       CSA: [slots, 2 ratio, 4, D], the C^a, C^b, Z^a, Z^b rows of position q at
+ *              ring row q mod 2 ratio; HCA: [slots, ratio, 2, D], the C, Z rows at ring
+ *              row q mod ratio; in stream_dtype.  Precondition: the rows of positions
+ *              ratio * (floor(length / ratio) - 1) .. length - 1 (those >= 0) (HCA: of
+ *              the current block) are in the ring.
+ *   itail      CSA: [slots, 2 ratio, 4, DI], the indexer streams, same rule
+ *   win        [slots, 2 n_win, D] raw KV rows, F32 or BF16: row j holds position
+ *              win_pos0[s] + j.  Precondition: positions max(0, length - n_win + 1) ..
+ *              length - 1 are present, and length - win_pos0[s] <= 2 n_win.  A row that
+ *              would fall past the buffer first moves the last n_win - 1 rows to the front
+ *              (win_pos0 advances).
+ *   win_pos0   int64 [slots]
+ * Paged caches, P = page_tokens / ratio entries per page:
+ *   kv_pages   [pages, P, D], the dtype of win (F32 or BF16)
+ *   ik_pages   [pages, P, DI] (CSA), the dtype of qI (F32, BF16 or MXFP4)
+ *   block_table int32 [slots, max_pages]: page holding entries j P .. (j + 1) P - 1 of the
+ *              slot.  Precondition: assigned for every block holding an entry
+ *              < (length + 1) / ratio.
+ * Step tensors: ca, cb, za, zb [B, D] (HCA: ca = C, za = Z) and ica, icb, iza, izb
+ *   [B, DI] (CSA): the new token's streams, in stream_dtype; biases as csa_compress;
+ *   kv_raw [B, D] in win's dtype; q [B, H, D] and out (q's dtype); qI [B, HI, DI] and wI
+ *   [B, HI] (CSA); sink [H]; q_norm / kv_norm [D] with CSA_FLAG_QKV_NORM.
+ *   idx_out (optional, CSA) int32 [B, topk]: the selected entries' pool rows (page * P +
+ *   offset), in increasing entry order, -1 padded.  scores_out (optional, CSA) float
+ *   [B, max_pages * P].
+ * Limits: page_tokens a power of two and a multiple of ratio; CSA: P >= 512 (an indexer
+ *   key range stays inside one page) and D + DI <= 2048; D <= 1024; distinct slots within
+ *   a batch; max_pages * P < 2^31.  FP8MIX caches are not taken here.
+ */
+typedef struct csa_decode_desc {
+  int32_t struct_size;   /* sizeof(csa_decode_desc) */
+  int32_t mode;          /* csa_mode */
+  int64_t B;             /* sequences in this step */
+  int64_t slots;         /* state-pool slots */
+  int64_t pages;         /* pages of each cache pool */
+  int32_t max_pages;     /* block-table row length */
+  int32_t page_tokens;   /* raw tokens per page */
+  int32_t D, H, HI, DI;
+  int32_t ratio, topk, n_win, rope_dims;
+  float rope_base, softmax_scale;
+  int64_t pos_offset;
+  int32_t stream_dtype;  /* F32 or BF16 */
+  int32_t flags;         /* CSA_FLAG_BF16_SCORES, CSA_FLAG_QKV_NORM */
+  float norm_eps;
+  int32_t reserved;      /* 0 */
+} csa_decode_desc;
+
+typedef struct csa_decode_io {
+  const int32_t* slot;                   /* [B] */
+  int64_t* length;                       /* [slots] in/out */
+  const void *ca, *cb, *za, *zb;         /* [B, D] */
+  const float *bias_a, *bias_b;          /* [ratio, D] or NULL */
+  const void *ica, *icb, *iza, *izb;     /* [B, DI] (CSA) */
+  const float *ibias_a, *ibias_b;
+  const void* kv_raw;                    /* [B, D] */
+  void* tail;                            /* state pool, in/out */
+  void* itail;
+  csa_buf win;
+  int64_t* win_pos0;
+  csa_buf kv_pages;                      /* paged caches, in/out */
+  csa_buf ik_pages;
+  const int32_t* block_table;
+  csa_buf q;                             /* [B, H, D] */
+  csa_buf qI;                            /* [B, HI, DI] (CSA) */
+  const float* wI;                       /* [B, HI] (CSA) */
+  const float* sink;                     /* [H] */
+  csa_buf out;                           /* [B, H, D] */
+  const float *q_norm, *kv_norm;         /* [D] (CSA_FLAG_QKV_NORM) */
+  int32_t* idx_out;                      /* optional [B, topk] (CSA) */
+  float* scores_out;                     /* optional [B, max_pages * P] (CSA) */
+} csa_decode_io;
+
+size_t csa_decode_step_workspace_size(const csa_decode_desc* L);
+csa_status csa_decode_step(const csa_decode_desc* L, const csa_decode_io* io, void* ws,
+                           size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -186,6 +186,48 @@ int main(void) {
         d.flags = 0;
       }
   }
+  /* decode step descriptors */
+  {
+    csa_decode_desc d;
+    csa_decode_io io;
+    memset(&d, 0, sizeof d);
+    memset(&io, 0, sizeof io);
+    expect(csa_decode_step(&d, &io, NULL, 0, NULL) == CSA_ERR_SHAPE, "decode: struct_size");
+    expect(csa_decode_step(NULL, &io, NULL, 0, NULL) == CSA_ERR_NULL, "decode: NULL descriptor");
+    d.struct_size = (int32_t)sizeof d;
+    d.B = 16;
+    d.slots = 16;
+    d.pages = 1100;
+    d.max_pages = 64;
+    d.page_tokens = 2048;
+    d.D = 512;
+    d.H = 128;
+    d.HI = 64;
+    d.DI = 128;
+    d.ratio = 4;
+    d.topk = 1024;
+    d.n_win = 128;
+    d.rope_dims = 64;
+    d.rope_base = 1e4f;
+    d.softmax_scale = 1.f;
+    d.stream_dtype = CSA_BF16;
+    expect(csa_decode_step_workspace_size(&d) > 0, "decode: size");
+    expect(csa_decode_step(&d, &io, NULL, 0, NULL) == CSA_ERR_NULL, "decode: empty io");
+    const int32_t pts[] = {1024, 3072, 2, 1 << 30};
+    for (unsigned i = 0; i < sizeof pts / sizeof pts[0]; ++i) {
+      d.page_tokens = pts[i];
+      expect(csa_decode_step_workspace_size(&d) == 0, "decode: bad page size");
+    }
+    d.page_tokens = 2048;
+    d.mode = CSA_MODE_HCA;
+    d.ratio = 128;
+    d.page_tokens = 4096;
+    d.max_pages = 256;
+    expect(csa_decode_step_workspace_size(&d) > 0, "decode: HCA size");
+    d.flags = CSA_FLAG_QKV_NORM;
+    d.norm_eps = 1e-6f;
+    expect(csa_decode_step_workspace_size(&d) > 0, "decode: HCA size with norms");
+  }
   if (failures == 0) printf("abi host check: ok\n");
   return failures == 0 ? 0 : 1;
 }

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.csa_abi_version() == 3
+    assert L.csa_abi_version() == 4
 
 
 def test_struct_layouts_match_the_header(tmp_path):
@@ -40,11 +40,13 @@ def test_struct_layouts_match_the_header(tmp_path):
     field offsets (the header compiled by the host C compiler)."""
     import shutil
     import subprocess
-    from compressed_sparse_attention_07_amd._lib import csa_forward_io, csa_layer_desc
+    from compressed_sparse_attention_07_amd._lib import (csa_decode_desc, csa_decode_io, csa_forward_io,
+                                                         csa_layer_desc)
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    fields = {"csa_layer_desc": csa_layer_desc, "csa_forward_io": csa_forward_io}
+    fields = {"csa_layer_desc": csa_layer_desc, "csa_forward_io": csa_forward_io, "csa_decode_desc": csa_decode_desc,
+              "csa_decode_io": csa_decode_io}
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "csa.h"', "int main(void) {"]
     for sname, cls in fields.items():
         lines.append(f'  printf("{sname} %zu\\n", sizeof({sname}));')
@@ -152,6 +154,49 @@ def test_forward_norm_flag_needs_weights(L):
     d.reserved = 0
     io = csa_forward_io()
     assert L.csa_forward(C.byref(d), C.byref(io), None, 0, None) != 0
+
+
+def _decode_desc(**over):
+    from compressed_sparse_attention_07_amd import decode_desc
+    kw = dict(mode=0, B=16, slots=16, pages=1100, max_pages=64, page_tokens=2048, D=512, H=128, HI=64, DI=128,
+              ratio=4, topk=1024, n_win=128, rope_dims=64, rope_base=10000.0, softmax_scale=0.044, stream_dtype=1)
+    kw.update(over)
+    return decode_desc(**kw)
+
+
+def test_decode_step_rejects_bad_descriptors(L):
+    """Page size rules (a power of two, a multiple of the ratio; CSA pages of at least
+    512 entries so an indexer key range stays in one page), shape limits and the struct
+    size: rejected by the size query (0) and the call."""
+    from compressed_sparse_attention_07_amd._lib import csa_decode_io
+    assert L.csa_decode_step_workspace_size(C.byref(_decode_desc())) > 0
+    assert L.csa_decode_step_workspace_size(C.byref(_decode_desc(mode=1, ratio=128, page_tokens=4096))) > 0
+    bad = [dict(page_tokens=3072), dict(page_tokens=1024), dict(page_tokens=2), dict(DI=1024),
+           dict(B=17), dict(max_pages=0), dict(ratio=0), dict(topk=0), dict(n_win=0), dict(flags=8),
+           dict(reserved=1), dict(D=2048)]
+    io = csa_decode_io()
+    for over in bad:
+        d = _decode_desc(**over)
+        assert L.csa_decode_step_workspace_size(C.byref(d)) == 0, over
+        assert L.csa_decode_step(C.byref(d), C.byref(io), None, 0, None) != 0, over
+    d = _decode_desc()
+    d.struct_size = 8
+    assert L.csa_decode_step(C.byref(d), C.byref(io), None, 0, None) == 2
+    # a valid descriptor with empty io: a missing pointer is reported, nothing launched
+    assert L.csa_decode_step(C.byref(_decode_desc()), C.byref(io), None, 0, None) == 1
+    # no sequences: nothing to do
+    assert L.csa_decode_step(C.byref(_decode_desc(B=0)), C.byref(io), None, 0, None) == 0
+
+
+def test_decode_workspace_grows_with_norms_and_scales_with_batch(L):
+    from compressed_sparse_attention_07_amd import CSA_FLAG_QKV_NORM
+    a = L.csa_decode_step_workspace_size(C.byref(_decode_desc(B=1)))
+    b = L.csa_decode_step_workspace_size(C.byref(_decode_desc(B=16)))
+    n = L.csa_decode_step_workspace_size(C.byref(_decode_desc(B=16, flags=CSA_FLAG_QKV_NORM, norm_eps=1e-6)))
+    assert 0 < a < b < n
+    # HCA uses every visible entry: the index list spans the whole block table
+    h = L.csa_decode_step_workspace_size(C.byref(_decode_desc(mode=1, ratio=128, page_tokens=4096, max_pages=256)))
+    assert h >= 16 * 256 * 32 * 4
 
 
 def test_topk_and_index_reject_bad_arguments(L):

@@ -339,9 +339,10 @@ def _attn_kernels(ws, M, sparse: bool) -> str:
     when the key range is split (the call then needs a workspace for the partials)."""
     # D = 512 with 64 RoPE dims takes the LDS-DMA kernels (bf16 or FP8MIX cache; FP8MIX
     # with 4 or 8 waves); sparse bf16 launches with fewer than 256 query tokens per
-    # sequence (128 heads) take the wave-pair kernel
+    # sequence (128 heads) and at most 4096 key slots per query take the wave-pair kernel
     dma = M["D"] == 512 and M["R"] == 64 and (M["kv_format"] != "fp8mix" or M["H"] % 64 == 0)
-    pair = dma and sparse and M["kv_format"] != "fp8mix" and M["Tq"] * max(1, M["H"] // 128) < 256
+    pair = (dma and sparse and M["kv_format"] != "fp8mix" and M["Tq"] * max(1, M["H"] // 128) < 256 and
+            M["k"] + M["W"] <= 4096)
     main = "attn_pair_kernel" if pair else ("attn_dma_kernel" if dma else "attn_mfma_kernel")
     return main + ("+attn_combine_kernel" if ws.numel() > 1 else "")
 
@@ -727,6 +728,75 @@ def layer_edges(wl: Workload, steps: int, reps: int):
     return out
 
 
+def decode_state_bench(wl: Workload, steps: int, warmup: int):
+    """The same decode layer served by csa_decode_step from a state pool and paged caches
+    (ragged lengths near the workload's context; every step appends one token per
+    sequence, so blocks complete and windows roll over as in serving).  Returns the
+    step rate, or None for workloads it does not cover."""
+    import torch
+
+    import compressed_sparse_attention_07_amd as csa
+    from synth import Gen, qstd
+
+    M = wl.meta
+    if M["Tq"] != 1 or M["kv_format"] == "fp8mix" or M["ik_format"] == "mxfp4":
+        return None
+    csa_mode = M["mode"] == "csa"
+    B, D, H, HI, DI, k, W, m, ctx, R = (M[x] for x in ("B", "D", "H", "HI", "DI", "k", "W", "m", "ctx", "R"))
+    cfg = wl.cfg
+    page_tokens = 2048 if csa_mode else 4096
+    total = steps + warmup + 4
+    # ragged lengths just below the context, so that every query sees at most the
+    # workload's entry count (the row length the top-k planner is shaped for)
+    lengths = [ctx - total - 2 * m - (b * 37) % 509 for b in range(B)]
+    max_pages = -(-ctx // page_tokens)
+    pages = B * max_pages
+    g = Gen(cfg.seed + 991, "cuda")
+    bf = torch.bfloat16
+    pool = csa.DecodePool(mode=csa.CSA_MODE_CSA if csa_mode else csa.CSA_MODE_HCA, slots=B, pages=pages,
+                          max_pages=max_pages, page_tokens=page_tokens, D=D, DI=DI, ratio=m, n_win=W,
+                          stream_dtype=csa.CSA_BF16, kv_dtype=csa.CSA_BF16, ik_dtype=csa.CSA_BF16)
+    gen = torch.Generator().manual_seed(cfg.seed)
+    pool.block_table.copy_(torch.randperm(pages, generator=gen).view(B, max_pages).to(torch.int32))
+    for x in (pool.kv_pages.data, pool.ik_pages.data if csa_mode else None, pool.tail, pool.itail, pool.win):
+        if x is not None:
+            for r0 in range(0, x.shape[0], 64):
+                x[r0:r0 + 64].copy_(g.normal(x[r0:r0 + 64].shape, 0.5, dtype=bf))
+    pool.length.copy_(torch.tensor(lengths, dtype=torch.int64))
+    pool.win_pos0.copy_(torch.tensor([n - W + 1 for n in lengths], dtype=torch.int64))
+    ns = 4 if csa_mode else 2
+    st = [g.normal((B, D), dtype=bf) for _ in range(ns)]
+    io = dict(pool.io(), slot=torch.arange(B, dtype=torch.int32, device="cuda"), kv_raw=g.normal((B, D), dtype=bf),
+              q=g.normal((B, H, D), qstd(D), dtype=bf), sink=g.normal((H,)),
+              out=torch.empty((B, H, D), dtype=bf, device="cuda"))
+    if csa_mode:
+        ist = [g.normal((B, DI), dtype=bf) for _ in range(4)]
+        io.update(ca=st[0], cb=st[1], za=st[2], zb=st[3], ica=ist[0], icb=ist[1], iza=ist[2], izb=ist[3],
+                  qI=g.normal((B, HI, DI), qstd(DI), dtype=bf), wI=g.uniform((B, HI)))
+    else:
+        io.update(ca=st[0], za=st[1])
+    desc = csa.decode_desc(mode=csa.CSA_MODE_CSA if csa_mode else csa.CSA_MODE_HCA, B=B, slots=B, pages=pages,
+                           max_pages=max_pages, page_tokens=page_tokens, D=D, H=H, HI=HI, DI=DI, ratio=m, topk=k,
+                           n_win=W, rope_dims=R, rope_base=cfg.rope_base, softmax_scale=cfg.softmax_scale,
+                           stream_dtype=csa.CSA_BF16)
+    ws = torch.empty(max(1, csa.csa_decode_step_workspace_size(desc)), dtype=torch.uint8, device="cuda")
+    call = csa.PreparedCall(csa.csa_decode_step, desc, io, ws=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log(f"  decode state step (ragged, paged {page_tokens}-token blocks): {ms * 1e3:.1f} us")
+    return dict(ms_per_step=round(ms, 5), value=round(B / (ms * 1e-3), 1), unit="tokens/s", B=B,
+                lengths=f"{min(lengths)}..{max(lengths)}", page_tokens=page_tokens,
+                step="csa_decode_step: append + (index + top-k) + attention")
+
+
 # ============================================================================ main
 
 
@@ -787,6 +857,7 @@ def main():
 
     wl, value, ms_per_step, stage_out, roofline = run_workload(args.config, steps, warmup, layers, reps)
     edges = layer_edges(wl, steps, reps)
+    dstate = decode_state_bench(wl, steps, warmup)
 
     if args.copy_probe:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB): the
@@ -825,6 +896,8 @@ def main():
         line["cache_build_compress"] = wl.build
     if edges:
         line["layer_edges"] = edges
+    if dstate:
+        line["decode_state"] = dstate
     if not args.no_others:
         # the other workloads at their full sizes, fewer steps each: their step rate,
         # every stage's time and fraction of peak, and the dominant stage's roofline
@@ -841,6 +914,9 @@ def main():
             e2 = layer_edges(w2, 16 if dec else 3, 10 if dec else 3)
             if e2:
                 others[WORKLOAD_TAGS[key]]["layer_edges"] = e2
+            d2 = decode_state_bench(w2, 16, 4) if dec else None
+            if d2:
+                others[WORKLOAD_TAGS[key]]["decode_state"] = d2
             del w2
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)

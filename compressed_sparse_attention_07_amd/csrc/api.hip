@@ -867,7 +867,8 @@ csa_status validate_decode_desc(const csa_decode_desc* L) {
                   index_min_page_entries * L->ratio);
     if (L->HI < 1 || L->HI > 128 || L->DI < 8 || L->DI > 512 || L->DI % 8)
       return fail(CSA_ERR_SHAPE, "indexer shape HI=%d DI=%d unsupported", L->HI, L->DI);
-    if (L->D + L->DI > 2048) return fail(CSA_ERR_UNSUPPORTED, "D + DI must be <= 2048");
+    if ((L->D / 8 + 63) / 64 * 64 + L->DI / 8 > 256)
+      return fail(CSA_ERR_UNSUPPORTED, "D / 8 rounded up to a multiple of 64, plus DI / 8, must be <= 256");
   }
   return CSA_OK;
 }

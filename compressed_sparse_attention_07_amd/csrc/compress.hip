@@ -678,110 +678,198 @@ __device__ __forceinline__ void raw8_store<uint16_t>(uint16_t* p, const Raw8<uin
   *reinterpret_cast<uint4*>(p) = r.w;
 }
 
+constexpr int kAppendBatch = 8;   // ring rows loaded together by the append kernel
+constexpr int kAppendGroups = 4;  // row groups of a long block (no indexer part)
+
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void state_append_kernel(AppendArgs a) {
   __shared__ uint32_t amax_lds[2][kThreads];
   __shared__ float ss_lds[2][kThreads];
+  __shared__ double theta_lds[64];  // RoPE angles, R <= 128
+  __shared__ float part_lds[kThreads * 3 * kVec];  // row-group partials (max, sum, weighted sum)
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
-  const int64_t s = a.slot[b];
-  const int64_t p = a.length[s];
   const int r = a.kv.ratio;
   const bool ov = a.kv.overlap != 0;
   const int ring = ov ? 2 * r : r;
+  // KV chunks on the first waves, the indexer's from the next wave on: the part a
+  // thread serves is uniform in its wave, so its arguments stay scalar.  Without an
+  // indexer part the waves split a block's rows into G groups instead (HCA: 128 rows).
   const int cD = a.kv.chunks, cI = a.has_ik ? a.ik.chunks : 0;
-  const bool kv_part = tid < cD;
-  const bool ik_part = !kv_part && tid < cD + cI;
+  const int ik0 = (cD + WAVE - 1) / WAVE * WAVE;
+  const int G = a.has_ik ? 1 : max(1, min(kAppendGroups, kThreads / ik0));
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const bool kv_part = wave < G * (ik0 / WAVE);
+  const int g = kv_part ? wave / (ik0 / WAVE) : 0;
+  const int c = kv_part ? tid - g * ik0 : tid - ik0;
+  const bool mine = kv_part ? c < cD : c < cI;
+  const bool ik_part = !kv_part && mine;
   const CompressArgs& A = kv_part ? a.kv : a.ik;
-  const int c = kv_part ? tid : tid - cD;
+  const int64_t D = A.D;
+  const int d0 = c * kVec;
+  const int ns = (kv_part && !ov) ? 2 : 4;  // streams in ring order: (C^a, C^b, Z^a, Z^b), or (C, Z)
+  // the token's rows first: they do not depend on the slot's state
+  Raw8<TIn> cur[4];
+  if (mine) {
+    const void* src[4] = {A.ca, ns == 4 ? A.cb : A.za, A.za, A.zb};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < ns) cur[q].load(static_cast<const TIn*>(src[q]) + b * D + d0);
+  }
+  const int64_t s = a.slot[b];
+  const int64_t p = a.length[s];
+  const int64_t wp0 = a.win_pos0[s];
   const bool completes = (p + 1) % r == 0;
   const int64_t I = p / r;
+  const int64_t out_row = completes ? paged_row(a.pmap, b, I) : 0;
   for (int i = tid; i < 2 * kThreads; i += kThreads) (&amax_lds[0][0])[i] = 0u;
+  if (a.kv.R > 0 && tid < a.kv.R / 2) theta_lds[tid] = rope_theta_rev(tid, a.kv.R, a.kv.log2_base);
+
+  // the raw KV row into the window; a full buffer first keeps its last n_win - 1 rows
+  const int64_t nwp0 = p - wp0 >= a.Ws ? p - a.n_win + 1 : wp0;
+  {
+    const int64_t rowb = static_cast<int64_t>(a.kv.D) * a.win_elem;  // bytes per row
+    const int64_t c16 = rowb / 16;
+    uint8_t* wb = static_cast<uint8_t*>(a.win) + s * a.Ws * rowb;
+    if (nwp0 != wp0) {
+      for (int64_t i = tid; i < static_cast<int64_t>(a.n_win - 1) * c16; i += kThreads) {
+        const int64_t j = i / c16, q = i % c16;
+        reinterpret_cast<uint4*>(wb + j * rowb)[q] = reinterpret_cast<const uint4*>(wb + (nwp0 - wp0 + j) * rowb)[q];
+      }
+    }
+    for (int64_t i = tid; i < c16; i += kThreads)
+      reinterpret_cast<uint4*>(wb + (p - nwp0) * rowb)[i] =
+          reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv_raw) + b * rowb)[i];
+  }
+  if (a.vis_idx) {
+    // every entry of a block before the token's own is visible (no overlap: dense);
+    // the table entries of a batch are read before its stores
+    const int64_t vis = p / r;
+    const int32_t* __restrict__ tbl = a.pmap.table + s * a.pmap.max_pages;
+    int32_t* __restrict__ out = a.vis_idx + b * a.vis_K;
+    const int64_t mask = (int64_t{1} << a.pmap.shift) - 1;
+    for (int64_t j0 = tid; j0 < a.vis_K; j0 += 8 * kThreads) {
+      int32_t pg[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + u * kThreads;
+        pg[u] = j < vis ? tbl[j >> a.pmap.shift] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + u * kThreads;
+        if (j < a.vis_K) out[j] = j < vis ? static_cast<int32_t>((static_cast<int64_t>(pg[u]) << a.pmap.shift) | (j & mask)) : -1;
+      }
+    }
+  }
 
   float val[kVec];
-  if (kv_part || ik_part) {
-    const int64_t D = A.D;
-    const int d0 = c * kVec;
-    const int ns = (kv_part && !ov) ? 2 : 4;
+  float m[kVec], sum[kVec], acc[kVec];
+  if (mine) {
     TIn* tl = static_cast<TIn*>(kv_part ? a.tail : a.itail) + s * ring * ns * D + d0;
-    // streams in ring order: overlap (C^a, C^b, Z^a, Z^b), else (C, Z)
-    const void* src[4] = {A.ca, ns == 4 ? A.cb : A.za, A.za, A.zb};
-    Raw8<TIn> cur[4];
+    if (g == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q < ns) {
-        cur[q].load(static_cast<const TIn*>(src[q]) + b * D + d0);
-        raw8_store<TIn>(tl + ((p % ring) * ns + q) * D, cur[q]);
-      }
+      for (int q = 0; q < 4; ++q)
+        if (q < ns) raw8_store<TIn>(tl + ((p % ring) * ns + q) * D, cur[q]);
     }
     if (completes) {
       // online softmax per channel over the block's rows (a-branch: block I) and, with
-      // overlap, the previous block's b-branch rows
-      const int zq_a = ns == 4 ? 2 : 1, cq_b = 1, zq_b = 3;
-      float m[kVec], sum[kVec], acc[kVec];
+      // overlap, the previous block's b-branch rows, kAppendBatch rows loaded at a time;
+      // the token's own row comes from registers
+      const int zq_a = ns == 4 ? 2 : 1;
 #pragma unroll
       for (int ch = 0; ch < kVec; ++ch) {
         m[ch] = -INFINITY;
         sum[ch] = 0.f;
         acc[ch] = 0.f;
       }
-      const int nrows = (ov && I >= 1) ? 2 * r : r;
-      for (int q = 0; q < nrows; ++q) {
-        const bool in_a = q < r;
-        const int j = in_a ? q : q - r;
-        const int64_t pos = in_a ? I * r + j : (I - 1) * r + j;
-        const int cq = in_a ? 0 : cq_b, zq = in_a ? zq_a : zq_b;
-        Raw8<TIn> cv, zv;
-        if (pos == p) {
-          cv = cur[cq];
-          zv = cur[zq];
-        } else {
-          cv.load(tl + ((pos % ring) * ns + cq) * D);
-          zv.load(tl + ((pos % ring) * ns + zq) * D);
+      const int all_rows = (ov && I >= 1) ? 2 * r : r;
+      const int q_begin = all_rows * g / G;
+      const int nrows = all_rows * (g + 1) / G;  // this group's rows: [q_begin, nrows)
+      for (int q0 = q_begin; q0 < nrows; q0 += kAppendBatch) {
+        Raw8<TIn> cv[kAppendBatch], zv[kAppendBatch];
+        float4 bz[kAppendBatch][2];
+#pragma unroll
+        for (int u = 0; u < kAppendBatch; ++u) {
+          const int q = q0 + u;
+          if (q >= nrows) break;
+          const bool in_a = q < r;
+          const int j = in_a ? q : q - r;
+          const int64_t pos = in_a ? I * r + j : (I - 1) * r + j;
+          const int cq = in_a ? 0 : 1, zq = in_a ? zq_a : 3;
+          if (pos == p) {
+            cv[u] = cur[cq];
+            zv[u] = cur[zq];
+          } else {
+            cv[u].load(tl + ((pos % ring) * ns + cq) * D);
+            zv[u].load(tl + ((pos % ring) * ns + zq) * D);
+          }
+          const float* bp = in_a ? A.bias_a : A.bias_b;
+          if (bp) {
+            bz[u][0] = reinterpret_cast<const float4*>(bp + j * D + d0)[0];
+            bz[u][1] = reinterpret_cast<const float4*>(bp + j * D + d0)[1];
+          } else {
+            bz[u][0] = bz[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
-        const float* bp = in_a ? A.bias_a : A.bias_b;
+#pragma unroll
+        for (int u = 0; u < kAppendBatch; ++u) {
+          if (q0 + u >= nrows) break;
+          const float bb[kVec] = {bz[u][0].x, bz[u][0].y, bz[u][0].z, bz[u][0].w,
+                                  bz[u][1].x, bz[u][1].y, bz[u][1].z, bz[u][1].w};
+#pragma unroll
+          for (int ch = 0; ch < kVec; ++ch) {
+            const float z = zv[u].get(ch) + bb[ch];
+            const float nm = fmaxf(m[ch], z);
+            const float sc = __expf(m[ch] - nm), pz = __expf(z - nm);
+            sum[ch] = sum[ch] * sc + pz;
+            acc[ch] = acc[ch] * sc + pz * cv[u].get(ch);
+            m[ch] = nm;
+          }
+        }
+      }
+      if (G > 1) {
+        float* pp = part_lds + (g * ik0 + c) * 3 * kVec;
 #pragma unroll
         for (int ch = 0; ch < kVec; ++ch) {
-          const float z = zv.get(ch) + (bp ? bp[j * D + d0 + ch] : 0.f);
-          const float nm = fmaxf(m[ch], z);
-          const float sc = __expf(m[ch] - nm), pz = __expf(z - nm);
-          sum[ch] = sum[ch] * sc + pz;
-          acc[ch] = acc[ch] * sc + pz * cv.get(ch);
+          pp[3 * ch] = m[ch];
+          pp[3 * ch + 1] = sum[ch];
+          pp[3 * ch + 2] = acc[ch];
+        }
+      }
+    }
+  }
+  __syncthreads();  // the LDS maxima are cleared, the RoPE angles and the row-group partials stored
+  if (completes && mine) {
+    if (kv_part && G > 1 && g == 0) {
+      // the groups' partials merged in group order
+#pragma unroll
+      for (int ch = 0; ch < kVec; ++ch) {
+        m[ch] = -INFINITY;
+        sum[ch] = 0.f;
+        acc[ch] = 0.f;
+      }
+      for (int gg = 0; gg < G; ++gg) {
+        const float* pp = part_lds + (gg * ik0 + c) * 3 * kVec;
+#pragma unroll
+        for (int ch = 0; ch < kVec; ++ch) {
+          const float om = pp[3 * ch];
+          const float nm = fmaxf(m[ch], om);
+          if (nm == -INFINITY) continue;
+          const float s1 = __expf(m[ch] - nm), s2 = __expf(om - nm);
+          sum[ch] = sum[ch] * s1 + pp[3 * ch + 1] * s2;
+          acc[ch] = acc[ch] * s1 + pp[3 * ch + 2] * s2;
           m[ch] = nm;
         }
       }
+    }
 #pragma unroll
-      for (int ch = 0; ch < kVec; ++ch) val[ch] = acc[ch] / sum[ch];
-    }
+    for (int ch = 0; ch < kVec; ++ch) val[ch] = acc[ch] / sum[ch];
   }
-  __syncthreads();  // the LDS maxima are cleared
   if (completes) {
-    const int64_t row = paged_row(a.pmap, b, I);
-    finish_entry(a.kv, kv_part, 0, I, tid, val, amax_lds[0], ss_lds[0], nullptr, row);
-    if (a.has_ik) finish_entry(a.ik, ik_part, 0, I, tid - cD, val, amax_lds[1], ss_lds[1], nullptr, row);
-  }
-
-  // the raw KV row into the window; a full buffer keeps its last n_win - 1 rows first
-  const int64_t wp0 = a.win_pos0[s];
-  int64_t nwp0 = wp0;
-  const int64_t rowb = static_cast<int64_t>(a.kv.D) * a.win_elem;  // bytes per row
-  const int64_t c16 = rowb / 16;
-  uint8_t* wb = static_cast<uint8_t*>(a.win) + s * a.Ws * rowb;
-  if (p - wp0 >= a.Ws) {
-    nwp0 = p - a.n_win + 1;
-    for (int64_t i = tid; i < static_cast<int64_t>(a.n_win - 1) * c16; i += kThreads) {
-      const int64_t j = i / c16, q = i % c16;
-      reinterpret_cast<uint4*>(wb + j * rowb)[q] = reinterpret_cast<const uint4*>(wb + (nwp0 - wp0 + j) * rowb)[q];
-    }
-  }
-  for (int64_t i = tid; i < c16; i += kThreads)
-    reinterpret_cast<uint4*>(wb + (p - nwp0) * rowb)[i] =
-        reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv_raw) + b * rowb)[i];
-  if (a.vis_idx) {
-    // every entry of a block before the token's own is visible (no overlap: dense)
-    const int64_t vis = p / r;
-    for (int64_t j = tid; j < a.vis_K; j += kThreads)
-      a.vis_idx[b * a.vis_K + j] = j < vis ? static_cast<int32_t>(paged_row(a.pmap, b, j)) : -1;
+    finish_entry(a.kv, kv_part && mine && g == 0, 0, I, c, val, amax_lds[0], ss_lds[0],
+                 a.kv.R > 0 ? theta_lds : nullptr, out_row);
+    if (a.has_ik) finish_entry(a.ik, ik_part, 0, I, c, val, amax_lds[1], ss_lds[1], nullptr, out_row);
   }
   __syncthreads();  // every thread has read length[s] and win_pos0[s]
   if (tid == 0) {
@@ -820,7 +908,7 @@ int launch_state_append(const StateAppendLaunch& L, hipStream_t stream) {
     i.norm_w = nullptr;
     i.chunks = L.DI / kVec;
   }
-  if (k.chunks + (a.has_ik ? a.ik.chunks : 0) > kThreads) return -2;
+  if ((k.chunks + WAVE - 1) / WAVE * WAVE + (a.has_ik ? a.ik.chunks : 0) > kThreads || L.rope_dims > 128) return -2;
   a.slot = L.slot;
   a.length = L.length;
   a.tail = L.tail;

@@ -1567,6 +1567,10 @@ enum class Kern { kReg, kDma, kPair };
 constexpr int kPairMaxBlocks = 4;       // 16-head blocks per wave-pair workgroup (8 waves)
 constexpr int64_t kMinSplitPair = 96;
 constexpr int64_t kMaxSplitsSparsePair = 8;
+// Longer key lists per query take the DMA kernel: the wave-pair kernel's head groups
+// each load every key row, which costs more than its shorter chain saves once the
+// rows, not the chain, set the time (an HCA decode query over all 8192 entries).
+constexpr int64_t kPairMaxSlots = 4096;
 
 Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma, bool sparse, Kern kern) {
   Plan p{mfma, 0, 1, 0};
@@ -1597,7 +1601,10 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
   int64_t ns = 1;
   if (units < 256) {
     const int64_t min_split = kern == Kern::kPair ? kMinSplitPair : (dma ? kMinSplitDma : kMinSplitMfma);
-    const int64_t mx = kern == Kern::kPair ? kMaxSplitsSparsePair : (sparse ? kMaxSplitsSparse : kMaxSplitsDense);
+    // a long sparse list (every entry of an HCA decode query) splits like a dense one
+    const int64_t mx = kern == Kern::kPair
+                           ? kMaxSplitsSparsePair
+                           : ((sparse && max_slots <= kPairMaxSlots) ? kMaxSplitsSparse : kMaxSplitsDense);
     ns = (max_slots + min_split - 1) / min_split;
     if (ns > mx) ns = mx;
     if (ns < 1) ns = 1;
@@ -1665,7 +1672,8 @@ bool pair_ok(const AttnLaunch& L) {
 Kern kern_of(const AttnLaunch& L) {
   if (!dma_ok(L)) return Kern::kReg;
   const int hpw = head_group(L.H, kDmaMaxWaves);
-  if (L.sparse && pair_ok(L) && hpw > 0 && L.Tq * (L.H / hpw) < 256) return Kern::kPair;
+  if (L.sparse && pair_ok(L) && hpw > 0 && L.Tq * (L.H / hpw) < 256 && max_slots_of(L) <= kPairMaxSlots)
+    return Kern::kPair;
   return Kern::kDma;
 }
 

@@ -112,6 +112,103 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+// Many rows (prefill): LDS-tiled GEMM.  A workgroup of four waves (2 x 2) computes a
+// 128 x 256 block of C; each wave a 64 x 128 sub-block, so every operand fragment read
+// from LDS feeds 4 or 8 MFMAs (about 96 B/clk of LDS reads per CU at the MFMA rate).
+// The A and W tiles of 32 k-columns enter a 3-stage LDS ring by direct global -> LDS
+// loads (one KiB per wave instruction: 16 rows of 64 bytes, the 16-byte chunks of a row
+// XOR-swizzled by row so that a fragment read hits 16 distinct bank groups); a stage is
+// read after its own loads have landed (vmcnt) and a barrier, and the stage two ahead is
+// requested right after that barrier.
+constexpr int kTBM = 128, kTBN = 256, kTKS = 32, kTStages = 3;
+constexpr int kTStageBytes = (kTBM + kTBN) * kTKS * 2;  // 24 KiB
+
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return static_cast<uint32_t>(row * (kTKS * 2) + ((chunk ^ ((row >> 2) & 3)) * 16));
+}
+
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTStages * kTStageBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int64_t batch = blockIdx.z;
+  const int64_t bm0 = static_cast<int64_t>(blockIdx.y) * kTBM;
+  const int64_t bn0 = static_cast<int64_t>(blockIdx.x) * kTBN;
+  const uint16_t* A = a.A + batch * a.sa;
+  const uint16_t* W = a.W + batch * a.sw;
+  const int nsteps = static_cast<int>(a.K / kTKS);
+  const uint32_t lds_b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+
+  // this wave's 6 of the stage's 24 one-KiB loads: A rows in loads 0..7, W rows in 8..23;
+  // lane l of a load fills row 16 i + l / 4 (clamped into the matrix), physical chunk l % 4
+  const uint16_t* src[6];
+  uint32_t dst[6];
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const int i = wid + 4 * u;
+    const bool isA = i < kTBM / 16;
+    const int row = (isA ? i : i - kTBM / 16) * 16 + (lane >> 2);
+    const int pc = lane & 3;
+    const int c = pc ^ ((row >> 2) & 3);
+    const int64_t g = isA ? min(bm0 + row, a.M - 1) : min(bn0 + row, a.N - 1);
+    src[u] = (isA ? A + g * a.lda : W + g * a.K) + 8 * c;
+    dst[u] = static_cast<uint32_t>((isA ? 0 : kTBM * kTKS * 2) + (isA ? i : i - kTBM / 16) * 1024);
+  }
+  auto issue = [&](int s) {
+    const uint32_t base = lds_b + static_cast<uint32_t>((s % kTStages) * kTStageBytes);
+#pragma unroll
+    for (int u = 0; u < 6; ++u) lds_dma16(src[u] + static_cast<int64_t>(s) * kTKS, base + dst[u]);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[f][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's part of stage s has landed; stage s - 1 is no longer read
+    if (s + 2 < nsteps) issue(s + 2);
+    const uint8_t* st = lds + (s % kTStages) * kTStageBytes;
+    bf16x8 af[4], wf[8];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      af[f] = *reinterpret_cast<const bf16x8*>(st + tile_off(wm * 64 + 16 * f + col, grp));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      wf[nb] = *reinterpret_cast<const bf16x8*>(st + kTBM * kTKS * 2 + tile_off(wn * 128 + 16 * nb + col, grp));
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[f], wf[nb], acc[f][nb], 0, 0, 0);
+  }
+  // lane (col, grp) holds C[m0 + 4 grp + r][n0 + col] of each 16 x 16 tile
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const int64_t n = bn0 + wn * 128 + 16 * nb + col;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = bm0 + wm * 64 + 16 * f + 4 * grp + r;
+        if (m >= a.M) continue;
+        const int64_t o = batch * a.sc + m * a.ldc + n;
+        if (a.out_f32) static_cast<float*>(a.C)[o] = acc[f][nb][r];
+        else static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(acc[f][nb][r]);
+      }
+    }
+  }
+}
+
 // sums the ksplit partials of every C element in split order
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -151,7 +248,11 @@ int launch_gemm(GemmArgs a, int64_t batch, float* part, hipStream_t stream) {
   a.part = part;
   if (a.ksplit > 1 && !part) return -2;
   const uint32_t gz = static_cast<uint32_t>(batch * a.ksplit);
-  if (a.M <= kFewRows) {  // few rows: 16 x 256 tiles, each weight row read once
+  if (a.M >= kTBM && a.ksplit == 1) {  // many rows: LDS-tiled blocks
+    const dim3 g(static_cast<uint32_t>((a.N + kTBN - 1) / kTBN), static_cast<uint32_t>((a.M + kTBM - 1) / kTBM),
+                 static_cast<uint32_t>(batch));
+    hipLaunchKernelGGL(gemm_tiled_kernel, g, dim3(256), 0, stream, a);
+  } else if (a.M <= kFewRows) {  // few rows: 16 x 256 tiles, each weight row read once
     const dim3 g(static_cast<uint32_t>((a.N + 255) / 256), static_cast<uint32_t>((a.M + 15) / 16), gz);
     hipLaunchKernelGGL((gemm_bf16_kernel<1, 4>), g, dim3(256), 0, stream, a);
   } else {

@@ -183,7 +183,7 @@ struct Shape {
 };
 // 16384-entry slices take 512 threads of 32 entries: two workgroups share a CU, so the
 // barrier-separated phases of one overlap the other's.  The 32768-entry shape serves
-// only single-level selections of a few rows.
+// only the selections of a few rows (decode): one level, or the first of two.
 constexpr Shape kShapes[] = {{256, 16}, {512, 16}, {512, 32}, {1024, 32}};
 constexpr int64_t kOneLevelMax = 32768;  // a row this long may take one workgroup
 
@@ -230,6 +230,18 @@ Levels plan_levels(int64_t rows, int64_t N, int k) {
     L.len[0] = N;
     L.slice[0] = N;
     L.slices[0] = 1;
+    return L;
+  }
+  // ... of at most twice that: two halves a row, then the 2k candidates in one small
+  // workgroup (a decode row just past 32768 entries)
+  if (N <= 2 * kOneLevelMax && rows <= 64 && 2 * static_cast<int64_t>(k) <= kMaxSlice) {
+    L.n = 2;
+    L.len[0] = N;
+    L.slice[0] = (N + 1) / 2;
+    L.slices[0] = 2;
+    L.len[1] = 2 * static_cast<int64_t>(k);
+    L.slice[1] = L.len[1];
+    L.slices[1] = 1;
     return L;
   }
   // level-1 slices: halved from 32768 (not below 4096 or 2k) while the launch has fewer

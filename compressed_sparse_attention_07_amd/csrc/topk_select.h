@@ -69,6 +69,7 @@ struct TopkArgs {
 };
 
 constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one wave
+constexpr int kPageLds = 1024;  // block-table entries a final level stages in LDS
 
 template <int NT>
 struct Shared {
@@ -253,6 +254,14 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
   const int64_t lo = static_cast<int64_t>(sl) * a.slice;
   const int n = static_cast<int>(min(a.n_in, lo + a.slice) - lo);
   const uint32_t K = static_cast<uint32_t>(a.k);
+  // paged output: the row's block-table row, fetched now and read after the selection
+  // (the selection's barriers order the LDS stores before those reads)
+  __shared__ int32_t pg_lds[FINAL ? kPageLds : 1];
+  const bool pg_in_lds = FINAL && a.omap.table && a.omap.max_pages <= kPageLds;
+  if (pg_in_lds) {
+    const int32_t* row = a.omap.table + static_cast<int64_t>(a.omap.slot[r / a.tq]) * a.omap.max_pages;
+    for (int i = tid; i < a.omap.max_pages; i += NT) pg_lds[i] = row[i];
+  }
 
   // ---- A: finite count, smallest and largest finite value
   uint32_t nfin = 0;
@@ -496,8 +505,12 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
   }
   auto put = [&](int j, uint32_t slot) {
     const int32_t e = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(lo + j * NT + tid);
-    if (FINAL && a.omap.table) oi[slot] = static_cast<int32_t>(paged_row(a.omap, r / a.tq, e));
-    else oi[slot] = e;
+    if (pg_in_lds)
+      oi[slot] = (pg_lds[e >> a.omap.shift] << a.omap.shift) | (e & ((1 << a.omap.shift) - 1));
+    else if (FINAL && a.omap.table)
+      oi[slot] = static_cast<int32_t>(paged_row(a.omap, r / a.tq, e));
+    else
+      oi[slot] = e;
     if (!FINAL) ov[slot] = v[j];
   };
   if (one_test && with_eq) {

@@ -434,8 +434,9 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
  *   offset), in increasing entry order, -1 padded.  scores_out (optional, CSA) float
  *   [B, max_pages * P].
  * Limits: page_tokens a power of two and a multiple of ratio; CSA: P >= 512 (an indexer
- *   key range stays inside one page) and D + DI <= 2048; D <= 1024; distinct slots within
- *   a batch; max_pages * P < 2^31.  FP8MIX caches are not taken here.
+ *   key range stays inside one page) and roundup(D / 8, 64) + DI / 8 <= 256 (one thread
+ *   per 8 channels); D <= 1024; distinct slots within a batch; max_pages * P < 2^31.
+ *   FP8MIX caches are not taken here.
  */
 typedef struct csa_decode_desc {
   int32_t struct_size;   /* sizeof(csa_decode_desc) */

@@ -125,6 +125,9 @@ def _check_proj(got, o, wg, wo, rows, dtype, what):
     (70, 8, 64, 2, 64, 130, "bf16"),     # 64 x 64 tiles with a ragged edge
     (33, 4, 128, 4, 32, 96, "f32"),      # one row past the few-rows tiles
     (1, 16, 32, 16, 32, 64, "bf16"),     # single token, one head per group
+    (300, 8, 64, 2, 96, 300, "f32"),     # LDS-tiled blocks: ragged rows and columns
+    (256, 4, 128, 4, 256, 512, "bf16"),  # LDS-tiled blocks, exact tiles
+    (0, 8, 64, 4, 96, 200, "f32"),       # no rows
 ])
 def test_grouped_out_proj_small(T, n_h, c, g_, d_g, d, dtype):
     say(f"grouped projection T={T} n_h={n_h} c={c} g={g_} d_g={d_g} d={d} {dtype}")
@@ -132,7 +135,8 @@ def test_grouped_out_proj_small(T, n_h, c, g_, d_g, d, dtype):
     out = torch.empty((T, d), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device=DEV)
     csa.csa_grouped_out_proj(o, wg, wo, out)
     torch.cuda.synchronize()
-    _check_proj(out, o, wg, wo, np.arange(T), dtype, "grouped projection")
+    if T:
+        _check_proj(out, o, wg, wo, np.arange(T), dtype, "grouped projection")
 
 
 @pytest.mark.parametrize("T", [16, 512])

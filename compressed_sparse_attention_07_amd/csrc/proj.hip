@@ -112,6 +112,99 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+// Few rows (decode): a wave computes every row (MB 16-row blocks) of 64 columns, so
+// each weight row is read by one wave only.  A lane loads 32 contiguous bytes of its
+// row per 64-element step (4 lanes: one 128-byte line), which feed two MFMAs: both
+// operands take the same permutation of the contraction index (lane group g holds
+// elements 16 g .. 16 g + 15 of the step; the first MFMA takes the first 8 of them,
+// the second the rest), so the products sum over the same elements.  Two steps of
+// loads are kept in flight ahead of the products.
+constexpr int kFewStep = 64;
+constexpr int kFewAhead = 2;
+
+template <int MB>
+__global__ __launch_bounds__(256) void gemm_few_kernel(GemmArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t batch = blockIdx.z / a.ksplit;
+  const int split = blockIdx.z % a.ksplit;
+  const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * 64;
+  if (n0 >= a.N) return;  // a whole wave outside C (no barrier below)
+  const int s_begin = split * a.steps_per_split;
+  const int nsteps = min(static_cast<int>(a.K / kFewStep) - s_begin, a.steps_per_split);
+  const uint16_t* ap[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    ap[mb] = a.A + batch * a.sa + min(static_cast<int64_t>(16 * mb + col), a.M - 1) * a.lda + 16 * grp +
+             static_cast<int64_t>(s_begin) * kFewStep;
+  const uint16_t* wp[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    wp[nb] = a.W + batch * a.sw + min(n0 + 16 * nb + col, a.N - 1) * a.K + 16 * grp +
+             static_cast<int64_t>(s_begin) * kFewStep;
+
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 af[kFewAhead + 1][MB][2], wf[kFewAhead + 1][4][2];
+  auto load = [&](int slot, int s) {
+    const int64_t o = static_cast<int64_t>(s) * kFewStep;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      af[slot][mb][0] = *reinterpret_cast<const bf16x8*>(ap[mb] + o);
+      af[slot][mb][1] = *reinterpret_cast<const bf16x8*>(ap[mb] + o + 8);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      wf[slot][nb][0] = *reinterpret_cast<const bf16x8*>(wp[nb] + o);
+      wf[slot][nb][1] = *reinterpret_cast<const bf16x8*>(wp[nb] + o + 8);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kFewAhead; ++s)
+    if (s < nsteps) load(s, s);
+  for (int s0 = 0; s0 < nsteps; s0 += kFewAhead + 1) {
+#pragma unroll
+    for (int u = 0; u <= kFewAhead; ++u) {
+      const int s = s0 + u;
+      if (s >= nsteps) break;
+      if (s + kFewAhead < nsteps) load((u + kFewAhead) % (kFewAhead + 1), s + kFewAhead);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mb][h], wf[u][nb][h], acc[mb][nb], 0, 0, 0);
+    }
+  }
+  // lane (col, grp) holds C[16 mb + 4 grp + r][n0 + 16 nb + col]
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t n = n0 + 16 * nb + col;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = 16 * mb + 4 * grp + r;
+        if (m >= a.M) continue;
+        if (a.ksplit > 1) {
+          a.part[((split * a.batch + batch) * a.M + m) * a.N + n] = acc[mb][nb][r];
+          continue;
+        }
+        const int64_t o = batch * a.sc + m * a.ldc + n;
+        if (a.out_f32) static_cast<float*>(a.C)[o] = acc[mb][nb][r];
+        else static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(acc[mb][nb][r]);
+      }
+    }
+  }
+}
+
 // Many rows (prefill): LDS-tiled GEMM.  A workgroup of four waves (2 x 2) computes a
 // 128 x 256 block of C; each wave a 64 x 128 sub-block, so every operand fragment read
 // from LDS feeds 4 or 8 MFMAs (about 96 B/clk of LDS reads per CU at the MFMA rate).
@@ -222,11 +315,14 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a) {
   else static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(acc);
 }
 
+// the few-rows kernel with the 64-element step
+bool few_path(int64_t M, int64_t K) { return M <= kFewRows && K % kFewStep == 0; }
+
 // contraction splits of a GEMM (1 unless few rows leave the chip underfilled)
 int gemm_splits(int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (M > kFewRows || M == 0) return 1;
-  const int64_t tiles = ((N + 255) / 256) * ((M + 15) / 16) * batch;
-  const int64_t steps = K / kKStep;
+  const int64_t tiles = ((N + 255) / 256) * (few_path(M, K) ? 1 : (M + 15) / 16) * batch;
+  const int64_t steps = K / (few_path(M, K) ? kFewStep : kKStep);
   int64_t s = (kTargetGroups + tiles - 1) / tiles;
   s = std::min(s, steps / kMinSplitSteps);
   return static_cast<int>(std::max<int64_t>(s, 1));
@@ -240,7 +336,7 @@ size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K, int64_t batch) {
 int launch_gemm(GemmArgs a, int64_t batch, float* part, hipStream_t stream) {
   if (a.M == 0 || a.N == 0 || batch == 0) return 0;
   if (a.K % kKStep) return -2;
-  const int steps = static_cast<int>(a.K / kKStep);
+  const int steps = static_cast<int>(a.K / (few_path(a.M, a.K) ? kFewStep : kKStep));
   a.batch = batch;
   a.ksplit = gemm_splits(a.M, a.N, a.K, batch);
   a.steps_per_split = (steps + a.ksplit - 1) / a.ksplit;
@@ -252,7 +348,11 @@ int launch_gemm(GemmArgs a, int64_t batch, float* part, hipStream_t stream) {
     const dim3 g(static_cast<uint32_t>((a.N + kTBN - 1) / kTBN), static_cast<uint32_t>((a.M + kTBM - 1) / kTBM),
                  static_cast<uint32_t>(batch));
     hipLaunchKernelGGL(gemm_tiled_kernel, g, dim3(256), 0, stream, a);
-  } else if (a.M <= kFewRows) {  // few rows: 16 x 256 tiles, each weight row read once
+  } else if (few_path(a.M, a.K)) {  // few rows: all rows x 256 columns per workgroup
+    const dim3 g(static_cast<uint32_t>((a.N + 255) / 256), 1, gz);
+    if (a.M <= 16) hipLaunchKernelGGL((gemm_few_kernel<1>), g, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((gemm_few_kernel<2>), g, dim3(256), 0, stream, a);
+  } else if (a.M <= kFewRows) {  // few rows, contraction not a multiple of 64: 16 x 256 tiles
     const dim3 g(static_cast<uint32_t>((a.N + 255) / 256), static_cast<uint32_t>((a.M + 15) / 16), gz);
     hipLaunchKernelGGL((gemm_bf16_kernel<1, 4>), g, dim3(256), 0, stream, a);
   } else {

@@ -591,7 +591,9 @@ KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip
                   "index_stream_kernel": ("indexer.hip",),
                   "index_mxfp4_kernel": ("indexer.hip",), "index_prefill_kernel": ("indexer.hip",),
                   "topk_kernel": ("topk.hip",),
-                  "compress_kernel": ("compress.hip",)}
+                  "compress_kernel": ("compress.hip",), "state_append_kernel": ("compress.hip",),
+                  "gemm_few_kernel": ("proj.hip",), "gemm_tiled_kernel": ("proj.hip",),
+                  "gemm_reduce_kernel": ("proj.hip",)}
 
 
 # ============================================================================ runs

@@ -210,14 +210,17 @@ __global__ __launch_bounds__(256) void gemm_few_kernel(GemmArgs a) {
 // from LDS feeds 4 or 8 MFMAs (about 96 B/clk of LDS reads per CU at the MFMA rate).
 // The A and W tiles of 32 k-columns enter a 3-stage LDS ring by direct global -> LDS
 // loads (one KiB per wave instruction: 16 rows of 64 bytes, the 16-byte chunks of a row
-// XOR-swizzled by row so that a fragment read hits 16 distinct bank groups); a stage is
+// XOR-swizzled by row so that a fragment read hits distinct bank groups); a stage is
 // read after its own loads have landed (vmcnt) and a barrier, and the stage two ahead is
 // requested right after that barrier.
 constexpr int kTBM = 128, kTBN = 256, kTKS = 32, kTStages = 3;
 constexpr int kTStageBytes = (kTBM + kTBN) * kTKS * 2;  // 24 KiB
 
+// The 16-byte chunk of a row holding logical chunk c: XOR-swizzled so that 8 (or 16)
+// lanes reading one logical chunk of 8 (or 16) consecutive rows hit distinct banks
+__device__ __forceinline__ int tile_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return static_cast<uint32_t>(row * (kTKS * 2) + ((chunk ^ ((row >> 2) & 3)) * 16));
+  return static_cast<uint32_t>(row * (kTKS * 2) + ((chunk ^ tile_swz(row)) * 16));
 }
 
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     const bool isA = i < kTBM / 16;
     const int row = (isA ? i : i - kTBM / 16) * 16 + (lane >> 2);
     const int pc = lane & 3;
-    const int c = pc ^ ((row >> 2) & 3);
+    const int c = pc ^ tile_swz(row);
     const int64_t g = isA ? min(bm0 + row, a.M - 1) : min(bn0 + row, a.N - 1);
     src[u] = (isA ? A + g * a.lda : W + g * a.K) + 8 * c;
     dst[u] = static_cast<uint32_t>((isA ? 0 : kTBM * kTKS * 2) + (isA ? i : i - kTBM / 16) * 1024);

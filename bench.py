@@ -707,6 +707,38 @@ def layer_edges(wl: Workload, steps: int, reps: int):
     log(f"  with Q/KV RMSNorm: step {ms * 1e3:.1f} us")
     del att, full, ws
 
+    # BF16 index scores ([V4-CN] §3.4): the same attend-only step with the scores rounded
+    # to bf16 before the selection, and the recall of the exact (fp32) selection
+    def flagged(d, f):
+        d2 = csa._lib.csa_layer_desc.from_buffer_copy(d)
+        d2.flags |= f
+        return d2
+
+    k, B, Tq = M["k"], M["B"], M["Tq"]
+    sel = []
+    for f in (0, csa.CSA_FLAG_BF16_SCORES):
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device="cuda")
+        d = flagged(wl.desc_attend, f)
+        w = torch.empty(max(1, csa.csa_forward_workspace_size(d)), dtype=torch.uint8, device="cuda")
+        csa.csa_forward(d, dict(wl.ios[0], idx_out=idx), ws=w)
+        sel.append(idx.cpu().numpy().reshape(B * Tq, k))
+    hits = total = 0
+    for r in range(B * Tq):
+        e = set(int(x) for x in sel[0][r] if x >= 0)
+        hits += len(e & set(int(x) for x in sel[1][r] if x >= 0))
+        total += len(e)
+    times = []
+    for f in (0, csa.CSA_FLAG_BF16_SCORES):
+        d = flagged(wl.desc_attend, f)
+        w = torch.empty(max(1, csa.csa_forward_workspace_size(d)), dtype=torch.uint8, device="cuda")
+        calls = [csa.ForwardCall(d, io, ws=w) for io in wl.ios]
+        times.append(time_stage(lambda i: calls[i % len(calls)](), reps))
+        del calls, w
+    out["bf16_scores"] = dict(attend_step_us=round(times[1] * 1e6, 2), attend_step_us_fp32=round(times[0] * 1e6, 2),
+                              recall=round(hits / max(1, total), 5), selections=B * Tq, k=k)
+    log(f"  BF16 scores: attend-only step {times[1] * 1e6:.1f} us (fp32 scores {times[0] * 1e6:.1f} us), "
+        f"recall of the exact selection {hits / max(1, total):.4f}")
+
     T = M["B"] * M["Tq"]
     n_h, c, ng, d_g, d = 128, 512, 16, 1024, 7168
     o = g.normal((T, n_h, c), dtype=torch.bfloat16)

@@ -755,7 +755,8 @@ def layer_edges(wl: Workload, steps: int, reps: int):
     out["grouped_out_proj"] = dict(us=round(t * 1e6, 2), tokens=T, GBps=round(nbytes / t / 1e9, 1),
                                    TFLOPs=round(flops / t / 1e12, 2), hbm_frac=round(nbytes / t / HBM_PEAK, 4),
                                    mfma_frac=round(flops / t / MFMA_BF16_PEAK, 4), bound=bound,
-                                   kernel="gemm_bf16_kernel" + ("+gemm_reduce_kernel" if T <= 32 else ""),
+                                   kernel=("gemm_few_kernel+gemm_reduce_kernel" if T <= 32 else
+                                           "gemm_tiled_kernel" if T >= 128 else "gemm_bf16_kernel"),
                                    algorithmic_bytes=int(nbytes), algorithmic_flops=int(flops))
     log(f"  grouped output projection ({T} tokens): {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s, "
         f"{flops / t / 1e12:.1f} TFLOP/s ({bound}-bound)")

@@ -294,7 +294,11 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
   }
   if (lane == 0) sh.wave_abc[wid] = make_uint4(nfin, __float_as_uint(vmax), __float_as_uint(vmin), nge);
   for (int i = tid; i < 2 * (kBins + 4); i += NT) (&sh.hist[0][0])[i] = 0u;
-  if (tid == 0) sh.ncand = 0u;
+  if (tid == 0) {
+    sh.ncand = 0u;
+    sh.cand[0] = 0xffffffffu;  // the threshold bin's smallest and largest key (crowded bins)
+    sh.cand[1] = 0u;
+  }
   __syncthreads();
   nfin = 0;
   vmax = -INFINITY;
@@ -386,6 +390,24 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
         ties = sh.info[1];
         total_eq = sh.info[2];
         found = true;
+      } else {
+        // a crowded threshold bin: when all its entries hold one value (scores rounded
+        // to few distinct values, as BF16 scores are) that value is the threshold
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          if (((binp[j / 2] >> (16 * (j & 1))) & 0xffffu) == tb) {
+            const uint32_t key = score_key(v[j]);
+            atomicMin(&sh.cand[0], key);
+            atomicMax(&sh.cand[1], key);
+          }
+        }
+        __syncthreads();
+        if (sh.cand[0] == sh.cand[1]) {
+          theta = key_value(sh.cand[0]);
+          ties = rem;
+          total_eq = cnt;
+          found = true;
+        }
       }
     }
     if (!found) {

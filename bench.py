@@ -774,7 +774,7 @@ def decode_state_bench(wl: Workload, steps: int, warmup: int):
     from synth import Gen, qstd
 
     M = wl.meta
-    if M["Tq"] != 1 or M["kv_format"] == "fp8mix" or M["ik_format"] == "mxfp4":
+    if M["Tq"] != 1:
         return None
     csa_mode = M["mode"] == "csa"
     B, D, H, HI, DI, k, W, m, ctx, R = (M[x] for x in ("B", "D", "H", "HI", "DI", "k", "W", "m", "ctx", "R"))
@@ -788,12 +788,34 @@ def decode_state_bench(wl: Workload, steps: int, warmup: int):
     pages = B * max_pages
     g = Gen(cfg.seed + 991, "cuda")
     bf = torch.bfloat16
+    kvd = csa.CSA_FP8MIX if M["kv_format"] == "fp8mix" else csa.CSA_BF16
+    ikd = csa.CSA_MXFP4 if M["ik_format"] == "mxfp4" else csa.CSA_BF16
     pool = csa.DecodePool(mode=csa.CSA_MODE_CSA if csa_mode else csa.CSA_MODE_HCA, slots=B, pages=pages,
                           max_pages=max_pages, page_tokens=page_tokens, D=D, DI=DI, ratio=m, n_win=W,
-                          stream_dtype=csa.CSA_BF16, kv_dtype=csa.CSA_BF16, ik_dtype=csa.CSA_BF16)
+                          stream_dtype=csa.CSA_BF16, kv_dtype=kvd, ik_dtype=ikd, rope_dims=R)
     gen = torch.Generator().manual_seed(cfg.seed)
     pool.block_table.copy_(torch.randperm(pages, generator=gen).view(B, max_pages).to(torch.int32))
-    for x in (pool.kv_pages.data, pool.ik_pages.data if csa_mode else None, pool.tail, pool.itail, pool.win):
+
+    def fill(buf, std):
+        # seeded Gaussians; quantized formats take fp32 rows through the library's quantizer
+        b = csa.Buf.of(buf)
+        flat = lambda t, k: None if t is None else t.reshape((-1,) + tuple(t.shape[k:]))
+        lead = len(b.data.shape) - 1
+        data, rope, scale = flat(b.data, lead), flat(b.rope, lead), flat(b.scale, lead)
+        for r0 in range(0, data.shape[0], 1 << 15):
+            r1 = min(data.shape[0], r0 + (1 << 15))
+            if b.dtype == csa.CSA_BF16:
+                data[r0:r1].copy_(g.normal(data[r0:r1].shape, std, dtype=bf))
+                continue
+            width = b.shape[-1]
+            part = csa.Buf(b.dtype, data[r0:r1], None if rope is None else rope[r0:r1], scale[r0:r1])
+            csa.csa_quantize(g.normal((r1 - r0, width), std), part, rope_dims=R if b.dtype == csa.CSA_FP8MIX else 0)
+
+    fill(pool.kv_pages, 0.5)
+    if csa_mode:
+        fill(pool.ik_pages, 0.5)
+    fill(pool.win, 0.5)
+    for x in (pool.tail, pool.itail):
         if x is not None:
             for r0 in range(0, x.shape[0], 64):
                 x[r0:r0 + 64].copy_(g.normal(x[r0:r0 + 64].shape, 0.5, dtype=bf))
@@ -801,13 +823,21 @@ def decode_state_bench(wl: Workload, steps: int, warmup: int):
     pool.win_pos0.copy_(torch.tensor([n - W + 1 for n in lengths], dtype=torch.int64))
     ns = 4 if csa_mode else 2
     st = [g.normal((B, D), dtype=bf) for _ in range(ns)]
-    io = dict(pool.io(), slot=torch.arange(B, dtype=torch.int32, device="cuda"), kv_raw=g.normal((B, D), dtype=bf),
+    kv_raw = csa.Buf.empty((B, D), kvd, rope_dims=R)
+    fill(kv_raw.data if kvd == csa.CSA_BF16 else kv_raw, 1.0)
+    io = dict(pool.io(), slot=torch.arange(B, dtype=torch.int32, device="cuda"), kv_raw=kv_raw,
               q=g.normal((B, H, D), qstd(D), dtype=bf), sink=g.normal((H,)),
               out=torch.empty((B, H, D), dtype=bf, device="cuda"))
     if csa_mode:
         ist = [g.normal((B, DI), dtype=bf) for _ in range(4)]
+        qI = csa.Buf.empty((B, HI, DI), ikd)
+        if ikd == csa.CSA_BF16:
+            qI.data.copy_(g.normal((B, HI, DI), qstd(DI), dtype=bf))
+        else:
+            csa.csa_quantize(g.normal((B * HI, DI), qstd(DI)), csa.Buf(ikd, qI.data.view(B * HI, -1), None,
+                                                                       qI.scale.view(B * HI, -1)))
         io.update(ca=st[0], cb=st[1], za=st[2], zb=st[3], ica=ist[0], icb=ist[1], iza=ist[2], izb=ist[3],
-                  qI=g.normal((B, HI, DI), qstd(DI), dtype=bf), wI=g.uniform((B, HI)))
+                  qI=qI, wI=g.uniform((B, HI)))
     else:
         io.update(ca=st[0], za=st[1])
     desc = csa.decode_desc(mode=csa.CSA_MODE_CSA if csa_mode else csa.CSA_MODE_HCA, B=B, slots=B, pages=pages,

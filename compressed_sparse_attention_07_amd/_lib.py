@@ -78,7 +78,7 @@ class csa_decode_io(C.Structure):
                 ("ca", C.c_void_p), ("cb", C.c_void_p), ("za", C.c_void_p), ("zb", C.c_void_p),
                 ("bias_a", C.c_void_p), ("bias_b", C.c_void_p),
                 ("ica", C.c_void_p), ("icb", C.c_void_p), ("iza", C.c_void_p), ("izb", C.c_void_p),
-                ("ibias_a", C.c_void_p), ("ibias_b", C.c_void_p), ("kv_raw", C.c_void_p),
+                ("ibias_a", C.c_void_p), ("ibias_b", C.c_void_p), ("kv_raw", csa_buf),
                 ("tail", C.c_void_p), ("itail", C.c_void_p), ("win", csa_buf), ("win_pos0", C.c_void_p),
                 ("kv_pages", csa_buf), ("ik_pages", csa_buf), ("block_table", C.c_void_p),
                 ("q", csa_buf), ("qI", csa_buf), ("wI", C.c_void_p), ("sink", C.c_void_p), ("out", csa_buf),
@@ -413,7 +413,7 @@ def csa_decode_step_workspace_size(desc: csa_decode_desc) -> int:
     return lib().csa_decode_step_workspace_size(C.byref(desc))
 
 
-_DECODE_BUFS = ("win", "kv_pages", "ik_pages", "q", "qI", "out")
+_DECODE_BUFS = ("kv_raw", "win", "kv_pages", "ik_pages", "q", "qI", "out")
 
 
 def _decode_io(io: dict) -> csa_decode_io:
@@ -442,7 +442,8 @@ class DecodePool:
     csa_decode_step documents (allocation only; every field is a plain tensor)."""
 
     def __init__(self, *, mode: int, slots: int, pages: int, max_pages: int, page_tokens: int, D: int, DI: int,
-                 ratio: int, n_win: int, stream_dtype: int, kv_dtype: int, ik_dtype: int, device="cuda"):
+                 ratio: int, n_win: int, stream_dtype: int, kv_dtype: int, ik_dtype: int, rope_dims: int = 0,
+                 device="cuda"):
         import torch
         st = torch.float32 if stream_dtype == CSA_F32 else torch.bfloat16
         kt = torch.float32 if kv_dtype == CSA_F32 else torch.bfloat16
@@ -453,9 +454,12 @@ class DecodePool:
         ring, nst = (2 * ratio, 4) if csa_mode else (ratio, 2)
         self.tail = torch.zeros((slots, ring, nst, D), dtype=st, device=device)
         self.itail = torch.zeros((slots, ring, 4, DI), dtype=st, device=device) if csa_mode else None
-        self.win = torch.zeros((slots, 2 * n_win, D), dtype=kt, device=device)
+        if kv_dtype == CSA_FP8MIX:
+            self.win = Buf.empty((slots, 2 * n_win, D), kv_dtype, rope_dims=rope_dims, device=device)
+        else:
+            self.win = torch.zeros((slots, 2 * n_win, D), dtype=kt, device=device)
         self.win_pos0 = torch.zeros(slots, dtype=torch.int64, device=device)
-        self.kv_pages = Buf.empty((pages, P, D), kv_dtype, device=device)
+        self.kv_pages = Buf.empty((pages, P, D), kv_dtype, rope_dims=rope_dims, device=device)
         self.ik_pages = Buf.empty((pages, P, DI), ik_dtype, device=device) if csa_mode else None
         self.block_table = torch.full((slots, max_pages), -1, dtype=torch.int32, device=device)
 

@@ -939,9 +939,8 @@ csa_status csa_decode_step(const csa_decode_desc* L, const csa_decode_io* io, vo
   const bool qkv_norm = (L->flags & CSA_FLAG_QKV_NORM) != 0;
   const int64_t Ws = 2 * static_cast<int64_t>(L->n_win);
   if (L->B == 0) return ok();
-  if (!io->slot || !io->length || !io->ca || !io->za || !io->kv_raw || !io->tail || !io->win_pos0 ||
-      !io->block_table)
-    return fail(CSA_ERR_NULL, "slot, length, ca, za, kv_raw, tail, win_pos0 and block_table are required");
+  if (!io->slot || !io->length || !io->ca || !io->za || !io->tail || !io->win_pos0 || !io->block_table)
+    return fail(CSA_ERR_NULL, "slot, length, ca, za, tail, win_pos0 and block_table are required");
   if (csa_mode && (!io->cb || !io->zb || !io->ica || !io->icb || !io->iza || !io->izb || !io->itail))
     return fail(CSA_ERR_NULL, "CSA needs cb, zb, the indexer streams and itail");
   CSA_TRY(check_buf(&io->q, "q"));
@@ -951,9 +950,18 @@ csa_status csa_decode_step(const csa_decode_desc* L, const csa_decode_io* io, vo
   if (!io->sink) return fail(CSA_ERR_NULL, "sink is required");
   if (io->q.dtype != CSA_F32 && io->q.dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "q must be F32 or BF16");
   if (io->out.dtype != io->q.dtype) return fail(CSA_ERR_DTYPE, "out must have the dtype of q");
-  if (io->kv_pages.dtype != CSA_F32 && io->kv_pages.dtype != CSA_BF16)
-    return fail(CSA_ERR_UNSUPPORTED, "the decode state takes F32 or BF16 caches and windows");
-  if (io->win.dtype != io->kv_pages.dtype) return fail(CSA_ERR_DTYPE, "win must have the dtype of kv_pages");
+  CSA_TRY(check_buf(&io->kv_raw, "kv_raw"));
+  if (io->kv_pages.dtype == CSA_MXFP4) return fail(CSA_ERR_DTYPE, "the attention cache cannot be MXFP4");
+  if (io->win.dtype != io->kv_pages.dtype || io->kv_raw.dtype != io->kv_pages.dtype)
+    return fail(CSA_ERR_DTYPE, "win and kv_raw must have the dtype of kv_pages");
+  if (io->kv_pages.dtype == CSA_FP8MIX) {
+    if ((L->D - L->rope_dims) % 16 || L->rope_dims % 8)
+      return fail(CSA_ERR_SHAPE, "FP8MIX needs (D - rope_dims) %% 16 == 0 and rope_dims %% 8 == 0");
+    if (L->rope_dims > 0 && (!io->kv_pages.rope || !io->win.rope || !io->kv_raw.rope))
+      return fail(CSA_ERR_NULL, "FP8MIX caches with rope_dims > 0 need rope pointers");
+    if (!io->win.scale || !io->kv_raw.scale) return fail(CSA_ERR_NULL, "FP8MIX windows need scale pointers");
+    if (qkv_norm) return fail(CSA_ERR_UNSUPPORTED, "CSA_FLAG_QKV_NORM takes F32 or BF16 windows");
+  }
   if (L->H < 1 || L->H > 256) return fail(CSA_ERR_SHAPE, "H=%d out of [1, 256]", L->H);
   CSA_TRY(check_rope(L->D, L->rope_dims, L->rope_base));
   if (csa_mode) {
@@ -1009,8 +1017,7 @@ csa_status csa_decode_step(const csa_decode_desc* L, const csa_decode_io* io, vo
   A.tail = io->tail;
   A.itail = io->itail;
   A.kv_raw = io->kv_raw;
-  A.win = io->win.data;
-  A.win_elem = elem_bytes(io->win.dtype);
+  A.win = io->win;
   A.n_win = L->n_win;
   A.Ws = Ws;
   A.win_pos0 = io->win_pos0;

@@ -652,9 +652,11 @@ struct AppendArgs {
   int64_t* length;      // [slots]
   void* tail;           // [slots, RING, NST, D] in the stream dtype (NST = 4 with overlap, else 2)
   void* itail;          // [slots, RING, 4, DI]
-  const void* kv_raw;   // [B, D] in the window dtype
-  void* win;            // [slots, Ws, D]
-  int win_elem;         // bytes per window element (4 or 2)
+  // the window's row planes (one for F32 / BF16; FP8MIX: codes, RoPE dims, scale) and
+  // the token's raw KV row in the same planes ([B] rows)
+  const void* raw[3];
+  void* win[3];
+  int plane_bytes[3];   // bytes per row of each plane (0: no plane)
   int n_win;
   int64_t Ws;
   int64_t* win_pos0;    // [slots]
@@ -725,21 +727,37 @@ __global__ __launch_bounds__(kThreads) void state_append_kernel(AppendArgs a) {
   for (int i = tid; i < 2 * kThreads; i += kThreads) (&amax_lds[0][0])[i] = 0u;
   if (a.kv.R > 0 && tid < a.kv.R / 2) theta_lds[tid] = rope_theta_rev(tid, a.kv.R, a.kv.log2_base);
 
-  // the raw KV row into the window; a full buffer first keeps its last n_win - 1 rows
+  // the raw KV row into the window; a full buffer first keeps its last n_win - 1 rows.
+  // Each plane moves in 16-byte pieces when its rows allow, else in dwords.
   const int64_t nwp0 = p - wp0 >= a.Ws ? p - a.n_win + 1 : wp0;
-  {
-    const int64_t rowb = static_cast<int64_t>(a.kv.D) * a.win_elem;  // bytes per row
-    const int64_t c16 = rowb / 16;
-    uint8_t* wb = static_cast<uint8_t*>(a.win) + s * a.Ws * rowb;
-    if (nwp0 != wp0) {
-      for (int64_t i = tid; i < static_cast<int64_t>(a.n_win - 1) * c16; i += kThreads) {
-        const int64_t j = i / c16, q = i % c16;
-        reinterpret_cast<uint4*>(wb + j * rowb)[q] = reinterpret_cast<const uint4*>(wb + (nwp0 - wp0 + j) * rowb)[q];
+#pragma unroll
+  for (int pl = 0; pl < 3; ++pl) {
+    const int64_t rowb = a.plane_bytes[pl];
+    if (rowb == 0) continue;
+    uint8_t* wb = static_cast<uint8_t*>(a.win[pl]) + s * a.Ws * rowb;
+    const uint8_t* rb = static_cast<const uint8_t*>(a.raw[pl]) + b * rowb;
+    if (rowb % 16 == 0) {
+      const int64_t c = rowb / 16;
+      if (nwp0 != wp0) {
+        for (int64_t i = tid; i < static_cast<int64_t>(a.n_win - 1) * c; i += kThreads) {
+          const int64_t j = i / c, q = i % c;
+          reinterpret_cast<uint4*>(wb + j * rowb)[q] = reinterpret_cast<const uint4*>(wb + (nwp0 - wp0 + j) * rowb)[q];
+        }
       }
+      for (int64_t i = tid; i < c; i += kThreads)
+        reinterpret_cast<uint4*>(wb + (p - nwp0) * rowb)[i] = reinterpret_cast<const uint4*>(rb)[i];
+    } else {
+      const int64_t c = rowb / 4;
+      if (nwp0 != wp0) {
+        for (int64_t i = tid; i < static_cast<int64_t>(a.n_win - 1) * c; i += kThreads) {
+          const int64_t j = i / c, q = i % c;
+          reinterpret_cast<uint32_t*>(wb + j * rowb)[q] =
+              reinterpret_cast<const uint32_t*>(wb + (nwp0 - wp0 + j) * rowb)[q];
+        }
+      }
+      for (int64_t i = tid; i < c; i += kThreads)
+        reinterpret_cast<uint32_t*>(wb + (p - nwp0) * rowb)[i] = reinterpret_cast<const uint32_t*>(rb)[i];
     }
-    for (int64_t i = tid; i < c16; i += kThreads)
-      reinterpret_cast<uint4*>(wb + (p - nwp0) * rowb)[i] =
-          reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.kv_raw) + b * rowb)[i];
   }
   if (a.vis_idx) {
     // every entry of a block before the token's own is visible (no overlap: dense);
@@ -913,9 +931,22 @@ int launch_state_append(const StateAppendLaunch& L, hipStream_t stream) {
   a.length = L.length;
   a.tail = L.tail;
   a.itail = L.itail;
-  a.kv_raw = L.kv_raw;
-  a.win = L.win;
-  a.win_elem = L.win_elem;
+  const int R = L.rope_dims;
+  if (L.win.dtype == CSA_FP8MIX) {
+    const void* raw[3] = {L.kv_raw.data, L.kv_raw.rope, L.kv_raw.scale};
+    void* win[3] = {L.win.data, L.win.rope, L.win.scale};
+    const int bytes[3] = {L.D - R, 2 * R, 4};
+    for (int i = 0; i < 3; ++i) {
+      a.raw[i] = raw[i];
+      a.win[i] = win[i];
+      a.plane_bytes[i] = bytes[i];
+      if (bytes[i] % 4) return -2;
+    }
+  } else {
+    a.raw[0] = L.kv_raw.data;
+    a.win[0] = L.win.data;
+    a.plane_bytes[0] = L.D * (L.win.dtype == CSA_F32 ? 4 : 2);
+  }
   a.n_win = L.n_win;
   a.Ws = L.Ws;
   a.win_pos0 = L.win_pos0;

@@ -49,9 +49,9 @@ struct StateAppendLaunch {
   const int32_t* slot;
   int64_t* length;
   void *tail, *itail;
-  const void* kv_raw;
-  void* win;
-  int win_elem, n_win;
+  csa_buf kv_raw;                     // [B, D] in the window's format
+  csa_buf win;                        // [slots, Ws, D] (F32, BF16 or FP8MIX planes)
+  int n_win;
   int64_t Ws;
   int64_t* win_pos0;
   int64_t *q_pos, *wp0_b, *wp0_adj;   // [B] outputs

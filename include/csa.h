@@ -414,29 +414,29 @@ csa_status csa_forward(const csa_layer_desc* L, const csa_forward_io* io, void* 
  *              ratio * (floor(length / ratio) - 1) .. length - 1 (those >= 0) (HCA: of
  *              the current block) are in the ring.
  *   itail      CSA: [slots, 2 ratio, 4, DI], the indexer streams, same rule
- *   win        [slots, 2 n_win, D] raw KV rows, F32 or BF16: row j holds position
+ *   win        [slots, 2 n_win, D] raw KV rows, F32, BF16 or FP8MIX: row j holds position
  *              win_pos0[s] + j.  Precondition: positions max(0, length - n_win + 1) ..
  *              length - 1 are present, and length - win_pos0[s] <= 2 n_win.  A row that
  *              would fall past the buffer first moves the last n_win - 1 rows to the front
  *              (win_pos0 advances).
  *   win_pos0   int64 [slots]
  * Paged caches, P = page_tokens / ratio entries per page:
- *   kv_pages   [pages, P, D], the dtype of win (F32 or BF16)
+ *   kv_pages   [pages, P, D], the format of win (F32, BF16 or FP8MIX)
  *   ik_pages   [pages, P, DI] (CSA), the dtype of qI (F32, BF16 or MXFP4)
  *   block_table int32 [slots, max_pages]: page holding entries j P .. (j + 1) P - 1 of the
  *              slot.  Precondition: assigned for every block holding an entry
  *              < (length + 1) / ratio.
  * Step tensors: ca, cb, za, zb [B, D] (HCA: ca = C, za = Z) and ica, icb, iza, izb
  *   [B, DI] (CSA): the new token's streams, in stream_dtype; biases as csa_compress;
- *   kv_raw [B, D] in win's dtype; q [B, H, D] and out (q's dtype); qI [B, HI, DI] and wI
+ *   kv_raw [B, D] in win's format; q [B, H, D] and out (q's dtype); qI [B, HI, DI] and wI
  *   [B, HI] (CSA); sink [H]; q_norm / kv_norm [D] with CSA_FLAG_QKV_NORM.
  *   idx_out (optional, CSA) int32 [B, topk]: the selected entries' pool rows (page * P +
  *   offset), in increasing entry order, -1 padded.  scores_out (optional, CSA) float
  *   [B, max_pages * P].
  * Limits: page_tokens a power of two and a multiple of ratio; CSA: P >= 512 (an indexer
  *   key range stays inside one page) and roundup(D / 8, 64) + DI / 8 <= 256 (one thread
- *   per 8 channels); D <= 1024; distinct slots within a batch; max_pages * P < 2^31.
- *   FP8MIX caches are not taken here.
+ *   per 8 channels); D <= 1024; distinct slots within a batch; max_pages * P < 2^31;
+ *   FP8MIX: (D - rope_dims) % 16 == 0, rope_dims % 8 == 0, no CSA_FLAG_QKV_NORM.
  */
 typedef struct csa_decode_desc {
   int32_t struct_size;   /* sizeof(csa_decode_desc) */
@@ -463,7 +463,7 @@ typedef struct csa_decode_io {
   const float *bias_a, *bias_b;          /* [ratio, D] or NULL */
   const void *ica, *icb, *iza, *izb;     /* [B, DI] (CSA) */
   const float *ibias_a, *ibias_b;
-  const void* kv_raw;                    /* [B, D] */
+  csa_buf kv_raw;                        /* [B, D], in win's format */
   void* tail;                            /* state pool, in/out */
   void* itail;
   csa_buf win;

@@ -23,8 +23,9 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import TOL, assert_close, ensure_built, f64, topk_sets_agree
+from helpers import assert_close, ensure_built, f64, topk_sets_agree
 from oracle import csa_oracle as O
+from oracle import quant as Q
 from synth import Gen, qstd
 
 pytestmark = pytest.mark.gpu
@@ -49,13 +50,47 @@ def _dt(name):
     return {"f32": (csa.CSA_F32, torch.float32), "bf16": (csa.CSA_BF16, torch.bfloat16)}[name]
 
 
+def decode_rows(b: "csa.Buf", rows) -> np.ndarray:
+    """Rows of a (flattened) buffer, dequantized on the host."""
+    rows = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=DEV)
+    if b.dtype in (csa.CSA_F32, csa.CSA_BF16):
+        return f64(b.data.reshape(-1, b.data.shape[-1])[rows])
+    if b.dtype == csa.CSA_FP8MIX:
+        return Q.fp8mix_dequantize(b.data.reshape(-1, b.data.shape[-1])[rows].cpu().numpy(),
+                                   b.rope.reshape(-1, b.rope.shape[-1])[rows].view(torch.int16).cpu().numpy()
+                                   .view(np.uint16), b.scale.reshape(-1)[rows].cpu().numpy())
+    return Q.mxfp4_dequantize(b.data.reshape(-1, b.data.shape[-1])[rows].cpu().numpy(),
+                              b.scale.reshape(-1, b.scale.shape[-1])[rows].cpu().numpy())
+
+
+def check_quantized(got, want, fmt, R, what):
+    """A stored entry against the oracle's fp64 value: nearly every element equals the
+    oracle's own quantization of it (the kernel rounds an fp32 value, so a code may
+    move one step where the fp64 value sits on a rounding boundary), and every element
+    lies within the format's rounding error of the exact value."""
+    if fmt == csa.CSA_FP8MIX:
+        ref = Q.fp8mix_dequantize(*Q.fp8mix_quantize(want, R))
+        assert np.mean(np.isclose(got, ref)) > 0.99, what
+        assert_close(got, want, "fp8", what)
+        return
+    ref = Q.mxfp4_dequantize(*Q.mxfp4_quantize(want))
+    assert np.mean(np.isclose(got, ref)) > 0.99, what
+    blk = np.abs(want).reshape(want.shape[0], -1, 32).max(-1)
+    err = np.abs(got - want).reshape(want.shape[0], -1, 32)
+    assert np.all(err <= blk[..., None] / 4 + 1e-6), what   # half an e2m1 step at the top binade
+
+
 class Harness:
     def __init__(self, mode, lengths, *, D, DI, H, HI, ratio, n_win, page_tokens, topk, R, dtype, seed, norm=False,
-                 rollover=(), steps=4, flags=0):
+                 rollover=(), steps=4, flags=0, quantized=False):
+        """quantized: FP8MIX KV cache and window, MXFP4 indexer keys and queries (bf16 streams)."""
         self.csa_mode = mode == csa.CSA_MODE_CSA
         self.g = g = Gen(seed, DEV)
         self.cd, self.td = _dt(dtype)
         self.dtype = dtype
+        self.quantized = quantized
+        self.kvd = csa.CSA_FP8MIX if quantized else self.cd
+        self.ikd = csa.CSA_MXFP4 if quantized else self.cd
         self.B = B = len(lengths)
         self.D, self.DI, self.H, self.HI, self.m, self.W, self.R, self.k = D, DI, H, HI, ratio, n_win, R, topk
         self.scale = D ** -0.5
@@ -65,8 +100,8 @@ class Harness:
         pages = slots * max_pages + 5
         self.P = P
         self.pool = csa.DecodePool(mode=mode, slots=slots, pages=pages, max_pages=max_pages, page_tokens=page_tokens,
-                                   D=D, DI=DI, ratio=ratio, n_win=n_win, stream_dtype=self.cd, kv_dtype=self.cd,
-                                   ik_dtype=self.cd)
+                                   D=D, DI=DI, ratio=ratio, n_win=n_win, stream_dtype=self.cd, kv_dtype=self.kvd,
+                                   ik_dtype=self.ikd, rope_dims=R)
         gen = torch.Generator().manual_seed(seed)
         self.slots_of = torch.randperm(slots, generator=gen)[:B].tolist()
         self.slot = torch.tensor(self.slots_of, dtype=torch.int32, device=DEV)
@@ -74,13 +109,14 @@ class Harness:
         self.table = table.numpy()
         self.pool.block_table.copy_(table)
         self.page_owner = {int(pg): (s, j) for s in range(slots) for j, pg in enumerate(self.table[s])}
-        # seeded contents: every page, ring row and window row
-        self.pool.kv_pages.data.copy_(g.normal(self.pool.kv_pages.data.shape, 0.5, dtype=self.td))
+        # seeded contents: every page, ring row and window row (quantized formats: seeded
+        # fp32 Gaussians through the library's quantizer)
+        self._fill(self.pool.kv_pages, self.kvd, pages * P, D, 0.5)
         if self.csa_mode:
-            self.pool.ik_pages.data.copy_(g.normal(self.pool.ik_pages.data.shape, 0.5, dtype=self.td))
+            self._fill(self.pool.ik_pages, self.ikd, pages * P, DI, 0.5)
             self.pool.itail.copy_(g.normal(self.pool.itail.shape, dtype=self.td))
         self.pool.tail.copy_(g.normal(self.pool.tail.shape, dtype=self.td))
-        self.pool.win.copy_(g.normal(self.pool.win.shape, dtype=self.td))
+        self._fill(self.pool.win, self.kvd, slots * 2 * n_win, D, 1.0)
         L = torch.zeros(slots, dtype=torch.int64)
         wp0 = torch.zeros(slots, dtype=torch.int64)
         for b, (s, n) in enumerate(zip(self.slots_of, lengths)):
@@ -104,7 +140,7 @@ class Harness:
         self.rows, self.raw = {}, {}
         tail = f64(self.pool.tail)
         itail = f64(self.pool.itail) if self.csa_mode else None
-        win = f64(self.pool.win)
+        win = decode_rows(csa.Buf.of(self.pool.win), np.arange(slots * 2 * n_win)).reshape(slots, 2 * n_win, D)
         ring = tail.shape[1]
         for s, n in zip(self.slots_of, lengths):
             first = ratio * (n // ratio - 1) if self.csa_mode else ratio * (n // ratio)
@@ -113,28 +149,69 @@ class Harness:
             for p in range(max(0, n - n_win + 1), n):
                 self.raw[s, p] = win[s, p - int(wp0[s])]
 
+    def _fill(self, buf, fmt, rows, width, std):
+        b = buf if isinstance(buf, csa.Buf) else csa.Buf.of(buf)
+        if fmt in (csa.CSA_F32, csa.CSA_BF16):
+            b.data.copy_(self.g.normal(b.data.shape, std, dtype=self.td))
+            return
+        for r0 in range(0, rows, 1 << 16):
+            r1 = min(rows, r0 + (1 << 16))
+            part = csa.Buf(fmt, b.data.reshape(-1, b.data.shape[-1])[r0:r1],
+                           None if b.rope is None else b.rope.reshape(-1, b.rope.shape[-1])[r0:r1],
+                           None if b.scale is None else (b.scale.reshape(-1)[r0:r1] if fmt == csa.CSA_FP8MIX else
+                                                         b.scale.reshape(-1, b.scale.shape[-1])[r0:r1]))
+            csa.csa_quantize(self.g.normal((r1 - r0, width), std), part, rope_dims=self.R if fmt == csa.CSA_FP8MIX else 0)
+
+    def _quantized(self, x, fmt):
+        """A [rows.., width] fp32 tensor stored in fmt (Buf), and its dequantized host copy."""
+        shape = tuple(x.shape)
+        b = csa.Buf.empty(shape, fmt, rope_dims=self.R if fmt == csa.CSA_FP8MIX else 0)
+        csa.csa_quantize(x.reshape(-1, shape[-1]).contiguous(), b, rope_dims=self.R if fmt == csa.CSA_FP8MIX else 0)
+        torch.cuda.synchronize()
+        flat = csa.Buf(fmt, b.data.reshape(-1, b.data.shape[-1]),
+                       None if b.rope is None else b.rope.reshape(-1, b.rope.shape[-1]),
+                       b.scale.reshape(-1) if fmt == csa.CSA_FP8MIX else b.scale.reshape(-1, b.scale.shape[-1]))
+        return b, decode_rows(flat, np.arange(int(np.prod(shape[:-1])))).reshape(shape)
+
     # ------------------------------------------------------------------ one step
     def inputs(self):
         g, B, D, DI = self.g, self.B, self.D, self.DI
         ns = 4 if self.csa_mode else 2
         x = dict(streams=[g.normal((B, D), dtype=self.td) for _ in range(ns)],
                  istreams=[g.normal((B, DI), dtype=self.td) for _ in range(4)] if self.csa_mode else None,
-                 kv_raw=g.normal((B, D), dtype=self.td), q=g.normal((B, self.H, D), qstd(D), dtype=self.td))
+                 q=g.normal((B, self.H, D), qstd(D), dtype=self.td))
+        if self.quantized:
+            x["kv_raw"], x["kv_raw_h"] = self._quantized(g.normal((B, D)), self.kvd)
+        else:
+            x["kv_raw"] = g.normal((B, D), dtype=self.td)
+            x["kv_raw_h"] = f64(x["kv_raw"])
         if self.csa_mode:
-            x.update(qI=g.normal((B, self.HI, DI), qstd(DI), dtype=self.td), wI=g.uniform((B, self.HI)))
+            if self.quantized:
+                x["qI"], x["qI_h"] = self._quantized(g.normal((B, self.HI, DI), qstd(DI)), self.ikd)
+            else:
+                x["qI"] = g.normal((B, self.HI, DI), qstd(DI), dtype=self.td)
+                x["qI_h"] = f64(x["qI"])
+            x["wI"] = g.uniform((B, self.HI))
         return x
+
+    @staticmethod
+    def _rows(t, sl):
+        if isinstance(t, csa.Buf):
+            return csa.Buf(t.dtype, t.data[sl].contiguous(), None if t.rope is None else t.rope[sl].contiguous(),
+                           None if t.scale is None else t.scale[sl].contiguous())
+        return t[sl].contiguous()
 
     def io(self, pool, x, rows=None):
         sl = slice(None) if rows is None else rows
         st = [t[sl].contiguous() for t in x["streams"]]
-        io = dict(pool.io(), slot=self.slot[sl].contiguous(), kv_raw=x["kv_raw"][sl].contiguous(),
+        io = dict(pool.io(), slot=self.slot[sl].contiguous(), kv_raw=self._rows(x["kv_raw"], sl),
                   q=x["q"][sl].contiguous(), sink=self.sink, out=torch.empty_like(x["q"][sl]), bias_a=self.bias[0],
                   q_norm=self.q_norm, kv_norm=self.kv_norm)
         if self.csa_mode:
             ist = [t[sl].contiguous() for t in x["istreams"]]
             n = x["q"][sl].shape[0]
             io.update(ca=st[0], cb=st[1], za=st[2], zb=st[3], bias_b=self.bias[1], ica=ist[0], icb=ist[1],
-                      iza=ist[2], izb=ist[3], ibias_a=self.ibias[0], ibias_b=self.ibias[1], qI=x["qI"][sl].contiguous(),
+                      iza=ist[2], izb=ist[3], ibias_a=self.ibias[0], ibias_b=self.ibias[1], qI=self._rows(x["qI"], sl),
                       wI=x["wI"][sl].contiguous(), idx_out=torch.empty((n, self.k), dtype=torch.int32, device=DEV),
                       scores_out=torch.empty((n, self.desc.max_pages * self.P), dtype=torch.float32, device=DEV))
         else:
@@ -144,12 +221,17 @@ class Harness:
     def clone_pool(self):
         c = csa.DecodePool.__new__(csa.DecodePool)
         c.P = self.pool.P
-        for name in ("length", "tail", "itail", "win", "win_pos0", "block_table"):
+        for name in ("length", "tail", "itail", "win_pos0", "block_table"):
             t = getattr(self.pool, name)
             setattr(c, name, None if t is None else t.clone())
-        for name in ("kv_pages", "ik_pages"):
+        for name in ("win", "kv_pages", "ik_pages"):
             b = getattr(self.pool, name)
-            setattr(c, name, None if b is None else csa.Buf(b.dtype, b.data.clone()))
+            if isinstance(b, csa.Buf):
+                b = csa.Buf(b.dtype, b.data.clone(), None if b.rope is None else b.rope.clone(),
+                            None if b.scale is None else b.scale.clone())
+            elif b is not None:
+                b = b.clone()
+            setattr(c, name, b)
         return c
 
     def run(self, x, *, invariance=False):
@@ -175,11 +257,12 @@ class Harness:
                 assert torch.equal(io["out"][b], solo[b]["out"][0]), f"output of sequence {b} depends on the batch"
                 if self.csa_mode:
                     assert torch.equal(io["idx_out"][b], solo[b]["idx_out"][0]), f"selection of sequence {b}"
-            for name in ("length", "win", "win_pos0", "tail") + (("itail",) if self.csa_mode else ()):
+            for name in ("length", "win_pos0", "tail") + (("itail",) if self.csa_mode else ()):
                 assert torch.equal(getattr(self.pool, name), getattr(cp, name)), f"state {name} depends on the batch"
-            assert torch.equal(self.pool.kv_pages.data, cp.kv_pages.data), "cache pages depend on the batch"
-            if self.csa_mode:
-                assert torch.equal(self.pool.ik_pages.data, cp.ik_pages.data), "key pages depend on the batch"
+            for name in ("win", "kv_pages") + (("ik_pages",) if self.csa_mode else ()):
+                a_, b_ = csa.Buf.of(getattr(self.pool, name)), csa.Buf.of(getattr(cp, name))
+                for x_, y_ in ((a_.data, b_.data), (a_.rope, b_.rope), (a_.scale, b_.scale)):
+                    assert (x_ is None) == (y_ is None) and (x_ is None or torch.equal(x_, y_)), f"{name} depends on the batch"
             say("  batch invariance: bitwise identical to one-sequence steps")
         return io, pre_len
 
@@ -188,15 +271,17 @@ class Harness:
         return int(self.table[s][e // self.P]) * self.P + e % self.P
 
     def gather(self, buf, s, ents, width):
-        rows = torch.tensor([self.pool_row(s, int(e)) for e in ents], dtype=torch.int64, device=DEV)
-        return f64(buf.data.view(-1, width)[rows]) if len(ents) else np.zeros((0, width))
+        if not len(ents):
+            return np.zeros((0, width))
+        return decode_rows(buf, [self.pool_row(s, int(e)) for e in ents])
 
     def check(self, x, io, pre_len):
         m, W, D, DI = self.m, self.W, self.D, self.DI
         kind = self.dtype
         length = self.pool.length.cpu().numpy()
         wp0 = self.pool.win_pos0.cpu().numpy()
-        win = f64(self.pool.win)
+        slots, rows2 = self.pool.length.shape[0], 2 * self.W
+        win = decode_rows(csa.Buf.of(self.pool.win), np.arange(slots * rows2)).reshape(slots, rows2, self.D)
         n_done = 0
         for b, s in enumerate(self.slots_of):
             p = int(pre_len[s])
@@ -204,7 +289,7 @@ class Harness:
             st = [f64(t[b]) for t in x["streams"]]
             ist = [f64(t[b]) for t in x["istreams"]] if self.csa_mode else None
             self.rows[s, p] = (np.stack(st), np.stack(ist) if self.csa_mode else None)
-            self.raw[s, p] = f64(x["kv_raw"][b])
+            self.raw[s, p] = x["kv_raw_h"][b]
             # window rows the attention reads: bitwise the rows handed in
             assert wp0[s] <= max(0, p - W + 1) and p - wp0[s] < 2 * W
             for q in range(max(0, p - W + 1), p + 1):
@@ -239,7 +324,10 @@ class Harness:
                               bias_a=f64(self.bias[0]), rope_dims=self.R, rope_base=BASE,
                               norm_weight=None if self.kv_norm is None else f64(self.kv_norm))
         got = self.gather(self.pool.kv_pages, s, [I], self.D)
-        assert_close(got, O.store(want, kind), kind, f"entry {I} of slot {s}")
+        if self.quantized:
+            check_quantized(got, want, csa.CSA_FP8MIX, self.R, f"entry {I} of slot {s}")
+        else:
+            assert_close(got, O.store(want, kind), kind, f"entry {I} of slot {s}")
         if self.csa_mode:
             icur, iprev = self._block(s, I, 1)
             iwant = O.compress(icur[:, 0], icur[:, 1], icur[:, 2], icur[:, 3], ratio=m, overlap=True, t0=m * I,
@@ -247,7 +335,10 @@ class Harness:
                                prev_zb=None if iprev is None else iprev[:, 3], bias_a=f64(self.ibias[0]),
                                bias_b=f64(self.ibias[1]))
             igot = self.gather(self.pool.ik_pages, s, [I], self.DI)
-            assert_close(igot, O.store(iwant, kind), kind, f"indexer key {I} of slot {s}")
+            if self.quantized:
+                check_quantized(igot, iwant, csa.CSA_MXFP4, 0, f"indexer key {I} of slot {s}")
+            else:
+                assert_close(igot, O.store(iwant, kind), kind, f"indexer key {I} of slot {s}")
 
     def _window(self, s, p):
         w0 = max(0, p - self.W + 1)
@@ -261,7 +352,7 @@ class Harness:
         m, k = self.m, self.k
         vis = p // m
         keys = self.gather(self.pool.ik_pages, s, range(vis), self.DI)
-        ref = O.index_scores(f64(x["qI"][b])[None], f64(x["wI"][b])[None], keys, np.array([p]), m)[0]
+        ref = O.index_scores(x["qI_h"][b][None], f64(x["wI"][b])[None], keys, np.array([p]), m)[0]
         gs = io["scores_out"][b].cpu().numpy().astype(np.float64)
         assert np.all(np.isneginf(gs[vis:])), "entries past the visible ones must score -inf"
         assert_close(gs[:vis], ref, "f32", f"scores of sequence {b}")
@@ -283,7 +374,8 @@ class Harness:
         win, w0 = self._window(s, p)
         want = O.mqa(f64(x["q"][b])[None], np.array([p]), kv, np.arange(cnt)[None], win, w0, self.W, f64(self.sink),
                      scale=self.scale, rope_dims=self.R, rope_base=BASE, **self._norms())[0]
-        assert_close(f64(io["out"][b]), O.store(want, kind), kind, f"output of sequence {b}")
+        assert_close(f64(io["out"][b]), O.store(want, kind), "fp8" if self.quantized else kind,
+                     f"output of sequence {b}")
 
     def _check_hca_query(self, b, s, p, x, io, kind):
         vis = p // self.m
@@ -334,6 +426,16 @@ def test_decode_state_bf16_fused_selection_norms():
     _run(h, 5, invariance_step=1)
 
 
+def test_decode_state_fp8_kv_mxfp4_indexer():
+    # the mixed-precision decode layer ([V4-CN] §2.3.4, §3.4): FP8MIX KV pages and
+    # window, MXFP4 indexer keys and queries; parity on dequantized inputs
+    say("decode state: CSA with FP8MIX KV and MXFP4 indexer")
+    lengths = [4095, 6000, 8191, 2050, 513, 10001, 3, 7]
+    h = Harness(csa.CSA_MODE_CSA, lengths, D=512, DI=128, H=64, HI=64, ratio=4, n_win=128, page_tokens=2048,
+                topk=256, R=64, dtype="bf16", seed=616, rollover=(1, 5), quantized=True)
+    assert _run(h, 4, invariance_step=2) >= 8
+
+
 def test_decode_state_hca():
     # HCA (m' = 128, no overlap): blocks complete at positions 127 mod 128; every
     # visible entry is attended through the block table (32 entries per 4096-token page)
@@ -350,3 +452,12 @@ def test_decode_state_hca_norms():
     h = Harness(csa.CSA_MODE_HCA, lengths, D=512, DI=128, H=16, HI=16, ratio=128, n_win=128, page_tokens=4096,
                 topk=1, R=64, dtype="bf16", seed=615, norm=True)
     assert _run(h, 2) >= 3
+
+
+def test_decode_state_hca_fp8_kv():
+    # HCA with an FP8MIX cache and window: completed blocks quantized in the append step
+    say("decode state: HCA with FP8MIX KV")
+    lengths = [127, 255, 4095, 9000]
+    h = Harness(csa.CSA_MODE_HCA, lengths, D=512, DI=128, H=64, HI=64, ratio=128, n_win=128, page_tokens=4096,
+                topk=1, R=64, dtype="bf16", seed=617, rollover=(2,), quantized=True)
+    assert _run(h, 2, invariance_step=1) >= 3

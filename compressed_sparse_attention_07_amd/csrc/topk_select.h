@@ -70,6 +70,7 @@ struct TopkArgs {
 
 constexpr int kFewCand = 64;  // a threshold bin this small is resolved by one wave
 constexpr int kPageLds = 1024;  // block-table entries a final level stages in LDS
+constexpr int kMaxTopK = 4096;  // largest k (the entry points reject more)
 
 template <int NT>
 struct Shared {
@@ -525,15 +526,20 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
     oi = a.out_idx + o;
     ov = a.out_val + o;
   }
+  // The last level stages the selected entries in LDS at their output slots and writes
+  // them (as pool rows for a paged cache) in one coalesced pass afterwards: each of the
+  // unrolled rounds below is then a few instructions, where translating in place put a
+  // page lookup into every round (the rounds run once per launch, from a cold
+  // instruction cache, so their code size is their cost).
+  __shared__ int32_t stg[FINAL ? kMaxTopK : 1];
   auto put = [&](int j, uint32_t slot) {
     const int32_t e = PAIRS ? ix[PAIRS ? j : 0] : static_cast<int32_t>(lo + j * NT + tid);
-    if (pg_in_lds)
-      oi[slot] = (pg_lds[e >> a.omap.shift] << a.omap.shift) | (e & ((1 << a.omap.shift) - 1));
-    else if (FINAL && a.omap.table)
-      oi[slot] = static_cast<int32_t>(paged_row(a.omap, r / a.tq, e));
-    else
+    if (FINAL) {
+      stg[slot] = e;
+    } else {
       oi[slot] = e;
-    if (!FINAL) ov[slot] = v[j];
+      ov[slot] = v[j];
+    }
   };
   if (one_test && with_eq) {
 #pragma unroll
@@ -559,12 +565,31 @@ __device__ __forceinline__ bool select_slice(const TopkArgs& a, Shared<NT>& sh, 
       if (gt || (eq && tbf < ties)) put(j, gb + (tbf < ties ? tbf : ties));
     }
   }
-  if (!FINAL && a.out_cnt) {
+  if (FINAL) {
+    __syncthreads();
+    const int n_sel = static_cast<int>(total_sel);
+    const int psh = a.omap.shift;
+    const int32_t pmask = (1 << psh) - 1;
+    if (pg_in_lds) {
+      for (int i = tid; i < a.k; i += NT) {
+        const int32_t e = i < n_sel ? stg[i] : 0;
+        oi[i] = i < n_sel ? ((pg_lds[e >> psh] << psh) | (e & pmask)) : -1;
+      }
+    } else if (a.omap.table) {
+      const int32_t* trow = a.omap.table + static_cast<int64_t>(a.omap.slot[r / a.tq]) * a.omap.max_pages;
+      for (int i = tid; i < a.k; i += NT) {
+        const int32_t e = i < n_sel ? stg[i] : 0;
+        oi[i] = i < n_sel ? ((trow[e >> psh] << psh) | (e & pmask)) : -1;
+      }
+    } else {
+      for (int i = tid; i < a.k; i += NT) oi[i] = i < n_sel ? stg[i] : -1;
+    }
+  } else if (a.out_cnt) {
     if (tid == 0) a.out_cnt[r * a.slices + sl] = static_cast<int32_t>(total_sel);
   } else {
     for (int i = static_cast<int>(total_sel) + tid; i < a.k; i += NT) {
       oi[i] = -1;
-      if (!FINAL) ov[i] = -INFINITY;
+      ov[i] = -INFINITY;
     }
   }
   if (FINAL && a.count && tid == 0) a.count[r] = static_cast<int32_t>(total_sel);

@@ -368,6 +368,9 @@ ATTN_CASES = [
     (1, 2, 32, 512, 3000, 2040, 128, "bf16", "bf16", 64, 1.0, [9000, 12100]),
     # window clipped at position 0, fewer selected entries than one tile
     (2, 1, 128, 512, 40, 30, 128, "bf16", "bf16", 64, 1.0, [60]),
+    # decode on the wave-pair kernel: 64 heads (two 32-head pairs), 16 heads (one 16-head pair)
+    (2, 2, 64, 512, 300, 128, 128, "bf16", "bf16", 64, 1.0, [1300, 5000]),
+    (1, 2, 16, 512, 300, 96, 128, "bf16", "bf16", 64, 1.0, [1300, 5000]),
     # every other instantiated kernel shape: LDS-DMA with 2 waves on the pipelined loop
     # (prefill), register-staged FP8MIX with 1 and 2 waves, D = 128 / 256 with 1-8 waves
     (1, 260, 32, 512, 400, 64, 128, "bf16", "bf16", 64, 1.0 / math.sqrt(512), list(range(1600, 1860))),

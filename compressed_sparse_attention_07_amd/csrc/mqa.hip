@@ -1316,8 +1316,8 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
 // (token, head), lane l owns output dims [8l, 8l + 8) (D <= 512, nsplit <= 64).
 // The split weights exp(m_i - M) * l_i are formed once per wave (lane i holds split
 // i) and broadcast; every lane issues all its partial loads before combining.
+template <int kBatchSplits>  // partial loads in flight per lane (no more than the splits when they fit)
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int kBatchSplits = 16;  // partial loads in flight per lane
   const int lane = threadIdx.x & 63;
   const int64_t th = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (th >= a.B * a.Tq * a.H) return;
@@ -1796,7 +1796,9 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
     if (hipGetLastError() != hipSuccess) return -1;
     if (P.nsplit > 1) {
       const int64_t waves = tokens * L.H;
-      hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<uint32_t>((waves + 3) / 4)), dim3(256), 0, stream, a);
+      const dim3 cg(static_cast<uint32_t>((waves + 3) / 4));
+      if (P.nsplit <= 8) hipLaunchKernelGGL(attn_combine_kernel<8>, cg, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL(attn_combine_kernel<16>, cg, dim3(256), 0, stream, a);
       if (hipGetLastError() != hipSuccess) return -1;
     }
     return 0;

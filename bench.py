@@ -763,6 +763,73 @@ def layer_edges(wl: Workload, steps: int, reps: int):
     return out
 
 
+def fp8_query_edge(wl: Workload, reps: int):
+    """The sparse attention stage over an FP8MIX cache with bf16 queries and with FP8MIX
+    queries (QK products of the codes on fp8 MFMA), same selections; plus the cost of
+    quantizing the step's queries.  CSA workloads with an FP8MIX cache, or prefill chunks
+    (whose bf16 cache is quantized for the comparison); None otherwise."""
+    import torch
+
+    import compressed_sparse_attention_07_amd as csa
+
+    M = wl.meta
+    fp8_cache = M["kv_format"] == "fp8mix"
+    if M["mode"] != "csa" or not (fp8_cache or M["Tq"] > 1) or M["D"] != 512 or M["R"] != 64:
+        return None
+    B, Tq, H, D, R, N, k, W = (M[x] for x in ("B", "Tq", "H", "D", "R", "N", "k", "W"))
+    io = wl.ios[0]
+    cfg = wl.cfg
+
+    def quantized(x):  # [.., D] bf16 or fp32 tensor -> FP8MIX Buf of the same rows
+        rows = x.numel() // D
+        b = csa.Buf.empty(tuple(x.shape), csa.CSA_FP8MIX, rope_dims=R)
+        flat = csa.Buf(b.dtype, b.data.view(rows, D - R), b.rope.view(rows, R), b.scale.view(rows))
+        xv = x.reshape(rows, D)
+        for r0 in range(0, rows, 1 << 16):
+            r1 = min(rows, r0 + (1 << 16))
+            csa.csa_quantize(xv[r0:r1].float().contiguous(),
+                             csa.Buf(b.dtype, flat.data[r0:r1], flat.rope[r0:r1], flat.scale[r0:r1]), rope_dims=R)
+        return b
+
+    kv8 = io["kv_cache"] if fp8_cache else quantized(io["kv_cache"].data if isinstance(io["kv_cache"], csa.Buf)
+                                                     else io["kv_cache"])
+    win8 = io["win"] if fp8_cache else quantized(io["win"].data if isinstance(io["win"], csa.Buf) else io["win"])
+    q = io["q"]
+    q8 = quantized(q)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device="cuda")
+    w = torch.empty(max(1, csa.csa_forward_workspace_size(wl.desc_attend)), dtype=torch.uint8, device="cuda")
+    csa.csa_forward(wl.desc_attend, dict(io, idx_out=idx), ws=w)
+    del w
+    mqa_ws = torch.empty(max(1, csa.lib().csa_sparse_mqa_workspace_size(B, Tq, H, D, k, W)), dtype=torch.uint8,
+                         device="cuda")
+    outs = [torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    calls = [csa.PreparedCall(csa.csa_sparse_mqa, qq, io["q_pos"], kv8, idx, win8, io["win_pos0"], io["sink"], o,
+                              N=N, n_win=W, softmax_scale=cfg.softmax_scale, rope_dims=R, rope_base=cfg.rope_base,
+                              ws=mqa_ws) for qq, o in ((q, outs[0]), (q8, outs[1]))]
+    t_bf16 = time_stage(lambda i: calls[0](), reps)
+    t_fp8 = time_stage(lambda i: calls[1](), reps)
+    qrows = B * Tq * H
+    qf32 = q.reshape(qrows, D).float().contiguous() if qrows <= (1 << 16) else None
+    t_quant = None
+    if qf32 is not None:
+        qb = csa.Buf(q8.dtype, q8.data.view(qrows, D - R), q8.rope.view(qrows, R), q8.scale.view(qrows))
+        qcall = csa.PreparedCall(csa.csa_quantize, qf32, qb, rope_dims=R)
+        t_quant = time_stage(lambda i: qcall(), reps)
+    torch.cuda.synchronize()
+    diff = (outs[0].float() - outs[1].float()).abs().max().item()
+    flops = wl.stages["sparse_mqa"].flops
+    res = dict(attend_us_bf16_query=round(t_bf16 * 1e6, 2), attend_us_fp8_query=round(t_fp8 * 1e6, 2),
+               mfma_frac_bf16_query=round(flops / t_bf16 / MFMA_BF16_PEAK, 4),
+               mfma_frac_fp8_query_vs_bf16_peak=round(flops / t_fp8 / MFMA_BF16_PEAK, 4),
+               query_quantize_us=None if t_quant is None else round(t_quant * 1e6, 2),
+               max_abs_diff_vs_bf16_query=round(diff, 5),
+               cache="FP8MIX" if fp8_cache else "FP8MIX quantized from the workload's bf16 cache",
+               kernel="attn_dma_kernel (fp8 query products)")
+    log(f"  FP8MIX cache: attention {t_bf16 * 1e6:.1f} us with bf16 queries, {t_fp8 * 1e6:.1f} us with FP8MIX "
+        f"queries (max |diff| {diff:.4f})")
+    return res
+
+
 def decode_state_bench(wl: Workload, steps: int, warmup: int):
     """The same decode layer served by csa_decode_step from a state pool and paged caches
     (ragged lengths near the workload's context; every step appends one token per
@@ -922,6 +989,7 @@ def main():
 
     wl, value, ms_per_step, stage_out, roofline = run_workload(args.config, steps, warmup, layers, reps)
     edges = layer_edges(wl, steps, reps)
+    fq = fp8_query_edge(wl, reps)
     dstate = decode_state_bench(wl, steps, warmup)
 
     if args.copy_probe:
@@ -961,6 +1029,8 @@ def main():
         line["cache_build_compress"] = wl.build
     if edges:
         line["layer_edges"] = edges
+    if fq:
+        line["fp8_query"] = fq
     if dstate:
         line["decode_state"] = dstate
     if not args.no_others:
@@ -979,6 +1049,9 @@ def main():
             e2 = layer_edges(w2, 16 if dec else 3, 10 if dec else 3)
             if e2:
                 others[WORKLOAD_TAGS[key]]["layer_edges"] = e2
+            f2 = fp8_query_edge(w2, 10 if dec else 3)
+            if f2:
+                others[WORKLOAD_TAGS[key]]["fp8_query"] = f2
             d2 = decode_state_bench(w2, 16, 4) if dec else None
             if d2:
                 others[WORKLOAD_TAGS[key]]["decode_state"] = d2

@@ -128,6 +128,25 @@ csa_status validate_compress(const void* ca, const void* cb, const void* za, con
   return CSA_OK;
 }
 
+// The query and output formats: F32 or BF16 queries with an output of the same dtype,
+// or FP8MIX queries (e4m3 codes of the D - R leading dims, bf16 RoPE dims, a scale per
+// head) with an FP8MIX cache, whose QK products then run on fp8 MFMA, and a BF16 output
+csa_status check_query(const csa_buf* q, int32_t kv_dtype, const csa_buf* out, int32_t D, int32_t rope_dims,
+                       int32_t H) {
+  if (q->dtype == CSA_FP8MIX) {
+    if (kv_dtype != CSA_FP8MIX) return fail(CSA_ERR_UNSUPPORTED, "FP8MIX queries need an FP8MIX cache");
+    if (D != 512 || rope_dims != 64 || (H != 64 && H != 128 && H != 256))
+      return fail(CSA_ERR_UNSUPPORTED, "FP8MIX queries need D = 512, rope_dims = 64 and H in {64, 128, 256}");
+    if (!q->rope) return fail(CSA_ERR_NULL, "FP8MIX queries need a rope pointer");
+    if (reinterpret_cast<uintptr_t>(q->scale) & 3) return fail(CSA_ERR_SHAPE, "the query scales must be 4-byte aligned");
+    if (out->dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "out must be BF16 for FP8MIX queries");
+    return CSA_OK;
+  }
+  if (q->dtype != CSA_F32 && q->dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "q must be F32, BF16 or FP8MIX");
+  if (out->dtype != q->dtype) return fail(CSA_ERR_DTYPE, "out must have the dtype of q");
+  return CSA_OK;
+}
+
 csa_status validate_attn(const csa_buf* q, const int64_t* q_pos, const csa_buf* kv, int64_t kv_rows,
                          const csa_buf* win, const int64_t* win_pos0, int64_t Tw, const float* sink,
                          int32_t rope_dims, float rope_base, int64_t B, int64_t Tq, int32_t H, int32_t D, int64_t N,
@@ -137,8 +156,7 @@ csa_status validate_attn(const csa_buf* q, const int64_t* q_pos, const csa_buf* 
   CSA_TRY(check_buf(win, "win"));
   CSA_TRY(check_buf(out, "out"));
   if (!q_pos || !win_pos0 || !sink) return fail(CSA_ERR_NULL, "q_pos, win_pos0 and sink are required");
-  if (q->dtype != CSA_F32 && q->dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "q must be F32 or BF16");
-  if (out->dtype != q->dtype) return fail(CSA_ERR_DTYPE, "out must have the dtype of q");
+  CSA_TRY(check_query(q, kv->dtype, out, D, rope_dims, H));
   if (kv->dtype == CSA_MXFP4) return fail(CSA_ERR_DTYPE, "attention cache cannot be MXFP4");
   if (win->dtype != kv->dtype) return fail(CSA_ERR_DTYPE, "win must have the dtype of kv");
   if (D < 8 || D > 1024 || D % 8) return fail(CSA_ERR_SHAPE, "D=%d must be a multiple of 8 in [8, 1024]", D);
@@ -948,8 +966,7 @@ csa_status csa_decode_step(const csa_decode_desc* L, const csa_decode_io* io, vo
   CSA_TRY(check_buf(&io->win, "win"));
   CSA_TRY(check_buf(&io->out, "out"));
   if (!io->sink) return fail(CSA_ERR_NULL, "sink is required");
-  if (io->q.dtype != CSA_F32 && io->q.dtype != CSA_BF16) return fail(CSA_ERR_DTYPE, "q must be F32 or BF16");
-  if (io->out.dtype != io->q.dtype) return fail(CSA_ERR_DTYPE, "out must have the dtype of q");
+  CSA_TRY(check_query(&io->q, io->kv_pages.dtype, &io->out, L->D, L->rope_dims, L->H));
   CSA_TRY(check_buf(&io->kv_raw, "kv_raw"));
   if (io->kv_pages.dtype == CSA_MXFP4) return fail(CSA_ERR_DTYPE, "the attention cache cannot be MXFP4");
   if (io->win.dtype != io->kv_pages.dtype || io->kv_raw.dtype != io->kv_pages.dtype)

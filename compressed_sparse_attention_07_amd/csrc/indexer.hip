@@ -631,8 +631,6 @@ PrefillKern pick_prefill(int HB, int KS) {
   return nullptr;
 }
 
-typedef int v8i32 __attribute__((ext_vector_type(8)));
-
 // MXFP4 scores: HB head blocks of 16, KS4 steps of 128 elements (DI = 128 KS4).  One
 // wave per token and key range, as index_mfma_kernel.
 template <int HB, int KS4>

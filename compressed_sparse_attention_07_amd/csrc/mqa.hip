@@ -48,6 +48,8 @@ struct AttnArgs {
   const float* kv_scale;
   const uint16_t* win_rope;
   const float* win_scale;
+  const uint16_t* q_rope;  // FP8MIX queries: bf16 RoPE dims [tokens, H, R]
+  const float* q_scale;    //               and the per-(token, head) scale
   const float* sink;
   void* out;
   uint16_t* part_o; // [tokens, H, nsplit, D] bf16, O / l of the split
@@ -521,7 +523,7 @@ constexpr int kDmaStages = 4;
 constexpr bool kDmaPipe = true;  // prefill launches take the software-pipelined loop
 constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
 
-template <int NW, int R, bool FP8, bool PIPE = false>
+template <int NW, int R, bool FP8, bool PIPE = false, bool FQ = false>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int D = 512;
   constexpr int NT = NW * 64;
@@ -534,11 +536,12 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int RAWROW = (D - R) + 2 * R;  // bytes of an FP8MIX row: codes, then bf16 RoPE dims
   static_assert(RPW * LPR * (kDmaStages - 2) < 64, "outstanding row loads must fit vmcnt");
   static_assert(!FP8 || STAGE * 2 + kDmaStages * kKT * RAWROW <= kDmaStages * STAGE * 2, "raw rows fit the ring");
+  static_assert(!FQ || (FP8 && !PIPE && R == 64), "FP8MIX queries go with an FP8MIX cache, 64 RoPE dims");
 
   // bf16: kDmaStages tiles.  FP8MIX: the converted tile (the first STAGE) and the raw
   // rows of kDmaStages tiles behind it.  The epilogue reuses all of it.
   __shared__ __attribute__((aligned(16))) uint16_t ring[kDmaStages * STAGE];
-  __shared__ float rscale[FP8 ? kDmaStages : 1][kKT];  // FP8MIX entry scales
+  __shared__ __attribute__((aligned(16))) float rscale[FP8 ? kDmaStages : 1][kKT];  // FP8MIX entry scales
   __shared__ __attribute__((aligned(16))) int idx_s[kDmaIdxCap];
   __shared__ __attribute__((aligned(16))) int kvalid[kDmaStages][kKT];
   __shared__ int64_t wpos_s[kDmaStages][kKT];  // window position of a window row, -1 otherwise
@@ -584,8 +587,30 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     idx_pre[u] = i < n_idx ? a.idx[bt * a.K + s_lo + i] : 0;
   }
   asm volatile("" ::: "memory");  // keep the index loads ahead of the query loads
-  uint4 qraw[NS];
-  {
+  uint4 qraw[FQ ? 1 : NS];
+  // FP8MIX queries (FQ): e4m3 codes as the B operand of the 128-deep fp8 products (lane
+  // (col, grp) holds codes 128 c + 32 grp .. + 32 of head col; the 64 past the D - R
+  // codes are zero), the head's scale, and its bf16 RoPE dims as a bf16 B operand
+  v8i32 q8[FQ ? 4 : 1];
+  uint4 qrraw[FQ ? 2 : 1];
+  float qsc = 0.f;
+  if constexpr (FQ) {
+    const int64_t qh = bt * a.H + hg * a.hpw + wid * 16 + col;
+    const uint8_t* qc = static_cast<const uint8_t*>(a.q) + qh * (D - R);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+      if (128 * c + 32 * grp < D - R) {
+        lo = *reinterpret_cast<const uint4*>(qc + 128 * c + 32 * grp);
+        hi = *reinterpret_cast<const uint4*>(qc + 128 * c + 32 * grp + 16);
+      }
+      q8[c] = v8i32{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                    static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    }
+    qsc = a.q_scale[qh];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) qrraw[s2] = *reinterpret_cast<const uint4*>(a.q_rope + qh * R + 32 * s2 + 8 * grp);
+  } else {
     const uint16_t* qrow =
         static_cast<const uint16_t*>(a.q) + (bt * a.H + hg * a.hpw + wid * 16 + col) * D + 8 * grp;
 #pragma unroll
@@ -763,11 +788,11 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   if (ntiles > 0) issue(0);
   if (ntiles > 1) issue(1);
   if (ntiles > 2) issue(2);
-  bf16x8 qf[NS];
+  bf16x8 qf[FQ ? 2 : NS];  // FQ: the RoPE dims only (k-steps nope / 32 .. NS - 1)
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    uint4 raw = qraw[s];
-    const int d0 = 32 * s + 8 * grp;
+  for (int s = 0; s < (FQ ? 2 : NS); ++s) {
+    uint4 raw = FQ ? qrraw[FQ ? s : 0] : qraw[FQ ? 0 : s];
+    const int d0 = (FQ ? nope : 0) + 32 * s + 8 * grp;
     if (d0 + 8 > nope) {
       float v[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
                     bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
@@ -791,6 +816,52 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // ---- FQ: S^T from the raw rows of stage st: the D - R coded dims by 128-deep fp8
+  // products (codes of key and query, exact products, fp32 sums) times the query and
+  // entry scales, plus the RoPE dims by bf16 products from the converted tile K
+  auto qk8 = [&](int st, const uint16_t* K, f32x4 (&sacc)[2]) {
+    const uint8_t* Rw = reinterpret_cast<const uint8_t*>(ring + STAGE) + st * kKT * RAWROW;
+    // codes 128 c + 32 grp .. + 32 of key row 16 kb + col (zero past the codes, where
+    // the RoPE bf16 values lie)
+    auto load8 = [&](int c, int kb) {
+      uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+      if (128 * c + 32 * grp < D - R) {
+        const uint8_t* p = Rw + (16 * kb + col) * RAWROW + 128 * c + 32 * grp;
+        lo = *reinterpret_cast<const uint4*>(p);
+        hi = *reinterpret_cast<const uint4*>(p + 16);
+      }
+      return v8i32{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                   static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    };
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    v8i32 kf[2];
+    kf[0] = load8(0, 0);
+    // (step c, key block kb) in order, the next one's fragment loading while this one's
+    // product runs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 1 < 8) kf[(i + 1) & 1] = load8((i + 1) >> 1, (i + 1) & 1);
+      // formats 0 / 0: e4m3 on both sides; block scales 127 = 2^0
+      sacc[i & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[i & 1], q8[FQ ? (i >> 1) : 0], sacc[i & 1],
+                                                                     0, 0, 0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // scaled code sums, then the RoPE dims' products accumulate onto them
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float4 es = *reinterpret_cast<const float4*>(&rscale[FP8 ? st : 0][16 * kb + 4 * grp]);
+      sacc[kb][0] *= qsc * es.x;
+      sacc[kb][1] *= qsc * es.y;
+      sacc[kb][2] *= qsc * es.z;
+      sacc[kb][3] *= qsc * es.w;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 kr = *reinterpret_cast<const bf16x8*>(K + (16 * kb + col) * KP + nope + 32 * s2 + 8 * grp);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, qf[s2], sacc[kb], 0, 0, 0);
+      }
+    }
+  };
   // ---- S^T = K Q^T for the 32 keys of a tile (two 16-key blocks)
   auto qk = [&](const uint16_t* K, f32x4 (&sacc)[2]) {
 #pragma unroll
@@ -800,7 +871,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(K + (16 * kb + col) * KP + 8 * grp + 32 * s);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[FQ ? 0 : s], sacc[kb], 0, 0, 0);
       }
     }
   };
@@ -916,7 +987,8 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
 
     const uint16_t* K = FP8 ? ring : ring + st * STAGE;
     f32x4 sacc[2];
-    qk(K, sacc);
+    if constexpr (FQ) qk8(st, K, sacc);
+    else qk(K, sacc);
     const bf16x8 pB = softmax(st, sacc);
     pv(K, pB);
   }
@@ -1623,6 +1695,12 @@ Plan make_plan(int64_t B, int64_t Tq, int H, int D, int64_t max_slots, bool mfma
 }
 
 bool mfma_ok(const AttnLaunch& L) {
+  if (L.q.dtype == CSA_FP8MIX) {
+    // FP8MIX queries: only the LDS-DMA kernel's fp8 products (the entry points reject
+    // every other shape before a launch)
+    return L.kv.dtype == CSA_FP8MIX && L.D == 512 && L.rope_dims == 64 && L.H % 64 == 0 &&
+           (head_group(L.H, kDmaMaxWaves) == 64 || head_group(L.H, kDmaMaxWaves) == 128);
+  }
   if (L.q.dtype != CSA_BF16) return false;
   if (L.kv.dtype != CSA_BF16 && L.kv.dtype != CSA_FP8MIX) return false;
   if (L.win.dtype != L.kv.dtype) return false;
@@ -1680,6 +1758,8 @@ Kern kern_of(const AttnLaunch& L) {
 AttnArgs make_args(const AttnLaunch& L, const Plan& P, void* ws) {
   AttnArgs a{};
   a.q = L.q.data;
+  a.q_rope = static_cast<const uint16_t*>(L.q.rope);
+  a.q_scale = static_cast<const float*>(L.q.scale);
   a.q_pos = L.q_pos;
   a.kv = L.kv.data;
   a.kv_rope = static_cast<const uint16_t*>(L.kv.rope);
@@ -1743,6 +1823,9 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
   const int64_t tokens = L.B * L.Tq;
   if (tokens == 0) return 0;
   const Kern kern = kern_of(L);
+  // FP8MIX queries run only on the LDS-DMA kernel's fp8 products (its alignment and
+  // staged-index limits included)
+  if (L.q.dtype == CSA_FP8MIX && kern != Kern::kDma) return -2;
   const bool dma = mfma_ok(L) && kern != Kern::kReg;
   const Plan P = make_plan(L.B, L.Tq, L.H, L.D, max_slots_of(L), mfma_ok(L), L.sparse != 0, kern);
   const bool mfma = P.mfma;
@@ -1770,6 +1853,9 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
         if (P.hpw == 64) hipLaunchKernelGGL(attn_pair_kernel<8>, g, pb, 0, stream, a);
         else if (P.hpw == 32) hipLaunchKernelGGL(attn_pair_kernel<4>, g, pb, 0, stream, a);
         else hipLaunchKernelGGL(attn_pair_kernel<2>, g, pb, 0, stream, a);
+      } else if (fp8 && L.q.dtype == CSA_FP8MIX) {  // fp8 query products, 4 or 8 waves
+        if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, true, false, true>), g, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_dma_kernel<4, 64, true, false, true>), g, block, 0, stream, a);
       } else if (fp8) {  // 4 or 8 waves (dma_ok)
         if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, true>), g, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_dma_kernel<4, 64, true>), g, block, 0, stream, a);

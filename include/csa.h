@@ -275,6 +275,17 @@ csa_status csa_index_topk(const csa_buf* qI, const float* wI, const csa_buf* kI,
  * Limits: D <= 1024; H <= 256; K + n_win <= 2^20.  The MFMA path needs a BF16 or
  * FP8MIX cache, BF16 q, H % 16 == 0 and D % 32 == 0; other combinations run a
  * slower SIMT kernel.
+ *
+ * FP8MIX queries ([V4-CN] §2.3.4: the attention arithmetic in FP8): q may be an FP8MIX
+ * buffer laid out like a cache row per (token, head) -- e4m3 codes [B, Tq, H, D - R],
+ * bf16 RoPE dims [B, Tq, H, R] (not roped), f32 scale [B, Tq, H] -- as csa_quantize
+ * writes it.  The QK products of the D - R coded dims then run on fp8 MFMA over the
+ * codes of query and key (exact products, fp32 sums, times both scales); the RoPE
+ * dims and the probability-weighted sum of values stay bf16.  The result is the
+ * attention of the dequantized query.  Needs an FP8MIX cache, D = 512, R = 64,
+ * H in {64, 128, 256} and a BF16 out; anything else returns CSA_ERR_UNSUPPORTED (or
+ * CSA_ERR_DTYPE for another out dtype) and launches nothing.  csa_forward and
+ * csa_decode_step take FP8MIX queries the same way (without CSA_FLAG_QKV_NORM).
  */
 size_t csa_sparse_mqa_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t D, int32_t K,
                                      int32_t n_win);
@@ -366,7 +377,7 @@ typedef struct csa_forward_io {
   const void *iprev_cb, *iprev_zb;
   csa_buf kv_cache;                      /* [B, cache_rows, D]  in/out */
   csa_buf ik_cache;                      /* [B, cache_rows, DI] in/out (CSA) */
-  csa_buf q;                             /* [B, Tq, H, D] */
+  csa_buf q;                             /* [B, Tq, H, D]: F32, BF16 or FP8MIX (see csa_sparse_mqa) */
   const int64_t* q_pos;                  /* [B, Tq] */
   csa_buf qI;                            /* [B, Tq, HI, DI] (CSA) */
   const float* wI;                       /* [B, Tq, HI] (CSA) */
@@ -471,7 +482,7 @@ typedef struct csa_decode_io {
   csa_buf kv_pages;                      /* paged caches, in/out */
   csa_buf ik_pages;
   const int32_t* block_table;
-  csa_buf q;                             /* [B, H, D] */
+  csa_buf q;                             /* [B, H, D]: F32, BF16 or FP8MIX (see csa_sparse_mqa) */
   csa_buf qI;                            /* [B, HI, DI] (CSA) */
   const float* wI;                       /* [B, HI] (CSA) */
   const float* sink;                     /* [H] */

@@ -232,6 +232,33 @@ def test_attention_rejects_bad_arguments(L):
                             1, 16, 128, 10, 8, C.byref(out), None, 0, None) == 1
 
 
+def test_fp8_queries_are_fenced(L):
+    # FP8MIX queries run only on the fp8-product attention kernel: an FP8MIX cache,
+    # D = 512 with 64 RoPE dims, 64 / 128 / 256 heads, a BF16 output (every other
+    # combination is rejected before any launch)
+    p = 0x100000
+    def fp8buf():
+        b = _buf(2)
+        b.rope, b.scale = p, p
+        return b
+    q8, kv8, win8 = fp8buf(), fp8buf(), fp8buf()
+    def call(q=q8, kv=kv8, win=win8, out=None, H=128, D=512, R=64):
+        out = out if out is not None else _buf(1)
+        return L.csa_sparse_mqa(C.byref(q), p, C.byref(kv), 10, p, 4, C.byref(win), p, 16, p, 1.0, R, 10000.0, 0, 1,
+                                1, H, D, 10, 8, C.byref(out), None, 0, None)
+    assert call(kv=_buf(1), win=_buf(1)) == 6   # bf16 cache
+    assert call(D=256) == 6
+    assert call(R=32) == 6
+    assert call(H=96) == 6
+    assert call(out=_buf(0)) == 3              # F32 output
+    q_norope = fp8buf()
+    q_norope.rope = None
+    assert call(q=q_norope) == 1
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == 5                      # valid: fails only for want of a GPU
+
+
 def test_forward_rejects_bad_descriptor(L):
     from compressed_sparse_attention_07_amd._lib import csa_forward_io, csa_layer_desc
     d = csa_layer_desc()

@@ -82,13 +82,15 @@ def check_quantized(got, want, fmt, R, what):
 
 class Harness:
     def __init__(self, mode, lengths, *, D, DI, H, HI, ratio, n_win, page_tokens, topk, R, dtype, seed, norm=False,
-                 rollover=(), steps=4, flags=0, quantized=False):
-        """quantized: FP8MIX KV cache and window, MXFP4 indexer keys and queries (bf16 streams)."""
+                 rollover=(), steps=4, flags=0, quantized=False, fp8_query=False):
+        """quantized: FP8MIX KV cache and window, MXFP4 indexer keys and queries (bf16 streams);
+        fp8_query: the attention queries FP8MIX too."""
         self.csa_mode = mode == csa.CSA_MODE_CSA
         self.g = g = Gen(seed, DEV)
         self.cd, self.td = _dt(dtype)
         self.dtype = dtype
         self.quantized = quantized
+        self.fp8_query = fp8_query
         self.kvd = csa.CSA_FP8MIX if quantized else self.cd
         self.ikd = csa.CSA_MXFP4 if quantized else self.cd
         self.B = B = len(lengths)
@@ -180,6 +182,9 @@ class Harness:
         x = dict(streams=[g.normal((B, D), dtype=self.td) for _ in range(ns)],
                  istreams=[g.normal((B, DI), dtype=self.td) for _ in range(4)] if self.csa_mode else None,
                  q=g.normal((B, self.H, D), qstd(D), dtype=self.td))
+        x["q_h"] = f64(x["q"])
+        if self.fp8_query:
+            x["q8"], x["q_h"] = self._quantized(x["q"].float(), csa.CSA_FP8MIX)
         if self.quantized:
             x["kv_raw"], x["kv_raw_h"] = self._quantized(g.normal((B, D)), self.kvd)
         else:
@@ -205,7 +210,7 @@ class Harness:
         sl = slice(None) if rows is None else rows
         st = [t[sl].contiguous() for t in x["streams"]]
         io = dict(pool.io(), slot=self.slot[sl].contiguous(), kv_raw=self._rows(x["kv_raw"], sl),
-                  q=x["q"][sl].contiguous(), sink=self.sink, out=torch.empty_like(x["q"][sl]), bias_a=self.bias[0],
+                  q=self._rows(x["q8"], sl) if self.fp8_query else x["q"][sl].contiguous(), sink=self.sink, out=torch.empty_like(x["q"][sl]), bias_a=self.bias[0],
                   q_norm=self.q_norm, kv_norm=self.kv_norm)
         if self.csa_mode:
             ist = [t[sl].contiguous() for t in x["istreams"]]
@@ -372,7 +377,7 @@ class Harness:
         assert ok, f"top-k of sequence {b} differs beyond the near-tie band"
         kv = self.gather(self.pool.kv_pages, s, ents, self.D)
         win, w0 = self._window(s, p)
-        want = O.mqa(f64(x["q"][b])[None], np.array([p]), kv, np.arange(cnt)[None], win, w0, self.W, f64(self.sink),
+        want = O.mqa(x["q_h"][b][None], np.array([p]), kv, np.arange(cnt)[None], win, w0, self.W, f64(self.sink),
                      scale=self.scale, rope_dims=self.R, rope_base=BASE, **self._norms())[0]
         assert_close(f64(io["out"][b]), O.store(want, kind), "fp8" if self.quantized else kind,
                      f"output of sequence {b}")
@@ -381,9 +386,10 @@ class Harness:
         vis = p // self.m
         kv = self.gather(self.pool.kv_pages, s, range(vis), self.D)
         win, w0 = self._window(s, p)
-        want = O.hca_dense(f64(x["q"][b])[None], np.array([p]), kv, win, w0, self.W, f64(self.sink), ratio=self.m,
+        want = O.hca_dense(x["q_h"][b][None], np.array([p]), kv, win, w0, self.W, f64(self.sink), ratio=self.m,
                            scale=self.scale, rope_dims=self.R, rope_base=BASE, **self._norms())[0]
-        assert_close(f64(io["out"][b]), O.store(want, kind), kind, f"output of sequence {b}")
+        assert_close(f64(io["out"][b]), O.store(want, kind), "fp8" if self.quantized else kind,
+                     f"output of sequence {b}")
 
 
 def _run(h, steps, invariance_step=0):
@@ -427,12 +433,12 @@ def test_decode_state_bf16_fused_selection_norms():
 
 
 def test_decode_state_fp8_kv_mxfp4_indexer():
-    # the mixed-precision decode layer ([V4-CN] §2.3.4, §3.4): FP8MIX KV pages and
-    # window, MXFP4 indexer keys and queries; parity on dequantized inputs
+    # the mixed-precision decode layer ([V4-CN] §2.3.4, §3.4): FP8MIX KV pages, window
+    # and attention queries, MXFP4 indexer keys and queries; parity on dequantized inputs
     say("decode state: CSA with FP8MIX KV and MXFP4 indexer")
     lengths = [4095, 6000, 8191, 2050, 513, 10001, 3, 7]
     h = Harness(csa.CSA_MODE_CSA, lengths, D=512, DI=128, H=64, HI=64, ratio=4, n_win=128, page_tokens=2048,
-                topk=256, R=64, dtype="bf16", seed=616, rollover=(1, 5), quantized=True)
+                topk=256, R=64, dtype="bf16", seed=616, rollover=(1, 5), quantized=True, fp8_query=True)
     assert _run(h, 4, invariance_step=2) >= 8
 
 
@@ -455,9 +461,10 @@ def test_decode_state_hca_norms():
 
 
 def test_decode_state_hca_fp8_kv():
-    # HCA with an FP8MIX cache and window: completed blocks quantized in the append step
+    # HCA with an FP8MIX cache, window and queries: completed blocks quantized in the
+    # append step
     say("decode state: HCA with FP8MIX KV")
     lengths = [127, 255, 4095, 9000]
     h = Harness(csa.CSA_MODE_HCA, lengths, D=512, DI=128, H=64, HI=64, ratio=128, n_win=128, page_tokens=4096,
-                topk=1, R=64, dtype="bf16", seed=617, rollover=(2,), quantized=True)
+                topk=1, R=64, dtype="bf16", seed=617, rollover=(2,), quantized=True, fp8_query=True)
     assert _run(h, 2, invariance_step=1) >= 3

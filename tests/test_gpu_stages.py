@@ -424,6 +424,59 @@ def test_sparse_mqa_sink_limits():
             assert torch.all(out[0, :, 1::2] == 0)
 
 
+FP8Q_CASES = [
+    # B, Tq, H, N, K (0: dense HCA, ratio 128), positions
+    (2, 2, 64, 300, 128, [1300, 5000]),               # decode: split key ranges, 4 waves
+    (1, 3, 128, 700, 256, [2900, 3100, 4000]),         # decode, 8 waves
+    (1, 260, 128, 400, 64, list(range(1600, 1860))),   # prefill-shaped: one range per query
+    (1, 2, 256, 300, 96, [1300, 5000]),                # two 128-head groups
+    (2, 2, 128, 300, 0, [20000, 38400]),               # dense HCA
+]
+
+
+@pytest.mark.parametrize("case", FP8Q_CASES, ids=lambda c: "-".join(str(x) for x in c[:5]))
+def test_attention_fp8_query(case):
+    # FP8MIX queries ([V4-CN] §2.3.4: FP8 attention arithmetic): the query's leading
+    # D - R dims as e4m3 codes with a scale per (token, head), the QK products of the
+    # codes on fp8 MFMA; parity against the oracle on the dequantized query and cache
+    B, Tq, H, N, K, positions = case
+    D, R, n_win = 512, 64, 128
+    say(f"attention with FP8MIX queries {case[:5]}")
+    g = Gen(4100 + H + N + K, DEV)
+    q, pos, kv, kv_o, idx, win, win_o, win_pos0, sink = _attn_inputs(g, B, Tq, H, D, N, K, n_win, "bf16", "fp8mix",
+                                                                       R, positions)
+    q32 = q.float()
+    q8 = csa.Buf.empty((B, Tq, H, D), csa.CSA_FP8MIX, rope_dims=R)
+    csa.csa_quantize(q32.reshape(-1, D).contiguous(),
+                     csa.Buf(q8.dtype, q8.data.view(-1, D - R), q8.rope.view(-1, R), q8.scale.view(-1)), rope_dims=R)
+    q_o = Q.fp8mix_dequantize(*Q.fp8mix_quantize(q32.cpu().numpy(), R))
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    if K:
+        csa.csa_sparse_mqa(q8, pos, kv, idx, win, win_pos0, sink, out, N=N, n_win=n_win, softmax_scale=1.0,
+                           rope_dims=R, rope_base=RB)
+    else:
+        csa.hca_dense_attn(q8, pos, kv, win, win_pos0, sink, out, N=N, ratio=128, n_win=n_win, softmax_scale=1.0,
+                           rope_dims=R, rope_base=RB)
+    torch.cuda.synchronize()
+    def oracle(qq, b):
+        if K:
+            return O.mqa(qq, pos[b].cpu().numpy(), kv_o[b], idx[b].cpu().numpy(), win_o[b], int(win_pos0[b]), n_win,
+                         f64(sink), scale=1.0, rope_dims=R, rope_base=RB)
+        return O.hca_dense(qq, pos[b].cpu().numpy(), kv_o[b], win_o[b], int(win_pos0[b]), n_win, f64(sink),
+                           ratio=128, scale=1.0, rope_dims=R, rope_base=RB)
+
+    for b in range(B):
+        got = f64(out[b])
+        want = oracle(q_o[b], b)
+        # the codes, scales and keys are exact on both sides: what remains is the
+        # kernel's bf16 rounding of the probabilities and value tile
+        assert_close(got, want, "bf16", f"fp8-query attention b={b}")
+        # and the result follows the quantized query, not the bf16 one it came from
+        e_q = np.sqrt(np.mean((got - want) ** 2))
+        e_b = np.sqrt(np.mean((got - oracle(f64(q[b]), b)) ** 2))
+        assert e_q < 0.5 * e_b, (e_q, e_b)
+
+
 HCA_CASES = [
     # B, Tq, H, D, N, ratio, n_win, qdt, kvf, positions
     (2, 4, 16, 128, 40, 8, 16, "bf16", "bf16", [0, 100, 255, 400]),

@@ -943,6 +943,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time spent on the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="time only --config (not the other workloads)")
+    ap.add_argument("--no-edges", action="store_true",
+                    help="skip the layer-edge, FP8-query and decode-state legs (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain 1 GiB device copy (PMC calibration)")
     ap.add_argument("--summarize-trace", metavar="DB", help="write a kernel-trace summary (no GPU work)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -988,9 +990,11 @@ def main():
     reps = args.stage_reps if args.stage_reps is not None else (20 if decode else 4)
 
     wl, value, ms_per_step, stage_out, roofline = run_workload(args.config, steps, warmup, layers, reps)
-    edges = layer_edges(wl, steps, reps)
-    fq = fp8_query_edge(wl, reps)
-    dstate = decode_state_bench(wl, steps, warmup)
+    edges = fq = dstate = None
+    if not args.no_edges:
+        edges = layer_edges(wl, steps, reps)
+        fq = fp8_query_edge(wl, reps)
+        dstate = decode_state_bench(wl, steps, warmup)
 
     if args.copy_probe:
         # a plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB): the

@@ -520,7 +520,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 // MFMA loop reads exactly as in the bf16 case.
 
 constexpr int kDmaStages = 4;
-constexpr bool kDmaPipe = true;  // prefill launches take the software-pipelined loop
+constexpr bool kDmaPipe = true;  // long key ranges take the software-pipelined loop
+constexpr int kPipeMinSlots = 8 * 32;  // ... ranges of at least 8 tiles, or unsplit ones
 constexpr int kDmaIdxCap = 2048;  // entry indices of one workgroup's slot range, staged in LDS
 
 template <int NW, int R, bool FP8, bool PIPE = false, bool FQ = false>
@@ -1860,7 +1861,7 @@ int launch_attn(const AttnLaunch& L, void* ws, size_t ws_bytes, hipStream_t stre
         if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, true>), g, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_dma_kernel<4, 64, true>), g, block, 0, stream, a);
       } else {
-        if (kDmaPipe && P.nsplit == 1) {  // long key ranges: the software-pipelined loop
+        if (kDmaPipe && (P.nsplit == 1 || P.sps >= kPipeMinSlots)) {  // long ranges: the pipelined loop
           if (nw == 8) hipLaunchKernelGGL((attn_dma_kernel<8, 64, false, true>), g, block, 0, stream, a);
           else if (nw == 4) hipLaunchKernelGGL((attn_dma_kernel<4, 64, false, true>), g, block, 0, stream, a);
           else hipLaunchKernelGGL((attn_dma_kernel<2, 64, false, true>), g, block, 0, stream, a);

@@ -485,6 +485,8 @@ HCA_CASES = [
     (2, 2, 64, 512, 100, 128, 128, "bf16", "fp8mix", [12800, 9000]),
     # 2-wave groups; the first query sees no compressed entry
     (1, 3, 32, 512, 80, 128, 128, "bf16", "bf16", [64, 5000, 10239]),
+    # decode over thousands of entries: split key ranges of 17 tiles on the pipelined loop
+    (1, 2, 128, 512, 4000, 128, 128, "bf16", "bf16", [512000, 512100]),
 ]
 
 

@@ -477,6 +477,32 @@ def test_attention_fp8_query(case):
         assert e_q < 0.5 * e_b, (e_q, e_b)
 
 
+def test_attention_fp8_query_zero_heads():
+    # all-zero query heads quantize to scale 1 and zero codes: their logits are the RoPE
+    # dims' alone (zero too), so each such head attends uniformly (with the sink); other
+    # heads keep their values.  Against the oracle on the dequantized query.
+    say("attention with FP8MIX queries: zero heads")
+    B, Tq, H, N, K, D, R, n_win = 1, 2, 64, 300, 128, 512, 64, 128
+    g = Gen(4321, DEV)
+    q, pos, kv, kv_o, idx, win, win_o, win_pos0, sink = _attn_inputs(g, B, Tq, H, D, N, K, n_win, "bf16", "fp8mix",
+                                                                       R, [1300, 5000])
+    q[:, :, ::3] = 0
+    q32 = q.float()
+    q8 = csa.Buf.empty((B, Tq, H, D), csa.CSA_FP8MIX, rope_dims=R)
+    csa.csa_quantize(q32.reshape(-1, D).contiguous(),
+                     csa.Buf(q8.dtype, q8.data.view(-1, D - R), q8.rope.view(-1, R), q8.scale.view(-1)), rope_dims=R)
+    torch.cuda.synchronize()
+    assert torch.all(q8.scale[:, :, ::3] == 1.0) and torch.all(q8.data[:, :, ::3] == 0)
+    q_o = Q.fp8mix_dequantize(*Q.fp8mix_quantize(q32.cpu().numpy(), R))
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    csa.csa_sparse_mqa(q8, pos, kv, idx, win, win_pos0, sink, out, N=N, n_win=n_win, softmax_scale=1.0, rope_dims=R,
+                       rope_base=RB)
+    torch.cuda.synchronize()
+    want = O.mqa(q_o[0], pos[0].cpu().numpy(), kv_o[0], idx[0].cpu().numpy(), win_o[0], int(win_pos0[0]), n_win,
+                 f64(sink), scale=1.0, rope_dims=R, rope_base=RB)
+    assert_close(f64(out[0]), want, "bf16", "fp8-query attention with zero heads")
+
+
 HCA_CASES = [
     # B, Tq, H, D, N, ratio, n_win, qdt, kvf, positions
     (2, 4, 16, 128, 40, 8, 16, "bf16", "bf16", [0, 100, 255, 400]),

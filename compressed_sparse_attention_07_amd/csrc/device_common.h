@@ -159,6 +159,24 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 
 // inclusive prefix sum over the 64 lanes
+// x combined over the four rows of the wave that share its column (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): gfx950's row-swap moves (v_permlane16_swap / v_permlane32_swap) in
+// place of two LDS-routed shuffles.  With both operands set to x, the swap leaves x's
+// partner row in one output and x in the other in every lane, so each lane combines the
+// same pair; both steps are commutative, so every lane ends with the same value.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
   v += dpp_u32<kRowShr1, true>(0u, v);
   v += dpp_u32<kRowShr2, true>(0u, v);

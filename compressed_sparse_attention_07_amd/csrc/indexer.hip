@@ -222,8 +222,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
           for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
         }
         // sum the four row groups (heads) holding the same entry
-        sc += __shfl_xor(sc, 16, WAVE);
-        sc += __shfl_xor(sc, 32, WAVE);
+        sc = rows4_sum(sc);
         part[tI] = sc;
       }
 #pragma unroll
@@ -402,8 +401,7 @@ __global__ __launch_bounds__(NWV * WAVE) void index_stream_kernel(IndexLaunch a,
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
       }
-      sc += __shfl_xor(sc, 16, WAVE);
-      sc += __shfl_xor(sc, 32, WAVE);
+      sc = rows4_sum(sc);
       // tiles are stored in runs of four: lane (col, grp) holds entry 16 grp + col of the run
       const int tile = t * TPS + tI;
       const int g = tile & 3;
@@ -594,8 +592,7 @@ __global__ __launch_bounds__(kPfWaves * WAVE) void index_prefill_kernel(IndexLau
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc = fmaf(w[u][hb][r], fmaxf(acc[r], 0.f), sc);
           }
-          sc += __shfl_xor(sc, 16, WAVE);
-          sc += __shfl_xor(sc, 32, WAVE);
+          sc = rows4_sum(sc);
           part[u][tI] = sc;
         }
       }
@@ -716,8 +713,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
         }
-        sc += __shfl_xor(sc, 16, WAVE);
-        sc += __shfl_xor(sc, 32, WAVE);
+        sc = rows4_sum(sc);
         part[tI] = sc;
       }
 #pragma unroll

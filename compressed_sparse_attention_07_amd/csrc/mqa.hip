@@ -399,8 +399,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         mt = fmaxf(mt, v);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    mt = rows4_max(mt);
     // Lazy rescaling: the exponentials use a reference max m_run that is raised only
     // when a logit exceeds it by more than kSlack (so p <= e^kSlack); O and l always
     // refer to the same m_run, so the result is exact whatever the reference.
@@ -458,8 +457,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 
   // sum of exponentials for head h: the four row groups hold disjoint keys
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, WAVE);
-  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  l_tot = rows4_sum(l_tot);
 
   const int64_t th = bt * a.H + h;
   if (a.nsplit > 1) {
@@ -891,8 +889,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
         mt = fmaxf(mt, v);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    mt = rows4_max(mt);
     constexpr float kSlack = 8.f;  // lazy rescale, as in attn_mfma_kernel
     const bool raise = mt > m_run + kSlack;
     const float m_ref = raise ? mt : m_run;
@@ -996,8 +993,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   }
 
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, WAVE);
-  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  l_tot = rows4_sum(l_tot);
 
   // The result rows (normalised partials, or the final output) leave through LDS: each
   // lane holds 4 dims of one head, so direct stores would write 32-byte pieces of 16
@@ -1291,8 +1287,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
         mt = fmaxf(mt, v);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    mt = rows4_max(mt);
     constexpr float kSlack = 8.f;  // lazy rescale, as in attn_mfma_kernel
     const bool raise = mt > m_run + kSlack;
     const float m_ref = raise ? mt : m_run;
@@ -1338,8 +1333,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
   }
 
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, WAVE);
-  l_tot += __shfl_xor(l_tot, 32, WAVE);
+  l_tot = rows4_sum(l_tot);
 
   const int64_t th = bt * a.H + h;
   const bool part = a.nsplit > 1;

@@ -152,7 +152,7 @@ def _check_queries(wl, io, units):
             qI = deq(io["qI"], b)
         for t in ts:
             say(f"  unit b={b} t={t} pos={pos[t]}")
-            q = f64(io["q"][b, t:t + 1])
+            q = deq(io["q"], b)[t:t + 1]
             p = pos[t:t + 1]
             if hca:
                 want = O.hca_dense(q, p, kv, win, wp0, W, sink, ratio=m, scale=cfg.softmax_scale, rope_dims=R,
@@ -217,3 +217,15 @@ def test_mixed_precision_decode_1m_b8():
     wl = bench.build_workload("4", layers=1)
     io = _run_step(wl)
     _check_queries(wl, io, [(0, 0), (3, 0), (7, 0)])
+    # the same step with FP8MIX queries: the QK products of the codes on fp8 MFMA
+    say("  ... with FP8MIX queries")
+    q = io["q"]
+    D, R = q.shape[-1], wl.meta["R"]
+    q8 = csa.Buf.empty(tuple(q.shape), csa.CSA_FP8MIX, rope_dims=R)
+    csa.csa_quantize(q.float().reshape(-1, D).contiguous(),
+                     csa.Buf(q8.dtype, q8.data.view(-1, D - R), q8.rope.view(-1, R), q8.scale.view(-1)), rope_dims=R)
+    io8 = dict(io, q=q8, out=torch.empty_like(io["out"]))
+    desc = wl.desc_full if wl.desc_full is not None else wl.desc_attend
+    csa.csa_forward(desc, io8, ws=wl.ws)
+    torch.cuda.synchronize()
+    _check_queries(wl, io8, [(1, 0), (6, 0)])

@@ -158,7 +158,6 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
 }
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 
-// inclusive prefix sum over the 64 lanes
 // x combined over the four rows of the wave that share its column (lanes l, l ^ 16,
 // l ^ 32, l ^ 48): gfx950's row-swap moves (v_permlane16_swap / v_permlane32_swap) in
 // place of two LDS-routed shuffles.  With both operands set to x, the swap leaves x's
@@ -177,6 +176,7 @@ __device__ __forceinline__ float rows4_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
   v += dpp_u32<kRowShr1, true>(0u, v);
   v += dpp_u32<kRowShr2, true>(0u, v);

@@ -321,6 +321,64 @@ def test_topk_prethresholded(k):
     assert not bad, f"rows differ: {bad[:10]}"
 
 
+def _topk_properties(s, idx, cnt, k, what):
+    """The definition checked on every row at once: the count is min(k, #finite), the
+    indices ascend (then -1), every selected score is finite and at least every
+    unselected finite score, and at the threshold value the selected entries come
+    before the unselected ones (ties go to the lower index)."""
+    fin = np.isfinite(s)
+    assert np.array_equal(cnt, np.minimum(fin.sum(1), k)), what
+    valid = np.arange(k)[None, :] < cnt[:, None]
+    assert np.all(idx[~valid] == -1), what
+    big = np.iinfo(np.int64).max
+    ii = np.where(valid, idx, big).astype(np.int64)
+    assert np.all((np.diff(ii, axis=1) > 0) | ~valid[:, 1:]), what
+    sel = np.where(valid, idx, 0).astype(np.int64)
+    vals = np.take_along_axis(s, sel, 1)
+    assert np.all(np.isfinite(vals) | ~valid), what
+    minsel = np.where(valid, vals, np.inf).min(1)
+    chosen = np.zeros(s.shape, dtype=bool)
+    rr = np.broadcast_to(np.arange(s.shape[0])[:, None], sel.shape)
+    chosen[rr[valid], sel[valid]] = True
+    unsel = fin & ~chosen
+    assert np.all(np.where(unsel, s, -np.inf).max(1) <= minsel), what
+    pos = np.arange(s.shape[1])[None, :]
+    last_eq = np.where(chosen & (s == minsel[:, None]), pos, -1).max(1)
+    first_un = np.where(unsel & (s == minsel[:, None]), pos, big).min(1)
+    assert np.all(first_un > last_eq), what
+
+
+@pytest.mark.parametrize("rows,N,k", [(1024, 65536 + 5, 1024), (512, 131072, 1024)])
+def test_topk_many_slices(rows, N, k):
+    """Launches of thousands of first-level slices, as the prefill rows give: a plain
+    two-level selection (with a ragged last slice per row) and the pre-thresholded one.
+    Special rows as above; every row is checked against the definition, a sample of
+    rows (and every special row) against the oracle."""
+    say(f"topk many slices rows={rows} N={N} k={k}")
+    g = Gen(6060 + rows, DEV)
+    s = g.normal((rows, N))
+    s[1] = torch.round(s[1] * 2) / 2
+    s[2, 1000:] = -float("inf")
+    s[3] = 1.0
+    s[4, ::5] = float("nan")
+    s[4, 1::7] = -0.0
+    s[4, 2::7] = 0.0
+    s[5] = -float("inf")
+    s[6, N - 3:] = 50.0                               # the largest in the last slice
+    idx = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((rows,), dtype=torch.int32, device=DEV)
+    csa.csa_topk(s, k, idx, cnt)
+    torch.cuda.synchronize()
+    sc = s.cpu().numpy().astype(np.float64)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    _topk_properties(sc, gi, gc, k, f"rows={rows} N={N}")
+    pick = np.unique(np.concatenate([np.arange(8), np.random.default_rng(rows).choice(rows, 40, replace=False),
+                                     [rows - 1]]))
+    wi, wc = O.topk(sc[pick], k)
+    bad = [int(r) for j, r in enumerate(pick) if gc[r] != wc[j] or not np.array_equal(gi[r], wi[j])]
+    assert not bad, f"rows differ: {bad[:10]}"
+
+
 # ------------------------------------------------------------------ attention
 
 

@@ -234,6 +234,15 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
              min(static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 47)), static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63))));
 }
 
+// ---- loads of data read once (a stream no other workgroup of the launch reads again):
+// the nontemporal hint keeps them from displacing data that is reused
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 // ---- direct global -> LDS loads
 //
 // One 16-byte-per-lane load to LDS (global_load_lds_dwordx4): lane i's 16 bytes land at
@@ -242,6 +251,16 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_byte) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(lds_byte)
+               : "memory");
+}
+
+// The same with the nontemporal hint, for rows that no other workgroup of the launch
+// reads again (a key stream scored once).
+__device__ __forceinline__ void lds_dma16_nt(const void* g, uint32_t lds_byte) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
                : "=&s"(saved)
                : "v"(g), "s"(lds_byte)
                : "memory");

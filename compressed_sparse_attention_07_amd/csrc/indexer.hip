@@ -347,7 +347,7 @@ __global__ __launch_bounds__(NWV * WAVE) void index_stream_kernel(IndexLaunch a,
       const int lc = ((off % RB) / 16) ^ (kk & (CPR - 1));  // logical chunk stored at this slot
       int64_t s = s_begin + static_cast<int64_t>(u) * KPS + kk;
       if (s >= vis_end) s = vis_end - 1;      // in bounds; masked when stored
-      lds_dma16(kbase + s * RB + lc * 16, ring_b + st * STAGE_B + i * 1024);
+      lds_dma16_nt(kbase + s * RB + lc * 16, ring_b + st * STAGE_B + i * 1024);
     }
   };
 #pragma unroll
@@ -686,8 +686,8 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
       if (s >= vis_end) s = vis_end - 1;  // clamp: in bounds, masked below
 #pragma unroll
       for (int ks = 0; ks < KS4; ++ks) {
-        kb[tI][ks] = *reinterpret_cast<const uint4*>(kc + s * (DI / 2) + ks * 64 + grp * 16);
-        ks4[tI][ks] = *reinterpret_cast<const uint32_t*>(ksp + s * (DI / 32) + ks * 4);
+        kb[tI][ks] = load_stream16(kc + s * (DI / 2) + ks * 64 + grp * 16);
+        ks4[tI][ks] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ksp + s * (DI / 32) + ks * 4));
       }
     }
   };

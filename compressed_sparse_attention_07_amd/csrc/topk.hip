@@ -89,7 +89,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   }
   __shared__ Shared<NT> sh;
   float v[PER];
-  load_slice<NT, PER, PAIRS>(a, blockIdx.x, v);
+  load_slice<NT, PER, PAIRS, FINAL>(a, blockIdx.x, v);
   select_slice<NT, PER, PAIRS, FINAL>(a, sh, blockIdx.x, v);
 }
 

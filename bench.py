@@ -109,7 +109,6 @@ class Stage:
     bytes: float                # algorithmic bytes per launch
     flops: float                # algorithmic FLOP per launch
     kernel: str                 # the kernels one launch of the stage runs, joined by "+"
-    src: tuple                  # its source files
     peak_flops: float = MFMA_BF16_PEAK
 
 
@@ -372,7 +371,7 @@ def _add_stages(wl: Workload, csa, torch, dev):
         cb = B * (nst * T * D * 2 + (T // m) * kv_entry)
         if not hca:
             cb += B * (4 * T * DI * 2 + (T // m) * ik_entry)
-        wl.stages["compress"] = Stage(st_compress, cb, 0.0, "compress_kernel", ("compress.hip",))
+        wl.stages["compress"] = Stage(st_compress, cb, 0.0, "compress_kernel")
 
     if not hca:
         scores = torch.empty((B, Tq, N), dtype=torch.float32, device=dev)
@@ -390,9 +389,8 @@ def _add_stages(wl: Workload, csa, torch, dev):
             st_index, B * N * ik_entry + B * Tq * (HI * q_entry + HI * 4 + N * 4), 2.0 * HI * DI * sum_vis,
             "index_mxfp4_kernel" if mx else ("index_prefill_kernel" if Tq >= 16 else
                                              ("index_stream_kernel" if DI <= 128 else "index_mfma_kernel")),
-            ("indexer.hip",),
             MFMA_FP4_PEAK if mx else MFMA_BF16_PEAK)
-        wl.stages["topk"] = Stage(st_topk, B * Tq * (N * 4 + k * 4), 0.0, "topk_kernel", ("topk.hip",))
+        wl.stages["topk"] = Stage(st_topk, B * Tq * (N * 4 + k * 4), 0.0, "topk_kernel")
         mqa_ws = torch.empty(max(1, csa.lib().csa_sparse_mqa_workspace_size(B, Tq, H, D, k, W)), dtype=torch.uint8,
                              device=dev)
         outs = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=dev)
@@ -406,8 +404,8 @@ def _add_stages(wl: Workload, csa, torch, dev):
         # algorithmic bytes: every distinct entry once (a prefill chunk's selections overlap), q, out, indices
         uniq = min(sum(keys), B * (N + M["Tw"]))
         wl.stages["sparse_mqa"] = Stage(st_attn, uniq * kv_entry + B * Tq * (4 * H * D + 4 * k),
-                                        4.0 * H * D * sum(keys), _attn_kernels(mqa_ws, M, True), ("mqa.hip",))
-        wl.stages["_prime"] = Stage(lambda i: (st_index(i), st_topk(i)), 0, 0, "", ())
+                                        4.0 * H * D * sum(keys), _attn_kernels(mqa_ws, M, True))
+        wl.stages["_prime"] = Stage(lambda i: (st_index(i), st_topk(i)), 0, 0, "")
     else:
         mqa_ws = torch.empty(max(1, csa.lib().hca_dense_attn_workspace_size(B, Tq, H, D, N, W)), dtype=torch.uint8,
                              device=dev)
@@ -421,7 +419,7 @@ def _add_stages(wl: Workload, csa, torch, dev):
         keys = [v + min(W, int(p) + 1) for row, prow in zip(vis, pos.tolist()) for v, p in zip(row, prow)]
         uniq = B * (N + M["Tw"]) if Tq > 1 else sum(keys)
         wl.stages["dense_attn"] = Stage(st_attn, uniq * kv_entry + B * Tq * 4 * H * D, 4.0 * H * D * sum(keys),
-                                        _attn_kernels(mqa_ws, M, False), ("mqa.hip",))
+                                        _attn_kernels(mqa_ws, M, False))
 
 
 def _prepare_stages(wl: Workload, csa):
@@ -587,14 +585,23 @@ def summarize_counters(csv_path: str, kernel: str, src: str, out: str, command: 
     print("\n".join(lines))
 
 
-KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",), "attn_mfma_kernel": ("mqa.hip",), "attn_pair_kernel": ("mqa.hip",),
-                  "attn_combine_kernel": ("mqa.hip",), "index_mfma_kernel": ("indexer.hip",),
-                  "index_stream_kernel": ("indexer.hip",),
-                  "index_mxfp4_kernel": ("indexer.hip",), "index_prefill_kernel": ("indexer.hip",),
-                  "topk_kernel": ("topk.hip",),
-                  "compress_kernel": ("compress.hip",), "state_append_kernel": ("compress.hip",),
-                  "gemm_few_kernel": ("proj.hip",), "gemm_tiled_kernel": ("proj.hip",),
-                  "gemm_reduce_kernel": ("proj.hip",)}
+# the sources a kernel's code comes from: its own file and the headers it includes
+_HDR = ("device_common.h", "launch.h", "rmsnorm.h")
+_HDR_SEL = _HDR + ("topk_select.h",)
+KERNEL_SOURCES = {"attn_dma_kernel": ("mqa.hip",) + _HDR, "attn_mfma_kernel": ("mqa.hip",) + _HDR,
+                  "attn_pair_kernel": ("mqa.hip",) + _HDR, "attn_combine_kernel": ("mqa.hip",) + _HDR,
+                  "index_mfma_kernel": ("indexer.hip",) + _HDR_SEL, "index_stream_kernel": ("indexer.hip",) + _HDR_SEL,
+                  "index_mxfp4_kernel": ("indexer.hip",) + _HDR_SEL, "index_prefill_kernel": ("indexer.hip",) + _HDR_SEL,
+                  "topk_kernel": ("topk.hip",) + _HDR_SEL,
+                  "compress_kernel": ("compress.hip",) + _HDR, "state_append_kernel": ("compress.hip",) + _HDR,
+                  "gemm_few_kernel": ("proj.hip",) + _HDR, "gemm_tiled_kernel": ("proj.hip",) + _HDR,
+                  "gemm_reduce_kernel": ("proj.hip",) + _HDR}
+
+
+def kernel_src_hash(kernels: str) -> str:
+    """Hash of the sources of the kernels named (joined by "+"): a committed profile
+    counts only while it matches."""
+    return src_hash(*sorted({f for kn in kernels.split("+") for f in KERNEL_SOURCES[kn]}))
 
 
 # ============================================================================ runs
@@ -645,12 +652,12 @@ def run_workload(key: str, steps: int, warmup: int, layers: int, reps: int):
     else:
         achieved, peak, unit = dom.flops / times[dom_name] / 1e12, dom.peak_flops / 1e12, "TFLOP/s"
     kern = dom.kernel
-    traffic = read_traffic(f"{kern}_{wl.name}_pmc.txt", src_hash(*dom.src))
+    traffic = read_traffic(f"{kern}_{wl.name}_pmc.txt", kernel_src_hash(kern))
     roofline = dict(kernel=kern, stage=dom_name, bound=stage_out[dom_name]["bound"], achieved=round(achieved, 2),
                     peak=peak, unit=unit, frac=round(achieved / peak, 4), traffic=traffic,
                     algorithmic_bytes=int(dom.bytes), algorithmic_flops=int(dom.flops),
                     avg_launch_us=round(times[dom_name] * 1e6, 2))
-    counters = read_counters(f"{kern.split('+')[0]}_{wl.name}_counters.txt", src_hash(*dom.src))
+    counters = read_counters(f"{kern.split('+')[0]}_{wl.name}_counters.txt", kernel_src_hash(kern.split('+')[0]))
     if counters:
         roofline["counters"] = counters
     return wl, value, ms_per_step, stage_out, roofline
@@ -962,14 +969,13 @@ def main():
     if args.summarize_counters:
         tag = WORKLOAD_TAGS[args.config]
         out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{tag}_counters.txt")
-        summarize_counters(args.summarize_counters, args.kernel, src_hash(*KERNEL_SOURCES[args.kernel]), out,
+        summarize_counters(args.summarize_counters, args.kernel, kernel_src_hash(args.kernel), out,
                            args.profile_cmd, tag)
         return
     if args.summarize_pmc:
         tag = WORKLOAD_TAGS[args.config]
         out = args.out or os.path.join(ROOT, "profiles", f"{args.kernel}_{tag}_pmc.txt")
-        srcs = sorted({f for kn in args.kernel.split("+") for f in KERNEL_SOURCES[kn]})
-        summarize_pmc(*args.summarize_pmc, args.kernel, src_hash(*srcs), out, args.profile_cmd, tag)
+        summarize_pmc(*args.summarize_pmc, args.kernel, kernel_src_hash(args.kernel), out, args.profile_cmd, tag)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): there is no multi-GPU path; "

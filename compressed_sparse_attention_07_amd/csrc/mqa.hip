@@ -110,6 +110,11 @@ __device__ __forceinline__ int64_t slot_row(const AttnArgs& a, const Slots& s, i
 
 constexpr int kKT = 32;   // keys per tile
 
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
+constexpr float kLn2 = 0.6931471805599453f;     // ln(2)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+
 // At D = 512 a wave needs ~400 registers (16 heads x 512 fp32 accumulators, the
 // queries and one prefetched tile), so those workgroups are capped at 4 waves.
 template <int D>
@@ -542,7 +547,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[kDmaStages * STAGE];
   __shared__ __attribute__((aligned(16))) float rscale[FP8 ? kDmaStages : 1][kKT];  // FP8MIX entry scales
   __shared__ __attribute__((aligned(16))) int idx_s[kDmaIdxCap];
-  __shared__ __attribute__((aligned(16))) int kvalid[kDmaStages][kKT];
+  __shared__ __attribute__((aligned(16))) float kbias[kDmaStages][kKT];  // 0, or -inf for an empty slot
   __shared__ int64_t wpos_s[kDmaStages][kKT];  // window position of a window row, -1 otherwise
   __shared__ float2 qcs[64];
   __shared__ double theta[64];
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
         if (a.sparse) e = idx_s[min(slot - u_lo, static_cast<int64_t>(kDmaIdxCap - 1))];
         const int64_t wp = u_wstart + (slot - u_nsel);
         const bool ok = live && (!sel || e >= 0);
-        kvalid[st][j] = ok ? 1 : 0;
+        kbias[st][j] = ok ? 0.f : -INFINITY;
         wpos_s[st][j] = (ok && !sel) ? wp : -1;
         if (ok && sel) {
           rid = S.b * a.kv_rows + e;
@@ -700,7 +705,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
       if (a.sparse) e = idx_s[min(slot - u_lo, static_cast<int64_t>(kDmaIdxCap - 1))];
       const int64_t wp = u_wstart + (slot - u_nsel);
       const bool ok = live && (!sel || e >= 0);
-      kvalid[st][j] = ok ? 1 : 0;
+      kbias[st][j] = ok ? 0.f : -INFINITY;
       wpos_s[st][j] = (ok && !sel) ? wp : -1;
       src = !ok ? win_self : (sel ? kv_b + e * D : win_b + wp * D);
     }
@@ -817,6 +822,8 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   f32x4 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max in base-2 units (logits scaled by scale * log2 e), exponentials by v_exp_f32
+  const float scale2 = a.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
 
   // ---- FQ: S^T from the raw rows of stage st: the D - R coded dims by 128-deep fp8
@@ -884,11 +891,11 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int4 kv4 = *reinterpret_cast<const int4*>(&kvalid[st][16 * kb + 4 * grp]);
-      const int vv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+      const float4 kb4 = *reinterpret_cast<const float4*>(&kbias[st][16 * kb + 4 * grp]);
+      const float bias[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = vv[r] ? a.scale * sacc[kb][r] : -INFINITY;
+        const float v = fmaf(sacc[kb][r], scale2, bias[r]);  // logit in base-2 units
         z[kb][r] = v;
         mt = fmaxf(mt, v);
       }
@@ -898,20 +905,20 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const bool raise = mt > m_run + kSlack;
     const float m_ref = raise ? mt : m_run;
     if (__any(raise)) {
-      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : __expf(m_run - m_ref);
+      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : exp2_fast(m_run - m_ref);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
     }
     m_run = m_ref;
-    const bool none = (m_run == -INFINITY);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // every key so far empty: each p is 2^-inf = 0
     float pn[8];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = none ? 0.f : __expf(z[kb][r] - m_run);
+        const float p = exp2_fast(z[kb][r] - m_use);
         psum += p;
         pn[4 * kb + r] = p;
       }
@@ -1012,7 +1019,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const float sk = a.sink[h];
     if (sk == INFINITY) scl = 0.f;
     else if (sk == -INFINITY) scl = 1.f / l_tot;
-    else scl = 1.f / (l_tot + __expf(sk - m_run));
+    else scl = 1.f / (l_tot + exp2_fast(fmaf(sk, kLog2e, -m_run)));
   }
   __syncthreads();  // every wave is done reading the ring
   uint16_t* rows = ring + wid * 16 * KP;  // this wave's 16 result rows, pitch KP
@@ -1032,7 +1039,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     }
     *reinterpret_cast<uint2*>(rows + col * KP + d0) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
-  if (part && grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
+  if (part && grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run * kLn2, l_tot);  // natural-log units
   // lane l moves dims [8 l, 8 l + 8) of each of the wave's 16 rows (written by this wave)
   const int64_t h0 = bt * a.H + hg * a.hpw + wid * 16;  // the wave's first (token, head) row
 #pragma unroll 4
@@ -1071,7 +1078,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t ring[kDmaStages * STAGE];
   __shared__ __attribute__((aligned(16))) int idx_s[kDmaIdxCap];
-  __shared__ __attribute__((aligned(16))) int kvalid[kDmaStages][kKT];
+  __shared__ __attribute__((aligned(16))) float kbias[kDmaStages][kKT];  // 0, or -inf for an empty slot
   __shared__ int64_t wpos_s[kDmaStages][kKT];
   __shared__ float2 qcs[64];
   __shared__ double theta[64];
@@ -1154,7 +1161,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
       if (a.sparse) e = idx_s[min(slot - u_lo, static_cast<int64_t>(kDmaIdxCap - 1))];
       const int64_t wp = u_wstart + (slot - u_nsel);
       const bool ok = live && (!sel || e >= 0);
-      kvalid[st][j] = ok ? 1 : 0;
+      kbias[st][j] = ok ? 0.f : -INFINITY;
       wpos_s[st][j] = (ok && !sel) ? wp : -1;
       src = !ok ? win_self : (sel ? kv_b + e * D : win_b + wp * D);
     }
@@ -1232,6 +1239,8 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
   f32x4 acc[NDBH];
 #pragma unroll
   for (int i = 0; i < NDBH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max in base-2 units (logits scaled by scale * log2 e), exponentials by v_exp_f32
+  const float scale2 = a.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
 
   for (int t = 0; t < ntiles; ++t) {
@@ -1282,11 +1291,11 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int4 kv4 = *reinterpret_cast<const int4*>(&kvalid[st][16 * kb + 4 * grp]);
-      const int vv[4] = {kv4.x, kv4.y, kv4.z, kv4.w};
+      const float4 kb4 = *reinterpret_cast<const float4*>(&kbias[st][16 * kb + 4 * grp]);
+      const float bias[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = vv[r] ? a.scale * sacc[kb][r] : -INFINITY;
+        const float v = fmaf(sacc[kb][r], scale2, bias[r]);  // logit in base-2 units
         z[kb][r] = v;
         mt = fmaxf(mt, v);
       }
@@ -1296,20 +1305,20 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
     const bool raise = mt > m_run + kSlack;
     const float m_ref = raise ? mt : m_run;
     if (__any(raise)) {
-      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : __expf(m_run - m_ref);
+      const float alpha = (m_run == -INFINITY || !raise) ? (raise ? 0.f : 1.f) : exp2_fast(m_run - m_ref);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDBH; ++db) acc[db] *= alpha;
     }
     m_run = m_ref;
-    const bool none = (m_run == -INFINITY);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // every key so far empty: each p is 2^-inf = 0
     float pn[8];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = none ? 0.f : __expf(z[kb][r] - m_run);
+        const float p = exp2_fast(z[kb][r] - m_use);
         psum += p;
         pn[4 * kb + r] = p;
       }
@@ -1348,7 +1357,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
     const float sk = a.sink[h];
     if (sk == INFINITY) scl = 0.f;
     else if (sk == -INFINITY) scl = 1.f / l_tot;
-    else scl = 1.f / (l_tot + __expf(sk - m_run));
+    else scl = 1.f / (l_tot + exp2_fast(fmaf(sk, kLog2e, -m_run)));
   }
   __syncthreads();  // every wave is done reading the ring
   // result rows leave through LDS so that every store writes 512 contiguous bytes
@@ -1369,7 +1378,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
     *reinterpret_cast<uint2*>(rows + col * KP + 16 * db + 4 * grp) =
         make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
-  if (part && hw == 0 && grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run, l_tot);
+  if (part && hw == 0 && grp == 0) a.part_ml[th * a.nsplit + sp] = make_float2(m_run * kLn2, l_tot);  // natural-log units
   // lanes 0-31 move row 2i, lanes 32-63 row 2i + 1: 16 bytes each of this wave's half
   const int64_t h0 = bt * a.H + hg * a.hpw + pr * 16;
   const int rsub = lane >> 5;

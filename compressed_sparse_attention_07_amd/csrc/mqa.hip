@@ -110,6 +110,13 @@ __device__ __forceinline__ int64_t slot_row(const AttnArgs& a, const Slots& s, i
 
 constexpr int kKT = 32;   // keys per tile
 
+// 16 bytes of a result row.  Split partials are read once, by the combine launch:
+// they are stored with the nontemporal hint.
+__device__ __forceinline__ void store_row16(uint16_t* dst, uint4 v, bool partial) {
+  if (partial) __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(dst));
+  else *reinterpret_cast<uint4*>(dst) = v;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 constexpr float kLn2 = 0.6931471805599453f;     // ln(2)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -1046,7 +1053,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   for (int r = 0; r < 16; ++r) {
     const uint4 v = *reinterpret_cast<const uint4*>(rows + r * KP + 8 * lane);
     uint16_t* dst = part ? a.part_o + ((h0 + r) * a.nsplit + sp) * D : static_cast<uint16_t*>(a.out) + (h0 + r) * D;
-    *reinterpret_cast<uint4*>(dst + 8 * lane) = v;
+    store_row16(dst + 8 * lane, v, part);
   }
 }
 
@@ -1388,7 +1395,7 @@ __global__ __launch_bounds__(NW * 64) void attn_pair_kernel(AttnArgs a) {
     const int r = 2 * i + rsub;
     const uint4 v = *reinterpret_cast<const uint4*>(rows + r * KP + dl);
     uint16_t* dst = part ? a.part_o + ((h0 + r) * a.nsplit + sp) * D : static_cast<uint16_t*>(a.out) + (h0 + r) * D;
-    *reinterpret_cast<uint4*>(dst + HD * hw + dl) = v;
+    store_row16(dst + HD * hw + dl, v, part);
   }
 }
 

@@ -41,6 +41,12 @@ namespace csa {
 
 namespace {
 
+// max(x, 0) as one integer max of the bit pattern: a float with the sign bit set is a
+// negative integer and becomes +0, any other value is unchanged.  fmaxf on an MFMA
+// result costs two instructions, the first quieting a possible signalling NaN.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+
 // A score as stored: fp32, or rounded to bf16 (nearest-even) for the BF16-score
 // variant ([V4-CN] §3.4 stores the index scores in BF16 for a faster selection).
 __device__ __forceinline__ float stored_score(const IndexLaunch& a, float v) {
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mfma_kernel(IndexLau
           for (int ks = 0; ks < KS; ++ks)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hb][ks], kb[tI][ks], acc, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
+          for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], relu_bits(acc[r]), sc);
         }
         // sum the four row groups (heads) holding the same entry
         sc = rows4_sum(sc);
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(NWV * WAVE) void index_stream_kernel(IndexLaunch a,
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hb][ks], kb[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
+        for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], relu_bits(acc[r]), sc);
       }
       sc = rows4_sum(sc);
       // tiles are stored in runs of four: lane (col, grp) holds entry 16 grp + col of the run
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(kPfWaves * WAVE) void index_prefill_kernel(IndexLau
             for (int ks = 0; ks < KS; ++ks)
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u][hb][ks], kb[ks], acc, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc = fmaf(w[u][hb][r], fmaxf(acc[r], 0.f), sc);
+            for (int r = 0; r < 4; ++r) sc = fmaf(w[u][hb][r], relu_bits(acc[r]), sc);
           }
           sc = rows4_sum(sc);
           part[u][tI] = sc;
@@ -711,7 +717,7 @@ __global__ __launch_bounds__(kWavesPerWG * WAVE) void index_mxfp4_kernel(IndexLa
                                                                     kscale);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], fmaxf(acc[r], 0.f), sc);
+          for (int r = 0; r < 4; ++r) sc = fmaf(w[hb][r], relu_bits(acc[r]), sc);
         }
         sc = rows4_sum(sc);
         part[tI] = sc;

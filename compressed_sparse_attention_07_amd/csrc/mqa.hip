@@ -1425,7 +1425,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   uint4 pv[kBatchSplits];
 #pragma unroll
   for (int u = 0; u < kBatchSplits; ++u)
-    pv[u] = *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(u < ns ? u : 0) * a.D);
+    pv[u] = load_stream16(pb + static_cast<int64_t>(u < ns ? u : 0) * a.D);
   const float M = wave_max_dpp(mlx);
   const float wgt = (mlx == -INFINITY) ? 0.f : __expf(mlx - M) * ml.y;
   const float L = wave_sum_dpp(wgt);
@@ -1434,7 +1434,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     if (i0 > 0) {
 #pragma unroll
       for (int u = 0; u < kBatchSplits; ++u)
-        pv[u] = *reinterpret_cast<const uint4*>(pb + static_cast<int64_t>(i0 + u < ns ? i0 + u : 0) * a.D);
+        pv[u] = load_stream16(pb + static_cast<int64_t>(i0 + u < ns ? i0 + u : 0) * a.D);
     }
 #pragma unroll
     for (int u = 0; u < kBatchSplits; ++u) {
